@@ -1,0 +1,192 @@
+/*
+ * lapsum.h -- C ABI of the MI355X (gfx950) Fast LapSum exact soft top-k library.
+ *
+ * Operator ("Fast LapSum: Exact Differentiable Top-k at Million Scale",
+ * section 2.1, eqs. (1)-(2)): for each row of scores r_1..r_n, a budget k with
+ * 0 < k < n and a temperature t > 0 (the Laplace scale),
+ *     p_i = F((r_i - b)/t),   F(z) = e^z/2 (z < 0),  1 - e^-z/2 (z >= 0),
+ * where the threshold b is the unique root of  sum_i p_i = k.  The backward
+ * pass is the analytic vector-Jacobian product (same section): with
+ * d_i = min(p_i, 1 - p_i)/t (the Laplace density at the score),
+ *     dk   = sum_i g_i d_i / sum_i d_i,     dr_i = d_i (g_i - dk).
+ *
+ * Solvers (section 2.2): a full sort of the row followed by one stable
+ * prefix/suffix scan, an index lookup of the balancing interval and a
+ * closed-form root; and, for million-scale rows, probabilistic bracketing
+ * (sample, binomial order-statistic bracket, one streaming pass that folds
+ * out-of-bracket scores into tail sums and keeps the middle band, an exact
+ * solve on the band, and certification with a deterministic full-sort
+ * fallback when the bracket misses).
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments marked "device" are device pointers on the current HIP
+ *     device; "host" pointers are read during the call only.
+ *   - r, p, g, dr are contiguous row-major [rows, n] fp32; b is fp64 [rows];
+ *     dk is fp32 [rows].  k and t are shared by all rows.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates or frees device memory, never synchronises the stream
+ *     and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Outputs are valid once the stream reaches the call's end.
+ *   - The returned status covers host-side argument checks and launch errors
+ *     only.  Per-row outcomes (bracket hit/miss, fallback, degenerate
+ *     backward) are reported through the optional `stats` array.
+ *   - Scores must be finite; non-finite scores give unspecified outputs (the
+ *     kernels still terminate).
+ *   - Results are deterministic: the same inputs, options and seed give
+ *     bitwise identical outputs.
+ */
+#ifndef LAPSUM_H
+#define LAPSUM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lapsum_status {
+    LAPSUM_OK = 0,
+    LAPSUM_ERR_NULL = 1,      /* a required pointer is NULL */
+    LAPSUM_ERR_SHAPE = 2,     /* rows < 1, n < 1, n > LAPSUM_MAX_N, rows > LAPSUM_MAX_ROWS */
+    LAPSUM_ERR_K = 3,         /* k not finite or not in (0, n) */
+    LAPSUM_ERR_T = 4,         /* t not finite or t <= 0 */
+    LAPSUM_ERR_WORKSPACE = 5, /* workspace smaller than lapsum_workspace_bytes() or not 256-byte aligned */
+    LAPSUM_ERR_PATH = 6,      /* the requested path cannot run this shape */
+    LAPSUM_ERR_OPTION = 7,    /* an option is out of range */
+    LAPSUM_ERR_HIP = 8        /* a HIP launch or runtime query failed */
+} lapsum_status;
+
+/* Longest row: sample indices use 32x32-bit products and tile counts fit int32. */
+#define LAPSUM_MAX_N ((int64_t)1 << 31)
+#define LAPSUM_MAX_ROWS ((int64_t)1 << 24)
+/* Longest row the on-chip (LDS/register) sort path takes. */
+#define LAPSUM_ONCHIP_MAX_N 8192
+
+typedef enum lapsum_path {
+    LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: FULLSORT; else BRACKET */
+    LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
+    LAPSUM_PATH_FULLSORT = 2, /* radix sort + tiled scan + locate/root + streaming apply */
+    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing with full-sort fallback */
+} lapsum_path;
+
+/* Per-row flags in lapsum_row_stats.flags. */
+#define LAPSUM_FLAG_BRACKET 0x1     /* the bracketing path ran for this row */
+#define LAPSUM_FLAG_HIT 0x2         /* the first bracket held (certified) */
+#define LAPSUM_FLAG_FALLBACK 0x4    /* b came from the full-sort fallback */
+#define LAPSUM_FLAG_OVERFLOW 0x8    /* the band exceeded its capacity (counted as a miss) */
+#define LAPSUM_FLAG_DEGENERATE 0x10 /* backward: every d_i was 0 in fp32, so dr = 0 and dk = 0 */
+
+/* Optional per-row diagnostics, written by lapsum_forward (all fields) and
+ * lapsum_backward (flags |= LAPSUM_FLAG_DEGENERATE only).  Device memory. */
+typedef struct lapsum_row_stats {
+    double a_lo, a_hi;       /* bracket [a_L, a_R); -inf / +inf when open */
+    double tail_lo, tail_hi; /* S_L = sum_{r<a_L} e^{(r-a_L)/t},  S_R = sum_{r>=a_R} e^{-(r-a_R)/t} */
+    int64_t count_lo;        /* c_L = #{r < a_L} */
+    int64_t count_hi;        /* c_R = #{r >= a_R} */
+    int64_t band;            /* M = #{a_L <= r < a_R} (may exceed the capacity) */
+    int32_t flags;           /* LAPSUM_FLAG_* */
+    int32_t reserved;
+} lapsum_row_stats;
+
+/* Stage ids for optional per-stage timing (lapsum_options.stage_events). */
+enum {
+    LAPSUM_STAGE_ONCHIP_FWD = 0, /* fused on-chip forward */
+    LAPSUM_STAGE_INIT = 1,       /* per-call state reset */
+    LAPSUM_STAGE_SAMPLE = 2,     /* kernel-noised sample */
+    LAPSUM_STAGE_SELECT = 3,     /* order statistics -> bracket */
+    LAPSUM_STAGE_FILTER = 4,     /* streaming tail sums + band compaction */
+    LAPSUM_STAGE_BAND = 5,       /* band sort + scan + root + certification */
+    LAPSUM_STAGE_FULLSORT = 6,   /* full-sort solve (full-sort path or fallback) */
+    LAPSUM_STAGE_APPLY = 7,      /* streaming Laplace-CDF apply */
+    LAPSUM_STAGE_ONCHIP_BWD = 8, /* fused on-chip backward */
+    LAPSUM_STAGE_BWD_REDUCE = 9, /* streaming backward reductions (D, G) */
+    LAPSUM_STAGE_BWD_APPLY = 10, /* streaming backward elementwise dr */
+    LAPSUM_STAGE_COUNT = 11
+};
+
+typedef struct lapsum_options {
+    int32_t path;          /* lapsum_path; LAPSUM_PATH_AUTO picks by n */
+    int32_t sample_log2;   /* bracketing sample size m = 2^sample_log2 (4..20);
+                              0 = min(16, max(4, floor(log2(n/16)))) */
+    double delta;          /* bracket miss probability bound in (0, 1); 0 = 1e-6 */
+    uint64_t seed;         /* Philox-4x32-10 key of the sample */
+    int64_t band_capacity; /* 0 = derived from (n, k, m, delta); else an override >= 1 */
+    const double *bracket_override; /* host [2] or NULL: force (a_L, a_R) on every row
+                                       instead of sampling (used to test the fallback) */
+    lapsum_row_stats *stats;        /* device [rows] or NULL */
+    void *const *stage_events;      /* host array of 2*LAPSUM_STAGE_COUNT hipEvent_t or NULL;
+                                       entries 2s and 2s+1 (if non-NULL) are recorded on the
+                                       stream before and after stage s */
+} lapsum_options;
+
+/* Resolved plan of a call (host-only query, no GPU needed). */
+typedef struct lapsum_plan_info {
+    int32_t path;          /* resolved lapsum_path */
+    int32_t sample_log2;   /* bracketing: log2(m) */
+    int64_t m;             /* bracketing: sample size */
+    int64_t lo, hi;        /* bracketing: 1-based order-statistic indices; lo = 0 means
+                              a_L = -inf, hi = m + 1 means a_R = +inf */
+    int64_t band_capacity; /* bracketing: band buffer length per row */
+    int32_t band_onchip;   /* bracketing: 1 if the band is solved on chip (capacity <= 8192) */
+    int32_t reserved;
+    uint64_t forward_bytes;  /* workspace bytes lapsum_forward needs */
+    uint64_t backward_bytes; /* workspace bytes lapsum_backward needs */
+} lapsum_plan_info;
+
+/* Fill *opt with defaults (AUTO path, default m and delta, seed 0, no
+ * diagnostics).  A NULL options pointer means the same defaults. */
+void lapsum_options_init(lapsum_options *opt);
+
+/* Human-readable name of a status code (static string). */
+const char *lapsum_status_string(lapsum_status st);
+
+/* Host-only: resolve the path, sample size, bracket indices, band capacity
+ * and workspace sizes for a call with these arguments.  Same argument
+ * checks as lapsum_forward. */
+lapsum_status lapsum_plan(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt,
+                          lapsum_plan_info *out);
+
+/* Host-only: the equal-tailed binomial order-statistic indices of the
+ * localisation step (section 2.2, probabilistic bracketing, step 1).  With
+ * N ~ Bin(m, 1 - k/n) the number of noised samples at or below b,
+ *   lo = max{l in [0, m]   : P(N <= l-1) <= delta/2},
+ *   hi = min{h in [1, m+1] : P(N >= h)   <= delta/2},
+ * so P(X_(lo) > b) <= delta/2 and P(X_(hi) <= b) <= delta/2. */
+lapsum_status lapsum_bracket_indices(int64_t n, double k, int64_t m, double delta, int64_t *lo, int64_t *hi);
+
+/* Workspace bytes sufficient for both lapsum_forward and lapsum_backward
+ * with these arguments (the maximum of the two; 0 when neither needs any). */
+size_t lapsum_workspace_bytes(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt);
+
+/* Forward (section 2.1 eqs. (1)-(2); solvers of section 2.2).
+ *   r  device [rows, n] fp32 scores (read only)
+ *   p  device [rows, n] fp32 output probabilities (must not alias r)
+ *   b  device [rows]    fp64 output thresholds
+ *   workspace, workspace_bytes: device scratch of at least
+ *       lapsum_workspace_bytes() bytes, 256-byte aligned (may be NULL when
+ *       that size is 0); its contents need no initialisation.
+ *   opt may be NULL.  Errors: LAPSUM_ERR_NULL, _SHAPE, _K, _T, _WORKSPACE,
+ *   _PATH, _OPTION (nothing launched), LAPSUM_ERR_HIP (launch failed). */
+lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, double t, float *p, double *b,
+                             void *workspace, size_t workspace_bytes, const lapsum_options *opt, void *stream);
+
+/* Backward: the analytic VJP of the forward (section 2.1).
+ *   g  device [rows, n] fp32 upstream gradient w.r.t. p
+ *   p  device [rows, n] fp32 probabilities from lapsum_forward
+ *   b  device [rows]    fp64 thresholds from lapsum_forward (accepted for
+ *      symmetry with the forward; the VJP needs only p and t because
+ *      min(p, 1 - p) is the Laplace density at the score)
+ *   dr device [rows, n] fp32 output (may alias g, not p)
+ *   dk device [rows]    fp32 output
+ *   Only opt->stats and opt->stage_events are read.  Errors as forward. */
+lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
+                              float *dr, float *dk, void *workspace, size_t workspace_bytes,
+                              const lapsum_options *opt, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAPSUM_H */

@@ -1,0 +1,269 @@
+"""MI355X (gfx950) Fast LapSum exact soft top-k: Python binding of liblapsum.so.
+
+This module only marshals arguments: every step of the operator runs in the
+HIP kernels of ``liblapsum.so`` (see ``include/lapsum.h``).  PyTorch provides
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library is missing or the tensors are not on a GPU, the calls raise.
+
+    p, b = lapsum_forward(r, k, t)          # r: [rows, n] fp32 on cuda
+    dr, dk = lapsum_backward(g, p, b, t)
+
+Source of the operator: "Fast LapSum: Exact Differentiable Top-k at Million
+Scale", section 2.1 (eqs. (1)-(2), analytic VJP) and section 2.2 (full-sort
+solver and probabilistic bracketing).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblapsum.so")
+
+PATH_AUTO, PATH_ONCHIP, PATH_FULLSORT, PATH_BRACKET = 0, 1, 2, 3
+PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "fullsort": PATH_FULLSORT, "bracket": PATH_BRACKET}
+FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE = 0x1, 0x2, 0x4, 0x8, 0x10
+ONCHIP_MAX_N = 8192
+(STAGE_ONCHIP_FWD, STAGE_INIT, STAGE_SAMPLE, STAGE_SELECT, STAGE_FILTER, STAGE_BAND, STAGE_FULLSORT,
+ STAGE_APPLY, STAGE_ONCHIP_BWD, STAGE_BWD_REDUCE, STAGE_BWD_APPLY, STAGE_COUNT) = range(12)
+STAGE_NAMES = ["onchip_fwd", "init", "sample", "select", "filter", "band", "fullsort", "apply",
+               "onchip_bwd", "bwd_reduce", "bwd_apply"]
+
+EXPORTED = ["lapsum_options_init", "lapsum_status_string", "lapsum_plan", "lapsum_bracket_indices",
+            "lapsum_workspace_bytes", "lapsum_forward", "lapsum_backward"]
+
+
+class LapsumError(RuntimeError):
+    pass
+
+
+class RowStats(ctypes.Structure):
+    _fields_ = [("a_lo", ctypes.c_double), ("a_hi", ctypes.c_double),
+                ("tail_lo", ctypes.c_double), ("tail_hi", ctypes.c_double),
+                ("count_lo", ctypes.c_int64), ("count_hi", ctypes.c_int64), ("band", ctypes.c_int64),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("sample_log2", ctypes.c_int32), ("delta", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("band_capacity", ctypes.c_int64),
+                ("bracket_override", ctypes.POINTER(ctypes.c_double)),
+                ("stats", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("sample_log2", ctypes.c_int32), ("m", ctypes.c_int64),
+                ("lo", ctypes.c_int64), ("hi", ctypes.c_int64), ("band_capacity", ctypes.c_int64),
+                ("band_onchip", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("forward_bytes", ctypes.c_uint64), ("backward_bytes", ctypes.c_uint64)]
+
+
+STATS_DTYPE_FIELDS = [f for f, _ in RowStats._fields_]
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load liblapsum.so (built in-tree by ``python -m sparse_selection_primitive_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LapsumError(f"{LIB_PATH} is missing: build it with `python -m sparse_selection_primitive_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.lapsum_options_init.argtypes = [ctypes.POINTER(Options)]
+    lib.lapsum_options_init.restype = None
+    lib.lapsum_status_string.argtypes = [ctypes.c_int]
+    lib.lapsum_status_string.restype = ctypes.c_char_p
+    lib.lapsum_plan.argtypes = [i64, i64, dbl, dbl, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
+    lib.lapsum_plan.restype = ctypes.c_int
+    lib.lapsum_bracket_indices.argtypes = [i64, dbl, i64, dbl, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.lapsum_bracket_indices.restype = ctypes.c_int
+    lib.lapsum_workspace_bytes.argtypes = [i64, i64, dbl, dbl, ctypes.POINTER(Options)]
+    lib.lapsum_workspace_bytes.restype = ctypes.c_size_t
+    lib.lapsum_forward.argtypes = [vp, i64, i64, dbl, dbl, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(Options), vp]
+    lib.lapsum_forward.restype = ctypes.c_int
+    lib.lapsum_backward.argtypes = [vp, vp, vp, i64, i64, dbl, vp, vp, vp, ctypes.c_size_t,
+                                    ctypes.POINTER(Options), vp]
+    lib.lapsum_backward.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().lapsum_status_string(rc).decode()
+        raise LapsumError(f"{what}: {msg} (status {rc})")
+
+
+def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0, bracket_override=None,
+                 stats_ptr=None, stage_events=None):
+    opt = Options()
+    load_library().lapsum_options_init(ctypes.byref(opt))
+    opt.path = PATHS[path] if isinstance(path, str) else int(path)
+    opt.sample_log2 = int(sample_log2)
+    opt.delta = float(delta)
+    opt.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    opt.band_capacity = int(band_capacity)
+    keep = []
+    if bracket_override is not None:
+        arr = (ctypes.c_double * 2)(float(bracket_override[0]), float(bracket_override[1]))
+        keep.append(arr)
+        opt.bracket_override = ctypes.cast(arr, ctypes.POINTER(ctypes.c_double))
+    if stats_ptr is not None:
+        opt.stats = ctypes.c_void_p(stats_ptr)
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * (2 * STAGE_COUNT))(*stage_events)
+        keep.append(arr)
+        opt.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    opt._keep = keep  # keep ctypes buffers alive with the struct
+    return opt
+
+
+def plan(rows: int, n: int, k: float, t: float, **opts) -> dict:
+    """Host-only: path, sample size, bracket indices, capacity and workspace sizes."""
+    info = PlanInfo()
+    opt = make_options(**opts)
+    _check(load_library().lapsum_plan(rows, n, float(k), float(t), ctypes.byref(opt), ctypes.byref(info)),
+           "lapsum_plan")
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_ if f != "reserved"}
+
+
+def bracket_indices(n: int, k: float, m: int, delta: float):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().lapsum_bracket_indices(n, float(k), m, float(delta), ctypes.byref(lo), ctypes.byref(hi)),
+           "lapsum_bracket_indices")
+    return lo.value, hi.value
+
+
+def workspace_bytes(rows: int, n: int, k: float, t: float, **opts) -> int:
+    opt = make_options(**opts)
+    return int(load_library().lapsum_workspace_bytes(rows, n, float(k), float(t), ctypes.byref(opt)))
+
+
+# --------------------------------------------------------------- torch side
+_ws_cache: dict = {}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _workspace(nbytes: int, device):
+    """A cached, 256-byte-aligned device buffer of at least nbytes."""
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    key = (device.type, device.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes + 256:
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    ptr = buf.data_ptr()
+    return ptr + ((-ptr) % 256), buf.numel() - ((-ptr) % 256)
+
+
+def _as_rows(x, name):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise LapsumError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if x.dtype != torch.float32:
+        raise LapsumError(f"{name} must be float32")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2:
+        raise LapsumError(f"{name} must be [rows, n] or [n]")
+    return x.contiguous()
+
+
+def lapsum_forward(r, k: float, t: float, *, path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
+                   bracket_override=None, stats=False, stage_events=None, out=None):
+    """p, b (and per-row stats if stats=True) for scores r [rows, n] fp32 on GPU.
+
+    p is fp32 [rows, n]; b is fp64 [rows].  Stats is an int/float dict of
+    per-row tensors (bracket ends, tail sums, counts, band size, flags)."""
+    torch = _torch()
+    lib = load_library()
+    r2 = _as_rows(r, "r")
+    rows, n = r2.shape
+    dev = r2.device
+    with torch.cuda.device(dev):
+        p = torch.empty_like(r2) if out is None else out[0]
+        b = torch.empty(rows, dtype=torch.float64, device=dev) if out is None else out[1]
+        st = torch.empty(rows * ctypes.sizeof(RowStats), dtype=torch.uint8, device=dev) if stats else None
+        opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
+                           st.data_ptr() if st is not None else None, stage_events)
+        nbytes = int(lib.lapsum_workspace_bytes(rows, n, float(k), float(t), ctypes.byref(opt)))
+        wptr, wlen = _workspace(nbytes, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.lapsum_forward(r2.data_ptr(), rows, n, float(k), float(t), p.data_ptr(), b.data_ptr(),
+                                wptr, wlen, ctypes.byref(opt), stream)
+        _check(rc, "lapsum_forward")
+    if r.dim() == 1:
+        p, b = p[0], b
+    if stats:
+        return p, b, decode_stats(st, rows)
+    return p, b
+
+
+def decode_stats(buf, rows: int) -> dict:
+    """Per-row lapsum_row_stats (device bytes) -> dict of CPU tensors."""
+    torch = _torch()
+    raw = buf.cpu().numpy().tobytes()
+    arr = (RowStats * rows).from_buffer_copy(raw)
+    out = {f: [getattr(arr[i], f) for i in range(rows)] for f in STATS_DTYPE_FIELDS if f != "reserved"}
+    return {f: torch.tensor(v) for f, v in out.items()}
+
+
+def lapsum_backward(g, p, b, t: float, *, stats_buf=None, stage_events=None, out=None):
+    """dr [rows, n] fp32 and dk [rows] fp32: the analytic VJP of the forward."""
+    torch = _torch()
+    lib = load_library()
+    g2 = _as_rows(g, "g")
+    p2 = _as_rows(p, "p")
+    if g2.shape != p2.shape:
+        raise LapsumError("g and p must have the same shape")
+    rows, n = g2.shape
+    dev = g2.device
+    if not (isinstance(b, torch.Tensor) and b.is_cuda and b.dtype == torch.float64 and b.numel() == rows):
+        raise LapsumError("b must be a float64 GPU tensor with one entry per row")
+    with torch.cuda.device(dev):
+        dr = torch.empty_like(g2) if out is None else out[0]
+        dk = torch.empty(rows, dtype=torch.float32, device=dev) if out is None else out[1]
+        opt = make_options(stats_ptr=stats_buf.data_ptr() if stats_buf is not None else None,
+                           stage_events=stage_events)
+        nbytes = int(lib.lapsum_workspace_bytes(rows, n, 0.5 * n, float(t), None))
+        wptr, wlen = _workspace(nbytes, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.lapsum_backward(g2.data_ptr(), p2.data_ptr(), b.contiguous().data_ptr(), rows, n, float(t),
+                                 dr.data_ptr(), dk.data_ptr(), wptr, wlen, ctypes.byref(opt), stream)
+        _check(rc, "lapsum_backward")
+    if g.dim() == 1:
+        dr = dr[0]
+    return dr, dk
+
+
+def soft_topk(r, k: float, t: float, **kw):
+    """Differentiable soft top-k: autograd wrapper over the two entry points."""
+    torch = _torch()
+
+    class _LapSum(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x):
+            p, b = lapsum_forward(x, k, t, **kw)
+            ctx.save_for_backward(p, b)
+            return p
+
+        @staticmethod
+        def backward(ctx, gp):
+            p, b = ctx.saved_tensors
+            dr, _ = lapsum_backward(gp.contiguous(), p, b, t)
+            return dr
+
+    return _LapSum.apply(r)

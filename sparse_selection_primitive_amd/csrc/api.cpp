@@ -1,0 +1,415 @@
+// Host runtime of the C ABI declared in include/lapsum.h: argument checks,
+// path choice, bracket indices, workspace layout and the launch sequence of
+// each path on the caller's stream.  No device memory is allocated here and
+// the stream is never synchronised.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "lapsum_device.hpp"
+#include "lapsum_internal.hpp"
+
+using namespace lapsum;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kOnchipMaxN = LAPSUM_ONCHIP_MAX_N;
+constexpr int64_t kFullsortMaxAutoN = (int64_t)1 << 20;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// Offsets of the workspace regions of the large-row solver for `rows` rows
+// of stride `stride` (a multiple of kTile).
+struct SegRegions {
+  size_t A, B, hist, dtot, tagg, tpre, tsuf;
+  int64_t stride;
+  int max_tiles;
+};
+
+SegRegions seg_regions(Layout &L, int64_t rows, int64_t len) {
+  SegRegions r;
+  r.stride = round_up(len < 1 ? 1 : len, kTile);
+  r.max_tiles = (int)(r.stride / kTile);
+  const size_t keys = (size_t)rows * (size_t)r.stride * sizeof(uint32_t);
+  r.A = L.take(keys);
+  r.B = L.take(keys);
+  r.hist = L.take((size_t)rows * 256 * (size_t)r.max_tiles * sizeof(uint32_t));
+  r.dtot = L.take((size_t)rows * 256 * sizeof(uint32_t));
+  r.tagg = L.take((size_t)rows * (size_t)r.max_tiles * tile_agg_bytes());
+  r.tpre = L.take((size_t)rows * (size_t)r.max_tiles * pre_bytes());
+  r.tsuf = L.take((size_t)rows * (size_t)r.max_tiles * suf_bytes());
+  return r;
+}
+
+struct Plan {
+  int path = 0;
+  int sample_log2 = 0;
+  int64_t m = 0, lo = 0, hi = 0;
+  int64_t cap = 0;  // band capacity per row
+  bool band_onchip = false;
+  // forward layout
+  size_t fwd_bytes = 0;
+  size_t st = 0, samples = 0, fpart = 0, band = 0;
+  int fgx = 0;
+  SegRegions band_seg{}, full_seg{};
+  // backward layout
+  size_t bwd_bytes = 0;
+  size_t bst = 0, bpart = 0;
+  int bgx = 0;
+};
+
+// Equal-tailed binomial order-statistic indices (host side of the
+// localisation step), with a one-entry cache per thread.
+lapsum_status bracket_indices(int64_t n, double k, int64_t m, double delta, int64_t *lo_out, int64_t *hi_out) {
+  thread_local int64_t c_n = -1, c_m = -1, c_lo = 0, c_hi = 0;
+  thread_local double c_k = -1.0, c_d = -1.0;
+  if (n == c_n && k == c_k && m == c_m && delta == c_d) {
+    *lo_out = c_lo;
+    *hi_out = c_hi;
+    return LAPSUM_OK;
+  }
+  // N ~ Bin(m, q), q = 1 - k/n: log pmf by the ratio recurrence from j = 0
+  const double lq = std::log1p(-k / (double)n);  // ln q
+  const double l1q = std::log(k / (double)n);    // ln (1 - q)
+  std::vector<double> lp((size_t)m + 1);
+  lp[0] = (double)m * l1q;
+  for (int64_t j = 0; j < m; ++j)
+    lp[(size_t)j + 1] = lp[(size_t)j] + std::log((double)(m - j) / (double)(j + 1)) + lq - l1q;
+  // normalise against the maximum to avoid underflow of the bulk, then sum tails
+  double mx = lp[0];
+  for (double v : lp) mx = v > mx ? v : mx;
+  std::vector<double> pmf((size_t)m + 1);
+  long double tot = 0.0L;
+  for (int64_t j = 0; j <= m; ++j) {
+    pmf[(size_t)j] = std::exp(lp[(size_t)j] - mx);
+    tot += pmf[(size_t)j];
+  }
+  const double half = 0.5 * delta;
+  // lo = max{l in [0, m] : P(N <= l-1) <= delta/2}
+  int64_t lo = 0;
+  long double acc = 0.0L;
+  for (int64_t l = 1; l <= m; ++l) {
+    acc += pmf[(size_t)(l - 1)];
+    if ((double)(acc / tot) <= half)
+      lo = l;
+    else
+      break;
+  }
+  // hi = min{h in [1, m+1] : P(N >= h) <= delta/2}
+  int64_t hi = m + 1;
+  acc = 0.0L;
+  for (int64_t h = m; h >= 1; --h) {
+    acc += pmf[(size_t)h];
+    if ((double)(acc / tot) <= half)
+      hi = h;
+    else
+      break;
+  }
+  c_n = n;
+  c_k = k;
+  c_m = m;
+  c_d = delta;
+  c_lo = lo;
+  c_hi = hi;
+  *lo_out = lo;
+  *hi_out = hi;
+  return LAPSUM_OK;
+}
+
+lapsum_status check_common(int64_t rows, int64_t n, double t) {
+  if (rows < 1 || n < 1 || n > LAPSUM_MAX_N || rows > LAPSUM_MAX_ROWS) return LAPSUM_ERR_SHAPE;
+  if ((double)rows * (double)n > 4.0e18) return LAPSUM_ERR_SHAPE;
+  if (!std::isfinite(t) || !(t > 0.0)) return LAPSUM_ERR_T;
+  return LAPSUM_OK;
+}
+
+lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt, Plan &P) {
+  lapsum_status st = check_common(rows, n, t);
+  if (st != LAPSUM_OK) return st;
+  if (!std::isfinite(k) || !(k > 0.0) || !(k < (double)n)) return LAPSUM_ERR_K;
+  lapsum_options o;
+  lapsum_options_init(&o);
+  if (opt) o = *opt;
+  if (o.path < LAPSUM_PATH_AUTO || o.path > LAPSUM_PATH_BRACKET) return LAPSUM_ERR_OPTION;
+  if (o.sample_log2 != 0 && (o.sample_log2 < 4 || o.sample_log2 > 20)) return LAPSUM_ERR_OPTION;
+  if (!(o.delta == 0.0 || (o.delta > 0.0 && o.delta < 1.0))) return LAPSUM_ERR_OPTION;
+  if (o.band_capacity < 0) return LAPSUM_ERR_OPTION;
+  if (o.bracket_override && !(o.bracket_override[0] < o.bracket_override[1])) return LAPSUM_ERR_OPTION;
+
+  int path = o.path;
+  if (path == LAPSUM_PATH_AUTO)
+    path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP : (n <= kFullsortMaxAutoN ? LAPSUM_PATH_FULLSORT : LAPSUM_PATH_BRACKET);
+  if (path == LAPSUM_PATH_ONCHIP && n > kOnchipMaxN) return LAPSUM_ERR_PATH;
+  P.path = path;
+
+  Layout F;
+  if (path == LAPSUM_PATH_FULLSORT) {
+    P.st = F.take((size_t)rows * row_state_bytes());
+    P.full_seg = seg_regions(F, rows, n);
+  } else if (path == LAPSUM_PATH_BRACKET) {
+    int sl = o.sample_log2;
+    if (sl == 0) {
+      sl = 4;
+      if (n >= 256) {
+        sl = (int)std::floor(std::log2((double)n / 16.0));
+        sl = sl < 4 ? 4 : (sl > 16 ? 16 : sl);
+      }
+    }
+    P.sample_log2 = sl;
+    P.m = (int64_t)1 << sl;
+    const double delta = o.delta == 0.0 ? 1e-6 : o.delta;
+    bracket_indices(n, k, P.m, delta, &P.lo, &P.hi);
+    if (o.band_capacity > 0) {
+      P.cap = o.band_capacity;
+    } else {
+      const int64_t lo_eff = P.lo, hi_eff = P.hi;  // lo = 0 / hi = m+1 mean open ends
+      const double frac = (double)(hi_eff - lo_eff) / (double)P.m;
+      double cap = 3.0 * frac * (double)n + 1024.0;
+      if (cap > (double)n) cap = (double)n;
+      P.cap = (int64_t)std::ceil(cap);
+    }
+    if (P.cap < 1) P.cap = 1;
+    P.band_onchip = P.cap <= kOnchipMaxN;
+    if (!P.band_onchip) P.cap = round_up(P.cap, kTile);
+    P.st = F.take((size_t)rows * row_state_bytes());
+    P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
+    P.fgx = filter_grid_x(rows, n);
+    P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
+    P.band = F.take((size_t)rows * (size_t)P.cap * sizeof(uint32_t));
+    if (!P.band_onchip) P.band_seg = seg_regions(F, rows, P.cap);
+    P.full_seg = seg_regions(F, rows, n);
+  }
+  P.fwd_bytes = F.off;
+
+  Layout B;
+  if (!onchip_backward_supported(n)) {
+    P.bst = B.take((size_t)rows * row_state_bytes());
+    P.bgx = bwd_grid_x(rows, n);
+    P.bpart = B.take(bwd_partial_bytes(rows, P.bgx));
+  }
+  P.bwd_bytes = B.off;
+  return LAPSUM_OK;
+}
+
+struct StageTimer {
+  void *const *ev;
+  hipStream_t s;
+  void mark(int stage, int which) const {
+    if (!ev) return;
+    void *e = ev[2 * stage + which];
+    if (e) (void)hipEventRecord((hipEvent_t)e, s);
+  }
+};
+
+lapsum_status hip_status(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LAPSUM_ERR_HIP; }
+
+#define LAPSUM_TRY(expr)                       \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return LAPSUM_ERR_HIP; \
+  } while (0)
+
+SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t n, const float *r,
+                 const uint32_t *band, RowState *st, double k, double t) {
+  SegArgs a;
+  a.mode = mode;
+  a.rows = (int)rows;
+  a.n = n;
+  a.r = r;
+  a.band = band;
+  a.A = reinterpret_cast<uint32_t *>(ws + R.A);
+  a.B = reinterpret_cast<uint32_t *>(ws + R.B);
+  a.stride = R.stride;
+  a.max_tiles = R.max_tiles;
+  a.hist = reinterpret_cast<uint32_t *>(ws + R.hist);
+  a.dtot = reinterpret_cast<uint32_t *>(ws + R.dtot);
+  a.tagg = reinterpret_cast<TileAgg *>(ws + R.tagg);
+  a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
+  a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);
+  a.st = st;
+  a.k = k;
+  a.t = t;
+  a.c = kLog2e / t;
+  a.cf = (float)a.c;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+void lapsum_options_init(lapsum_options *opt) {
+  if (!opt) return;
+  std::memset(opt, 0, sizeof(*opt));
+  opt->path = LAPSUM_PATH_AUTO;
+}
+
+const char *lapsum_status_string(lapsum_status st) {
+  switch (st) {
+    case LAPSUM_OK: return "ok";
+    case LAPSUM_ERR_NULL: return "a required pointer is NULL";
+    case LAPSUM_ERR_SHAPE: return "invalid shape (rows, n)";
+    case LAPSUM_ERR_K: return "k must be finite with 0 < k < n";
+    case LAPSUM_ERR_T: return "t must be finite and > 0";
+    case LAPSUM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case LAPSUM_ERR_PATH: return "the requested path cannot run this shape";
+    case LAPSUM_ERR_OPTION: return "an option is out of range";
+    case LAPSUM_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+lapsum_status lapsum_bracket_indices(int64_t n, double k, int64_t m, double delta, int64_t *lo, int64_t *hi) {
+  if (!lo || !hi) return LAPSUM_ERR_NULL;
+  if (n < 1 || n > LAPSUM_MAX_N || m < 1 || m > ((int64_t)1 << 24)) return LAPSUM_ERR_SHAPE;
+  if (!std::isfinite(k) || !(k > 0.0) || !(k < (double)n)) return LAPSUM_ERR_K;
+  if (!(delta > 0.0 && delta < 1.0)) return LAPSUM_ERR_OPTION;
+  return bracket_indices(n, k, m, delta, lo, hi);
+}
+
+lapsum_status lapsum_plan(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt,
+                          lapsum_plan_info *out) {
+  if (!out) return LAPSUM_ERR_NULL;
+  Plan P;
+  const lapsum_status st = make_plan(rows, n, k, t, opt, P);
+  if (st != LAPSUM_OK) return st;
+  std::memset(out, 0, sizeof(*out));
+  out->path = P.path;
+  out->sample_log2 = P.sample_log2;
+  out->m = P.m;
+  out->lo = P.lo;
+  out->hi = P.hi;
+  out->band_capacity = P.cap;
+  out->band_onchip = P.band_onchip ? 1 : 0;
+  out->forward_bytes = P.fwd_bytes;
+  out->backward_bytes = P.bwd_bytes;
+  return LAPSUM_OK;
+}
+
+size_t lapsum_workspace_bytes(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt) {
+  Plan P;
+  if (make_plan(rows, n, k, t, opt, P) != LAPSUM_OK) return 0;
+  return P.fwd_bytes > P.bwd_bytes ? P.fwd_bytes : P.bwd_bytes;
+}
+
+lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, double t, float *p, double *b,
+                             void *workspace, size_t workspace_bytes, const lapsum_options *opt, void *stream) {
+  Plan P;
+  const lapsum_status st0 = make_plan(rows, n, k, t, opt, P);
+  if (st0 != LAPSUM_OK) return st0;
+  if (!r || !p || !b) return LAPSUM_ERR_NULL;
+  if (P.fwd_bytes > 0) {
+    if (!workspace) return LAPSUM_ERR_NULL;
+    if (workspace_bytes < P.fwd_bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+      return LAPSUM_ERR_WORKSPACE;
+  }
+  lapsum_options o;
+  lapsum_options_init(&o);
+  if (opt) o = *opt;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const StageTimer tm{o.stage_events, s};
+  char *ws = reinterpret_cast<char *>(workspace);
+
+  if (P.path == LAPSUM_PATH_ONCHIP) {
+    tm.mark(LAPSUM_STAGE_ONCHIP_FWD, 0);
+    LAPSUM_TRY(launch_onchip_forward(r, rows, (int)n, k, t, p, b, o.stats, s));
+    tm.mark(LAPSUM_STAGE_ONCHIP_FWD, 1);
+    return LAPSUM_OK;
+  }
+
+  RowState *rs = reinterpret_cast<RowState *>(ws + P.st);
+  if (P.path == LAPSUM_PATH_FULLSORT) {
+    tm.mark(LAPSUM_STAGE_INIT, 0);
+    LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
+    tm.mark(LAPSUM_STAGE_INIT, 1);
+    tm.mark(LAPSUM_STAGE_FULLSORT, 0);
+    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFull, rows, n, r, nullptr, rs, k, t), s));
+    tm.mark(LAPSUM_STAGE_FULLSORT, 1);
+  } else {
+    const double *ovr = o.bracket_override;
+    tm.mark(LAPSUM_STAGE_INIT, 0);
+    LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, s));
+    tm.mark(LAPSUM_STAGE_INIT, 1);
+    if (!ovr) {
+      float *samples = reinterpret_cast<float *>(ws + P.samples);
+      tm.mark(LAPSUM_STAGE_SAMPLE, 0);
+      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, s));
+      tm.mark(LAPSUM_STAGE_SAMPLE, 1);
+      tm.mark(LAPSUM_STAGE_SELECT, 0);
+      LAPSUM_TRY(launch_select(samples, rows, P.m, P.lo, P.hi, rs, s));
+      tm.mark(LAPSUM_STAGE_SELECT, 1);
+    }
+    uint32_t *band = reinterpret_cast<uint32_t *>(ws + P.band);
+    tm.mark(LAPSUM_STAGE_FILTER, 0);
+    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, band, P.cap, ws + P.fpart, P.fgx, s));
+    tm.mark(LAPSUM_STAGE_FILTER, 1);
+    tm.mark(LAPSUM_STAGE_BAND, 0);
+    if (P.band_onchip)
+      LAPSUM_TRY(launch_band_onchip(band, rows, P.cap, rs, k, t, s));
+    else
+      LAPSUM_TRY(launch_segment(seg_args(P.band_seg, ws, kSegBand, rows, n, r, band, rs, k, t), s));
+    tm.mark(LAPSUM_STAGE_BAND, 1);
+    tm.mark(LAPSUM_STAGE_FULLSORT, 0);
+    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t), s));
+    tm.mark(LAPSUM_STAGE_FULLSORT, 1);
+  }
+  tm.mark(LAPSUM_STAGE_APPLY, 0);
+  LAPSUM_TRY(launch_apply(r, rows, n, rs, t, p, b, s));
+  tm.mark(LAPSUM_STAGE_APPLY, 1);
+  if (o.stats) LAPSUM_TRY(launch_copy_stats(rs, rows, o.stats, s));
+  return LAPSUM_OK;
+}
+
+lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
+                              float *dr, float *dk, void *workspace, size_t workspace_bytes,
+                              const lapsum_options *opt, void *stream) {
+  lapsum_status st0 = check_common(rows, n, t);
+  if (st0 != LAPSUM_OK) return st0;
+  if (!g || !p || !b || !dr || !dk) return LAPSUM_ERR_NULL;
+  Plan P;
+  // the backward layout depends on (rows, n) only; k = n/2 is always valid for planning
+  st0 = make_plan(rows, n, 0.5 * (double)n, t, nullptr, P);
+  if (st0 != LAPSUM_OK) return st0;
+  if (P.bwd_bytes > 0) {
+    if (!workspace) return LAPSUM_ERR_NULL;
+    if (workspace_bytes < P.bwd_bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+      return LAPSUM_ERR_WORKSPACE;
+  }
+  lapsum_options o;
+  lapsum_options_init(&o);
+  if (opt) o = *opt;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const StageTimer tm{o.stage_events, s};
+  if (onchip_backward_supported(n)) {
+    tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 0);
+    LAPSUM_TRY(launch_onchip_backward(g, p, rows, (int)n, t, dr, dk, o.stats, s));
+    tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 1);
+    return LAPSUM_OK;
+  }
+  char *ws = reinterpret_cast<char *>(workspace);
+  RowState *rs = reinterpret_cast<RowState *>(ws + P.bst);
+  LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
+  tm.mark(LAPSUM_STAGE_BWD_REDUCE, 0);
+  LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, rs, ws + P.bpart, P.bgx, dk, o.stats, s));
+  tm.mark(LAPSUM_STAGE_BWD_REDUCE, 1);
+  tm.mark(LAPSUM_STAGE_BWD_APPLY, 0);
+  LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, rs, t, dr, s));
+  tm.mark(LAPSUM_STAGE_BWD_APPLY, 1);
+  return LAPSUM_OK;
+}
+
+}  // extern "C"

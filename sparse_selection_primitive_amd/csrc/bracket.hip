@@ -1,0 +1,418 @@
+// Probabilistic bracketing ("Fast LapSum: Exact Differentiable Top-k at
+// Million Scale", section 2.2, "Probabilistic Bracketing"):
+//
+//  step 1, localisation -- sample_kernel draws m kernel-noised scores
+//    X_j = r_I + t L (I uniform with replacement, L ~ Laplace(0, 1)), whose
+//    CDF is 1 - f(x)/n, so #{X_j <= b} ~ Bin(m, 1 - k/n); select_kernel takes
+//    the binomial order statistics X_(lo), X_(hi) as the bracket [a_L, a_R);
+//  step 2, stream and filter -- filter_kernel reads every score once: below
+//    a_L it adds e^{(r - a_L)/t} to S_L, at or above a_R it adds
+//    e^{-(r - a_R)/t} to S_R, and in between it appends the key to the band
+//    (wave ballot, one atomic per wave).  Tail sums are fp64 and finalized in
+//    a fixed order by the last block.
+//
+// Random numbers: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
+// key (seed low, seed high) and counter (j, row, 0, 0): words x0, x1 give
+// I = floor((x1 2^32 + x0) n / 2^64), word x2 gives u = (x2 + 1/2)/2^32 and
+// L = F^-1(u) in fp64; X is rounded to fp32.
+#include "lapsum_device.hpp"
+#include "lapsum_internal.hpp"
+
+namespace lapsum {
+
+LDEV void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+__global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ r, int64_t n, double t, int64_t m,
+                                                     uint32_t k0, uint32_t k1, float *__restrict__ samples) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = blockIdx.y;
+  if (j >= m) return;
+  uint32_t c[4] = {(uint32_t)j, (uint32_t)row, 0u, 0u};
+  philox4x32_10(c, k0, k1);
+  const uint64_t nn = (uint64_t)n;
+  const uint64_t idx = ((uint64_t)c[1] * nn + (((uint64_t)c[0] * nn) >> 32)) >> 32;
+  const double u = ((double)c[2] + 0.5) * 0x1p-32;
+  const double lap = u < 0.5 ? log(2.0 * u) : -log(2.0 * (1.0 - u));
+  const double x = __dadd_rn((double)r[row * n + (int64_t)idx], __dmul_rn(t, lap));
+  samples[row * m + j] = (float)x;
+}
+
+hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
+                         float *samples, hipStream_t s) {
+  const int64_t gx = (m + 255) / 256;
+  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)gx, (unsigned)rows), dim3(256), 0, s, r, n, t, m,
+                     (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- order statistics
+// One workgroup of 1024 threads per row.  Exact selection of the ranks
+// lo-1 and hi-1 (0-based) among the m samples by key: a 15-bit histogram of
+// the key's top bits in LDS locates the bin of each rank; the bin's keys are
+// then gathered and ranked directly when few (<= kSelectCap), else the
+// histogram is refined on the next 15 bits, then the last 2.
+constexpr int kSelThreads = 1024;
+constexpr int kSelBins = 1 << 15;
+
+struct SelectLds {
+  uint32_t hist[kSelBins];
+  uint32_t cand[2][kSelectCap];
+  uint32_t ccount[2];
+  uint32_t wsum[kSelThreads / kWave];
+  uint32_t found_bin[2];
+  uint32_t found_rank[2];
+  uint32_t result[2];
+};
+
+LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum, uint32_t &total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) {
+    const uint32_t x = wsum[i];
+    if (i < w) before += x;
+    tot += x;
+  }
+  total = tot;
+  return before + inc - v;
+}
+
+// histogram of bits [shift, shift+nb) over keys matching (key >> pshift) == prefix
+LDEV void select_histogram(const float *X, int64_t m, int pshift, uint32_t prefix, int shift, int nb,
+                           SelectLds &L) {
+  const uint32_t nbins = 1u << nb;
+  for (uint32_t i = threadIdx.x; i < nbins; i += kSelThreads) L.hist[i] = 0u;
+  __syncthreads();
+  for (int64_t j = threadIdx.x; j < m; j += kSelThreads) {
+    const uint32_t kk = key_of(X[j]);
+    if (pshift >= 32 || (kk >> pshift) == prefix) atomicAdd(&L.hist[(kk >> shift) & (nbins - 1)], 1u);
+  }
+  __syncthreads();
+}
+
+// find the bin holding rank R (0-based) of the histogram; writes found_bin/rank[tgt]
+LDEV void select_locate(int nb, uint32_t R, int tgt, SelectLds &L) {
+  const uint32_t nbins = 1u << nb;
+  const uint32_t per = (nbins + kSelThreads - 1) / kSelThreads;
+  const uint32_t b0 = threadIdx.x * per;
+  uint32_t local = 0;
+  for (uint32_t i = 0; i < per; ++i)
+    if (b0 + i < nbins) local += L.hist[b0 + i];
+  uint32_t total;
+  const uint32_t before = block_excl_scan_u32(local, L.wsum, total);
+  if (local > 0 && before <= R && R < before + local) {
+    uint32_t acc = before;
+    for (uint32_t i = 0; i < per; ++i) {
+      const uint32_t h = L.hist[b0 + i];
+      if (R < acc + h) {
+        L.found_bin[tgt] = b0 + i;
+        L.found_rank[tgt] = R - acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ samples, int64_t m,
+                                                             int64_t lo, int64_t hi, RowState *__restrict__ st) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  SelectLds &L = *reinterpret_cast<SelectLds *>(lds_raw);
+  const int64_t row = blockIdx.x;
+  const float *X = samples + row * m;
+  const bool want[2] = {lo >= 1, hi <= m};
+  const uint32_t R0[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
+
+  // level 0: top 15 bits of every key
+  select_histogram(X, m, 32, 0u, 17, 15, L);
+  int pshift[2] = {32, 32};
+  uint32_t prefix[2] = {0u, 0u}, R[2] = {R0[0], R0[1]}, cnt[2] = {0u, 0u};
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;
+    select_locate(15, R[tg], tg, L);
+    prefix[tg] = L.found_bin[tg];
+    R[tg] = L.found_rank[tg];
+    cnt[tg] = L.hist[prefix[tg]];
+    pshift[tg] = 17;
+  }
+  __syncthreads();
+  // refinement when a bin holds too many keys for the direct ranking
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;
+    const int shifts[2] = {2, 0};
+    for (int lv = 0; lv < 2 && cnt[tg] > (uint32_t)kSelectCap && pshift[tg] > 0; ++lv) {
+      const int sh = shifts[lv];
+      const int nb = pshift[tg] - sh;
+      select_histogram(X, m, pshift[tg], prefix[tg], sh, nb, L);
+      select_locate(nb, R[tg], tg, L);
+      prefix[tg] = (prefix[tg] << nb) | L.found_bin[tg];
+      R[tg] = L.found_rank[tg];
+      cnt[tg] = L.hist[L.found_bin[tg]];
+      pshift[tg] = sh;
+      __syncthreads();
+    }
+  }
+  // gather the candidates of each target's final bin
+  if (threadIdx.x < 2) {
+    L.ccount[threadIdx.x] = 0u;
+    L.result[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  const bool gather0 = want[0] && pshift[0] > 0, gather1 = want[1] && pshift[1] > 0;
+  if (gather0 || gather1) {
+    for (int64_t j = threadIdx.x; j < m; j += kSelThreads) {
+      const uint32_t kk = key_of(X[j]);
+      if (gather0 && (kk >> pshift[0]) == prefix[0]) {
+        const uint32_t slot = atomicAdd(&L.ccount[0], 1u);
+        if (slot < (uint32_t)kSelectCap) L.cand[0][slot] = kk;
+      }
+      if (gather1 && (kk >> pshift[1]) == prefix[1]) {
+        const uint32_t slot = atomicAdd(&L.ccount[1], 1u);
+        if (slot < (uint32_t)kSelectCap) L.cand[1][slot] = kk;
+      }
+    }
+  }
+  __syncthreads();
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;
+    if (pshift[tg] == 0) {
+      if (threadIdx.x == 0) L.result[tg] = prefix[tg];
+      continue;
+    }
+    const uint32_t nc = min(L.ccount[tg], (uint32_t)kSelectCap);
+    for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
+      const uint32_t ci = L.cand[tg][i];
+      uint32_t less = 0, leq = 0;
+      for (uint32_t q = 0; q < nc; ++q) {
+        const uint32_t cq = L.cand[tg][q];
+        less += cq < ci ? 1u : 0u;
+        leq += cq <= ci ? 1u : 0u;
+      }
+      if (less <= R[tg] && R[tg] < leq) L.result[tg] = ci;  // equal keys write the same value
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st[row].a_lo = want[0] ? (double)value_of(L.result[0]) : -INFINITY;
+    st[row].a_hi = want[1] ? (double)value_of(L.result[1]) : INFINITY;
+  }
+}
+
+hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
+                         hipStream_t s) {
+  static bool attr_set = false;
+  const size_t lds = sizeof(SelectLds);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(kSelThreads), lds, s, samples, m, lo, hi, st);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- stream & filter
+struct FilterPartial {
+  double sl, sr;
+  unsigned long long cl, cr;
+};
+
+LDEV void filter_one(float x, float aL, float aR, float cf, float &fl, float &fr, uint32_t &cl, uint32_t &cr,
+                     bool &mid) {
+  const bool lo = x < aL;
+  const bool hi = x >= aR;
+  const float z = lo ? (x - aL) : (aR - x);  // <= 0 whenever it is used
+  const float w = __builtin_amdgcn_exp2f(z * cf);
+  fl += lo ? w : 0.0f;
+  fr += hi ? w : 0.0f;
+  cl += lo ? 1u : 0u;
+  cr += hi ? 1u : 0u;
+  mid = !lo && !hi;
+}
+
+LDEV uint32_t mbcnt64(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__restrict__ r, int64_t n,
+                                                                RowState *__restrict__ st,
+                                                                uint32_t *__restrict__ band, int64_t cap,
+                                                                FilterPartial *__restrict__ part, int gx, double t) {
+  __shared__ double lds_d[2 * kStreamThreads / kWave];
+  __shared__ unsigned long long lds_c[2 * kStreamThreads / kWave];
+  __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
+  __shared__ int is_last;
+  const int64_t row = blockIdx.y;
+  RowState &S = st[row];
+  const float aL = (float)S.a_lo, aR = (float)S.a_hi;
+  const float cf = (float)(kLog2e / t);
+  const float *rr = r + row * n;
+  uint32_t *bb = band + row * cap;
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  double sl = 0.0, sr = 0.0;
+  uint32_t cl = 0, cr = 0;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+
+  const bool vec = (n & 3) == 0 && (((uintptr_t)r & 15u) == 0);
+  const int64_t nitems = vec ? (n >> 2) : n;
+  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < nitems; i += stride) {
+    float x[4];
+    int nx;
+    if (vec) {
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr) + i);
+      x[0] = v.x;
+      x[1] = v.y;
+      x[2] = v.z;
+      x[3] = v.w;
+      nx = 4;
+    } else {
+      x[0] = rr[i];
+      x[1] = x[2] = x[3] = 0.0f;
+      nx = 1;
+    }
+    float fl = 0.0f, fr = 0.0f;
+    bool mid[4] = {false, false, false, false};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < nx) filter_one(x[q], aL, aR, cf, fl, fr, cl, cr, mid[q]);
+    sl += (double)fl;
+    sr += (double)fr;
+    const bool any = mid[0] || mid[1] || mid[2] || mid[3];
+    const unsigned long long wany = __ballot(any);
+    if (wany) {
+      const unsigned long long active = __ballot(1);
+      const int leader = __ffsll((long long)active) - 1;
+      unsigned long long mq[4];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mq[q] = __ballot(mid[q]);
+        tot += (uint32_t)__popcll(mq[q]);
+      }
+      unsigned long long base = 0;
+      if (lane_id() == leader) base = atomicAdd(&S.band, (unsigned long long)tot);
+      base = __shfl(base, leader, kWave);
+      unsigned long long off = base;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (mid[q]) {
+          const unsigned long long pos = off + mbcnt64(mq[q]);
+          const uint32_t kk = key_of(x[q]);
+          if (pos < (unsigned long long)cap) bb[pos] = kk;
+          kmn = min(kmn, kk);
+          kmx = max(kmx, kk);
+        }
+        off += (unsigned long long)__popcll(mq[q]);
+      }
+    }
+  }
+
+  // block reduction (fixed order)
+  unsigned long long ccl = cl, ccr = cr;
+#pragma unroll
+  for (int msk = 1; msk < kWave; msk <<= 1) {
+    sl += __shfl_xor(sl, msk, kWave);
+    sr += __shfl_xor(sr, msk, kWave);
+    ccl += __shfl_xor(ccl, msk, kWave);
+    ccr += __shfl_xor(ccr, msk, kWave);
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, msk, kWave));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, msk, kWave));
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds_d[2 * w] = sl;
+    lds_d[2 * w + 1] = sr;
+    lds_c[2 * w] = ccl;
+    lds_c[2 * w + 1] = ccr;
+    lds_k[2 * w] = kmn;
+    lds_k[2 * w + 1] = kmx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = 0.0, b = 0.0;
+    unsigned long long c0 = 0, c1 = 0;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = 0; i < kStreamThreads / kWave; ++i) {
+      a += lds_d[2 * i];
+      b += lds_d[2 * i + 1];
+      c0 += lds_c[2 * i];
+      c1 += lds_c[2 * i + 1];
+      mn = min(mn, lds_k[2 * i]);
+      mx = max(mx, lds_k[2 * i + 1]);
+    }
+    part[row * gx + blockIdx.x] = FilterPartial{a, b, c0, c1};
+    if (mn <= mx) {
+      atomicMin(&S.kmin, mn);
+      atomicMax(&S.kmax, mx);
+    }
+    __threadfence();
+    const unsigned prev = atomicAdd(&S.ticket, 1u);
+    is_last = (prev == (unsigned)gx - 1u);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const volatile FilterPartial *vp = part + row * gx;
+    double a = 0.0, b = 0.0;
+    unsigned long long c0 = 0, c1 = 0;
+    for (int i = 0; i < gx; ++i) {
+      a += vp[i].sl;
+      b += vp[i].sr;
+      c0 += vp[i].cl;
+      c1 += vp[i].cr;
+    }
+    S.tail_lo = a;
+    S.tail_hi = b;
+    S.count_lo = c0;
+    S.count_hi = c1;
+    S.ticket = 0u;
+  }
+}
+
+int filter_grid_x(int64_t rows, int64_t n) {
+  const int64_t per_row_need = (n / 4 + kStreamThreads - 1) / kStreamThreads;
+  int64_t target = 4096 / (rows > 0 ? rows : 1);
+  if (target < 1) target = 1;
+  int64_t gx = per_row_need < target ? per_row_need : target;
+  return (int)(gx < 1 ? 1 : gx);
+}
+
+size_t filter_partial_bytes(int64_t rows, int grid_x) {
+  return sizeof(FilterPartial) * (size_t)rows * (size_t)grid_x;
+}
+
+hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *band,
+                         int64_t cap, void *partials, int grid_x, hipStream_t s) {
+  hipLaunchKernelGGL(filter_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, band, cap,
+                     reinterpret_cast<FilterPartial *>(partials), grid_x, t);
+  return hipGetLastError();
+}
+
+}  // namespace lapsum

@@ -1,0 +1,514 @@
+// Device building blocks of the gfx950 Fast LapSum kernels.
+//
+// Method: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
+//   section 2.1 (eq. (1): p_i = F((r_i - b)/t), F the unit Laplace CDF;
+//   eq. (2): sum_i p_i = k fixes b), section 2.2 (full-sort solver: sort,
+//   one stable prefix/suffix scan giving the threshold curve, index lookup of
+//   the balancing interval, closed-form root; probabilistic bracketing).
+//
+// Numerics used by every solver in this library:
+//   * Sums of shifted exponentials are carried as "anchored" pairs: a fp32
+//     anchor key a and an fp64 sum s of exp(+-(x_i - a)/t) over a range whose
+//     terms are all <= 1.  Re-anchoring multiplies by exp of a key difference,
+//     computed from the two fp32 keys (never as a product of many step
+//     multipliers), so every term keeps a relative error of a few 1e-7
+//     whatever the number of elements in between.  s == 0 marks an empty
+//     range (a non-empty range always contains its anchor's term, 1).
+//   * The threshold curve is the budget at the sorted knots,
+//       g_j = f(s_j) = (P_j - 1)/2 + #{i >= j} - S_j/2,
+//     with P_j (resp. S_j) the anchored sum of everything at or below
+//     (at or above) knot j.  The root inside the located interval solves
+//       P/(2y) + c - Q y/2 = k,   y = exp((b - x)/t),
+//     for an anchor knot x, P = sum_{below} e^{(s_i-x)/t},
+//     Q = sum_{above} e^{-(s_i-x)/t} and c = #above: the positive root of
+//     Q y^2 - 2(c-k) y - P = 0, taken in log form without cancellation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LDEV __device__ __forceinline__
+
+namespace lapsum {
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ keys
+// Order-preserving map of fp32 onto uint32: the unsigned order of keys is
+// the numeric order of finite values (-0.0 sorts just below +0.0).
+LDEV uint32_t key_of(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+LDEV float value_of(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// exp(d/t) for d <= 0, with c = log2(e)/t: the product in fp64, the power of
+// two by the hardware exp2 in fp32 (results below 2^-126 flush toward 0,
+// which only drops terms far below the anchored sums' unit term).
+LDEV float wexp(double d, double c) { return __builtin_amdgcn_exp2f((float)(d * c)); }
+LDEV float wexpf(float d, float cf) { return __builtin_amdgcn_exp2f(d * cf); }
+
+// ------------------------------------------------------- anchored sums
+struct Pre {  // prefix-type: s = sum exp((x_i - a)/t) over a range ending at its anchor a
+  float a;
+  double s;
+};
+struct Suf {  // suffix-type: s = sum exp(-(x_i - a)/t) over a range starting at its anchor a
+  float a;
+  double s;
+};
+
+// left range followed by right range
+LDEV Pre join(Pre l, Pre r, double c) {
+  if (r.s == 0.0) return l;
+  if (l.s == 0.0) return r;
+  return Pre{r.a, l.s * (double)wexp((double)l.a - (double)r.a, c) + r.s};
+}
+LDEV Suf join(Suf l, Suf r, double c) {
+  if (l.s == 0.0) return r;
+  if (r.s == 0.0) return l;
+  return Suf{l.a, l.s + r.s * (double)wexp((double)l.a - (double)r.a, c)};
+}
+
+// ---------------------------------------------------- closed-form root
+// b = x + t ln y, y the positive root of Q y^2 - 2(c-k) y - P = 0, given
+// ln P and ln Q (either may be -inf for an empty side).  Logs are used
+// throughout so that sums shifted by e^{-delta/t} far below the fp32/fp64
+// range (t far below the gaps between scores) still place b correctly.
+// ln(|e| + sqrt(e^2 + PQ)) is formed relative to max(ln|e|, ln sqrt(PQ)) so
+// that neither a tiny nor a huge PQ loses digits.
+LDEV double solve_root(double x, double lnP, double lnQ, double cnt, double k, double t) {
+  const double e = cnt - k;
+  const double h = 0.5 * (lnP + lnQ);
+  const double a = e != 0.0 ? log(fabs(e)) : -INFINITY;
+  const double m = fmax(a, h);
+  double L;
+  if (m == -INFINITY) {
+    L = -INFINITY;
+  } else {
+    const double ea = exp(a - m), eh = exp(h - m);
+    L = m + log(ea + sqrt(ea * ea + eh * eh));
+  }
+  const double lny = (e >= 0.0) ? (L - lnQ) : (lnP - L);
+  return x + t * lny;
+}
+LDEV double safe_log(double v) { return v > 0.0 ? log(v) : -INFINITY; }
+
+// --------------------------------------------------------- wave shuffles
+template <int CTRL>
+LDEV uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int PATTERN>
+LDEV uint32_t swz(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, PATTERN);
+}
+// value held by lane (lane ^ MASK) of the same wave
+template <int MASK>
+LDEV uint32_t xor_lanes(uint32_t v) {
+  if constexpr (MASK == 1) return dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (MASK == 2) return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (MASK == 3) return dpp<0x1B>(v);   // quad_perm [3,2,1,0]
+  else if constexpr (MASK == 7) return dpp<0x141>(v);  // row_half_mirror
+  else if constexpr (MASK == 8) return dpp<0x128>(v);  // row_ror:8 (within 16 lanes)
+  else if constexpr (MASK == 15) return dpp<0x140>(v); // row_mirror
+  else if constexpr (MASK < 32) return swz<(MASK << 10) | 0x1F>(v);  // bit-mask swizzle
+  else return (uint32_t)__shfl_xor((int)v, MASK, kWave);
+}
+
+LDEV int lane_id() { return (int)__lane_id(); }
+
+// ------------------------------------------------------------- teams
+// A team owns one segment of sorted keys in a blocked layout: team lane l
+// holds elements [l*E, l*E + E).  A WaveTeam is LANES (<= 64) consecutive
+// lanes of one wave; a BlockTeam is the whole workgroup.
+
+template <int LANES>
+struct WaveTeam {
+  static constexpr int kLanes = LANES;
+  int lane;
+  LDEV WaveTeam() : lane(lane_id() & (LANES - 1)) {}
+
+  // dst[e] = partner's src[REV ? E-1-e : e], partner = lane ^ MASK
+  template <int MASK, bool REV, int E>
+  LDEV void exchange(const uint32_t (&src)[E], uint32_t (&dst)[E]) const {
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = xor_lanes<MASK>(src[REV ? E - 1 - e : e]);
+  }
+  LDEV int sum(int v) const {
+#pragma unroll
+    for (int m = 1; m < LANES; m <<= 1) v += __shfl_xor(v, m, LANES);
+    return v;
+  }
+  LDEV double sum(double v) const {
+#pragma unroll
+    for (int m = 1; m < LANES; m <<= 1) v += __shfl_xor(v, m, LANES);
+    return v;
+  }
+  LDEV double bcast(double v, int src) const { return __shfl(v, src, LANES); }
+  LDEV float bcast(float v, int src) const { return __shfl(v, src, LANES); }
+  LDEV void sync() const {}
+
+  LDEV Pre excl_scan(Pre x, double c) const {
+    Pre inc = x;
+#pragma unroll
+    for (int off = 1; off < LANES; off <<= 1) {
+      Pre y{__shfl_up(inc.a, off, LANES), __shfl_up(inc.s, off, LANES)};
+      if (lane >= off) inc = join(y, inc, c);
+    }
+    Pre ex{__shfl_up(inc.a, 1, LANES), __shfl_up(inc.s, 1, LANES)};
+    if (lane == 0) ex.s = 0.0;
+    return ex;
+  }
+  LDEV Suf excl_scan(Suf x, double c) const {
+    Suf inc = x;
+#pragma unroll
+    for (int off = 1; off < LANES; off <<= 1) {
+      Suf y{__shfl_down(inc.a, off, LANES), __shfl_down(inc.s, off, LANES)};
+      if (lane + off < LANES) inc = join(inc, y, c);
+    }
+    Suf ex{__shfl_down(inc.a, 1, LANES), __shfl_down(inc.s, 1, LANES)};
+    if (lane == LANES - 1) ex.s = 0.0;
+    return ex;
+  }
+};
+
+// LDS scratch of a BlockTeam: exchange buffer for cross-wave stages plus
+// small slots for scans, sums and broadcasts.
+template <int LANES, int E>
+struct BlockTeamLds {
+  uint32_t xchg[E * LANES];
+  float wa[LANES / kWave];
+  double ws[LANES / kWave];
+  int wi[LANES / kWave];
+  double bd;
+  float bf;
+};
+
+template <int LANES, int E>
+struct BlockTeam {
+  static constexpr int kLanes = LANES;
+  static constexpr int kWaves = LANES / kWave;
+  int lane;
+  BlockTeamLds<LANES, E> *lds;
+  LDEV explicit BlockTeam(BlockTeamLds<LANES, E> *l) : lane((int)threadIdx.x), lds(l) {}
+
+  template <int MASK, bool REV>
+  LDEV void exchange(const uint32_t (&src)[E], uint32_t (&dst)[E]) const {
+    if constexpr (MASK < kWave) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = xor_lanes<MASK>(src[REV ? E - 1 - e : e]);
+    } else {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) lds->xchg[e * LANES + lane] = src[e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = lds->xchg[(REV ? E - 1 - e : e) * LANES + (lane ^ MASK)];
+    }
+  }
+  LDEV int sum(int v) const {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+    __syncthreads();
+    if ((lane & (kWave - 1)) == 0) lds->wi[lane / kWave] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += lds->wi[w];
+    return t;
+  }
+  LDEV double sum(double v) const {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+    __syncthreads();
+    if ((lane & (kWave - 1)) == 0) lds->ws[lane / kWave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += lds->ws[w];
+    return t;
+  }
+  LDEV double bcast(double v, int src) const {
+    __syncthreads();
+    if (lane == src) lds->bd = v;
+    __syncthreads();
+    return lds->bd;
+  }
+  LDEV float bcast(float v, int src) const {
+    __syncthreads();
+    if (lane == src) lds->bf = v;
+    __syncthreads();
+    return lds->bf;
+  }
+  LDEV void sync() const { __syncthreads(); }
+
+  LDEV Pre excl_scan(Pre x, double c) const {
+    const int wl = lane & (kWave - 1), w = lane / kWave;
+    Pre inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      Pre y{__shfl_up(inc.a, off, kWave), __shfl_up(inc.s, off, kWave)};
+      if (wl >= off) inc = join(y, inc, c);
+    }
+    __syncthreads();
+    if (wl == kWave - 1) {
+      lds->wa[w] = inc.a;
+      lds->ws[w] = inc.s;
+    }
+    __syncthreads();
+    Pre wp{0.0f, 0.0};
+    for (int i = 0; i < w; ++i) wp = join(wp, Pre{lds->wa[i], lds->ws[i]}, c);
+    Pre ex{__shfl_up(inc.a, 1, kWave), __shfl_up(inc.s, 1, kWave)};
+    if (wl == 0) ex.s = 0.0;
+    return join(wp, ex, c);
+  }
+  LDEV Suf excl_scan(Suf x, double c) const {
+    const int wl = lane & (kWave - 1), w = lane / kWave;
+    Suf inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      Suf y{__shfl_down(inc.a, off, kWave), __shfl_down(inc.s, off, kWave)};
+      if (wl + off < kWave) inc = join(inc, y, c);
+    }
+    __syncthreads();
+    if (wl == 0) {
+      lds->wa[w] = inc.a;
+      lds->ws[w] = inc.s;
+    }
+    __syncthreads();
+    Suf ws{0.0f, 0.0};
+    for (int i = kWaves - 1; i > w; --i) ws = join(Suf{lds->wa[i], lds->ws[i]}, ws, c);
+    Suf ex{__shfl_down(inc.a, 1, kWave), __shfl_down(inc.s, 1, kWave)};
+    if (wl == kWave - 1) ex.s = 0.0;
+    return join(ex, ws, c);
+  }
+};
+
+// ------------------------------------------------------- bitonic sort
+// Ascending sort of E*LANES keys held blocked across a team.  Network: for
+// each merge size 2^s, one stage pairing i with i ^ (2^s - 1) (the mirror
+// of its block), then stages pairing i with i ^ d for d = 2^(s-2) .. 1; the
+// lower index keeps the minimum.  Stages with d < E stay in registers;
+// larger ones exchange with lane (lane ^ mask) of the team.
+template <int D, bool MIRROR, int E, class Team>
+LDEV void bitonic_stage(uint32_t (&key)[E], const Team &team) {
+  if constexpr (D < E) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if ((i & D) == 0) {
+        const int j = MIRROR ? (i ^ (2 * D - 1)) : (i ^ D);
+        const uint32_t x = key[i], y = key[j];
+        key[i] = min(x, y);
+        key[j] = max(x, y);
+      }
+    }
+  } else {
+    constexpr int LM = D / E;
+    constexpr int MASK = MIRROR ? (2 * LM - 1) : LM;
+    uint32_t recv[E];
+    team.template exchange<MASK, MIRROR>(key, recv);
+    const bool lower = (team.lane & LM) == 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = lower ? min(key[e], recv[e]) : max(key[e], recv[e]);
+  }
+}
+
+template <int D, int E, class Team>
+LDEV void bitonic_cleaners(uint32_t (&key)[E], const Team &team) {
+  if constexpr (D >= 1) {
+    bitonic_stage<D, false>(key, team);
+    bitonic_cleaners<D / 2>(key, team);
+  }
+}
+
+template <int S, int LOGN, int E, class Team>
+LDEV void bitonic_merges(uint32_t (&key)[E], const Team &team) {
+  if constexpr (S <= LOGN) {
+    constexpr int HALF = 1 << (S - 1);
+    bitonic_stage<HALF, true>(key, team);
+    bitonic_cleaners<HALF / 2>(key, team);
+    bitonic_merges<S + 1, LOGN>(key, team);
+  }
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+template <int E, class Team>
+LDEV void bitonic_sort(uint32_t (&key)[E], const Team &team) {
+  constexpr int NP = E * Team::kLanes;
+  bitonic_merges<1, ilog2(NP)>(key, team);
+}
+
+// ----------------------------------------------------- segment solve
+// Inputs describing one part of a sorted segment held by a team:
+struct PartInfo {
+  int nvalid;        // valid sorted keys in this part (a prefix of the team's blocked range)
+  double above;      // #elements of the whole problem at or after this part's first element
+  Pre seed_lo;       // everything before the part (left tail, earlier tiles)
+  Suf seed_hi;       // everything after the part (later tiles, right tail)
+  bool first;        // the part starts the segment: nothing but seed_lo lies below it
+  bool last;         // the part ends the segment: nothing but seed_hi lies above it
+};
+
+// Threshold curve + locate + closed-form root over one team part
+// (section 2.2, full-sort solver).  s[] are the part's sorted values,
+// blocked (lane l holds indices l*E..l*E+E-1), nv of them valid in this
+// lane.  Returns b on every team lane.
+template <int E, class Team>
+LDEV double segment_solve(const float (&s)[E], int nv, const PartInfo &part, double k, double t, double c,
+                          float cf, const Team &team) {
+  // step multipliers between consecutive knots of this lane
+  float mul[E];
+  mul[0] = 0.0f;
+#pragma unroll
+  for (int e = 1; e < E; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], cf) : 0.0f;
+
+  // lane aggregates
+  double pl = 0.0, sl = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv) pl = pl * (double)mul[e] + 1.0;
+#pragma unroll
+  for (int e = E - 1; e >= 0; --e)
+    if (e < nv) sl = (e + 1 < E ? sl * (double)mul[e + 1] : 0.0) + 1.0;
+  float last_s = s[0];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv) last_s = s[e];
+  const Pre mine_p{last_s, nv > 0 ? pl : 0.0};
+  const Suf mine_s{s[0], nv > 0 ? sl : 0.0};
+
+  const Pre pin = join(part.seed_lo, team.excl_scan(mine_p, c), c);
+  const Suf sin = join(team.excl_scan(mine_s, c), part.seed_hi, c);
+
+  // full P_j for this lane's knots
+  double P[E];
+  double acc = (pin.s == 0.0) ? 0.0 : pin.s * (double)wexp((double)pin.a - (double)s[0], c);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < nv) acc = (e == 0 ? acc : acc * (double)mul[e]) + 1.0;
+    P[e] = acc;
+  }
+  const double s_after = (sin.s == 0.0) ? 0.0 : sin.s * (double)wexp((double)last_s - (double)sin.a, c);
+
+  // threshold curve and the count of knots with g_j >= k
+  const int base = team.lane * E;
+  int cnt = 0;
+  {
+    double S = 0.0;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) {
+      if (e < nv) {
+        S = (e == nv - 1) ? s_after + 1.0 : S * (double)mul[e + 1 < E ? e + 1 : 0] + 1.0;
+        const double g = 0.5 * (P[e] - 1.0) + (part.above - (double)(base + e)) - 0.5 * S;
+        cnt += (g >= k) ? 1 : 0;
+      }
+    }
+  }
+  const int Mp = team.sum(nv);
+  const int jstar = team.sum(cnt) - 1;  // -1 .. Mp-1, part-local
+
+  // the lane holding the first knot above b (or the last knot) solves
+  const bool right_end = (jstar + 1 >= Mp);
+  const int owner = Mp == 0 ? 0 : (right_end ? (Mp - 1) / E : (jstar + 1) / E);
+  double b = 0.0;
+  if (team.lane == owner) {
+    // anchor knot x, ln of the sums below (lP) and above (lQ) relative to x
+    const double it = 1.0 / t;
+    double x, lP, lQ, cabove, lo = -INFINITY, hi = INFINITY;
+    if (Mp == 0) {
+      if (pin.s != 0.0) {
+        x = pin.a;
+        lP = log(pin.s);
+        lQ = sin.s == 0.0 ? -INFINITY : log(sin.s) + (x - (double)sin.a) * it;
+      } else {
+        x = sin.a;
+        lP = -INFINITY;
+        lQ = safe_log(sin.s);
+      }
+      cabove = part.above;
+    } else if (!right_end) {
+      const int e1 = jstar + 1 - base;  // first knot above b, in this lane
+      double S1 = 1.0, S = 0.0;
+      float s1 = s[0];
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e) {
+        if (e < nv) {
+          S = (e == nv - 1) ? s_after + 1.0 : S * (double)mul[e + 1 < E ? e + 1 : 0] + 1.0;
+          if (e == e1) {
+            S1 = S;
+            s1 = s[e];
+          }
+        }
+      }
+      if (e1 > 0) {
+        x = s[0];
+        double Pv = P[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e)
+          if (e == e1 - 1) {
+            x = s[e];
+            Pv = P[e];
+          }
+        lo = x;
+        lP = log(Pv);
+        lQ = log(S1) + (x - (double)s1) * it;
+        cabove = part.above - (double)(jstar + 1);
+      } else if (!(part.first && owner == 0)) {
+        x = pin.a;  // previous knot: last of the previous lane or tile
+        lP = log(pin.s);
+        lo = x;
+        lQ = log(S1) + (x - (double)s1) * it;
+        cabove = part.above - (double)(jstar + 1);
+      } else {
+        // b below every knot of the segment
+        x = s1;
+        lP = pin.s == 0.0 ? -INFINITY : log(pin.s) + ((double)pin.a - x) * it;
+        lQ = log(S1);
+        cabove = part.above;
+      }
+      hi = s1;
+    } else {
+      const int e0 = Mp - 1 - base;
+      x = s[0];
+      double Pv = P[0];
+#pragma unroll
+      for (int e = 1; e < E; ++e)
+        if (e == e0) {
+          x = s[e];
+          Pv = P[e];
+        }
+      lP = log(Pv);
+      lQ = sin.s == 0.0 ? -INFINITY : log(sin.s) + (x - (double)sin.a) * it;
+      cabove = part.above - (double)Mp;
+      lo = x;
+      hi = (part.last || sin.s == 0.0) ? INFINITY : (double)sin.a;
+    }
+    b = solve_root(x, lP, lQ, cabove, k, t);
+    b = fmin(fmax(b, lo), hi);
+  }
+  return team.bcast(b, owner);
+}
+
+// ----------------------------------------------------------- row state
+// Per-row state of the bracketing and full-sort pipelines (workspace).
+struct RowState {
+  double a_lo, a_hi;        // bracket
+  double tail_lo, tail_hi;  // S_L, S_R
+  unsigned long long count_lo, count_hi;
+  unsigned long long band;  // M: atomic append counter
+  double b;                 // threshold from the band solve or the fallback
+  uint32_t kmin, kmax;      // key range of the band
+  int32_t flags;
+  uint32_t ticket;          // last-block-done counter (filter / backward)
+  double dk;                // backward: dk in fp64
+  uint32_t ticket2;
+  int32_t pad;
+};
+
+}  // namespace lapsum

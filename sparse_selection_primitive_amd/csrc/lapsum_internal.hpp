@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI host runtime (api.cpp) and the HIP
+// kernel files.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lapsum.h"
+
+namespace lapsum {
+
+struct RowState;
+struct TileAgg;
+struct Pre;
+struct Suf;
+
+constexpr int kTile = 4096;          // keys per tile of the large-row sort and scan
+constexpr int kSegThreads = 256;     // threads per workgroup of the large-row kernels
+constexpr int kSelectCap = 1024;     // direct-selection capacity of the bracket select
+constexpr int kStreamThreads = 256;  // threads per workgroup of the streaming kernels
+
+// Arguments of the cooperative large-row sort + threshold-curve + root kernel.
+struct SegArgs {
+  int mode;             // kSegFull, kSegBand or kSegFallback
+  int rows;
+  int64_t n;            // row length (full rows / fallback)
+  const float *r;       // [rows][n] scores (full rows / fallback)
+  const uint32_t *band; // [rows][stride] raw band keys (band mode)
+  uint32_t *A, *B;      // [rows][stride] key ping-pong buffers
+  int64_t stride;       // per-row stride of band/A/B, a multiple of kTile
+  int max_tiles;        // stride / kTile
+  uint32_t *hist;       // [rows][256][max_tiles] tile digit counts -> offsets
+  uint32_t *dtot;       // [rows][256] digit totals
+  TileAgg *tagg;        // [rows][max_tiles] tile aggregates
+  Pre *tpre;            // [rows][max_tiles] prefix before each tile
+  Suf *tsuf;            // [rows][max_tiles] suffix after each tile
+  RowState *st;         // [rows]
+  double k, t, c;       // c = log2(e)/t
+  float cf;
+};
+enum { kSegFull = 0, kSegBand = 1, kSegFallback = 2 };
+
+// Launchers (each returns the first HIP error, or hipSuccess).
+hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2,
+                            hipStream_t s);
+hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
+                                 lapsum_row_stats *stats, hipStream_t s);
+hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, float *dr,
+                                  float *dk, lapsum_row_stats *stats, hipStream_t s);
+bool onchip_backward_supported(int64_t n);
+hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
+                         float *samples, hipStream_t s);
+hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
+                         hipStream_t s);
+hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *band,
+                         int64_t cap, void *partials, int grid_x, hipStream_t s);
+int filter_grid_x(int64_t rows, int64_t n);
+size_t filter_partial_bytes(int64_t rows, int grid_x);
+hipError_t launch_band_onchip(const uint32_t *band, int64_t rows, int64_t cap, RowState *st, double k, double t,
+                              hipStream_t s);
+hipError_t launch_segment(const SegArgs &a, hipStream_t s);
+hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
+                        double *b, hipStream_t s);
+hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st,
+                             void *partials, int grid_x, float *dk, lapsum_row_stats *stats, hipStream_t s);
+hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const RowState *st,
+                            double t, float *dr, hipStream_t s);
+int bwd_grid_x(int64_t rows, int64_t n);
+size_t bwd_partial_bytes(int64_t rows, int grid_x);
+hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats *stats, hipStream_t s);
+
+size_t row_state_bytes();
+size_t tile_agg_bytes();
+size_t pre_bytes();
+size_t suf_bytes();
+
+}  // namespace lapsum

@@ -1,0 +1,285 @@
+// On-chip (register + LDS) kernels for rows of up to 8192 scores.
+//
+// Forward ("Fast LapSum: Exact Differentiable Top-k at Million Scale",
+// section 2.2, full-sort solver; section 2.1, eq. (1) for the apply): one
+// team of lanes owns one row.  The row is read once from HBM, sorted by a
+// bitonic network in registers (cross-lane stages by DPP / swizzle within a
+// wave, through LDS across waves), scanned into the threshold curve,
+// located, solved in closed form, and p is written from the original
+// values still held in registers.  The only HBM traffic is r in, p and b out.
+//
+// Backward (section 2.1, analytic VJP): one team per row reads g and p once,
+// forms D = sum d and G = sum g d in fp64, and writes dr = d (g - G/D).
+//
+// Band solve (section 2.2, probabilistic bracketing, step 3): the same
+// sort + curve + root on the compacted middle band, seeded with the tail
+// sums of the streaming pass, followed by the certification of step 4.
+#include "lapsum_device.hpp"
+#include "lapsum_internal.hpp"
+
+namespace lapsum {
+
+LDEV bool aligned16(const void *q) { return ((uintptr_t)q & 15u) == 0; }
+
+// p = F((x - b)/t); z2 = (x - b) log2(e)/t formed from an fp64 difference.
+LDEV float laplace_cdf_at(float x, double b, double c) {
+  const float z2 = (float)(((double)x - b) * c);
+  return z2 < 0.0f ? 0.5f * __builtin_amdgcn_exp2f(z2) : 1.0f - 0.5f * __builtin_amdgcn_exp2f(-z2);
+}
+
+template <int E>
+LDEV void load_row(const float *rr, int n, int base, bool ok, bool vec, float (&v)[E]) {
+  if (vec && (E % 4) == 0) {
+#pragma unroll
+    for (int q = 0; q < E; q += 4) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok && base + q < n) x = *reinterpret_cast<const float4 *>(rr + base + q);
+      v[q] = x.x;
+      v[q + 1] = x.y;
+      v[q + 2] = x.z;
+      v[q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = (ok && base + e < n) ? rr[base + e] : 0.0f;
+  }
+}
+
+template <int E>
+LDEV void store_row(float *pp, int n, int base, bool ok, bool vec, const float (&v)[E]) {
+  if (!ok) return;
+  if (vec && (E % 4) == 0) {
+#pragma unroll
+    for (int q = 0; q < E; q += 4)
+      if (base + q < n) *reinterpret_cast<float4 *>(pp + base + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (base + e < n) pp[base + e] = v[e];
+  }
+}
+
+// Whole forward of one row held by a team.
+template <int E, class Team>
+LDEV void onchip_row_forward(const Team &team, const float *rr, int n, bool ok, double k, double t, float *pp,
+                             double *bout, lapsum_row_stats *stats) {
+  const bool vec = (n & 3) == 0 && aligned16(rr) && aligned16(pp);
+  const int base = team.lane * E;
+  float v[E];
+  load_row<E>(rr, n, base, ok, vec, v);
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (ok && base + e < n) ? key_of(v[e]) : 0xFFFFFFFFu;
+
+  bitonic_sort<E>(key, team);
+
+  const int nv = ok ? min(max(n - base, 0), E) : 0;
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+
+  const double c = kLog2e / t;
+  const float cf = (float)c;
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)n;
+  part.seed_lo = Pre{0.0f, 0.0};
+  part.seed_hi = Suf{0.0f, 0.0};
+  part.first = true;
+  part.last = true;
+  const double b = segment_solve<E>(s, nv, part, k, t, c, cf, team);
+
+  float out[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = laplace_cdf_at(v[e], b, c);
+  store_row<E>(pp, n, base, ok, vec, out);
+  if (ok && team.lane == 0) {
+    *bout = b;
+    if (stats) {
+      stats->a_lo = -INFINITY;
+      stats->a_hi = INFINITY;
+      stats->tail_lo = 0.0;
+      stats->tail_hi = 0.0;
+      stats->count_lo = 0;
+      stats->count_hi = 0;
+      stats->band = n;
+      stats->flags = 0;
+      stats->reserved = 0;
+    }
+  }
+}
+
+// Teams inside one wave: NP = LANES * E <= 1024, 256 threads = 256/LANES rows.
+template <int NP, int LANES>
+__global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restrict__ r, int64_t rows, int n,
+                                                           double k, double t, float *__restrict__ p,
+                                                           double *__restrict__ b, lapsum_row_stats *stats) {
+  constexpr int E = NP / LANES;
+  WaveTeam<LANES> team;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  const bool ok = row < rows;
+  const int64_t rr = ok ? row : 0;
+  onchip_row_forward<E>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr);
+}
+
+// One row per workgroup: NP = 16 * LANES, LANES threads.
+template <int NP>
+__global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int64_t rows, int n,
+                                                                double k, double t, float *__restrict__ p,
+                                                                double *__restrict__ b, lapsum_row_stats *stats) {
+  constexpr int E = 16, LANES = NP / 16;
+  __shared__ BlockTeamLds<LANES, E> lds;
+  BlockTeam<LANES, E> team(&lds);
+  const int64_t row = blockIdx.x;
+  onchip_row_forward<E>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr);
+}
+
+template <int NP, int LANES>
+static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
+                                  lapsum_row_stats *stats, hipStream_t s) {
+  constexpr int RPB = 256 / LANES;
+  const int64_t grid = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((onchip_forward_wave<NP, LANES>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n, k, t, p,
+                     b, stats);
+  return hipGetLastError();
+}
+
+template <int NP>
+static hipError_t launch_fwd_block(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
+                                   lapsum_row_stats *stats, hipStream_t s) {
+  hipLaunchKernelGGL((onchip_forward_block<NP>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, rows, n, k, t, p, b,
+                     stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
+                                 lapsum_row_stats *stats, hipStream_t s) {
+  if (n <= 64) return launch_fwd_wave<64, 16>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 128) return launch_fwd_wave<128, 16>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 256) return launch_fwd_wave<256, 16>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 512) return launch_fwd_wave<512, 32>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 1024) return launch_fwd_wave<1024, 64>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 2048) return launch_fwd_block<2048>(r, rows, n, k, t, p, b, stats, s);
+  if (n <= 4096) return launch_fwd_block<4096>(r, rows, n, k, t, p, b, stats, s);
+  return launch_fwd_block<8192>(r, rows, n, k, t, p, b, stats, s);
+}
+
+// ------------------------------------------------------------ backward
+template <int NP, int LANES>
+__global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restrict__ g, const float *__restrict__ p,
+                                                            int64_t rows, int n, double t, float *__restrict__ dr,
+                                                            float *__restrict__ dk, lapsum_row_stats *stats) {
+  constexpr int E = NP / LANES;
+  WaveTeam<LANES> team;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  const bool ok = row < rows;
+  const int64_t rr = ok ? row : 0;
+  const bool vec = (n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr);
+  const int base = team.lane * E;
+  float gv[E], pv[E];
+  load_row<E>(g + rr * n, n, base, ok, vec, gv);
+  load_row<E>(p + rr * n, n, base, ok, vec, pv);
+  double D = 0.0, G = 0.0;
+  float q[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    // min(p, 1 - p) is the Laplace density at the score (times t)
+    q[e] = (ok && base + e < n) ? fminf(pv[e], 1.0f - pv[e]) : 0.0f;
+    D += (double)q[e];
+    G += (double)gv[e] * (double)q[e];
+  }
+  D = team.sum(D);
+  G = team.sum(G);
+  const double dkd = D > 0.0 ? G / D : 0.0;
+  const float dkf = (float)dkd;
+  const float inv_t = (float)(1.0 / t);
+  float out[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (gv[e] - dkf) : 0.0f;
+  store_row<E>(dr + rr * n, n, base, ok, vec, out);
+  if (ok && team.lane == 0) {
+    dk[rr] = dkf;
+    if (stats && !(D > 0.0)) atomicOr(&stats[rr].flags, LAPSUM_FLAG_DEGENERATE);
+  }
+}
+
+bool onchip_backward_supported(int64_t n) { return n >= 1 && n <= 1024; }
+
+template <int NP, int LANES>
+static hipError_t launch_bwd_wave(const float *g, const float *p, int64_t rows, int n, double t, float *dr, float *dk,
+                                  lapsum_row_stats *stats, hipStream_t s) {
+  constexpr int RPB = 256 / LANES;
+  const int64_t grid = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((onchip_backward_wave<NP, LANES>), dim3((unsigned)grid), dim3(256), 0, s, g, p, rows, n, t, dr,
+                     dk, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, float *dr,
+                                  float *dk, lapsum_row_stats *stats, hipStream_t s) {
+  if (n <= 64) return launch_bwd_wave<64, 16>(g, p, rows, n, t, dr, dk, stats, s);
+  if (n <= 128) return launch_bwd_wave<128, 16>(g, p, rows, n, t, dr, dk, stats, s);
+  if (n <= 256) return launch_bwd_wave<256, 16>(g, p, rows, n, t, dr, dk, stats, s);
+  if (n <= 512) return launch_bwd_wave<512, 32>(g, p, rows, n, t, dr, dk, stats, s);
+  return launch_bwd_wave<1024, 64>(g, p, rows, n, t, dr, dk, stats, s);
+}
+
+// ----------------------------------------------------------- band solve
+// One workgroup per row; the band (capacity <= NP) is read from the
+// workspace, sorted, and solved with the tail sums as boundary seeds.  The
+// result is certified: the root must lie inside [a_L, a_R).
+template <int NP>
+__global__ __launch_bounds__(NP / 16) void band_solve_onchip(const uint32_t *__restrict__ band, int64_t cap,
+                                                             RowState *__restrict__ st, double k, double t) {
+  constexpr int E = 16, LANES = NP / 16;
+  __shared__ BlockTeamLds<LANES, E> lds;
+  BlockTeam<LANES, E> team(&lds);
+  const int64_t row = blockIdx.x;
+  RowState &S = st[row];
+  const unsigned long long M = S.band;
+  if (M > (unsigned long long)cap) {
+    if (threadIdx.x == 0) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
+    return;
+  }
+  const int m = (int)M;
+  const int base = team.lane * E;
+  uint32_t key[E];
+  const uint32_t *src = band + row * cap;
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (base + e < m) ? src[base + e] : 0xFFFFFFFFu;
+  bitonic_sort<E>(key, team);
+  const int nv = min(max(m - base, 0), E);
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+
+  const double c = kLog2e / t;
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)m + (double)S.count_hi;
+  part.seed_lo = Pre{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
+  part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
+  part.first = true;
+  part.last = true;
+  const double b = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
+  if (threadIdx.x == 0) {
+    S.b = b;
+    const bool hit = (b >= S.a_lo) && (b < S.a_hi);
+    S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+  }
+}
+
+hipError_t launch_band_onchip(const uint32_t *band, int64_t rows, int64_t cap, RowState *st, double k, double t,
+                              hipStream_t s) {
+  if (cap <= 1024)
+    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(64), 0, s, band, cap, st, k, t);
+  else if (cap <= 2048)
+    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(128), 0, s, band, cap, st, k, t);
+  else if (cap <= 4096)
+    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(256), 0, s, band, cap, st, k, t);
+  else
+    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(512), 0, s, band, cap, st, k, t);
+  return hipGetLastError();
+}
+
+}  // namespace lapsum

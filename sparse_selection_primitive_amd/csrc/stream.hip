@@ -1,0 +1,270 @@
+// Streaming (HBM-bound) kernels for large rows.
+//
+//  * apply: p_i = F((r_i - b)/t) ("Fast LapSum: Exact Differentiable Top-k at
+//    Million Scale", section 2.1, eq. (1)), 4 B read + 4 B written per score;
+//  * backward, section 2.1 (analytic VJP): pass 1 reads g and p (8 B/score)
+//    and forms D = sum d, G = sum g d in fp64 with a deterministic
+//    last-block finalize giving dk = G/D; pass 2 reads g and p again and
+//    writes dr = d (g - dk) (12 B/score), d = min(p, 1 - p)/t.
+//
+// Loads and stores are 16 B per lane and non-temporal: every byte is used
+// once, so nothing is worth keeping in the caches.  Grids are 2-D
+// (blocks per row x rows) with grid-stride loops inside a row.
+#include "lapsum_device.hpp"
+#include "lapsum_internal.hpp"
+
+namespace lapsum {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+LDEV bool aligned16(const void *q) { return ((uintptr_t)q & 15u) == 0; }
+
+LDEV float cdf_at(float x, double b, double c) {
+  const float z2 = (float)(((double)x - b) * c);
+  return z2 < 0.0f ? 0.5f * __builtin_amdgcn_exp2f(z2) : 1.0f - 0.5f * __builtin_amdgcn_exp2f(-z2);
+}
+
+// ----------------------------------------------------------- row state
+__global__ void init_rows_kernel(RowState *st, int64_t rows, int32_t flags, int has_override, double o_lo,
+                                 double o_hi) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  RowState z;
+  z.a_lo = has_override ? o_lo : -INFINITY;
+  z.a_hi = has_override ? o_hi : INFINITY;
+  z.tail_lo = 0.0;
+  z.tail_hi = 0.0;
+  z.count_lo = 0;
+  z.count_hi = 0;
+  z.band = 0;
+  z.b = 0.0;
+  z.kmin = 0xFFFFFFFFu;
+  z.kmax = 0u;
+  z.flags = flags;
+  z.ticket = 0u;
+  z.dk = 0.0;
+  z.ticket2 = 0u;
+  z.pad = 0;
+  st[row] = z;
+}
+
+hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, hipStream_t s) {
+  const int64_t grid = (rows + 255) / 256;
+  hipLaunchKernelGGL(init_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, st, rows, flags,
+                     override2 ? 1 : 0, override2 ? override2[0] : 0.0, override2 ? override2[1] : 0.0);
+  return hipGetLastError();
+}
+
+__global__ void copy_stats_kernel(const RowState *st, int64_t rows, lapsum_row_stats *out) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const RowState &s = st[row];
+  lapsum_row_stats o;
+  o.a_lo = s.a_lo;
+  o.a_hi = s.a_hi;
+  o.tail_lo = s.tail_lo;
+  o.tail_hi = s.tail_hi;
+  o.count_lo = (int64_t)s.count_lo;
+  o.count_hi = (int64_t)s.count_hi;
+  o.band = (int64_t)s.band;
+  o.flags = s.flags;
+  o.reserved = 0;
+  out[row] = o;
+}
+
+hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats *stats, hipStream_t s) {
+  const int64_t grid = (rows + 255) / 256;
+  hipLaunchKernelGGL(copy_stats_kernel, dim3((unsigned)grid), dim3(256), 0, s, st, rows, stats);
+  return hipGetLastError();
+}
+
+size_t row_state_bytes() { return sizeof(RowState); }
+
+// ---------------------------------------------------------------- apply
+__global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__restrict__ r, int64_t n,
+                                                               const RowState *__restrict__ st, double t,
+                                                               float *__restrict__ p, double *__restrict__ bout) {
+  const int64_t row = blockIdx.y;
+  const double b = st[row].b;
+  const double c = kLog2e / t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) bout[row] = b;
+  const float *rr = r + row * n;
+  float *pp = p + row * n;
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  if ((n & 3) == 0 && aligned16(r) && aligned16(p)) {
+    const int64_t n4 = n >> 2;
+    const f4 *r4 = reinterpret_cast<const f4 *>(rr);
+    f4 *p4 = reinterpret_cast<f4 *>(pp);
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
+      const f4 x = __builtin_nontemporal_load(r4 + i);
+      f4 y;
+      y.x = cdf_at(x.x, b, c);
+      y.y = cdf_at(x.y, b, c);
+      y.z = cdf_at(x.z, b, c);
+      y.w = cdf_at(x.w, b, c);
+      __builtin_nontemporal_store(y, p4 + i);
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
+      pp[i] = cdf_at(rr[i], b, c);
+  }
+}
+
+static int stream_grid_x(int64_t rows, int64_t n) {
+  const int64_t per_row_need = (n / 4 + kStreamThreads - 1) / kStreamThreads;
+  int64_t target = 4096 / (rows > 0 ? rows : 1);
+  if (target < 1) target = 1;
+  int64_t gx = per_row_need < target ? per_row_need : target;
+  if (gx < 1) gx = 1;
+  return (int)gx;
+}
+
+hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p, double *b,
+                        hipStream_t s) {
+  const int gx = stream_grid_x(rows, n);
+  hipLaunchKernelGGL(apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, t, p, b);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ backward
+struct BwdPartial {
+  double D, G;
+};
+
+template <int NT>
+LDEV void block_sum2(double &a, double &b, double *lds) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    a += __shfl_xor(a, m, kWave);
+    b += __shfl_xor(b, m, kWave);
+  }
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds[2 * w] = a;
+    lds[2 * w + 1] = b;
+  }
+  __syncthreads();
+  a = 0.0;
+  b = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    a += lds[2 * i];
+    b += lds[2 * i + 1];
+  }
+}
+
+__global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float *__restrict__ g,
+                                                                    const float *__restrict__ p, int64_t n,
+                                                                    RowState *__restrict__ st,
+                                                                    BwdPartial *__restrict__ part, int gx,
+                                                                    float *__restrict__ dk,
+                                                                    lapsum_row_stats *stats) {
+  __shared__ double lds[2 * kStreamThreads / kWave];
+  __shared__ int is_last;
+  const int64_t row = blockIdx.y;
+  const float *gg = g + row * n;
+  const float *pp = p + row * n;
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  double D = 0.0, G = 0.0;
+  if ((n & 3) == 0 && aligned16(g) && aligned16(p)) {
+    const int64_t n4 = n >> 2;
+    const f4 *g4 = reinterpret_cast<const f4 *>(gg);
+    const f4 *p4 = reinterpret_cast<const f4 *>(pp);
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
+      const f4 pv = __builtin_nontemporal_load(p4 + i);
+      const f4 gv = __builtin_nontemporal_load(g4 + i);
+      const float q0 = fminf(pv.x, 1.0f - pv.x), q1 = fminf(pv.y, 1.0f - pv.y);
+      const float q2 = fminf(pv.z, 1.0f - pv.z), q3 = fminf(pv.w, 1.0f - pv.w);
+      D += (double)((q0 + q1) + (q2 + q3));
+      G += (double)((gv.x * q0 + gv.y * q1) + (gv.z * q2 + gv.w * q3));
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride) {
+      const float q = fminf(pp[i], 1.0f - pp[i]);
+      D += (double)q;
+      G += (double)gg[i] * (double)q;
+    }
+  }
+  block_sum2<kStreamThreads>(D, G, lds);
+  if (threadIdx.x == 0) {
+    part[row * gx + blockIdx.x] = BwdPartial{D, G};
+    __threadfence();
+    const unsigned prev = atomicAdd(&st[row].ticket, 1u);
+    is_last = (prev == (unsigned)gx - 1u);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  // deterministic finalize: fixed assignment of partials to threads, fixed tree
+  double Ds = 0.0, Gs = 0.0;
+  const volatile BwdPartial *vp = part + row * gx;
+  for (int i = threadIdx.x; i < gx; i += kStreamThreads) {
+    Ds += vp[i].D;
+    Gs += vp[i].G;
+  }
+  block_sum2<kStreamThreads>(Ds, Gs, lds);
+  if (threadIdx.x == 0) {
+    const double dkd = Ds > 0.0 ? Gs / Ds : 0.0;
+    st[row].dk = dkd;
+    dk[row] = (float)dkd;
+    if (!(Ds > 0.0)) {
+      st[row].flags |= LAPSUM_FLAG_DEGENERATE;
+      if (stats) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
+    }
+    st[row].ticket = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *__restrict__ g,
+                                                                   const float *__restrict__ p, int64_t n,
+                                                                   const RowState *__restrict__ st, double t,
+                                                                   float *__restrict__ dr) {
+  const int64_t row = blockIdx.y;
+  const double dkd = st[row].dk;
+  const bool degenerate = (st[row].flags & LAPSUM_FLAG_DEGENERATE) != 0;
+  const float dkf = (float)dkd;
+  const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
+  const float *gg = g + row * n;
+  const float *pp = p + row * n;
+  float *dd = dr + row * n;
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  if ((n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr)) {
+    const int64_t n4 = n >> 2;
+    const f4 *g4 = reinterpret_cast<const f4 *>(gg);
+    const f4 *p4 = reinterpret_cast<const f4 *>(pp);
+    f4 *d4 = reinterpret_cast<f4 *>(dd);
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
+      const f4 pv = __builtin_nontemporal_load(p4 + i);
+      const f4 gv = __builtin_nontemporal_load(g4 + i);
+      f4 o;
+      o.x = fminf(pv.x, 1.0f - pv.x) * inv_t * (gv.x - dkf);
+      o.y = fminf(pv.y, 1.0f - pv.y) * inv_t * (gv.y - dkf);
+      o.z = fminf(pv.z, 1.0f - pv.z) * inv_t * (gv.z - dkf);
+      o.w = fminf(pv.w, 1.0f - pv.w) * inv_t * (gv.w - dkf);
+      __builtin_nontemporal_store(o, d4 + i);
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
+      dd[i] = fminf(pp[i], 1.0f - pp[i]) * inv_t * (gg[i] - dkf);
+  }
+}
+
+int bwd_grid_x(int64_t rows, int64_t n) { return stream_grid_x(rows, n); }
+size_t bwd_partial_bytes(int64_t rows, int grid_x) { return sizeof(BwdPartial) * (size_t)rows * (size_t)grid_x; }
+
+hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st, void *partials,
+                             int grid_x, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n, st,
+                     reinterpret_cast<BwdPartial *>(partials), grid_x, dk, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const RowState *st, double t,
+                            float *dr, hipStream_t s) {
+  const int gx = stream_grid_x(rows, n);
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n, st, t, dr);
+  return hipGetLastError();
+}
+
+}  // namespace lapsum

@@ -1,0 +1,75 @@
+"""Comparison helpers for the GPU parity tests (tolerances of the operator's
+accuracy bar, written out here):
+
+  max|p_gpu - p_oracle|            <= 2e-5
+  |sum p_gpu - k|                  <= 1e-5 max(1, k)      (per row, fp64 sum)
+  |b_gpu - b_oracle| / t           <= 1e-4
+  ||dr_gpu - dr_oracle|| / ||dr_oracle||            <= 1e-4 (per row)
+  |dk_gpu - dk_oracle| / sum_i (d_i/D)|g_i|         <= 1e-4 (dk is the
+                                     d-weighted mean of g; that is its scale)
+
+The budget bound follows the pages' reported normalisation error (< 1e-5 at
+all scales, "Fast LapSum: Exact Differentiable Top-k at Million Scale",
+section 4.1).
+"""
+import math
+import sys
+
+import numpy as np
+
+TOL_P = 2e-5
+TOL_SUM = 1e-5
+TOL_B = 1e-4
+TOL_GRAD = 1e-4
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_forward(name, k, t, p_gpu, b_gpu, p_or, b_or, rows_idx=None):
+    p_gpu = np.asarray(p_gpu, dtype=np.float64)
+    p_or = np.asarray(p_or, dtype=np.float64)
+    b_gpu = np.atleast_1d(np.asarray(b_gpu, dtype=np.float64))
+    b_or = np.atleast_1d(np.asarray(b_or, dtype=np.float64))
+    dp = float(np.max(np.abs(p_gpu - p_or))) if p_gpu.size else 0.0
+    db = float(np.max(np.abs(b_gpu - b_or))) / t
+    assert np.all(np.isfinite(p_gpu)) and np.all(np.isfinite(b_gpu)), name
+    assert dp <= TOL_P, f"{name}: max|dp| = {dp:.3e}"
+    assert db <= TOL_B, f"{name}: max|db|/t = {db:.3e}"
+    return dp, db
+
+
+def check_budget(name, k, p_gpu):
+    p = np.asarray(p_gpu, dtype=np.float64)
+    if p.ndim == 1:
+        p = p[None, :]
+    sums = np.array([math.fsum(row) for row in p])
+    err = float(np.max(np.abs(sums - k)))
+    assert err <= TOL_SUM * max(1.0, k), f"{name}: |sum p - k| = {err:.3e}"
+    return err
+
+
+def check_backward(name, r, b_or, g, t, dr_gpu, dk_gpu, dr_or, dk_or):
+    r = np.asarray(r, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    if r.ndim == 1:
+        r, g = r[None, :], g[None, :]
+    dr_gpu = np.asarray(dr_gpu, dtype=np.float64).reshape(r.shape)
+    dr_or = np.asarray(dr_or, dtype=np.float64).reshape(r.shape)
+    dk_gpu = np.atleast_1d(np.asarray(dk_gpu, dtype=np.float64))
+    dk_or = np.atleast_1d(np.asarray(dk_or, dtype=np.float64))
+    worst_dr = worst_dk = 0.0
+    for i in range(r.shape[0]):
+        den = np.linalg.norm(dr_or[i])
+        if den > 0:
+            worst_dr = max(worst_dr, float(np.linalg.norm(dr_gpu[i] - dr_or[i]) / den))
+        a = np.abs(r[i] - b_or[i])
+        w = np.exp(-(a - a.min()) / t)
+        scale = float(np.sum(w * np.abs(g[i])) / np.sum(w))
+        if scale > 0:
+            worst_dk = max(worst_dk, abs(dk_gpu[i] - dk_or[i]) / scale)
+    assert worst_dr <= TOL_GRAD, f"{name}: dr rel err = {worst_dr:.3e}"
+    assert worst_dk <= TOL_GRAD, f"{name}: dk rel err = {worst_dk:.3e}"
+    return worst_dr, worst_dk

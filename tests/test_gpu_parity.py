@@ -1,0 +1,324 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Operator: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
+section 2.1 (eqs. (1)-(2), analytic VJP); solvers of section 2.2 (full sort;
+probabilistic bracketing with certification and a full-sort fallback).
+Tolerances: tests/parity.py.  Inputs: sparse_selection_primitive_amd.workloads
+(seeded numpy generators shared by both sides).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from parity import check_backward, check_budget, check_forward, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_selection_primitive_amd as lib
+    lib.load_library()  # fails loudly when the HIP library is missing
+    return lib
+
+
+@pytest.fixture(scope="module")
+def O():
+    import oracle
+    oracle._load()
+    return oracle
+
+
+def gpu(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(L, r, k, t, g=None, **opts):
+    rt = gpu(r)
+    out = L.lapsum_forward(rt, k, t, **opts)
+    p, b = out[0], out[1]
+    res = {"p": p, "b": b}
+    if len(out) > 2:
+        res["stats"] = out[2]
+    if g is not None:
+        dr, dk = L.lapsum_backward(gpu(g), p, b, t)
+        res["dr"], res["dk"] = dr, dk
+    torch.cuda.synchronize()
+    return {key: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for key, v in res.items()}
+
+
+def full_check(name, L, O, r, g, k, t, **opts):
+    log(f"[case] {name} shape={r.shape} k={k} t={t} opts={opts}")
+    res = run(L, r, k, t, g, **opts)
+    p_or, b_or = O.forward(r, k, t)
+    dp, db = check_forward(name, k, t, res["p"], res["b"], p_or, b_or)
+    err = check_budget(name, k, res["p"])
+    out = f"  max|dp|={dp:.2e} max|db|/t={db:.2e} |sum-k|={err:.2e}"
+    if g is not None:
+        dr_or, dk_or = O.backward(r, b_or, g, t)
+        edr, edk = check_backward(name, r, b_or, g, t, res["dr"], res["dk"], dr_or, dk_or)
+        out += f" dr_rel={edr:.2e} dk_rel={edk:.2e}"
+    log(out)
+    return res, p_or, b_or
+
+
+# ------------------------------------------------------------ on-chip path
+def test_onchip_brute_force_golden(L):
+    """n <= 8 against the 50-digit exhaustive solutions in tests/golden."""
+    import mpmath
+    path = os.path.join(os.path.dirname(__file__), "golden", "brute_small.json")
+    cases = json.load(open(path))["cases"]
+    log(f"[case] brute golden, {len(cases)} rows of n <= 8")
+    worst = 0.0
+    for c in cases:
+        r = np.array([c["r"]], np.float32)
+        res = run(L, r, c["k"], c["t"])
+        be = float(mpmath.mpf(c["b"]))
+        assert abs(res["b"][0] - be) / c["t"] <= 1e-4 or abs(res["b"][0] - be) <= 1e-12 * max(1, abs(be)), c
+        with mpmath.workdps(40):
+            for i, x in enumerate(c["r"]):
+                z = (mpmath.mpf(x) - mpmath.mpf(c["b"])) / c["t"]
+                pe = float(mpmath.exp(z) / 2 if z < 0 else 1 - mpmath.exp(-z) / 2)
+                worst = max(worst, abs(res["p"][0, i] - pe))
+    assert worst <= 2e-5, worst
+    log(f"  max|dp| vs brute = {worst:.2e}")
+
+
+def test_onchip_tiny(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.tiny()
+    full_check(w.name, L, O, w.r, w.g, w.k, w.t)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 17, 63, 64, 65, 100, 255, 256, 257, 511, 512, 513, 1000, 1023, 1024,
+                               1025, 2047, 2049, 4095, 4097, 6000, 8191, 8192])
+def test_onchip_ragged_sizes(L, O, n):
+    g0 = np.random.Generator(np.random.PCG64(1000 + n))
+    rows = int(g0.integers(1, 6))
+    r = g0.standard_normal((rows, n)).astype(np.float32)
+    g = g0.standard_normal((rows, n)).astype(np.float32)
+    k = float(g0.uniform(0.05, n - 0.05)) if n > 1 else 0.37
+    t = float(10 ** g0.uniform(-1.5, 0.5))
+    full_check(f"onchip n={n}", L, O, r, g, k, t)
+
+
+def test_onchip_routing_with_ties(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.routing()
+    res, p_or, b_or = full_check(w.name, L, O, w.r, w.g, w.k, w.t)
+    # tied scores get bitwise identical probabilities
+    for row in w.meta["tie_rows"][:64]:
+        vals, inv = np.unique(w.r[row], return_inverse=True)
+        for j in range(vals.size):
+            pj = res["p"][row][inv == j]
+            assert np.all(pj == pj[0])
+    const_row = w.meta["tie_rows"][0]
+    np.testing.assert_allclose(res["p"][const_row], w.k / w.n, atol=1e-6)
+
+
+@pytest.mark.parametrize("k", [1e-4, 0.5, 255.5, 256 - 1e-4])
+def test_onchip_end_cases(L, O, k):
+    g0 = np.random.Generator(np.random.PCG64(77))
+    r = g0.standard_normal((3, 256)).astype(np.float32)
+    g = g0.standard_normal((3, 256)).astype(np.float32)
+    full_check(f"onchip k={k}", L, O, r, g, k, 0.3)
+
+
+def test_onchip_constant_and_single(L, O):
+    r = np.full((2, 300), -2.5, np.float32)
+    full_check("constant rows", L, O, r, None, 7.0, 0.05)
+    r1 = np.array([[0.25], [-3.0]], np.float32)
+    res = run(L, r1, 0.3, 0.2)
+    np.testing.assert_allclose(res["p"][:, 0], 0.3, atol=1e-6)
+
+
+def test_onchip_tiny_temperature_limit(L, O):
+    """t far below the gaps: b -> midpoint of the k-th and (k+1)-th largest."""
+    g0 = np.random.Generator(np.random.PCG64(78))
+    r = (np.round(g0.standard_normal((4, 64)) * 50) / 50).astype(np.float32)
+    res = run(L, r, 5.0, 1e-4)
+    for i in range(4):
+        s = np.sort(r[i].astype(np.float64))[::-1]
+        if s[4] - s[5] > 0.02:
+            assert abs(res["b"][i] - 0.5 * (s[4] + s[5])) <= 0.5e-4 * math.log(64) + 1e-6
+    p_or, b_or = O.forward(r, 5.0, 1e-4)
+    assert np.max(np.abs(res["p"] - p_or)) <= 2e-5
+
+
+# ----------------------------------------------------------- full-sort path
+def test_fullsort_coder(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder()
+    full_check(w.name + " fullsort", L, O, w.r, w.g, w.k, w.t, path="fullsort")
+
+
+@pytest.mark.parametrize("n,rows", [(8193, 3), (10000, 2), (70001, 2), (300, 4)])
+def test_fullsort_ragged(L, O, n, rows):
+    g0 = np.random.Generator(np.random.PCG64(2000 + n))
+    r = g0.standard_normal((rows, n)).astype(np.float32)
+    g = g0.standard_normal((rows, n)).astype(np.float32)
+    k = float(g0.uniform(1, n - 1))
+    full_check(f"fullsort n={n}", L, O, r, g, k, 0.05, path="fullsort")
+
+
+# ---------------------------------------------------------- bracketing path
+def check_bracket_stats(name, L, O, r, k, t, stats, seed, m_log2=None, delta=1e-6):
+    from oracle import bracket as ob
+    rows, n = r.shape
+    plan = L.plan(rows, n, k, t, path="bracket", seed=seed, sample_log2=m_log2 or 0, delta=delta)
+    m = plan["m"]
+    for i in range(rows):
+        a_lo, a_hi, lo, hi = ob.bracket(r[i], k, t, m, delta, seed, row=i)
+        for got, want in ((stats["a_lo"][i].item(), a_lo), (stats["a_hi"][i].item(), a_hi)):
+            if math.isinf(want):
+                assert got == want
+            else:
+                assert abs(got - want) <= 2.5e-7 * abs(want) + 1e-30, (name, i, got, want)
+        ts = O.tail_sums(r[i], stats["a_lo"][i].item(), stats["a_hi"][i].item(), t)
+        assert stats["count_lo"][i].item() == ts["c_L"]
+        assert stats["count_hi"][i].item() == ts["c_R"]
+        assert stats["band"][i].item() == ts["M"]
+        for key, ref in (("tail_lo", ts["S_L"]), ("tail_hi", ts["S_R"])):
+            assert abs(stats[key][i].item() - ref) <= 1e-5 * abs(ref) + 1e-30, (name, key)
+
+
+def test_bracket_coder_matches_fullsort(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder()
+    res, p_or, b_or = full_check(w.name + " bracket", L, O, w.r, w.g, w.k, w.t, path="bracket", stats=True)
+    st = res["stats"]
+    assert np.all(st["flags"].numpy() & L.FLAG_HIT), st["flags"]
+    check_bracket_stats(w.name, L, O, w.r, w.k, w.t, st, seed=0)
+    full = run(L, w.r, w.k, w.t, path="fullsort")
+    assert np.max(np.abs(full["p"] - res["p"])) <= 2e-5
+    assert np.max(np.abs(full["b"] - res["b"])) / w.t <= 1e-4
+
+
+def test_bracket_attack(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.attack()
+    res, _, _ = full_check(w.name, L, O, w.r, w.g, w.k, w.t, stats=True)
+    st = res["stats"]
+    assert st["flags"][0].item() & L.FLAG_HIT
+    check_bracket_stats(w.name, L, O, w.r, w.k, w.t, st, seed=0)
+    log(f"  band M={st['band'][0].item()} a=[{st['a_lo'][0].item():.6f}, {st['a_hi'][0].item()}]")
+
+
+def test_bracket_forced_miss_falls_back(L, O):
+    """A bracket that excludes b must be caught by certification and the
+    full-sort fallback must still meet every tolerance."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=4, n=65536)
+    _, b_or = O.forward(w.r, w.k, w.t)
+    lo = float(np.max(b_or)) + 0.5
+    res, _, _ = full_check("forced miss (bracket above b)", L, O, w.r, w.g, w.k, w.t, path="bracket",
+                           bracket_override=(lo, lo + 1.0), stats=True)
+    fl = res["stats"]["flags"].numpy()
+    assert np.all(fl & L.FLAG_FALLBACK) and not np.any(fl & L.FLAG_HIT)
+    hi = float(np.min(b_or)) - 0.2
+    full_check("forced miss (bracket below b)", L, O, w.r, None, w.k, w.t, path="bracket",
+               bracket_override=(hi - 1.0, hi))
+
+
+def test_bracket_band_overflow_falls_back(L, O):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=2, n=65536)
+    res, _, _ = full_check("band overflow", L, O, w.r, None, w.k, w.t, path="bracket", band_capacity=16,
+                           stats=True)
+    fl = res["stats"]["flags"].numpy()
+    assert np.all(fl & L.FLAG_OVERFLOW) and np.all(fl & L.FLAG_FALLBACK)
+
+
+def test_bracket_loose_delta_many_seeds(L, O):
+    """delta = 0.9 makes misses common; every row must still match."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=8, n=65536)
+    p_or, b_or = O.forward(w.r, w.k, w.t)
+    misses = 0
+    for seed in range(6):
+        res = run(L, w.r, w.k, w.t, path="bracket", delta=0.9, seed=seed, stats=True)
+        check_forward(f"delta=0.9 seed={seed}", w.k, w.t, res["p"], res["b"], p_or, b_or)
+        misses += int(np.sum(res["stats"]["flags"].numpy() & L.FLAG_FALLBACK != 0))
+    log(f"  fallbacks over 48 rows: {misses}")
+    assert misses > 0
+
+
+def test_bracket_large_band_path(L, O):
+    """A band above the on-chip capacity goes through the radix band sort."""
+    g0 = np.random.Generator(np.random.PCG64(3001))
+    n, k, t = 2_000_000, 20000.0, 0.01
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    plan = L.plan(1, n, k, t, path="bracket")
+    assert plan["band_onchip"] == 0
+    res, _, _ = full_check("bracket large band", L, O, r, g, k, t, path="bracket", stats=True)
+    assert res["stats"]["flags"][0].item() & L.FLAG_HIT
+
+
+def test_bracket_extreme_sampled(L, O):
+    """1e8 scores: b against the oracle's bisection over the whole row, p and
+    dr on a million sampled indices, and the budget over the whole row."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.extreme()
+    log(f"[case] {w.name} k={w.k} t={w.t}")
+    rt, gt = gpu(w.r), gpu(w.g)
+    p, b, st = L.lapsum_forward(rt, w.k, w.t, stats=True)
+    dr, dk = L.lapsum_backward(gt, p, b, w.t)
+    torch.cuda.synchronize()
+    assert st["flags"][0].item() & L.FLAG_HIT
+    psum = float(torch.sum(p.double()).item())
+    assert abs(psum - w.k) <= 1e-5 * w.k, psum
+    del rt, gt
+    r64 = w.r[0].astype(np.float64)
+    _, b_or = O.forward(w.r, w.k, w.t)
+    db = abs(b.item() - b_or[0]) / w.t
+    assert db <= 1e-4, db
+    idx = np.random.Generator(np.random.PCG64(9)).integers(0, w.n, 1_000_000)
+    z = (r64[idx] - b_or[0]) / w.t
+    p_ref = np.where(z < 0, 0.5 * np.exp(np.minimum(z, 0)), 1 - 0.5 * np.exp(-np.maximum(z, 0)))
+    pg = p[0, torch.from_numpy(idx).cuda()].double().cpu().numpy()
+    assert np.max(np.abs(pg - p_ref)) <= 2e-5
+    # gradient: dk over the whole row, dr on the sample
+    dr_or, dk_or = O.backward(w.r, b_or, w.g, w.t)
+    drg = dr[0].double().cpu().numpy()
+    rel = np.linalg.norm(drg - dr_or[0]) / np.linalg.norm(dr_or[0])
+    assert rel <= 1e-4, rel
+    a = np.abs(r64 - b_or[0])
+    wgt = np.exp(-(a - a.min()) / w.t)
+    scale = float(np.sum(wgt * np.abs(w.g[0])) / np.sum(wgt))
+    assert abs(dk.item() - dk_or[0]) / scale <= 1e-4
+    log(f"  db/t={db:.2e} |sum-k|={abs(psum - w.k):.2e} dr_rel={rel:.2e} band={st['band'][0].item()}")
+
+
+# ------------------------------------------------------------ determinism
+def test_determinism(L):
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=4)
+    for path in ("bracket", "fullsort"):
+        a = run(L, w.r, w.k, w.t, w.g, path=path)
+        b = run(L, w.r, w.k, w.t, w.g, path=path)
+        for key in ("p", "b", "dr", "dk"):
+            assert np.array_equal(a[key], b[key]), (path, key)
+    w = workloads.routing(rows=512)
+    a = run(L, w.r, w.k, w.t, w.g)
+    b = run(L, w.r, w.k, w.t, w.g)
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_autograd_wrapper(L):
+    g0 = np.random.Generator(np.random.PCG64(5))
+    r = torch.from_numpy(g0.standard_normal((4, 300)).astype(np.float32)).cuda().requires_grad_(True)
+    p = L.soft_topk(r, 10.0, 0.1)
+    w = torch.from_numpy(g0.standard_normal((4, 300)).astype(np.float32)).cuda()
+    (p * w).sum().backward()
+    dr, _ = L.lapsum_backward(w, p.detach(), L.lapsum_forward(r.detach(), 10.0, 0.1)[1], 0.1)
+    assert torch.equal(r.grad, dr)
