@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restr
   const float inv_t = (float)(1.0 / t);
   float out[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (gv[e] - dkf) : 0.0f;
+  for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (float)((double)gv[e] - dkd) : 0.0f;
   store_row<E>(dr + rr * n, n, base, ok, vec, out);
   if (ok && team.lane == 0) {
     dk[rr] = dkf;

@@ -223,7 +223,6 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
   const int64_t row = blockIdx.y;
   const double dkd = st[row].dk;
   const bool degenerate = (st[row].flags & LAPSUM_FLAG_DEGENERATE) != 0;
-  const float dkf = (float)dkd;
   const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
   const float *gg = g + row * n;
   const float *pp = p + row * n;
@@ -238,15 +237,15 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
       const f4 pv = __builtin_nontemporal_load(p4 + i);
       const f4 gv = __builtin_nontemporal_load(g4 + i);
       f4 o;
-      o.x = fminf(pv.x, 1.0f - pv.x) * inv_t * (gv.x - dkf);
-      o.y = fminf(pv.y, 1.0f - pv.y) * inv_t * (gv.y - dkf);
-      o.z = fminf(pv.z, 1.0f - pv.z) * inv_t * (gv.z - dkf);
-      o.w = fminf(pv.w, 1.0f - pv.w) * inv_t * (gv.w - dkf);
+      o.x = fminf(pv.x, 1.0f - pv.x) * inv_t * (float)((double)gv.x - dkd);
+      o.y = fminf(pv.y, 1.0f - pv.y) * inv_t * (float)((double)gv.y - dkd);
+      o.z = fminf(pv.z, 1.0f - pv.z) * inv_t * (float)((double)gv.z - dkd);
+      o.w = fminf(pv.w, 1.0f - pv.w) * inv_t * (float)((double)gv.w - dkd);
       __builtin_nontemporal_store(o, d4 + i);
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
-      dd[i] = fminf(pp[i], 1.0f - pp[i]) * inv_t * (gg[i] - dkf);
+      dd[i] = fminf(pp[i], 1.0f - pp[i]) * inv_t * (float)((double)gg[i] - dkd);
   }
 }
 

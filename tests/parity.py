@@ -7,6 +7,8 @@ accuracy bar, written out here):
   ||dr_gpu - dr_oracle|| / ||dr_oracle||            <= 1e-4 (per row)
   |dk_gpu - dk_oracle| / sum_i (d_i/D)|g_i|         <= 1e-4 (dk is the
                                      d-weighted mean of g; that is its scale)
+  both gradient bounds plus the resolution floor of fp32 probabilities
+  (see check_backward)
 
 The budget bound follows the pages' reported normalisation error (< 1e-5 at
 all scales, "Fast LapSum: Exact Differentiable Top-k at Million Scale",
@@ -52,6 +54,11 @@ def check_budget(name, k, p_gpu):
 
 
 def check_backward(name, r, b_or, g, t, dr_gpu, dk_gpu, dr_or, dk_or):
+    """Per row: ||dr_gpu - dr_or|| <= 1e-4 ||dr_or|| + floor and
+    |dk_gpu - dk_or| <= 1e-4 scale_dk + floor_dk.  The floors are the
+    resolution of d = min(p, 1-p)/t when p is fp32: for p > 1/2, 1 - p is
+    known only to 2^-25 absolutely, so d_i carries an absolute error of up to
+    2^-25/t (taken as 2^-24/t) and dr_i = d_i (g_i - dk) inherits it."""
     r = np.asarray(r, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     if r.ndim == 1:
@@ -60,16 +67,24 @@ def check_backward(name, r, b_or, g, t, dr_gpu, dk_gpu, dr_or, dk_or):
     dr_or = np.asarray(dr_or, dtype=np.float64).reshape(r.shape)
     dk_gpu = np.atleast_1d(np.asarray(dk_gpu, dtype=np.float64))
     dk_or = np.atleast_1d(np.asarray(dk_or, dtype=np.float64))
+    u = 2.0 ** -24
     worst_dr = worst_dk = 0.0
     for i in range(r.shape[0]):
-        den = np.linalg.norm(dr_or[i])
+        zed = (r[i] - b_or[i]) / t
+        above = zed > 0                      # p > 1/2
+        dev = g[i] - dk_or[i]
+        floor_dr = (u / t) * float(np.linalg.norm(dev[above]))
+        den = float(np.linalg.norm(dr_or[i])) + floor_dr / TOL_GRAD
         if den > 0:
-            worst_dr = max(worst_dr, float(np.linalg.norm(dr_gpu[i] - dr_or[i]) / den))
-        a = np.abs(r[i] - b_or[i])
-        w = np.exp(-(a - a.min()) / t)
+            worst_dr = max(worst_dr, float(np.linalg.norm(dr_gpu[i] - dr_or[i])) / den)
+        a = np.abs(zed)
+        w = np.exp(-(a - a.min()))
         scale = float(np.sum(w * np.abs(g[i])) / np.sum(w))
-        if scale > 0:
-            worst_dk = max(worst_dk, abs(dk_gpu[i] - dk_or[i]) / scale)
+        D = float(np.sum(0.5 * np.exp(-a))) / t
+        floor_dk = (u / t) * float(np.sum(np.abs(dev[above]))) / D if D > 0 else math.inf
+        den_k = scale + floor_dk / TOL_GRAD
+        if den_k > 0 and math.isfinite(den_k):
+            worst_dk = max(worst_dk, abs(dk_gpu[i] - dk_or[i]) / den_k)
     assert worst_dr <= TOL_GRAD, f"{name}: dr rel err = {worst_dr:.3e}"
     assert worst_dk <= TOL_GRAD, f"{name}: dk rel err = {worst_dk:.3e}"
     return worst_dr, worst_dk
