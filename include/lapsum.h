@@ -29,7 +29,8 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Outputs are valid once the stream reaches the call's end.
  *   - The returned status covers host-side argument checks and launch errors
- *     only.  Per-row outcomes (bracket hit/miss, fallback, degenerate
+ *     only.  Each call first clears any non-sticky HIP error left pending on
+ *     the calling thread by earlier runtime calls.  Per-row outcomes (bracket hit/miss, fallback, degenerate
  *     backward) are reported through the optional `stats` array.
  *   - Scores must be finite; non-finite scores give unspecified outputs (the
  *     kernels still terminate).

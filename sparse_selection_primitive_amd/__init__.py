@@ -267,3 +267,52 @@ def soft_topk(r, k: float, t: float, **kw):
             return dr
 
     return _LapSum.apply(r)
+
+
+class Operator:
+    """Prepared calls for a fixed (rows, n, k, t) and options: the options
+    struct, workspace and stream are resolved once, so each call is a single
+    C-ABI call with raw device pointers (for tight loops and benchmarks).
+    Outputs are written into caller-provided tensors."""
+
+    def __init__(self, rows: int, n: int, k: float, t: float, device=None, stream=None, path="auto", seed=0,
+                 sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None):
+        torch = _torch()
+        self.lib = load_library()
+        self.rows, self.n, self.k, self.t = int(rows), int(n), float(k), float(t)
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
+                                stats_buf.data_ptr() if stats_buf is not None else None)
+        nbytes = int(self.lib.lapsum_workspace_bytes(self.rows, self.n, self.k, self.t, ctypes.byref(self.opt)))
+        self._ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device) if nbytes else None
+        if self._ws is not None:
+            ptr = self._ws.data_ptr()
+            self.wptr, self.wlen = ptr + ((-ptr) % 256), self._ws.numel() - ((-ptr) % 256)
+        else:
+            self.wptr, self.wlen = None, 0
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.stream = s.cuda_stream
+        self._opt_ref = ctypes.byref(self.opt)
+        self._ev_arrays = {}
+
+    def _opt_with_events(self, events):
+        if events is None:
+            self.opt.stage_events = None
+            return self._opt_ref
+        arr = (ctypes.c_void_p * (2 * STAGE_COUNT))(*events)
+        self._ev_keep = arr
+        self.opt.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        return self._opt_ref
+
+    def forward(self, r, p, b, stage_events=None):
+        rc = self.lib.lapsum_forward(r.data_ptr(), self.rows, self.n, self.k, self.t, p.data_ptr(), b.data_ptr(),
+                                     self.wptr, self.wlen, self._opt_with_events(stage_events), self.stream)
+        if rc:
+            _check(rc, "lapsum_forward")
+
+    def backward(self, g, p, b, dr, dk, stage_events=None):
+        rc = self.lib.lapsum_backward(g.data_ptr(), p.data_ptr(), b.data_ptr(), self.rows, self.n, self.t,
+                                      dr.data_ptr(), dk.data_ptr(), self.wptr, self.wlen,
+                                      self._opt_with_events(stage_events), self.stream)
+        if rc:
+            _check(rc, "lapsum_backward")

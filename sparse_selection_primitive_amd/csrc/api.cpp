@@ -63,7 +63,7 @@ struct Plan {
   bool band_onchip = false;
   // forward layout
   size_t fwd_bytes = 0;
-  size_t st = 0, samples = 0, fpart = 0, band = 0;
+  size_t st = 0, samples = 0, fpart = 0, band = 0, slots = 0, offs = 0;
   int fgx = 0;
   SegRegions band_seg{}, full_seg{};
   // backward layout
@@ -137,6 +137,17 @@ lapsum_status check_common(int64_t rows, int64_t n, double t) {
   return LAPSUM_OK;
 }
 
+// Workspace of the backward: depends on (rows, n) only.
+void bwd_layout(int64_t rows, int64_t n, Plan &P) {
+  Layout B;
+  if (!onchip_backward_supported(n)) {
+    P.bst = B.take((size_t)rows * row_state_bytes());
+    P.bgx = bwd_grid_x(rows, n);
+    P.bpart = B.take(bwd_partial_bytes(rows, P.bgx));
+  }
+  P.bwd_bytes = B.off;
+}
+
 lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt, Plan &P) {
   lapsum_status st = check_common(rows, n, t);
   if (st != LAPSUM_OK) return st;
@@ -189,19 +200,15 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
     P.fgx = filter_grid_x(rows, n);
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
+    P.slots = F.take(band_slot_bytes(rows, P.fgx));
+    P.offs = F.take(band_offs_bytes(rows, P.fgx));
     P.band = F.take((size_t)rows * (size_t)P.cap * sizeof(uint32_t));
     if (!P.band_onchip) P.band_seg = seg_regions(F, rows, P.cap);
     P.full_seg = seg_regions(F, rows, n);
   }
   P.fwd_bytes = F.off;
 
-  Layout B;
-  if (!onchip_backward_supported(n)) {
-    P.bst = B.take((size_t)rows * row_state_bytes());
-    P.bgx = bwd_grid_x(rows, n);
-    P.bpart = B.take(bwd_partial_bytes(rows, P.bgx));
-  }
-  P.bwd_bytes = B.off;
+  bwd_layout(rows, n, P);
   return LAPSUM_OK;
 }
 
@@ -224,13 +231,17 @@ lapsum_status hip_status(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LA
   } while (0)
 
 SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t n, const float *r,
-                 const uint32_t *band, RowState *st, double k, double t) {
+                 uint32_t *band, RowState *st, double k, double t, const uint32_t *slots = nullptr,
+                 const uint32_t *offs = nullptr, int gx = 0) {
   SegArgs a;
   a.mode = mode;
   a.rows = (int)rows;
   a.n = n;
   a.r = r;
   a.band = band;
+  a.slots = slots;
+  a.offs = offs;
+  a.gx = gx;
   a.A = reinterpret_cast<uint32_t *>(ws + R.A);
   a.B = reinterpret_cast<uint32_t *>(ws + R.B);
   a.stride = R.stride;
@@ -323,6 +334,9 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const StageTimer tm{o.stage_events, s};
   char *ws = reinterpret_cast<char *>(workspace);
+  // Launch errors are read back with hipGetLastError(); drop any non-sticky
+  // error an earlier, unrelated runtime call left pending on this thread.
+  (void)hipGetLastError();
 
   if (P.path == LAPSUM_PATH_ONCHIP) {
     tm.mark(LAPSUM_STAGE_ONCHIP_FWD, 0);
@@ -354,17 +368,20 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
       tm.mark(LAPSUM_STAGE_SELECT, 1);
     }
     uint32_t *band = reinterpret_cast<uint32_t *>(ws + P.band);
+    uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);
+    uint32_t *offs = reinterpret_cast<uint32_t *>(ws + P.offs);
     tm.mark(LAPSUM_STAGE_FILTER, 0);
-    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, band, P.cap, ws + P.fpart, P.fgx, s));
+    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, offs, P.cap, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
     if (P.band_onchip)
-      LAPSUM_TRY(launch_band_onchip(band, rows, P.cap, rs, k, t, s));
+      LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, s));
     else
-      LAPSUM_TRY(launch_segment(seg_args(P.band_seg, ws, kSegBand, rows, n, r, band, rs, k, t), s));
+      LAPSUM_TRY(launch_segment(
+          seg_args(P.band_seg, ws, kSegBand, rows, n, r, band, rs, k, t, slots, offs, P.fgx), s));
     tm.mark(LAPSUM_STAGE_BAND, 1);
     tm.mark(LAPSUM_STAGE_FULLSORT, 0);
-    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t), s));
+    LAPSUM_TRY(launch_fallback(seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t), s));
     tm.mark(LAPSUM_STAGE_FULLSORT, 1);
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);
@@ -381,9 +398,7 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   if (st0 != LAPSUM_OK) return st0;
   if (!g || !p || !b || !dr || !dk) return LAPSUM_ERR_NULL;
   Plan P;
-  // the backward layout depends on (rows, n) only; k = n/2 is always valid for planning
-  st0 = make_plan(rows, n, 0.5 * (double)n, t, nullptr, P);
-  if (st0 != LAPSUM_OK) return st0;
+  bwd_layout(rows, n, P);
   if (P.bwd_bytes > 0) {
     if (!workspace) return LAPSUM_ERR_NULL;
     if (workspace_bytes < P.bwd_bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
@@ -394,6 +409,7 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   if (opt) o = *opt;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const StageTimer tm{o.stage_events, s};
+  (void)hipGetLastError();  // see lapsum_forward
   if (onchip_backward_supported(n)) {
     tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 0);
     LAPSUM_TRY(launch_onchip_backward(g, p, rows, (int)n, t, dr, dk, o.stats, s));
@@ -402,7 +418,6 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   }
   char *ws = reinterpret_cast<char *>(workspace);
   RowState *rs = reinterpret_cast<RowState *>(ws + P.bst);
-  LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 0);
   LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, rs, ws + P.bpart, P.bgx, dk, o.stats, s));
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 1);

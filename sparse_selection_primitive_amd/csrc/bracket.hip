@@ -240,6 +240,9 @@ hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t 
 struct FilterPartial {
   double sl, sr;
   unsigned long long cl, cr;
+  uint32_t cnt;       // band keys this block found (may exceed kBandSlot)
+  uint32_t kmn, kmx;  // key range of those band keys
+  uint32_t pad;
 };
 
 LDEV void filter_one(float x, float aL, float aR, float cf, float &fl, float &fr, uint32_t &cl, uint32_t &cr,
@@ -259,20 +262,27 @@ LDEV uint32_t mbcnt64(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// One coalesced pass over the row.  Band keys go to this block's own slot
+// (positions reserved by an LDS counter, one LDS atomic per wave); the tail
+// sums, counts and the band key range go to the block's partial.  No global
+// atomics: the per-row finalize adds the partials in a fixed order and turns
+// the slot counts into offsets.
 __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__restrict__ r, int64_t n,
-                                                                RowState *__restrict__ st,
-                                                                uint32_t *__restrict__ band, int64_t cap,
+                                                                const RowState *__restrict__ st,
+                                                                uint32_t *__restrict__ slots,
                                                                 FilterPartial *__restrict__ part, int gx, double t) {
   __shared__ double lds_d[2 * kStreamThreads / kWave];
   __shared__ unsigned long long lds_c[2 * kStreamThreads / kWave];
   __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
-  __shared__ int is_last;
+  __shared__ uint32_t lcount;
   const int64_t row = blockIdx.y;
-  RowState &S = st[row];
+  const RowState &S = st[row];
+  if (threadIdx.x == 0) lcount = 0u;
+  __syncthreads();
   const float aL = (float)S.a_lo, aR = (float)S.a_hi;
   const float cf = (float)(kLog2e / t);
   const float *rr = r + row * n;
-  uint32_t *bb = band + row * cap;
+  uint32_t *slot = slots + ((int64_t)row * gx + blockIdx.x) * kBandSlot;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
   double sl = 0.0, sr = 0.0;
   uint32_t cl = 0, cr = 0;
@@ -315,20 +325,20 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
         mq[q] = __ballot(mid[q]);
         tot += (uint32_t)__popcll(mq[q]);
       }
-      unsigned long long base = 0;
-      if (lane_id() == leader) base = atomicAdd(&S.band, (unsigned long long)tot);
+      uint32_t base = 0u;
+      if (lane_id() == leader) base = atomicAdd(&lcount, tot);
       base = __shfl(base, leader, kWave);
-      unsigned long long off = base;
+      uint32_t off = base;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (mid[q]) {
-          const unsigned long long pos = off + mbcnt64(mq[q]);
+          const uint32_t pos = off + mbcnt64(mq[q]);
           const uint32_t kk = key_of(x[q]);
-          if (pos < (unsigned long long)cap) bb[pos] = kk;
+          if (pos < (uint32_t)kBandSlot) slot[pos] = kk;  // beyond the slot: counted, row falls back
           kmn = min(kmn, kk);
           kmx = max(kmx, kk);
         }
-        off += (unsigned long long)__popcll(mq[q]);
+        off += (uint32_t)__popcll(mq[q]);
       }
     }
   }
@@ -355,44 +365,128 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    double a = 0.0, b = 0.0;
-    unsigned long long c0 = 0, c1 = 0;
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    FilterPartial fp;
+    fp.sl = 0.0;
+    fp.sr = 0.0;
+    fp.cl = 0;
+    fp.cr = 0;
+    fp.kmn = 0xFFFFFFFFu;
+    fp.kmx = 0u;
     for (int i = 0; i < kStreamThreads / kWave; ++i) {
-      a += lds_d[2 * i];
-      b += lds_d[2 * i + 1];
-      c0 += lds_c[2 * i];
-      c1 += lds_c[2 * i + 1];
-      mn = min(mn, lds_k[2 * i]);
-      mx = max(mx, lds_k[2 * i + 1]);
+      fp.sl += lds_d[2 * i];
+      fp.sr += lds_d[2 * i + 1];
+      fp.cl += lds_c[2 * i];
+      fp.cr += lds_c[2 * i + 1];
+      fp.kmn = min(fp.kmn, lds_k[2 * i]);
+      fp.kmx = max(fp.kmx, lds_k[2 * i + 1]);
     }
-    part[row * gx + blockIdx.x] = FilterPartial{a, b, c0, c1};
-    if (mn <= mx) {
-      atomicMin(&S.kmin, mn);
-      atomicMax(&S.kmax, mx);
+    fp.cnt = lcount;
+    fp.pad = 0u;
+    part[row * gx + blockIdx.x] = fp;
+  }
+}
+
+// Per row, in a fixed order: tail sums and counts, band size M, band key
+// range, and the exclusive offsets of the block slots (offs[gx] = M).  A
+// slot that overflowed, or M beyond the band capacity, sends the row to the
+// full-sort fallback.
+__global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const FilterPartial *__restrict__ part,
+                                                                         int gx, int64_t cap,
+                                                                         RowState *__restrict__ st,
+                                                                         uint32_t *__restrict__ offs) {
+  __shared__ double lds_d[2 * kStreamThreads / kWave];
+  __shared__ unsigned long long lds_c[2 * kStreamThreads / kWave];
+  __shared__ uint32_t lds_k[3 * kStreamThreads / kWave];
+  __shared__ uint32_t wsum[kStreamThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const FilterPartial *vp = part + row * gx;
+  uint32_t *ro = offs + row * (int64_t)(gx + 1);
+  // contiguous chunk of blocks per thread, so the offsets come out in order
+  const int per = (gx + kStreamThreads - 1) / kStreamThreads;
+  const int b0 = threadIdx.x * per;
+  double a = 0.0, b = 0.0;
+  unsigned long long c0 = 0, c1 = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, csum = 0u, big = 0u;
+  for (int i = 0; i < per; ++i) {
+    const int j = b0 + i;
+    if (j < gx) {
+      const FilterPartial fp = vp[j];
+      a += fp.sl;
+      b += fp.sr;
+      c0 += fp.cl;
+      c1 += fp.cr;
+      mn = min(mn, fp.kmn);
+      mx = max(mx, fp.kmx);
+      csum += fp.cnt;
+      big |= fp.cnt > (uint32_t)kBandSlot ? 1u : 0u;
     }
-    __threadfence();
-    const unsigned prev = atomicAdd(&S.ticket, 1u);
-    is_last = (prev == (unsigned)gx - 1u);
+  }
+  // exclusive scan of the chunk sums
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  uint32_t inc = csum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = 0u, total = 0u;
+  for (int i = 0; i < kStreamThreads / kWave; ++i) {
+    if (i < w) before += wsum[i];
+    total += wsum[i];
+  }
+  uint32_t run = before + inc - csum;
+  for (int i = 0; i < per; ++i) {
+    const int j = b0 + i;
+    if (j < gx) {
+      ro[j] = run;
+      run += vp[j].cnt;
+    }
+  }
+  if (threadIdx.x == kStreamThreads - 1) ro[gx] = total;
+#pragma unroll
+  for (int msk = 1; msk < kWave; msk <<= 1) {
+    a += __shfl_xor(a, msk, kWave);
+    b += __shfl_xor(b, msk, kWave);
+    c0 += __shfl_xor(c0, msk, kWave);
+    c1 += __shfl_xor(c1, msk, kWave);
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, msk, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, msk, kWave));
+    big |= (uint32_t)__shfl_xor((int)big, msk, kWave);
+  }
+  if (lane == 0) {
+    lds_d[2 * w] = a;
+    lds_d[2 * w + 1] = b;
+    lds_c[2 * w] = c0;
+    lds_c[2 * w + 1] = c1;
+    lds_k[3 * w] = mn;
+    lds_k[3 * w + 1] = mx;
+    lds_k[3 * w + 2] = big;
   }
   __syncthreads();
-  if (!is_last) return;
   if (threadIdx.x == 0) {
-    __threadfence();
-    const volatile FilterPartial *vp = part + row * gx;
-    double a = 0.0, b = 0.0;
-    unsigned long long c0 = 0, c1 = 0;
-    for (int i = 0; i < gx; ++i) {
-      a += vp[i].sl;
-      b += vp[i].sr;
-      c0 += vp[i].cl;
-      c1 += vp[i].cr;
+    double ta = 0.0, tb = 0.0;
+    unsigned long long tc0 = 0, tc1 = 0;
+    uint32_t tmn = 0xFFFFFFFFu, tmx = 0u, tbig = 0u;
+    for (int i = 0; i < kStreamThreads / kWave; ++i) {
+      ta += lds_d[2 * i];
+      tb += lds_d[2 * i + 1];
+      tc0 += lds_c[2 * i];
+      tc1 += lds_c[2 * i + 1];
+      tmn = min(tmn, lds_k[3 * i]);
+      tmx = max(tmx, lds_k[3 * i + 1]);
+      tbig |= lds_k[3 * i + 2];
     }
-    S.tail_lo = a;
-    S.tail_hi = b;
-    S.count_lo = c0;
-    S.count_hi = c1;
-    S.ticket = 0u;
+    RowState &S = st[row];
+    S.tail_lo = ta;
+    S.tail_hi = tb;
+    S.count_lo = tc0;
+    S.count_hi = tc1;
+    S.band = total;
+    S.kmin = tmn;
+    S.kmax = tmx;
+    if (tbig || (int64_t)total > cap) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
   }
 }
 
@@ -407,11 +501,19 @@ int filter_grid_x(int64_t rows, int64_t n) {
 size_t filter_partial_bytes(int64_t rows, int grid_x) {
   return sizeof(FilterPartial) * (size_t)rows * (size_t)grid_x;
 }
+size_t band_slot_bytes(int64_t rows, int grid_x) {
+  return sizeof(uint32_t) * (size_t)rows * (size_t)grid_x * (size_t)kBandSlot;
+}
+size_t band_offs_bytes(int64_t rows, int grid_x) { return sizeof(uint32_t) * (size_t)rows * (size_t)(grid_x + 1); }
 
-hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *band,
-                         int64_t cap, void *partials, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(filter_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, band, cap,
+hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
+                         uint32_t *offs, int64_t cap, void *partials, int grid_x, hipStream_t s) {
+  hipLaunchKernelGGL(filter_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, slots,
                      reinterpret_cast<FilterPartial *>(partials), grid_x, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(filter_finalize_kernel, dim3((unsigned)rows), dim3(kStreamThreads), 0, s,
+                     reinterpret_cast<const FilterPartial *>(partials), grid_x, cap, st, offs);
   return hipGetLastError();
 }
 

@@ -505,10 +505,8 @@ struct RowState {
   double b;                 // threshold from the band solve or the fallback
   uint32_t kmin, kmax;      // key range of the band
   int32_t flags;
-  uint32_t ticket;          // last-block-done counter (filter / backward)
+  int32_t pad0;
   double dk;                // backward: dk in fp64
-  uint32_t ticket2;
-  int32_t pad;
 };
 
 }  // namespace lapsum

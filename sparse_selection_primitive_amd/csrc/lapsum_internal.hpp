@@ -19,14 +19,19 @@ constexpr int kTile = 4096;          // keys per tile of the large-row sort and 
 constexpr int kSegThreads = 256;     // threads per workgroup of the large-row kernels
 constexpr int kSelectCap = 1024;     // direct-selection capacity of the bracket select
 constexpr int kStreamThreads = 256;  // threads per workgroup of the streaming kernels
+constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
+constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
-// Arguments of the cooperative large-row sort + threshold-curve + root kernel.
+// Arguments of the large-row sort + threshold-curve + root kernels.
 struct SegArgs {
   int mode;             // kSegFull, kSegBand or kSegFallback
   int rows;
   int64_t n;            // row length (full rows / fallback)
   const float *r;       // [rows][n] scores (full rows / fallback)
-  const uint32_t *band; // [rows][stride] raw band keys (band mode)
+  uint32_t *band;       // [rows][stride] raw band keys, compacted from the slots (band mode)
+  const uint32_t *slots; // [rows][gx][kBandSlot] band keys per filter workgroup (band mode)
+  const uint32_t *offs;  // [rows][gx + 1] slot offsets (band mode)
+  int gx;               // filter workgroups per row (band mode)
   uint32_t *A, *B;      // [rows][stride] key ping-pong buffers
   int64_t stride;       // per-row stride of band/A/B, a multiple of kTile
   int max_tiles;        // stride / kTile
@@ -53,13 +58,16 @@ hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int6
                          float *samples, hipStream_t s);
 hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
                          hipStream_t s);
-hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *band,
-                         int64_t cap, void *partials, int grid_x, hipStream_t s);
+hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
+                         uint32_t *offs, int64_t cap, void *partials, int grid_x, hipStream_t s);
 int filter_grid_x(int64_t rows, int64_t n);
 size_t filter_partial_bytes(int64_t rows, int grid_x);
-hipError_t launch_band_onchip(const uint32_t *band, int64_t rows, int64_t cap, RowState *st, double k, double t,
-                              hipStream_t s);
+size_t band_slot_bytes(int64_t rows, int grid_x);
+size_t band_offs_bytes(int64_t rows, int grid_x);
+hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
+                              RowState *st, double k, double t, hipStream_t s);
 hipError_t launch_segment(const SegArgs &a, hipStream_t s);
+hipError_t launch_fallback(const SegArgs &a, hipStream_t s);
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
                         double *b, hipStream_t s);
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st,

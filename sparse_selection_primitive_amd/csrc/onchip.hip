@@ -225,28 +225,45 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
 }
 
 // ----------------------------------------------------------- band solve
-// One workgroup per row; the band (capacity <= NP) is read from the
-// workspace, sorted, and solved with the tail sums as boundary seeds.  The
-// result is certified: the root must lie inside [a_L, a_R).
+// One workgroup per row; the band (at most NP keys) is gathered from the
+// filter's per-workgroup slots, sorted, and solved with the tail sums as
+// boundary seeds.  The result is certified: the root must lie inside
+// [a_L, a_R), else the row goes to the full-sort fallback.
 template <int NP>
-__global__ __launch_bounds__(NP / 16) void band_solve_onchip(const uint32_t *__restrict__ band, int64_t cap,
+__global__ __launch_bounds__(NP / 16) void band_solve_onchip(const uint32_t *__restrict__ slots,
+                                                             const uint32_t *__restrict__ offs, int gx,
                                                              RowState *__restrict__ st, double k, double t) {
   constexpr int E = 16, LANES = NP / 16;
   __shared__ BlockTeamLds<LANES, E> lds;
+  __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
   BlockTeam<LANES, E> team(&lds);
   const int64_t row = blockIdx.x;
   RowState &S = st[row];
-  const unsigned long long M = S.band;
-  if (M > (unsigned long long)cap) {
-    if (threadIdx.x == 0) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
-    return;
-  }
-  const int m = (int)M;
+  if (S.flags & LAPSUM_FLAG_OVERFLOW) return;  // the finalize already routed the row to the fallback
+  const int m = (int)S.band;
+  const uint32_t *ro = offs + row * (int64_t)(gx + 1);
+  for (int i = threadIdx.x; i <= gx; i += LANES) soffs[i] = ro[i];
+  __syncthreads();
   const int base = team.lane * E;
+  // slot holding index `base`: the last b with soffs[b] <= base
+  int lo = 0, hi = gx - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)soffs[mid] <= base) lo = mid;
+    else hi = mid - 1;
+  }
+  int b = lo;
   uint32_t key[E];
-  const uint32_t *src = band + row * cap;
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (base + e < m) ? src[base + e] : 0xFFFFFFFFu;
+  for (int e = 0; e < E; ++e) {
+    const int j = base + e;
+    if (j < m) {
+      while ((int)soffs[b + 1] <= j) ++b;
+      key[e] = slots[((int64_t)row * gx + b) * kBandSlot + (j - (int)soffs[b])];
+    } else {
+      key[e] = 0xFFFFFFFFu;
+    }
+  }
   bitonic_sort<E>(key, team);
   const int nv = min(max(m - base, 0), E);
   float s[E];
@@ -261,24 +278,24 @@ __global__ __launch_bounds__(NP / 16) void band_solve_onchip(const uint32_t *__r
   part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
   part.first = true;
   part.last = true;
-  const double b = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
+  const double bb = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
   if (threadIdx.x == 0) {
-    S.b = b;
-    const bool hit = (b >= S.a_lo) && (b < S.a_hi);
+    S.b = bb;
+    const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
     S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
   }
 }
 
-hipError_t launch_band_onchip(const uint32_t *band, int64_t rows, int64_t cap, RowState *st, double k, double t,
-                              hipStream_t s) {
+hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
+                              RowState *st, double k, double t, hipStream_t s) {
   if (cap <= 1024)
-    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(64), 0, s, band, cap, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(64), 0, s, slots, offs, gx, st, k, t);
   else if (cap <= 2048)
-    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(128), 0, s, band, cap, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(128), 0, s, slots, offs, gx, st, k, t);
   else if (cap <= 4096)
-    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(256), 0, s, band, cap, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(256), 0, s, slots, offs, gx, st, k, t);
   else
-    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(512), 0, s, band, cap, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(512), 0, s, slots, offs, gx, st, k, t);
   return hipGetLastError();
 }
 

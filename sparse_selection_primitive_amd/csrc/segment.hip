@@ -1,30 +1,28 @@
 // Large-row full-sort solver ("Fast LapSum: Exact Differentiable Top-k at
-// Million Scale", section 2.2, full-sort solver) as one cooperative launch:
+// Million Scale", section 2.2, full-sort solver) for rows that do not fit one
+// workgroup's registers: the full-sort path, the compacted band of the
+// bracketing path, and the bracketing fallback.
 //
-//   for each 8-bit digit pass (least significant first):
-//     H: per-tile digit histograms                       (grid sync)
-//     S: per-digit exclusive scan over tiles            (grid sync)
-//     X: stable scatter: wave-ballot ranking, LDS stage,
-//        coalesced runs per digit                          (grid sync)
-//   C: per-tile anchored aggregates of the sorted keys  (grid sync)
-//   L: per row, scan of the tile aggregates (with the bracket's tail sums as
-//      boundary seeds), threshold curve at tile ends, locate of the
-//      balancing tile, per-knot curve inside it, closed-form root,
-//      certification against the bracket.
+//   sort:  least-significant-digit radix sort of the order-preserving keys,
+//          8-bit digits; per pass a tile histogram, a per-digit scan over
+//          tiles, and a stable scatter (wave-ballot ranking inside the tile,
+//          LDS staging, coalesced runs per digit);
+//   curve: per-tile anchored aggregates of the sorted keys, then per row a
+//          scan of the tile aggregates (seeded with the bracket's tail sums),
+//          the threshold curve at tile ends, the balancing tile, the curve at
+//          every knot inside it, and the closed-form root.
 //
-// Modes: full rows (the full-sort path), the compacted band of the
-// bracketing path (keys offset by the band's minimum key so that only the
-// needed digit passes run), and the deterministic fallback, which sorts the
-// whole row only for rows whose bracket missed (and returns at once when
-// none did).  Tiles hold 4096 keys (256 threads x 16).
-#include <hip/hip_cooperative_groups.h>
-
+// Full-sort rows and the band run one regular launch per phase (a kernel
+// boundary is the cheapest grid-wide synchronisation on this GPU, far below
+// a cooperative launch or an in-kernel grid barrier).  The fallback runs as a
+// single launch with one workgroup per row that sorts and solves the whole
+// row by itself: when every bracket held it returns at once, which keeps the
+// common case to one short launch; on a miss it is slower but exact and
+// deterministic.
 #include "lapsum_device.hpp"
 #include "lapsum_internal.hpp"
 
 namespace lapsum {
-
-namespace cg = cooperative_groups;
 
 struct TileAgg {
   float aP, aS;
@@ -34,26 +32,30 @@ size_t tile_agg_bytes() { return sizeof(TileAgg); }
 size_t pre_bytes() { return sizeof(Pre); }
 size_t suf_bytes() { return sizeof(Suf); }
 
-constexpr int kKpt = kTile / kSegThreads;  // 16 keys per thread
-constexpr int kSegWaves = kSegThreads / kWave;
+constexpr int kKpt = 16;  // keys per thread in a tile
 
-struct ScatterLds {
-  uint32_t stage[kTile];
-  uint32_t wcnt[kSegWaves][256];
+template <int NT>
+struct RankLds {
+  static constexpr int NW = NT / kWave;
+  uint32_t stage[NT * kKpt];
+  uint32_t wcnt[NW][256];
   uint32_t tstart[256];
   uint32_t dglob[256];
-  uint32_t wsum[kSegWaves];
-};
-union SegLds {
-  ScatterLds sc;
-  BlockTeamLds<kSegThreads, 1> tm;
+  uint32_t wsum[NW];
 };
 
+template <int NT>
+union SegLds {
+  RankLds<NT> rk;
+  BlockTeamLds<NT, 1> tm;
+};
+
+// ------------------------------------------------------------- row helpers
 LDEV bool seg_active(const SegArgs &a, int row) {
   const RowState &s = a.st[row];
   if (a.mode == kSegFull) return true;
   if (a.mode == kSegFallback) return (s.flags & LAPSUM_FLAG_FALLBACK) != 0;
-  return s.band <= (unsigned long long)a.stride;
+  return !(s.flags & LAPSUM_FLAG_OVERFLOW) && s.band <= (unsigned long long)a.stride;
 }
 LDEV int64_t seg_len(const SegArgs &a, int row) {
   if (!seg_active(a, row)) return 0;
@@ -65,9 +67,20 @@ LDEV uint32_t seg_kbase(const SegArgs &a, int row) {
   const RowState &s = a.st[row];
   return s.band > 0 ? s.kmin : 0u;
 }
+// digit passes this row needs: the band sorts key - kmin, so only the digits
+// spanned by its key range
+LDEV int seg_npasses(const SegArgs &a, int row) {
+  if (a.mode != kSegBand) return 4;
+  const RowState &s = a.st[row];
+  const uint32_t span = (s.band > 1 && s.kmax > s.kmin) ? s.kmax - s.kmin : 0u;
+  const int bits = span == 0u ? 1 : 32 - __clz((int)span);
+  return (bits + 7) / 8;
+}
+LDEV const uint32_t *seg_final(const SegArgs &a, int row) { return (seg_npasses(a, row) & 1) ? a.A : a.B; }
 
-// exclusive scan of one uint32 per thread over the workgroup
+template <int NT>
 LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   uint32_t inc = v;
 #pragma unroll
@@ -80,11 +93,12 @@ LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
   __syncthreads();
   uint32_t before = 0;
 #pragma unroll
-  for (int i = 0; i < kSegWaves; ++i)
+  for (int i = 0; i < NW; ++i)
     if (i < w) before += wsum[i];
   return before + inc - v;
 }
 
+// key of element i of `row` read by digit pass `pass`
 LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i, uint32_t kbase) {
   if (pass == 0) {
     if (a.mode == kSegBand) return a.band[(int64_t)row * a.stride + i] - kbase;
@@ -93,138 +107,93 @@ LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i, uint32_t 
   const uint32_t *src = (pass & 1) ? a.A : a.B;
   return src[(int64_t)row * a.stride + i];
 }
+LDEV uint32_t *pass_dst(const SegArgs &a, int pass) { return (pass & 1) ? a.B : a.A; }
 
-LDEV void phase_hist(const SegArgs &a, int pass, SegLds &L) {
-  const int shift = 8 * pass;
-  uint32_t *h = L.sc.wcnt[0];  // 256 counters
-  const int64_t items = (int64_t)a.rows * a.max_tiles;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int row = (int)(it / a.max_tiles), tile = (int)(it % a.max_tiles);
-    const int64_t len = seg_len(a, row);
-    const int64_t nt = (len + kTile - 1) / kTile;
-    if (tile >= nt) continue;
-    const uint32_t kbase = seg_kbase(a, row);
-    h[threadIdx.x] = 0u;
-    __syncthreads();
-    for (int q = 0; q < kKpt; ++q) {
-      const int64_t gi = (int64_t)tile * kTile + q * kSegThreads + threadIdx.x;
-      if (gi < len) atomicAdd(&h[(load_key(a, pass, row, gi, kbase) >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    a.hist[((int64_t)row * 256 + threadIdx.x) * a.max_tiles + tile] = h[threadIdx.x];
-    __syncthreads();
-  }
-}
-
-LDEV void phase_scan_digits(const SegArgs &a) {
+// ----------------------------------------------------------- tile routines
+// Keys of one tile, wave-striped: thread (w, lane) holds tile positions
+// w*64*16 + q*64 + lane, q = 0..15, which is also their stable order.
+template <int NT>
+LDEV void load_tile(const SegArgs &a, int pass, int row, int64_t t0, int64_t len, uint32_t kbase, int shift,
+                    uint32_t (&key)[kKpt], int (&dig)[kKpt]) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int64_t items = (int64_t)a.rows * 256;
-  for (int64_t it = (int64_t)blockIdx.x * kSegWaves + w; it < items; it += (int64_t)gridDim.x * kSegWaves) {
-    const int row = (int)(it >> 8), d = (int)(it & 255);
-    const int64_t len = seg_len(a, row);
-    const int nt = (int)((len + kTile - 1) / kTile);
-    if (nt == 0) continue;
-    uint32_t *h = a.hist + ((int64_t)row * 256 + d) * a.max_tiles;
-    uint32_t carry = 0;
-    for (int base = 0; base < nt; base += kWave) {
-      const int i = base + lane;
-      const uint32_t v = i < nt ? h[i] : 0u;
-      uint32_t inc = v;
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += y;
-      }
-      if (i < nt) h[i] = carry + inc - v;
-      carry += __shfl(inc, kWave - 1, kWave);
-    }
-    if (lane == 0) a.dtot[(int64_t)row * 256 + d] = carry;
+  for (int q = 0; q < kKpt; ++q) {
+    const int64_t gi = t0 + w * (kWave * kKpt) + q * kWave + lane;
+    const bool valid = gi < len;
+    key[q] = valid ? load_key(a, pass, row, gi, kbase) : 0u;
+    dig[q] = valid ? (int)((key[q] >> shift) & 255u) : 256;
   }
 }
 
-LDEV void phase_scatter(const SegArgs &a, int pass, SegLds &L) {
-  const int shift = 8 * pass;
+// Stable scatter of one tile.  Thread d < 256 passes in `digit_base`, the
+// position in `dst` where this tile's keys of digit d start; it gets back the
+// number of this tile's keys of digit d.
+template <int NT>
+LDEV uint32_t scatter_tile(const uint32_t (&key)[kKpt], const int (&dig)[kKpt], int shift, int vc,
+                           uint32_t digit_base, uint32_t *dst, RankLds<NT> &L) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const unsigned long long ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t *dst = (pass & 1) ? a.B : a.A;
-  const int64_t items = (int64_t)a.rows * a.max_tiles;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int row = (int)(it / a.max_tiles), tile = (int)(it % a.max_tiles);
-    const int64_t len = seg_len(a, row);
-    const int64_t nt = (len + kTile - 1) / kTile;
-    if (tile >= nt) continue;
-    const uint32_t kbase = seg_kbase(a, row);
-
-    uint32_t key[kKpt], rnk[kKpt];
-    int dig[kKpt];
+  volatile uint32_t *wc = L.wcnt[w];
 #pragma unroll
-    for (int q = 0; q < kKpt; ++q) {
-      const int64_t gi = (int64_t)tile * kTile + w * (kWave * kKpt) + q * kWave + lane;
-      const bool valid = gi < len;
-      key[q] = valid ? load_key(a, pass, row, gi, kbase) : 0u;
-      dig[q] = valid ? (int)((key[q] >> shift) & 255u) : 256;
+  for (int i = 0; i < 256 / kWave; ++i) wc[lane + i * kWave] = 0u;
+  __syncthreads();
+  // rank within the wave's chunk, round by round: peers with the same digit
+  // by 8 ballots, one LDS read-modify-write per digit group
+  uint32_t rnk[kKpt];
+#pragma unroll
+  for (int q = 0; q < kKpt; ++q) {
+    const int d = dig[q];
+    const bool valid = d < 256;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (d >> bit) & 1;
+      const unsigned long long bb = __ballot(set);
+      peers &= set ? bb : ~bb;
     }
-    // global start of each digit in this row, and this tile's offset within it
-    const uint32_t dtot = a.dtot[(int64_t)row * 256 + threadIdx.x];
-    const uint32_t dbase = wg_excl_scan(dtot, L.sc.wsum);
-    const uint32_t tofs = a.hist[((int64_t)row * 256 + threadIdx.x) * a.max_tiles + tile];
-    volatile uint32_t *wc = L.sc.wcnt[w];
-#pragma unroll
-    for (int i = 0; i < 256 / kWave; ++i) wc[lane + i * kWave] = 0u;
-    __syncthreads();
-    // stable rank within the wave's chunk, round by round
-#pragma unroll
-    for (int q = 0; q < kKpt; ++q) {
-      const int d = dig[q];
-      const bool valid = d < 256;
-      unsigned long long peers = __ballot(valid);
-#pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
-        const bool set = (d >> bit) & 1;
-        const unsigned long long bb = __ballot(set);
-        peers &= set ? bb : ~bb;
-      }
-      const uint32_t lt = (uint32_t)__popcll(peers & ltmask);
-      uint32_t prev = 0u;
-      if (valid) prev = wc[d];
-      rnk[q] = prev + lt;
-      if (valid && lt == 0u) wc[d] = prev + (uint32_t)__popcll(peers);
-    }
-    __syncthreads();
-    {
-      const int d = threadIdx.x;
-      uint32_t run = 0u;
-#pragma unroll
-      for (int ww = 0; ww < kSegWaves; ++ww) {
-        const uint32_t c = L.sc.wcnt[ww][d];
-        L.sc.wcnt[ww][d] = run;
-        run += c;
-      }
-      const uint32_t ts = wg_excl_scan(run, L.sc.wsum);
-      L.sc.tstart[d] = ts;
-      L.sc.dglob[d] = dbase + tofs - ts;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kKpt; ++q) {
-      const int d = dig[q];
-      if (d < 256) L.sc.stage[L.sc.tstart[d] + L.sc.wcnt[w][d] + rnk[q]] = key[q];
-    }
-    __syncthreads();
-    const int vc = (int)min((int64_t)kTile, len - (int64_t)tile * kTile);
-    uint32_t *drow = dst + (int64_t)row * a.stride;
-    for (int i = threadIdx.x; i < vc; i += kSegThreads) {
-      const uint32_t kk = L.sc.stage[i];
-      drow[L.sc.dglob[(kk >> shift) & 255u] + i] = kk;
-    }
-    __syncthreads();
+    const uint32_t lt = (uint32_t)__popcll(peers & ltmask);
+    uint32_t prev = 0u;
+    if (valid) prev = wc[d];
+    rnk[q] = prev + lt;
+    if (valid && lt == 0u) wc[d] = prev + (uint32_t)__popcll(peers);
   }
+  __syncthreads();
+  const int d = threadIdx.x;
+  uint32_t tcount = 0u;
+  if (d < 256) {
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const uint32_t c = L.wcnt[ww][d];
+      L.wcnt[ww][d] = tcount;
+      tcount += c;
+    }
+  }
+  const uint32_t ts = wg_excl_scan<NT>(d < 256 ? tcount : 0u, L.wsum);
+  if (d < 256) {
+    L.tstart[d] = ts;
+    L.dglob[d] = digit_base - ts;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kKpt; ++q) {
+    const int dq = dig[q];
+    if (dq < 256) L.stage[L.tstart[dq] + L.wcnt[w][dq] + rnk[q]] = key[q];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < vc; i += NT) {
+    const uint32_t kk = L.stage[i];
+    dst[L.dglob[(kk >> shift) & 255u] + i] = kk;
+  }
+  __syncthreads();
+  return tcount;
 }
 
-// sorted tile -> values (blocked, 16 per thread)
-LDEV int load_sorted_tile(const SegArgs &a, const uint32_t *fin, int row, int tile, int64_t len, uint32_t kbase,
-                          float (&s)[kKpt]) {
-  const int64_t base = (int64_t)tile * kTile + (int64_t)threadIdx.x * kKpt;
+// Sorted keys t0 .. t0 + NT*16 of `fin` as values, blocked (16 per thread).
+template <int NT>
+LDEV int load_sorted(const SegArgs &a, const uint32_t *fin, int row, int64_t t0, int64_t len, uint32_t kbase,
+                     float (&s)[kKpt]) {
+  const int64_t base = t0 + (int64_t)threadIdx.x * kKpt;
   const int nv = (int)min(max(len - base, (int64_t)0), (int64_t)kKpt);
   const uint32_t *src = fin + (int64_t)row * a.stride + base;
 #pragma unroll
@@ -232,184 +201,279 @@ LDEV int load_sorted_tile(const SegArgs &a, const uint32_t *fin, int row, int ti
   return nv;
 }
 
-LDEV void phase_tiles(const SegArgs &a, const uint32_t *fin, SegLds &L) {
-  BlockTeam<kSegThreads, 1> team(&L.tm);
-  const int64_t items = (int64_t)a.rows * a.max_tiles;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int row = (int)(it / a.max_tiles), tile = (int)(it % a.max_tiles);
-    const int64_t len = seg_len(a, row);
-    const int64_t nt = (len + kTile - 1) / kTile;
-    if (tile >= nt) continue;
-    float s[kKpt];
-    const int nv = load_sorted_tile(a, fin, row, tile, len, seg_kbase(a, row), s);
-    float mul[kKpt];
-    mul[0] = 0.0f;
+// Anchored aggregates of one sorted tile: P-type relative to its last key,
+// S-type relative to its first key.
+template <int NT>
+LDEV void tile_aggregate(const float (&s)[kKpt], int nv, double c, float cf, const BlockTeam<NT, 1> &team,
+                         TileAgg *out) {
+  float mul[kKpt];
+  mul[0] = 0.0f;
 #pragma unroll
-    for (int e = 1; e < kKpt; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], a.cf) : 0.0f;
-    double pl = 0.0, sl = 0.0;
-    float last = s[0];
+  for (int e = 1; e < kKpt; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], cf) : 0.0f;
+  double pl = 0.0, sl = 0.0;
+  float last = s[0];
 #pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if (e < nv) {
-        pl = pl * (double)mul[e] + 1.0;
-        last = s[e];
-      }
-#pragma unroll
-    for (int e = kKpt - 1; e >= 0; --e)
-      if (e < nv) sl = (e + 1 < kKpt ? sl * (double)mul[e + 1] : 0.0) + 1.0;
-    const Pre mp{last, nv > 0 ? pl : 0.0};
-    const Suf ms{s[0], nv > 0 ? sl : 0.0};
-    const Pre ep = team.excl_scan(mp, a.c);
-    const Suf es = team.excl_scan(ms, a.c);
-    TileAgg *ta = a.tagg + (int64_t)row * a.max_tiles + tile;
-    if (threadIdx.x == kSegThreads - 1) {
-      const Pre tp = join(ep, mp, a.c);
-      ta->aP = tp.a;
-      ta->sP = tp.s;
+  for (int e = 0; e < kKpt; ++e)
+    if (e < nv) {
+      pl = pl * (double)mul[e] + 1.0;
+      last = s[e];
     }
-    if (threadIdx.x == 0) {
-      const Suf ts = join(ms, es, a.c);
-      ta->aS = ts.a;
-      ta->sS = ts.s;
-    }
-    __syncthreads();
+#pragma unroll
+  for (int e = kKpt - 1; e >= 0; --e)
+    if (e < nv) sl = (e + 1 < kKpt ? sl * (double)mul[e + 1] : 0.0) + 1.0;
+  const Pre mp{last, nv > 0 ? pl : 0.0};
+  const Suf ms{s[0], nv > 0 ? sl : 0.0};
+  const Pre ep = team.excl_scan(mp, c);
+  const Suf es = team.excl_scan(ms, c);
+  if (threadIdx.x == NT - 1) {
+    const Pre tp = join(ep, mp, c);
+    out->aP = tp.a;
+    out->sP = tp.s;
   }
+  if (threadIdx.x == 0) {
+    const Suf tsf = join(ms, es, c);
+    out->aS = tsf.a;
+    out->sS = tsf.s;
+  }
+  __syncthreads();
 }
 
-LDEV void phase_locate(const SegArgs &a, const uint32_t *fin, SegLds &L) {
-  BlockTeam<kSegThreads, 1> team(&L.tm);
-  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    RowState &S = a.st[row];
-    if (a.mode == kSegBand && S.band > (unsigned long long)a.stride) {
-      if (threadIdx.x == 0) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
-      continue;
-    }
-    if (!seg_active(a, row)) continue;
-    const int64_t len = seg_len(a, row);
-    const int nt = (int)((len + kTile - 1) / kTile);
-    const bool band = a.mode == kSegBand;
-    const Pre seed_lo{(float)S.a_lo, (band && S.count_lo) ? S.tail_lo : 0.0};
-    const Suf seed_hi{(float)S.a_hi, (band && S.count_hi) ? S.tail_hi : 0.0};
-    const double cR = band ? (double)S.count_hi : 0.0;
-    const TileAgg *ta = a.tagg + (int64_t)row * a.max_tiles;
-    Pre *tp = a.tpre + (int64_t)row * a.max_tiles;
-    Suf *ts = a.tsuf + (int64_t)row * a.max_tiles;
+// Per row: scan of the tile aggregates, threshold curve at the tile ends,
+// the balancing tile, and the closed-form root inside it (tiles of NT*16).
+template <int NT>
+LDEV void locate_row(const SegArgs &a, int row, const uint32_t *fin, const BlockTeam<NT, 1> &team) {
+  constexpr int TT = NT * kKpt;
+  RowState &S = a.st[row];
+  const int64_t len = seg_len(a, row);
+  const int nt = (int)((len + TT - 1) / TT);
+  const bool band = a.mode == kSegBand;
+  const Pre seed_lo{(float)S.a_lo, (band && S.count_lo) ? S.tail_lo : 0.0};
+  const Suf seed_hi{(float)S.a_hi, (band && S.count_hi) ? S.tail_hi : 0.0};
+  const double cR = band ? (double)S.count_hi : 0.0;
+  const TileAgg *ta = a.tagg + (int64_t)row * a.max_tiles;
+  Pre *tp = a.tpre + (int64_t)row * a.max_tiles;
+  Suf *ts = a.tsuf + (int64_t)row * a.max_tiles;
 
-    Pre carry = seed_lo;
-    for (int T0 = 0; T0 < nt; T0 += kSegThreads) {
-      const int T = T0 + threadIdx.x;
-      const Pre mine = T < nt ? Pre{ta[T].aP, ta[T].sP} : Pre{0.0f, 0.0};
-      const Pre ex = team.excl_scan(mine, a.c);
-      if (T < nt) tp[T] = join(carry, ex, a.c);
-      const Pre tot = join(ex, mine, a.c);
-      const Pre chunk{team.bcast(tot.a, kSegThreads - 1), team.bcast(tot.s, kSegThreads - 1)};
-      carry = join(carry, chunk, a.c);
-    }
-    Suf carry_s = seed_hi;
-    for (int T0 = ((nt - 1) / kSegThreads) * kSegThreads; nt > 0 && T0 >= 0; T0 -= kSegThreads) {
-      const int T = T0 + threadIdx.x;
-      const Suf mine = T < nt ? Suf{ta[T].aS, ta[T].sS} : Suf{0.0f, 0.0};
-      const Suf ex = team.excl_scan(mine, a.c);
-      if (T < nt) ts[T] = join(ex, carry_s, a.c);
-      const Suf tot = join(mine, ex, a.c);
-      const Suf chunk{team.bcast(tot.a, 0), team.bcast(tot.s, 0)};
-      carry_s = join(chunk, carry_s, a.c);
-    }
-    __syncthreads();
-    // threshold curve at the last knot of every tile
-    int cnt = 0;
-    for (int T = threadIdx.x; T < nt; T += kSegThreads) {
-      const Pre pl = join(tp[T], Pre{ta[T].aP, ta[T].sP}, a.c);
-      const Suf sa = ts[T];
-      const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, a.c));
-      const int64_t nvT = min((int64_t)kTile, len - (int64_t)T * kTile);
-      const int64_t j_last = (int64_t)T * kTile + nvT - 1;
-      const double g = 0.5 * (pl.s - 1.0) + ((double)(len - j_last) + cR) - 0.5 * s_last;
-      cnt += (g >= a.k) ? 1 : 0;
-    }
-    const int tstar = team.sum(cnt);
-    const int tsel = nt == 0 ? 0 : min(tstar, nt - 1);
-    float s[kKpt];
-    int nv = 0;
-    if (nt > 0) nv = load_sorted_tile(a, fin, row, tsel, len, seg_kbase(a, row), s);
-    else {
-#pragma unroll
-      for (int e = 0; e < kKpt; ++e) s[e] = 0.0f;
-    }
-    PartInfo part;
-    part.nvalid = nv;
-    part.above = (double)(len - (int64_t)tsel * kTile) + cR;
-    part.seed_lo = nt > 0 ? tp[tsel] : seed_lo;
-    part.seed_hi = nt > 0 ? ts[tsel] : seed_hi;
-    part.first = tsel == 0;
-    part.last = tsel >= nt - 1;
-    const double b = segment_solve<kKpt>(s, nv, part, a.k, a.t, a.c, a.cf, team);
-    if (threadIdx.x == 0) {
-      S.b = b;
-      if (band) {
-        const bool hit = (b >= S.a_lo) && (b < S.a_hi);
-        S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
-      }
-    }
-    __syncthreads();
+  Pre carry = seed_lo;
+  for (int T0 = 0; T0 < nt; T0 += NT) {
+    const int T = T0 + threadIdx.x;
+    const Pre mine = T < nt ? Pre{ta[T].aP, ta[T].sP} : Pre{0.0f, 0.0};
+    const Pre ex = team.excl_scan(mine, a.c);
+    if (T < nt) tp[T] = join(carry, ex, a.c);
+    const Pre tot = join(ex, mine, a.c);
+    const Pre chunk{team.bcast(tot.a, NT - 1), team.bcast(tot.s, NT - 1)};
+    carry = join(carry, chunk, a.c);
   }
+  Suf carry_s = seed_hi;
+  for (int T0 = ((nt - 1) / NT) * NT; nt > 0 && T0 >= 0; T0 -= NT) {
+    const int T = T0 + threadIdx.x;
+    const Suf mine = T < nt ? Suf{ta[T].aS, ta[T].sS} : Suf{0.0f, 0.0};
+    const Suf ex = team.excl_scan(mine, a.c);
+    if (T < nt) ts[T] = join(ex, carry_s, a.c);
+    const Suf tot = join(mine, ex, a.c);
+    const Suf chunk{team.bcast(tot.a, 0), team.bcast(tot.s, 0)};
+    carry_s = join(chunk, carry_s, a.c);
+  }
+  __syncthreads();
+  // threshold curve at the last knot of every tile
+  int cnt = 0;
+  for (int T = threadIdx.x; T < nt; T += NT) {
+    const Pre pl = join(tp[T], Pre{ta[T].aP, ta[T].sP}, a.c);
+    const Suf sa = ts[T];
+    const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, a.c));
+    const int64_t nvT = min((int64_t)TT, len - (int64_t)T * TT);
+    const int64_t j_last = (int64_t)T * TT + nvT - 1;
+    const double g = 0.5 * (pl.s - 1.0) + ((double)(len - j_last) + cR) - 0.5 * s_last;
+    cnt += (g >= a.k) ? 1 : 0;
+  }
+  const int tstar = team.sum(cnt);
+  const int tsel = nt == 0 ? 0 : min(tstar, nt - 1);
+  float s[kKpt];
+  int nv = 0;
+  if (nt > 0) {
+    nv = load_sorted<NT>(a, fin, row, (int64_t)tsel * TT, len, seg_kbase(a, row), s);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) s[e] = 0.0f;
+  }
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)(len - (int64_t)tsel * TT) + cR;
+  part.seed_lo = nt > 0 ? tp[tsel] : seed_lo;
+  part.seed_hi = nt > 0 ? ts[tsel] : seed_hi;
+  part.first = tsel == 0;
+  part.last = tsel >= nt - 1;
+  const double b = segment_solve<kKpt>(s, nv, part, a.k, a.t, a.c, a.cf, team);
+  if (threadIdx.x == 0) {
+    S.b = b;
+    if (band) {
+      const bool hit = (b >= S.a_lo) && (b < S.a_hi);
+      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+    }
+  }
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(kSegThreads) void segment_kernel(SegArgs a) {
-  __shared__ SegLds L;
-  // uniform early exit (every workgroup reads the same state)
-  int npasses = 4;
-  if (a.mode == kSegFallback) {
-    bool any = false;
-    for (int row = 0; row < a.rows; ++row) any |= (a.st[row].flags & LAPSUM_FLAG_FALLBACK) != 0;
-    if (!any) return;
-  } else if (a.mode == kSegBand) {
-    uint32_t span = 0u;
-    for (int row = 0; row < a.rows; ++row) {
-      const RowState &s = a.st[row];
-      if (s.band > 1 && s.band <= (unsigned long long)a.stride && s.kmax > s.kmin) span = max(span, s.kmax - s.kmin);
+// --------------------------------------------- multi-launch kernels (256)
+constexpr int kNT = kSegThreads;
+
+// band: gather the filter's per-workgroup slots into the contiguous band
+__global__ __launch_bounds__(kNT) void seg_compact_kernel(SegArgs a) {
+  const int row = blockIdx.y, b = blockIdx.x;
+  if (!seg_active(a, row)) return;
+  const uint32_t *ro = a.offs + (int64_t)row * (a.gx + 1);
+  const uint32_t o0 = ro[b], cnt = ro[b + 1] - o0;
+  const uint32_t *src = a.slots + ((int64_t)row * a.gx + b) * kBandSlot;
+  uint32_t *dst = a.band + (int64_t)row * a.stride + o0;
+  for (uint32_t i = threadIdx.x; i < cnt; i += kNT) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kNT) void seg_hist_kernel(SegArgs a, int pass) {
+  __shared__ uint32_t h[256];
+  const int row = blockIdx.y, tile = blockIdx.x;
+  if (pass >= seg_npasses(a, row)) return;
+  const int64_t len = seg_len(a, row);
+  if ((int64_t)tile * kTile >= len) return;
+  const int shift = 8 * pass;
+  const uint32_t kbase = seg_kbase(a, row);
+  h[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int q = 0; q < kKpt; ++q) {
+    const int64_t gi = (int64_t)tile * kTile + q * kNT + threadIdx.x;
+    if (gi < len) atomicAdd(&h[(load_key(a, pass, row, gi, kbase) >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  a.hist[((int64_t)row * 256 + threadIdx.x) * a.max_tiles + tile] = h[threadIdx.x];
+}
+
+// one wave per (row, digit): exclusive scan over the row's tiles, in place
+__global__ __launch_bounds__(kNT) void seg_scan_kernel(SegArgs a, int pass) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int row = blockIdx.y, d = blockIdx.x * (kNT / kWave) + w;
+  if (pass >= seg_npasses(a, row)) return;
+  const int64_t len = seg_len(a, row);
+  const int nt = (int)((len + kTile - 1) / kTile);
+  if (nt == 0) return;
+  uint32_t *h = a.hist + ((int64_t)row * 256 + d) * a.max_tiles;
+  uint32_t carry = 0;
+  for (int base = 0; base < nt; base += kWave) {
+    const int i = base + lane;
+    const uint32_t v = i < nt ? h[i] : 0u;
+    uint32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t y = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += y;
     }
-    const int bits = span == 0u ? 1 : 32 - __clz((int)span);
-    npasses = (bits + 7) / 8;
+    if (i < nt) h[i] = carry + inc - v;
+    carry += __shfl(inc, kWave - 1, kWave);
   }
-  cg::grid_group grid = cg::this_grid();
-  for (int pass = 0; pass < npasses; ++pass) {
-    phase_hist(a, pass, L);
-    grid.sync();
-    phase_scan_digits(a);
-    grid.sync();
-    phase_scatter(a, pass, L);
-    grid.sync();
+  if (lane == 0) a.dtot[(int64_t)row * 256 + d] = carry;
+}
+
+__global__ __launch_bounds__(kNT) void seg_scatter_kernel(SegArgs a, int pass) {
+  __shared__ RankLds<kNT> L;
+  const int row = blockIdx.y, tile = blockIdx.x;
+  if (pass >= seg_npasses(a, row)) return;
+  const int64_t len = seg_len(a, row);
+  if ((int64_t)tile * kTile >= len) return;
+  const int shift = 8 * pass;
+  uint32_t key[kKpt];
+  int dig[kKpt];
+  load_tile<kNT>(a, pass, row, (int64_t)tile * kTile, len, seg_kbase(a, row), shift, key, dig);
+  // global start of each digit in this row, plus this tile's offset within it
+  const uint32_t dtot = a.dtot[(int64_t)row * 256 + threadIdx.x];
+  const uint32_t dbase = wg_excl_scan<kNT>(dtot, L.wsum);
+  const uint32_t tofs = a.hist[((int64_t)row * 256 + threadIdx.x) * a.max_tiles + tile];
+  const int vc = (int)min((int64_t)kTile, len - (int64_t)tile * kTile);
+  scatter_tile<kNT>(key, dig, shift, vc, dbase + tofs, pass_dst(a, pass) + (int64_t)row * a.stride, L);
+}
+
+__global__ __launch_bounds__(kNT) void seg_tiles_kernel(SegArgs a) {
+  __shared__ BlockTeamLds<kNT, 1> lds;
+  BlockTeam<kNT, 1> team(&lds);
+  const int row = blockIdx.y, tile = blockIdx.x;
+  const int64_t len = seg_len(a, row);
+  if ((int64_t)tile * kTile >= len) return;
+  float s[kKpt];
+  const int nv = load_sorted<kNT>(a, seg_final(a, row), row, (int64_t)tile * kTile, len, seg_kbase(a, row), s);
+  tile_aggregate<kNT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
+}
+
+__global__ __launch_bounds__(kNT) void seg_locate_kernel(SegArgs a) {
+  __shared__ BlockTeamLds<kNT, 1> lds;
+  BlockTeam<kNT, 1> team(&lds);
+  const int row = blockIdx.x;
+  RowState &S = a.st[row];
+  if (a.mode == kSegBand && ((S.flags & LAPSUM_FLAG_OVERFLOW) || S.band > (unsigned long long)a.stride)) {
+    if (threadIdx.x == 0) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
+    return;
   }
-  const uint32_t *fin = (npasses & 1) ? a.A : a.B;
-  phase_tiles(a, fin, L);
-  grid.sync();
-  phase_locate(a, fin, L);
+  if (!seg_active(a, row)) return;
+  locate_row<kNT>(a, row, seg_final(a, row), team);
 }
 
 hipError_t launch_segment(const SegArgs &a, hipStream_t s) {
-  static int cached_dev = -1, max_blocks = 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (cached_dev != dev) {
-    int cus = 0, per_cu = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const dim3 tiles((unsigned)a.max_tiles, (unsigned)a.rows);
+  if (a.mode == kSegBand) {
+    hipLaunchKernelGGL(seg_compact_kernel, dim3((unsigned)a.gx, (unsigned)a.rows), dim3(kNT), 0, s, a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, segment_kernel, kSegThreads, 0);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1) return hipErrorInvalidConfiguration;
-    max_blocks = cus * (per_cu < 4 ? per_cu : 4);
-    cached_dev = dev;
   }
-  int64_t need = (int64_t)a.rows * a.max_tiles;
-  const int64_t scan_need = ((int64_t)a.rows * 256 + kSegWaves - 1) / kSegWaves;
-  if (scan_need > need) need = scan_need;
-  if ((int64_t)a.rows > need) need = a.rows;
-  const int grid = (int)(need < max_blocks ? need : max_blocks);
-  SegArgs copy = a;
-  void *args[] = {(void *)&copy};
-  return hipLaunchCooperativeKernel((const void *)segment_kernel, dim3(grid), dim3(kSegThreads), args, 0, s);
+  for (int pass = 0; pass < 4; ++pass) {
+    hipLaunchKernelGGL(seg_hist_kernel, tiles, dim3(kNT), 0, s, a, pass);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(256 / (kNT / kWave), (unsigned)a.rows), dim3(kNT), 0, s, a, pass);
+    hipLaunchKernelGGL(seg_scatter_kernel, tiles, dim3(kNT), 0, s, a, pass);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(seg_tiles_kernel, tiles, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(seg_locate_kernel, dim3((unsigned)a.rows), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------- fallback: one workgroup per row
+constexpr int kFbNT = 1024;
+constexpr int kFbTile = kFbNT * kKpt;
+
+__global__ __launch_bounds__(kFbNT) void fallback_kernel(SegArgs a) {
+  __shared__ SegLds<kFbNT> L;
+  __shared__ uint32_t h[256];
+  const int row = blockIdx.x;
+  if (!seg_active(a, row)) return;  // the bracket held: nothing to do
+  const int64_t len = seg_len(a, row);
+  const int64_t ntiles = (len + kFbTile - 1) / kFbTile;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    if (threadIdx.x < 256) h[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < len; i += kFbNT) atomicAdd(&h[(load_key(a, pass, row, i, 0u) >> shift) & 255u], 1u);
+    __syncthreads();
+    // running start of each digit, advanced tile by tile (thread d owns digit d)
+    uint32_t run = wg_excl_scan<kFbNT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.rk.wsum);
+    uint32_t *dst = pass_dst(a, pass) + (int64_t)row * a.stride;
+    for (int64_t tile = 0; tile < ntiles; ++tile) {
+      uint32_t key[kKpt];
+      int dig[kKpt];
+      load_tile<kFbNT>(a, pass, row, tile * kFbTile, len, 0u, shift, key, dig);
+      const int vc = (int)min((int64_t)kFbTile, len - tile * kFbTile);
+      run += scatter_tile<kFbNT>(key, dig, shift, vc, run, dst, L.rk);
+    }
+  }
+  const uint32_t *fin = a.B;  // four passes
+  BlockTeam<kFbNT, 1> team(&L.tm);
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    float s[kKpt];
+    const int nv = load_sorted<kFbNT>(a, fin, row, tile * kFbTile, len, 0u, s);
+    tile_aggregate<kFbNT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
+  }
+  __syncthreads();
+  locate_row<kFbNT>(a, row, fin, team);
+}
+
+hipError_t launch_fallback(const SegArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(fallback_kernel, dim3((unsigned)a.rows), dim3(kFbNT), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace lapsum

@@ -41,10 +41,8 @@ __global__ void init_rows_kernel(RowState *st, int64_t rows, int32_t flags, int 
   z.kmin = 0xFFFFFFFFu;
   z.kmax = 0u;
   z.flags = flags;
-  z.ticket = 0u;
+  z.pad0 = 0;
   z.dk = 0.0;
-  z.ticket2 = 0u;
-  z.pad = 0;
   st[row] = z;
 }
 
@@ -156,12 +154,8 @@ LDEV void block_sum2(double &a, double &b, double *lds) {
 
 __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float *__restrict__ g,
                                                                     const float *__restrict__ p, int64_t n,
-                                                                    RowState *__restrict__ st,
-                                                                    BwdPartial *__restrict__ part, int gx,
-                                                                    float *__restrict__ dk,
-                                                                    lapsum_row_stats *stats) {
+                                                                    BwdPartial *__restrict__ part, int gx) {
   __shared__ double lds[2 * kStreamThreads / kWave];
-  __shared__ int is_last;
   const int64_t row = blockIdx.y;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
@@ -187,18 +181,18 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
     }
   }
   block_sum2<kStreamThreads>(D, G, lds);
-  if (threadIdx.x == 0) {
-    part[row * gx + blockIdx.x] = BwdPartial{D, G};
-    __threadfence();
-    const unsigned prev = atomicAdd(&st[row].ticket, 1u);
-    is_last = (prev == (unsigned)gx - 1u);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // deterministic finalize: fixed assignment of partials to threads, fixed tree
+  if (threadIdx.x == 0) part[row * gx + blockIdx.x] = BwdPartial{D, G};
+}
+
+// dk = G/D per row from the block partials, summed in a fixed order
+__global__ __launch_bounds__(kStreamThreads) void bwd_finalize_kernel(const BwdPartial *__restrict__ part, int gx,
+                                                                      RowState *__restrict__ st,
+                                                                      float *__restrict__ dk,
+                                                                      lapsum_row_stats *stats) {
+  __shared__ double lds[2 * kStreamThreads / kWave];
+  const int64_t row = blockIdx.x;
   double Ds = 0.0, Gs = 0.0;
-  const volatile BwdPartial *vp = part + row * gx;
+  const BwdPartial *vp = part + row * gx;
   for (int i = threadIdx.x; i < gx; i += kStreamThreads) {
     Ds += vp[i].D;
     Gs += vp[i].G;
@@ -207,12 +201,9 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
   if (threadIdx.x == 0) {
     const double dkd = Ds > 0.0 ? Gs / Ds : 0.0;
     st[row].dk = dkd;
+    st[row].flags = Ds > 0.0 ? 0 : LAPSUM_FLAG_DEGENERATE;
     dk[row] = (float)dkd;
-    if (!(Ds > 0.0)) {
-      st[row].flags |= LAPSUM_FLAG_DEGENERATE;
-      if (stats) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
-    }
-    st[row].ticket = 0u;
+    if (stats && !(Ds > 0.0)) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
   }
 }
 
@@ -254,8 +245,12 @@ size_t bwd_partial_bytes(int64_t rows, int grid_x) { return sizeof(BwdPartial) *
 
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st, void *partials,
                              int grid_x, float *dk, lapsum_row_stats *stats, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n, st,
-                     reinterpret_cast<BwdPartial *>(partials), grid_x, dk, stats);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
+                     reinterpret_cast<BwdPartial *>(partials), grid_x);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)rows), dim3(kStreamThreads), 0, s,
+                     reinterpret_cast<const BwdPartial *>(partials), grid_x, st, dk, stats);
   return hipGetLastError();
 }
 
