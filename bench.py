@@ -90,12 +90,14 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def stages_of(L, path, n):
-    """Stage ids a call on this path records (forward, then backward)."""
+def stages_of(L, plan, n):
+    """Stage ids a call with this plan records (forward, then backward)."""
+    path = plan["path"]
+    fallback = [] if plan.get("band_onchip") else [L.STAGE_FULLSORT]  # fused into the band kernel
     fwd = {L.PATH_ONCHIP: [L.STAGE_ONCHIP_FWD],
            L.PATH_FULLSORT: [L.STAGE_INIT, L.STAGE_FULLSORT, L.STAGE_APPLY],
-           L.PATH_BRACKET: [L.STAGE_INIT, L.STAGE_SAMPLE, L.STAGE_SELECT, L.STAGE_FILTER, L.STAGE_BAND,
-                            L.STAGE_FULLSORT, L.STAGE_APPLY]}[path]
+           L.PATH_BRACKET: [L.STAGE_SAMPLE, L.STAGE_SELECT, L.STAGE_FILTER, L.STAGE_BAND]
+           + fallback + [L.STAGE_APPLY]}[path]
     bwd = [L.STAGE_ONCHIP_BWD] if n <= 1024 else [L.STAGE_BWD_REDUCE, L.STAGE_BWD_APPLY]
     return fwd + bwd
 
@@ -141,7 +143,7 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
         evsets.append(evs)
         step(i, evs)
     torch.cuda.synchronize()
-    ran = stages_of(L, plan["path"], n)
+    ran = stages_of(L, plan, n)
     for evs in evsets:
         for s in ran:
             ms = hip.elapsed_ms(evs[2 * s], evs[2 * s + 1])

@@ -355,13 +355,15 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     tm.mark(LAPSUM_STAGE_FULLSORT, 1);
   } else {
     const double *ovr = o.bracket_override;
-    tm.mark(LAPSUM_STAGE_INIT, 0);
-    LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, s));
-    tm.mark(LAPSUM_STAGE_INIT, 1);
-    if (!ovr) {
+    if (ovr) {
+      tm.mark(LAPSUM_STAGE_INIT, 0);
+      LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, s));
+      tm.mark(LAPSUM_STAGE_INIT, 1);
+    } else {
+      // the sample kernel also resets the rows' state
       float *samples = reinterpret_cast<float *>(ws + P.samples);
       tm.mark(LAPSUM_STAGE_SAMPLE, 0);
-      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, s));
+      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, rs, LAPSUM_FLAG_BRACKET, s));
       tm.mark(LAPSUM_STAGE_SAMPLE, 1);
       tm.mark(LAPSUM_STAGE_SELECT, 0);
       LAPSUM_TRY(launch_select(samples, rows, P.m, P.lo, P.hi, rs, s));
@@ -374,15 +376,19 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, offs, P.cap, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
-    if (P.band_onchip)
-      LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, s));
-    else
+    const SegArgs fb = seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t);
+    if (P.band_onchip) {
+      // the band kernel also runs the fallback for rows whose bracket missed
+      LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, fb, s));
+      tm.mark(LAPSUM_STAGE_BAND, 1);
+    } else {
       LAPSUM_TRY(launch_segment(
           seg_args(P.band_seg, ws, kSegBand, rows, n, r, band, rs, k, t, slots, offs, P.fgx), s));
-    tm.mark(LAPSUM_STAGE_BAND, 1);
-    tm.mark(LAPSUM_STAGE_FULLSORT, 0);
-    LAPSUM_TRY(launch_fallback(seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t), s));
-    tm.mark(LAPSUM_STAGE_FULLSORT, 1);
+      tm.mark(LAPSUM_STAGE_BAND, 1);
+      tm.mark(LAPSUM_STAGE_FULLSORT, 0);
+      LAPSUM_TRY(launch_fallback(fb, s));
+      tm.mark(LAPSUM_STAGE_FULLSORT, 1);
+    }
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);
   LAPSUM_TRY(launch_apply(r, rows, n, rs, t, p, b, s));

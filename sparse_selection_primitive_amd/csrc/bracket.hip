@@ -38,9 +38,11 @@ LDEV void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 }
 
 __global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ r, int64_t n, double t, int64_t m,
-                                                     uint32_t k0, uint32_t k1, float *__restrict__ samples) {
+                                                     uint32_t k0, uint32_t k1, float *__restrict__ samples,
+                                                     RowState *__restrict__ st, int32_t flags) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = blockIdx.y;
+  if (j == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state of the row
   if (j >= m) return;
   uint32_t c[4] = {(uint32_t)j, (uint32_t)row, 0u, 0u};
   philox4x32_10(c, k0, k1);
@@ -53,21 +55,24 @@ __global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ r
 }
 
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, hipStream_t s) {
+                         float *samples, RowState *st, int32_t flags, hipStream_t s) {
   const int64_t gx = (m + 255) / 256;
   hipLaunchKernelGGL(sample_kernel, dim3((unsigned)gx, (unsigned)rows), dim3(256), 0, s, r, n, t, m,
-                     (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples);
+                     (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, st, flags);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------- order statistics
-// One workgroup of 1024 threads per row.  Exact selection of the ranks
-// lo-1 and hi-1 (0-based) among the m samples by key: a 15-bit histogram of
-// the key's top bits in LDS locates the bin of each rank; the bin's keys are
-// then gathered and ranked directly when few (<= kSelectCap), else the
-// histogram is refined on the next 15 bits, then the last 2.
+// One workgroup of 1024 threads per row selects the ranks lo-1 and hi-1
+// (0-based) of the m samples, by key.  A histogram of the key's top 15 bits
+// in LDS gives each rank's bin and its rank inside the bin; the bin's keys
+// are then gathered and ranked directly when few (<= kSelectCap), while a
+// crowded bin is refined by histograms of the next 9 bits, then the last 8.
+// Every pass over the samples is latency-bound, so each thread issues all
+// of its loads (16 x 16 B per 65536 samples) before using any of them.
 constexpr int kSelThreads = 1024;
 constexpr int kSelBins = 1 << 15;
+constexpr int kSelChunk = kSelThreads * 64;
 
 struct SelectLds {
   uint32_t hist[kSelBins];
@@ -76,10 +81,33 @@ struct SelectLds {
   uint32_t wsum[kSelThreads / kWave];
   uint32_t found_bin[2];
   uint32_t found_rank[2];
+  uint32_t found_cnt[2];
   uint32_t result[2];
 };
 
-LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum, uint32_t &total) {
+// f(key) for every sample; thread t handles 64 consecutive samples per chunk
+template <class F>
+LDEV void for_each_sample(const float *X, int64_t m, F &&f) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  for (int64_t c0 = 0; c0 < m; c0 += kSelChunk) {
+    const int64_t base = c0 + (int64_t)threadIdx.x * 64;
+    f4 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      v[q] = (base + 4 * q < m) ? *reinterpret_cast<const f4 *>(X + base + 4 * q) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (base + 4 * q < m) {
+        f(key_of(v[q].x));
+        f(key_of(v[q].y));
+        f(key_of(v[q].z));
+        f(key_of(v[q].w));
+      }
+    }
+  }
+}
+
+LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   uint32_t inc = v;
 #pragma unroll
@@ -90,49 +118,49 @@ LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum, uint32_t &total) {
   __syncthreads();
   if (lane == kWave - 1) wsum[w] = inc;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) {
-    const uint32_t x = wsum[i];
-    if (i < w) before += x;
-    tot += x;
-  }
-  total = tot;
+  uint32_t before = 0;
+  for (int i = 0; i < kSelThreads / kWave; ++i)
+    if (i < w) before += wsum[i];
   return before + inc - v;
 }
 
-// histogram of bits [shift, shift+nb) over keys matching (key >> pshift) == prefix
-LDEV void select_histogram(const float *X, int64_t m, int pshift, uint32_t prefix, int shift, int nb,
-                           SelectLds &L) {
-  const uint32_t nbins = 1u << nb;
-  for (uint32_t i = threadIdx.x; i < nbins; i += kSelThreads) L.hist[i] = 0u;
-  __syncthreads();
-  for (int64_t j = threadIdx.x; j < m; j += kSelThreads) {
-    const uint32_t kk = key_of(X[j]);
-    if (pshift >= 32 || (kk >> pshift) == prefix) atomicAdd(&L.hist[(kk >> shift) & (nbins - 1)], 1u);
-  }
-  __syncthreads();
-}
-
-// find the bin holding rank R (0-based) of the histogram; writes found_bin/rank[tgt]
-LDEV void select_locate(int nb, uint32_t R, int tgt, SelectLds &L) {
-  const uint32_t nbins = 1u << nb;
-  const uint32_t per = (nbins + kSelThreads - 1) / kSelThreads;
-  const uint32_t b0 = threadIdx.x * per;
+// Bins holding ranks R[0] and R[1] (where want[t]) of the LDS histogram of
+// `nbins` counts, one scan for both: each thread owns `per` consecutive bins
+// (read 16 B at a time when per is a multiple of 4); writes
+// found_bin/rank/cnt[t].
+LDEV void locate_ranks(int nbins, const uint32_t (&R)[2], const bool (&want)[2], SelectLds &L) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const int per = (nbins + kSelThreads - 1) / kSelThreads;
+  const int b0 = threadIdx.x * per;
+  uint32_t c[32];
   uint32_t local = 0;
-  for (uint32_t i = 0; i < per; ++i)
-    if (b0 + i < nbins) local += L.hist[b0 + i];
-  uint32_t total;
-  const uint32_t before = block_excl_scan_u32(local, L.wsum, total);
-  if (local > 0 && before <= R && R < before + local) {
+  if (per == 32) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u4 v = *reinterpret_cast<const u4 *>(&L.hist[b0 + 4 * q]);
+      c[4 * q] = v.x;
+      c[4 * q + 1] = v.y;
+      c[4 * q + 2] = v.z;
+      c[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) c[i] = (i < per && b0 + i < nbins) ? L.hist[b0 + i] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) local += c[i];
+  const uint32_t before = block_excl_scan_u32(local, L.wsum);
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg] || local == 0 || R[tg] < before || R[tg] >= before + local) continue;
     uint32_t acc = before;
-    for (uint32_t i = 0; i < per; ++i) {
-      const uint32_t h = L.hist[b0 + i];
-      if (R < acc + h) {
-        L.found_bin[tgt] = b0 + i;
-        L.found_rank[tgt] = R - acc;
-        break;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (R[tg] >= acc && R[tg] < acc + c[i]) {
+        L.found_bin[tg] = (uint32_t)(b0 + i);
+        L.found_rank[tg] = R[tg] - acc;
+        L.found_cnt[tg] = c[i];
       }
-      acc += h;
+      acc += c[i];
     }
   }
   __syncthreads();
@@ -145,35 +173,47 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
   const int64_t row = blockIdx.x;
   const float *X = samples + row * m;
   const bool want[2] = {lo >= 1, hi <= m};
-  const uint32_t R0[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
+  uint32_t R[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
+  uint32_t prefix[2] = {0u, 0u}, cnt[2] = {0u, 0u};
+  int pshift[2] = {17, 17};
 
-  // level 0: top 15 bits of every key
-  select_histogram(X, m, 32, 0u, 17, 15, L);
-  int pshift[2] = {32, 32};
-  uint32_t prefix[2] = {0u, 0u}, R[2] = {R0[0], R0[1]}, cnt[2] = {0u, 0u};
-  for (int tg = 0; tg < 2; ++tg) {
-    if (!want[tg]) continue;
-    select_locate(15, R[tg], tg, L);
-    prefix[tg] = L.found_bin[tg];
-    R[tg] = L.found_rank[tg];
-    cnt[tg] = L.hist[prefix[tg]];
-    pshift[tg] = 17;
+  {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 z4 = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < kSelBins / 4; i += kSelThreads) reinterpret_cast<u4 *>(L.hist)[i] = z4;
   }
   __syncthreads();
-  // refinement when a bin holds too many keys for the direct ranking
+  for_each_sample(X, m, [&](uint32_t kk) { atomicAdd(&L.hist[kk >> 17], 1u); });
+  __syncthreads();
+  locate_ranks(kSelBins, R, want, L);
   for (int tg = 0; tg < 2; ++tg) {
     if (!want[tg]) continue;
-    const int shifts[2] = {2, 0};
-    for (int lv = 0; lv < 2 && cnt[tg] > (uint32_t)kSelectCap && pshift[tg] > 0; ++lv) {
-      const int sh = shifts[lv];
+    prefix[tg] = L.found_bin[tg];
+    R[tg] = L.found_rank[tg];
+    cnt[tg] = L.found_cnt[tg];
+  }
+  // refinement of a crowded bin: 9 more bits, then the last 8
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;
+    while (cnt[tg] > (uint32_t)kSelectCap && pshift[tg] > 0) {
+      const int sh = pshift[tg] > 8 ? 8 : 0;
       const int nb = pshift[tg] - sh;
-      select_histogram(X, m, pshift[tg], prefix[tg], sh, nb, L);
-      select_locate(nb, R[tg], tg, L);
-      prefix[tg] = (prefix[tg] << nb) | L.found_bin[tg];
-      R[tg] = L.found_rank[tg];
-      cnt[tg] = L.hist[L.found_bin[tg]];
-      pshift[tg] = sh;
+      const uint32_t pf = prefix[tg];
+      const int ps = pshift[tg];
       __syncthreads();
+      for (int i = threadIdx.x; i < (1 << nb); i += kSelThreads) L.hist[i] = 0u;
+      __syncthreads();
+      for_each_sample(X, m, [&](uint32_t kk) {
+        if ((kk >> ps) == pf) atomicAdd(&L.hist[(kk >> sh) & ((1u << nb) - 1u)], 1u);
+      });
+      __syncthreads();
+      const uint32_t Rt[2] = {R[tg], R[tg]};
+      const bool wt[2] = {tg == 0, tg == 1};
+      locate_ranks(1 << nb, Rt, wt, L);
+      prefix[tg] = (pf << nb) | L.found_bin[tg];
+      R[tg] = L.found_rank[tg];
+      cnt[tg] = L.found_cnt[tg];
+      pshift[tg] = sh;
     }
   }
   // gather the candidates of each target's final bin
@@ -184,17 +224,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
   __syncthreads();
   const bool gather0 = want[0] && pshift[0] > 0, gather1 = want[1] && pshift[1] > 0;
   if (gather0 || gather1) {
-    for (int64_t j = threadIdx.x; j < m; j += kSelThreads) {
-      const uint32_t kk = key_of(X[j]);
-      if (gather0 && (kk >> pshift[0]) == prefix[0]) {
+    const int ps0 = pshift[0], ps1 = pshift[1];
+    const uint32_t pf0 = prefix[0], pf1 = prefix[1];
+    for_each_sample(X, m, [&](uint32_t kk) {
+      if (gather0 && (kk >> ps0) == pf0) {
         const uint32_t slot = atomicAdd(&L.ccount[0], 1u);
         if (slot < (uint32_t)kSelectCap) L.cand[0][slot] = kk;
       }
-      if (gather1 && (kk >> pshift[1]) == prefix[1]) {
+      if (gather1 && (kk >> ps1) == pf1) {
         const uint32_t slot = atomicAdd(&L.ccount[1], 1u);
         if (slot < (uint32_t)kSelectCap) L.cand[1][slot] = kk;
       }
-    }
+    });
   }
   __syncthreads();
   for (int tg = 0; tg < 2; ++tg) {
@@ -288,40 +329,48 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   uint32_t cl = 0, cr = 0;
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 
+  typedef float f4 __attribute__((ext_vector_type(4)));
   const bool vec = (n & 3) == 0 && (((uintptr_t)r & 15u) == 0);
   const int64_t nitems = vec ? (n >> 2) : n;
-  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < nitems; i += stride) {
-    float x[4];
-    int nx;
-    if (vec) {
-      typedef float f4 __attribute__((ext_vector_type(4)));
-      const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr) + i);
-      x[0] = v.x;
-      x[1] = v.y;
-      x[2] = v.z;
-      x[3] = v.w;
-      nx = 4;
-    } else {
-      x[0] = rr[i];
-      x[1] = x[2] = x[3] = 0.0f;
-      nx = 1;
+  // kUnroll items (16 B each on the vector path) per thread and iteration,
+  // all loads issued before any is used
+  for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < nitems;
+       i0 += stride * kUnroll) {
+    float x[4 * kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * kStreamThreads;
+      f4 v = {0.f, 0.f, 0.f, 0.f};
+      if (i < nitems) {
+        if (vec) v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr) + i);
+        else v.x = rr[i];
+      }
+      x[4 * u] = v.x;
+      x[4 * u + 1] = v.y;
+      x[4 * u + 2] = v.z;
+      x[4 * u + 3] = v.w;
     }
     float fl = 0.0f, fr = 0.0f;
-    bool mid[4] = {false, false, false, false};
+    bool mid[4 * kUnroll];
+    bool any = false;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q < nx) filter_one(x[q], aL, aR, cf, fl, fr, cl, cr, mid[q]);
+    for (int q = 0; q < 4 * kUnroll; ++q) {
+      const int64_t i = i0 + (q / 4) * kStreamThreads;
+      const bool ok = i < nitems && (vec || (q & 3) == 0);
+      mid[q] = false;
+      if (ok) filter_one(x[q], aL, aR, cf, fl, fr, cl, cr, mid[q]);
+      any |= mid[q];
+    }
     sl += (double)fl;
     sr += (double)fr;
-    const bool any = mid[0] || mid[1] || mid[2] || mid[3];
     const unsigned long long wany = __ballot(any);
     if (wany) {
       const unsigned long long active = __ballot(1);
       const int leader = __ffsll((long long)active) - 1;
-      unsigned long long mq[4];
+      unsigned long long mq[4 * kUnroll];
       uint32_t tot = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4 * kUnroll; ++q) {
         mq[q] = __ballot(mid[q]);
         tot += (uint32_t)__popcll(mq[q]);
       }
@@ -330,7 +379,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
       base = __shfl(base, leader, kWave);
       uint32_t off = base;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4 * kUnroll; ++q) {
         if (mid[q]) {
           const uint32_t pos = off + mbcnt64(mq[q]);
           const uint32_t kk = key_of(x[q]);
@@ -491,8 +540,8 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
 }
 
 int filter_grid_x(int64_t rows, int64_t n) {
-  const int64_t per_row_need = (n / 4 + kStreamThreads - 1) / kStreamThreads;
-  int64_t target = 4096 / (rows > 0 ? rows : 1);
+  const int64_t per_row_need = (n / 4 + kStreamThreads * kUnroll - 1) / (kStreamThreads * kUnroll);
+  int64_t target = 1024 / (rows > 0 ? rows : 1);
   if (target < 1) target = 1;
   int64_t gx = per_row_need < target ? per_row_need : target;
   return (int)(gx < 1 ? 1 : gx);

@@ -509,4 +509,23 @@ struct RowState {
   double dk;                // backward: dk in fp64
 };
 
+// Per-call reset of one row's state (bracket open unless forced).
+LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_override, double o_lo, double o_hi) {
+  RowState z;
+  z.a_lo = has_override ? o_lo : -INFINITY;
+  z.a_hi = has_override ? o_hi : INFINITY;
+  z.tail_lo = 0.0;
+  z.tail_hi = 0.0;
+  z.count_lo = 0;
+  z.count_hi = 0;
+  z.band = 0;
+  z.b = 0.0;
+  z.kmin = 0xFFFFFFFFu;
+  z.kmax = 0u;
+  z.flags = flags;
+  z.pad0 = 0;
+  z.dk = 0.0;
+  st[row] = z;
+}
+
 }  // namespace lapsum

@@ -19,6 +19,7 @@ constexpr int kTile = 4096;          // keys per tile of the large-row sort and 
 constexpr int kSegThreads = 256;     // threads per workgroup of the large-row kernels
 constexpr int kSelectCap = 1024;     // direct-selection capacity of the bracket select
 constexpr int kStreamThreads = 256;  // threads per workgroup of the streaming kernels
+constexpr int kUnroll = 4;           // independent 16 B loads per thread per stream and iteration
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
@@ -55,7 +56,7 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
                                   float *dk, lapsum_row_stats *stats, hipStream_t s);
 bool onchip_backward_supported(int64_t n);
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, hipStream_t s);
+                         float *samples, RowState *st, int32_t flags, hipStream_t s);
 hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
                          hipStream_t s);
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
@@ -65,7 +66,7 @@ size_t filter_partial_bytes(int64_t rows, int grid_x);
 size_t band_slot_bytes(int64_t rows, int grid_x);
 size_t band_offs_bytes(int64_t rows, int grid_x);
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
-                              RowState *st, double k, double t, hipStream_t s);
+                              RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
 hipError_t launch_segment(const SegArgs &a, hipStream_t s);
 hipError_t launch_fallback(const SegArgs &a, hipStream_t s);
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,

@@ -14,8 +14,7 @@
 // Band solve (section 2.2, probabilistic bracketing, step 3): the same
 // sort + curve + root on the compacted middle band, seeded with the tail
 // sums of the streaming pass, followed by the certification of step 4.
-#include "lapsum_device.hpp"
-#include "lapsum_internal.hpp"
+#include "segment_dev.hpp"
 
 namespace lapsum {
 
@@ -225,77 +224,89 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
 }
 
 // ----------------------------------------------------------- band solve
-// One workgroup per row; the band (at most NP keys) is gathered from the
-// filter's per-workgroup slots, sorted, and solved with the tail sums as
-// boundary seeds.  The result is certified: the root must lie inside
-// [a_L, a_R), else the row goes to the full-sort fallback.
+// One workgroup of 512 threads per row; the band (at most NP keys) is
+// gathered from the filter's per-workgroup slots, sorted, and solved with the
+// tail sums as boundary seeds.  The result is certified: the root must lie
+// inside [a_L, a_R).  A row whose bracket missed (or whose band overflowed)
+// is then sorted and solved in full by the same workgroup, so no separate
+// fallback launch is needed on this path.
+constexpr int kBandNT = 512;
+
 template <int NP>
-__global__ __launch_bounds__(NP / 16) void band_solve_onchip(const uint32_t *__restrict__ slots,
+__global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__restrict__ slots,
                                                              const uint32_t *__restrict__ offs, int gx,
-                                                             RowState *__restrict__ st, double k, double t) {
-  constexpr int E = 16, LANES = NP / 16;
-  __shared__ BlockTeamLds<LANES, E> lds;
+                                                             RowState *__restrict__ st, double k, double t,
+                                                             SegArgs fb) {
+  constexpr int E = NP / kBandNT;
+  union BandLds {
+    BlockTeamLds<kBandNT, E> band;
+    SegLds<kBandNT> full;
+  };
+  __shared__ BandLds lds;
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
-  BlockTeam<LANES, E> team(&lds);
   const int64_t row = blockIdx.x;
   RowState &S = st[row];
-  if (S.flags & LAPSUM_FLAG_OVERFLOW) return;  // the finalize already routed the row to the fallback
-  const int m = (int)S.band;
-  const uint32_t *ro = offs + row * (int64_t)(gx + 1);
-  for (int i = threadIdx.x; i <= gx; i += LANES) soffs[i] = ro[i];
-  __syncthreads();
-  const int base = team.lane * E;
-  // slot holding index `base`: the last b with soffs[b] <= base
-  int lo = 0, hi = gx - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int)soffs[mid] <= base) lo = mid;
-    else hi = mid - 1;
-  }
-  int b = lo;
-  uint32_t key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = base + e;
-    if (j < m) {
-      while ((int)soffs[b + 1] <= j) ++b;
-      key[e] = slots[((int64_t)row * gx + b) * kBandSlot + (j - (int)soffs[b])];
-    } else {
-      key[e] = 0xFFFFFFFFu;
+  if (!(S.flags & LAPSUM_FLAG_OVERFLOW)) {
+    BlockTeam<kBandNT, E> team(&lds.band);
+    const int m = (int)S.band;
+    const uint32_t *ro = offs + row * (int64_t)(gx + 1);
+    for (int i = threadIdx.x; i <= gx; i += kBandNT) soffs[i] = ro[i];
+    __syncthreads();
+    const int base = team.lane * E;
+    // slot holding index `base`: the last b with soffs[b] <= base
+    int lo = 0, hi = gx - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)soffs[mid] <= base) lo = mid;
+      else hi = mid - 1;
     }
-  }
-  bitonic_sort<E>(key, team);
-  const int nv = min(max(m - base, 0), E);
-  float s[E];
+    int b = lo;
+    uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+    for (int e = 0; e < E; ++e) {
+      const int j = base + e;
+      if (j < m) {
+        while ((int)soffs[b + 1] <= j) ++b;
+        key[e] = slots[((int64_t)row * gx + b) * kBandSlot + (j - (int)soffs[b])];
+      } else {
+        key[e] = 0xFFFFFFFFu;
+      }
+    }
+    bitonic_sort<E>(key, team);
+    const int nv = min(max(m - base, 0), E);
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
 
-  const double c = kLog2e / t;
-  PartInfo part;
-  part.nvalid = nv;
-  part.above = (double)m + (double)S.count_hi;
-  part.seed_lo = Pre{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
-  part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
-  part.first = true;
-  part.last = true;
-  const double bb = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
-  if (threadIdx.x == 0) {
-    S.b = bb;
-    const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
-    S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+    const double c = kLog2e / t;
+    PartInfo part;
+    part.nvalid = nv;
+    part.above = (double)m + (double)S.count_hi;
+    part.seed_lo = Pre{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
+    part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
+    part.first = true;
+    part.last = true;
+    const double bb = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
+    if (threadIdx.x == 0) {
+      S.b = bb;
+      const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
+      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+    }
+    __syncthreads();
   }
+  if (S.flags & LAPSUM_FLAG_FALLBACK) fallback_row<kBandNT>(fb, (int)row, lds.full);
 }
 
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
-                              RowState *st, double k, double t, hipStream_t s) {
+                              RowState *st, double k, double t, const SegArgs &fb, hipStream_t s) {
   if (cap <= 1024)
-    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(64), 0, s, slots, offs, gx, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
   else if (cap <= 2048)
-    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(128), 0, s, slots, offs, gx, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
   else if (cap <= 4096)
-    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(256), 0, s, slots, offs, gx, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
   else
-    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(512), 0, s, slots, offs, gx, st, k, t);
+    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
   return hipGetLastError();
 }
 

@@ -1,0 +1,339 @@
+// Device routines of the large-row full-sort solver shared by the
+// multi-launch kernels (segment.hip), the one-workgroup fallback and the
+// on-chip band kernel (onchip.hip): tile loads, stable scatter of a tile,
+// tile aggregates of sorted keys, and the per-row locate + closed-form root.
+// Method: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
+// section 2.2, full-sort solver.
+#pragma once
+
+#include "lapsum_device.hpp"
+#include "lapsum_internal.hpp"
+
+namespace lapsum {
+
+struct TileAgg {
+  float aP, aS;
+  double sP, sS;
+};
+
+constexpr int kKpt = 16;  // keys per thread in a tile
+
+template <int NT>
+struct RankLds {
+  static constexpr int NW = NT / kWave;
+  uint32_t stage[NT * kKpt];
+  uint32_t wcnt[NW][256];
+  uint32_t tstart[256];
+  uint32_t dglob[256];
+  uint32_t wsum[NW];
+};
+
+template <int NT>
+union SegLds {
+  RankLds<NT> rk;
+  BlockTeamLds<NT, 1> tm;
+};
+
+// ------------------------------------------------------------- row helpers
+LDEV bool seg_active(const SegArgs &a, int row) {
+  const RowState &s = a.st[row];
+  if (a.mode == kSegFull) return true;
+  if (a.mode == kSegFallback) return (s.flags & LAPSUM_FLAG_FALLBACK) != 0;
+  return !(s.flags & LAPSUM_FLAG_OVERFLOW) && s.band <= (unsigned long long)a.stride;
+}
+LDEV int64_t seg_len(const SegArgs &a, int row) {
+  if (!seg_active(a, row)) return 0;
+  if (a.mode == kSegBand) return (int64_t)a.st[row].band;
+  return a.n;
+}
+LDEV uint32_t seg_kbase(const SegArgs &a, int row) {
+  if (a.mode != kSegBand) return 0u;
+  const RowState &s = a.st[row];
+  return s.band > 0 ? s.kmin : 0u;
+}
+// digit passes this row needs: the band sorts key - kmin, so only the digits
+// spanned by its key range
+LDEV int seg_npasses(const SegArgs &a, int row) {
+  if (a.mode != kSegBand) return 4;
+  const RowState &s = a.st[row];
+  const uint32_t span = (s.band > 1 && s.kmax > s.kmin) ? s.kmax - s.kmin : 0u;
+  const int bits = span == 0u ? 1 : 32 - __clz((int)span);
+  return (bits + 7) / 8;
+}
+LDEV const uint32_t *seg_final(const SegArgs &a, int row) { return (seg_npasses(a, row) & 1) ? a.A : a.B; }
+
+template <int NT>
+LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < w) before += wsum[i];
+  return before + inc - v;
+}
+
+// key of element i of `row` read by digit pass `pass`
+LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i, uint32_t kbase) {
+  if (pass == 0) {
+    if (a.mode == kSegBand) return a.band[(int64_t)row * a.stride + i] - kbase;
+    return key_of(a.r[(int64_t)row * a.n + i]);
+  }
+  const uint32_t *src = (pass & 1) ? a.A : a.B;
+  return src[(int64_t)row * a.stride + i];
+}
+LDEV uint32_t *pass_dst(const SegArgs &a, int pass) { return (pass & 1) ? a.B : a.A; }
+
+// ----------------------------------------------------------- tile routines
+// Keys of one tile, wave-striped: thread (w, lane) holds tile positions
+// w*64*16 + q*64 + lane, q = 0..15, which is also their stable order.
+template <int NT>
+LDEV void load_tile(const SegArgs &a, int pass, int row, int64_t t0, int64_t len, uint32_t kbase, int shift,
+                    uint32_t (&key)[kKpt], int (&dig)[kKpt]) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int q = 0; q < kKpt; ++q) {
+    const int64_t gi = t0 + w * (kWave * kKpt) + q * kWave + lane;
+    const bool valid = gi < len;
+    key[q] = valid ? load_key(a, pass, row, gi, kbase) : 0u;
+    dig[q] = valid ? (int)((key[q] >> shift) & 255u) : 256;
+  }
+}
+
+// Stable scatter of one tile.  Thread d < 256 passes in `digit_base`, the
+// position in `dst` where this tile's keys of digit d start; it gets back the
+// number of this tile's keys of digit d.
+template <int NT>
+LDEV uint32_t scatter_tile(const uint32_t (&key)[kKpt], const int (&dig)[kKpt], int shift, int vc,
+                           uint32_t digit_base, uint32_t *dst, RankLds<NT> &L) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const unsigned long long ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  volatile uint32_t *wc = L.wcnt[w];
+#pragma unroll
+  for (int i = 0; i < 256 / kWave; ++i) wc[lane + i * kWave] = 0u;
+  __syncthreads();
+  // rank within the wave's chunk, round by round: peers with the same digit
+  // by 8 ballots, one LDS read-modify-write per digit group
+  uint32_t rnk[kKpt];
+#pragma unroll
+  for (int q = 0; q < kKpt; ++q) {
+    const int d = dig[q];
+    const bool valid = d < 256;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (d >> bit) & 1;
+      const unsigned long long bb = __ballot(set);
+      peers &= set ? bb : ~bb;
+    }
+    const uint32_t lt = (uint32_t)__popcll(peers & ltmask);
+    uint32_t prev = 0u;
+    if (valid) prev = wc[d];
+    rnk[q] = prev + lt;
+    if (valid && lt == 0u) wc[d] = prev + (uint32_t)__popcll(peers);
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  uint32_t tcount = 0u;
+  if (d < 256) {
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const uint32_t c = L.wcnt[ww][d];
+      L.wcnt[ww][d] = tcount;
+      tcount += c;
+    }
+  }
+  const uint32_t ts = wg_excl_scan<NT>(d < 256 ? tcount : 0u, L.wsum);
+  if (d < 256) {
+    L.tstart[d] = ts;
+    L.dglob[d] = digit_base - ts;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kKpt; ++q) {
+    const int dq = dig[q];
+    if (dq < 256) L.stage[L.tstart[dq] + L.wcnt[w][dq] + rnk[q]] = key[q];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < vc; i += NT) {
+    const uint32_t kk = L.stage[i];
+    dst[L.dglob[(kk >> shift) & 255u] + i] = kk;
+  }
+  __syncthreads();
+  return tcount;
+}
+
+// Sorted keys t0 .. t0 + NT*16 of `fin` as values, blocked (16 per thread).
+template <int NT>
+LDEV int load_sorted(const SegArgs &a, const uint32_t *fin, int row, int64_t t0, int64_t len, uint32_t kbase,
+                     float (&s)[kKpt]) {
+  const int64_t base = t0 + (int64_t)threadIdx.x * kKpt;
+  const int nv = (int)min(max(len - base, (int64_t)0), (int64_t)kKpt);
+  const uint32_t *src = fin + (int64_t)row * a.stride + base;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) s[e] = (e < nv) ? value_of(src[e] + kbase) : 0.0f;
+  return nv;
+}
+
+// Anchored aggregates of one sorted tile: P-type relative to its last key,
+// S-type relative to its first key.
+template <int NT>
+LDEV void tile_aggregate(const float (&s)[kKpt], int nv, double c, float cf, const BlockTeam<NT, 1> &team,
+                         TileAgg *out) {
+  float mul[kKpt];
+  mul[0] = 0.0f;
+#pragma unroll
+  for (int e = 1; e < kKpt; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], cf) : 0.0f;
+  double pl = 0.0, sl = 0.0;
+  float last = s[0];
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e)
+    if (e < nv) {
+      pl = pl * (double)mul[e] + 1.0;
+      last = s[e];
+    }
+#pragma unroll
+  for (int e = kKpt - 1; e >= 0; --e)
+    if (e < nv) sl = (e + 1 < kKpt ? sl * (double)mul[e + 1] : 0.0) + 1.0;
+  const Pre mp{last, nv > 0 ? pl : 0.0};
+  const Suf ms{s[0], nv > 0 ? sl : 0.0};
+  const Pre ep = team.excl_scan(mp, c);
+  const Suf es = team.excl_scan(ms, c);
+  if (threadIdx.x == NT - 1) {
+    const Pre tp = join(ep, mp, c);
+    out->aP = tp.a;
+    out->sP = tp.s;
+  }
+  if (threadIdx.x == 0) {
+    const Suf tsf = join(ms, es, c);
+    out->aS = tsf.a;
+    out->sS = tsf.s;
+  }
+  __syncthreads();
+}
+
+// Per row: scan of the tile aggregates, threshold curve at the tile ends,
+// the balancing tile, and the closed-form root inside it (tiles of NT*16).
+template <int NT>
+LDEV void locate_row(const SegArgs &a, int row, const uint32_t *fin, const BlockTeam<NT, 1> &team) {
+  constexpr int TT = NT * kKpt;
+  RowState &S = a.st[row];
+  const int64_t len = seg_len(a, row);
+  const int nt = (int)((len + TT - 1) / TT);
+  const bool band = a.mode == kSegBand;
+  const Pre seed_lo{(float)S.a_lo, (band && S.count_lo) ? S.tail_lo : 0.0};
+  const Suf seed_hi{(float)S.a_hi, (band && S.count_hi) ? S.tail_hi : 0.0};
+  const double cR = band ? (double)S.count_hi : 0.0;
+  const TileAgg *ta = a.tagg + (int64_t)row * a.max_tiles;
+  Pre *tp = a.tpre + (int64_t)row * a.max_tiles;
+  Suf *ts = a.tsuf + (int64_t)row * a.max_tiles;
+
+  Pre carry = seed_lo;
+  for (int T0 = 0; T0 < nt; T0 += NT) {
+    const int T = T0 + threadIdx.x;
+    const Pre mine = T < nt ? Pre{ta[T].aP, ta[T].sP} : Pre{0.0f, 0.0};
+    const Pre ex = team.excl_scan(mine, a.c);
+    if (T < nt) tp[T] = join(carry, ex, a.c);
+    const Pre tot = join(ex, mine, a.c);
+    const Pre chunk{team.bcast(tot.a, NT - 1), team.bcast(tot.s, NT - 1)};
+    carry = join(carry, chunk, a.c);
+  }
+  Suf carry_s = seed_hi;
+  for (int T0 = ((nt - 1) / NT) * NT; nt > 0 && T0 >= 0; T0 -= NT) {
+    const int T = T0 + threadIdx.x;
+    const Suf mine = T < nt ? Suf{ta[T].aS, ta[T].sS} : Suf{0.0f, 0.0};
+    const Suf ex = team.excl_scan(mine, a.c);
+    if (T < nt) ts[T] = join(ex, carry_s, a.c);
+    const Suf tot = join(mine, ex, a.c);
+    const Suf chunk{team.bcast(tot.a, 0), team.bcast(tot.s, 0)};
+    carry_s = join(chunk, carry_s, a.c);
+  }
+  __syncthreads();
+  // threshold curve at the last knot of every tile
+  int cnt = 0;
+  for (int T = threadIdx.x; T < nt; T += NT) {
+    const Pre pl = join(tp[T], Pre{ta[T].aP, ta[T].sP}, a.c);
+    const Suf sa = ts[T];
+    const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, a.c));
+    const int64_t nvT = min((int64_t)TT, len - (int64_t)T * TT);
+    const int64_t j_last = (int64_t)T * TT + nvT - 1;
+    const double g = 0.5 * (pl.s - 1.0) + ((double)(len - j_last) + cR) - 0.5 * s_last;
+    cnt += (g >= a.k) ? 1 : 0;
+  }
+  const int tstar = team.sum(cnt);
+  const int tsel = nt == 0 ? 0 : min(tstar, nt - 1);
+  float s[kKpt];
+  int nv = 0;
+  if (nt > 0) {
+    nv = load_sorted<NT>(a, fin, row, (int64_t)tsel * TT, len, seg_kbase(a, row), s);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) s[e] = 0.0f;
+  }
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)(len - (int64_t)tsel * TT) + cR;
+  part.seed_lo = nt > 0 ? tp[tsel] : seed_lo;
+  part.seed_hi = nt > 0 ? ts[tsel] : seed_hi;
+  part.first = tsel == 0;
+  part.last = tsel >= nt - 1;
+  const double b = segment_solve<kKpt>(s, nv, part, a.k, a.t, a.c, a.cf, team);
+  if (threadIdx.x == 0) {
+    S.b = b;
+    if (band) {
+      const bool hit = (b >= S.a_lo) && (b < S.a_hi);
+      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+    }
+  }
+  __syncthreads();
+}
+
+
+// The deterministic full-sort fallback for one row, run by a whole
+// workgroup of NT threads: four stable 8-bit digit passes through the key
+// buffers A -> B -> A -> B, tile aggregates, locate and root.
+template <int NT>
+LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
+  constexpr int TT = NT * kKpt;
+  __shared__ uint32_t h[256];
+  const int64_t len = a.n;
+  const int64_t ntiles = (len + TT - 1) / TT;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += NT) h[i] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < len; i += NT) atomicAdd(&h[(load_key(a, pass, row, i, 0u) >> shift) & 255u], 1u);
+    __syncthreads();
+    // running start of each digit, advanced tile by tile (thread d owns digit d)
+    uint32_t run = wg_excl_scan<NT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.rk.wsum);
+    uint32_t *dst = pass_dst(a, pass) + (int64_t)row * a.stride;
+    for (int64_t tile = 0; tile < ntiles; ++tile) {
+      uint32_t key[kKpt];
+      int dig[kKpt];
+      load_tile<NT>(a, pass, row, tile * TT, len, 0u, shift, key, dig);
+      const int vc = (int)min((int64_t)TT, len - tile * TT);
+      run += scatter_tile<NT>(key, dig, shift, vc, run, dst, L.rk);
+    }
+  }
+  const uint32_t *fin = a.B;  // four passes
+  BlockTeam<NT, 1> team(&L.tm);
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    float s[kKpt];
+    const int nv = load_sorted<NT>(a, fin, row, tile * TT, len, 0u, s);
+    tile_aggregate<NT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
+  }
+  __syncthreads();
+  locate_row<NT>(a, row, fin, team);
+}
+
+}  // namespace lapsum

@@ -28,28 +28,13 @@ LDEV float cdf_at(float x, double b, double c) {
 __global__ void init_rows_kernel(RowState *st, int64_t rows, int32_t flags, int has_override, double o_lo,
                                  double o_hi) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
-  RowState z;
-  z.a_lo = has_override ? o_lo : -INFINITY;
-  z.a_hi = has_override ? o_hi : INFINITY;
-  z.tail_lo = 0.0;
-  z.tail_hi = 0.0;
-  z.count_lo = 0;
-  z.count_hi = 0;
-  z.band = 0;
-  z.b = 0.0;
-  z.kmin = 0xFFFFFFFFu;
-  z.kmax = 0u;
-  z.flags = flags;
-  z.pad0 = 0;
-  z.dk = 0.0;
-  st[row] = z;
+  if (row < rows) reset_row_state(st, row, flags, has_override, o_lo, o_hi);
 }
 
 hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, hipStream_t s) {
   const int64_t grid = (rows + 255) / 256;
-  hipLaunchKernelGGL(init_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, st, rows, flags,
-                     override2 ? 1 : 0, override2 ? override2[0] : 0.0, override2 ? override2[1] : 0.0);
+  hipLaunchKernelGGL(init_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, st, rows, flags, override2 ? 1 : 0,
+                     override2 ? override2[0] : 0.0, override2 ? override2[1] : 0.0);
   return hipGetLastError();
 }
 
@@ -93,14 +78,26 @@ __global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__re
     const int64_t n4 = n >> 2;
     const f4 *r4 = reinterpret_cast<const f4 *>(rr);
     f4 *p4 = reinterpret_cast<f4 *>(pp);
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-      const f4 x = __builtin_nontemporal_load(r4 + i);
-      f4 y;
-      y.x = cdf_at(x.x, b, c);
-      y.y = cdf_at(x.y, b, c);
-      y.z = cdf_at(x.z, b, c);
-      y.w = cdf_at(x.w, b, c);
-      __builtin_nontemporal_store(y, p4 + i);
+    for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < n4;
+         i0 += stride * kUnroll) {
+      f4 x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kStreamThreads;
+        x[u] = i < n4 ? __builtin_nontemporal_load(r4 + i) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kStreamThreads;
+        if (i < n4) {
+          f4 y;
+          y.x = cdf_at(x[u].x, b, c);
+          y.y = cdf_at(x[u].y, b, c);
+          y.z = cdf_at(x[u].z, b, c);
+          y.w = cdf_at(x[u].w, b, c);
+          __builtin_nontemporal_store(y, p4 + i);
+        }
+      }
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
@@ -109,8 +106,8 @@ __global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__re
 }
 
 static int stream_grid_x(int64_t rows, int64_t n) {
-  const int64_t per_row_need = (n / 4 + kStreamThreads - 1) / kStreamThreads;
-  int64_t target = 4096 / (rows > 0 ? rows : 1);
+  const int64_t per_row_need = (n / 4 + kStreamThreads * kUnroll - 1) / (kStreamThreads * kUnroll);
+  int64_t target = 2048 / (rows > 0 ? rows : 1);
   if (target < 1) target = 1;
   int64_t gx = per_row_need < target ? per_row_need : target;
   if (gx < 1) gx = 1;
@@ -165,13 +162,23 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
     const int64_t n4 = n >> 2;
     const f4 *g4 = reinterpret_cast<const f4 *>(gg);
     const f4 *p4 = reinterpret_cast<const f4 *>(pp);
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-      const f4 pv = __builtin_nontemporal_load(p4 + i);
-      const f4 gv = __builtin_nontemporal_load(g4 + i);
-      const float q0 = fminf(pv.x, 1.0f - pv.x), q1 = fminf(pv.y, 1.0f - pv.y);
-      const float q2 = fminf(pv.z, 1.0f - pv.z), q3 = fminf(pv.w, 1.0f - pv.w);
-      D += (double)((q0 + q1) + (q2 + q3));
-      G += (double)((gv.x * q0 + gv.y * q1) + (gv.z * q2 + gv.w * q3));
+    for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < n4;
+         i0 += stride * kUnroll) {
+      f4 pv[kUnroll], gv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kStreamThreads;
+        const bool ok = i < n4;
+        pv[u] = ok ? __builtin_nontemporal_load(p4 + i) : f4{0.f, 0.f, 0.f, 0.f};
+        gv[u] = ok ? __builtin_nontemporal_load(g4 + i) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float q0 = fminf(pv[u].x, 1.0f - pv[u].x), q1 = fminf(pv[u].y, 1.0f - pv[u].y);
+        const float q2 = fminf(pv[u].z, 1.0f - pv[u].z), q3 = fminf(pv[u].w, 1.0f - pv[u].w);
+        D += (double)((q0 + q1) + (q2 + q3));
+        G += (double)((gv[u].x * q0 + gv[u].y * q1) + (gv[u].z * q2 + gv[u].w * q3));
+      }
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride) {
@@ -224,15 +231,28 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
     const f4 *g4 = reinterpret_cast<const f4 *>(gg);
     const f4 *p4 = reinterpret_cast<const f4 *>(pp);
     f4 *d4 = reinterpret_cast<f4 *>(dd);
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-      const f4 pv = __builtin_nontemporal_load(p4 + i);
-      const f4 gv = __builtin_nontemporal_load(g4 + i);
-      f4 o;
-      o.x = fminf(pv.x, 1.0f - pv.x) * inv_t * (float)((double)gv.x - dkd);
-      o.y = fminf(pv.y, 1.0f - pv.y) * inv_t * (float)((double)gv.y - dkd);
-      o.z = fminf(pv.z, 1.0f - pv.z) * inv_t * (float)((double)gv.z - dkd);
-      o.w = fminf(pv.w, 1.0f - pv.w) * inv_t * (float)((double)gv.w - dkd);
-      __builtin_nontemporal_store(o, d4 + i);
+    for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < n4;
+         i0 += stride * kUnroll) {
+      f4 pv[kUnroll], gv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kStreamThreads;
+        const bool ok = i < n4;
+        pv[u] = ok ? __builtin_nontemporal_load(p4 + i) : f4{0.f, 0.f, 0.f, 0.f};
+        gv[u] = ok ? __builtin_nontemporal_load(g4 + i) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * kStreamThreads;
+        if (i < n4) {
+          f4 o;
+          o.x = fminf(pv[u].x, 1.0f - pv[u].x) * inv_t * (float)((double)gv[u].x - dkd);
+          o.y = fminf(pv[u].y, 1.0f - pv[u].y) * inv_t * (float)((double)gv[u].y - dkd);
+          o.z = fminf(pv[u].z, 1.0f - pv[u].z) * inv_t * (float)((double)gv[u].z - dkd);
+          o.w = fminf(pv[u].w, 1.0f - pv[u].w) * inv_t * (float)((double)gv[u].w - dkd);
+          __builtin_nontemporal_store(o, d4 + i);
+        }
+      }
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
