@@ -82,9 +82,23 @@ WORKLOADS = {
 }
 
 
-def source_sha() -> str:
+# Source files each streaming kernel is compiled from (a change to any of them
+# invalidates the HBM traffic counters recorded for that kernel).
+_COMMON_SRC = ["lapsum_device.hpp", "lapsum_internal.hpp"]
+KERNEL_SOURCES = {"filter": ["bracket.hip"] + _COMMON_SRC,
+                  "apply": ["stream.hip"] + _COMMON_SRC,
+                  "bwd_reduce": ["stream.hip"] + _COMMON_SRC,
+                  "bwd_apply": ["stream.hip"] + _COMMON_SRC,
+                  "onchip_fwd": ["onchip.hip", "segment_dev.hpp"] + _COMMON_SRC,
+                  "onchip_bwd": ["onchip.hip", "segment_dev.hpp"] + _COMMON_SRC}
+
+
+def source_sha(files=None) -> str:
+    """Hash of the kernel sources (all of csrc/ unless `files` names some)."""
+    csrc = os.path.join(ROOT, "sparse_selection_primitive_amd", "csrc")
+    paths = sorted(glob.glob(os.path.join(csrc, "*"))) if files is None else [os.path.join(csrc, f) for f in files]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_selection_primitive_amd", "csrc", "*"))):
+    for f in paths:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -236,13 +250,15 @@ def cpu_baseline(w_extreme_r, k, t, n_sample):
                       f"fp64 bisection forward + analytic VJP, {dt:.2f} s wall"}
 
 
-def load_traffic(kernel_stage: str, workload: str, sha: str):
+def load_traffic(kernel_stage: str, workload: str):
+    """Calibrated HBM bytes per launch from the committed counter summary, or
+    None when there is none or the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_stage}_{workload}.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel_stage not in KERNEL_SOURCES:
         return None
     with open(path) as f:
         tr = json.load(f)
-    if tr.get("source_sha") != sha:
+    if tr.get("kernel_source_sha") != source_sha(KERNEL_SOURCES[kernel_stage]):
         return None
     return tr.get("bytes_per_launch")
 
@@ -255,7 +271,7 @@ def main():
     ap.add_argument("--configs", default="extreme,attack,routing,coder_bracket,coder_fullsort,tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-trials", type=int, default=20)
-    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
@@ -287,7 +303,7 @@ def main():
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         bb = torch.empty_like(a)
         for _ in range(3):
-            bb.copy_(a)
+            torch.neg(a, out=bb)  # one elementwise kernel: 1 GiB read + 1 GiB written
         torch.cuda.synchronize()
         del a, bb
 
@@ -308,7 +324,7 @@ def main():
     head = results[head_name]
     sha = source_sha()
     dom = head["dominant"]
-    traffic = load_traffic(dom["stage"], head_name, sha)
+    traffic = load_traffic(dom["stage"], head_name)
     roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": dom["GBps"] * 1e9 / HBM_PEAK, "traffic": traffic,
                 "kernel": dom["kernel"], "algorithmic_bytes_per_launch": dom["bytes"],
