@@ -55,6 +55,30 @@ SegRegions seg_regions(Layout &L, int64_t rows, int64_t len) {
   return r;
 }
 
+// Offsets of the workspace regions of the bucketed band solve.
+struct BandRegions {
+  size_t keys, tmp, hist, btot, bstart, bagg, tagg, tpre, tsuf;
+  int nblk, group, max_tiles;
+};
+
+BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx) {
+  BandRegions r;
+  r.nblk = band_count_blocks(gx, &r.group);
+  r.max_tiles = (int)(cap / kTile);
+  const size_t keys = (size_t)rows * (size_t)cap * sizeof(uint32_t);
+  const size_t nb = (size_t)rows * kBandBuckets;
+  r.keys = L.take(keys);
+  r.tmp = L.take(keys);
+  r.hist = L.take(nb * (size_t)r.nblk * sizeof(uint32_t));
+  r.btot = L.take(nb * sizeof(uint32_t));
+  r.bstart = L.take(nb * sizeof(uint32_t));
+  r.bagg = L.take(nb * tile_agg_bytes());
+  r.tagg = L.take((size_t)rows * (size_t)r.max_tiles * tile_agg_bytes());
+  r.tpre = L.take((size_t)rows * (size_t)r.max_tiles * pre_bytes());
+  r.tsuf = L.take((size_t)rows * (size_t)r.max_tiles * suf_bytes());
+  return r;
+}
+
 struct Plan {
   int path = 0;
   int sample_log2 = 0;
@@ -63,9 +87,10 @@ struct Plan {
   bool band_onchip = false;
   // forward layout
   size_t fwd_bytes = 0;
-  size_t st = 0, samples = 0, fpart = 0, band = 0, slots = 0, offs = 0;
+  size_t st = 0, samples = 0, fpart = 0, slots = 0, offs = 0;
   int fgx = 0;
-  SegRegions band_seg{}, full_seg{};
+  BandRegions bnd{};
+  SegRegions full_seg{};
   // backward layout
   size_t bwd_bytes = 0;
   size_t bst = 0, bpart = 0;
@@ -202,8 +227,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
     P.offs = F.take(band_offs_bytes(rows, P.fgx));
-    P.band = F.take((size_t)rows * (size_t)P.cap * sizeof(uint32_t));
-    if (!P.band_onchip) P.band_seg = seg_regions(F, rows, P.cap);
+    if (!P.band_onchip) P.bnd = band_regions(F, rows, P.cap, P.fgx);
     P.full_seg = seg_regions(F, rows, n);
   }
   P.fwd_bytes = F.off;
@@ -230,18 +254,13 @@ lapsum_status hip_status(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LA
     if (_e != hipSuccess) return LAPSUM_ERR_HIP; \
   } while (0)
 
-SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t n, const float *r,
-                 uint32_t *band, RowState *st, double k, double t, const uint32_t *slots = nullptr,
-                 const uint32_t *offs = nullptr, int gx = 0) {
+SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t n, const float *r, RowState *st,
+                 double k, double t) {
   SegArgs a;
   a.mode = mode;
   a.rows = (int)rows;
   a.n = n;
   a.r = r;
-  a.band = band;
-  a.slots = slots;
-  a.offs = offs;
-  a.gx = gx;
   a.A = reinterpret_cast<uint32_t *>(ws + R.A);
   a.B = reinterpret_cast<uint32_t *>(ws + R.B);
   a.stride = R.stride;
@@ -252,6 +271,35 @@ SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t 
   a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
   a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);
   a.st = st;
+  a.k = k;
+  a.t = t;
+  a.c = kLog2e / t;
+  a.cf = (float)a.c;
+  return a;
+}
+
+BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots,
+                   const uint32_t *offs, double k, double t) {
+  const BandRegions &R = P.bnd;
+  BandArgs a;
+  a.rows = (int)rows;
+  a.gx = P.fgx;
+  a.group = R.group;
+  a.nblk = R.nblk;
+  a.slots = slots;
+  a.offs = offs;
+  a.st = st;
+  a.keys = reinterpret_cast<uint32_t *>(ws + R.keys);
+  a.tmp = reinterpret_cast<uint32_t *>(ws + R.tmp);
+  a.hist = reinterpret_cast<uint32_t *>(ws + R.hist);
+  a.btot = reinterpret_cast<uint32_t *>(ws + R.btot);
+  a.bstart = reinterpret_cast<uint32_t *>(ws + R.bstart);
+  a.bagg = reinterpret_cast<TileAgg *>(ws + R.bagg);
+  a.tagg = reinterpret_cast<TileAgg *>(ws + R.tagg);
+  a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
+  a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);
+  a.cap = P.cap;
+  a.max_tiles = R.max_tiles;
   a.k = k;
   a.t = t;
   a.c = kLog2e / t;
@@ -351,7 +399,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
     tm.mark(LAPSUM_STAGE_INIT, 1);
     tm.mark(LAPSUM_STAGE_FULLSORT, 0);
-    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFull, rows, n, r, nullptr, rs, k, t), s));
+    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFull, rows, n, r, rs, k, t), s));
     tm.mark(LAPSUM_STAGE_FULLSORT, 1);
   } else {
     const double *ovr = o.bracket_override;
@@ -369,21 +417,19 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
       LAPSUM_TRY(launch_select(samples, rows, P.m, P.lo, P.hi, rs, s));
       tm.mark(LAPSUM_STAGE_SELECT, 1);
     }
-    uint32_t *band = reinterpret_cast<uint32_t *>(ws + P.band);
     uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);
     uint32_t *offs = reinterpret_cast<uint32_t *>(ws + P.offs);
     tm.mark(LAPSUM_STAGE_FILTER, 0);
     LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, offs, P.cap, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
-    const SegArgs fb = seg_args(P.full_seg, ws, kSegFallback, rows, n, r, nullptr, rs, k, t);
+    const SegArgs fb = seg_args(P.full_seg, ws, kSegFallback, rows, n, r, rs, k, t);
     if (P.band_onchip) {
       // the band kernel also runs the fallback for rows whose bracket missed
       LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, fb, s));
       tm.mark(LAPSUM_STAGE_BAND, 1);
     } else {
-      LAPSUM_TRY(launch_segment(
-          seg_args(P.band_seg, ws, kSegBand, rows, n, r, band, rs, k, t, slots, offs, P.fgx), s));
+      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t), s));
       tm.mark(LAPSUM_STAGE_BAND, 1);
       tm.mark(LAPSUM_STAGE_FULLSORT, 0);
       LAPSUM_TRY(launch_fallback(fb, s));

@@ -1,0 +1,437 @@
+// Bucketed band solve for bands too large for one workgroup ("Fast LapSum:
+// Exact Differentiable Top-k at Million Scale", section 2.2, probabilistic
+// bracketing, step 3: the band is sorted and solved exactly, seeded with the
+// tail sums; step 4: certification).
+//
+// The band keys lie in [kmin, kmax].  Bucket j holds the keys with
+// (key - kmin) >> shift == j, shift the smallest value that leaves at most
+// kBandBuckets buckets; every key of bucket j is below every key of bucket
+// j + 1, so sorting each bucket on its own sorts the band (one
+// most-significant-digit radix pass, then independent bucket sorts).
+//
+//   band_count_kernel    bucket counts of each workgroup's filter slots
+//   band_scan_kernel     per bucket, offsets of the workgroups inside it
+//   band_scatter_kernel  keys to their bucket (order inside a bucket free)
+//   band_sort_kernel     one wave sorts each bucket of at most 1024 keys in
+//                        registers; larger buckets are sorted by the whole
+//                        workgroup; anchored aggregates of every bucket
+//   band_locate_kernel   scan of the bucket aggregates between the tail
+//                        seeds, threshold curve at the bucket ends, the
+//                        balancing bucket, the root inside it, certification
+//
+// Every count is an integer and every floating-point sum runs over sorted
+// keys in a fixed order, so the result does not depend on the order in which
+// the scatter placed keys inside a bucket.
+#include <limits.h>
+
+#include "segment_dev.hpp"
+
+namespace lapsum {
+
+constexpr int kBT = 256;                   // threads per workgroup of every band kernel
+constexpr int kBPT = kBandBuckets / kBT;   // buckets per thread in the per-row scans
+constexpr int kWaveBucket = 16 * kWave;    // largest bucket one wave sorts
+static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of the workgroup size");
+
+LDEV bool band_active(const RowState &S) { return !(S.flags & LAPSUM_FLAG_OVERFLOW); }
+
+LDEV int band_shift(const RowState &S) {
+  const uint32_t span = (S.band > 1 && S.kmax > S.kmin) ? S.kmax - S.kmin : 0u;
+  const int bits = span == 0u ? 0 : 32 - __clz((int)span);
+  return max(bits - kBandBucketBits, 0);
+}
+
+// Band keys of count/scatter workgroup `blk`: wave w walks the workgroup's
+// slots w, w + 4, ...; its lanes stride through each slot.
+template <class F>
+LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, F &&f) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const uint32_t *ro = a.offs + row * (a.gx + 1);
+  const int s0 = blk * a.group, s1 = min(a.gx, s0 + a.group);
+  for (int sl = s0 + w; sl < s1; sl += kBT / kWave) {
+    const uint32_t cnt = ro[sl + 1] - ro[sl];
+    const uint32_t *src = a.slots + (row * a.gx + sl) * (int64_t)kBandSlot;
+    for (uint32_t i = lane; i < cnt; i += kWave) f(src[i]);
+  }
+}
+
+__global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
+  __shared__ uint32_t h[kBandBuckets];
+  const int64_t row = blockIdx.y;
+  const int blk = blockIdx.x;
+  const RowState &S = a.st[row];
+  if (!band_active(S)) return;
+  const uint32_t kmin = S.kmin;
+  const int shift = band_shift(S);
+  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) h[j] = 0u;
+  __syncthreads();
+  for_each_band_key(a, row, blk, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
+  __syncthreads();
+  uint32_t *dst = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
+  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) dst[j] = h[j];
+}
+
+// one thread per bucket: exclusive scan over the count workgroups, in place
+__global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
+  const int64_t row = blockIdx.y;
+  if (!band_active(a.st[row])) return;
+  const int j = blockIdx.x * kBT + threadIdx.x;
+  uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
+  uint32_t run = 0u;
+  int b = 0;
+  for (; b + 8 <= a.nblk; b += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = h[(int64_t)(b + u) * kBandBuckets];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      h[(int64_t)(b + u) * kBandBuckets] = run;
+      run += v[u];
+    }
+  }
+  for (; b < a.nblk; ++b) {
+    const uint32_t v = h[(int64_t)b * kBandBuckets];
+    h[(int64_t)b * kBandBuckets] = run;
+    run += v;
+  }
+  a.btot[row * kBandBuckets + j] = run;
+}
+
+__global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
+  __shared__ uint32_t base[kBandBuckets];
+  __shared__ uint32_t wsum[kBT / kWave];
+  const int64_t row = blockIdx.y;
+  const int blk = blockIdx.x;
+  const RowState &S = a.st[row];
+  if (!band_active(S)) return;
+  const uint32_t kmin = S.kmin;
+  const int shift = band_shift(S);
+  // bucket starts (thread i owns buckets i*kBPT ..), plus this workgroup's
+  // offset inside each bucket
+  const int64_t o = row * kBandBuckets;
+  uint32_t v[kBPT];
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    v[u] = a.btot[o + threadIdx.x * kBPT + u];
+    sum += v[u];
+  }
+  uint32_t run = wg_excl_scan<kBT>(sum, wsum);
+  const uint32_t *hin = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    const int j = threadIdx.x * kBPT + u;
+    base[j] = run + hin[j];
+    if (blk == 0) a.bstart[o + j] = run;
+    run += v[u];
+  }
+  __syncthreads();
+  uint32_t *dst = a.keys + row * a.cap;
+  for_each_band_key(a, row, blk, [&](uint32_t key) {
+    const uint32_t pos = atomicAdd(&base[(key - kmin) >> shift], 1u);
+    dst[pos] = key;
+  });
+}
+
+// ------------------------------------------------------------ bucket sort
+LDEV void write_agg(TileAgg *out, Pre p, Suf s) {
+  out->aP = p.a;
+  out->sP = p.s;
+  out->aS = s.a;
+  out->sS = s.s;
+}
+
+// One wave sorts a bucket of cnt <= 64*E keys in registers (blocked, E per
+// lane), writes it back and stores its anchored aggregates.
+template <int E>
+LDEV void wave_bucket(uint32_t *kb, int cnt, double c, float cf, TileAgg *out) {
+  WaveTeam<kWave> team;
+  const int base = team.lane * E;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (base + e < cnt) ? kb[base + e] : 0xFFFFFFFFu;
+  bitonic_sort<E>(key, team);
+  const int nv = min(max(cnt - base, 0), E);
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+    if (e < nv) kb[base + e] = key[e];
+  }
+  team_aggregate<E>(s, nv, c, cf, team, out);
+}
+
+union BandSortLds {
+  RankLds<kBT> rk;
+  BlockTeamLds<kBT, kKpt> sort;
+  BlockTeamLds<kBT, 1> scan;
+};
+
+// The whole workgroup sorts one bucket of more than 1024 keys: a register
+// bitonic sort up to 4096 keys, else a stable LSD radix sort (8-bit digits)
+// of the keys relative to the bucket's lowest possible key `kb0` (they differ
+// in their low `bits` bits only).  Then the bucket's aggregates, tile by tile.
+LDEV void block_bucket(uint32_t *kb, uint32_t *tb, int cnt, uint32_t kb0, int bits, double c, float cf,
+                       BandSortLds &L, TileAgg *lagg, TileAgg *out) {
+  constexpr int TT = kBT * kKpt;
+  if (cnt <= TT) {
+    BlockTeam<kBT, kKpt> team(&L.sort);
+    const int base = threadIdx.x * kKpt;
+    uint32_t key[kKpt];
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) key[e] = (base + e < cnt) ? kb[base + e] : 0xFFFFFFFFu;
+    bitonic_sort<kKpt>(key, team);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if (base + e < cnt) kb[base + e] = key[e];
+    __syncthreads();
+  } else {
+    __shared__ uint32_t h[256];
+    for (int i = threadIdx.x; i < cnt; i += kBT) kb[i] -= kb0;
+    __syncthreads();
+    uint32_t *src = kb, *dst = tb;
+    const int npass = (bits + 7) / 8;
+    const int ntiles = (cnt + TT - 1) / TT;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    for (int pass = 0; pass < npass; ++pass) {
+      const int sh = 8 * pass;
+      h[threadIdx.x] = 0u;
+      __syncthreads();
+      for (int i = threadIdx.x; i < cnt; i += kBT) atomicAdd(&h[(src[i] >> sh) & 255u], 1u);
+      __syncthreads();
+      uint32_t run = wg_excl_scan<kBT>(h[threadIdx.x], L.rk.wsum);
+      for (int tile = 0; tile < ntiles; ++tile) {
+        uint32_t key[kKpt];
+        int dig[kKpt];
+#pragma unroll
+        for (int q = 0; q < kKpt; ++q) {
+          const int gi = tile * TT + w * (kWave * kKpt) + q * kWave + lane;
+          const bool valid = gi < cnt;
+          key[q] = valid ? src[gi] : 0u;
+          dig[q] = valid ? (int)((key[q] >> sh) & 255u) : 256;
+        }
+        const int vc = min(TT, cnt - tile * TT);
+        run += scatter_tile<kBT>(key, dig, sh, vc, run, dst, L.rk);
+      }
+      uint32_t *x = src;
+      src = dst;
+      dst = x;
+    }
+    for (int i = threadIdx.x; i < cnt; i += kBT) kb[i] = src[i] + kb0;
+    __syncthreads();
+  }
+  // aggregates of the sorted bucket, tile by tile, joined in order
+  BlockTeam<kBT, 1> team(&L.scan);
+  Pre ap{0.0f, 0.0};
+  Suf as{0.0f, 0.0};
+  for (int t0 = 0; t0 < cnt; t0 += TT) {
+    float s[kKpt];
+    const int nv = load_sorted_at<kBT>(kb, t0, cnt, 0u, s);
+    team_aggregate<kKpt>(s, nv, c, cf, team, lagg);
+    ap = join(ap, Pre{lagg->aP, lagg->sP}, c);
+    as = join(as, Suf{lagg->aS, lagg->sS}, c);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) write_agg(out, ap, as);
+}
+
+__global__ __launch_bounds__(kBT) void band_sort_kernel(BandArgs a) {
+  __shared__ BandSortLds L;
+  __shared__ TileAgg lagg;
+  const int64_t row = blockIdx.y;
+  const RowState &S = a.st[row];
+  if (!band_active(S)) return;
+  const int shift = band_shift(S);
+  const int64_t o = row * kBandBuckets;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = blockIdx.x * (kBT / kWave) + (int)threadIdx.x / kWave;
+  const int cnt = (int)a.btot[o + j];
+  uint32_t *kb = a.keys + row * a.cap + a.bstart[o + j];
+  TileAgg *out = a.bagg + o + j;
+  if (cnt == 0) {
+    if (lane == 0) write_agg(out, Pre{0.0f, 0.0}, Suf{0.0f, 0.0});
+  } else if (shift == 0) {
+    // every key of the bucket is the same value
+    if (lane == 0) {
+      const float x = value_of(kb[0]);
+      write_agg(out, Pre{x, (double)cnt}, Suf{x, (double)cnt});
+    }
+  } else if (cnt <= 64) {
+    wave_bucket<1>(kb, cnt, a.c, a.cf, out);
+  } else if (cnt <= 128) {
+    wave_bucket<2>(kb, cnt, a.c, a.cf, out);
+  } else if (cnt <= 256) {
+    wave_bucket<4>(kb, cnt, a.c, a.cf, out);
+  } else if (cnt <= 512) {
+    wave_bucket<8>(kb, cnt, a.c, a.cf, out);
+  } else if (cnt <= kWaveBucket) {
+    wave_bucket<16>(kb, cnt, a.c, a.cf, out);
+  }
+  if (shift == 0) return;
+  // buckets beyond one wave: the whole workgroup, one after another
+  for (int w = 0; w < kBT / kWave; ++w) {
+    const int jj = blockIdx.x * (kBT / kWave) + w;
+    const int cc = (int)a.btot[o + jj];
+    if (cc <= kWaveBucket) continue;
+    __syncthreads();
+    const uint32_t st0 = a.bstart[o + jj];
+    block_bucket(a.keys + row * a.cap + st0, a.tmp + row * a.cap + st0, cc, S.kmin + ((uint32_t)jj << shift), shift,
+                 a.c, a.cf, L, &lagg, a.bagg + o + jj);
+  }
+}
+
+// ---------------------------------------------------------------- locate
+__global__ __launch_bounds__(kBT) void band_locate_kernel(BandArgs a) {
+  __shared__ BlockTeamLds<kBT, 1> lds;
+  __shared__ int red[3][kBT / kWave];
+  __shared__ float sel_pa, sel_sa;
+  __shared__ double sel_ps, sel_ss;
+  BlockTeam<kBT, 1> team(&lds);
+  const int64_t row = blockIdx.x;
+  RowState &S = a.st[row];
+  if (!band_active(S)) return;  // the fallback solves this row
+  const double c = a.c;
+  const int64_t M = (int64_t)S.band;
+  const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
+  const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
+  const double cR = (double)S.count_hi;
+  const int64_t o = row * kBandBuckets;
+  const int j0 = threadIdx.x * kBPT;
+
+  TileAgg g[kBPT];
+  uint32_t cnt[kBPT], st0[kBPT];
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    g[u] = a.bagg[o + j0 + u];
+    cnt[u] = a.btot[o + j0 + u];
+    st0[u] = a.bstart[o + j0 + u];
+  }
+  // everything before this thread's buckets, everything after them
+  Pre tp{0.0f, 0.0};
+  Suf ts{0.0f, 0.0};
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) tp = join(tp, Pre{g[u].aP, g[u].sP}, c);
+#pragma unroll
+  for (int u = kBPT - 1; u >= 0; --u) ts = join(Suf{g[u].aS, g[u].sS}, ts, c);
+  const Pre ex_p = join(seed_lo, team.excl_scan(tp, c), c);
+  const Suf ex_s = join(team.excl_scan(ts, c), seed_hi, c);
+  Pre before[kBPT];
+  Suf after[kBPT];
+  {
+    Pre run = ex_p;
+#pragma unroll
+    for (int u = 0; u < kBPT; ++u) {
+      before[u] = run;
+      run = join(run, Pre{g[u].aP, g[u].sP}, c);
+    }
+    Suf runs = ex_s;
+#pragma unroll
+    for (int u = kBPT - 1; u >= 0; --u) {
+      after[u] = runs;
+      runs = join(Suf{g[u].aS, g[u].sS}, runs, c);
+    }
+  }
+  // threshold curve at the last knot of every non-empty bucket
+  int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) {
+    if (cnt[u] > 0u) {
+      const int j = j0 + u;
+      const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
+      const Suf sa = after[u];
+      const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
+      const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
+      const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
+      if (gv < a.k) first_lt = min(first_lt, j);
+      first_ne = min(first_ne, j);
+      last_ne = max(last_ne, j);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    first_lt = min(first_lt, __shfl_xor(first_lt, m, kWave));
+    first_ne = min(first_ne, __shfl_xor(first_ne, m, kWave));
+    last_ne = max(last_ne, __shfl_xor(last_ne, m, kWave));
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[0][w] = first_lt;
+    red[1][w] = first_ne;
+    red[2][w] = last_ne;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBT / kWave; ++i) {
+    first_lt = min(first_lt, red[0][i]);
+    first_ne = min(first_ne, red[1][i]);
+    last_ne = max(last_ne, red[2][i]);
+  }
+  // the balancing bucket: the first whose last knot has g < k, else the last
+  const int J = first_lt != INT_MAX ? first_lt : last_ne;  // -1: empty band
+  if (J >= 0 && (int)threadIdx.x == J / kBPT) {
+#pragma unroll
+    for (int u = 0; u < kBPT; ++u)
+      if (u == J % kBPT) {
+        sel_pa = before[u].a;
+        sel_ps = before[u].s;
+        sel_sa = after[u].a;
+        sel_ss = after[u].s;
+      }
+  }
+  __syncthreads();
+  const int64_t cJ = J >= 0 ? (int64_t)a.btot[o + J] : 0;
+  const int64_t sJ = J >= 0 ? (int64_t)a.bstart[o + J] : 0;
+  const Pre slo = J >= 0 ? Pre{sel_pa, sel_ps} : seed_lo;
+  const Suf shi = J >= 0 ? Suf{sel_sa, sel_ss} : seed_hi;
+  const double cR_eff = (double)(M - sJ - cJ) + cR;
+  const bool first = J < 0 || J == first_ne;
+  const bool last = J < 0 || J == last_ne;
+  const uint32_t *src = a.keys + row * a.cap + sJ;
+  double b;
+  if (cJ <= (int64_t)kBT * kKpt) {
+    float s[kKpt];
+    const int nv = load_sorted_at<kBT>(src, 0, cJ, 0u, s);
+    PartInfo part;
+    part.nvalid = nv;
+    part.above = (double)cJ + cR_eff;
+    part.seed_lo = slo;
+    part.seed_hi = shi;
+    part.first = first;
+    part.last = last;
+    b = segment_solve<kKpt>(s, nv, part, a.k, a.t, c, a.cf, team);
+  } else {
+    // a bucket of several tiles: its tile aggregates, then locate over them
+    constexpr int TT = kBT * kKpt;
+    TileAgg *ta = a.tagg + row * a.max_tiles;
+    for (int64_t t0 = 0; t0 < cJ; t0 += TT) {
+      float s[kKpt];
+      const int nv = load_sorted_at<kBT>(src, t0, cJ, 0u, s);
+      tile_aggregate<kBT>(s, nv, c, a.cf, team, ta + t0 / TT);
+    }
+    b = locate_sorted<kBT>(src, cJ, 0u, slo, shi, cR_eff, first, last, ta, a.tpre + row * a.max_tiles,
+                           a.tsuf + row * a.max_tiles, a.k, a.t, c, a.cf, team);
+  }
+  if (threadIdx.x == 0) {
+    S.b = b;
+    const bool hit = (b >= S.a_lo) && (b < S.a_hi);
+    S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+  }
+}
+
+int band_count_blocks(int gx, int *group) {
+  const int nblk = gx < kBandCountBlocks ? gx : kBandCountBlocks;
+  *group = (gx + nblk - 1) / nblk;
+  return (gx + *group - 1) / *group;
+}
+
+hipError_t launch_band_buckets(const BandArgs &a, hipStream_t s) {
+  const dim3 blk((unsigned)a.nblk, (unsigned)a.rows);
+  hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_scan_kernel, dim3(kBandBuckets / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_sort_kernel, dim3(kBandBuckets / (kBT / kWave), (unsigned)a.rows), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kBT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lapsum

@@ -25,16 +25,12 @@ constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
 // Arguments of the large-row sort + threshold-curve + root kernels.
 struct SegArgs {
-  int mode;             // kSegFull, kSegBand or kSegFallback
+  int mode;             // kSegFull (every row) or kSegFallback (rows flagged for the fallback)
   int rows;
-  int64_t n;            // row length (full rows / fallback)
-  const float *r;       // [rows][n] scores (full rows / fallback)
-  uint32_t *band;       // [rows][stride] raw band keys, compacted from the slots (band mode)
-  const uint32_t *slots; // [rows][gx][kBandSlot] band keys per filter workgroup (band mode)
-  const uint32_t *offs;  // [rows][gx + 1] slot offsets (band mode)
-  int gx;               // filter workgroups per row (band mode)
+  int64_t n;            // row length
+  const float *r;       // [rows][n] scores
   uint32_t *A, *B;      // [rows][stride] key ping-pong buffers
-  int64_t stride;       // per-row stride of band/A/B, a multiple of kTile
+  int64_t stride;       // per-row stride of A/B, a multiple of kTile
   int max_tiles;        // stride / kTile
   uint32_t *hist;       // [rows][256][max_tiles] tile digit counts -> offsets
   uint32_t *dtot;       // [rows][256] digit totals
@@ -45,7 +41,38 @@ struct SegArgs {
   double k, t, c;       // c = log2(e)/t
   float cf;
 };
-enum { kSegFull = 0, kSegBand = 1, kSegFallback = 2 };
+enum { kSegFull = 0, kSegFallback = 1 };
+
+// Bucketed band solve (bands too large for one workgroup): the band keys are
+// spread over kBandBuckets buckets by their leading bits above the band's
+// smallest key, each bucket is sorted on its own, and the threshold curve is
+// located over the bucket aggregates.
+constexpr int kBandBucketBits = 11;
+constexpr int kBandBuckets = 1 << kBandBucketBits;
+constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row, at most
+
+struct BandArgs {
+  int rows;
+  int gx;               // filter workgroups (slots) per row
+  int group;            // slots per count/scatter workgroup
+  int nblk;             // count/scatter workgroups per row
+  const uint32_t *slots; // [rows][gx][kBandSlot] band keys per filter workgroup
+  const uint32_t *offs;  // [rows][gx + 1] slot offsets
+  RowState *st;         // [rows]
+  uint32_t *keys;       // [rows][cap] bucketed band keys, sorted inside each bucket
+  uint32_t *tmp;        // [rows][cap] scratch of the large-bucket sort
+  uint32_t *hist;       // [rows][nblk][kBandBuckets] counts -> offsets inside buckets
+  uint32_t *btot;       // [rows][kBandBuckets] bucket sizes
+  uint32_t *bstart;     // [rows][kBandBuckets] bucket starts
+  TileAgg *bagg;        // [rows][kBandBuckets] anchored aggregates of the buckets
+  TileAgg *tagg;        // [rows][max_tiles] tile aggregates of a large balancing bucket
+  Pre *tpre;            // [rows][max_tiles]
+  Suf *tsuf;            // [rows][max_tiles]
+  int64_t cap;          // per-row stride of keys/tmp (a multiple of kTile)
+  int max_tiles;        // cap / kTile
+  double k, t, c;
+  float cf;
+};
 
 // Launchers (each returns the first HIP error, or hipSuccess).
 hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2,
@@ -68,6 +95,8 @@ size_t band_offs_bytes(int64_t rows, int grid_x);
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
                               RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
 hipError_t launch_segment(const SegArgs &a, hipStream_t s);
+hipError_t launch_band_buckets(const BandArgs &a, hipStream_t s);
+int band_count_blocks(int gx, int *group);
 hipError_t launch_fallback(const SegArgs &a, hipStream_t s);
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
                         double *b, hipStream_t s);

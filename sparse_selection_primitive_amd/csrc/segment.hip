@@ -1,7 +1,6 @@
 // Large-row full-sort solver ("Fast LapSum: Exact Differentiable Top-k at
 // Million Scale", section 2.2, full-sort solver) for rows that do not fit one
-// workgroup's registers: the full-sort path, the compacted band of the
-// bracketing path, and the bracketing fallback.
+// workgroup's registers: the full-sort path and the bracketing fallback.
 //
 //   sort:  least-significant-digit radix sort of the order-preserving keys,
 //          8-bit digits; per pass a tile histogram, a per-digit scan over
@@ -12,7 +11,7 @@
 //          the threshold curve at tile ends, the balancing tile, the curve at
 //          every knot inside it, and the closed-form root.
 //
-// Full-sort rows and the band run one regular launch per phase (a kernel
+// Full-sort rows run one regular launch per phase (a kernel
 // boundary is the cheapest grid-wide synchronisation on this GPU, far below
 // a cooperative launch or an in-kernel grid barrier).  The fallback runs as a
 // single launch with one workgroup per row that sorts and solves the whole
@@ -30,30 +29,17 @@ size_t suf_bytes() { return sizeof(Suf); }
 // --------------------------------------------- multi-launch kernels (256)
 constexpr int kNT = kSegThreads;
 
-// band: gather the filter's per-workgroup slots into the contiguous band
-__global__ __launch_bounds__(kNT) void seg_compact_kernel(SegArgs a) {
-  const int row = blockIdx.y, b = blockIdx.x;
-  if (!seg_active(a, row)) return;
-  const uint32_t *ro = a.offs + (int64_t)row * (a.gx + 1);
-  const uint32_t o0 = ro[b], cnt = ro[b + 1] - o0;
-  const uint32_t *src = a.slots + ((int64_t)row * a.gx + b) * kBandSlot;
-  uint32_t *dst = a.band + (int64_t)row * a.stride + o0;
-  for (uint32_t i = threadIdx.x; i < cnt; i += kNT) dst[i] = src[i];
-}
-
 __global__ __launch_bounds__(kNT) void seg_hist_kernel(SegArgs a, int pass) {
   __shared__ uint32_t h[256];
   const int row = blockIdx.y, tile = blockIdx.x;
-  if (pass >= seg_npasses(a, row)) return;
   const int64_t len = seg_len(a, row);
   if ((int64_t)tile * kTile >= len) return;
   const int shift = 8 * pass;
-  const uint32_t kbase = seg_kbase(a, row);
   h[threadIdx.x] = 0u;
   __syncthreads();
   for (int q = 0; q < kKpt; ++q) {
     const int64_t gi = (int64_t)tile * kTile + q * kNT + threadIdx.x;
-    if (gi < len) atomicAdd(&h[(load_key(a, pass, row, gi, kbase) >> shift) & 255u], 1u);
+    if (gi < len) atomicAdd(&h[(load_key(a, pass, row, gi) >> shift) & 255u], 1u);
   }
   __syncthreads();
   a.hist[((int64_t)row * 256 + threadIdx.x) * a.max_tiles + tile] = h[threadIdx.x];
@@ -63,7 +49,6 @@ __global__ __launch_bounds__(kNT) void seg_hist_kernel(SegArgs a, int pass) {
 __global__ __launch_bounds__(kNT) void seg_scan_kernel(SegArgs a, int pass) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int row = blockIdx.y, d = blockIdx.x * (kNT / kWave) + w;
-  if (pass >= seg_npasses(a, row)) return;
   const int64_t len = seg_len(a, row);
   const int nt = (int)((len + kTile - 1) / kTile);
   if (nt == 0) return;
@@ -87,13 +72,12 @@ __global__ __launch_bounds__(kNT) void seg_scan_kernel(SegArgs a, int pass) {
 __global__ __launch_bounds__(kNT) void seg_scatter_kernel(SegArgs a, int pass) {
   __shared__ RankLds<kNT> L;
   const int row = blockIdx.y, tile = blockIdx.x;
-  if (pass >= seg_npasses(a, row)) return;
   const int64_t len = seg_len(a, row);
   if ((int64_t)tile * kTile >= len) return;
   const int shift = 8 * pass;
   uint32_t key[kKpt];
   int dig[kKpt];
-  load_tile<kNT>(a, pass, row, (int64_t)tile * kTile, len, seg_kbase(a, row), shift, key, dig);
+  load_tile<kNT>(a, pass, row, (int64_t)tile * kTile, len, shift, key, dig);
   // global start of each digit in this row, plus this tile's offset within it
   const uint32_t dtot = a.dtot[(int64_t)row * 256 + threadIdx.x];
   const uint32_t dbase = wg_excl_scan<kNT>(dtot, L.wsum);
@@ -109,7 +93,7 @@ __global__ __launch_bounds__(kNT) void seg_tiles_kernel(SegArgs a) {
   const int64_t len = seg_len(a, row);
   if ((int64_t)tile * kTile >= len) return;
   float s[kKpt];
-  const int nv = load_sorted<kNT>(a, seg_final(a, row), row, (int64_t)tile * kTile, len, seg_kbase(a, row), s);
+  const int nv = load_sorted<kNT>(a, row, (int64_t)tile * kTile, len, s);
   tile_aggregate<kNT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
 }
 
@@ -117,22 +101,12 @@ __global__ __launch_bounds__(kNT) void seg_locate_kernel(SegArgs a) {
   __shared__ BlockTeamLds<kNT, 1> lds;
   BlockTeam<kNT, 1> team(&lds);
   const int row = blockIdx.x;
-  RowState &S = a.st[row];
-  if (a.mode == kSegBand && ((S.flags & LAPSUM_FLAG_OVERFLOW) || S.band > (unsigned long long)a.stride)) {
-    if (threadIdx.x == 0) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
-    return;
-  }
   if (!seg_active(a, row)) return;
-  locate_row<kNT>(a, row, seg_final(a, row), team);
+  locate_row<kNT>(a, row, team);
 }
 
 hipError_t launch_segment(const SegArgs &a, hipStream_t s) {
   const dim3 tiles((unsigned)a.max_tiles, (unsigned)a.rows);
-  if (a.mode == kSegBand) {
-    hipLaunchKernelGGL(seg_compact_kernel, dim3((unsigned)a.gx, (unsigned)a.rows), dim3(kNT), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   for (int pass = 0; pass < 4; ++pass) {
     hipLaunchKernelGGL(seg_hist_kernel, tiles, dim3(kNT), 0, s, a, pass);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(256 / (kNT / kWave), (unsigned)a.rows), dim3(kNT), 0, s, a, pass);

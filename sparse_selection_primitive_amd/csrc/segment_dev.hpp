@@ -1,7 +1,8 @@
 // Device routines of the large-row full-sort solver shared by the
-// multi-launch kernels (segment.hip), the one-workgroup fallback and the
-// on-chip band kernel (onchip.hip): tile loads, stable scatter of a tile,
-// tile aggregates of sorted keys, and the per-row locate + closed-form root.
+// multi-launch kernels (segment.hip), the one-workgroup fallback, the on-chip
+// band kernel (onchip.hip) and the bucketed band solve (band.hip): tile
+// loads, stable scatter of a tile, anchored aggregates of sorted runs, and
+// locate + closed-form root over a sorted range.
 // Method: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
 // section 2.2, full-sort solver.
 #pragma once
@@ -36,31 +37,12 @@ union SegLds {
 
 // ------------------------------------------------------------- row helpers
 LDEV bool seg_active(const SegArgs &a, int row) {
-  const RowState &s = a.st[row];
   if (a.mode == kSegFull) return true;
-  if (a.mode == kSegFallback) return (s.flags & LAPSUM_FLAG_FALLBACK) != 0;
-  return !(s.flags & LAPSUM_FLAG_OVERFLOW) && s.band <= (unsigned long long)a.stride;
+  return (a.st[row].flags & LAPSUM_FLAG_FALLBACK) != 0;
 }
-LDEV int64_t seg_len(const SegArgs &a, int row) {
-  if (!seg_active(a, row)) return 0;
-  if (a.mode == kSegBand) return (int64_t)a.st[row].band;
-  return a.n;
-}
-LDEV uint32_t seg_kbase(const SegArgs &a, int row) {
-  if (a.mode != kSegBand) return 0u;
-  const RowState &s = a.st[row];
-  return s.band > 0 ? s.kmin : 0u;
-}
-// digit passes this row needs: the band sorts key - kmin, so only the digits
-// spanned by its key range
-LDEV int seg_npasses(const SegArgs &a, int row) {
-  if (a.mode != kSegBand) return 4;
-  const RowState &s = a.st[row];
-  const uint32_t span = (s.band > 1 && s.kmax > s.kmin) ? s.kmax - s.kmin : 0u;
-  const int bits = span == 0u ? 1 : 32 - __clz((int)span);
-  return (bits + 7) / 8;
-}
-LDEV const uint32_t *seg_final(const SegArgs &a, int row) { return (seg_npasses(a, row) & 1) ? a.A : a.B; }
+LDEV int64_t seg_len(const SegArgs &a, int row) { return seg_active(a, row) ? a.n : 0; }
+// four 8-bit digit passes A -> B -> A -> B: the sorted keys end in B
+LDEV const uint32_t *seg_final(const SegArgs &a) { return a.B; }
 
 template <int NT>
 LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
@@ -83,11 +65,8 @@ LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
 }
 
 // key of element i of `row` read by digit pass `pass`
-LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i, uint32_t kbase) {
-  if (pass == 0) {
-    if (a.mode == kSegBand) return a.band[(int64_t)row * a.stride + i] - kbase;
-    return key_of(a.r[(int64_t)row * a.n + i]);
-  }
+LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i) {
+  if (pass == 0) return key_of(a.r[(int64_t)row * a.n + i]);
   const uint32_t *src = (pass & 1) ? a.A : a.B;
   return src[(int64_t)row * a.stride + i];
 }
@@ -97,14 +76,14 @@ LDEV uint32_t *pass_dst(const SegArgs &a, int pass) { return (pass & 1) ? a.B : 
 // Keys of one tile, wave-striped: thread (w, lane) holds tile positions
 // w*64*16 + q*64 + lane, q = 0..15, which is also their stable order.
 template <int NT>
-LDEV void load_tile(const SegArgs &a, int pass, int row, int64_t t0, int64_t len, uint32_t kbase, int shift,
+LDEV void load_tile(const SegArgs &a, int pass, int row, int64_t t0, int64_t len, int shift,
                     uint32_t (&key)[kKpt], int (&dig)[kKpt]) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
 #pragma unroll
   for (int q = 0; q < kKpt; ++q) {
     const int64_t gi = t0 + w * (kWave * kKpt) + q * kWave + lane;
     const bool valid = gi < len;
-    key[q] = valid ? load_key(a, pass, row, gi, kbase) : 0u;
+    key[q] = valid ? load_key(a, pass, row, gi) : 0u;
     dig[q] = valid ? (int)((key[q] >> shift) & 255u) : 256;
   }
 }
@@ -173,109 +152,117 @@ LDEV uint32_t scatter_tile(const uint32_t (&key)[kKpt], const int (&dig)[kKpt], 
   return tcount;
 }
 
-// Sorted keys t0 .. t0 + NT*16 of `fin` as values, blocked (16 per thread).
+// Sorted keys t0 .. t0 + NT*16 of the sorted range `src` as values, blocked
+// (16 per thread); kbase is added back to each stored key.
 template <int NT>
-LDEV int load_sorted(const SegArgs &a, const uint32_t *fin, int row, int64_t t0, int64_t len, uint32_t kbase,
-                     float (&s)[kKpt]) {
+LDEV int load_sorted_at(const uint32_t *src, int64_t t0, int64_t len, uint32_t kbase, float (&s)[kKpt]) {
   const int64_t base = t0 + (int64_t)threadIdx.x * kKpt;
   const int nv = (int)min(max(len - base, (int64_t)0), (int64_t)kKpt);
-  const uint32_t *src = fin + (int64_t)row * a.stride + base;
+  const uint32_t *p = src + base;
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e) s[e] = (e < nv) ? value_of(src[e] + kbase) : 0.0f;
+  for (int e = 0; e < kKpt; ++e) s[e] = (e < nv) ? value_of(p[e] + kbase) : 0.0f;
   return nv;
 }
-
-// Anchored aggregates of one sorted tile: P-type relative to its last key,
-// S-type relative to its first key.
 template <int NT>
-LDEV void tile_aggregate(const float (&s)[kKpt], int nv, double c, float cf, const BlockTeam<NT, 1> &team,
-                         TileAgg *out) {
-  float mul[kKpt];
+LDEV int load_sorted(const SegArgs &a, int row, int64_t t0, int64_t len, float (&s)[kKpt]) {
+  return load_sorted_at<NT>(seg_final(a) + (int64_t)row * a.stride, t0, len, 0u, s);
+}
+
+// Anchored aggregates of a sorted run held blocked by a team (lane l holds
+// its elements l*E .. l*E+E-1, nv of them valid): P-type relative to the
+// run's last key (written by the team's last lane), S-type relative to its
+// first key (written by lane 0).
+template <int E, class Team>
+LDEV void team_aggregate(const float (&s)[E], int nv, double c, float cf, const Team &team, TileAgg *out) {
+  float mul[E];
   mul[0] = 0.0f;
 #pragma unroll
-  for (int e = 1; e < kKpt; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], cf) : 0.0f;
+  for (int e = 1; e < E; ++e) mul[e] = (e < nv) ? wexpf(s[e - 1] - s[e], cf) : 0.0f;
   double pl = 0.0, sl = 0.0;
   float last = s[0];
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e)
+  for (int e = 0; e < E; ++e)
     if (e < nv) {
       pl = pl * (double)mul[e] + 1.0;
       last = s[e];
     }
 #pragma unroll
-  for (int e = kKpt - 1; e >= 0; --e)
-    if (e < nv) sl = (e + 1 < kKpt ? sl * (double)mul[e + 1] : 0.0) + 1.0;
+  for (int e = E - 1; e >= 0; --e)
+    if (e < nv) sl = (e + 1 < E ? sl * (double)mul[e + 1] : 0.0) + 1.0;
   const Pre mp{last, nv > 0 ? pl : 0.0};
   const Suf ms{s[0], nv > 0 ? sl : 0.0};
   const Pre ep = team.excl_scan(mp, c);
   const Suf es = team.excl_scan(ms, c);
-  if (threadIdx.x == NT - 1) {
+  if (team.lane == Team::kLanes - 1) {
     const Pre tp = join(ep, mp, c);
     out->aP = tp.a;
     out->sP = tp.s;
   }
-  if (threadIdx.x == 0) {
+  if (team.lane == 0) {
     const Suf tsf = join(ms, es, c);
     out->aS = tsf.a;
     out->sS = tsf.s;
   }
-  __syncthreads();
+  team.sync();
+}
+template <int NT>
+LDEV void tile_aggregate(const float (&s)[kKpt], int nv, double c, float cf, const BlockTeam<NT, 1> &team,
+                         TileAgg *out) {
+  team_aggregate<kKpt>(s, nv, c, cf, team, out);
 }
 
-// Per row: scan of the tile aggregates, threshold curve at the tile ends,
-// the balancing tile, and the closed-form root inside it (tiles of NT*16).
+// Locate + closed-form root over one sorted range of `len` keys (stored
+// minus kbase) split into tiles of NT*16 whose anchored aggregates `ta` are
+// given: scan of the tile aggregates between the outer seeds, threshold
+// curve at the tile ends, the balancing tile, and the root inside it.
+// seed_lo / seed_hi hold everything below / above the range, cR counts the
+// elements above it; first / last say whether the range starts / ends the
+// sorted segment (no knots below / above it).  tp, ts: scratch [nt].
+// Returns b on every thread.
 template <int NT>
-LDEV void locate_row(const SegArgs &a, int row, const uint32_t *fin, const BlockTeam<NT, 1> &team) {
+LDEV double locate_sorted(const uint32_t *src, int64_t len, uint32_t kbase, Pre seed_lo, Suf seed_hi, double cR,
+                          bool first, bool last, const TileAgg *ta, Pre *tp, Suf *ts, double k, double t, double c,
+                          float cf, const BlockTeam<NT, 1> &team) {
   constexpr int TT = NT * kKpt;
-  RowState &S = a.st[row];
-  const int64_t len = seg_len(a, row);
   const int nt = (int)((len + TT - 1) / TT);
-  const bool band = a.mode == kSegBand;
-  const Pre seed_lo{(float)S.a_lo, (band && S.count_lo) ? S.tail_lo : 0.0};
-  const Suf seed_hi{(float)S.a_hi, (band && S.count_hi) ? S.tail_hi : 0.0};
-  const double cR = band ? (double)S.count_hi : 0.0;
-  const TileAgg *ta = a.tagg + (int64_t)row * a.max_tiles;
-  Pre *tp = a.tpre + (int64_t)row * a.max_tiles;
-  Suf *ts = a.tsuf + (int64_t)row * a.max_tiles;
-
   Pre carry = seed_lo;
   for (int T0 = 0; T0 < nt; T0 += NT) {
     const int T = T0 + threadIdx.x;
     const Pre mine = T < nt ? Pre{ta[T].aP, ta[T].sP} : Pre{0.0f, 0.0};
-    const Pre ex = team.excl_scan(mine, a.c);
-    if (T < nt) tp[T] = join(carry, ex, a.c);
-    const Pre tot = join(ex, mine, a.c);
+    const Pre ex = team.excl_scan(mine, c);
+    if (T < nt) tp[T] = join(carry, ex, c);
+    const Pre tot = join(ex, mine, c);
     const Pre chunk{team.bcast(tot.a, NT - 1), team.bcast(tot.s, NT - 1)};
-    carry = join(carry, chunk, a.c);
+    carry = join(carry, chunk, c);
   }
   Suf carry_s = seed_hi;
   for (int T0 = ((nt - 1) / NT) * NT; nt > 0 && T0 >= 0; T0 -= NT) {
     const int T = T0 + threadIdx.x;
     const Suf mine = T < nt ? Suf{ta[T].aS, ta[T].sS} : Suf{0.0f, 0.0};
-    const Suf ex = team.excl_scan(mine, a.c);
-    if (T < nt) ts[T] = join(ex, carry_s, a.c);
-    const Suf tot = join(mine, ex, a.c);
+    const Suf ex = team.excl_scan(mine, c);
+    if (T < nt) ts[T] = join(ex, carry_s, c);
+    const Suf tot = join(mine, ex, c);
     const Suf chunk{team.bcast(tot.a, 0), team.bcast(tot.s, 0)};
-    carry_s = join(chunk, carry_s, a.c);
+    carry_s = join(chunk, carry_s, c);
   }
   __syncthreads();
   // threshold curve at the last knot of every tile
   int cnt = 0;
   for (int T = threadIdx.x; T < nt; T += NT) {
-    const Pre pl = join(tp[T], Pre{ta[T].aP, ta[T].sP}, a.c);
+    const Pre pl = join(tp[T], Pre{ta[T].aP, ta[T].sP}, c);
     const Suf sa = ts[T];
-    const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, a.c));
+    const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
     const int64_t nvT = min((int64_t)TT, len - (int64_t)T * TT);
     const int64_t j_last = (int64_t)T * TT + nvT - 1;
     const double g = 0.5 * (pl.s - 1.0) + ((double)(len - j_last) + cR) - 0.5 * s_last;
-    cnt += (g >= a.k) ? 1 : 0;
+    cnt += (g >= k) ? 1 : 0;
   }
   const int tstar = team.sum(cnt);
   const int tsel = nt == 0 ? 0 : min(tstar, nt - 1);
   float s[kKpt];
   int nv = 0;
   if (nt > 0) {
-    nv = load_sorted<NT>(a, fin, row, (int64_t)tsel * TT, len, seg_kbase(a, row), s);
+    nv = load_sorted_at<NT>(src, (int64_t)tsel * TT, len, kbase, s);
   } else {
 #pragma unroll
     for (int e = 0; e < kKpt; ++e) s[e] = 0.0f;
@@ -285,16 +272,20 @@ LDEV void locate_row(const SegArgs &a, int row, const uint32_t *fin, const Block
   part.above = (double)(len - (int64_t)tsel * TT) + cR;
   part.seed_lo = nt > 0 ? tp[tsel] : seed_lo;
   part.seed_hi = nt > 0 ? ts[tsel] : seed_hi;
-  part.first = tsel == 0;
-  part.last = tsel >= nt - 1;
-  const double b = segment_solve<kKpt>(s, nv, part, a.k, a.t, a.c, a.cf, team);
-  if (threadIdx.x == 0) {
-    S.b = b;
-    if (band) {
-      const bool hit = (b >= S.a_lo) && (b < S.a_hi);
-      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
-    }
-  }
+  part.first = first && tsel == 0;
+  part.last = last && tsel >= nt - 1;
+  return segment_solve<kKpt>(s, nv, part, k, t, c, cf, team);
+}
+
+// Per row of the full-sort path or the fallback: locate + root over the
+// whole sorted row.
+template <int NT>
+LDEV void locate_row(const SegArgs &a, int row, const BlockTeam<NT, 1> &team) {
+  const int64_t o = (int64_t)row * a.max_tiles;
+  const double b = locate_sorted<NT>(seg_final(a) + (int64_t)row * a.stride, seg_len(a, row), 0u,
+                                     Pre{0.0f, 0.0}, Suf{0.0f, 0.0}, 0.0, true, true, a.tagg + o, a.tpre + o,
+                                     a.tsuf + o, a.k, a.t, a.c, a.cf, team);
+  if (threadIdx.x == 0) a.st[row].b = b;
   __syncthreads();
 }
 
@@ -312,7 +303,7 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
     const int shift = 8 * pass;
     for (int i = threadIdx.x; i < 256; i += NT) h[i] = 0u;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < len; i += NT) atomicAdd(&h[(load_key(a, pass, row, i, 0u) >> shift) & 255u], 1u);
+    for (int64_t i = threadIdx.x; i < len; i += NT) atomicAdd(&h[(load_key(a, pass, row, i) >> shift) & 255u], 1u);
     __syncthreads();
     // running start of each digit, advanced tile by tile (thread d owns digit d)
     uint32_t run = wg_excl_scan<NT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.rk.wsum);
@@ -320,20 +311,19 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
     for (int64_t tile = 0; tile < ntiles; ++tile) {
       uint32_t key[kKpt];
       int dig[kKpt];
-      load_tile<NT>(a, pass, row, tile * TT, len, 0u, shift, key, dig);
+      load_tile<NT>(a, pass, row, tile * TT, len, shift, key, dig);
       const int vc = (int)min((int64_t)TT, len - tile * TT);
       run += scatter_tile<NT>(key, dig, shift, vc, run, dst, L.rk);
     }
   }
-  const uint32_t *fin = a.B;  // four passes
   BlockTeam<NT, 1> team(&L.tm);
   for (int64_t tile = 0; tile < ntiles; ++tile) {
     float s[kKpt];
-    const int nv = load_sorted<NT>(a, fin, row, tile * TT, len, 0u, s);
+    const int nv = load_sorted<NT>(a, row, tile * TT, len, s);
     tile_aggregate<NT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
   }
   __syncthreads();
-  locate_row<NT>(a, row, fin, team);
+  locate_row<NT>(a, row, team);
 }
 
 }  // namespace lapsum

@@ -252,7 +252,7 @@ def test_bracket_loose_delta_many_seeds(L, O):
 
 
 def test_bracket_large_band_path(L, O):
-    """A band above the on-chip capacity goes through the radix band sort."""
+    """A band above the on-chip capacity goes through the bucketed band solve."""
     g0 = np.random.Generator(np.random.PCG64(3001))
     n, k, t = 2_000_000, 20000.0, 0.01
     r = g0.standard_normal((1, n)).astype(np.float32)
@@ -261,6 +261,87 @@ def test_bracket_large_band_path(L, O):
     assert plan["band_onchip"] == 0
     res, _, _ = full_check("bracket large band", L, O, r, g, k, t, path="bracket", stats=True)
     assert res["stats"]["flags"][0].item() & L.FLAG_HIT
+
+
+# ------------------------------------------------- bucketed band solve
+# Bands above the on-chip capacity are spread over buckets by their leading
+# key bits; buckets of <= 1024 keys are sorted by one wave, larger ones by a
+# workgroup (register bitonic up to 4096 keys, LSD radix beyond).
+
+def test_bucket_band_multirow(L, O):
+    """Coder rows with the capacity forced above one workgroup: per-row
+    bucket indexing, and bitwise equal results on a second call (the
+    scatter's order inside a bucket is free)."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder()
+    assert L.plan(w.rows, w.n, w.k, w.t, path="bracket", band_capacity=65536)["band_onchip"] == 0
+    res, _, _ = full_check(w.name + " bucket band", L, O, w.r, w.g, w.k, w.t, path="bracket",
+                           band_capacity=65536, stats=True)
+    assert np.all(res["stats"]["flags"].numpy() & L.FLAG_HIT)
+    again = run(L, w.r, w.k, w.t, w.g, path="bracket", band_capacity=65536)
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(res[key], again[key]), key
+
+
+@pytest.mark.parametrize("step", [1.0 / 64, 1.0 / 512])
+def test_bucket_band_quantized_ties(L, O, step):
+    """Scores on a grid: each bucket holds whole runs of equal keys, 1.5K to
+    12K of them, so the workgroup bitonic and radix bucket sorts both run;
+    b sits near 0, so the band holds keys of both signs (and -0.0)."""
+    g0 = np.random.Generator(np.random.PCG64(3101))
+    n, t = 2_000_000, 0.01
+    r = (np.round(g0.standard_normal((1, n)) / step) * step).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = n / 2 + 12345.5
+    assert L.plan(1, n, k, t, path="bracket")["band_onchip"] == 0
+    res, _, _ = full_check(f"bucket band quantized {step}", L, O, r, g, k, t, path="bracket", stats=True)
+    st = res["stats"]
+    log(f"  band M={st['band'][0].item()} flags={st['flags'][0].item()}")
+    assert st["flags"][0].item() & L.FLAG_HIT
+
+
+def test_bucket_band_single_value(L, O):
+    """A band of one repeated value (every bucket key equal): the bucket
+    aggregates come from the count alone."""
+    g0 = np.random.Generator(np.random.PCG64(3201))
+    n, t = 1_000_000, 0.01
+    q = 350_000  # scores far below and far above; 300000 copies of 0.5 in between
+    r = np.full((1, n), 0.5, dtype=np.float32)
+    r[0, :q] = (g0.standard_normal(q) - 10.0).astype(np.float32)
+    r[0, q: 2 * q] = (g0.standard_normal(q) + 10.0).astype(np.float32)
+    g0.shuffle(r[0])
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = n / 2 + 50000.0
+    res, _, _ = full_check("bucket band single value", L, O, r, g, k, t, path="bracket", band_capacity=1 << 20,
+                           stats=True)
+    st = res["stats"]
+    log(f"  band M={st['band'][0].item()} flags={st['flags'][0].item()}")
+    assert st["flags"][0].item() & L.FLAG_HIT
+
+
+def test_bucket_band_spans_zero(L, O):
+    """b near 0 on continuous scores: the band's keys straddle the sign
+    change, so bucket widths in value differ by octave."""
+    g0 = np.random.Generator(np.random.PCG64(3301))
+    n, t = 2_000_000, 0.001
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = n / 2 + 0.25
+    res, _, _ = full_check("bucket band spans zero", L, O, r, g, k, t, path="bracket", stats=True)
+    assert res["stats"]["flags"][0].item() & L.FLAG_HIT
+
+
+def test_bucket_band_forced_miss(L, O):
+    """Certification on the bucketed band: a forced bracket below b must
+    send every row to the fallback."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=3, n=65536)
+    _, b_or = O.forward(w.r, w.k, w.t)
+    hi = float(np.min(b_or)) - 0.05
+    res, _, _ = full_check("bucket band forced miss", L, O, w.r, None, w.k, w.t, path="bracket",
+                           band_capacity=65536, bracket_override=(hi - 0.3, hi), stats=True)
+    fl = res["stats"]["flags"].numpy()
+    assert np.all(fl & L.FLAG_FALLBACK) and not np.any(fl & L.FLAG_HIT)
 
 
 def test_bracket_extreme_sampled(L, O):
