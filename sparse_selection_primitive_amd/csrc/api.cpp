@@ -87,7 +87,7 @@ struct Plan {
   bool band_onchip = false;
   // forward layout
   size_t fwd_bytes = 0;
-  size_t st = 0, samples = 0, fpart = 0, slots = 0, offs = 0;
+  size_t st = 0, samples = 0, spart = 0, fpart = 0, slots = 0, offs = 0;
   int fgx = 0;
   BandRegions bnd{};
   SegRegions full_seg{};
@@ -223,6 +223,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     if (!P.band_onchip) P.cap = round_up(P.cap, kTile);
     P.st = F.take((size_t)rows * row_state_bytes());
     P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
+    P.spart = F.take(sample_start_bytes(rows, P.m));
     P.fgx = filter_grid_x(rows, n);
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
@@ -410,11 +411,12 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     } else {
       // the sample kernel also resets the rows' state
       float *samples = reinterpret_cast<float *>(ws + P.samples);
+      uint16_t *spart = reinterpret_cast<uint16_t *>(ws + P.spart);
       tm.mark(LAPSUM_STAGE_SAMPLE, 0);
-      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, rs, LAPSUM_FLAG_BRACKET, s));
+      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, spart, rs, LAPSUM_FLAG_BRACKET, s));
       tm.mark(LAPSUM_STAGE_SAMPLE, 1);
       tm.mark(LAPSUM_STAGE_SELECT, 0);
-      LAPSUM_TRY(launch_select(samples, rows, P.m, P.lo, P.hi, rs, s));
+      LAPSUM_TRY(launch_select(samples, spart, rows, P.m, P.lo, P.hi, rs, s));
       tm.mark(LAPSUM_STAGE_SELECT, 1);
     }
     uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);

@@ -37,34 +37,105 @@ LDEV void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
   }
 }
 
-__global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ r, int64_t n, double t, int64_t m,
-                                                     uint32_t k0, uint32_t k1, float *__restrict__ samples,
-                                                     RowState *__restrict__ st, int32_t flags) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Each workgroup draws kSampleWg consecutive samples of one row (counters
+// j = group * kSampleWg + q * kSampleThreads + thread), sorts them inside the
+// workgroup by the top kCoarseBits bits of their keys, and writes them in
+// that order to its slice of `samples`, with the 16-bit start of every
+// coarse bin inside the slice to `starts`.  (The sample is a multiset: its order statistics
+// do not depend on the order it is stored in.)
+constexpr int kSampleThreads = 1024;
+constexpr int kSamplePerThread = 2;
+constexpr int kSampleWg = kSampleThreads * kSamplePerThread;
+constexpr int kCoarseBits = 10;
+constexpr int kCoarseBins = 1 << kCoarseBits;
+static_assert(kCoarseBins == kSampleThreads, "one coarse bin per sample thread");
+
+LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i)
+    if (i < w) before += wsum[i];
+  return before + inc - v;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__restrict__ r, int64_t n, double t,
+                                                                int64_t m, uint32_t k0, uint32_t k1,
+                                                                float *__restrict__ samples,
+                                                                uint16_t *__restrict__ starts,
+                                                                RowState *__restrict__ st, int32_t flags) {
+  __shared__ uint32_t cnt[kCoarseBins];
+  __shared__ uint32_t wsum[kSampleThreads / kWave];
+  __shared__ float stage[kSampleWg];
   const int64_t row = blockIdx.y;
-  if (j == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state of the row
-  if (j >= m) return;
-  uint32_t c[4] = {(uint32_t)j, (uint32_t)row, 0u, 0u};
-  philox4x32_10(c, k0, k1);
+  const int64_t g0 = (int64_t)blockIdx.x * kSampleWg;
+  if (blockIdx.x == 0 && threadIdx.x == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state
+  cnt[threadIdx.x] = 0u;
+  // indices and noise of this thread's samples first, then all the gathers
   const uint64_t nn = (uint64_t)n;
-  const uint64_t idx = ((uint64_t)c[1] * nn + (((uint64_t)c[0] * nn) >> 32)) >> 32;
-  const double u = ((double)c[2] + 0.5) * 0x1p-32;
-  const double lap = u < 0.5 ? log(2.0 * u) : -log(2.0 * (1.0 - u));
-  const double x = __dadd_rn((double)r[row * n + (int64_t)idx], __dmul_rn(t, lap));
-  samples[row * m + j] = (float)x;
+  int64_t idx[kSamplePerThread];
+  double lap[kSamplePerThread];
+#pragma unroll
+  for (int q = 0; q < kSamplePerThread; ++q) {
+    const int64_t j = g0 + q * kSampleThreads + threadIdx.x;
+    uint32_t c[4] = {(uint32_t)j, (uint32_t)row, 0u, 0u};
+    philox4x32_10(c, k0, k1);
+    idx[q] = (int64_t)(((uint64_t)c[1] * nn + (((uint64_t)c[0] * nn) >> 32)) >> 32);
+    const double u = ((double)c[2] + 0.5) * 0x1p-32;
+    lap[q] = u < 0.5 ? log(2.0 * u) : -log(2.0 * (1.0 - u));
+  }
+  float rv[kSamplePerThread];
+#pragma unroll
+  for (int q = 0; q < kSamplePerThread; ++q)
+    rv[q] = (g0 + q * kSampleThreads + threadIdx.x < m) ? r[row * n + idx[q]] : 0.0f;
+  float x[kSamplePerThread];
+  uint32_t bin[kSamplePerThread], slot[kSamplePerThread];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSamplePerThread; ++q) {
+    x[q] = (float)__dadd_rn((double)rv[q], __dmul_rn(t, lap[q]));
+    bin[q] = key_of(x[q]) >> (32 - kCoarseBits);
+    slot[q] = 0u;
+    if (g0 + q * kSampleThreads + threadIdx.x < m) slot[q] = atomicAdd(&cnt[bin[q]], 1u);
+  }
+  __syncthreads();
+  const uint32_t c = cnt[threadIdx.x];
+  const uint32_t start = block_excl_scan_u32(c, wsum);
+  starts[(row * gridDim.x + blockIdx.x) * (int64_t)kCoarseBins + threadIdx.x] = (uint16_t)start;
+  cnt[threadIdx.x] = start;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSamplePerThread; ++q)
+    if (g0 + q * kSampleThreads + threadIdx.x < m) stage[cnt[bin[q]] + slot[q]] = x[q];
+  __syncthreads();
+  const int nvalid = (int)min(m - g0, (int64_t)kSampleWg);
+  for (int i = threadIdx.x; i < nvalid; i += kSampleThreads) samples[row * m + g0 + i] = stage[i];
+}
+
+int sample_groups(int64_t m) { return (int)((m + kSampleWg - 1) / kSampleWg); }
+size_t sample_start_bytes(int64_t rows, int64_t m) {
+  return sizeof(uint16_t) * (size_t)rows * (size_t)sample_groups(m) * kCoarseBins;
 }
 
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, RowState *st, int32_t flags, hipStream_t s) {
-  const int64_t gx = (m + 255) / 256;
-  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)gx, (unsigned)rows), dim3(256), 0, s, r, n, t, m,
-                     (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, st, flags);
+                         float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s) {
+  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)sample_groups(m), (unsigned)rows), dim3(kSampleThreads), 0, s,
+                     r, n, t, m, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, starts, st,
+                     flags);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------- order statistics
 // One workgroup of 1024 threads per row selects the ranks lo-1 and hi-1
-// (0-based) of the m samples, by key.  A histogram of the key's top 15 bits
+// (0-based) of the m samples, by key.  General path (any m):  A histogram of the key's top 15 bits
 // in LDS gives each rank's bin and its rank inside the bin; the bin's keys
 // are then gathered and ranked directly when few (<= kSelectCap), while a
 // crowded bin is refined by histograms of the next 9 bits, then the last 8.
@@ -105,23 +176,6 @@ LDEV void for_each_sample(const float *X, int64_t m, F &&f) {
       }
     }
   }
-}
-
-LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += y;
-  }
-  __syncthreads();
-  if (lane == kWave - 1) wsum[w] = inc;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < kSelThreads / kWave; ++i)
-    if (i < w) before += wsum[i];
-  return before + inc - v;
 }
 
 // Bins holding ranks R[0] and R[1] (where want[t]) of the LDS histogram of
@@ -263,8 +317,248 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
   }
 }
 
-hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
-                         hipStream_t s) {
+// Fast path, m <= kSelMaxGroups * kSampleWg: the sample arrives bucketed by
+// coarse bin inside each sample workgroup, with the bins' starts, so this
+// workgroup reads the starts (64 KB) and then only the keys of the two
+// target bins.  A crowded bin is refined by histograms of the next (up to)
+// 11 bits until at most kSortCand keys share the prefix; one wave sorts
+// those in registers and reads the rank off.  Scans over bins are done by
+// one wave (no workgroup barriers inside).
+constexpr int kSelMaxGroups = 32;
+constexpr int kCandCap = 8192;
+constexpr int kFineBins = 2048;
+constexpr int kSortCand = 16 * kWave;  // largest key set one wave sorts in registers
+
+struct SelectBucketLds {
+  uint16_t start[kSelMaxGroups][kCoarseBins];  // bin starts inside each group's slice
+  uint32_t hist[kFineBins];
+  uint32_t cand[kCandCap];
+  uint32_t fin[2][kSortCand];
+  uint32_t goff[2][kSelMaxGroups + 1];  // candidate index where each group's part of the bin starts
+  uint32_t bin[2], rank[2], count[2];
+  uint32_t nfin[2], result[2];
+};
+
+// One wave sorts the nf <= 64*E keys f[] in registers (blocked, E per lane)
+// and writes the key of rank R to *out.
+template <int E>
+LDEV void wave_sort_pick(const uint32_t *f, int nf, uint32_t R, uint32_t *out) {
+  WaveTeam<kWave> team;
+  const int base = team.lane * E;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = base + e < nf ? f[base + e] : 0xFFFFFFFFu;
+  bitonic_sort<E>(key, team);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((uint32_t)(base + e) == R) *out = key[e];
+}
+
+// One wave: for each wanted target tg, the bin of rank R[tg] in the LDS
+// histogram h of NB (a multiple of 64) counts, its rank inside the bin and
+// its count, to bin/rank/count[tg].  Lane l owns bins l*PER .. l*PER+PER-1
+// (summed in a rotated order: no bank conflicts).
+template <int NB>
+LDEV void wave_locate(const uint32_t *h, const uint32_t (&R)[2], const bool (&want)[2], SelectBucketLds &L) {
+  constexpr int PER = NB / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b0 = lane * PER;
+  uint32_t c[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) c[q] = h[b0 + ((q + lane) & (PER - 1))];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) local += c[q];
+  uint32_t inc = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  const uint32_t before = inc - local;
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg] || R[tg] < before || R[tg] >= before + local) continue;
+    uint32_t acc = before;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const uint32_t cq = h[b0 + q];
+      if (R[tg] >= acc && R[tg] < acc + cq) {
+        L.bin[tg] = (uint32_t)(b0 + q);
+        L.rank[tg] = R[tg] - acc;
+        L.count[tg] = cq;
+      }
+      acc += cq;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_bucket_kernel(const float *__restrict__ samples,
+                                                                    const uint16_t *__restrict__ starts,
+                                                                    int groups, int64_t m, int64_t lo, int64_t hi,
+                                                                    RowState *__restrict__ st) {
+  __shared__ SelectBucketLds L;
+  const int64_t row = blockIdx.x;
+  const float *X = samples + row * m;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  constexpr int kWaves = kSelThreads / kWave;
+  {
+    // bin starts of every group (16-bit, read as pairs): thread t reads
+    // pair t & 511 of groups (t >> 9), (t >> 9) + 2, ...
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(starts + row * (int64_t)groups * kCoarseBins);
+    const int col = threadIdx.x & (kCoarseBins / 2 - 1), g0 = threadIdx.x / (kCoarseBins / 2);
+    constexpr int kStep = kSelThreads / (kCoarseBins / 2);
+    uint32_t v[kSelMaxGroups / kStep];
+#pragma unroll
+    for (int j = 0; j < kSelMaxGroups / kStep; ++j) {
+      const int g = g0 + kStep * j;
+      v[j] = g < groups ? s32[g * (kCoarseBins / 2) + col] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelMaxGroups / kStep; ++j) {
+      const int g = g0 + kStep * j;
+      if (g < groups) reinterpret_cast<uint32_t *>(L.start[g])[col] = v[j];
+    }
+  }
+  __syncthreads();
+  // count of bin b in group g: the next start (or the group's size) minus this one
+  auto gcount = [&](int g, uint32_t b) -> uint32_t {
+    const uint32_t end = b + 1 < (uint32_t)kCoarseBins
+                             ? (uint32_t)L.start[g][b + 1]
+                             : (uint32_t)min((int64_t)kSampleWg, m - (int64_t)g * kSampleWg);
+    return end - (uint32_t)L.start[g][b];
+  };
+  // bin totals as differences of the starts summed over the groups
+  {
+    uint32_t S = 0u;
+    for (int g = 0; g < groups; ++g) S += L.start[g][threadIdx.x];
+    L.hist[threadIdx.x] = S;  // kCoarseBins == kSelThreads
+  }
+  __syncthreads();
+  {
+    const uint32_t nxt = threadIdx.x + 1 < (unsigned)kCoarseBins ? L.hist[threadIdx.x + 1] : (uint32_t)m;
+    const uint32_t tot = nxt - L.hist[threadIdx.x];
+    __syncthreads();
+    L.hist[threadIdx.x] = tot;
+  }
+  __syncthreads();
+  const bool want[2] = {lo >= 1, hi <= m};
+  uint32_t R[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
+  if (w == 0) {
+    // target bins, then the groups' offsets into each target's candidate list
+    wave_locate<kCoarseBins>(L.hist, R, want, L);
+    __builtin_amdgcn_wave_barrier();
+    for (int tg = 0; tg < 2; ++tg) {
+      if (!want[tg]) continue;
+      const uint32_t c = lane < groups ? gcount(lane, L.bin[tg]) : 0u;
+      uint32_t inc = c;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += y;
+      }
+      if (lane <= groups) L.goff[tg][lane] = inc - c;
+    }
+  }
+  __syncthreads();
+  uint32_t B[2], nc[2];
+  for (int tg = 0; tg < 2; ++tg) {
+    B[tg] = want[tg] ? L.bin[tg] : 0u;
+    R[tg] = want[tg] ? L.rank[tg] : 0u;
+    nc[tg] = want[tg] ? L.count[tg] : 0u;
+  }
+  // candidates of both targets into LDS (once when they share a bin)
+  const bool same = want[0] && want[1] && B[0] == B[1];
+  const bool fit[2] = {nc[0] <= (uint32_t)kCandCap,
+                       same ? nc[0] <= (uint32_t)kCandCap
+                            : nc[1] <= (uint32_t)kCandCap - (nc[0] <= (uint32_t)kCandCap ? nc[0] : 0u)};
+  const uint32_t cbase[2] = {0u, same ? 0u : (fit[0] ? nc[0] : 0u)};
+  auto cand_global = [&](int tg, uint32_t i) -> uint32_t {
+    int lo_g = 0, hi_g = groups - 1;  // last group with goff <= i
+    while (lo_g < hi_g) {
+      const int mid = (lo_g + hi_g + 1) >> 1;
+      if (L.goff[tg][mid] <= i) lo_g = mid;
+      else hi_g = mid - 1;
+    }
+    return key_of(X[(int64_t)lo_g * kSampleWg + L.start[lo_g][B[tg]] + (i - L.goff[tg][lo_g])]);
+  };
+  {
+    const uint32_t n0 = (want[0] && fit[0]) ? nc[0] : 0u;
+    const uint32_t n1 = (want[1] && fit[1] && !same) ? nc[1] : 0u;
+    for (uint32_t i = threadIdx.x; i < n0 + n1; i += kSelThreads) {
+      const int tg = i < n0 ? 0 : 1;
+      const uint32_t j = i < n0 ? i : i - n0;
+      L.cand[cbase[tg] + j] = cand_global(tg, j);
+    }
+  }
+  __syncthreads();
+  auto cand_at = [&](int tg, uint32_t i) -> uint32_t { return fit[tg] ? L.cand[cbase[tg] + i] : cand_global(tg, i); };
+  // refine a crowded bin by histograms of the next (up to) 11 bits
+  uint32_t prefix[2] = {B[0], B[1]};
+  int shift[2] = {32 - kCoarseBits, 32 - kCoarseBits};
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;
+    uint32_t nct = nc[tg];
+    while (nct > (uint32_t)kSortCand && shift[tg] > 0) {
+      const int nb = shift[tg] < 11 ? shift[tg] : 11;
+      const int sh = shift[tg] - nb;
+      for (int i = threadIdx.x; i < kFineBins; i += kSelThreads) L.hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < nc[tg]; i += kSelThreads) {
+        const uint32_t kk = cand_at(tg, i);
+        if ((kk >> shift[tg]) == prefix[tg]) atomicAdd(&L.hist[(kk >> sh) & ((1u << nb) - 1u)], 1u);
+      }
+      __syncthreads();
+      const uint32_t Rq[2] = {R[tg], 0u};
+      const bool wq[2] = {true, false};
+      if (w == 0) wave_locate<kFineBins>(L.hist, Rq, wq, L);
+      __syncthreads();
+      prefix[tg] = (prefix[tg] << nb) | L.bin[0];
+      R[tg] = L.rank[0];
+      nct = L.count[0];
+      shift[tg] = sh;
+      __syncthreads();
+    }
+  }
+  // the keys sharing each target's final prefix (at most kSortCand), sorted
+  // by one wave; both targets share the sort when their prefixes agree
+  const bool live[2] = {want[0] && shift[0] > 0, want[1] && shift[1] > 0};
+  const bool share = live[0] && live[1] && shift[0] == shift[1] && prefix[0] == prefix[1];
+  if (threadIdx.x < 2) L.nfin[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!live[tg] || (tg == 1 && share)) continue;
+    for (uint32_t i = threadIdx.x; i < nc[tg]; i += kSelThreads) {
+      const uint32_t kk = cand_at(tg, i);
+      if ((kk >> shift[tg]) == prefix[tg]) L.fin[tg][atomicAdd(&L.nfin[tg], 1u)] = kk;  // <= kSortCand
+    }
+  }
+  __syncthreads();
+  if (w < 2 && live[w]) {
+    const int src = (w == 1 && share) ? 0 : w;
+    const int nf = (int)L.nfin[src];
+    const uint32_t *f = L.fin[src];
+    if (nf <= 64) wave_sort_pick<1>(f, nf, R[w], &L.result[w]);
+    else if (nf <= 128) wave_sort_pick<2>(f, nf, R[w], &L.result[w]);
+    else if (nf <= 256) wave_sort_pick<4>(f, nf, R[w], &L.result[w]);
+    else if (nf <= 512) wave_sort_pick<8>(f, nf, R[w], &L.result[w]);
+    else wave_sort_pick<16>(f, nf, R[w], &L.result[w]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r0 = live[0] ? L.result[0] : prefix[0];
+    const uint32_t r1 = live[1] ? L.result[1] : prefix[1];
+    st[row].a_lo = want[0] ? (double)value_of(r0) : -INFINITY;
+    st[row].a_hi = want[1] ? (double)value_of(r1) : INFINITY;
+  }
+}
+
+hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
+                         int64_t hi, RowState *st, hipStream_t s) {
+  if (sample_groups(m) <= kSelMaxGroups) {
+    hipLaunchKernelGGL(select_bucket_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, s, samples, starts,
+                       sample_groups(m), m, lo, hi, st);
+    return hipGetLastError();
+  }
   static bool attr_set = false;
   const size_t lds = sizeof(SelectLds);
   if (!attr_set) {

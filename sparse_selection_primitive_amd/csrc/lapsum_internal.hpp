@@ -83,9 +83,10 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
                                   float *dk, lapsum_row_stats *stats, hipStream_t s);
 bool onchip_backward_supported(int64_t n);
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, RowState *st, int32_t flags, hipStream_t s);
-hipError_t launch_select(const float *samples, int64_t rows, int64_t m, int64_t lo, int64_t hi, RowState *st,
-                         hipStream_t s);
+                         float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s);
+size_t sample_start_bytes(int64_t rows, int64_t m);
+hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
+                         int64_t hi, RowState *st, hipStream_t s);
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
                          uint32_t *offs, int64_t cap, void *partials, int grid_x, hipStream_t s);
 int filter_grid_x(int64_t rows, int64_t n);

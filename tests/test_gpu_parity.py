@@ -212,6 +212,34 @@ def test_bracket_attack(L, O):
     log(f"  band M={st['band'][0].item()} a=[{st['a_lo'][0].item():.6f}, {st['a_hi'][0].item()}]")
 
 
+def _row_case(kind, n, seed):
+    g0 = np.random.Generator(np.random.PCG64(seed))
+    if kind == "normal":
+        r = g0.standard_normal((1, n))
+    elif kind == "grid":  # 1/8 grid: samples tie exactly when t is far below the grid
+        r = np.round(g0.standard_normal((1, n)) * 8.0) / 8.0
+    else:
+        raise ValueError(kind)
+    return r.astype(np.float32), g0.standard_normal((1, n)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind,k_frac,t,m_log2", [
+    ("normal", 0.5, 0.01, 0),      # median: crowded coarse bins, refined twice
+    ("grid", 1.0 / 3.0, 1e-12, 0),  # every sample on the grid: selection ends on a whole key
+    ("normal", 0.01, 0.01, 18),    # sample above the register-resident size
+    ("normal", 0.2, 0.05, 4),      # 16 samples
+])
+def test_bracket_select_paths(L, O, kind, k_frac, t, m_log2):
+    """Bracket ends against the oracle's own Philox sample and order
+    statistics, then full parity, over the selection paths."""
+    n = 1_000_000
+    r, g = _row_case(kind, n, 3401)
+    k = k_frac * n
+    opts = dict(path="bracket", stats=True, sample_log2=m_log2) if m_log2 else dict(path="bracket", stats=True)
+    res, _, _ = full_check(f"select {kind} k/n={k_frac:.3g} m_log2={m_log2}", L, O, r, g, k, t, **opts)
+    check_bracket_stats(kind, L, O, r, k, t, res["stats"], seed=0, m_log2=m_log2 or None)
+
+
 def test_bracket_forced_miss_falls_back(L, O):
     """A bracket that excludes b must be caught by certification and the
     full-sort fallback must still meet every tolerance."""
