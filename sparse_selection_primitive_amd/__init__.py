@@ -74,6 +74,10 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise LapsumError(f"{LIB_PATH} is missing: build it with `python -m sparse_selection_primitive_amd.build`")
+    # torch first: the library must bind to the HIP runtime torch already
+    # loaded (its own copy of libamdhip64), or streams and device pointers
+    # would belong to a second runtime in the same process
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.lapsum_options_init.argtypes = [ctypes.POINTER(Options)]

@@ -7,9 +7,9 @@
 //    the binomial order statistics X_(lo), X_(hi) as the bracket [a_L, a_R);
 //  step 2, stream and filter -- filter_kernel reads every score once: below
 //    a_L it adds e^{(r - a_L)/t} to S_L, at or above a_R it adds
-//    e^{-(r - a_R)/t} to S_R, and in between it appends the key to the band
-//    (wave ballot, one atomic per wave).  Tail sums are fp64 and finalized in
-//    a fixed order by the last block.
+//    e^{-(r - a_R)/t} to S_R, and in between it appends the key to its
+//    workgroup's band slot; filter_finalize_kernel adds the workgroups'
+//    partial sums and counts per row in a fixed order (fp64).
 //
 // Random numbers: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
 // key (seed low, seed high) and counter (j, row, 0, 0): words x0, x1 give
@@ -574,40 +574,61 @@ hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t r
 // --------------------------------------------------------- stream & filter
 struct FilterPartial {
   double sl, sr;
-  unsigned long long cl, cr;
+  unsigned long long cl;      // scores below a_L
   uint32_t cnt;       // band keys this block found (may exceed kBandSlot)
   uint32_t kmn, kmx;  // key range of those band keys
   uint32_t pad;
 };
-
-LDEV void filter_one(float x, float aL, float aR, float cf, float &fl, float &fr, uint32_t &cl, uint32_t &cr,
-                     bool &mid) {
-  const bool lo = x < aL;
-  const bool hi = x >= aR;
-  const float z = lo ? (x - aL) : (aR - x);  // <= 0 whenever it is used
-  const float w = __builtin_amdgcn_exp2f(z * cf);
-  fl += lo ? w : 0.0f;
-  fr += hi ? w : 0.0f;
-  cl += lo ? 1u : 0u;
-  cr += hi ? 1u : 0u;
-  mid = !lo && !hi;
-}
 
 LDEV uint32_t mbcnt64(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // One coalesced pass over the row.  Band keys go to this block's own slot
-// (positions reserved by an LDS counter, one LDS atomic per wave); the tail
-// sums, counts and the band key range go to the block's partial.  No global
-// atomics: the per-row finalize adds the partials in a fixed order and turns
-// the slot counts into offsets.
+// (positions reserved by an LDS counter, one LDS atomic per wave and group
+// of elements that holds any); the tail sums and the band key range go to
+// the block's partial, the count below a_L is taken from wave ballots.  No
+// global atomics: the per-row finalize adds the partials in a fixed order,
+// derives the count above a_R and turns the slot counts into offsets.
+template <bool CHECK>
+LDEV void filter_items(const float (&x)[4 * kUnroll], const bool (&ok)[4 * kUnroll], float aL, float aR, float cf,
+                       double &sl, double &sr, unsigned long long &cl, uint32_t &kmn, uint32_t &kmx,
+                       uint32_t *slot, uint32_t &lcount) {
+  float fl = 0.0f, fr = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4 * kUnroll; ++q) {
+    const bool valid = !CHECK || ok[q];
+    const bool lo = valid && x[q] < aL;
+    const bool hi = valid && x[q] >= aR;
+    const float z = lo ? (x[q] - aL) : (aR - x[q]);  // <= 0 whenever it is used
+    const float w = __builtin_amdgcn_exp2f(z * cf);
+    fl += lo ? w : 0.0f;
+    fr += hi ? w : 0.0f;
+    cl += (unsigned long long)__popcll(__ballot(lo));
+    const unsigned long long mq = __ballot(valid && !lo && !hi);
+    if (mq) {  // wave-uniform: some lane holds a band key at position q
+      uint32_t base = 0u;
+      if (lane_id() == __ffsll((long long)mq) - 1) base = atomicAdd(&lcount, (uint32_t)__popcll(mq));
+      base = __shfl(base, __ffsll((long long)mq) - 1, kWave);
+      if ((mq >> lane_id()) & 1ull) {
+        const uint32_t pos = base + mbcnt64(mq);
+        const uint32_t kk = key_of(x[q]);
+        if (pos < (uint32_t)kBandSlot) slot[pos] = kk;  // beyond the slot: counted, row falls back
+        kmn = min(kmn, kk);
+        kmx = max(kmx, kk);
+      }
+    }
+  }
+  sl += (double)fl;
+  sr += (double)fr;
+}
+
 __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__restrict__ r, int64_t n,
                                                                 const RowState *__restrict__ st,
                                                                 uint32_t *__restrict__ slots,
                                                                 FilterPartial *__restrict__ part, int gx, double t) {
   __shared__ double lds_d[2 * kStreamThreads / kWave];
-  __shared__ unsigned long long lds_c[2 * kStreamThreads / kWave];
+  __shared__ unsigned long long lds_c[kStreamThreads / kWave];
   __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
   __shared__ uint32_t lcount;
   const int64_t row = blockIdx.y;
@@ -620,22 +641,44 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   uint32_t *slot = slots + ((int64_t)row * gx + blockIdx.x) * kBandSlot;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
   double sl = 0.0, sr = 0.0;
-  uint32_t cl = 0, cr = 0;
+  unsigned long long cl = 0;  // wave-uniform
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 
   typedef float f4 __attribute__((ext_vector_type(4)));
   const bool vec = (n & 3) == 0 && (((uintptr_t)r & 15u) == 0);
   const int64_t nitems = vec ? (n >> 2) : n;
+  bool ok[4 * kUnroll];
+  float x[4 * kUnroll];
   // kUnroll items (16 B each on the vector path) per thread and iteration,
-  // all loads issued before any is used
-  for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < nitems;
-       i0 += stride * kUnroll) {
-    float x[4 * kUnroll];
+  // all loads issued before any is used; whole waves of full iterations
+  // skip the bounds checks
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x;
+  if (vec) {
+    // the wave's last item of this iteration is i0 - lane + 63 + (kUnroll-1)*kStreamThreads
+    for (; i0 - lane + (kWave - 1) + (kUnroll - 1) * kStreamThreads < nitems; i0 += stride * kUnroll) {
+      f4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr) + i0 + u * kStreamThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        x[4 * u] = v[u].x;
+        x[4 * u + 1] = v[u].y;
+        x[4 * u + 2] = v[u].z;
+        x[4 * u + 3] = v[u].w;
+      }
+      filter_items<false>(x, ok, aL, aR, cf, sl, sr, cl, kmn, kmx, slot, lcount);
+    }
+  }
+  // the rest (and every item of the scalar path), with bounds checks
+  for (; i0 - lane < nitems; i0 += stride * kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = i0 + u * kStreamThreads;
       f4 v = {0.f, 0.f, 0.f, 0.f};
-      if (i < nitems) {
+      const bool in = i < nitems;
+      if (in) {
         if (vec) v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr) + i);
         else v.x = rr[i];
       }
@@ -643,57 +686,19 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
       x[4 * u + 1] = v.y;
       x[4 * u + 2] = v.z;
       x[4 * u + 3] = v.w;
+      ok[4 * u] = in;
+      ok[4 * u + 1] = in && vec;
+      ok[4 * u + 2] = in && vec;
+      ok[4 * u + 3] = in && vec;
     }
-    float fl = 0.0f, fr = 0.0f;
-    bool mid[4 * kUnroll];
-    bool any = false;
-#pragma unroll
-    for (int q = 0; q < 4 * kUnroll; ++q) {
-      const int64_t i = i0 + (q / 4) * kStreamThreads;
-      const bool ok = i < nitems && (vec || (q & 3) == 0);
-      mid[q] = false;
-      if (ok) filter_one(x[q], aL, aR, cf, fl, fr, cl, cr, mid[q]);
-      any |= mid[q];
-    }
-    sl += (double)fl;
-    sr += (double)fr;
-    const unsigned long long wany = __ballot(any);
-    if (wany) {
-      const unsigned long long active = __ballot(1);
-      const int leader = __ffsll((long long)active) - 1;
-      unsigned long long mq[4 * kUnroll];
-      uint32_t tot = 0;
-#pragma unroll
-      for (int q = 0; q < 4 * kUnroll; ++q) {
-        mq[q] = __ballot(mid[q]);
-        tot += (uint32_t)__popcll(mq[q]);
-      }
-      uint32_t base = 0u;
-      if (lane_id() == leader) base = atomicAdd(&lcount, tot);
-      base = __shfl(base, leader, kWave);
-      uint32_t off = base;
-#pragma unroll
-      for (int q = 0; q < 4 * kUnroll; ++q) {
-        if (mid[q]) {
-          const uint32_t pos = off + mbcnt64(mq[q]);
-          const uint32_t kk = key_of(x[q]);
-          if (pos < (uint32_t)kBandSlot) slot[pos] = kk;  // beyond the slot: counted, row falls back
-          kmn = min(kmn, kk);
-          kmx = max(kmx, kk);
-        }
-        off += (uint32_t)__popcll(mq[q]);
-      }
-    }
+    filter_items<true>(x, ok, aL, aR, cf, sl, sr, cl, kmn, kmx, slot, lcount);
   }
 
-  // block reduction (fixed order)
-  unsigned long long ccl = cl, ccr = cr;
+  // block reduction (fixed order); cl is already per wave
 #pragma unroll
   for (int msk = 1; msk < kWave; msk <<= 1) {
     sl += __shfl_xor(sl, msk, kWave);
     sr += __shfl_xor(sr, msk, kWave);
-    ccl += __shfl_xor(ccl, msk, kWave);
-    ccr += __shfl_xor(ccr, msk, kWave);
     kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, msk, kWave));
     kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, msk, kWave));
   }
@@ -701,8 +706,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   if ((threadIdx.x & (kWave - 1)) == 0) {
     lds_d[2 * w] = sl;
     lds_d[2 * w + 1] = sr;
-    lds_c[2 * w] = ccl;
-    lds_c[2 * w + 1] = ccr;
+    lds_c[w] = cl;
     lds_k[2 * w] = kmn;
     lds_k[2 * w + 1] = kmx;
   }
@@ -712,14 +716,12 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
     fp.sl = 0.0;
     fp.sr = 0.0;
     fp.cl = 0;
-    fp.cr = 0;
     fp.kmn = 0xFFFFFFFFu;
     fp.kmx = 0u;
     for (int i = 0; i < kStreamThreads / kWave; ++i) {
       fp.sl += lds_d[2 * i];
       fp.sr += lds_d[2 * i + 1];
-      fp.cl += lds_c[2 * i];
-      fp.cr += lds_c[2 * i + 1];
+      fp.cl += lds_c[i];
       fp.kmn = min(fp.kmn, lds_k[2 * i]);
       fp.kmx = max(fp.kmx, lds_k[2 * i + 1]);
     }
@@ -734,11 +736,11 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
 // slot that overflowed, or M beyond the band capacity, sends the row to the
 // full-sort fallback.
 __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const FilterPartial *__restrict__ part,
-                                                                         int gx, int64_t cap,
+                                                                         int gx, int64_t n, int64_t cap,
                                                                          RowState *__restrict__ st,
                                                                          uint32_t *__restrict__ offs) {
   __shared__ double lds_d[2 * kStreamThreads / kWave];
-  __shared__ unsigned long long lds_c[2 * kStreamThreads / kWave];
+  __shared__ unsigned long long lds_c[kStreamThreads / kWave];
   __shared__ uint32_t lds_k[3 * kStreamThreads / kWave];
   __shared__ uint32_t wsum[kStreamThreads / kWave];
   const int64_t row = blockIdx.x;
@@ -748,7 +750,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
   const int per = (gx + kStreamThreads - 1) / kStreamThreads;
   const int b0 = threadIdx.x * per;
   double a = 0.0, b = 0.0;
-  unsigned long long c0 = 0, c1 = 0;
+  unsigned long long c0 = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, csum = 0u, big = 0u;
   for (int i = 0; i < per; ++i) {
     const int j = b0 + i;
@@ -757,7 +759,6 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
       a += fp.sl;
       b += fp.sr;
       c0 += fp.cl;
-      c1 += fp.cr;
       mn = min(mn, fp.kmn);
       mx = max(mx, fp.kmx);
       csum += fp.cnt;
@@ -793,7 +794,6 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
     a += __shfl_xor(a, msk, kWave);
     b += __shfl_xor(b, msk, kWave);
     c0 += __shfl_xor(c0, msk, kWave);
-    c1 += __shfl_xor(c1, msk, kWave);
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, msk, kWave));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, msk, kWave));
     big |= (uint32_t)__shfl_xor((int)big, msk, kWave);
@@ -801,8 +801,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
   if (lane == 0) {
     lds_d[2 * w] = a;
     lds_d[2 * w + 1] = b;
-    lds_c[2 * w] = c0;
-    lds_c[2 * w + 1] = c1;
+    lds_c[w] = c0;
     lds_k[3 * w] = mn;
     lds_k[3 * w + 1] = mx;
     lds_k[3 * w + 2] = big;
@@ -810,13 +809,12 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
   __syncthreads();
   if (threadIdx.x == 0) {
     double ta = 0.0, tb = 0.0;
-    unsigned long long tc0 = 0, tc1 = 0;
+    unsigned long long tc0 = 0;
     uint32_t tmn = 0xFFFFFFFFu, tmx = 0u, tbig = 0u;
     for (int i = 0; i < kStreamThreads / kWave; ++i) {
       ta += lds_d[2 * i];
       tb += lds_d[2 * i + 1];
-      tc0 += lds_c[2 * i];
-      tc1 += lds_c[2 * i + 1];
+      tc0 += lds_c[i];
       tmn = min(tmn, lds_k[3 * i]);
       tmx = max(tmx, lds_k[3 * i + 1]);
       tbig |= lds_k[3 * i + 2];
@@ -825,7 +823,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
     S.tail_lo = ta;
     S.tail_hi = tb;
     S.count_lo = tc0;
-    S.count_hi = tc1;
+    S.count_hi = (unsigned long long)n - tc0 - total;  // every score is below, inside or above
     S.band = total;
     S.kmin = tmn;
     S.kmax = tmx;
@@ -856,7 +854,7 @@ hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(filter_finalize_kernel, dim3((unsigned)rows), dim3(kStreamThreads), 0, s,
-                     reinterpret_cast<const FilterPartial *>(partials), grid_x, cap, st, offs);
+                     reinterpret_cast<const FilterPartial *>(partials), grid_x, n, cap, st, offs);
   return hipGetLastError();
 }
 
