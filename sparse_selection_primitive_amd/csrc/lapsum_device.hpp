@@ -79,29 +79,42 @@ LDEV Suf join(Suf l, Suf r, double c) {
 // ln P and ln Q (either may be -inf for an empty side).  Logs are used
 // throughout so that sums shifted by e^{-delta/t} far below the fp32/fp64
 // range (t far below the gaps between scores) still place b correctly.
-// ln(|e| + sqrt(e^2 + PQ)) is formed relative to max(ln|e|, ln sqrt(PQ)) so
-// that neither a tiny nor a huge PQ loses digits.
+// With a = ln|c-k| and h = ln sqrt(PQ), ln(|c-k| + sqrt((c-k)^2 + PQ)) is
+// m + ln(u + sqrt(1 + r^2)), m = max(a, h), r = e^{min(a,h) - m} <= 1 and
+// u = 1 when a >= h, else r: no digits are lost to a tiny or huge PQ.
+//
+// Accuracy: b only needs ln y to about 1e-7 absolute (an error d in ln y
+// moves b by t*d and the budget by at most d relative), so the logs below
+// take the binary exponent exactly in fp64 and only the log of a mantissa in
+// [0.5, 1) or of a value in [1, 1 + sqrt 2] in fp32 (absolute error ~1e-7);
+// every sum and difference stays in fp64.
+constexpr double kLn2 = 0.69314718055994530942;
+LDEV double log_pos(double v) {  // ln v, v > 0 finite
+  int ex;
+  const double mt = frexp(v, &ex);  // v = mt 2^ex, mt in [0.5, 1)
+  return (double)ex * kLn2 + (double)__logf((float)mt);
+}
 LDEV double solve_root(double x, double lnP, double lnQ, double cnt, double k, double t) {
   const double e = cnt - k;
   const double h = 0.5 * (lnP + lnQ);
-  const double a = e != 0.0 ? log(fabs(e)) : -INFINITY;
+  const double a = e != 0.0 ? log_pos(fabs(e)) : -INFINITY;
   const double m = fmax(a, h);
-  double L;
-  if (m == -INFINITY) {
-    L = -INFINITY;
-  } else {
-    const double ea = exp(a - m), eh = exp(h - m);
-    L = m + log(ea + sqrt(ea * ea + eh * eh));
+  double L = -INFINITY;
+  if (m != -INFINITY) {
+    const float r = __expf((float)(fmin(a, h) - m));  // in [0, 1]
+    L = m + (double)__logf((a >= h ? 1.0f : r) + sqrtf(1.0f + r * r));
   }
   const double lny = (e >= 0.0) ? (L - lnQ) : (lnP - L);
   return x + t * lny;
 }
-LDEV double safe_log(double v) { return v > 0.0 ? log(v) : -INFINITY; }
+LDEV double safe_log(double v) { return v > 0.0 ? log_pos(v) : -INFINITY; }
 
 // --------------------------------------------------------- wave shuffles
+// DPP lane move inside rows of 16 lanes (every pattern used here reads a
+// lane of the same row, so no lane is left without a source)
 template <int CTRL>
 LDEV uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 template <int PATTERN>
 LDEV uint32_t swz(uint32_t v) {
@@ -139,39 +152,83 @@ struct WaveTeam {
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[e] = xor_lanes<MASK>(src[REV ? E - 1 - e : e]);
   }
+  // Team-local lane moves.  Teams inside one DPP row (LANES <= 16) use DPP:
+  // row_shr / row_shl for shifts, quad_perm and mirrors for the butterfly
+  // (any pairing of the halves serves a sum); wider teams use ds_bpermute.
+  template <int OFF>
+  LDEV static uint32_t up(uint32_t v) {
+    if constexpr (LANES <= 16) return dpp<0x110 + OFF>(v);
+    else return (uint32_t)__shfl_up((int)v, OFF, LANES);
+  }
+  template <int OFF>
+  LDEV static uint32_t down(uint32_t v) {
+    if constexpr (LANES <= 16) return dpp<0x100 + OFF>(v);
+    else return (uint32_t)__shfl_down((int)v, OFF, LANES);
+  }
+  template <int M>
+  LDEV static uint32_t pair(uint32_t v) {  // partner of the butterfly step M
+    if constexpr (LANES <= 16) return xor_lanes<M == 4 ? 7 : (M == 8 ? 15 : M)>(v);
+    else return (uint32_t)__shfl_xor((int)v, M, LANES);
+  }
+  template <int OFF, class F>
+  LDEV static double move64(double v, F f) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = f((uint32_t)u), hi = f((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  }
+  template <int M>
+  LDEV static void sum_steps(int &v) {
+    if constexpr (M < LANES) {
+      v += (int)pair<M>((uint32_t)v);
+      sum_steps<2 * M>(v);
+    }
+  }
+  template <int M>
+  LDEV static void sum_steps(double &v) {
+    if constexpr (M < LANES) {
+      v += move64<M>(v, [](uint32_t x) { return pair<M>(x); });
+      sum_steps<2 * M>(v);
+    }
+  }
   LDEV int sum(int v) const {
-#pragma unroll
-    for (int m = 1; m < LANES; m <<= 1) v += __shfl_xor(v, m, LANES);
+    sum_steps<1>(v);
     return v;
   }
   LDEV double sum(double v) const {
-#pragma unroll
-    for (int m = 1; m < LANES; m <<= 1) v += __shfl_xor(v, m, LANES);
+    sum_steps<1>(v);
     return v;
   }
   LDEV double bcast(double v, int src) const { return __shfl(v, src, LANES); }
   LDEV float bcast(float v, int src) const { return __shfl(v, src, LANES); }
   LDEV void sync() const {}
 
+  template <int OFF>
+  LDEV void pre_steps(Pre &inc, double c) const {
+    if constexpr (OFF < LANES) {
+      const Pre y{__uint_as_float(up<OFF>(__float_as_uint(inc.a))), move64<OFF>(inc.s, [](uint32_t x) { return up<OFF>(x); })};
+      if (lane >= OFF) inc = join(y, inc, c);
+      pre_steps<2 * OFF>(inc, c);
+    }
+  }
+  template <int OFF>
+  LDEV void suf_steps(Suf &inc, double c) const {
+    if constexpr (OFF < LANES) {
+      const Suf y{__uint_as_float(down<OFF>(__float_as_uint(inc.a))), move64<OFF>(inc.s, [](uint32_t x) { return down<OFF>(x); })};
+      if (lane + OFF < LANES) inc = join(inc, y, c);
+      suf_steps<2 * OFF>(inc, c);
+    }
+  }
   LDEV Pre excl_scan(Pre x, double c) const {
     Pre inc = x;
-#pragma unroll
-    for (int off = 1; off < LANES; off <<= 1) {
-      Pre y{__shfl_up(inc.a, off, LANES), __shfl_up(inc.s, off, LANES)};
-      if (lane >= off) inc = join(y, inc, c);
-    }
-    Pre ex{__shfl_up(inc.a, 1, LANES), __shfl_up(inc.s, 1, LANES)};
+    pre_steps<1>(inc, c);
+    Pre ex{__uint_as_float(up<1>(__float_as_uint(inc.a))), move64<1>(inc.s, [](uint32_t v) { return up<1>(v); })};
     if (lane == 0) ex.s = 0.0;
     return ex;
   }
   LDEV Suf excl_scan(Suf x, double c) const {
     Suf inc = x;
-#pragma unroll
-    for (int off = 1; off < LANES; off <<= 1) {
-      Suf y{__shfl_down(inc.a, off, LANES), __shfl_down(inc.s, off, LANES)};
-      if (lane + off < LANES) inc = join(inc, y, c);
-    }
-    Suf ex{__shfl_down(inc.a, 1, LANES), __shfl_down(inc.s, 1, LANES)};
+    suf_steps<1>(inc, c);
+    Suf ex{__uint_as_float(down<1>(__float_as_uint(inc.a))), move64<1>(inc.s, [](uint32_t v) { return down<1>(v); })};
     if (lane == LANES - 1) ex.s = 0.0;
     return ex;
   }
@@ -418,24 +475,23 @@ LDEV double segment_solve(const float (&s)[E], int nv, const PartInfo &part, dou
   const int owner = Mp == 0 ? 0 : (right_end ? (Mp - 1) / E : (jstar + 1) / E);
   double b = 0.0;
   if (team.lane == owner) {
-    // anchor knot x, ln of the sums below (lP) and above (lQ) relative to x
+    // Anchor knot x and the two sums around it in the form ln(A) + B/t:
+    // P-side (everything at or below x) and Q-side (everything above the
+    // interval that holds b), plus the count above and the interval ends.
     const double it = 1.0 / t;
-    double x, lP, lQ, cabove, lo = -INFINITY, hi = INFINITY;
+    double x, PA, PB = 0.0, QA, QB = 0.0, cabove, lo = -INFINITY, hi = INFINITY;
     if (Mp == 0) {
-      if (pin.s != 0.0) {
-        x = pin.a;
-        lP = log(pin.s);
-        lQ = sin.s == 0.0 ? -INFINITY : log(sin.s) + (x - (double)sin.a) * it;
-      } else {
-        x = sin.a;
-        lP = -INFINITY;
-        lQ = safe_log(sin.s);
-      }
+      // no knots in this part: the seeds alone bound b
+      const bool has_lo = pin.s != 0.0;
+      x = has_lo ? (double)pin.a : (double)sin.a;
+      PA = has_lo ? pin.s : 0.0;
+      QA = sin.s;
+      QB = has_lo ? x - (double)sin.a : 0.0;
       cabove = part.above;
     } else if (!right_end) {
       const int e1 = jstar + 1 - base;  // first knot above b, in this lane
-      double S1 = 1.0, S = 0.0;
-      float s1 = s[0];
+      double S1 = 1.0, S = 0.0, Pm = 0.0;
+      float s1 = s[0], sm = s[0];
 #pragma unroll
       for (int e = E - 1; e >= 0; --e) {
         if (e < nv) {
@@ -445,50 +501,46 @@ LDEV double segment_solve(const float (&s)[E], int nv, const PartInfo &part, dou
             s1 = s[e];
           }
         }
+        if (e == e1 - 1) {
+          Pm = P[e];
+          sm = s[e];
+        }
       }
+      const bool below_all = e1 == 0 && part.first && owner == 0;  // b below every knot
       if (e1 > 0) {
-        x = s[0];
-        double Pv = P[0];
-#pragma unroll
-        for (int e = 1; e < E; ++e)
-          if (e == e1 - 1) {
-            x = s[e];
-            Pv = P[e];
-          }
-        lo = x;
-        lP = log(Pv);
-        lQ = log(S1) + (x - (double)s1) * it;
-        cabove = part.above - (double)(jstar + 1);
-      } else if (!(part.first && owner == 0)) {
-        x = pin.a;  // previous knot: last of the previous lane or tile
-        lP = log(pin.s);
-        lo = x;
-        lQ = log(S1) + (x - (double)s1) * it;
-        cabove = part.above - (double)(jstar + 1);
+        x = sm;  // the knot just below, in this lane
+        PA = Pm;
+      } else if (!below_all) {
+        x = pin.a;  // the knot just below: last of the previous lane or tile
+        PA = pin.s;
       } else {
-        // b below every knot of the segment
         x = s1;
-        lP = pin.s == 0.0 ? -INFINITY : log(pin.s) + ((double)pin.a - x) * it;
-        lQ = log(S1);
-        cabove = part.above;
+        PA = pin.s;
+        PB = (double)pin.a - x;
       }
+      QA = S1;
+      QB = below_all ? 0.0 : x - (double)s1;
+      cabove = below_all ? part.above : part.above - (double)(jstar + 1);
+      if (!below_all) lo = x;
       hi = s1;
     } else {
       const int e0 = Mp - 1 - base;
       x = s[0];
-      double Pv = P[0];
+      PA = P[0];
 #pragma unroll
       for (int e = 1; e < E; ++e)
         if (e == e0) {
           x = s[e];
-          Pv = P[e];
+          PA = P[e];
         }
-      lP = log(Pv);
-      lQ = sin.s == 0.0 ? -INFINITY : log(sin.s) + (x - (double)sin.a) * it;
+      QA = sin.s;
+      QB = x - (double)sin.a;
       cabove = part.above - (double)Mp;
       lo = x;
       hi = (part.last || sin.s == 0.0) ? INFINITY : (double)sin.a;
     }
+    const double lP = PA > 0.0 ? log_pos(PA) + PB * it : -INFINITY;
+    const double lQ = QA > 0.0 ? log_pos(QA) + QB * it : -INFINITY;
     b = solve_root(x, lP, lQ, cabove, k, t);
     b = fmin(fmax(b, lo), hi);
   }

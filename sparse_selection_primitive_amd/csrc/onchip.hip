@@ -26,13 +26,25 @@ LDEV float laplace_cdf_at(float x, double b, double c) {
   return z2 < 0.0f ? 0.5f * __builtin_amdgcn_exp2f(z2) : 1.0f - 0.5f * __builtin_amdgcn_exp2f(-z2);
 }
 
-template <int E>
-LDEV void load_row(const float *rr, int n, int base, bool ok, bool vec, float (&v)[E]) {
+// Where lane `lane` of a team of LANES keeps its E scores of the row.  On
+// the vector path slot e = 4q + i is element q*4*LANES + 4*lane + i: each
+// 16-byte load or store instruction of the team covers 64*LANES contiguous
+// bytes.  Otherwise slot e is element lane*E + e.  (The sort does not care
+// which scores a lane starts with; the apply writes each p where its score
+// came from.)
+template <int E, int LANES>
+LDEV int slot_index(int lane, int e, bool vec) {
+  return vec ? (e >> 2) * (4 * LANES) + 4 * lane + (e & 3) : lane * E + e;
+}
+
+template <int E, int LANES>
+LDEV void load_row(const float *rr, int n, int lane, bool ok, bool vec, float (&v)[E]) {
   if (vec && (E % 4) == 0) {
 #pragma unroll
     for (int q = 0; q < E; q += 4) {
+      const int i = slot_index<E, LANES>(lane, q, true);
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok && base + q < n) x = *reinterpret_cast<const float4 *>(rr + base + q);
+      if (ok && i < n) x = *reinterpret_cast<const float4 *>(rr + i);
       v[q] = x.x;
       v[q + 1] = x.y;
       v[q + 2] = x.z;
@@ -40,39 +52,51 @@ LDEV void load_row(const float *rr, int n, int base, bool ok, bool vec, float (&
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = (ok && base + e < n) ? rr[base + e] : 0.0f;
+    for (int e = 0; e < E; ++e) {
+      const int i = slot_index<E, LANES>(lane, e, false);
+      v[e] = (ok && i < n) ? rr[i] : 0.0f;
+    }
   }
 }
 
-template <int E>
-LDEV void store_row(float *pp, int n, int base, bool ok, bool vec, const float (&v)[E]) {
+template <int E, int LANES>
+LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (&v)[E]) {
   if (!ok) return;
   if (vec && (E % 4) == 0) {
 #pragma unroll
-    for (int q = 0; q < E; q += 4)
-      if (base + q < n) *reinterpret_cast<float4 *>(pp + base + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    for (int q = 0; q < E; q += 4) {
+      const int i = slot_index<E, LANES>(lane, q, true);
+      if (i < n) *reinterpret_cast<float4 *>(pp + i) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (base + e < n) pp[base + e] = v[e];
+    for (int e = 0; e < E; ++e) {
+      const int i = slot_index<E, LANES>(lane, e, false);
+      if (i < n) pp[i] = v[e];
+    }
   }
 }
 
-// Whole forward of one row held by a team.
-template <int E, class Team>
-LDEV void onchip_row_forward(const Team &team, const float *rr, int n, bool ok, double k, double t, float *pp,
+// Whole forward of one row held by a team.  FULL: n == E * lanes, so every
+// lane holds E valid scores and no validity test is needed.
+template <int E, bool FULL, class Team>
+LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool ok, double k, double t, float *pp,
                              double *bout, lapsum_row_stats *stats) {
+  const int n = FULL ? E * Team::kLanes : n_arg;
+  constexpr int LANES = Team::kLanes;
   const bool vec = (n & 3) == 0 && aligned16(rr) && aligned16(pp);
-  const int base = team.lane * E;
+  const int base = team.lane * E;  // first sorted position held by this lane
   float v[E];
-  load_row<E>(rr, n, base, ok, vec, v);
+  load_row<E, LANES>(rr, n, team.lane, ok, vec, v);
   uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (ok && base + e < n) ? key_of(v[e]) : 0xFFFFFFFFu;
+  for (int e = 0; e < E; ++e)
+    key[e] = (FULL || (ok && slot_index<E, LANES>(team.lane, e, vec) < n)) ? key_of(v[e]) : 0xFFFFFFFFu;
 
   bitonic_sort<E>(key, team);
 
-  const int nv = ok ? min(max(n - base, 0), E) : 0;
+  // rows past the end (ok false) compute on zeros and store nothing
+  const int nv = FULL ? E : (ok ? min(max(n - base, 0), E) : 0);
   float s[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
@@ -91,7 +115,7 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n, bool ok, 
   float out[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = laplace_cdf_at(v[e], b, c);
-  store_row<E>(pp, n, base, ok, vec, out);
+  store_row<E, LANES>(pp, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
     *bout = b;
     if (stats) {
@@ -109,7 +133,7 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n, bool ok, 
 }
 
 // Teams inside one wave: NP = LANES * E <= 1024, 256 threads = 256/LANES rows.
-template <int NP, int LANES>
+template <int NP, int LANES, bool FULL>
 __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restrict__ r, int64_t rows, int n,
                                                            double k, double t, float *__restrict__ p,
                                                            double *__restrict__ b, lapsum_row_stats *stats) {
@@ -118,7 +142,7 @@ __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restri
   const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
   const bool ok = row < rows;
   const int64_t rr = ok ? row : 0;
-  onchip_row_forward<E>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr);
+  onchip_row_forward<E, FULL>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr);
 }
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
@@ -130,7 +154,7 @@ __global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__r
   __shared__ BlockTeamLds<LANES, E> lds;
   BlockTeam<LANES, E> team(&lds);
   const int64_t row = blockIdx.x;
-  onchip_row_forward<E>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr);
+  onchip_row_forward<E, false>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr);
 }
 
 template <int NP, int LANES>
@@ -138,8 +162,12 @@ static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k,
                                   lapsum_row_stats *stats, hipStream_t s) {
   constexpr int RPB = 256 / LANES;
   const int64_t grid = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((onchip_forward_wave<NP, LANES>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n, k, t, p,
-                     b, stats);
+  if (n == NP)
+    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, true>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n, k,
+                       t, p, b, stats);
+  else
+    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, false>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n,
+                       k, t, p, b, stats);
   return hipGetLastError();
 }
 
@@ -174,16 +202,15 @@ __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restr
   const bool ok = row < rows;
   const int64_t rr = ok ? row : 0;
   const bool vec = (n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr);
-  const int base = team.lane * E;
   float gv[E], pv[E];
-  load_row<E>(g + rr * n, n, base, ok, vec, gv);
-  load_row<E>(p + rr * n, n, base, ok, vec, pv);
+  load_row<E, LANES>(g + rr * n, n, team.lane, ok, vec, gv);
+  load_row<E, LANES>(p + rr * n, n, team.lane, ok, vec, pv);
   double D = 0.0, G = 0.0;
   float q[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     // min(p, 1 - p) is the Laplace density at the score (times t)
-    q[e] = (ok && base + e < n) ? fminf(pv[e], 1.0f - pv[e]) : 0.0f;
+    q[e] = (ok && slot_index<E, LANES>(team.lane, e, vec) < n) ? fminf(pv[e], 1.0f - pv[e]) : 0.0f;
     D += (double)q[e];
     G += (double)gv[e] * (double)q[e];
   }
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restr
   float out[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (float)((double)gv[e] - dkd) : 0.0f;
-  store_row<E>(dr + rr * n, n, base, ok, vec, out);
+  store_row<E, LANES>(dr + rr * n, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
     dk[rr] = dkf;
     if (stats && !(D > 0.0)) atomicOr(&stats[rr].flags, LAPSUM_FLAG_DEGENERATE);
