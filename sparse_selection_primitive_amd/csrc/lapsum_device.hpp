@@ -45,6 +45,13 @@ LDEV float value_of(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
 }
+LDEV uint32_t to_bits(uint32_t v) { return v; }
+LDEV uint32_t to_bits(float v) { return __float_as_uint(v); }
+template <class T>
+LDEV T from_bits(uint32_t v) {
+  if constexpr (sizeof(T) == 4 && T(0.5) != T(0)) return __uint_as_float(v);
+  else return v;
+}
 
 // exp(d/t) for d <= 0, with c = log2(e)/t: the product in fp64, the power of
 // two by the hardware exp2 in fp32 (results below 2^-126 flush toward 0,
@@ -147,10 +154,10 @@ struct WaveTeam {
   LDEV WaveTeam() : lane(lane_id() & (LANES - 1)) {}
 
   // dst[e] = partner's src[REV ? E-1-e : e], partner = lane ^ MASK
-  template <int MASK, bool REV, int E>
-  LDEV void exchange(const uint32_t (&src)[E], uint32_t (&dst)[E]) const {
+  template <int MASK, bool REV, int E, class T>
+  LDEV void exchange(const T (&src)[E], T (&dst)[E]) const {
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = xor_lanes<MASK>(src[REV ? E - 1 - e : e]);
+    for (int e = 0; e < E; ++e) dst[e] = from_bits<T>(xor_lanes<MASK>(to_bits(src[REV ? E - 1 - e : e])));
   }
   // Team-local lane moves.  Teams inside one DPP row (LANES <= 16) use DPP:
   // row_shr / row_shl for shifts, quad_perm and mirrors for the butterfly
@@ -254,18 +261,18 @@ struct BlockTeam {
   BlockTeamLds<LANES, E> *lds;
   LDEV explicit BlockTeam(BlockTeamLds<LANES, E> *l) : lane((int)threadIdx.x), lds(l) {}
 
-  template <int MASK, bool REV>
-  LDEV void exchange(const uint32_t (&src)[E], uint32_t (&dst)[E]) const {
+  template <int MASK, bool REV, class T>
+  LDEV void exchange(const T (&src)[E], T (&dst)[E]) const {
     if constexpr (MASK < kWave) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) dst[e] = xor_lanes<MASK>(src[REV ? E - 1 - e : e]);
+      for (int e = 0; e < E; ++e) dst[e] = from_bits<T>(xor_lanes<MASK>(to_bits(src[REV ? E - 1 - e : e])));
     } else {
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < E; ++e) lds->xchg[e * LANES + lane] = src[e];
+      for (int e = 0; e < E; ++e) lds->xchg[e * LANES + lane] = to_bits(src[e]);
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < E; ++e) dst[e] = lds->xchg[(REV ? E - 1 - e : e) * LANES + (lane ^ MASK)];
+      for (int e = 0; e < E; ++e) dst[e] = from_bits<T>(lds->xchg[(REV ? E - 1 - e : e) * LANES + (lane ^ MASK)]);
     }
   }
   LDEV int sum(int v) const {
@@ -351,15 +358,18 @@ struct BlockTeam {
 // each merge size 2^s, one stage pairing i with i ^ (2^s - 1) (the mirror
 // of its block), then stages pairing i with i ^ d for d = 2^(s-2) .. 1; the
 // lower index keeps the minimum.  Stages with d < E stay in registers;
-// larger ones exchange with lane (lane ^ mask) of the team.
-template <int D, bool MIRROR, int E, class Team>
-LDEV void bitonic_stage(uint32_t (&key)[E], const Team &team) {
+// larger ones exchange with lane (lane ^ mask) of the team.  Keys are either
+// order-preserving uint32 keys or finite fp32 values (padding +inf); for
+// fp32 a cross-lane step is one median: med3(own, partner, -inf) is the
+// minimum, med3(own, partner, +inf) the maximum.
+template <int D, bool MIRROR, int E, class T, class Team>
+LDEV void bitonic_stage(T (&key)[E], const Team &team) {
   if constexpr (D < E) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       if ((i & D) == 0) {
         const int j = MIRROR ? (i ^ (2 * D - 1)) : (i ^ D);
-        const uint32_t x = key[i], y = key[j];
+        const T x = key[i], y = key[j];
         key[i] = min(x, y);
         key[j] = max(x, y);
       }
@@ -367,24 +377,30 @@ LDEV void bitonic_stage(uint32_t (&key)[E], const Team &team) {
   } else {
     constexpr int LM = D / E;
     constexpr int MASK = MIRROR ? (2 * LM - 1) : LM;
-    uint32_t recv[E];
+    T recv[E];
     team.template exchange<MASK, MIRROR>(key, recv);
     const bool lower = (team.lane & LM) == 0;
+    if constexpr (sizeof(T) == 4 && T(0.5) != T(0)) {
+      const float bound = lower ? -INFINITY : INFINITY;
 #pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = lower ? min(key[e], recv[e]) : max(key[e], recv[e]);
+      for (int e = 0; e < E; ++e) key[e] = __builtin_amdgcn_fmed3f(key[e], recv[e], bound);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) key[e] = lower ? min(key[e], recv[e]) : max(key[e], recv[e]);
+    }
   }
 }
 
-template <int D, int E, class Team>
-LDEV void bitonic_cleaners(uint32_t (&key)[E], const Team &team) {
+template <int D, int E, class T, class Team>
+LDEV void bitonic_cleaners(T (&key)[E], const Team &team) {
   if constexpr (D >= 1) {
     bitonic_stage<D, false>(key, team);
     bitonic_cleaners<D / 2>(key, team);
   }
 }
 
-template <int S, int LOGN, int E, class Team>
-LDEV void bitonic_merges(uint32_t (&key)[E], const Team &team) {
+template <int S, int LOGN, int E, class T, class Team>
+LDEV void bitonic_merges(T (&key)[E], const Team &team) {
   if constexpr (S <= LOGN) {
     constexpr int HALF = 1 << (S - 1);
     bitonic_stage<HALF, true>(key, team);
@@ -395,8 +411,8 @@ LDEV void bitonic_merges(uint32_t (&key)[E], const Team &team) {
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
-template <int E, class Team>
-LDEV void bitonic_sort(uint32_t (&key)[E], const Team &team) {
+template <int E, class T, class Team>
+LDEV void bitonic_sort(T (&key)[E], const Team &team) {
   constexpr int NP = E * Team::kLanes;
   bitonic_merges<1, ilog2(NP)>(key, team);
 }

@@ -88,18 +88,19 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
   const int base = team.lane * E;  // first sorted position held by this lane
   float v[E];
   load_row<E, LANES>(rr, n, team.lane, ok, vec, v);
-  uint32_t key[E];
+  // the scores themselves are sorted (finite, so fp32 order is numeric
+  // order; equal values, -0 and +0 included, need no order among them)
+  float s[E];
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    key[e] = (FULL || (ok && slot_index<E, LANES>(team.lane, e, vec) < n)) ? key_of(v[e]) : 0xFFFFFFFFu;
+    s[e] = (FULL || (ok && slot_index<E, LANES>(team.lane, e, vec) < n)) ? v[e] : INFINITY;
 
-  bitonic_sort<E>(key, team);
+  bitonic_sort<E>(s, team);
 
   // rows past the end (ok false) compute on zeros and store nothing
   const int nv = FULL ? E : (ok ? min(max(n - base, 0), E) : 0);
-  float s[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? s[e] : 0.0f;
 
   const double c = kLog2e / t;
   const float cf = (float)c;
