@@ -184,6 +184,31 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
     hip.destroy([e for pair in dom_events for e in pair])
     dom_avg = sum(dom_ms) / len(dom_ms)
 
+    # the same steps replayed from HIP graphs (one captured forward+backward
+    # per buffer set): the launch cost of each kernel leaves the step
+    graphs = []
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        for i in range(nsets):
+            r, g, p, b, dr, dk = sets[i]
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                cs = cap.cuda_stream
+                op.forward(r, p, b, stream=cs)
+                op.backward(g, p, b, dr, dk, stream=cs)
+            graphs.append(gr)
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    for i in range(max(warmup, nsets)):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    wall_graph = time.perf_counter() - t2
+    del graphs
+
     # forward-only timing (same rotation)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -195,6 +220,7 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
 
     ms_step = 1e3 * wall / steps
     ms_fwd = 1e3 * wall_fwd / steps
+    ms_graph = 1e3 * wall_graph / steps
     step_bytes = (spec["fwd_b"] + spec["bwd_b"]) * elems
     dom_bytes = STAGE_BYTES[dominant] * elems
     out = {
@@ -205,6 +231,9 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
         "ms_per_step": ms_step, "ms_fwd": ms_fwd,
         "hbm_fraction_step": step_bytes / (ms_step * 1e-3) / HBM_PEAK,
         "hbm_fraction_fwd": spec["fwd_b"] * elems / (ms_fwd * 1e-3) / HBM_PEAK,
+        "ms_per_step_graph": ms_graph,
+        "fwd_bwd_elements_per_s_graph": elems / (ms_graph * 1e-3),
+        "hbm_fraction_step_graph": step_bytes / (ms_graph * 1e-3) / HBM_PEAK,
         "bytes_per_element_fwd_bwd": spec["fwd_b"] + spec["bwd_b"],
         "buffer_sets": nsets,
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
@@ -296,7 +325,8 @@ def main():
         if name == "extreme":
             extreme_w = w
         print(f"# {name}: {res['fwd_bwd_elements_per_s']:.3e} el/s fwd+bwd, {res['ms_per_step']:.4f} ms/step, "
-              f"{100 * res['hbm_fraction_step']:.1f}% HBM, dominant {res['dominant']['stage']} "
+              f"{100 * res['hbm_fraction_step']:.1f}% HBM (graph replay {res['ms_per_step_graph']:.4f} ms, "
+              f"{100 * res['hbm_fraction_step_graph']:.1f}%), dominant {res['dominant']['stage']} "
               f"{res['dominant']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.calib_copy:

@@ -308,15 +308,19 @@ class Operator:
         self.opt.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
         return self._opt_ref
 
-    def forward(self, r, p, b, stage_events=None):
+    def forward(self, r, p, b, stage_events=None, stream=None):
+        """stream: a raw hipStream_t (int) overriding the prepared one, e.g.
+        the capturing stream inside ``torch.cuda.graph``."""
         rc = self.lib.lapsum_forward(r.data_ptr(), self.rows, self.n, self.k, self.t, p.data_ptr(), b.data_ptr(),
-                                     self.wptr, self.wlen, self._opt_with_events(stage_events), self.stream)
+                                     self.wptr, self.wlen, self._opt_with_events(stage_events),
+                                     self.stream if stream is None else stream)
         if rc:
             _check(rc, "lapsum_forward")
 
-    def backward(self, g, p, b, dr, dk, stage_events=None):
+    def backward(self, g, p, b, dr, dk, stage_events=None, stream=None):
         rc = self.lib.lapsum_backward(g.data_ptr(), p.data_ptr(), b.data_ptr(), self.rows, self.n, self.t,
                                       dr.data_ptr(), dk.data_ptr(), self.wptr, self.wlen,
-                                      self._opt_with_events(stage_events), self.stream)
+                                      self._opt_with_events(stage_events),
+                                      self.stream if stream is None else stream)
         if rc:
             _check(rc, "lapsum_backward")
