@@ -193,19 +193,14 @@ hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, 
 }
 
 // ------------------------------------------------------------ backward
+// One team per row, 256/LANES rows per workgroup and step; each workgroup
+// strides over the row groups and loads the next group's g and p before it
+// reduces and writes the current one, so reads and writes overlap.
 template <int NP, int LANES>
-__global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restrict__ g, const float *__restrict__ p,
-                                                            int64_t rows, int n, double t, float *__restrict__ dr,
-                                                            float *__restrict__ dk, lapsum_row_stats *stats) {
+LDEV void bwd_row(const WaveTeam<LANES> &team, const float (&gv)[NP / LANES], const float (&pv)[NP / LANES],
+                  int64_t row, bool ok, int n, bool vec, float inv_t, float *__restrict__ dr, float *__restrict__ dk,
+                  lapsum_row_stats *stats) {
   constexpr int E = NP / LANES;
-  WaveTeam<LANES> team;
-  const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
-  const bool ok = row < rows;
-  const int64_t rr = ok ? row : 0;
-  const bool vec = (n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr);
-  float gv[E], pv[E];
-  load_row<E, LANES>(g + rr * n, n, team.lane, ok, vec, gv);
-  load_row<E, LANES>(p + rr * n, n, team.lane, ok, vec, pv);
   double D = 0.0, G = 0.0;
   float q[E];
 #pragma unroll
@@ -218,25 +213,63 @@ __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restr
   D = team.sum(D);
   G = team.sum(G);
   const double dkd = D > 0.0 ? G / D : 0.0;
-  const float dkf = (float)dkd;
-  const float inv_t = (float)(1.0 / t);
   float out[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (float)((double)gv[e] - dkd) : 0.0f;
-  store_row<E, LANES>(dr + rr * n, n, team.lane, ok, vec, out);
+  store_row<E, LANES>(dr + row * n, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
-    dk[rr] = dkf;
-    if (stats && !(D > 0.0)) atomicOr(&stats[rr].flags, LAPSUM_FLAG_DEGENERATE);
+    dk[row] = (float)dkd;
+    if (stats && !(D > 0.0)) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
+  }
+}
+
+template <int NP, int LANES>
+__global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restrict__ g, const float *__restrict__ p,
+                                                            int64_t rows, int n, double t, float *__restrict__ dr,
+                                                            float *__restrict__ dk, lapsum_row_stats *stats) {
+  constexpr int E = NP / LANES, RPW = 256 / LANES;
+  WaveTeam<LANES> team;
+  const bool vec = (n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr);
+  const float inv_t = (float)(1.0 / t);
+  const int64_t groups = (rows + RPW - 1) / RPW;
+  const int sub = threadIdx.x / LANES;
+  int64_t grp = blockIdx.x;
+  float gv[E], pv[E];
+  {
+    const int64_t row = grp * RPW + sub;
+    const bool ok = grp < groups && row < rows;
+    const int64_t rr = ok ? row : 0;
+    load_row<E, LANES>(g + rr * n, n, team.lane, ok, vec, gv);
+    load_row<E, LANES>(p + rr * n, n, team.lane, ok, vec, pv);
+  }
+  for (; grp < groups; grp += gridDim.x) {
+    const int64_t nrow = (grp + gridDim.x) * RPW + sub;
+    const bool nok = grp + gridDim.x < groups && nrow < rows;
+    const int64_t nr = nok ? nrow : 0;
+    float gn[E], pn[E];
+    load_row<E, LANES>(g + nr * n, n, team.lane, nok, vec, gn);
+    load_row<E, LANES>(p + nr * n, n, team.lane, nok, vec, pn);
+    const int64_t row = grp * RPW + sub;
+    const bool ok = row < rows;
+    bwd_row<NP, LANES>(team, gv, pv, ok ? row : 0, ok, n, vec, inv_t, dr, dk, stats);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gv[e] = gn[e];
+      pv[e] = pn[e];
+    }
   }
 }
 
 bool onchip_backward_supported(int64_t n) { return n >= 1 && n <= 1024; }
 
+constexpr int64_t kBwdMaxGroups = 4096;  // workgroups of the on-chip backward, at most
+
 template <int NP, int LANES>
 static hipError_t launch_bwd_wave(const float *g, const float *p, int64_t rows, int n, double t, float *dr, float *dk,
                                   lapsum_row_stats *stats, hipStream_t s) {
   constexpr int RPB = 256 / LANES;
-  const int64_t grid = (rows + RPB - 1) / RPB;
+  const int64_t groups = (rows + RPB - 1) / RPB;
+  const int64_t grid = groups < kBwdMaxGroups ? groups : kBwdMaxGroups;
   hipLaunchKernelGGL((onchip_backward_wave<NP, LANES>), dim3((unsigned)grid), dim3(256), 0, s, g, p, rows, n, t, dr,
                      dk, stats);
   return hipGetLastError();
