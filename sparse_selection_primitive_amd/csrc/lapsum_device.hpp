@@ -210,6 +210,22 @@ struct WaveTeam {
   LDEV void sync() const {}
 
   template <int OFF>
+  LDEV void int_steps(int &inc) const {
+    if constexpr (OFF < LANES) {
+      const int y = (int)up<OFF>((uint32_t)inc);
+      if (lane >= OFF) inc += y;
+      int_steps<2 * OFF>(inc);
+    }
+  }
+  // exclusive prefix sum over the team; *total gets the team's sum
+  LDEV int excl_scan(int v, int *total) const {
+    int inc = v;
+    int_steps<1>(inc);
+    *total = __shfl(inc, LANES - 1, LANES);
+    return inc - v;
+  }
+
+  template <int OFF>
   LDEV void pre_steps(Pre &inc, double c) const {
     if constexpr (OFF < LANES) {
       const Pre y{__uint_as_float(up<OFF>(__float_as_uint(inc.a))), move64<OFF>(inc.s, [](uint32_t x) { return up<OFF>(x); })};

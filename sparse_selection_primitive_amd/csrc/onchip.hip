@@ -77,45 +77,127 @@ LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (
   }
 }
 
+// Certified window for a small budget: with the K-th largest (K = ceil(k))
+// of the lanes' second-largest scores as a, at least 2K >= 2k scores are
+// >= a, each with p >= 1/2 at b = a, so f(a) >= k and b >= a.  Only the
+// scores >= a (the candidates, typically a few times k) are sorted and
+// scanned; everything below a enters as one exact tail sum anchored at a,
+// exactly as the bracketing band solve seeds its scan.  A budget near n uses
+// the complement: b(-r, n - k) = -b(r, k).  Returns false (and the caller
+// sorts the whole row) when k and n - k both exceed the lane count or the
+// candidates overflow the 4*LANES buffer.  buf: this team's 4*LANES floats
+// of LDS.
+template <int E, int LANES>
+LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const bool (&valid)[E], int n, double k,
+                       double t, double c, float cf, float *buf, double &b_out) {
+  constexpr int CAP = 4 * LANES;
+  const bool mirror = k > (double)LANES;
+  const double kk = mirror ? (double)n - k : k;
+  if (kk > (double)LANES) return false;
+  const float sg = mirror ? -1.0f : 1.0f;
+  float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float w = valid[e] ? sg * v[e] : -INFINITY;
+    m2 = fmaxf(m2, fminf(m1, w));
+    m1 = fmaxf(m1, w);
+  }
+  float x[1] = {m2};
+  bitonic_sort<1>(x, team);
+  const int K = (int)ceil(kk);
+  const float a = team.bcast(x[0], LANES - K);
+  if (!(a > -INFINITY)) return false;
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += (valid[e] && sg * v[e] >= a) ? 1 : 0;
+  int C;
+  int o = team.excl_scan(mine, &C);
+  if (C > CAP) return false;
+  double S = 0.0;  // tail below a, anchored at a
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float w = sg * v[e];
+    if (valid[e] && w >= a) buf[o++] = w;
+    if (valid[e] && w < a) S += (double)__builtin_amdgcn_exp2f((w - a) * cf);
+  }
+  S = team.sum(S);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float s4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s4[q] = 4 * team.lane + q < C ? buf[4 * team.lane + q] : INFINITY;
+  bitonic_sort<4>(s4, team);
+  const int nv = min(max(C - 4 * team.lane, 0), 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s4[q] = q < nv ? s4[q] : 0.0f;
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)C;
+  part.seed_lo = Pre{a, S};
+  part.seed_hi = Suf{0.0f, 0.0};
+  part.first = true;
+  part.last = true;
+  const double bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
+  b_out = mirror ? -bw : bw;
+  return true;
+}
+
 // Whole forward of one row held by a team.  FULL: n == E * lanes, so every
 // lane holds E valid scores and no validity test is needed.
 template <int E, bool FULL, class Team>
 LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool ok, double k, double t, float *pp,
-                             double *bout, lapsum_row_stats *stats) {
+                             double *bout, lapsum_row_stats *stats, float *wbuf = nullptr) {
   const int n = FULL ? E * Team::kLanes : n_arg;
   constexpr int LANES = Team::kLanes;
   const bool vec = (n & 3) == 0 && aligned16(rr) && aligned16(pp);
   const int base = team.lane * E;  // first sorted position held by this lane
   float v[E];
   load_row<E, LANES>(rr, n, team.lane, ok, vec, v);
-  // the scores themselves are sorted (finite, so fp32 order is numeric
-  // order; equal values, -0 and +0 included, need no order among them)
-  float s[E];
+  bool valid[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    s[e] = (FULL || (ok && slot_index<E, LANES>(team.lane, e, vec) < n)) ? v[e] : INFINITY;
-
-  bitonic_sort<E>(s, team);
-
-  // rows past the end (ok false) compute on zeros and store nothing
-  const int nv = FULL ? E : (ok ? min(max(n - base, 0), E) : 0);
-#pragma unroll
-  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? s[e] : 0.0f;
-
+  for (int e = 0; e < E; ++e) valid[e] = FULL || (ok && slot_index<E, LANES>(team.lane, e, vec) < n);
   const double c = kLog2e / t;
   const float cf = (float)c;
-  PartInfo part;
-  part.nvalid = nv;
-  part.above = (double)n;
-  part.seed_lo = Pre{0.0f, 0.0};
-  part.seed_hi = Suf{0.0f, 0.0};
-  part.first = true;
-  part.last = true;
-  const double b = segment_solve<E>(s, nv, part, k, t, c, cf, team);
 
+  double b = 0.0;
+  bool done = !ok;  // rows past the end compute nothing and store nothing
+  if constexpr (Team::kLanes <= kWave) {
+    if (wbuf != nullptr && !done) done = window_solve<E>(team, v, valid, n, k, t, c, cf, wbuf, b);
+  }
+  if (!done) {
+    // the scores themselves are sorted (finite, so fp32 order is numeric
+    // order; equal values, -0 and +0 included, need no order among them)
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = valid[e] ? v[e] : INFINITY;
+
+    bitonic_sort<E>(s, team);
+
+    const int nv = FULL ? E : (ok ? min(max(n - base, 0), E) : 0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = (e < nv) ? s[e] : 0.0f;
+
+    PartInfo part;
+    part.nvalid = nv;
+    part.above = (double)n;
+    part.seed_lo = Pre{0.0f, 0.0};
+    part.seed_hi = Suf{0.0f, 0.0};
+    part.first = true;
+    part.last = true;
+    b = segment_solve<E>(s, nv, part, k, t, c, cf, team);
+  }
+
+  // p = F((x - b)/t) in fp32 with b split into bh + bl: x - bh is exact or
+  // rounds relative to itself, so p carries a few 1e-8 absolute error at most
+  const float bh = (float)b, bl = (float)(b - (double)bh);
   float out[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = laplace_cdf_at(v[e], b, c);
+  for (int e = 0; e < E; ++e) {
+    const float z2 = ((v[e] - bh) - bl) * cf;
+    const float h = 0.5f * __builtin_amdgcn_exp2f(-fabsf(z2));
+    out[e] = z2 < 0.0f ? h : 1.0f - h;
+  }
   store_row<E, LANES>(pp, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
     *bout = b;
@@ -139,11 +221,13 @@ __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restri
                                                            double k, double t, float *__restrict__ p,
                                                            double *__restrict__ b, lapsum_row_stats *stats) {
   constexpr int E = NP / LANES;
+  __shared__ float wbuf[4 * 256];  // candidate buffers of the certified window, 4*LANES per team
   WaveTeam<LANES> team;
   const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
   const bool ok = row < rows;
   const int64_t rr = ok ? row : 0;
-  onchip_row_forward<E, FULL>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr);
+  onchip_row_forward<E, FULL>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr,
+                              wbuf + (threadIdx.x / LANES) * (4 * LANES));
 }
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
