@@ -107,11 +107,10 @@ def source_sha(files=None) -> str:
 def stages_of(L, plan, n):
     """Stage ids a call with this plan records (forward, then backward)."""
     path = plan["path"]
-    fallback = [] if plan.get("band_onchip") else [L.STAGE_FULLSORT]  # fused into the band kernel
     fwd = {L.PATH_ONCHIP: [L.STAGE_ONCHIP_FWD],
            L.PATH_FULLSORT: [L.STAGE_INIT, L.STAGE_FULLSORT, L.STAGE_APPLY],
-           L.PATH_BRACKET: [L.STAGE_SAMPLE, L.STAGE_SELECT, L.STAGE_FILTER, L.STAGE_BAND]
-           + fallback + [L.STAGE_APPLY]}[path]
+           L.PATH_BRACKET: [L.STAGE_SAMPLE, L.STAGE_SELECT, L.STAGE_FILTER, L.STAGE_BAND,
+                            L.STAGE_APPLY]}[path]  # the fallback runs inside the band stage
     bwd = [L.STAGE_ONCHIP_BWD] if n <= 1024 else [L.STAGE_BWD_REDUCE, L.STAGE_BWD_APPLY]
     return fwd + bwd
 

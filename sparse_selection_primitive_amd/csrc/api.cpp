@@ -426,17 +426,12 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
     const SegArgs fb = seg_args(P.full_seg, ws, kSegFallback, rows, n, r, rs, k, t);
-    if (P.band_onchip) {
-      // the band kernel also runs the fallback for rows whose bracket missed
+    // the band kernels also run the fallback for rows whose bracket missed
+    if (P.band_onchip)
       LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, fb, s));
-      tm.mark(LAPSUM_STAGE_BAND, 1);
-    } else {
-      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t), s));
-      tm.mark(LAPSUM_STAGE_BAND, 1);
-      tm.mark(LAPSUM_STAGE_FULLSORT, 0);
-      LAPSUM_TRY(launch_fallback(fb, s));
-      tm.mark(LAPSUM_STAGE_FULLSORT, 1);
-    }
+    else
+      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t), fb, s));
+    tm.mark(LAPSUM_STAGE_BAND, 1);
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);
   LAPSUM_TRY(launch_apply(r, rows, n, rs, t, p, b, s));

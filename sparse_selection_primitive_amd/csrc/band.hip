@@ -17,7 +17,9 @@
 //                        workgroup; anchored aggregates of every bucket
 //   band_locate_kernel   scan of the bucket aggregates between the tail
 //                        seeds, threshold curve at the bucket ends, the
-//                        balancing bucket, the root inside it, certification
+//                        balancing bucket, the root inside it,
+//                        certification, and the full-sort fallback of a row
+//                        whose bracket missed
 //
 // Every count is an integer and every floating-point sum runs over sorted
 // keys in a fixed order, so the result does not depend on the order in which
@@ -281,141 +283,148 @@ __global__ __launch_bounds__(kBT) void band_sort_kernel(BandArgs a) {
 }
 
 // ---------------------------------------------------------------- locate
-__global__ __launch_bounds__(kBT) void band_locate_kernel(BandArgs a) {
-  __shared__ BlockTeamLds<kBT, 1> lds;
-  __shared__ int red[3][kBT / kWave];
+// One workgroup of kLocT threads per row, two buckets per thread: a
+// workgroup scan of the bucket aggregates between the tail seeds, the
+// threshold curve at the bucket ends, the balancing bucket, and the root
+// inside it (by one wave when the bucket fits its registers, else by the
+// whole workgroup).  A row whose root falls outside its bracket is then
+// sorted and solved in full by the same workgroup (the deterministic
+// fallback), so no separate launch is needed.
+constexpr int kLocT = 1024;
+constexpr int kLocPer = kBandBuckets / kLocT;
+static_assert(kLocPer == 2, "two buckets per locate thread");
+
+union BandLocLds {
+  BlockTeamLds<kLocT, 1> team;
+  SegLds<kLocT> fb;
+};
+
+__global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs fb) {
+  __shared__ BandLocLds L;
+  __shared__ int red[3][kLocT / kWave];
   __shared__ float sel_pa, sel_sa;
-  __shared__ double sel_ps, sel_ss;
-  BlockTeam<kBT, 1> team(&lds);
+  __shared__ double sel_ps, sel_ss, sel_b;
   const int64_t row = blockIdx.x;
   RowState &S = a.st[row];
-  if (!band_active(S)) return;  // the fallback solves this row
-  const double c = a.c;
-  const int64_t M = (int64_t)S.band;
-  const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
-  const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
-  const double cR = (double)S.count_hi;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
-  const int j0 = threadIdx.x * kBPT;
-
-  TileAgg g[kBPT];
-  uint32_t cnt[kBPT], st0[kBPT];
+  const int j0 = threadIdx.x * kLocPer;
+  // this thread's bucket records (issued before the row state is examined)
+  TileAgg g[kLocPer];
+  uint32_t cnt[kLocPer], st0[kLocPer];
 #pragma unroll
-  for (int u = 0; u < kBPT; ++u) {
+  for (int u = 0; u < kLocPer; ++u) {
     g[u] = a.bagg[o + j0 + u];
     cnt[u] = a.btot[o + j0 + u];
     st0[u] = a.bstart[o + j0 + u];
   }
-  // everything before this thread's buckets, everything after them
-  Pre tp{0.0f, 0.0};
-  Suf ts{0.0f, 0.0};
+  if (band_active(S)) {
+    BlockTeam<kLocT, 1> team(&L.team);
+    const double c = a.c;
+    const int64_t M = (int64_t)S.band;
+    const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
+    const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
+    const double cR = (double)S.count_hi;
+    const Pre p0{g[0].aP, g[0].sP}, p1{g[1].aP, g[1].sP};
+    const Suf q0{g[0].aS, g[0].sS}, q1{g[1].aS, g[1].sS};
+    const Pre ex_p = join(seed_lo, team.excl_scan(join(p0, p1, c), c), c);
+    const Suf ex_s = join(team.excl_scan(join(q0, q1, c), c), seed_hi, c);
+    const Pre before[kLocPer] = {ex_p, join(ex_p, p0, c)};
+    const Suf after[kLocPer] = {join(q1, ex_s, c), ex_s};
+    // threshold curve at the last knot of every non-empty bucket
+    int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
 #pragma unroll
-  for (int u = 0; u < kBPT; ++u) tp = join(tp, Pre{g[u].aP, g[u].sP}, c);
-#pragma unroll
-  for (int u = kBPT - 1; u >= 0; --u) ts = join(Suf{g[u].aS, g[u].sS}, ts, c);
-  const Pre ex_p = join(seed_lo, team.excl_scan(tp, c), c);
-  const Suf ex_s = join(team.excl_scan(ts, c), seed_hi, c);
-  Pre before[kBPT];
-  Suf after[kBPT];
-  {
-    Pre run = ex_p;
-#pragma unroll
-    for (int u = 0; u < kBPT; ++u) {
-      before[u] = run;
-      run = join(run, Pre{g[u].aP, g[u].sP}, c);
-    }
-    Suf runs = ex_s;
-#pragma unroll
-    for (int u = kBPT - 1; u >= 0; --u) {
-      after[u] = runs;
-      runs = join(Suf{g[u].aS, g[u].sS}, runs, c);
-    }
-  }
-  // threshold curve at the last knot of every non-empty bucket
-  int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
-#pragma unroll
-  for (int u = 0; u < kBPT; ++u) {
-    if (cnt[u] > 0u) {
-      const int j = j0 + u;
-      const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
-      const Suf sa = after[u];
-      const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
-      const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
-      const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
-      if (gv < a.k) first_lt = min(first_lt, j);
-      first_ne = min(first_ne, j);
-      last_ne = max(last_ne, j);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    first_lt = min(first_lt, __shfl_xor(first_lt, m, kWave));
-    first_ne = min(first_ne, __shfl_xor(first_ne, m, kWave));
-    last_ne = max(last_ne, __shfl_xor(last_ne, m, kWave));
-  }
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    red[0][w] = first_lt;
-    red[1][w] = first_ne;
-    red[2][w] = last_ne;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kBT / kWave; ++i) {
-    first_lt = min(first_lt, red[0][i]);
-    first_ne = min(first_ne, red[1][i]);
-    last_ne = max(last_ne, red[2][i]);
-  }
-  // the balancing bucket: the first whose last knot has g < k, else the last
-  const int J = first_lt != INT_MAX ? first_lt : last_ne;  // -1: empty band
-  if (J >= 0 && (int)threadIdx.x == J / kBPT) {
-#pragma unroll
-    for (int u = 0; u < kBPT; ++u)
-      if (u == J % kBPT) {
-        sel_pa = before[u].a;
-        sel_ps = before[u].s;
-        sel_sa = after[u].a;
-        sel_ss = after[u].s;
+    for (int u = 0; u < kLocPer; ++u) {
+      if (cnt[u] > 0u) {
+        const int j = j0 + u;
+        const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
+        const Suf sa = after[u];
+        const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
+        const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
+        const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
+        if (gv < a.k) first_lt = min(first_lt, j);
+        first_ne = min(first_ne, j);
+        last_ne = max(last_ne, j);
       }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      first_lt = min(first_lt, __shfl_xor(first_lt, m, kWave));
+      first_ne = min(first_ne, __shfl_xor(first_ne, m, kWave));
+      last_ne = max(last_ne, __shfl_xor(last_ne, m, kWave));
+    }
+    if (lane == 0) {
+      red[0][w] = first_lt;
+      red[1][w] = first_ne;
+      red[2][w] = last_ne;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kLocT / kWave; ++i) {
+      first_lt = min(first_lt, red[0][i]);
+      first_ne = min(first_ne, red[1][i]);
+      last_ne = max(last_ne, red[2][i]);
+    }
+    // the balancing bucket: the first whose last knot has g < k, else the last
+    const int J = first_lt != INT_MAX ? first_lt : last_ne;  // -1: empty band
+    if (J >= 0 && (int)threadIdx.x == J / kLocPer) {
+      const int u = J % kLocPer;
+      sel_pa = u == 0 ? before[0].a : before[1].a;
+      sel_ps = u == 0 ? before[0].s : before[1].s;
+      sel_sa = u == 0 ? after[0].a : after[1].a;
+      sel_ss = u == 0 ? after[0].s : after[1].s;
+    }
+    __syncthreads();
+    const int64_t cJ = J >= 0 ? (int64_t)a.btot[o + J] : 0;
+    const int64_t sJ = J >= 0 ? (int64_t)a.bstart[o + J] : 0;
+    const Pre slo = J >= 0 ? Pre{sel_pa, sel_ps} : seed_lo;
+    const Suf shi = J >= 0 ? Suf{sel_sa, sel_ss} : seed_hi;
+    const double cR_eff = (double)(M - sJ - cJ) + cR;
+    const bool first = J < 0 || J == first_ne;
+    const bool last = J < 0 || J == last_ne;
+    const uint32_t *src = a.keys + row * a.cap + sJ;
+    if (cJ <= (int64_t)kWaveBucket) {
+      if (w == 0) {
+        WaveTeam<kWave> wteam;
+        float s[16];
+        const int base = wteam.lane * 16;
+        const int nv = (int)min(max(cJ - base, (int64_t)0), (int64_t)16);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = e < nv ? value_of(src[base + e]) : 0.0f;
+        PartInfo part;
+        part.nvalid = nv;
+        part.above = (double)cJ + cR_eff;
+        part.seed_lo = slo;
+        part.seed_hi = shi;
+        part.first = first;
+        part.last = last;
+        const double bb = segment_solve<16>(s, nv, part, a.k, a.t, c, a.cf, wteam);
+        if (lane == 0) sel_b = bb;
+      }
+    } else {
+      // a bucket of several tiles: its tile aggregates, then locate over them
+      constexpr int TT = kLocT * kKpt;
+      TileAgg *ta = a.tagg + row * a.max_tiles;
+      for (int64_t t0 = 0; t0 < cJ; t0 += TT) {
+        float s[kKpt];
+        const int nv = load_sorted_at<kLocT>(src, t0, cJ, 0u, s);
+        tile_aggregate<kLocT>(s, nv, c, a.cf, team, ta + t0 / TT);
+      }
+      const double bb = locate_sorted<kLocT>(src, cJ, 0u, slo, shi, cR_eff, first, last, ta,
+                                             a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, a.k, a.t, c,
+                                             a.cf, team);
+      if (threadIdx.x == 0) sel_b = bb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const double bb = sel_b;
+      S.b = bb;
+      const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
+      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+    }
   }
   __syncthreads();
-  const int64_t cJ = J >= 0 ? (int64_t)a.btot[o + J] : 0;
-  const int64_t sJ = J >= 0 ? (int64_t)a.bstart[o + J] : 0;
-  const Pre slo = J >= 0 ? Pre{sel_pa, sel_ps} : seed_lo;
-  const Suf shi = J >= 0 ? Suf{sel_sa, sel_ss} : seed_hi;
-  const double cR_eff = (double)(M - sJ - cJ) + cR;
-  const bool first = J < 0 || J == first_ne;
-  const bool last = J < 0 || J == last_ne;
-  const uint32_t *src = a.keys + row * a.cap + sJ;
-  double b;
-  if (cJ <= (int64_t)kBT * kKpt) {
-    float s[kKpt];
-    const int nv = load_sorted_at<kBT>(src, 0, cJ, 0u, s);
-    PartInfo part;
-    part.nvalid = nv;
-    part.above = (double)cJ + cR_eff;
-    part.seed_lo = slo;
-    part.seed_hi = shi;
-    part.first = first;
-    part.last = last;
-    b = segment_solve<kKpt>(s, nv, part, a.k, a.t, c, a.cf, team);
-  } else {
-    // a bucket of several tiles: its tile aggregates, then locate over them
-    constexpr int TT = kBT * kKpt;
-    TileAgg *ta = a.tagg + row * a.max_tiles;
-    for (int64_t t0 = 0; t0 < cJ; t0 += TT) {
-      float s[kKpt];
-      const int nv = load_sorted_at<kBT>(src, t0, cJ, 0u, s);
-      tile_aggregate<kBT>(s, nv, c, a.cf, team, ta + t0 / TT);
-    }
-    b = locate_sorted<kBT>(src, cJ, 0u, slo, shi, cR_eff, first, last, ta, a.tpre + row * a.max_tiles,
-                           a.tsuf + row * a.max_tiles, a.k, a.t, c, a.cf, team);
-  }
-  if (threadIdx.x == 0) {
-    S.b = b;
-    const bool hit = (b >= S.a_lo) && (b < S.a_hi);
-    S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
-  }
+  if (S.flags & LAPSUM_FLAG_FALLBACK) fallback_row<kLocT>(fb, (int)row, L.fb);
 }
 
 int band_count_blocks(int gx, int *group) {
@@ -424,13 +433,13 @@ int band_count_blocks(int gx, int *group) {
   return (gx + *group - 1) / *group;
 }
 
-hipError_t launch_band_buckets(const BandArgs &a, hipStream_t s) {
+hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t s) {
   const dim3 blk((unsigned)a.nblk, (unsigned)a.rows);
   hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scan_kernel, dim3(kBandBuckets / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_sort_kernel, dim3(kBandBuckets / (kBT / kWave), (unsigned)a.rows), dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kLocT), 0, s, a, fb);
   return hipGetLastError();
 }
 

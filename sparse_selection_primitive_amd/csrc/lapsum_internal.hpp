@@ -96,9 +96,8 @@ size_t band_offs_bytes(int64_t rows, int grid_x);
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
                               RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
 hipError_t launch_segment(const SegArgs &a, hipStream_t s);
-hipError_t launch_band_buckets(const BandArgs &a, hipStream_t s);
+hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fallback, hipStream_t s);
 int band_count_blocks(int gx, int *group);
-hipError_t launch_fallback(const SegArgs &a, hipStream_t s);
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
                         double *b, hipStream_t s);
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st,

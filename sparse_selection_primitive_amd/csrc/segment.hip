@@ -11,13 +11,12 @@
 //          the threshold curve at tile ends, the balancing tile, the curve at
 //          every knot inside it, and the closed-form root.
 //
-// Full-sort rows run one regular launch per phase (a kernel
-// boundary is the cheapest grid-wide synchronisation on this GPU, far below
-// a cooperative launch or an in-kernel grid barrier).  The fallback runs as a
-// single launch with one workgroup per row that sorts and solves the whole
-// row by itself: when every bracket held it returns at once, which keeps the
-// common case to one short launch; on a miss it is slower but exact and
-// deterministic.
+// Full-sort rows run one regular launch per phase (a kernel boundary is the
+// cheapest grid-wide synchronisation on this GPU, far below a cooperative
+// launch or an in-kernel grid barrier).  The bracketing fallback
+// (fallback_row) instead sorts and solves a whole row inside one workgroup,
+// at the end of the band kernel of that row: when every bracket held it costs
+// nothing; on a miss it is slower but exact and deterministic.
 #include "segment_dev.hpp"
 
 namespace lapsum {
@@ -116,21 +115,6 @@ hipError_t launch_segment(const SegArgs &a, hipStream_t s) {
   }
   hipLaunchKernelGGL(seg_tiles_kernel, tiles, dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(seg_locate_kernel, dim3((unsigned)a.rows), dim3(kNT), 0, s, a);
-  return hipGetLastError();
-}
-
-// -------------------------------------------- fallback: one workgroup per row
-constexpr int kFbNT = 1024;
-
-__global__ __launch_bounds__(kFbNT) void fallback_kernel(SegArgs a) {
-  __shared__ SegLds<kFbNT> L;
-  const int row = blockIdx.x;
-  if (!seg_active(a, row)) return;  // the bracket held: nothing to do
-  fallback_row<kFbNT>(a, row, L);
-}
-
-hipError_t launch_fallback(const SegArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(fallback_kernel, dim3((unsigned)a.rows), dim3(kFbNT), 0, s, a);
   return hipGetLastError();
 }
 
