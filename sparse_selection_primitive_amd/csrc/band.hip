@@ -44,57 +44,58 @@ LDEV int band_shift(const RowState &S) {
 }
 
 // Band keys of count/scatter workgroup `blk`: wave w walks the workgroup's
-// slots w, w + 4, ...; its lanes stride through each slot.
-template <class F>
-LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, F &&f) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+// slots w, w + 4, ...; its lanes stride through each slot.  The slot bounds
+// of all the workgroup's slots are read first (one round trip), into `sb`.
+constexpr int kMaxGroup = 64;  // filter slots per count/scatter workgroup, at most
+LDEV void load_slot_bounds(const BandArgs &a, int64_t row, int blk, uint32_t *sb) {
   const uint32_t *ro = a.offs + row * (a.gx + 1);
-  const int s0 = blk * a.group, s1 = min(a.gx, s0 + a.group);
-  for (int sl = s0 + w; sl < s1; sl += kBT / kWave) {
-    const uint32_t cnt = ro[sl + 1] - ro[sl];
-    const uint32_t *src = a.slots + (row * a.gx + sl) * (int64_t)kBandSlot;
-    for (uint32_t i = lane; i < cnt; i += kWave) f(src[i]);
+  const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
+  for (int i = threadIdx.x; i <= ns; i += kBT) sb[i] = ro[s0 + i];
+}
+template <class F>
+LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint32_t *sb, F &&f) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
+  for (int i = w; i < ns; i += kBT / kWave) {
+    const uint32_t cnt = sb[i + 1] - sb[i];
+    const uint32_t *src = a.slots + (row * a.gx + s0 + i) * (int64_t)kBandSlot;
+    for (uint32_t q = lane; q < cnt; q += kWave) f(src[q]);
   }
 }
 
 __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   __shared__ uint32_t h[kBandBuckets];
+  __shared__ uint32_t sb[kMaxGroup + 1];
   const int64_t row = blockIdx.y;
   const int blk = blockIdx.x;
   const RowState &S = a.st[row];
+  load_slot_bounds(a, row, blk, sb);
+  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) h[j] = 0u;
   if (!band_active(S)) return;
   const uint32_t kmin = S.kmin;
   const int shift = band_shift(S);
-  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) h[j] = 0u;
   __syncthreads();
-  for_each_band_key(a, row, blk, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
+  for_each_band_key(a, row, blk, sb, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
   __syncthreads();
   uint32_t *dst = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
   for (int j = threadIdx.x; j < kBandBuckets; j += kBT) dst[j] = h[j];
 }
 
-// one thread per bucket: exclusive scan over the count workgroups, in place
+// one thread per bucket: exclusive scan over the count workgroups, in
+// place; every count is loaded before the first is used
 __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   const int64_t row = blockIdx.y;
-  if (!band_active(a.st[row])) return;
   const int j = blockIdx.x * kBT + threadIdx.x;
   uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
+  uint32_t v[kBandCountBlocks];
+#pragma unroll
+  for (int b = 0; b < kBandCountBlocks; ++b) v[b] = b < a.nblk ? h[(int64_t)b * kBandBuckets] : 0u;
+  if (!band_active(a.st[row])) return;
   uint32_t run = 0u;
-  int b = 0;
-  for (; b + 8 <= a.nblk; b += 8) {
-    uint32_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = h[(int64_t)(b + u) * kBandBuckets];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      h[(int64_t)(b + u) * kBandBuckets] = run;
-      run += v[u];
-    }
-  }
-  for (; b < a.nblk; ++b) {
-    const uint32_t v = h[(int64_t)b * kBandBuckets];
-    h[(int64_t)b * kBandBuckets] = run;
-    run += v;
+  for (int b = 0; b < kBandCountBlocks; ++b) {
+    if (b < a.nblk) h[(int64_t)b * kBandBuckets] = run;
+    run += v[b];
   }
   a.btot[row * kBandBuckets + j] = run;
 }
@@ -102,34 +103,38 @@ __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
 __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   __shared__ uint32_t base[kBandBuckets];
   __shared__ uint32_t wsum[kBT / kWave];
+  __shared__ uint32_t sb[kMaxGroup + 1];
   const int64_t row = blockIdx.y;
   const int blk = blockIdx.x;
   const RowState &S = a.st[row];
-  if (!band_active(S)) return;
-  const uint32_t kmin = S.kmin;
-  const int shift = band_shift(S);
-  // bucket starts (thread i owns buckets i*kBPT ..), plus this workgroup's
-  // offset inside each bucket
+  // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
+  // inside each bucket and its slot bounds, all loaded before any is used
   const int64_t o = row * kBandBuckets;
-  uint32_t v[kBPT];
-  uint32_t sum = 0u;
+  const uint32_t *hin = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
+  uint32_t v[kBPT], hv[kBPT];
 #pragma unroll
   for (int u = 0; u < kBPT; ++u) {
     v[u] = a.btot[o + threadIdx.x * kBPT + u];
-    sum += v[u];
+    hv[u] = hin[threadIdx.x * kBPT + u];
   }
+  load_slot_bounds(a, row, blk, sb);
+  if (!band_active(S)) return;
+  const uint32_t kmin = S.kmin;
+  const int shift = band_shift(S);
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int u = 0; u < kBPT; ++u) sum += v[u];
   uint32_t run = wg_excl_scan<kBT>(sum, wsum);
-  const uint32_t *hin = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
 #pragma unroll
   for (int u = 0; u < kBPT; ++u) {
     const int j = threadIdx.x * kBPT + u;
-    base[j] = run + hin[j];
+    base[j] = run + hv[u];
     if (blk == 0) a.bstart[o + j] = run;
     run += v[u];
   }
   __syncthreads();
   uint32_t *dst = a.keys + row * a.cap;
-  for_each_band_key(a, row, blk, [&](uint32_t key) {
+  for_each_band_key(a, row, blk, sb, [&](uint32_t key) {
     const uint32_t pos = atomicAdd(&base[(key - kmin) >> shift], 1u);
     dst[pos] = key;
   });
@@ -242,13 +247,14 @@ __global__ __launch_bounds__(kBT) void band_sort_kernel(BandArgs a) {
   __shared__ TileAgg lagg;
   const int64_t row = blockIdx.y;
   const RowState &S = a.st[row];
-  if (!band_active(S)) return;
-  const int shift = band_shift(S);
   const int64_t o = row * kBandBuckets;
   const int lane = threadIdx.x & (kWave - 1);
   const int j = blockIdx.x * (kBT / kWave) + (int)threadIdx.x / kWave;
   const int cnt = (int)a.btot[o + j];
-  uint32_t *kb = a.keys + row * a.cap + a.bstart[o + j];
+  const uint32_t bst = a.bstart[o + j];
+  if (!band_active(S)) return;
+  const int shift = band_shift(S);
+  uint32_t *kb = a.keys + row * a.cap + bst;
   TileAgg *out = a.bagg + o + j;
   if (cnt == 0) {
     if (lane == 0) write_agg(out, Pre{0.0f, 0.0}, Suf{0.0f, 0.0});
@@ -304,6 +310,8 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   __shared__ int red[3][kLocT / kWave];
   __shared__ float sel_pa, sel_sa;
   __shared__ double sel_ps, sel_ss, sel_b;
+  __shared__ uint32_t sel_c, sel_st;
+  __shared__ int sel_fb;
   const int64_t row = blockIdx.x;
   RowState &S = a.st[row];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -318,7 +326,9 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     cnt[u] = a.btot[o + j0 + u];
     st0[u] = a.bstart[o + j0 + u];
   }
-  if (band_active(S)) {
+  const bool active = band_active(S);
+  if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
+  if (active) {
     BlockTeam<kLocT, 1> team(&L.team);
     const double c = a.c;
     const int64_t M = (int64_t)S.band;
@@ -373,10 +383,12 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       sel_ps = u == 0 ? before[0].s : before[1].s;
       sel_sa = u == 0 ? after[0].a : after[1].a;
       sel_ss = u == 0 ? after[0].s : after[1].s;
+      sel_c = u == 0 ? cnt[0] : cnt[1];
+      sel_st = u == 0 ? st0[0] : st0[1];
     }
     __syncthreads();
-    const int64_t cJ = J >= 0 ? (int64_t)a.btot[o + J] : 0;
-    const int64_t sJ = J >= 0 ? (int64_t)a.bstart[o + J] : 0;
+    const int64_t cJ = J >= 0 ? (int64_t)sel_c : 0;
+    const int64_t sJ = J >= 0 ? (int64_t)sel_st : 0;
     const Pre slo = J >= 0 ? Pre{sel_pa, sel_ps} : seed_lo;
     const Suf shi = J >= 0 ? Suf{sel_sa, sel_ss} : seed_hi;
     const double cR_eff = (double)(M - sJ - cJ) + cR;
@@ -421,10 +433,11 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       S.b = bb;
       const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
       S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+      sel_fb = hit ? 0 : 1;
     }
   }
   __syncthreads();
-  if (S.flags & LAPSUM_FLAG_FALLBACK) fallback_row<kLocT>(fb, (int)row, L.fb);
+  if (sel_fb) fallback_row<kLocT>(fb, (int)row, L.fb);
 }
 
 int band_count_blocks(int gx, int *group) {

@@ -377,69 +377,85 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
 // fallback launch is needed on this path.
 constexpr int kBandNT = 512;
 
-template <int NP>
+// Sort + solve + certify the band of one row with NP >= m keys (m = band
+// size), E = NP / kBandNT keys per thread.
+template <int NP, class Lds>
+LDEV void band_onchip_row(const uint32_t *__restrict__ slots, const uint32_t *soffs, int gx, int64_t row, int m,
+                          RowState &S, double k, double t, Lds &lds) {
+  constexpr int E = NP / kBandNT;
+  BlockTeam<kBandNT, E> team(reinterpret_cast<BlockTeamLds<kBandNT, E> *>(&lds));
+  const int base = team.lane * E;
+  // slot holding index `base`: the last b with soffs[b] <= base
+  int lo = 0, hi = gx - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)soffs[mid] <= base) lo = mid;
+    else hi = mid - 1;
+  }
+  int b = lo;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = base + e;
+    if (j < m) {
+      while ((int)soffs[b + 1] <= j) ++b;
+      key[e] = slots[(row * gx + b) * kBandSlot + (j - (int)soffs[b])];
+    } else {
+      key[e] = 0xFFFFFFFFu;
+    }
+  }
+  bitonic_sort<E>(key, team);
+  const int nv = min(max(m - base, 0), E);
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+
+  const double c = kLog2e / t;
+  PartInfo part;
+  part.nvalid = nv;
+  part.above = (double)m + (double)S.count_hi;
+  part.seed_lo = Pre{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
+  part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
+  part.first = true;
+  part.last = true;
+  const double bb = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
+  if (threadIdx.x == 0) {
+    S.b = bb;
+    const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
+    S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+  }
+  __syncthreads();
+}
+
+// The band's actual size picks the sort (1024 .. NPMAX keys), so a band far
+// below its capacity is not sorted at the capacity.
+template <int NPMAX>
 __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__restrict__ slots,
                                                              const uint32_t *__restrict__ offs, int gx,
                                                              RowState *__restrict__ st, double k, double t,
                                                              SegArgs fb) {
-  constexpr int E = NP / kBandNT;
   union BandLds {
-    BlockTeamLds<kBandNT, E> band;
+    BlockTeamLds<kBandNT, NPMAX / kBandNT> band;
     SegLds<kBandNT> full;
   };
   __shared__ BandLds lds;
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
+  __shared__ int fall;
   const int64_t row = blockIdx.x;
   RowState &S = st[row];
+  const uint32_t *ro = offs + row * (int64_t)(gx + 1);
+  for (int i = threadIdx.x; i <= gx; i += kBandNT) soffs[i] = ro[i];
+  __syncthreads();
   if (!(S.flags & LAPSUM_FLAG_OVERFLOW)) {
-    BlockTeam<kBandNT, E> team(&lds.band);
     const int m = (int)S.band;
-    const uint32_t *ro = offs + row * (int64_t)(gx + 1);
-    for (int i = threadIdx.x; i <= gx; i += kBandNT) soffs[i] = ro[i];
-    __syncthreads();
-    const int base = team.lane * E;
-    // slot holding index `base`: the last b with soffs[b] <= base
-    int lo = 0, hi = gx - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)soffs[mid] <= base) lo = mid;
-      else hi = mid - 1;
-    }
-    int b = lo;
-    uint32_t key[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = base + e;
-      if (j < m) {
-        while ((int)soffs[b + 1] <= j) ++b;
-        key[e] = slots[((int64_t)row * gx + b) * kBandSlot + (j - (int)soffs[b])];
-      } else {
-        key[e] = 0xFFFFFFFFu;
-      }
-    }
-    bitonic_sort<E>(key, team);
-    const int nv = min(max(m - base, 0), E);
-    float s[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
-
-    const double c = kLog2e / t;
-    PartInfo part;
-    part.nvalid = nv;
-    part.above = (double)m + (double)S.count_hi;
-    part.seed_lo = Pre{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
-    part.seed_hi = Suf{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
-    part.first = true;
-    part.last = true;
-    const double bb = segment_solve<E>(s, nv, part, k, t, c, (float)c, team);
-    if (threadIdx.x == 0) {
-      S.b = bb;
-      const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
-      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
-    }
-    __syncthreads();
+    if (m <= 1024 || NPMAX == 1024) band_onchip_row<1024>(slots, soffs, gx, row, m, S, k, t, lds);
+    else if (m <= 2048 || NPMAX == 2048) band_onchip_row<(NPMAX < 2048 ? NPMAX : 2048)>(slots, soffs, gx, row, m, S, k, t, lds);
+    else if (m <= 4096 || NPMAX == 4096) band_onchip_row<(NPMAX < 4096 ? NPMAX : 4096)>(slots, soffs, gx, row, m, S, k, t, lds);
+    else band_onchip_row<NPMAX>(slots, soffs, gx, row, m, S, k, t, lds);
   }
-  if (S.flags & LAPSUM_FLAG_FALLBACK) fallback_row<kBandNT>(fb, (int)row, lds.full);
+  if (threadIdx.x == 0) fall = (S.flags & LAPSUM_FLAG_FALLBACK) != 0;
+  __syncthreads();
+  if (fall) fallback_row<kBandNT>(fb, (int)row, lds.full);
 }
 
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
