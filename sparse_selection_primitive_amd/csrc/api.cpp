@@ -55,15 +55,21 @@ SegRegions seg_regions(Layout &L, int64_t rows, int64_t len) {
   return r;
 }
 
-// Offsets of the workspace regions of the bucketed band solve.
+// Offsets of the workspace regions of the bucketed sort + solve: the band of
+// the bracketing path (slots from gx filter workgroups), or whole rows of the
+// full-sort path (full = true, n scores per row).
 struct BandRegions {
-  size_t keys, tmp, hist, btot, bstart, bagg, tagg, tpre, tsuf;
+  size_t keys, tmp, hist, btot, bstart, bagg, tagg, tpre, tsuf, mm;
   int nblk, group, max_tiles;
+  int64_t chunk;
 };
 
-BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx) {
+BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx, bool full, int64_t n) {
   BandRegions r;
-  r.nblk = band_count_blocks(gx, &r.group);
+  r.group = 0;
+  r.chunk = 0;
+  r.mm = 0;
+  r.nblk = full ? full_count_blocks(n, &r.chunk) : band_count_blocks(gx, &r.group);
   r.max_tiles = (int)(cap / kTile);
   const size_t keys = (size_t)rows * (size_t)cap * sizeof(uint32_t);
   const size_t nb = (size_t)rows * kBandBuckets;
@@ -76,6 +82,7 @@ BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx) {
   r.tagg = L.take((size_t)rows * (size_t)r.max_tiles * tile_agg_bytes());
   r.tpre = L.take((size_t)rows * (size_t)r.max_tiles * pre_bytes());
   r.tsuf = L.take((size_t)rows * (size_t)r.max_tiles * suf_bytes());
+  if (full) r.mm = L.take((size_t)rows * (size_t)r.nblk * 2 * sizeof(uint32_t));
   return r;
 }
 
@@ -195,7 +202,8 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
   Layout F;
   if (path == LAPSUM_PATH_FULLSORT) {
     P.st = F.take((size_t)rows * row_state_bytes());
-    P.full_seg = seg_regions(F, rows, n);
+    P.cap = round_up(n, kTile);
+    P.bnd = band_regions(F, rows, P.cap, 0, true, n);
   } else if (path == LAPSUM_PATH_BRACKET) {
     int sl = o.sample_log2;
     if (sl == 0) {
@@ -228,7 +236,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
     P.offs = F.take(band_offs_bytes(rows, P.fgx));
-    if (!P.band_onchip) P.bnd = band_regions(F, rows, P.cap, P.fgx);
+    if (!P.band_onchip) P.bnd = band_regions(F, rows, P.cap, P.fgx, false, n);
     P.full_seg = seg_regions(F, rows, n);
   }
   P.fwd_bytes = F.off;
@@ -280,7 +288,7 @@ SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t 
 }
 
 BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots,
-                   const uint32_t *offs, double k, double t) {
+                   const uint32_t *offs, double k, double t, const float *r = nullptr, int64_t n = 0) {
   const BandRegions &R = P.bnd;
   BandArgs a;
   a.rows = (int)rows;
@@ -289,6 +297,13 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   a.nblk = R.nblk;
   a.slots = slots;
   a.offs = offs;
+  a.r = r;
+  a.n = n;
+  a.chunk = R.chunk;
+  // about 32 keys per bucket: the whole row, or the band expected for this
+  // capacity (a third of it)
+  a.bbits = bucket_bits(r != nullptr ? n : P.cap / 3);
+  a.mm = r != nullptr ? reinterpret_cast<uint32_t *>(ws + R.mm) : nullptr;
   a.st = st;
   a.keys = reinterpret_cast<uint32_t *>(ws + R.keys);
   a.tmp = reinterpret_cast<uint32_t *>(ws + R.tmp);
@@ -400,7 +415,8 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
     tm.mark(LAPSUM_STAGE_INIT, 1);
     tm.mark(LAPSUM_STAGE_FULLSORT, 0);
-    LAPSUM_TRY(launch_segment(seg_args(P.full_seg, ws, kSegFull, rows, n, r, rs, k, t), s));
+    const SegArgs none{};  // full rows have no bracket, so no fallback
+    LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, nullptr, nullptr, k, t, r, n), none, s));
     tm.mark(LAPSUM_STAGE_FULLSORT, 1);
   } else {
     const double *ovr = o.bracket_override;

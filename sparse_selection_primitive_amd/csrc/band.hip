@@ -1,29 +1,33 @@
-// Bucketed band solve for bands too large for one workgroup ("Fast LapSum:
-// Exact Differentiable Top-k at Million Scale", section 2.2, probabilistic
-// bracketing, step 3: the band is sorted and solved exactly, seeded with the
-// tail sums; step 4: certification).
+// Bucketed sort + solve ("Fast LapSum: Exact Differentiable Top-k at Million
+// Scale", section 2.2) for key sets too large for one workgroup: the band of
+// the probabilistic bracketing (step 3: the band is sorted and solved
+// exactly, seeded with the tail sums; step 4: certification), and whole rows
+// of the full-sort solver (full-row mode: the keys are read from the scores,
+// a min/max pass first gives their range, and there is no bracket).
 //
 // The band keys lie in [kmin, kmax].  Bucket j holds the keys with
 // (key - kmin) >> shift == j, shift the smallest value that leaves at most
-// kBandBuckets buckets; every key of bucket j is below every key of bucket
-// j + 1, so sorting each bucket on its own sorts the band (one
-// most-significant-digit radix pass, then independent bucket sorts).
+// 2^bbits buckets (bbits chosen for about 32 keys per bucket, at most
+// kBandBuckets buckets); every key of bucket j is below every key of bucket
+// j + 1 (one most-significant-digit radix pass).  The anchored sums of a
+// bucket need only its smallest and largest key, so no bucket is sorted but
+// the one that holds the root.
 //
-//   band_count_kernel    bucket counts of each workgroup's filter slots
+//   band_minmax_kernel   (full-row mode) key range of each workgroup's chunk
+//   band_count_kernel    bucket counts of each workgroup's filter slots or chunk
 //   band_scan_kernel     per bucket, offsets of the workgroups inside it
 //   band_scatter_kernel  keys to their bucket (order inside a bucket free)
-//   band_sort_kernel     one wave sorts each bucket of at most 1024 keys in
-//                        registers; larger buckets are sorted by the whole
-//                        workgroup; anchored aggregates of every bucket
+//   band_agg_kernel      anchored aggregates of every bucket, order-free
 //   band_locate_kernel   scan of the bucket aggregates between the tail
 //                        seeds, threshold curve at the bucket ends, the
-//                        balancing bucket, the root inside it,
+//                        balancing bucket, its sort and the root inside it,
 //                        certification, and the full-sort fallback of a row
 //                        whose bracket missed
 //
-// Every count is an integer and every floating-point sum runs over sorted
-// keys in a fixed order, so the result does not depend on the order in which
-// the scatter placed keys inside a bucket.
+// Every count is an integer, the bucket sums are fixed-point integer sums,
+// and the balancing bucket is sorted before anything is summed over it in
+// order, so the result does not depend on the order in which the scatter
+// placed keys inside a bucket.
 #include <limits.h>
 
 #include "segment_dev.hpp"
@@ -32,15 +36,32 @@ namespace lapsum {
 
 constexpr int kBT = 256;                   // threads per workgroup of every band kernel
 constexpr int kBPT = kBandBuckets / kBT;   // buckets per thread in the per-row scans
-constexpr int kWaveBucket = 16 * kWave;    // largest bucket one wave sorts
+constexpr int kWaveBucket = 16 * kWave;    // largest balancing bucket one wave sorts
 static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of the workgroup size");
 
 LDEV bool band_active(const RowState &S) { return !(S.flags & LAPSUM_FLAG_OVERFLOW); }
 
-LDEV int band_shift(const RowState &S) {
+LDEV int band_shift(const RowState &S, int bbits) {
   const uint32_t span = (S.band > 1 && S.kmax > S.kmin) ? S.kmax - S.kmin : 0u;
   const int bits = span == 0u ? 0 : 32 - __clz((int)span);
-  return max(bits - kBandBucketBits, 0);
+  return max(bits - bbits, 0);
+}
+
+// Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
+// an L2 of its own.  Renumbered so that consecutive (row, chunk) pairs share
+// an XCD, the partial-line key writes of one row (and their later reads)
+// stay inside one L2 instead of being merged from eight.
+constexpr int kXcds = 8;
+LDEV int64_t xcd_linear() {
+  const int64_t T = (int64_t)gridDim.x * gridDim.y;
+  const int64_t L = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+  const int64_t x = L % kXcds, per = T / kXcds, rem = T % kXcds;
+  return x * per + min(x, rem) + L / kXcds;
+}
+LDEV void xcd_tile(int64_t &row, int &blk) {
+  const int64_t p = xcd_linear();
+  row = p / gridDim.x;
+  blk = (int)(p % gridDim.x);
 }
 
 // Band keys of count/scatter workgroup `blk`: wave w walks the workgroup's
@@ -52,8 +73,45 @@ LDEV void load_slot_bounds(const BandArgs &a, int64_t row, int blk, uint32_t *sb
   const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
   for (int i = threadIdx.x; i <= ns; i += kBT) sb[i] = ro[s0 + i];
 }
+// Scores of full-row workgroup `blk`: its chunk, 16 bytes per thread and
+// step on the vector path.
+template <class F>
+LDEV void for_each_row_key(const BandArgs &a, int64_t row, int blk, F &&f) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const float *rr = a.r + row * a.n;
+  const int64_t c0 = (int64_t)blk * a.chunk, c1 = min(a.n, c0 + a.chunk);
+  const bool vec = (a.n & 3) == 0 && (((uintptr_t)a.r & 15u) == 0);
+  if (vec) {
+    // kRowLoads loads in flight per thread and round (the chunk is a
+    // multiple of 4 long, so a vector that starts inside it ends inside it)
+    constexpr int kRowLoads = 4;
+    for (int64_t i = c0 + 4 * (int64_t)threadIdx.x; i < c1; i += 4 * kBT * kRowLoads) {
+      f4 v[kRowLoads];
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) {
+        const int64_t ii = i + (int64_t)u * 4 * kBT;
+        v[u] = ii < c1 ? __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr + ii)) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) {
+        if (i + (int64_t)u * 4 * kBT < c1) {
+          f(key_of(v[u].x));
+          f(key_of(v[u].y));
+          f(key_of(v[u].z));
+          f(key_of(v[u].w));
+        }
+      }
+    }
+  } else {
+    for (int64_t i = c0 + threadIdx.x; i < c1; i += kBT) f(key_of(rr[i]));
+  }
+}
 template <class F>
 LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint32_t *sb, F &&f) {
+  if (a.r != nullptr) {
+    for_each_row_key(a, row, blk, f);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
   for (int i = w; i < ns; i += kBT / kWave) {
@@ -63,22 +121,91 @@ LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint3
   }
 }
 
+// full-row mode: key minimum and maximum of each workgroup's chunk
+__global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
+  __shared__ uint32_t lmn[kBT / kWave], lmx[kBT / kWave];
+  const int64_t row = blockIdx.y;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for_each_row_key(a, row, blockIdx.x, [&](uint32_t k) {
+    mn = min(mn, k);
+    mx = max(mx, k);
+  });
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, m, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, kWave));
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lmn[w] = mn;
+    lmx[w] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < kBT / kWave; ++i) {
+      mn = min(mn, lmn[i]);
+      mx = max(mx, lmx[i]);
+    }
+    a.mm[(row * a.nblk + blockIdx.x) * 2] = mn;
+    a.mm[(row * a.nblk + blockIdx.x) * 2 + 1] = mx;
+  }
+}
+
 __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   __shared__ uint32_t h[kBandBuckets];
   __shared__ uint32_t sb[kMaxGroup + 1];
   const int64_t row = blockIdx.y;
   const int blk = blockIdx.x;
-  const RowState &S = a.st[row];
-  load_slot_bounds(a, row, blk, sb);
-  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) h[j] = 0u;
-  if (!band_active(S)) return;
-  const uint32_t kmin = S.kmin;
-  const int shift = band_shift(S);
+  __shared__ uint32_t rng[2];
+  RowState &S = a.st[row];
+  if (a.r == nullptr) load_slot_bounds(a, row, blk, sb);
+  const int nb = 1 << a.bbits;
+  for (int j = threadIdx.x; j < nb; j += kBT) h[j] = 0u;
+  if (a.r != nullptr) {
+    // full-row mode: the row's key range from the min/max partials; the
+    // first workgroup records it (and the key count) for the later kernels
+    if (threadIdx.x < kWave) {
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+      for (int i = threadIdx.x; i < a.nblk; i += kWave) {
+        mn = min(mn, a.mm[(row * a.nblk + i) * 2]);
+        mx = max(mx, a.mm[(row * a.nblk + i) * 2 + 1]);
+      }
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, m, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, kWave));
+      }
+      if (threadIdx.x == 0) {
+        rng[0] = mn;
+        rng[1] = mx;
+        if (blk == 0) {
+          S.kmin = mn;
+          S.kmax = mx;
+          S.band = (unsigned long long)a.n;
+        }
+      }
+    }
+  } else if (!band_active(S)) {
+    return;
+  }
   __syncthreads();
+  uint32_t kmin;
+  int shift;
+  if (a.r != nullptr) {
+    RowState R;
+    R.kmin = rng[0];
+    R.kmax = rng[1];
+    R.band = (unsigned long long)a.n;
+    kmin = R.kmin;
+    shift = band_shift(R, a.bbits);
+  } else {
+    kmin = S.kmin;
+    shift = band_shift(S, a.bbits);
+  }
   for_each_band_key(a, row, blk, sb, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
   __syncthreads();
   uint32_t *dst = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
-  for (int j = threadIdx.x; j < kBandBuckets; j += kBT) dst[j] = h[j];
+  for (int j = threadIdx.x; j < nb; j += kBT) dst[j] = h[j];
 }
 
 // one thread per bucket: exclusive scan over the count workgroups, in
@@ -86,6 +213,7 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
 __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   const int64_t row = blockIdx.y;
   const int j = blockIdx.x * kBT + threadIdx.x;
+  if (j >= (1 << a.bbits)) return;
   uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
   uint32_t v[kBandCountBlocks];
 #pragma unroll
@@ -104,23 +232,26 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   __shared__ uint32_t base[kBandBuckets];
   __shared__ uint32_t wsum[kBT / kWave];
   __shared__ uint32_t sb[kMaxGroup + 1];
-  const int64_t row = blockIdx.y;
-  const int blk = blockIdx.x;
+  int64_t row;
+  int blk;
+  xcd_tile(row, blk);
   const RowState &S = a.st[row];
   // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
   // inside each bucket and its slot bounds, all loaded before any is used
   const int64_t o = row * kBandBuckets;
   const uint32_t *hin = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
+  const int nb = 1 << a.bbits;
   uint32_t v[kBPT], hv[kBPT];
 #pragma unroll
   for (int u = 0; u < kBPT; ++u) {
-    v[u] = a.btot[o + threadIdx.x * kBPT + u];
-    hv[u] = hin[threadIdx.x * kBPT + u];
+    const int j = threadIdx.x * kBPT + u;
+    v[u] = j < nb ? a.btot[o + j] : 0u;
+    hv[u] = j < nb ? hin[j] : 0u;
   }
-  load_slot_bounds(a, row, blk, sb);
+  if (a.r == nullptr) load_slot_bounds(a, row, blk, sb);
   if (!band_active(S)) return;
   const uint32_t kmin = S.kmin;
-  const int shift = band_shift(S);
+  const int shift = band_shift(S, a.bbits);
   uint32_t sum = 0u;
 #pragma unroll
   for (int u = 0; u < kBPT; ++u) sum += v[u];
@@ -128,8 +259,10 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
 #pragma unroll
   for (int u = 0; u < kBPT; ++u) {
     const int j = threadIdx.x * kBPT + u;
-    base[j] = run + hv[u];
-    if (blk == 0) a.bstart[o + j] = run;
+    if (j < nb) {
+      base[j] = run + hv[u];
+      if (blk == 0) a.bstart[o + j] = run;
+    }
     run += v[u];
   }
   __syncthreads();
@@ -140,7 +273,7 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   });
 }
 
-// ------------------------------------------------------------ bucket sort
+// ------------------------------------------------------ bucket aggregates
 LDEV void write_agg(TileAgg *out, Pre p, Suf s) {
   out->aP = p.a;
   out->sP = p.s;
@@ -148,10 +281,168 @@ LDEV void write_agg(TileAgg *out, Pre p, Suf s) {
   out->sS = s.s;
 }
 
-// One wave sorts a bucket of cnt <= 64*E keys in registers (blocked, E per
-// lane), writes it back and stores its anchored aggregates.
+// The anchored sums of a bucket need its extreme keys, not its order: the
+// P-type sum is anchored at the largest key, the S-type sum at the smallest,
+// and every term e^{-|x - anchor|/t} lies in [0, 1].  Each term is added as
+// a 64-bit fixed-point number with `fb` fraction bits, fb chosen from the
+// bucket size so that the sum stays below 2^62.  Integer sums do not depend
+// on the order in which the scatter left the keys, so the aggregates (and
+// everything computed from them) are bitwise reproducible.  A term loses at
+// most 2^-(fb+1) to the rounding; fb >= 30 for any bucket.
+LDEV int agg_frac_bits(uint32_t cnt) { return 62 - (32 - __clz((int)cnt)); }
+LDEV unsigned long long fixed_term(float v, int fb) { return __float2ull_rn(ldexpf(v, fb)); }
+LDEV double fixed_value(unsigned long long v, int fb) { return ldexp((double)v, -fb); }
+
+LDEV void agg_write(TileAgg *out, uint32_t kmx, uint32_t kmn, unsigned long long sp, unsigned long long ss, int fb) {
+  write_agg(out, Pre{value_of(kmx), fixed_value(sp, fb)}, Suf{value_of(kmn), fixed_value(ss, fb)});
+}
+
+// A team of LANES lanes aggregates one bucket, kAggE keys per lane and
+// round, the round's loads issued together (a bucket of one round keeps its
+// keys in registers for the second pass).
+constexpr int kAggE = 8;
+template <int LANES>
+LDEV void bucket_agg(const uint32_t *kb, int cnt, double c, TileAgg *out) {
+  constexpr int R = kAggE * LANES;  // keys per round
+  WaveTeam<LANES> team;
+  uint32_t key[kAggE];
+  uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+  for (int i0 = 0; i0 < cnt; i0 += R) {
+#pragma unroll
+    for (int e = 0; e < kAggE; ++e) {
+      const int i = i0 + e * LANES + team.lane;
+      key[e] = i < cnt ? kb[i] : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < kAggE; ++e) {
+      if (i0 + e * LANES + team.lane < cnt) {
+        kmx = max(kmx, key[e]);
+        kmn = min(kmn, key[e]);
+      }
+    }
+  }
+  kmx = team.umax(kmx);
+  kmn = team.umin(kmn);
+  const int fb = agg_frac_bits((uint32_t)cnt);
+  const double hi = (double)value_of(kmx), lo = (double)value_of(kmn);
+  unsigned long long sp = 0ull, ss = 0ull;
+  const bool reload = cnt > R;
+  for (int i0 = 0; i0 < cnt; i0 += R) {
+    if (reload) {
+#pragma unroll
+      for (int e = 0; e < kAggE; ++e) {
+        const int i = i0 + e * LANES + team.lane;
+        key[e] = i < cnt ? kb[i] : 0u;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kAggE; ++e) {
+      if (i0 + e * LANES + team.lane < cnt) {
+        const double x = (double)value_of(key[e]);
+        sp += fixed_term(wexp(x - hi, c), fb);
+        ss += fixed_term(wexp(lo - x, c), fb);
+      }
+    }
+  }
+  sp = team.sum(sp);
+  ss = team.sum(ss);
+  if (team.lane == 0) agg_write(out, kmx, kmn, sp, ss, fb);
+}
+
+// Each workgroup owns kAggGroup consecutive buckets of one row, one per
+// 16-lane team; a bucket of more than kAggTeamMax keys is left to a whole
+// wave, the workgroup's large buckets dealt out to its waves in turn.
+constexpr int kAggTeam = 16;
+constexpr int kAggGroup = kBT / kAggTeam;
+constexpr int kAggTeamMax = 4 * kAggE * kAggTeam;
+
+__global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
+  __shared__ uint32_t big;  // the workgroup's buckets too large for a team
+  int64_t row;
+  int blk;
+  xcd_tile(row, blk);
+  const RowState &S = a.st[row];
+  const int64_t o = row * kBandBuckets;
+  const int q = (int)threadIdx.x / kAggTeam;
+  const int j = blk * kAggGroup + q;
+  const int cnt = (int)a.btot[o + j];
+  const uint32_t bst = a.bstart[o + j];
+  if (!band_active(S)) return;
+  const int shift = band_shift(S, a.bbits);
+  const uint32_t *kb = a.keys + row * a.cap + bst;
+  TileAgg *out = a.bagg + o + j;
+  const int tl = threadIdx.x & (kAggTeam - 1);
+  if (threadIdx.x == 0) big = 0u;
+  __syncthreads();
+  if (cnt == 0) {
+    if (tl == 0) write_agg(out, Pre{0.0f, 0.0}, Suf{0.0f, 0.0});
+  } else if (shift == 0) {
+    // the bucket holds one distinct key
+    if (tl == 0) {
+      const float x = value_of(kb[0]);
+      write_agg(out, Pre{x, (double)cnt}, Suf{x, (double)cnt});
+    }
+  } else if (cnt <= kAggTeamMax) {
+    bucket_agg<kAggTeam>(kb, cnt, a.c, out);
+  } else if (tl == 0) {
+    atomicOr(&big, 1u << q);
+  }
+  __syncthreads();
+  const int w = threadIdx.x / kWave;
+  int i = 0;
+  for (uint32_t m = big; m != 0u; m &= m - 1u, ++i) {
+    if ((i & (kBT / kWave - 1)) != w) continue;
+    const int jj = blk * kAggGroup + __ffs((int)m) - 1;
+    bucket_agg<kWave>(a.keys + row * a.cap + a.bstart[o + jj], (int)a.btot[o + jj], a.c, a.bagg + o + jj);
+  }
+}
+
+// The whole workgroup sorts the keys kb[0 .. cnt) in place: stable LSD
+// radix passes (8-bit digits) over the keys relative to `kb0`, the lowest
+// key the range may hold (they differ from it in their low `bits` bits);
+// tb is scratch of the same size.
+template <int NT>
+LDEV void block_radix_sort(uint32_t *kb, uint32_t *tb, int64_t cnt, uint32_t kb0, int bits, RankLds<NT> &L) {
+  constexpr int TT = NT * kKpt;
+  __shared__ uint32_t h[256];
+  for (int64_t i = threadIdx.x; i < cnt; i += NT) kb[i] -= kb0;
+  __syncthreads();
+  uint32_t *src = kb, *dst = tb;
+  const int npass = (bits + 7) / 8;
+  const int64_t ntiles = (cnt + TT - 1) / TT;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int sh = 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += NT) h[i] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < cnt; i += NT) atomicAdd(&h[(src[i] >> sh) & 255u], 1u);
+    __syncthreads();
+    uint32_t run = wg_excl_scan<NT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.wsum);
+    for (int64_t tile = 0; tile < ntiles; ++tile) {
+      uint32_t key[kKpt];
+      int dig[kKpt];
+#pragma unroll
+      for (int q = 0; q < kKpt; ++q) {
+        const int64_t gi = tile * TT + w * (kWave * kKpt) + q * kWave + lane;
+        const bool valid = gi < cnt;
+        key[q] = valid ? src[gi] : 0u;
+        dig[q] = valid ? (int)((key[q] >> sh) & 255u) : 256;
+      }
+      const int vc = (int)min((int64_t)TT, cnt - tile * TT);
+      run += scatter_tile<NT>(key, dig, sh, vc, run, dst, L);
+    }
+    uint32_t *x = src;
+    src = dst;
+    dst = x;
+  }
+  for (int64_t i = threadIdx.x; i < cnt; i += NT) kb[i] = src[i] + kb0;
+  __syncthreads();
+}
+
+// One wave sorts a range of cnt <= 64*E keys in registers (blocked, E per
+// lane) and solves for the root inside it.
 template <int E>
-LDEV void wave_bucket(uint32_t *kb, int cnt, double c, float cf, TileAgg *out) {
+LDEV double wave_sort_solve(const uint32_t *kb, int cnt, PartInfo part, double k, double t, double c, float cf) {
   WaveTeam<kWave> team;
   const int base = team.lane * E;
   uint32_t key[E];
@@ -161,139 +452,18 @@ LDEV void wave_bucket(uint32_t *kb, int cnt, double c, float cf, TileAgg *out) {
   const int nv = min(max(cnt - base, 0), E);
   float s[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
-    if (e < nv) kb[base + e] = key[e];
-  }
-  team_aggregate<E>(s, nv, c, cf, team, out);
-}
-
-union BandSortLds {
-  RankLds<kBT> rk;
-  BlockTeamLds<kBT, kKpt> sort;
-  BlockTeamLds<kBT, 1> scan;
-};
-
-// The whole workgroup sorts one bucket of more than 1024 keys: a register
-// bitonic sort up to 4096 keys, else a stable LSD radix sort (8-bit digits)
-// of the keys relative to the bucket's lowest possible key `kb0` (they differ
-// in their low `bits` bits only).  Then the bucket's aggregates, tile by tile.
-LDEV void block_bucket(uint32_t *kb, uint32_t *tb, int cnt, uint32_t kb0, int bits, double c, float cf,
-                       BandSortLds &L, TileAgg *lagg, TileAgg *out) {
-  constexpr int TT = kBT * kKpt;
-  if (cnt <= TT) {
-    BlockTeam<kBT, kKpt> team(&L.sort);
-    const int base = threadIdx.x * kKpt;
-    uint32_t key[kKpt];
-#pragma unroll
-    for (int e = 0; e < kKpt; ++e) key[e] = (base + e < cnt) ? kb[base + e] : 0xFFFFFFFFu;
-    bitonic_sort<kKpt>(key, team);
-#pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if (base + e < cnt) kb[base + e] = key[e];
-    __syncthreads();
-  } else {
-    __shared__ uint32_t h[256];
-    for (int i = threadIdx.x; i < cnt; i += kBT) kb[i] -= kb0;
-    __syncthreads();
-    uint32_t *src = kb, *dst = tb;
-    const int npass = (bits + 7) / 8;
-    const int ntiles = (cnt + TT - 1) / TT;
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    for (int pass = 0; pass < npass; ++pass) {
-      const int sh = 8 * pass;
-      h[threadIdx.x] = 0u;
-      __syncthreads();
-      for (int i = threadIdx.x; i < cnt; i += kBT) atomicAdd(&h[(src[i] >> sh) & 255u], 1u);
-      __syncthreads();
-      uint32_t run = wg_excl_scan<kBT>(h[threadIdx.x], L.rk.wsum);
-      for (int tile = 0; tile < ntiles; ++tile) {
-        uint32_t key[kKpt];
-        int dig[kKpt];
-#pragma unroll
-        for (int q = 0; q < kKpt; ++q) {
-          const int gi = tile * TT + w * (kWave * kKpt) + q * kWave + lane;
-          const bool valid = gi < cnt;
-          key[q] = valid ? src[gi] : 0u;
-          dig[q] = valid ? (int)((key[q] >> sh) & 255u) : 256;
-        }
-        const int vc = min(TT, cnt - tile * TT);
-        run += scatter_tile<kBT>(key, dig, sh, vc, run, dst, L.rk);
-      }
-      uint32_t *x = src;
-      src = dst;
-      dst = x;
-    }
-    for (int i = threadIdx.x; i < cnt; i += kBT) kb[i] = src[i] + kb0;
-    __syncthreads();
-  }
-  // aggregates of the sorted bucket, tile by tile, joined in order
-  BlockTeam<kBT, 1> team(&L.scan);
-  Pre ap{0.0f, 0.0};
-  Suf as{0.0f, 0.0};
-  for (int t0 = 0; t0 < cnt; t0 += TT) {
-    float s[kKpt];
-    const int nv = load_sorted_at<kBT>(kb, t0, cnt, 0u, s);
-    team_aggregate<kKpt>(s, nv, c, cf, team, lagg);
-    ap = join(ap, Pre{lagg->aP, lagg->sP}, c);
-    as = join(as, Suf{lagg->aS, lagg->sS}, c);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) write_agg(out, ap, as);
-}
-
-__global__ __launch_bounds__(kBT) void band_sort_kernel(BandArgs a) {
-  __shared__ BandSortLds L;
-  __shared__ TileAgg lagg;
-  const int64_t row = blockIdx.y;
-  const RowState &S = a.st[row];
-  const int64_t o = row * kBandBuckets;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int j = blockIdx.x * (kBT / kWave) + (int)threadIdx.x / kWave;
-  const int cnt = (int)a.btot[o + j];
-  const uint32_t bst = a.bstart[o + j];
-  if (!band_active(S)) return;
-  const int shift = band_shift(S);
-  uint32_t *kb = a.keys + row * a.cap + bst;
-  TileAgg *out = a.bagg + o + j;
-  if (cnt == 0) {
-    if (lane == 0) write_agg(out, Pre{0.0f, 0.0}, Suf{0.0f, 0.0});
-  } else if (shift == 0) {
-    // every key of the bucket is the same value
-    if (lane == 0) {
-      const float x = value_of(kb[0]);
-      write_agg(out, Pre{x, (double)cnt}, Suf{x, (double)cnt});
-    }
-  } else if (cnt <= 64) {
-    wave_bucket<1>(kb, cnt, a.c, a.cf, out);
-  } else if (cnt <= 128) {
-    wave_bucket<2>(kb, cnt, a.c, a.cf, out);
-  } else if (cnt <= 256) {
-    wave_bucket<4>(kb, cnt, a.c, a.cf, out);
-  } else if (cnt <= 512) {
-    wave_bucket<8>(kb, cnt, a.c, a.cf, out);
-  } else if (cnt <= kWaveBucket) {
-    wave_bucket<16>(kb, cnt, a.c, a.cf, out);
-  }
-  if (shift == 0) return;
-  // buckets beyond one wave: the whole workgroup, one after another
-  for (int w = 0; w < kBT / kWave; ++w) {
-    const int jj = blockIdx.x * (kBT / kWave) + w;
-    const int cc = (int)a.btot[o + jj];
-    if (cc <= kWaveBucket) continue;
-    __syncthreads();
-    const uint32_t st0 = a.bstart[o + jj];
-    block_bucket(a.keys + row * a.cap + st0, a.tmp + row * a.cap + st0, cc, S.kmin + ((uint32_t)jj << shift), shift,
-                 a.c, a.cf, L, &lagg, a.bagg + o + jj);
-  }
+  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
+  part.nvalid = nv;
+  return segment_solve<E>(s, nv, part, k, t, c, cf, team);
 }
 
 // ---------------------------------------------------------------- locate
 // One workgroup of kLocT threads per row, two buckets per thread: a
 // workgroup scan of the bucket aggregates between the tail seeds, the
 // threshold curve at the bucket ends, the balancing bucket, and the root
-// inside it (by one wave when the bucket fits its registers, else by the
-// whole workgroup).  A row whose root falls outside its bracket is then
+// inside it.  Only that bucket is sorted: by one wave in registers when it
+// holds at most 1024 keys, else by the whole workgroup (radix passes in
+// place, then tile aggregates).  A row whose root falls outside its bracket is then
 // sorted and solved in full by the same workgroup (the deterministic
 // fallback), so no separate launch is needed.
 constexpr int kLocT = 1024;
@@ -312,7 +482,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   __shared__ double sel_ps, sel_ss, sel_b;
   __shared__ uint32_t sel_c, sel_st;
   __shared__ int sel_fb;
-  const int64_t row = blockIdx.x;
+  const int64_t row = xcd_linear();
   RowState &S = a.st[row];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
@@ -320,11 +490,13 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   // this thread's bucket records (issued before the row state is examined)
   TileAgg g[kLocPer];
   uint32_t cnt[kLocPer], st0[kLocPer];
+  const int nb = 1 << a.bbits;
 #pragma unroll
   for (int u = 0; u < kLocPer; ++u) {
-    g[u] = a.bagg[o + j0 + u];
-    cnt[u] = a.btot[o + j0 + u];
-    st0[u] = a.bstart[o + j0 + u];
+    const bool in = j0 + u < nb;
+    g[u] = in ? a.bagg[o + j0 + u] : TileAgg{0.0f, 0.0f, 0.0, 0.0};
+    cnt[u] = in ? a.btot[o + j0 + u] : 0u;
+    st0[u] = in ? a.bstart[o + j0 + u] : 0u;
   }
   const bool active = band_active(S);
   if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
@@ -394,35 +566,33 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     const double cR_eff = (double)(M - sJ - cJ) + cR;
     const bool first = J < 0 || J == first_ne;
     const bool last = J < 0 || J == last_ne;
-    const uint32_t *src = a.keys + row * a.cap + sJ;
+    uint32_t *kb = a.keys + row * a.cap + sJ;
+    PartInfo part;
+    part.nvalid = 0;
+    part.above = (double)cJ + cR_eff;
+    part.seed_lo = slo;
+    part.seed_hi = shi;
+    part.first = first;
+    part.last = last;
     if (cJ <= (int64_t)kWaveBucket) {
       if (w == 0) {
-        WaveTeam<kWave> wteam;
-        float s[16];
-        const int base = wteam.lane * 16;
-        const int nv = (int)min(max(cJ - base, (int64_t)0), (int64_t)16);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = e < nv ? value_of(src[base + e]) : 0.0f;
-        PartInfo part;
-        part.nvalid = nv;
-        part.above = (double)cJ + cR_eff;
-        part.seed_lo = slo;
-        part.seed_hi = shi;
-        part.first = first;
-        part.last = last;
-        const double bb = segment_solve<16>(s, nv, part, a.k, a.t, c, a.cf, wteam);
+        const double bb = cJ <= 4 * kWave ? wave_sort_solve<4>(kb, (int)cJ, part, a.k, a.t, c, a.cf)
+                                          : wave_sort_solve<16>(kb, (int)cJ, part, a.k, a.t, c, a.cf);
         if (lane == 0) sel_b = bb;
       }
     } else {
-      // a bucket of several tiles: its tile aggregates, then locate over them
+      // a bucket of several tiles: sorted in place by the workgroup, its tile
+      // aggregates, then locate over them
+      const int shift = band_shift(S, a.bbits);
+      block_radix_sort<kLocT>(kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, L.fb.rk);
       constexpr int TT = kLocT * kKpt;
       TileAgg *ta = a.tagg + row * a.max_tiles;
       for (int64_t t0 = 0; t0 < cJ; t0 += TT) {
         float s[kKpt];
-        const int nv = load_sorted_at<kLocT>(src, t0, cJ, 0u, s);
+        const int nv = load_sorted_at<kLocT>(kb, t0, cJ, 0u, s);
         tile_aggregate<kLocT>(s, nv, c, a.cf, team, ta + t0 / TT);
       }
-      const double bb = locate_sorted<kLocT>(src, cJ, 0u, slo, shi, cR_eff, first, last, ta,
+      const double bb = locate_sorted<kLocT>(kb, cJ, 0u, slo, shi, cR_eff, first, last, ta,
                                              a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, a.k, a.t, c,
                                              a.cf, team);
       if (threadIdx.x == 0) sel_b = bb;
@@ -431,9 +601,11 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     if (threadIdx.x == 0) {
       const double bb = sel_b;
       S.b = bb;
-      const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
-      S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
-      sel_fb = hit ? 0 : 1;
+      if (a.r == nullptr) {  // certification against the bracket
+        const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
+        S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
+        sel_fb = hit ? 0 : 1;
+      }
     }
   }
   __syncthreads();
@@ -446,12 +618,30 @@ int band_count_blocks(int gx, int *group) {
   return (gx + *group - 1) / *group;
 }
 
+int bucket_bits(int64_t keys) {
+  int b = 4;
+  while (b < kBandBucketBits && ((int64_t)32 << b) < keys) ++b;
+  return b;
+}
+
+int full_count_blocks(int64_t n, int64_t *chunk) {
+  int64_t nblk = (n + kTile - 1) / kTile;
+  if (nblk > kBandCountBlocks) nblk = kBandCountBlocks;
+  if (nblk < 1) nblk = 1;
+  int64_t c = (n + nblk - 1) / nblk;
+  c = (c + 3) / 4 * 4;
+  *chunk = c;
+  return (int)((n + c - 1) / c);
+}
+
 hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t s) {
   const dim3 blk((unsigned)a.nblk, (unsigned)a.rows);
+  if (a.r != nullptr) hipLaunchKernelGGL(band_minmax_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(band_scan_kernel, dim3(kBandBuckets / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
+  const int nb = 1 << a.bbits;
+  hipLaunchKernelGGL(band_scan_kernel, dim3((nb + kBT - 1) / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(band_sort_kernel, dim3(kBandBuckets / (kBT / kWave), (unsigned)a.rows), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_agg_kernel, dim3((nb + kAggGroup - 1) / kAggGroup, (unsigned)a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kLocT), 0, s, a, fb);
   return hipGetLastError();
 }

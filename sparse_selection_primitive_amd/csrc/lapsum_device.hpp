@@ -205,6 +205,35 @@ struct WaveTeam {
     sum_steps<1>(v);
     return v;
   }
+  template <int M>
+  LDEV static void sum_steps(unsigned long long &v) {
+    if constexpr (M < LANES) {
+      const uint32_t lo = pair<M>((uint32_t)v), hi = pair<M>((uint32_t)(v >> 32));
+      v += ((unsigned long long)hi << 32) | lo;
+      sum_steps<2 * M>(v);
+    }
+  }
+  LDEV unsigned long long sum(unsigned long long v) const {
+    sum_steps<1>(v);
+    return v;
+  }
+  // largest / smallest value over the team, on every lane
+  template <int M, bool MAX>
+  LDEV static void ext_steps(uint32_t &v) {
+    if constexpr (M < LANES) {
+      const uint32_t y = pair<M>(v);
+      v = MAX ? (y > v ? y : v) : (y < v ? y : v);
+      ext_steps<2 * M, MAX>(v);
+    }
+  }
+  LDEV uint32_t umax(uint32_t v) const {
+    ext_steps<1, true>(v);
+    return v;
+  }
+  LDEV uint32_t umin(uint32_t v) const {
+    ext_steps<1, false>(v);
+    return v;
+  }
   LDEV double bcast(double v, int src) const { return __shfl(v, src, LANES); }
   LDEV float bcast(float v, int src) const { return __shfl(v, src, LANES); }
   LDEV void sync() const {}

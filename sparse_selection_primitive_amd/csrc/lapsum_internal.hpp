@@ -43,21 +43,26 @@ struct SegArgs {
 };
 enum { kSegFull = 0, kSegFallback = 1 };
 
-// Bucketed band solve (bands too large for one workgroup): the band keys are
-// spread over kBandBuckets buckets by their leading bits above the band's
-// smallest key, each bucket is sorted on its own, and the threshold curve is
-// located over the bucket aggregates.
+// Bucketed sort + solve (bands too large for one workgroup, and whole rows of
+// the full-sort path): the keys are spread over up to kBandBuckets buckets by
+// their leading bits above the smallest key, each bucket is sorted on its
+// own, and the threshold curve is located over the bucket aggregates.
 constexpr int kBandBucketBits = 11;
 constexpr int kBandBuckets = 1 << kBandBucketBits;
 constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row, at most
 
 struct BandArgs {
   int rows;
-  int gx;               // filter workgroups (slots) per row
-  int group;            // slots per count/scatter workgroup
+  int gx;               // band mode: filter workgroups (slots) per row
+  int group;            // band mode: slots per count/scatter workgroup
   int nblk;             // count/scatter workgroups per row
-  const uint32_t *slots; // [rows][gx][kBandSlot] band keys per filter workgroup
-  const uint32_t *offs;  // [rows][gx + 1] slot offsets
+  int bbits;            // buckets per row = 2^bbits <= kBandBuckets (about 32 keys per bucket)
+  const uint32_t *slots; // band mode: [rows][gx][kBandSlot] band keys per filter workgroup
+  const uint32_t *offs;  // band mode: [rows][gx + 1] slot offsets
+  const float *r;       // full-row mode (non-null): the scores [rows][n], every one a key
+  int64_t n;            // full-row mode: row length
+  int64_t chunk;        // full-row mode: scores per count/scatter workgroup (a multiple of 4)
+  uint32_t *mm;         // full-row mode: [rows][nblk][2] key minimum and maximum per workgroup
   RowState *st;         // [rows]
   uint32_t *keys;       // [rows][cap] bucketed band keys, sorted inside each bucket
   uint32_t *tmp;        // [rows][cap] scratch of the large-bucket sort
@@ -98,6 +103,8 @@ hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int g
 hipError_t launch_segment(const SegArgs &a, hipStream_t s);
 hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fallback, hipStream_t s);
 int band_count_blocks(int gx, int *group);
+int full_count_blocks(int64_t n, int64_t *chunk);
+int bucket_bits(int64_t keys);
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
                         double *b, hipStream_t s);
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st,
