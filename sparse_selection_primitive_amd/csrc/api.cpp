@@ -35,7 +35,7 @@ struct Layout {
 // Offsets of the workspace regions of the large-row solver for `rows` rows
 // of stride `stride` (a multiple of kTile).
 struct SegRegions {
-  size_t A, B, hist, dtot, tagg, tpre, tsuf;
+  size_t A, B, tagg, tpre, tsuf;
   int64_t stride;
   int max_tiles;
 };
@@ -47,8 +47,6 @@ SegRegions seg_regions(Layout &L, int64_t rows, int64_t len) {
   const size_t keys = (size_t)rows * (size_t)r.stride * sizeof(uint32_t);
   r.A = L.take(keys);
   r.B = L.take(keys);
-  r.hist = L.take((size_t)rows * 256 * (size_t)r.max_tiles * sizeof(uint32_t));
-  r.dtot = L.take((size_t)rows * 256 * sizeof(uint32_t));
   r.tagg = L.take((size_t)rows * (size_t)r.max_tiles * tile_agg_bytes());
   r.tpre = L.take((size_t)rows * (size_t)r.max_tiles * pre_bytes());
   r.tsuf = L.take((size_t)rows * (size_t)r.max_tiles * suf_bytes());
@@ -263,10 +261,9 @@ lapsum_status hip_status(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LA
     if (_e != hipSuccess) return LAPSUM_ERR_HIP; \
   } while (0)
 
-SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t n, const float *r, RowState *st,
-                 double k, double t) {
+SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const float *r, RowState *st, double k,
+                 double t) {
   SegArgs a;
-  a.mode = mode;
   a.rows = (int)rows;
   a.n = n;
   a.r = r;
@@ -274,8 +271,6 @@ SegArgs seg_args(const SegRegions &R, char *ws, int mode, int64_t rows, int64_t 
   a.B = reinterpret_cast<uint32_t *>(ws + R.B);
   a.stride = R.stride;
   a.max_tiles = R.max_tiles;
-  a.hist = reinterpret_cast<uint32_t *>(ws + R.hist);
-  a.dtot = reinterpret_cast<uint32_t *>(ws + R.dtot);
   a.tagg = reinterpret_cast<TileAgg *>(ws + R.tagg);
   a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
   a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);
@@ -441,7 +436,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, offs, P.cap, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
-    const SegArgs fb = seg_args(P.full_seg, ws, kSegFallback, rows, n, r, rs, k, t);
+    const SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
     // the band kernels also run the fallback for rows whose bracket missed
     if (P.band_onchip)
       LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, fb, s));

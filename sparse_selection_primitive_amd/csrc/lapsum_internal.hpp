@@ -23,17 +23,15 @@ constexpr int kUnroll = 4;           // independent 16 B loads per thread per st
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
-// Arguments of the large-row sort + threshold-curve + root kernels.
+// Arguments of the one-workgroup full-sort fallback (a row whose bracket
+// missed, or whose band overflowed, is sorted and solved in full).
 struct SegArgs {
-  int mode;             // kSegFull (every row) or kSegFallback (rows flagged for the fallback)
   int rows;
   int64_t n;            // row length
   const float *r;       // [rows][n] scores
   uint32_t *A, *B;      // [rows][stride] key ping-pong buffers
   int64_t stride;       // per-row stride of A/B, a multiple of kTile
   int max_tiles;        // stride / kTile
-  uint32_t *hist;       // [rows][256][max_tiles] tile digit counts -> offsets
-  uint32_t *dtot;       // [rows][256] digit totals
   TileAgg *tagg;        // [rows][max_tiles] tile aggregates
   Pre *tpre;            // [rows][max_tiles] prefix before each tile
   Suf *tsuf;            // [rows][max_tiles] suffix after each tile
@@ -41,12 +39,12 @@ struct SegArgs {
   double k, t, c;       // c = log2(e)/t
   float cf;
 };
-enum { kSegFull = 0, kSegFallback = 1 };
 
-// Bucketed sort + solve (bands too large for one workgroup, and whole rows of
-// the full-sort path): the keys are spread over up to kBandBuckets buckets by
-// their leading bits above the smallest key, each bucket is sorted on its
-// own, and the threshold curve is located over the bucket aggregates.
+// Bucketed solve (bands too large for one workgroup, and whole rows of the
+// full-sort path): the keys are spread over up to kBandBuckets buckets by
+// their leading bits above the smallest key, the threshold curve is located
+// over the bucket aggregates, and only the bucket that holds the root is
+// sorted.
 constexpr int kBandBucketBits = 11;
 constexpr int kBandBuckets = 1 << kBandBucketBits;
 constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row, at most
@@ -64,7 +62,7 @@ struct BandArgs {
   int64_t chunk;        // full-row mode: scores per count/scatter workgroup (a multiple of 4)
   uint32_t *mm;         // full-row mode: [rows][nblk][2] key minimum and maximum per workgroup
   RowState *st;         // [rows]
-  uint32_t *keys;       // [rows][cap] bucketed band keys, sorted inside each bucket
+  uint32_t *keys;       // [rows][cap] bucketed band keys (the balancing bucket sorted by the locate)
   uint32_t *tmp;        // [rows][cap] scratch of the large-bucket sort
   uint32_t *hist;       // [rows][nblk][kBandBuckets] counts -> offsets inside buckets
   uint32_t *btot;       // [rows][kBandBuckets] bucket sizes
@@ -100,7 +98,6 @@ size_t band_slot_bytes(int64_t rows, int grid_x);
 size_t band_offs_bytes(int64_t rows, int grid_x);
 hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
                               RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
-hipError_t launch_segment(const SegArgs &a, hipStream_t s);
 hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fallback, hipStream_t s);
 int band_count_blocks(int gx, int *group);
 int full_count_blocks(int64_t n, int64_t *chunk);

@@ -1,8 +1,7 @@
-// Device routines of the large-row full-sort solver shared by the
-// multi-launch kernels (segment.hip), the one-workgroup fallback, the on-chip
-// band kernel (onchip.hip) and the bucketed band solve (band.hip): tile
-// loads, stable scatter of a tile, anchored aggregates of sorted runs, and
-// locate + closed-form root over a sorted range.
+// Device routines of the full-sort solver shared by the one-workgroup
+// fallback, the on-chip band kernel (onchip.hip) and the bucketed band solve
+// (band.hip): tile loads, stable scatter of a tile, anchored aggregates of
+// sorted runs, and locate + closed-form root over a sorted range.
 // Method: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
 // section 2.2, full-sort solver.
 #pragma once
@@ -36,10 +35,7 @@ union SegLds {
 };
 
 // ------------------------------------------------------------- row helpers
-LDEV bool seg_active(const SegArgs &a, int row) {
-  if (a.mode == kSegFull) return true;
-  return (a.st[row].flags & LAPSUM_FLAG_FALLBACK) != 0;
-}
+LDEV bool seg_active(const SegArgs &a, int row) { return (a.st[row].flags & LAPSUM_FLAG_FALLBACK) != 0; }
 LDEV int64_t seg_len(const SegArgs &a, int row) { return seg_active(a, row) ? a.n : 0; }
 // four 8-bit digit passes A -> B -> A -> B: the sorted keys end in B
 LDEV const uint32_t *seg_final(const SegArgs &a) { return a.B; }
