@@ -458,17 +458,22 @@ LDEV double wave_sort_solve(const uint32_t *kb, int cnt, PartInfo part, double k
 }
 
 // ---------------------------------------------------------------- locate
-// One workgroup of kLocT threads per row, two buckets per thread: a
-// workgroup scan of the bucket aggregates between the tail seeds, the
-// threshold curve at the bucket ends, the balancing bucket, and the root
-// inside it.  Only that bucket is sorted: by one wave in registers when it
-// holds at most 1024 keys, else by the whole workgroup (radix passes in
-// place, then tile aggregates).  A row whose root falls outside its bracket is then
-// sorted and solved in full by the same workgroup (the deterministic
-// fallback), so no separate launch is needed.
+// One workgroup of kLocT threads per row.  Its first kLocScanT threads
+// (two waves per SIMD) search the buckets, kLocPer consecutive buckets each:
+// a scan of the bucket aggregates between the tail seeds (DPP inside waves,
+// the wave totals through LDS), the threshold curve at the bucket ends and
+// the balancing bucket.  Only that bucket is sorted: by one wave in
+// registers when it holds at most 1024 keys, else by the whole workgroup
+// (radix passes in place, then tile aggregates), and the root is taken
+// inside it.  A row whose root falls outside its bracket is then sorted and
+// solved in full by the same workgroup (the deterministic fallback), so no
+// separate launch is needed.
 constexpr int kLocT = 1024;
-constexpr int kLocPer = kBandBuckets / kLocT;
-static_assert(kLocPer == 2, "two buckets per locate thread");
+constexpr int kLocScanT = 512;                     // threads of the bucket search
+constexpr int kLocScanW = kLocScanT / kWave;
+constexpr int kLocPer = kBandBuckets / kLocScanT;  // buckets per search thread
+static_assert(kLocPer * kLocScanT == kBandBuckets, "every bucket has a search thread");
+static_assert(kLocScanW <= 16, "wave totals are scanned inside one DPP row");
 
 union BandLocLds {
   BlockTeamLds<kLocT, 1> team;
@@ -477,7 +482,9 @@ union BandLocLds {
 
 __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs fb) {
   __shared__ BandLocLds L;
-  __shared__ int red[3][kLocT / kWave];
+  __shared__ int red[3][kLocScanW];
+  __shared__ float tw_a[2][kLocScanW];
+  __shared__ double tw_s[2][kLocScanW];
   __shared__ float sel_pa, sel_sa;
   __shared__ double sel_ps, sel_ss, sel_b;
   __shared__ uint32_t sel_c, sel_st;
@@ -486,6 +493,9 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   RowState &S = a.st[row];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
+  // The bucket search runs on the first kLocScanW waves only (two per SIMD):
+  // each of their threads owns kLocPer consecutive buckets.
+  const bool searcher = threadIdx.x < kLocScanT;
   const int j0 = threadIdx.x * kLocPer;
   // this thread's bucket records (issued before the row state is examined)
   TileAgg g[kLocPer];
@@ -493,7 +503,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   const int nb = 1 << a.bbits;
 #pragma unroll
   for (int u = 0; u < kLocPer; ++u) {
-    const bool in = j0 + u < nb;
+    const bool in = searcher && j0 + u < nb;
     g[u] = in ? a.bagg[o + j0 + u] : TileAgg{0.0f, 0.0f, 0.0, 0.0};
     cnt[u] = in ? a.btot[o + j0 + u] : 0u;
     st0[u] = in ? a.bstart[o + j0 + u] : 0u;
@@ -507,42 +517,72 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
     const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
     const double cR = (double)S.count_hi;
-    const Pre p0{g[0].aP, g[0].sP}, p1{g[1].aP, g[1].sP};
-    const Suf q0{g[0].aS, g[0].sS}, q1{g[1].aS, g[1].sS};
-    const Pre ex_p = join(seed_lo, team.excl_scan(join(p0, p1, c), c), c);
-    const Suf ex_s = join(team.excl_scan(join(q0, q1, c), c), seed_hi, c);
-    const Pre before[kLocPer] = {ex_p, join(ex_p, p0, c)};
-    const Suf after[kLocPer] = {join(q1, ex_s, c), ex_s};
-    // threshold curve at the last knot of every non-empty bucket
-    int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
+    // this thread's buckets joined, then exclusive scans over the search
+    // threads: inside each wave, then across the search waves
+    Pre tp{0.0f, 0.0}, xp{0.0f, 0.0};
+    Suf ts{0.0f, 0.0}, xs{0.0f, 0.0};
 #pragma unroll
-    for (int u = 0; u < kLocPer; ++u) {
-      if (cnt[u] > 0u) {
-        const int j = j0 + u;
-        const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
-        const Suf sa = after[u];
-        const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
-        const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
-        const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
-        if (gv < a.k) first_lt = min(first_lt, j);
-        first_ne = min(first_ne, j);
-        last_ne = max(last_ne, j);
+    for (int u = 0; u < kLocPer; ++u) tp = join(tp, Pre{g[u].aP, g[u].sP}, c);
+#pragma unroll
+    for (int u = kLocPer - 1; u >= 0; --u) ts = join(Suf{g[u].aS, g[u].sS}, ts, c);
+    if (searcher) {
+      const Pre ip = wave_scan(tp, c, &xp);
+      const Suf is = wave_scan(ts, c, &xs);
+      if (lane == kWave - 1) {
+        tw_a[0][w] = ip.a;
+        tw_s[0][w] = ip.s;
+      }
+      if (lane == 0) {
+        tw_a[1][w] = is.a;
+        tw_s[1][w] = is.s;
       }
     }
+    __syncthreads();
+    int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
+    Pre before[kLocPer];
+    Suf after[kLocPer];
+    if (searcher) {
+      Pre twp = lane < kLocScanW ? Pre{tw_a[0][lane], tw_s[0][lane]} : Pre{0.0f, 0.0};
+      Suf tws = lane < kLocScanW ? Suf{tw_a[1][lane], tw_s[1][lane]} : Suf{0.0f, 0.0};
+      row_pre_steps<1>(twp, c);
+      row_suf_steps<1>(tws, c);
+      const int wb = __builtin_amdgcn_readfirstlane(w - 1), wa = __builtin_amdgcn_readfirstlane(w + 1);
+      const Pre wp = w == 0 ? Pre{0.0f, 0.0} : Pre{read_lane(twp.a, wb), read_lane(twp.s, wb)};
+      const Suf ws = w == kLocScanW - 1 ? Suf{0.0f, 0.0} : Suf{read_lane(tws.a, wa), read_lane(tws.s, wa)};
+      // everything before / after each bucket of this thread
+      before[0] = join(seed_lo, join(wp, xp, c), c);
+      after[kLocPer - 1] = join(join(xs, ws, c), seed_hi, c);
 #pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      first_lt = min(first_lt, __shfl_xor(first_lt, m, kWave));
-      first_ne = min(first_ne, __shfl_xor(first_ne, m, kWave));
-      last_ne = max(last_ne, __shfl_xor(last_ne, m, kWave));
-    }
-    if (lane == 0) {
-      red[0][w] = first_lt;
-      red[1][w] = first_ne;
-      red[2][w] = last_ne;
+      for (int u = 1; u < kLocPer; ++u) before[u] = join(before[u - 1], Pre{g[u - 1].aP, g[u - 1].sP}, c);
+#pragma unroll
+      for (int u = kLocPer - 2; u >= 0; --u) after[u] = join(Suf{g[u + 1].aS, g[u + 1].sS}, after[u + 1], c);
+      // threshold curve at the last knot of every non-empty bucket
+#pragma unroll
+      for (int u = 0; u < kLocPer; ++u) {
+        if (cnt[u] > 0u) {
+          const int j = j0 + u;
+          const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
+          const Suf sa = after[u];
+          const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
+          const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
+          const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
+          if (gv < a.k) first_lt = min(first_lt, j);
+          first_ne = min(first_ne, j);
+          last_ne = max(last_ne, j);
+        }
+      }
+      first_lt = wave_reduce(first_lt, [](int x, int y) { return min(x, y); });
+      first_ne = wave_reduce(first_ne, [](int x, int y) { return min(x, y); });
+      last_ne = wave_reduce(last_ne, [](int x, int y) { return max(x, y); });
+      if (lane == 0) {
+        red[0][w] = first_lt;
+        red[1][w] = first_ne;
+        red[2][w] = last_ne;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kLocT / kWave; ++i) {
+    for (int i = 0; i < kLocScanW; ++i) {
       first_lt = min(first_lt, red[0][i]);
       first_ne = min(first_ne, red[1][i]);
       last_ne = max(last_ne, red[2][i]);
@@ -551,12 +591,17 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     const int J = first_lt != INT_MAX ? first_lt : last_ne;  // -1: empty band
     if (J >= 0 && (int)threadIdx.x == J / kLocPer) {
       const int u = J % kLocPer;
-      sel_pa = u == 0 ? before[0].a : before[1].a;
-      sel_ps = u == 0 ? before[0].s : before[1].s;
-      sel_sa = u == 0 ? after[0].a : after[1].a;
-      sel_ss = u == 0 ? after[0].s : after[1].s;
-      sel_c = u == 0 ? cnt[0] : cnt[1];
-      sel_st = u == 0 ? st0[0] : st0[1];
+#pragma unroll
+      for (int q = 0; q < kLocPer; ++q) {
+        if (q == u) {
+          sel_pa = before[q].a;
+          sel_ps = before[q].s;
+          sel_sa = after[q].a;
+          sel_ss = after[q].s;
+          sel_c = cnt[q];
+          sel_st = st0[q];
+        }
+      }
     }
     __syncthreads();
     const int64_t cJ = J >= 0 ? (int64_t)sel_c : 0;

@@ -574,7 +574,7 @@ hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t r
 // --------------------------------------------------------- stream & filter
 struct FilterPartial {
   double sl, sr;
-  unsigned long long cl;      // scores below a_L
+  unsigned long long cnl;     // scores at or above a_L
   uint32_t cnt;       // band keys this block found (may exceed kBandSlot)
   uint32_t kmn, kmx;  // key range of those band keys
   uint32_t pad;
@@ -584,38 +584,44 @@ LDEV uint32_t mbcnt64(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// One coalesced pass over the row.  Band keys go to this block's own slot
-// (positions reserved by an LDS counter, one LDS atomic per wave and group
-// of elements that holds any); the tail sums and the band key range go to
-// the block's partial, the count below a_L is taken from wave ballots.  No
-// global atomics: the per-row finalize adds the partials in a fixed order,
-// derives the count above a_R and turns the slot counts into offsets.
+// One coalesced pass over the row.  A score below a_L (the bulk of the row
+// when k is small) costs one compare, its lower-tail term and a masked add.
+// Scores at or above a_L are rare: a wave takes a uniform branch only for a
+// group of elements that holds one, counts them from the ballot, adds the
+// upper-tail terms of those at or above a_R and appends the band keys to
+// this block's own slot (positions reserved by an LDS counter, one LDS atomic
+// per wave and group).  The tail sums, the count at or above a_L and the band
+// key range go to the block's partial.  No global atomics: the per-row
+// finalize adds the partials in a fixed order, derives the counts below a_L
+// and above a_R and turns the slot counts into offsets.
 template <bool CHECK>
 LDEV void filter_items(const float (&x)[4 * kUnroll], const bool (&ok)[4 * kUnroll], float aL, float aR, float cf,
-                       double &sl, double &sr, unsigned long long &cl, uint32_t &kmn, uint32_t &kmx,
+                       double &sl, double &sr, unsigned long long &cnl, uint32_t &kmn, uint32_t &kmx,
                        uint32_t *slot, uint32_t &lcount) {
   float fl = 0.0f, fr = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4 * kUnroll; ++q) {
     const bool valid = !CHECK || ok[q];
     const bool lo = valid && x[q] < aL;
-    const bool hi = valid && x[q] >= aR;
-    const float z = lo ? (x[q] - aL) : (aR - x[q]);  // <= 0 whenever it is used
-    const float w = __builtin_amdgcn_exp2f(z * cf);
+    const float w = __builtin_amdgcn_exp2f((x[q] - aL) * cf);  // used only below a_L, where it is <= 1
     fl += lo ? w : 0.0f;
-    fr += hi ? w : 0.0f;
-    cl += (unsigned long long)__popcll(__ballot(lo));
-    const unsigned long long mq = __ballot(valid && !lo && !hi);
-    if (mq) {  // wave-uniform: some lane holds a band key at position q
-      uint32_t base = 0u;
-      if (lane_id() == __ffsll((long long)mq) - 1) base = atomicAdd(&lcount, (uint32_t)__popcll(mq));
-      base = __shfl(base, __ffsll((long long)mq) - 1, kWave);
-      if ((mq >> lane_id()) & 1ull) {
-        const uint32_t pos = base + mbcnt64(mq);
-        const uint32_t kk = key_of(x[q]);
-        if (pos < (uint32_t)kBandSlot) slot[pos] = kk;  // beyond the slot: counted, row falls back
-        kmn = min(kmn, kk);
-        kmx = max(kmx, kk);
+    const unsigned long long nl = __ballot(valid && !lo);
+    if (nl) {  // wave-uniform: some lane holds a score at or above a_L at position q
+      cnl += (unsigned long long)__popcll(nl);
+      const bool hi = valid && x[q] >= aR;
+      if (hi) fr += __builtin_amdgcn_exp2f((aR - x[q]) * cf);
+      const unsigned long long mq = nl & ~__ballot(hi);
+      if (mq) {  // band keys
+        uint32_t base = 0u;
+        if (lane_id() == __ffsll((long long)mq) - 1) base = atomicAdd(&lcount, (uint32_t)__popcll(mq));
+        base = __shfl(base, __ffsll((long long)mq) - 1, kWave);
+        if ((mq >> lane_id()) & 1ull) {
+          const uint32_t pos = base + mbcnt64(mq);
+          const uint32_t kk = key_of(x[q]);
+          if (pos < (uint32_t)kBandSlot) slot[pos] = kk;  // beyond the slot: counted, row falls back
+          kmn = min(kmn, kk);
+          kmx = max(kmx, kk);
+        }
       }
     }
   }
@@ -641,7 +647,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   uint32_t *slot = slots + ((int64_t)row * gx + blockIdx.x) * kBandSlot;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
   double sl = 0.0, sr = 0.0;
-  unsigned long long cl = 0;  // wave-uniform
+  unsigned long long cnl = 0;  // wave-uniform
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 
   typedef float f4 __attribute__((ext_vector_type(4)));
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
         x[4 * u + 2] = v[u].z;
         x[4 * u + 3] = v[u].w;
       }
-      filter_items<false>(x, ok, aL, aR, cf, sl, sr, cl, kmn, kmx, slot, lcount);
+      filter_items<false>(x, ok, aL, aR, cf, sl, sr, cnl, kmn, kmx, slot, lcount);
     }
   }
   // the rest (and every item of the scalar path), with bounds checks
@@ -691,10 +697,10 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
       ok[4 * u + 2] = in && vec;
       ok[4 * u + 3] = in && vec;
     }
-    filter_items<true>(x, ok, aL, aR, cf, sl, sr, cl, kmn, kmx, slot, lcount);
+    filter_items<true>(x, ok, aL, aR, cf, sl, sr, cnl, kmn, kmx, slot, lcount);
   }
 
-  // block reduction (fixed order); cl is already per wave
+  // block reduction (fixed order); cnl is already per wave
 #pragma unroll
   for (int msk = 1; msk < kWave; msk <<= 1) {
     sl += __shfl_xor(sl, msk, kWave);
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   if ((threadIdx.x & (kWave - 1)) == 0) {
     lds_d[2 * w] = sl;
     lds_d[2 * w + 1] = sr;
-    lds_c[w] = cl;
+    lds_c[w] = cnl;
     lds_k[2 * w] = kmn;
     lds_k[2 * w + 1] = kmx;
   }
@@ -715,13 +721,13 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
     FilterPartial fp;
     fp.sl = 0.0;
     fp.sr = 0.0;
-    fp.cl = 0;
+    fp.cnl = 0;
     fp.kmn = 0xFFFFFFFFu;
     fp.kmx = 0u;
     for (int i = 0; i < kStreamThreads / kWave; ++i) {
       fp.sl += lds_d[2 * i];
       fp.sr += lds_d[2 * i + 1];
-      fp.cl += lds_c[i];
+      fp.cnl += lds_c[i];
       fp.kmn = min(fp.kmn, lds_k[2 * i]);
       fp.kmx = max(fp.kmx, lds_k[2 * i + 1]);
     }
@@ -758,7 +764,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
       const FilterPartial fp = vp[j];
       a += fp.sl;
       b += fp.sr;
-      c0 += fp.cl;
+      c0 += fp.cnl;
       mn = min(mn, fp.kmn);
       mx = max(mx, fp.kmx);
       csum += fp.cnt;
@@ -822,8 +828,9 @@ __global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const F
     RowState &S = st[row];
     S.tail_lo = ta;
     S.tail_hi = tb;
-    S.count_lo = tc0;
-    S.count_hi = (unsigned long long)n - tc0 - total;  // every score is below, inside or above
+    // every score is below a_L, inside the band or at or above a_R
+    S.count_lo = (unsigned long long)n - tc0;
+    S.count_hi = tc0 - total;
     S.band = total;
     S.kmin = tmn;
     S.kmax = tmx;

@@ -142,6 +142,105 @@ LDEV uint32_t xor_lanes(uint32_t v) {
 
 LDEV int lane_id() { return (int)__lane_id(); }
 
+// ------------------------------------------------- whole-wave helpers
+// A 64-lane wave is four DPP rows of 16 lanes.  Butterflies and scans run
+// inside the rows on DPP moves; the four row results are then read once each
+// with v_readlane (uniform values) and combined on every lane, so no step
+// of a wave-wide sum, extreme or scan goes through LDS.
+LDEV uint32_t read_lane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+LDEV float read_lane(float v, int l) { return __uint_as_float(read_lane(__float_as_uint(v), l)); }
+LDEV int read_lane(int v, int l) { return (int)read_lane((uint32_t)v, l); }
+LDEV unsigned long long read_lane(unsigned long long v, int l) {
+  return ((unsigned long long)read_lane((uint32_t)(v >> 32), l) << 32) | read_lane((uint32_t)v, l);
+}
+LDEV double read_lane(double v, int l) {
+  return __longlong_as_double((long long)read_lane((unsigned long long)__double_as_longlong(v), l));
+}
+template <int CTRL>
+LDEV unsigned long long dpp64(unsigned long long v) {
+  return ((unsigned long long)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+LDEV double dpp64(double v) {
+  return __longlong_as_double((long long)dpp64<CTRL>((unsigned long long)__double_as_longlong(v)));
+}
+// value of lane (lane ^ M) of the same row, M = 1, 2, 4, 8 (a butterfly
+// pairing: any pairing of the halves serves a commutative reduction)
+template <int M>
+LDEV uint32_t row_pair(uint32_t v) {
+  return xor_lanes<M == 4 ? 7 : (M == 8 ? 15 : M)>(v);
+}
+template <int M>
+LDEV unsigned long long row_pair(unsigned long long v) {
+  return ((unsigned long long)row_pair<M>((uint32_t)(v >> 32)) << 32) | row_pair<M>((uint32_t)v);
+}
+template <int M>
+LDEV double row_pair(double v) {
+  return __longlong_as_double((long long)row_pair<M>((unsigned long long)__double_as_longlong(v)));
+}
+template <int M>
+LDEV int row_pair(int v) {
+  return (int)row_pair<M>((uint32_t)v);
+}
+// reduction over the whole wave (op commutative and associative), on every lane
+template <class T, class Op>
+LDEV T wave_reduce(T v, Op op) {
+  v = op(v, row_pair<1>(v));
+  v = op(v, row_pair<2>(v));
+  v = op(v, row_pair<4>(v));
+  v = op(v, row_pair<8>(v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
+template <int CTRL>
+LDEV Pre dpp_pre(Pre x) {
+  return Pre{__uint_as_float(dpp<CTRL>(__float_as_uint(x.a))), dpp64<CTRL>(x.s)};
+}
+template <int CTRL>
+LDEV Suf dpp_suf(Suf x) {
+  return Suf{__uint_as_float(dpp<CTRL>(__float_as_uint(x.a))), dpp64<CTRL>(x.s)};
+}
+// inclusive scans inside each row: a lane whose source lies before (after)
+// its row start (end) reads zeros, i.e. an empty range
+template <int OFF>
+LDEV void row_pre_steps(Pre &inc, double c) {
+  if constexpr (OFF < 16) {
+    inc = join(dpp_pre<0x110 + OFF>(inc), inc, c);  // row_shr:OFF
+    row_pre_steps<2 * OFF>(inc, c);
+  }
+}
+template <int OFF>
+LDEV void row_suf_steps(Suf &inc, double c) {
+  if constexpr (OFF < 16) {
+    inc = join(inc, dpp_suf<0x100 + OFF>(inc), c);  // row_shl:OFF
+    row_suf_steps<2 * OFF>(inc, c);
+  }
+}
+// P-type scan over the wave: returns the inclusive value, *ex the exclusive
+LDEV Pre wave_scan(Pre x, double c, Pre *ex) {
+  const int row = lane_id() >> 4;
+  Pre inc = x;
+  row_pre_steps<1>(inc, c);
+  const Pre t0{read_lane(inc.a, 15), read_lane(inc.s, 15)};
+  const Pre t01 = join(t0, Pre{read_lane(inc.a, 31), read_lane(inc.s, 31)}, c);
+  const Pre t012 = join(t01, Pre{read_lane(inc.a, 47), read_lane(inc.s, 47)}, c);
+  const Pre before = row == 0 ? Pre{0.0f, 0.0} : (row == 1 ? t0 : (row == 2 ? t01 : t012));
+  *ex = join(before, dpp_pre<0x111>(inc), c);
+  return join(before, inc, c);
+}
+// S-type scan over the wave (from the last lane down)
+LDEV Suf wave_scan(Suf x, double c, Suf *ex) {
+  const int row = lane_id() >> 4;
+  Suf inc = x;
+  row_suf_steps<1>(inc, c);
+  const Suf t3{read_lane(inc.a, 48), read_lane(inc.s, 48)};
+  const Suf t23 = join(Suf{read_lane(inc.a, 32), read_lane(inc.s, 32)}, t3, c);
+  const Suf t123 = join(Suf{read_lane(inc.a, 16), read_lane(inc.s, 16)}, t23, c);
+  const Suf after = row == 3 ? Suf{0.0f, 0.0} : (row == 2 ? t3 : (row == 1 ? t23 : t123));
+  *ex = join(dpp_suf<0x101>(inc), after, c);
+  return join(inc, after, c);
+}
+
 // ------------------------------------------------------------- teams
 // A team owns one segment of sorted keys in a blocked layout: team lane l
 // holds elements [l*E, l*E + E).  A WaveTeam is LANES (<= 64) consecutive
@@ -198,10 +297,12 @@ struct WaveTeam {
     }
   }
   LDEV int sum(int v) const {
+    if constexpr (LANES == kWave) return wave_reduce(v, [](int x, int y) { return x + y; });
     sum_steps<1>(v);
     return v;
   }
   LDEV double sum(double v) const {
+    if constexpr (LANES == kWave) return wave_reduce(v, [](double x, double y) { return x + y; });
     sum_steps<1>(v);
     return v;
   }
@@ -214,6 +315,8 @@ struct WaveTeam {
     }
   }
   LDEV unsigned long long sum(unsigned long long v) const {
+    if constexpr (LANES == kWave)
+      return wave_reduce(v, [](unsigned long long x, unsigned long long y) { return x + y; });
     sum_steps<1>(v);
     return v;
   }
@@ -227,15 +330,24 @@ struct WaveTeam {
     }
   }
   LDEV uint32_t umax(uint32_t v) const {
+    if constexpr (LANES == kWave) return wave_reduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
     ext_steps<1, true>(v);
     return v;
   }
   LDEV uint32_t umin(uint32_t v) const {
+    if constexpr (LANES == kWave) return wave_reduce(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
     ext_steps<1, false>(v);
     return v;
   }
-  LDEV double bcast(double v, int src) const { return __shfl(v, src, LANES); }
-  LDEV float bcast(float v, int src) const { return __shfl(v, src, LANES); }
+  // value of team lane src; a whole wave requires src to be the same on every lane
+  LDEV double bcast(double v, int src) const {
+    if constexpr (LANES == kWave) return read_lane(v, __builtin_amdgcn_readfirstlane(src));
+    return __shfl(v, src, LANES);
+  }
+  LDEV float bcast(float v, int src) const {
+    if constexpr (LANES == kWave) return read_lane(v, __builtin_amdgcn_readfirstlane(src));
+    return __shfl(v, src, LANES);
+  }
   LDEV void sync() const {}
 
   template <int OFF>
@@ -271,6 +383,11 @@ struct WaveTeam {
     }
   }
   LDEV Pre excl_scan(Pre x, double c) const {
+    if constexpr (LANES == kWave) {
+      Pre ex;
+      wave_scan(x, c, &ex);
+      return ex;
+    }
     Pre inc = x;
     pre_steps<1>(inc, c);
     Pre ex{__uint_as_float(up<1>(__float_as_uint(inc.a))), move64<1>(inc.s, [](uint32_t v) { return up<1>(v); })};
@@ -278,6 +395,11 @@ struct WaveTeam {
     return ex;
   }
   LDEV Suf excl_scan(Suf x, double c) const {
+    if constexpr (LANES == kWave) {
+      Suf ex;
+      wave_scan(x, c, &ex);
+      return ex;
+    }
     Suf inc = x;
     suf_steps<1>(inc, c);
     Suf ex{__uint_as_float(down<1>(__float_as_uint(inc.a))), move64<1>(inc.s, [](uint32_t v) { return down<1>(v); })};
@@ -356,44 +478,41 @@ struct BlockTeam {
   }
   LDEV void sync() const { __syncthreads(); }
 
+  // Scans: each wave scans its lanes (DPP + v_readlane), the wave totals go
+  // through LDS, and every wave scans the kWaves totals inside one DPP row
+  // to get what lies before (after) it.
   LDEV Pre excl_scan(Pre x, double c) const {
+    static_assert(kWaves <= 16, "wave totals are scanned inside one DPP row");
     const int wl = lane & (kWave - 1), w = lane / kWave;
-    Pre inc = x;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      Pre y{__shfl_up(inc.a, off, kWave), __shfl_up(inc.s, off, kWave)};
-      if (wl >= off) inc = join(y, inc, c);
-    }
+    Pre ex;
+    const Pre inc = wave_scan(x, c, &ex);
     __syncthreads();
     if (wl == kWave - 1) {
       lds->wa[w] = inc.a;
       lds->ws[w] = inc.s;
     }
     __syncthreads();
-    Pre wp{0.0f, 0.0};
-    for (int i = 0; i < w; ++i) wp = join(wp, Pre{lds->wa[i], lds->ws[i]}, c);
-    Pre ex{__shfl_up(inc.a, 1, kWave), __shfl_up(inc.s, 1, kWave)};
-    if (wl == 0) ex.s = 0.0;
+    Pre tw = wl < kWaves ? Pre{lds->wa[wl], lds->ws[wl]} : Pre{0.0f, 0.0};
+    row_pre_steps<1>(tw, c);
+    const int src = __builtin_amdgcn_readfirstlane(w - 1);  // the same on every lane of the wave
+    const Pre wp = w == 0 ? Pre{0.0f, 0.0} : Pre{read_lane(tw.a, src), read_lane(tw.s, src)};
     return join(wp, ex, c);
   }
   LDEV Suf excl_scan(Suf x, double c) const {
+    static_assert(kWaves <= 16, "wave totals are scanned inside one DPP row");
     const int wl = lane & (kWave - 1), w = lane / kWave;
-    Suf inc = x;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      Suf y{__shfl_down(inc.a, off, kWave), __shfl_down(inc.s, off, kWave)};
-      if (wl + off < kWave) inc = join(inc, y, c);
-    }
+    Suf ex;
+    const Suf inc = wave_scan(x, c, &ex);
     __syncthreads();
     if (wl == 0) {
       lds->wa[w] = inc.a;
       lds->ws[w] = inc.s;
     }
     __syncthreads();
-    Suf ws{0.0f, 0.0};
-    for (int i = kWaves - 1; i > w; --i) ws = join(Suf{lds->wa[i], lds->ws[i]}, ws, c);
-    Suf ex{__shfl_down(inc.a, 1, kWave), __shfl_down(inc.s, 1, kWave)};
-    if (wl == kWave - 1) ex.s = 0.0;
+    Suf tw = wl < kWaves ? Suf{lds->wa[wl], lds->ws[wl]} : Suf{0.0f, 0.0};
+    row_suf_steps<1>(tw, c);
+    const int src = __builtin_amdgcn_readfirstlane(w + 1);
+    const Suf ws = w == kWaves - 1 ? Suf{0.0f, 0.0} : Suf{read_lane(tw.a, src), read_lane(tw.s, src)};
     return join(ex, ws, c);
   }
 };
