@@ -98,8 +98,8 @@ enum {
     LAPSUM_STAGE_SAMPLE = 2,     /* kernel-noised sample */
     LAPSUM_STAGE_SELECT = 3,     /* order statistics -> bracket */
     LAPSUM_STAGE_FILTER = 4,     /* streaming tail sums + band compaction */
-    LAPSUM_STAGE_BAND = 5,       /* band sort + scan + root + certification */
-    LAPSUM_STAGE_FULLSORT = 6,   /* full-sort solve (full-sort path or fallback) */
+    LAPSUM_STAGE_BAND = 5,       /* band solve + certification (+ fallback of a missed row) */
+    LAPSUM_STAGE_FULLSORT = 6,   /* full-sort solve of whole rows (full-sort path) */
     LAPSUM_STAGE_APPLY = 7,      /* streaming Laplace-CDF apply */
     LAPSUM_STAGE_ONCHIP_BWD = 8, /* fused on-chip backward */
     LAPSUM_STAGE_BWD_REDUCE = 9, /* streaming backward reductions (D, G) */
