@@ -157,11 +157,18 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
   const float *gg = g + row * n;
   const float *pp = p + row * n;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  // Every product g q and every sum in fp64 (g and q are fp32, so g q is
+  // exact): when one score holds nearly all of the d-weight, dk is within a
+  // few 1e-4 of that score's g, and dr = d (g - dk) keeps the relative
+  // accuracy of dk only if dk itself is accurate far below fp32 rounding.
   double D = 0.0, G = 0.0;
   if ((n & 3) == 0 && aligned16(g) && aligned16(p)) {
     const int64_t n4 = n >> 2;
     const f4 *g4 = reinterpret_cast<const f4 *>(gg);
     const f4 *p4 = reinterpret_cast<const f4 *>(pp);
+    double Du[kUnroll], Gu[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Du[u] = Gu[u] = 0.0;
     for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < n4;
          i0 += stride * kUnroll) {
       f4 pv[kUnroll], gv[kUnroll];
@@ -174,11 +181,16 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const float q0 = fminf(pv[u].x, 1.0f - pv[u].x), q1 = fminf(pv[u].y, 1.0f - pv[u].y);
-        const float q2 = fminf(pv[u].z, 1.0f - pv[u].z), q3 = fminf(pv[u].w, 1.0f - pv[u].w);
-        D += (double)((q0 + q1) + (q2 + q3));
-        G += (double)((gv[u].x * q0 + gv[u].y * q1) + (gv[u].z * q2 + gv[u].w * q3));
+        const double q0 = fminf(pv[u].x, 1.0f - pv[u].x), q1 = fminf(pv[u].y, 1.0f - pv[u].y);
+        const double q2 = fminf(pv[u].z, 1.0f - pv[u].z), q3 = fminf(pv[u].w, 1.0f - pv[u].w);
+        Du[u] += (q0 + q1) + (q2 + q3);
+        Gu[u] += ((double)gv[u].x * q0 + (double)gv[u].y * q1) + ((double)gv[u].z * q2 + (double)gv[u].w * q3);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      D += Du[u];
+      G += Gu[u];
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride) {

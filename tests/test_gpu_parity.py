@@ -169,6 +169,54 @@ def test_fullsort_ragged(L, O, n, rows):
     full_check(f"fullsort n={n}", L, O, r, g, k, 0.05, path="fullsort")
 
 
+def test_fullsort_auto_boundary(L, O):
+    """n = 2^20, the largest row the automatic dispatch sends to the
+    full-sort path (2048 buckets of about 512 keys)."""
+    n = 1 << 20
+    assert L.plan(1, n, 1000.0, 0.01)["path"] == L.PATH_FULLSORT
+    assert L.plan(1, n + 1, 1000.0, 0.01)["path"] == L.PATH_BRACKET
+    g0 = np.random.Generator(np.random.PCG64(2101))
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    full_check("fullsort n=2^20", L, O, r, g, 1000.0, 0.01)
+
+
+def test_fullsort_tight_cluster(L, O):
+    """Most of each row in a cluster far narrower than the bucket width the
+    outliers force: the balancing bucket holds tens of thousands of keys, so
+    its sums take whole waves and its sort the workgroup radix passes."""
+    g0 = np.random.Generator(np.random.PCG64(2201))
+    rows, n = 2, 65536
+    r = (100.0 * g0.standard_normal((rows, n))).astype(np.float32)
+    for i in range(rows):
+        idx = g0.choice(n, size=60000, replace=False)
+        r[i, idx] = (1.0 + 1e-4 * g0.standard_normal(60000)).astype(np.float32)
+    g = g0.standard_normal((rows, n)).astype(np.float32)
+    full_check("fullsort tight cluster", L, O, r, g, 30000.5, 1e-3, path="fullsort")
+
+
+@pytest.mark.parametrize("k", [1e-3, 0.5, 9999.5])
+def test_fullsort_end_budgets(L, O, k):
+    """Budgets near 0 and near n: the balancing bucket is the first or the
+    last non-empty one."""
+    g0 = np.random.Generator(np.random.PCG64(2301))
+    n = 10000
+    r = g0.standard_normal((2, n)).astype(np.float32)
+    g = g0.standard_normal((2, n)).astype(np.float32)
+    full_check(f"fullsort end budget k={k}", L, O, r, g, k, 0.05, path="fullsort")
+
+
+def test_fullsort_constant_rows(L, O):
+    """Rows of one value (every bucket key equal) and a row of two values:
+    the aggregates come from the counts alone, b sits at the value."""
+    n = 20000
+    r = np.full((3, n), 0.25, dtype=np.float32)
+    r[1, :] = -3.0
+    r[2, : n // 2] = 1.0
+    r[2, n // 2:] = 2.0
+    full_check("fullsort constant rows", L, O, r, None, 1234.5, 0.1, path="fullsort")
+
+
 # ---------------------------------------------------------- bracketing path
 def check_bracket_stats(name, L, O, r, k, t, stats, seed, m_log2=None, delta=1e-6):
     from oracle import bracket as ob
