@@ -288,6 +288,21 @@ def test_bracket_select_paths(L, O, kind, k_frac, t, m_log2):
     check_bracket_stats(kind, L, O, r, k, t, res["stats"], seed=0, m_log2=m_log2 or None)
 
 
+@pytest.mark.parametrize("n,k", [(300_000, 0.5), (300_000, 300_000 - 0.5), (2_000_000, 3.0),
+                                 (2_000_000, 2_000_000 - 1e-3)])
+def test_bracket_end_budgets(L, O, n, k):
+    """Budgets near 0 and near n on the bracketing path: one bracket end is
+    open (lo = 0 or hi = m + 1), so one tail is empty and the root lies
+    beyond the last knot of the band on that side."""
+    g0 = np.random.Generator(np.random.PCG64(3401 + n % 97))
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    res, _, _ = full_check(f"bracket end budget n={n} k={k}", L, O, r, g, k, 0.02, path="bracket", stats=True)
+    st = res["stats"]
+    log(f"  a_lo={st['a_lo'][0].item()} a_hi={st['a_hi'][0].item()} band={st['band'][0].item()} "
+        f"flags={st['flags'][0].item()}")
+
+
 def test_bracket_forced_miss_falls_back(L, O):
     """A bracket that excludes b must be caught by certification and the
     full-sort fallback must still meet every tolerance."""
