@@ -113,32 +113,49 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
   int C;
   int o = team.excl_scan(mine, &C);
   if (C > CAP) return false;
-  double S = 0.0;  // tail below a, anchored at a
+  // tail below a, anchored at a: this lane's E terms (each <= 1) in fp32,
+  // the lane sums in fp64
+  float Sl = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float w = sg * v[e];
     if (valid[e] && w >= a) buf[o++] = w;
-    if (valid[e] && w < a) S += (double)__builtin_amdgcn_exp2f((w - a) * cf);
+    if (valid[e] && w < a) Sl += __builtin_amdgcn_exp2f((w - a) * cf);
   }
-  S = team.sum(S);
+  const double S = team.sum((double)Sl);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float s4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) s4[q] = 4 * team.lane + q < C ? buf[4 * team.lane + q] : INFINITY;
-  bitonic_sort<4>(s4, team);
-  const int nv = min(max(C - 4 * team.lane, 0), 4);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) s4[q] = q < nv ? s4[q] : 0.0f;
   PartInfo part;
-  part.nvalid = nv;
   part.above = (double)C;
   part.seed_lo = Pre{a, S};
   part.seed_hi = Suf{0.0f, 0.0};
   part.first = true;
   part.last = true;
-  const double bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
+  double bw;
+  // the candidates sorted at two per lane when every team of the wave has
+  // at most 2*LANES of them (the usual case), else at four per lane
+  if (__ballot(C > 2 * LANES) == 0ull) {
+    float s2[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) s2[q] = 2 * team.lane + q < C ? buf[2 * team.lane + q] : INFINITY;
+    bitonic_sort<2>(s2, team);
+    const int nv = min(max(C - 2 * team.lane, 0), 2);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) s2[q] = q < nv ? s2[q] : 0.0f;
+    part.nvalid = nv;
+    bw = segment_solve<2>(s2, nv, part, kk, t, c, cf, team);
+  } else {
+    float s4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s4[q] = 4 * team.lane + q < C ? buf[4 * team.lane + q] : INFINITY;
+    bitonic_sort<4>(s4, team);
+    const int nv = min(max(C - 4 * team.lane, 0), 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s4[q] = q < nv ? s4[q] : 0.0f;
+    part.nvalid = nv;
+    bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
+  }
   b_out = mirror ? -bw : bw;
   return true;
 }
@@ -195,7 +212,7 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float z2 = ((v[e] - bh) - bl) * cf;
-    const float h = 0.5f * __builtin_amdgcn_exp2f(-fabsf(z2));
+    const float h = __builtin_amdgcn_exp2f(-1.0f - fabsf(z2));  // e^{-|z|}/2
     out[e] = z2 < 0.0f ? h : 1.0f - h;
   }
   store_row<E, LANES>(pp, n, team.lane, ok, vec, out);
