@@ -19,6 +19,7 @@
 namespace lapsum {
 
 LDEV bool aligned16(const void *q) { return ((uintptr_t)q & 15u) == 0; }
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 // p = F((x - b)/t); z2 = (x - b) log2(e)/t formed from an fp64 difference.
 LDEV float laplace_cdf_at(float x, double b, double c) {
@@ -44,7 +45,12 @@ LDEV void load_row(const float *rr, int n, int lane, bool ok, bool vec, float (&
     for (int q = 0; q < E; q += 4) {
       const int i = slot_index<E, LANES>(lane, q, true);
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok && i < n) x = *reinterpret_cast<const float4 *>(rr + i);
+      if (ok && i < n) {
+        // rows are read once and written once: non-temporal, so nothing is
+        // left dirty in L2 for the end-of-kernel write-back
+        const f4 y = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr + i));
+        x = make_float4(y.x, y.y, y.z, y.w);
+      }
       v[q] = x.x;
       v[q + 1] = x.y;
       v[q + 2] = x.z;
@@ -66,7 +72,10 @@ LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (
 #pragma unroll
     for (int q = 0; q < E; q += 4) {
       const int i = slot_index<E, LANES>(lane, q, true);
-      if (i < n) *reinterpret_cast<float4 *>(pp + i) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+      if (i < n) {
+        const f4 y = {v[q], v[q + 1], v[q + 2], v[q + 3]};
+        __builtin_nontemporal_store(y, reinterpret_cast<f4 *>(pp + i));
+      }
     }
   } else {
 #pragma unroll
