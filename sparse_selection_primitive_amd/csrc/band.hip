@@ -90,7 +90,9 @@ LDEV void for_each_row_key(const BandArgs &a, int64_t row, int blk, F &&f) {
 #pragma unroll
       for (int u = 0; u < kRowLoads; ++u) {
         const int64_t ii = i + (int64_t)u * 4 * kBT;
-        v[u] = ii < c1 ? __builtin_nontemporal_load(reinterpret_cast<const f4 *>(rr + ii)) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        // ordinary (temporal) loads: the min/max, count and scatter passes
+        // read the same chunk, so a later pass may find it in cache
+        v[u] = ii < c1 ? *reinterpret_cast<const f4 *>(rr + ii) : f4{0.0f, 0.0f, 0.0f, 0.0f};
       }
 #pragma unroll
       for (int u = 0; u < kRowLoads; ++u) {
