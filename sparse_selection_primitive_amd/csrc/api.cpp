@@ -98,7 +98,7 @@ struct Plan {
   SegRegions full_seg{};
   // backward layout
   size_t bwd_bytes = 0;
-  size_t bst = 0, bpart = 0;
+  size_t bpart = 0;
   int bgx = 0;
 };
 
@@ -171,7 +171,6 @@ lapsum_status check_common(int64_t rows, int64_t n, double t) {
 void bwd_layout(int64_t rows, int64_t n, Plan &P) {
   Layout B;
   if (!onchip_backward_supported(n)) {
-    P.bst = B.take((size_t)rows * row_state_bytes());
     P.bgx = bwd_grid_x(rows, n);
     P.bpart = B.take(bwd_partial_bytes(rows, P.bgx));
   }
@@ -477,12 +476,11 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
     return LAPSUM_OK;
   }
   char *ws = reinterpret_cast<char *>(workspace);
-  RowState *rs = reinterpret_cast<RowState *>(ws + P.bst);
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 0);
-  LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, rs, ws + P.bpart, P.bgx, dk, o.stats, s));
+  LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, ws + P.bpart, P.bgx, s));
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 1);
   tm.mark(LAPSUM_STAGE_BWD_APPLY, 0);
-  LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, rs, t, dr, s));
+  LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, ws + P.bpart, P.bgx, t, dr, dk, o.stats, s));
   tm.mark(LAPSUM_STAGE_BWD_APPLY, 1);
   return LAPSUM_OK;
 }

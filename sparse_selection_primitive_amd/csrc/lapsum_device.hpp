@@ -738,7 +738,6 @@ struct RowState {
   uint32_t kmin, kmax;      // key range of the band
   int32_t flags;
   int32_t pad0;
-  double dk;                // backward: dk in fp64
 };
 
 // Per-call reset of one row's state (bracket open unless forced).
@@ -756,7 +755,6 @@ LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_over
   z.kmax = 0u;
   z.flags = flags;
   z.pad0 = 0;
-  z.dk = 0.0;
   st[row] = z;
 }
 

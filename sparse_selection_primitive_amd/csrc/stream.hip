@@ -203,56 +203,55 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
   if (threadIdx.x == 0) part[row * gx + blockIdx.x] = BwdPartial{D, G};
 }
 
-// dk = G/D per row from the block partials, summed in a fixed order
-__global__ __launch_bounds__(kStreamThreads) void bwd_finalize_kernel(const BwdPartial *__restrict__ part, int gx,
-                                                                      RowState *__restrict__ st,
-                                                                      float *__restrict__ dk,
-                                                                      lapsum_row_stats *stats) {
-  __shared__ double lds[2 * kStreamThreads / kWave];
-  const int64_t row = blockIdx.x;
+// dr = d (g - dk).  Every workgroup adds the reduce pass's partials of its
+// row in the same fixed order, so all of them hold the same dk (bitwise) and
+// no finalize launch is needed; the first one writes dk.  The first batch of
+// scores is already in flight while the partials are added.
+LDEV void bwd_row_total(const BwdPartial *__restrict__ vp, int gx, double *lds, double &dkd, bool &degenerate) {
   double Ds = 0.0, Gs = 0.0;
-  const BwdPartial *vp = part + row * gx;
   for (int i = threadIdx.x; i < gx; i += kStreamThreads) {
     Ds += vp[i].D;
     Gs += vp[i].G;
   }
   block_sum2<kStreamThreads>(Ds, Gs, lds);
-  if (threadIdx.x == 0) {
-    const double dkd = Ds > 0.0 ? Gs / Ds : 0.0;
-    st[row].dk = dkd;
-    st[row].flags = Ds > 0.0 ? 0 : LAPSUM_FLAG_DEGENERATE;
-    dk[row] = (float)dkd;
-    if (stats && !(Ds > 0.0)) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
-  }
+  degenerate = !(Ds > 0.0);
+  dkd = degenerate ? 0.0 : Gs / Ds;
 }
 
 __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *__restrict__ g,
                                                                    const float *__restrict__ p, int64_t n,
-                                                                   const RowState *__restrict__ st, double t,
-                                                                   float *__restrict__ dr) {
+                                                                   const BwdPartial *__restrict__ part, int gx,
+                                                                   double t, float *__restrict__ dr,
+                                                                   float *__restrict__ dk, lapsum_row_stats *stats) {
+  __shared__ double lds[2 * kStreamThreads / kWave];
   const int64_t row = blockIdx.y;
-  const double dkd = st[row].dk;
-  const bool degenerate = (st[row].flags & LAPSUM_FLAG_DEGENERATE) != 0;
-  const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
+  const BwdPartial *vp = part + row * gx;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
   float *dd = dr + row * n;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  double dkd;
+  bool degenerate;
   if ((n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr)) {
     const int64_t n4 = n >> 2;
     const f4 *g4 = reinterpret_cast<const f4 *>(gg);
     const f4 *p4 = reinterpret_cast<const f4 *>(pp);
     f4 *d4 = reinterpret_cast<f4 *>(dd);
-    for (int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x; i0 < n4;
-         i0 += stride * kUnroll) {
-      f4 pv[kUnroll], gv[kUnroll];
+    f4 pv[kUnroll], gv[kUnroll];
+    int64_t i0 = (int64_t)blockIdx.x * kStreamThreads * kUnroll + threadIdx.x;
+    auto load = [&](int64_t j0) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = i0 + u * kStreamThreads;
+        const int64_t i = j0 + u * kStreamThreads;
         const bool ok = i < n4;
         pv[u] = ok ? __builtin_nontemporal_load(p4 + i) : f4{0.f, 0.f, 0.f, 0.f};
         gv[u] = ok ? __builtin_nontemporal_load(g4 + i) : f4{0.f, 0.f, 0.f, 0.f};
       }
+    };
+    load(i0);
+    bwd_row_total(vp, gx, lds, dkd, degenerate);
+    const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
+    while (i0 < n4) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t i = i0 + u * kStreamThreads;
@@ -265,31 +264,35 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
           __builtin_nontemporal_store(o, d4 + i);
         }
       }
+      i0 += stride * kUnroll;
+      if (i0 < n4) load(i0);
     }
   } else {
+    bwd_row_total(vp, gx, lds, dkd, degenerate);
+    const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
       dd[i] = fminf(pp[i], 1.0f - pp[i]) * inv_t * (float)((double)gg[i] - dkd);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    dk[row] = (float)dkd;
+    if (stats && degenerate) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
   }
 }
 
 int bwd_grid_x(int64_t rows, int64_t n) { return stream_grid_x(rows, n); }
 size_t bwd_partial_bytes(int64_t rows, int grid_x) { return sizeof(BwdPartial) * (size_t)rows * (size_t)grid_x; }
 
-hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, RowState *st, void *partials,
-                             int grid_x, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, void *partials, int grid_x,
+                             hipStream_t s) {
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
                      reinterpret_cast<BwdPartial *>(partials), grid_x);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)rows), dim3(kStreamThreads), 0, s,
-                     reinterpret_cast<const BwdPartial *>(partials), grid_x, st, dk, stats);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const RowState *st, double t,
-                            float *dr, hipStream_t s) {
-  const int gx = stream_grid_x(rows, n);
-  hipLaunchKernelGGL(bwd_apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n, st, t, dr);
+hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const void *partials,
+                            int grid_x, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
+                     reinterpret_cast<const BwdPartial *>(partials), grid_x, t, dr, dk, stats);
   return hipGetLastError();
 }
 
