@@ -107,7 +107,7 @@ hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState 
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, void *partials, int grid_x,
                              hipStream_t s);
 hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const void *partials,
-                            int grid_x, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s);
+                            int npart, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s);
 int bwd_grid_x(int64_t rows, int64_t n);
 size_t bwd_partial_bytes(int64_t rows, int grid_x);
 hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats *stats, hipStream_t s);

@@ -290,9 +290,10 @@ hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64
 }
 
 hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const void *partials,
-                            int grid_x, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_apply_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
-                     reinterpret_cast<const BwdPartial *>(partials), grid_x, t, dr, dk, stats);
+                            int npart, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+  const int gx = stream_grid_x(rows, n);
+  hipLaunchKernelGGL(bwd_apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
+                     reinterpret_cast<const BwdPartial *>(partials), npart, t, dr, dk, stats);
   return hipGetLastError();
 }
 
