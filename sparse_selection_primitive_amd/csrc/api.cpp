@@ -281,8 +281,8 @@ SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const f
   return a;
 }
 
-BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots,
-                   const uint32_t *offs, double k, double t, const float *r = nullptr, int64_t n = 0) {
+BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots, uint32_t *offs,
+                   double k, double t, const float *r, int64_t n) {
   const BandRegions &R = P.bnd;
   BandArgs a;
   a.rows = (int)rows;
@@ -291,6 +291,7 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   a.nblk = R.nblk;
   a.slots = slots;
   a.offs = offs;
+  a.part = reinterpret_cast<const FilterPartial *>(ws + P.fpart);
   a.r = r;
   a.n = n;
   a.chunk = R.chunk;
@@ -432,15 +433,15 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);
     uint32_t *offs = reinterpret_cast<uint32_t *>(ws + P.offs);
     tm.mark(LAPSUM_STAGE_FILTER, 0);
-    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, offs, P.cap, ws + P.fpart, P.fgx, s));
+    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
     const SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
     // the band kernels also run the fallback for rows whose bracket missed
     if (P.band_onchip)
-      LAPSUM_TRY(launch_band_onchip(slots, offs, P.fgx, rows, P.cap, rs, k, t, fb, s));
+      LAPSUM_TRY(launch_band_onchip(slots, ws + P.fpart, P.fgx, rows, n, P.cap, rs, k, t, fb, s));
     else
-      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t), fb, s));
+      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t, nullptr, n), fb, s));
     tm.mark(LAPSUM_STAGE_BAND, 1);
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);

@@ -30,6 +30,7 @@
 // placed keys inside a bucket.
 #include <limits.h>
 
+#include "filter_dev.hpp"
 #include "segment_dev.hpp"
 
 namespace lapsum {
@@ -155,14 +156,15 @@ __global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
 
 __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   __shared__ uint32_t h[kBandBuckets];
-  __shared__ uint32_t sb[kMaxGroup + 1];
+  __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
+  __shared__ uint32_t rng[2];
   const int64_t row = blockIdx.y;
   const int blk = blockIdx.x;
-  __shared__ uint32_t rng[2];
   RowState &S = a.st[row];
-  if (a.r == nullptr) load_slot_bounds(a, row, blk, sb);
   const int nb = 1 << a.bbits;
   for (int j = threadIdx.x; j < nb; j += kBT) h[j] = 0u;
+  RowState R;  // the key range and count this workgroup buckets by
+  const uint32_t *sb = soffs;
   if (a.r != nullptr) {
     // full-row mode: the row's key range from the min/max partials; the
     // first workgroup records it (and the key count) for the later kernels
@@ -187,23 +189,28 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
         }
       }
     }
-  } else if (!band_active(S)) {
-    return;
-  }
-  __syncthreads();
-  uint32_t kmin;
-  int shift;
-  if (a.r != nullptr) {
-    RowState R;
+    __syncthreads();
     R.kmin = rng[0];
     R.kmax = rng[1];
     R.band = (unsigned long long)a.n;
-    kmin = R.kmin;
-    shift = band_shift(R, a.bbits);
   } else {
-    kmin = S.kmin;
-    shift = band_shift(S, a.bbits);
+    // band mode: the streaming filter's partials of the row, added by every
+    // workgroup in the same fixed order; the first one records the totals
+    // and the slot offsets for the later kernels
+    const FilterTotals T = filter_totals<kBT>(a.part + row * a.gx, a.gx, a.n, a.cap, soffs);
+    if (blk == 0) {
+      if (threadIdx.x == 0) store_filter_totals(S, T);
+      uint32_t *ro = a.offs + row * (int64_t)(a.gx + 1);
+      for (int i = threadIdx.x; i <= a.gx; i += kBT) ro[i] = soffs[i];
+    }
+    if (T.overflow) return;  // the row takes the fallback
+    R.kmin = T.kmin;
+    R.kmax = T.kmax;
+    R.band = T.band;
+    sb = soffs + blk * a.group;
   }
+  const uint32_t kmin = R.kmin;
+  const int shift = band_shift(R, a.bbits);
   for_each_band_key(a, row, blk, sb, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
   __syncthreads();
   uint32_t *dst = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;

@@ -8,13 +8,14 @@
 //  step 2, stream and filter -- filter_kernel reads every score once: below
 //    a_L it adds e^{(r - a_L)/t} to S_L, at or above a_R it adds
 //    e^{-(r - a_R)/t} to S_R, and in between it appends the key to its
-//    workgroup's band slot; filter_finalize_kernel adds the workgroups'
-//    partial sums and counts per row in a fixed order (fp64).
+//    workgroup's band slot and leaves its partial sums and counts; the band
+//    solve's first kernel adds them per row in a fixed order (fp64).
 //
 // Random numbers: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
 // key (seed low, seed high) and counter (j, row, 0, 0): words x0, x1 give
 // I = floor((x1 2^32 + x0) n / 2^64), word x2 gives u = (x2 + 1/2)/2^32 and
 // L = F^-1(u) in fp64; X is rounded to fp32.
+#include "filter_dev.hpp"
 #include "lapsum_device.hpp"
 #include "lapsum_internal.hpp"
 
@@ -572,14 +573,6 @@ hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t r
 }
 
 // --------------------------------------------------------- stream & filter
-struct FilterPartial {
-  double sl, sr;
-  unsigned long long cnl;     // scores at or above a_L
-  uint32_t cnt;       // band keys this block found (may exceed kBandSlot)
-  uint32_t kmn, kmx;  // key range of those band keys
-  uint32_t pad;
-};
-
 LDEV uint32_t mbcnt64(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
@@ -591,9 +584,9 @@ LDEV uint32_t mbcnt64(unsigned long long mask) {
 // upper-tail terms of those at or above a_R and appends the band keys to
 // this block's own slot (positions reserved by an LDS counter, one LDS atomic
 // per wave and group).  The tail sums, the count at or above a_L and the band
-// key range go to the block's partial.  No global atomics: the per-row
-// finalize adds the partials in a fixed order, derives the counts below a_L
-// and above a_R and turns the slot counts into offsets.
+// key range go to the block's partial.  No global atomics: the band solve
+// adds the partials in a fixed order, derives the counts below a_L and above
+// a_R and turns the slot counts into offsets (filter_totals).
 template <bool CHECK>
 LDEV void filter_items(const float (&x)[4 * kUnroll], const bool (&ok)[4 * kUnroll], float aL, float aR, float cf,
                        double &sl, double &sr, unsigned long long &cnl, uint32_t &kmn, uint32_t &kmx,
@@ -737,107 +730,6 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   }
 }
 
-// Per row, in a fixed order: tail sums and counts, band size M, band key
-// range, and the exclusive offsets of the block slots (offs[gx] = M).  A
-// slot that overflowed, or M beyond the band capacity, sends the row to the
-// full-sort fallback.
-__global__ __launch_bounds__(kStreamThreads) void filter_finalize_kernel(const FilterPartial *__restrict__ part,
-                                                                         int gx, int64_t n, int64_t cap,
-                                                                         RowState *__restrict__ st,
-                                                                         uint32_t *__restrict__ offs) {
-  __shared__ double lds_d[2 * kStreamThreads / kWave];
-  __shared__ unsigned long long lds_c[kStreamThreads / kWave];
-  __shared__ uint32_t lds_k[3 * kStreamThreads / kWave];
-  __shared__ uint32_t wsum[kStreamThreads / kWave];
-  const int64_t row = blockIdx.x;
-  const FilterPartial *vp = part + row * gx;
-  uint32_t *ro = offs + row * (int64_t)(gx + 1);
-  // contiguous chunk of blocks per thread, so the offsets come out in order
-  const int per = (gx + kStreamThreads - 1) / kStreamThreads;
-  const int b0 = threadIdx.x * per;
-  double a = 0.0, b = 0.0;
-  unsigned long long c0 = 0;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u, csum = 0u, big = 0u;
-  for (int i = 0; i < per; ++i) {
-    const int j = b0 + i;
-    if (j < gx) {
-      const FilterPartial fp = vp[j];
-      a += fp.sl;
-      b += fp.sr;
-      c0 += fp.cnl;
-      mn = min(mn, fp.kmn);
-      mx = max(mx, fp.kmx);
-      csum += fp.cnt;
-      big |= fp.cnt > (uint32_t)kBandSlot ? 1u : 0u;
-    }
-  }
-  // exclusive scan of the chunk sums
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  uint32_t inc = csum;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += y;
-  }
-  if (lane == kWave - 1) wsum[w] = inc;
-  __syncthreads();
-  uint32_t before = 0u, total = 0u;
-  for (int i = 0; i < kStreamThreads / kWave; ++i) {
-    if (i < w) before += wsum[i];
-    total += wsum[i];
-  }
-  uint32_t run = before + inc - csum;
-  for (int i = 0; i < per; ++i) {
-    const int j = b0 + i;
-    if (j < gx) {
-      ro[j] = run;
-      run += vp[j].cnt;
-    }
-  }
-  if (threadIdx.x == kStreamThreads - 1) ro[gx] = total;
-#pragma unroll
-  for (int msk = 1; msk < kWave; msk <<= 1) {
-    a += __shfl_xor(a, msk, kWave);
-    b += __shfl_xor(b, msk, kWave);
-    c0 += __shfl_xor(c0, msk, kWave);
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, msk, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, msk, kWave));
-    big |= (uint32_t)__shfl_xor((int)big, msk, kWave);
-  }
-  if (lane == 0) {
-    lds_d[2 * w] = a;
-    lds_d[2 * w + 1] = b;
-    lds_c[w] = c0;
-    lds_k[3 * w] = mn;
-    lds_k[3 * w + 1] = mx;
-    lds_k[3 * w + 2] = big;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double ta = 0.0, tb = 0.0;
-    unsigned long long tc0 = 0;
-    uint32_t tmn = 0xFFFFFFFFu, tmx = 0u, tbig = 0u;
-    for (int i = 0; i < kStreamThreads / kWave; ++i) {
-      ta += lds_d[2 * i];
-      tb += lds_d[2 * i + 1];
-      tc0 += lds_c[i];
-      tmn = min(tmn, lds_k[3 * i]);
-      tmx = max(tmx, lds_k[3 * i + 1]);
-      tbig |= lds_k[3 * i + 2];
-    }
-    RowState &S = st[row];
-    S.tail_lo = ta;
-    S.tail_hi = tb;
-    // every score is below a_L, inside the band or at or above a_R
-    S.count_lo = (unsigned long long)n - tc0;
-    S.count_hi = tc0 - total;
-    S.band = total;
-    S.kmin = tmn;
-    S.kmax = tmx;
-    if (tbig || (int64_t)total > cap) S.flags |= LAPSUM_FLAG_OVERFLOW | LAPSUM_FLAG_FALLBACK;
-  }
-}
-
 int filter_grid_x(int64_t rows, int64_t n) {
   const int64_t per_row_need = (n / 4 + kStreamThreads * kUnroll - 1) / (kStreamThreads * kUnroll);
   int64_t target = 1024 / (rows > 0 ? rows : 1);
@@ -855,13 +747,9 @@ size_t band_slot_bytes(int64_t rows, int grid_x) {
 size_t band_offs_bytes(int64_t rows, int grid_x) { return sizeof(uint32_t) * (size_t)rows * (size_t)(grid_x + 1); }
 
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
-                         uint32_t *offs, int64_t cap, void *partials, int grid_x, hipStream_t s) {
+                         void *partials, int grid_x, hipStream_t s) {
   hipLaunchKernelGGL(filter_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, slots,
                      reinterpret_cast<FilterPartial *>(partials), grid_x, t);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(filter_finalize_kernel, dim3((unsigned)rows), dim3(kStreamThreads), 0, s,
-                     reinterpret_cast<const FilterPartial *>(partials), grid_x, n, cap, st, offs);
   return hipGetLastError();
 }
 

@@ -49,6 +49,8 @@ constexpr int kBandBucketBits = 11;
 constexpr int kBandBuckets = 1 << kBandBucketBits;
 constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row, at most
 
+struct FilterPartial;
+
 struct BandArgs {
   int rows;
   int gx;               // band mode: filter workgroups (slots) per row
@@ -56,9 +58,10 @@ struct BandArgs {
   int nblk;             // count/scatter workgroups per row
   int bbits;            // buckets per row = 2^bbits <= kBandBuckets (about 32 keys per bucket)
   const uint32_t *slots; // band mode: [rows][gx][kBandSlot] band keys per filter workgroup
-  const uint32_t *offs;  // band mode: [rows][gx + 1] slot offsets
+  uint32_t *offs;        // band mode: [rows][gx + 1] slot offsets (written by the count kernel)
+  const FilterPartial *part;  // band mode: [rows][gx] streaming-filter partials
   const float *r;       // full-row mode (non-null): the scores [rows][n], every one a key
-  int64_t n;            // full-row mode: row length
+  int64_t n;            // row length
   int64_t chunk;        // full-row mode: scores per count/scatter workgroup (a multiple of 4)
   uint32_t *mm;         // full-row mode: [rows][nblk][2] key minimum and maximum per workgroup
   RowState *st;         // [rows]
@@ -91,13 +94,13 @@ size_t sample_start_bytes(int64_t rows, int64_t m);
 hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
                          int64_t hi, RowState *st, hipStream_t s);
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
-                         uint32_t *offs, int64_t cap, void *partials, int grid_x, hipStream_t s);
+                         void *partials, int grid_x, hipStream_t s);
 int filter_grid_x(int64_t rows, int64_t n);
 size_t filter_partial_bytes(int64_t rows, int grid_x);
 size_t band_slot_bytes(int64_t rows, int grid_x);
 size_t band_offs_bytes(int64_t rows, int grid_x);
-hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
-                              RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
+hipError_t launch_band_onchip(const uint32_t *slots, const void *partials, int gx, int64_t rows, int64_t n,
+                              int64_t cap, RowState *st, double k, double t, const SegArgs &fb, hipStream_t s);
 hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fallback, hipStream_t s);
 int band_count_blocks(int gx, int *group);
 int full_count_blocks(int64_t n, int64_t *chunk);

@@ -14,6 +14,7 @@
 // Band solve (section 2.2, probabilistic bracketing, step 3): the same
 // sort + curve + root on the compacted middle band, seeded with the tail
 // sums of the streaming pass, followed by the certification of step 4.
+#include "filter_dev.hpp"
 #include "segment_dev.hpp"
 
 namespace lapsum {
@@ -457,9 +458,9 @@ LDEV void band_onchip_row(const uint32_t *__restrict__ slots, const uint32_t *so
 // below its capacity is not sorted at the capacity.
 template <int NPMAX>
 __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__restrict__ slots,
-                                                             const uint32_t *__restrict__ offs, int gx,
-                                                             RowState *__restrict__ st, double k, double t,
-                                                             SegArgs fb) {
+                                                             const FilterPartial *__restrict__ part, int gx,
+                                                             int64_t n, int64_t cap, RowState *__restrict__ st,
+                                                             double k, double t, SegArgs fb) {
   union BandLds {
     BlockTeamLds<kBandNT, NPMAX / kBandNT> band;
     SegLds<kBandNT> full;
@@ -469,10 +470,11 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   __shared__ int fall;
   const int64_t row = blockIdx.x;
   RowState &S = st[row];
-  const uint32_t *ro = offs + row * (int64_t)(gx + 1);
-  for (int i = threadIdx.x; i <= gx; i += kBandNT) soffs[i] = ro[i];
+  // the streaming filter's partials of the row: totals and slot offsets
+  const FilterTotals T = filter_totals<kBandNT>(part + row * gx, gx, n, cap, soffs);
+  if (threadIdx.x == 0) store_filter_totals(S, T);
   __syncthreads();
-  if (!(S.flags & LAPSUM_FLAG_OVERFLOW)) {
+  if (!T.overflow) {
     const int m = (int)S.band;
     if (m <= 1024 || NPMAX == 1024) band_onchip_row<1024>(slots, soffs, gx, row, m, S, k, t, lds);
     else if (m <= 2048 || NPMAX == 2048) band_onchip_row<(NPMAX < 2048 ? NPMAX : 2048)>(slots, soffs, gx, row, m, S, k, t, lds);
@@ -484,16 +486,21 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   if (fall) fallback_row<kBandNT>(fb, (int)row, lds.full);
 }
 
-hipError_t launch_band_onchip(const uint32_t *slots, const uint32_t *offs, int gx, int64_t rows, int64_t cap,
-                              RowState *st, double k, double t, const SegArgs &fb, hipStream_t s) {
+hipError_t launch_band_onchip(const uint32_t *slots, const void *partials, int gx, int64_t rows, int64_t n,
+                              int64_t cap, RowState *st, double k, double t, const SegArgs &fb, hipStream_t s) {
+  const FilterPartial *part = reinterpret_cast<const FilterPartial *>(partials);
   if (cap <= 1024)
-    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
+                       st, k, t, fb);
   else if (cap <= 2048)
-    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
+                       st, k, t, fb);
   else if (cap <= 4096)
-    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
+                       st, k, t, fb);
   else
-    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, offs, gx, st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
+                       st, k, t, fb);
   return hipGetLastError();
 }
 
