@@ -470,6 +470,29 @@ def test_bracket_extreme_sampled(L, O):
     log(f"  db/t={db:.2e} |sum-k|={abs(psum - w.k):.2e} dr_rel={rel:.2e} band={st['band'][0].item()}")
 
 
+# ------------------------------------------------------- non-finite scores
+@pytest.mark.parametrize("path,n", [("onchip", 300), ("fullsort", 20000), ("bracket", 300_000)])
+def test_non_finite_rows_stay_contained(L, O, path, n):
+    """Non-finite scores break the operator's precondition, so their rows'
+    outputs are unspecified; the call must still return, and the finite row
+    of the same batch must still match the oracle."""
+    g0 = np.random.Generator(np.random.PCG64(3501 + n % 89))
+    r = g0.standard_normal((3, n)).astype(np.float32)
+    g = g0.standard_normal((3, n)).astype(np.float32)
+    r[1, g0.choice(n, size=7, replace=False)] = np.nan
+    r[2, :5] = np.inf
+    r[2, 5:9] = -np.inf
+    k, t = 0.1 * n + 0.5, 0.05
+    log(f"[case] non-finite rows {path} n={n}")
+    res = run(L, r, k, t, g, path=path)
+    p_or, b_or = O.forward(r[:1], k, t)
+    name = f"non-finite batch, finite row ({path})"
+    check_forward(name, k, t, res["p"][:1], res["b"][:1], p_or, b_or)
+    check_budget(name, k, res["p"][:1])
+    dr_or, dk_or = O.backward(r[:1], b_or, g[:1], t)
+    check_backward(name, r[:1], b_or, g[:1], t, res["dr"][:1], res["dk"][:1], dr_or, dk_or)
+
+
 # ------------------------------------------------------------ determinism
 def test_determinism(L):
     from sparse_selection_primitive_amd import workloads
