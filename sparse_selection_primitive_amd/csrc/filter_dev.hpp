@@ -57,13 +57,18 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
       big |= fp.cnt > (uint32_t)kBandSlot ? 1u : 0u;
     }
   }
-  // exclusive scan of the chunk sums
+  // exclusive scan of the chunk sums: inside each DPP row of 16 lanes, then
+  // the row totals (v_readlane), then the wave totals through LDS
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   uint32_t inc = csum;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += y;
+  inc += dpp<0x111>(inc);  // row_shr:1 (a lane before its row's start reads 0)
+  inc += dpp<0x112>(inc);
+  inc += dpp<0x114>(inc);
+  inc += dpp<0x118>(inc);
+  {
+    const uint32_t r0 = read_lane(inc, 15), r1 = read_lane(inc, 31), r2 = read_lane(inc, 47);
+    const int rw = lane >> 4;
+    inc += rw == 0 ? 0u : (rw == 1 ? r0 : (rw == 2 ? r0 + r1 : r0 + r1 + r2));
   }
   if (lane == kWave - 1) wsum[w] = inc;
   __syncthreads();
@@ -81,15 +86,12 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
     }
   }
   if (threadIdx.x == NT - 1) ro[gx] = total;
-#pragma unroll
-  for (int msk = 1; msk < kWave; msk <<= 1) {
-    a += __shfl_xor(a, msk, kWave);
-    b += __shfl_xor(b, msk, kWave);
-    c0 += __shfl_xor(c0, msk, kWave);
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, msk, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, msk, kWave));
-    big |= (uint32_t)__shfl_xor((int)big, msk, kWave);
-  }
+  a = wave_reduce(a, [](double x, double y) { return x + y; });
+  b = wave_reduce(b, [](double x, double y) { return x + y; });
+  c0 = wave_reduce(c0, [](unsigned long long x, unsigned long long y) { return x + y; });
+  mn = wave_reduce(mn, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+  mx = wave_reduce(mx, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+  big = wave_reduce(big, [](uint32_t x, uint32_t y) { return x | y; });
   if (lane == 0) {
     lds_d[2 * w] = a;
     lds_d[2 * w + 1] = b;

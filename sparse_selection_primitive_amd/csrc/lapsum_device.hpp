@@ -443,8 +443,7 @@ struct BlockTeam {
     }
   }
   LDEV int sum(int v) const {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+    v = wave_reduce(v, [](int x, int y) { return x + y; });
     __syncthreads();
     if ((lane & (kWave - 1)) == 0) lds->wi[lane / kWave] = v;
     __syncthreads();
@@ -454,8 +453,7 @@ struct BlockTeam {
     return t;
   }
   LDEV double sum(double v) const {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+    v = wave_reduce(v, [](double x, double y) { return x + y; });
     __syncthreads();
     if ((lane & (kWave - 1)) == 0) lds->ws[lane / kWave] = v;
     __syncthreads();
