@@ -217,6 +217,16 @@ def test_fullsort_constant_rows(L, O):
     full_check("fullsort constant rows", L, O, r, None, 1234.5, 0.1, path="fullsort")
 
 
+@pytest.mark.parametrize("k", [1000.0, 1000.5])
+def test_fullsort_tiny_temperature(L, O, k):
+    """t = 1e-6, far below the gaps between neighbouring scores: the budget is
+    flat between knots and b rests on sums e^{-gap/t} far below the fp32 range
+    (an integer k puts b where the two neighbouring tails balance)."""
+    g0 = np.random.Generator(np.random.PCG64(3601 + 20000 % 83))
+    r = g0.standard_normal((2, 20000)).astype(np.float32)
+    full_check(f"fullsort tiny t k={k}", L, O, r, None, k, 1e-6, path="fullsort")
+
+
 # ---------------------------------------------------------- bracketing path
 def check_bracket_stats(name, L, O, r, k, t, stats, seed, m_log2=None, delta=1e-6):
     from oracle import bracket as ob
@@ -301,6 +311,15 @@ def test_bracket_end_budgets(L, O, n, k):
     st = res["stats"]
     log(f"  a_lo={st['a_lo'][0].item()} a_hi={st['a_hi'][0].item()} band={st['band'][0].item()} "
         f"flags={st['flags'][0].item()}")
+
+
+def test_bracket_tiny_temperature(L, O):
+    """The bracketing path at t = 1e-6: the kernel-noised sample is nearly
+    the scores themselves and the band solve rests on log-space tails."""
+    g0 = np.random.Generator(np.random.PCG64(3601 + 300000 % 83))
+    r = g0.standard_normal((1, 300000)).astype(np.float32)
+    res, _, _ = full_check("bracket tiny t", L, O, r, None, 1000.5, 1e-6, path="bracket", stats=True)
+    log(f"  band={res['stats']['band'][0].item()} flags={res['stats']['flags'][0].item()}")
 
 
 def test_bracket_forced_miss_falls_back(L, O):
