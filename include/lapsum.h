@@ -68,7 +68,8 @@ typedef enum lapsum_status {
 typedef enum lapsum_path {
     LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: FULLSORT; else BRACKET */
     LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
-    LAPSUM_PATH_FULLSORT = 2, /* radix sort + tiled scan + locate/root + streaming apply */
+    LAPSUM_PATH_FULLSORT = 2, /* one radix (bucket) pass over the row, order-free bucket sums, locate,
+                                 sort of the balancing bucket only, root + streaming apply */
     LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing with full-sort fallback */
 } lapsum_path;
 
