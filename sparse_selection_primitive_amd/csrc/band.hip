@@ -30,8 +30,8 @@
 // placed keys inside a bucket.
 #include <limits.h>
 
+#include "bucket_dev.hpp"
 #include "filter_dev.hpp"
-#include "segment_dev.hpp"
 
 namespace lapsum {
 
@@ -298,9 +298,6 @@ LDEV void write_agg(TileAgg *out, Pre p, Suf s) {
 // on the order in which the scatter left the keys, so the aggregates (and
 // everything computed from them) are bitwise reproducible.  A term loses at
 // most 2^-(fb+1) to the rounding; fb >= 30 for any bucket.
-LDEV int agg_frac_bits(uint32_t cnt) { return 62 - (32 - __clz((int)cnt)); }
-LDEV unsigned long long fixed_term(float v, int fb) { return __float2ull_rn(ldexpf(v, fb)); }
-LDEV double fixed_value(unsigned long long v, int fb) { return ldexp((double)v, -fb); }
 
 LDEV void agg_write(TileAgg *out, uint32_t kmx, uint32_t kmn, unsigned long long sp, unsigned long long ss, int fb) {
   write_agg(out, Pre{value_of(kmx), fixed_value(sp, fb)}, Suf{value_of(kmn), fixed_value(ss, fb)});
@@ -406,66 +403,6 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
   }
 }
 
-// The whole workgroup sorts the keys kb[0 .. cnt) in place: stable LSD
-// radix passes (8-bit digits) over the keys relative to `kb0`, the lowest
-// key the range may hold (they differ from it in their low `bits` bits);
-// tb is scratch of the same size.
-template <int NT>
-LDEV void block_radix_sort(uint32_t *kb, uint32_t *tb, int64_t cnt, uint32_t kb0, int bits, RankLds<NT> &L) {
-  constexpr int TT = NT * kKpt;
-  __shared__ uint32_t h[256];
-  for (int64_t i = threadIdx.x; i < cnt; i += NT) kb[i] -= kb0;
-  __syncthreads();
-  uint32_t *src = kb, *dst = tb;
-  const int npass = (bits + 7) / 8;
-  const int64_t ntiles = (cnt + TT - 1) / TT;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  for (int pass = 0; pass < npass; ++pass) {
-    const int sh = 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += NT) h[i] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < cnt; i += NT) atomicAdd(&h[(src[i] >> sh) & 255u], 1u);
-    __syncthreads();
-    uint32_t run = wg_excl_scan<NT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.wsum);
-    for (int64_t tile = 0; tile < ntiles; ++tile) {
-      uint32_t key[kKpt];
-      int dig[kKpt];
-#pragma unroll
-      for (int q = 0; q < kKpt; ++q) {
-        const int64_t gi = tile * TT + w * (kWave * kKpt) + q * kWave + lane;
-        const bool valid = gi < cnt;
-        key[q] = valid ? src[gi] : 0u;
-        dig[q] = valid ? (int)((key[q] >> sh) & 255u) : 256;
-      }
-      const int vc = (int)min((int64_t)TT, cnt - tile * TT);
-      run += scatter_tile<NT>(key, dig, sh, vc, run, dst, L);
-    }
-    uint32_t *x = src;
-    src = dst;
-    dst = x;
-  }
-  for (int64_t i = threadIdx.x; i < cnt; i += NT) kb[i] = src[i] + kb0;
-  __syncthreads();
-}
-
-// One wave sorts a range of cnt <= 64*E keys in registers (blocked, E per
-// lane) and solves for the root inside it.
-template <int E>
-LDEV double wave_sort_solve(const uint32_t *kb, int cnt, PartInfo part, double k, double t, double c, float cf) {
-  WaveTeam<kWave> team;
-  const int base = team.lane * E;
-  uint32_t key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (base + e < cnt) ? kb[base + e] : 0xFFFFFFFFu;
-  bitonic_sort<E>(key, team);
-  const int nv = min(max(cnt - base, 0), E);
-  float s[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) s[e] = (e < nv) ? value_of(key[e]) : 0.0f;
-  part.nvalid = nv;
-  return segment_solve<E>(s, nv, part, k, t, c, cf, team);
-}
-
 // ---------------------------------------------------------------- locate
 // One workgroup of kLocT threads per row.  Its first kLocScanT threads
 // (two waves per SIMD) search the buckets, kLocPer consecutive buckets each:
@@ -491,143 +428,47 @@ union BandLocLds {
 
 __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs fb) {
   __shared__ BandLocLds L;
-  __shared__ int red[3][kLocScanW];
-  __shared__ float tw_a[2][kLocScanW];
-  __shared__ double tw_s[2][kLocScanW];
-  __shared__ float sel_pa, sel_sa;
-  __shared__ double sel_ps, sel_ss, sel_b;
-  __shared__ uint32_t sel_c, sel_st;
+  __shared__ double sel_b;
   __shared__ int sel_fb;
   const int64_t row = xcd_linear();
   RowState &S = a.st[row];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
   // The bucket search runs on the first kLocScanW waves only (two per SIMD):
-  // each of their threads owns kLocPer consecutive buckets.
-  const bool searcher = threadIdx.x < kLocScanT;
+  // each of their threads owns kLocPer consecutive buckets.  This thread's
+  // bucket records are loaded before the row state is examined.
   const int j0 = threadIdx.x * kLocPer;
-  // this thread's bucket records (issued before the row state is examined)
   TileAgg g[kLocPer];
-  uint32_t cnt[kLocPer], st0[kLocPer];
+  uint32_t cnt[kLocPer];
   const int nb = 1 << a.bbits;
 #pragma unroll
   for (int u = 0; u < kLocPer; ++u) {
-    const bool in = searcher && j0 + u < nb;
+    const bool in = threadIdx.x < kLocScanT && j0 + u < nb;
     g[u] = in ? a.bagg[o + j0 + u] : TileAgg{0.0f, 0.0f, 0.0, 0.0};
     cnt[u] = in ? a.btot[o + j0 + u] : 0u;
-    st0[u] = in ? a.bstart[o + j0 + u] : 0u;
   }
   const bool active = band_active(S);
   if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
   if (active) {
-    BlockTeam<kLocT, 1> team(&L.team);
     const double c = a.c;
     const int64_t M = (int64_t)S.band;
     const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
     const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
     const double cR = (double)S.count_hi;
-    // this thread's buckets joined, then exclusive scans over the search
-    // threads: inside each wave, then across the search waves
-    Pre tp{0.0f, 0.0}, xp{0.0f, 0.0};
-    Suf ts{0.0f, 0.0}, xs{0.0f, 0.0};
-#pragma unroll
-    for (int u = 0; u < kLocPer; ++u) tp = join(tp, Pre{g[u].aP, g[u].sP}, c);
-#pragma unroll
-    for (int u = kLocPer - 1; u >= 0; --u) ts = join(Suf{g[u].aS, g[u].sS}, ts, c);
-    if (searcher) {
-      const Pre ip = wave_scan(tp, c, &xp);
-      const Suf is = wave_scan(ts, c, &xs);
-      if (lane == kWave - 1) {
-        tw_a[0][w] = ip.a;
-        tw_s[0][w] = ip.s;
-      }
-      if (lane == 0) {
-        tw_a[1][w] = is.a;
-        tw_s[1][w] = is.s;
-      }
-    }
-    __syncthreads();
-    int first_lt = INT_MAX, first_ne = INT_MAX, last_ne = -1;
-    Pre before[kLocPer];
-    Suf after[kLocPer];
-    if (searcher) {
-      Pre twp = lane < kLocScanW ? Pre{tw_a[0][lane], tw_s[0][lane]} : Pre{0.0f, 0.0};
-      Suf tws = lane < kLocScanW ? Suf{tw_a[1][lane], tw_s[1][lane]} : Suf{0.0f, 0.0};
-      row_pre_steps<1>(twp, c);
-      row_suf_steps<1>(tws, c);
-      const int wb = __builtin_amdgcn_readfirstlane(w - 1), wa = __builtin_amdgcn_readfirstlane(w + 1);
-      const Pre wp = w == 0 ? Pre{0.0f, 0.0} : Pre{read_lane(twp.a, wb), read_lane(twp.s, wb)};
-      const Suf ws = w == kLocScanW - 1 ? Suf{0.0f, 0.0} : Suf{read_lane(tws.a, wa), read_lane(tws.s, wa)};
-      // everything before / after each bucket of this thread
-      before[0] = join(seed_lo, join(wp, xp, c), c);
-      after[kLocPer - 1] = join(join(xs, ws, c), seed_hi, c);
-#pragma unroll
-      for (int u = 1; u < kLocPer; ++u) before[u] = join(before[u - 1], Pre{g[u - 1].aP, g[u - 1].sP}, c);
-#pragma unroll
-      for (int u = kLocPer - 2; u >= 0; --u) after[u] = join(Suf{g[u + 1].aS, g[u + 1].sS}, after[u + 1], c);
-      // threshold curve at the last knot of every non-empty bucket
-#pragma unroll
-      for (int u = 0; u < kLocPer; ++u) {
-        if (cnt[u] > 0u) {
-          const int j = j0 + u;
-          const Pre pl = join(before[u], Pre{g[u].aP, g[u].sP}, c);
-          const Suf sa = after[u];
-          const double s_last = 1.0 + (sa.s == 0.0 ? 0.0 : sa.s * (double)wexp((double)pl.a - (double)sa.a, c));
-          const int64_t j_last = (int64_t)st0[u] + cnt[u] - 1;
-          const double gv = 0.5 * (pl.s - 1.0) + ((double)(M - j_last) + cR) - 0.5 * s_last;
-          if (gv < a.k) first_lt = min(first_lt, j);
-          first_ne = min(first_ne, j);
-          last_ne = max(last_ne, j);
-        }
-      }
-      first_lt = wave_reduce(first_lt, [](int x, int y) { return min(x, y); });
-      first_ne = wave_reduce(first_ne, [](int x, int y) { return min(x, y); });
-      last_ne = wave_reduce(last_ne, [](int x, int y) { return max(x, y); });
-      if (lane == 0) {
-        red[0][w] = first_lt;
-        red[1][w] = first_ne;
-        red[2][w] = last_ne;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kLocScanW; ++i) {
-      first_lt = min(first_lt, red[0][i]);
-      first_ne = min(first_ne, red[1][i]);
-      last_ne = max(last_ne, red[2][i]);
-    }
-    // the balancing bucket: the first whose last knot has g < k, else the last
-    const int J = first_lt != INT_MAX ? first_lt : last_ne;  // -1: empty band
-    if (J >= 0 && (int)threadIdx.x == J / kLocPer) {
-      const int u = J % kLocPer;
-#pragma unroll
-      for (int q = 0; q < kLocPer; ++q) {
-        if (q == u) {
-          sel_pa = before[q].a;
-          sel_ps = before[q].s;
-          sel_sa = after[q].a;
-          sel_ss = after[q].s;
-          sel_c = cnt[q];
-          sel_st = st0[q];
-        }
-      }
-    }
-    __syncthreads();
-    const int64_t cJ = J >= 0 ? (int64_t)sel_c : 0;
-    const int64_t sJ = J >= 0 ? (int64_t)sel_st : 0;
-    const Pre slo = J >= 0 ? Pre{sel_pa, sel_ps} : seed_lo;
-    const Suf shi = J >= 0 ? Suf{sel_sa, sel_ss} : seed_hi;
+    const BucketPick P = bucket_search<kLocT, kLocScanT, kLocPer>(g, cnt, seed_lo, seed_hi, cR, M, a.k, c);
+    const int J = P.J;
+    const int64_t cJ = P.cnt, sJ = P.start;
+    const Pre slo{P.lo_a, P.lo_s};
+    const Suf shi{P.hi_a, P.hi_s};
     const double cR_eff = (double)(M - sJ - cJ) + cR;
-    const bool first = J < 0 || J == first_ne;
-    const bool last = J < 0 || J == last_ne;
     uint32_t *kb = a.keys + row * a.cap + sJ;
     PartInfo part;
     part.nvalid = 0;
     part.above = (double)cJ + cR_eff;
     part.seed_lo = slo;
     part.seed_hi = shi;
-    part.first = first;
-    part.last = last;
+    part.first = P.first != 0;
+    part.last = P.last != 0;
     if (cJ <= (int64_t)kWaveBucket) {
       if (w == 0) {
         const double bb = cJ <= 4 * kWave ? wave_sort_solve<4>(kb, (int)cJ, part, a.k, a.t, c, a.cf)
@@ -638,17 +479,10 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       // a bucket of several tiles: sorted in place by the workgroup, its tile
       // aggregates, then locate over them
       const int shift = band_shift(S, a.bbits);
-      block_radix_sort<kLocT>(kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, L.fb.rk);
-      constexpr int TT = kLocT * kKpt;
-      TileAgg *ta = a.tagg + row * a.max_tiles;
-      for (int64_t t0 = 0; t0 < cJ; t0 += TT) {
-        float s[kKpt];
-        const int nv = load_sorted_at<kLocT>(kb, t0, cJ, 0u, s);
-        tile_aggregate<kLocT>(s, nv, c, a.cf, team, ta + t0 / TT);
-      }
-      const double bb = locate_sorted<kLocT>(kb, cJ, 0u, slo, shi, cR_eff, first, last, ta,
-                                             a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, a.k, a.t, c,
-                                             a.cf, team);
+      const double bb = sorted_range_solve<kLocT>(
+          kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, slo, shi, cR_eff, part.first,
+          part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, a.k, a.t,
+          c, a.cf, L.fb);
       if (threadIdx.x == 0) sel_b = bb;
     }
     __syncthreads();

@@ -60,16 +60,7 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
   // exclusive scan of the chunk sums: inside each DPP row of 16 lanes, then
   // the row totals (v_readlane), then the wave totals through LDS
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  uint32_t inc = csum;
-  inc += dpp<0x111>(inc);  // row_shr:1 (a lane before its row's start reads 0)
-  inc += dpp<0x112>(inc);
-  inc += dpp<0x114>(inc);
-  inc += dpp<0x118>(inc);
-  {
-    const uint32_t r0 = read_lane(inc, 15), r1 = read_lane(inc, 31), r2 = read_lane(inc, 47);
-    const int rw = lane >> 4;
-    inc += rw == 0 ? 0u : (rw == 1 ? r0 : (rw == 2 ? r0 + r1 : r0 + r1 + r2));
-  }
+  const uint32_t inc = wave_incl_scan(csum);
   if (lane == kWave - 1) wsum[w] = inc;
   __syncthreads();
   uint32_t before = 0u, total = 0u;

@@ -216,6 +216,16 @@ LDEV void row_suf_steps(Suf &inc, double c) {
     row_suf_steps<2 * OFF>(inc, c);
   }
 }
+// inclusive sum of v over the lanes up to this one (whole wave)
+LDEV uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<0x111>(v);  // row_shr:1 (a lane before its row's start reads 0)
+  v += dpp<0x112>(v);
+  v += dpp<0x114>(v);
+  v += dpp<0x118>(v);
+  const uint32_t r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row == 0 ? 0u : (row == 1 ? r0 : (row == 2 ? r0 + r1 : r0 + r1 + r2)));
+}
 // P-type scan over the wave: returns the inclusive value, *ex the exclusive
 LDEV Pre wave_scan(Pre x, double c, Pre *ex) {
   const int row = lane_id() >> 4;

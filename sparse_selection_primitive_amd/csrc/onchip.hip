@@ -14,8 +14,8 @@
 // Band solve (section 2.2, probabilistic bracketing, step 3): the same
 // sort + curve + root on the compacted middle band, seeded with the tail
 // sums of the streaming pass, followed by the certification of step 4.
+#include "bucket_dev.hpp"
 #include "filter_dev.hpp"
-#include "segment_dev.hpp"
 
 namespace lapsum {
 

@@ -1,7 +1,7 @@
 // Device routines of the full-sort solver shared by the one-workgroup
 // fallback, the on-chip band kernel (onchip.hip) and the bucketed band solve
-// (band.hip): tile loads, stable scatter of a tile, anchored aggregates of
-// sorted runs, and locate + closed-form root over a sorted range.
+// (band.hip): stable scatter of a tile, anchored aggregates of sorted runs,
+// and locate + closed-form root over a sorted range.
 // Method: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
 // section 2.2, full-sort solver.
 #pragma once
@@ -28,17 +28,21 @@ struct RankLds {
   uint32_t wsum[NW];
 };
 
+// Buckets of the one-workgroup fallback's key sets: counts, key extremes and
+// fixed-point sums anchored at the extremes.
+constexpr int kFallbackBucketBits = 11;
+constexpr int kFallbackBuckets = 1 << kFallbackBucketBits;
+struct BucketSelLds {
+  uint32_t cnt[kFallbackBuckets], kmx[kFallbackBuckets], kmn[kFallbackBuckets];
+  unsigned long long sp[kFallbackBuckets], ss[kFallbackBuckets];
+};
+
 template <int NT>
 union SegLds {
   RankLds<NT> rk;
   BlockTeamLds<NT, 1> tm;
+  BucketSelLds bs;
 };
-
-// ------------------------------------------------------------- row helpers
-LDEV bool seg_active(const SegArgs &a, int row) { return (a.st[row].flags & LAPSUM_FLAG_FALLBACK) != 0; }
-LDEV int64_t seg_len(const SegArgs &a, int row) { return seg_active(a, row) ? a.n : 0; }
-// four 8-bit digit passes A -> B -> A -> B: the sorted keys end in B
-LDEV const uint32_t *seg_final(const SegArgs &a) { return a.B; }
 
 template <int NT>
 LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
@@ -60,30 +64,7 @@ LDEV uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum) {
   return before + inc - v;
 }
 
-// key of element i of `row` read by digit pass `pass`
-LDEV uint32_t load_key(const SegArgs &a, int pass, int row, int64_t i) {
-  if (pass == 0) return key_of(a.r[(int64_t)row * a.n + i]);
-  const uint32_t *src = (pass & 1) ? a.A : a.B;
-  return src[(int64_t)row * a.stride + i];
-}
-LDEV uint32_t *pass_dst(const SegArgs &a, int pass) { return (pass & 1) ? a.B : a.A; }
-
 // ----------------------------------------------------------- tile routines
-// Keys of one tile, wave-striped: thread (w, lane) holds tile positions
-// w*64*16 + q*64 + lane, q = 0..15, which is also their stable order.
-template <int NT>
-LDEV void load_tile(const SegArgs &a, int pass, int row, int64_t t0, int64_t len, int shift,
-                    uint32_t (&key)[kKpt], int (&dig)[kKpt]) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int q = 0; q < kKpt; ++q) {
-    const int64_t gi = t0 + w * (kWave * kKpt) + q * kWave + lane;
-    const bool valid = gi < len;
-    key[q] = valid ? load_key(a, pass, row, gi) : 0u;
-    dig[q] = valid ? (int)((key[q] >> shift) & 255u) : 256;
-  }
-}
-
 // Stable scatter of one tile.  Thread d < 256 passes in `digit_base`, the
 // position in `dst` where this tile's keys of digit d start; it gets back the
 // number of this tile's keys of digit d.
@@ -159,11 +140,6 @@ LDEV int load_sorted_at(const uint32_t *src, int64_t t0, int64_t len, uint32_t k
   for (int e = 0; e < kKpt; ++e) s[e] = (e < nv) ? value_of(p[e] + kbase) : 0.0f;
   return nv;
 }
-template <int NT>
-LDEV int load_sorted(const SegArgs &a, int row, int64_t t0, int64_t len, float (&s)[kKpt]) {
-  return load_sorted_at<NT>(seg_final(a) + (int64_t)row * a.stride, t0, len, 0u, s);
-}
-
 // Anchored aggregates of a sorted run held blocked by a team (lane l holds
 // its elements l*E .. l*E+E-1, nv of them valid): P-type relative to the
 // run's last key (written by the team's last lane), S-type relative to its
@@ -271,55 +247,6 @@ LDEV double locate_sorted(const uint32_t *src, int64_t len, uint32_t kbase, Pre 
   part.first = first && tsel == 0;
   part.last = last && tsel >= nt - 1;
   return segment_solve<kKpt>(s, nv, part, k, t, c, cf, team);
-}
-
-// Per row of the full-sort path or the fallback: locate + root over the
-// whole sorted row.
-template <int NT>
-LDEV void locate_row(const SegArgs &a, int row, const BlockTeam<NT, 1> &team) {
-  const int64_t o = (int64_t)row * a.max_tiles;
-  const double b = locate_sorted<NT>(seg_final(a) + (int64_t)row * a.stride, seg_len(a, row), 0u,
-                                     Pre{0.0f, 0.0}, Suf{0.0f, 0.0}, 0.0, true, true, a.tagg + o, a.tpre + o,
-                                     a.tsuf + o, a.k, a.t, a.c, a.cf, team);
-  if (threadIdx.x == 0) a.st[row].b = b;
-  __syncthreads();
-}
-
-
-// The deterministic full-sort fallback for one row, run by a whole
-// workgroup of NT threads: four stable 8-bit digit passes through the key
-// buffers A -> B -> A -> B, tile aggregates, locate and root.
-template <int NT>
-LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
-  constexpr int TT = NT * kKpt;
-  __shared__ uint32_t h[256];
-  const int64_t len = a.n;
-  const int64_t ntiles = (len + TT - 1) / TT;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += NT) h[i] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < len; i += NT) atomicAdd(&h[(load_key(a, pass, row, i) >> shift) & 255u], 1u);
-    __syncthreads();
-    // running start of each digit, advanced tile by tile (thread d owns digit d)
-    uint32_t run = wg_excl_scan<NT>(threadIdx.x < 256 ? h[threadIdx.x] : 0u, L.rk.wsum);
-    uint32_t *dst = pass_dst(a, pass) + (int64_t)row * a.stride;
-    for (int64_t tile = 0; tile < ntiles; ++tile) {
-      uint32_t key[kKpt];
-      int dig[kKpt];
-      load_tile<NT>(a, pass, row, tile * TT, len, shift, key, dig);
-      const int vc = (int)min((int64_t)TT, len - tile * TT);
-      run += scatter_tile<NT>(key, dig, shift, vc, run, dst, L.rk);
-    }
-  }
-  BlockTeam<NT, 1> team(&L.tm);
-  for (int64_t tile = 0; tile < ntiles; ++tile) {
-    float s[kKpt];
-    const int nv = load_sorted<NT>(a, row, tile * TT, len, s);
-    tile_aggregate<NT>(s, nv, a.c, a.cf, team, a.tagg + (int64_t)row * a.max_tiles + tile);
-  }
-  __syncthreads();
-  locate_row<NT>(a, row, team);
 }
 
 }  // namespace lapsum

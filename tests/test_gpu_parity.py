@@ -347,6 +347,41 @@ def test_bracket_band_overflow_falls_back(L, O):
     assert np.all(fl & L.FLAG_OVERFLOW) and np.all(fl & L.FLAG_FALLBACK)
 
 
+def test_fallback_nested_buckets(L, O):
+    """A forced miss on a row whose root lies in a cluster far narrower than
+    the row's range: the fallback's first bucket holds most of the row, so it
+    descends two more levels (the last one with a single distinct key per
+    bucket); the result must match the oracle and repeat bitwise."""
+    g0 = np.random.Generator(np.random.PCG64(3701))
+    n = 2_000_000
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    idx = g0.choice(n, size=1_500_000, replace=False)
+    r[0, idx] = (1.0 + 1e-5 * g0.standard_normal(idx.size)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = float(np.sum(r > 1.0001)) + 700_000.5
+    opts = dict(path="bracket", bracket_override=(-20.0, -19.0), stats=True)
+    res, _, _ = full_check("fallback nested buckets", L, O, r, g, k, 1e-3, **opts)
+    assert res["stats"]["flags"][0].item() & L.FLAG_FALLBACK
+    again = run(L, r, k, 1e-3, g, **opts)
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(res[key], again[key]), key
+
+
+def test_fallback_heavy_ties_overflow(L, O):
+    """Quantised scores with a bracket around a huge run of equal values: the
+    band overflows, and the fallback's buckets near the root each hold one
+    repeated key."""
+    g0 = np.random.Generator(np.random.PCG64(3801))
+    n = 1_000_000
+    r = np.round(g0.standard_normal((1, n)) * 4.0).astype(np.float32) / 4.0
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = float(np.sum(r > 0.0)) + 1234.5  # inside the run of zeros
+    res, _, _ = full_check("fallback heavy ties", L, O, r, g, k, 0.01, path="bracket", band_capacity=4096,
+                           bracket_override=(-0.1, 0.1), stats=True)
+    fl = res["stats"]["flags"][0].item()
+    assert fl & L.FLAG_OVERFLOW and fl & L.FLAG_FALLBACK
+
+
 def test_bracket_loose_delta_many_seeds(L, O):
     """delta = 0.9 makes misses common; every row must still match."""
     from sparse_selection_primitive_amd import workloads
