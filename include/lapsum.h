@@ -15,8 +15,11 @@
  * closed-form root; and, for million-scale rows, probabilistic bracketing
  * (sample, binomial order-statistic bracket, one streaming pass that folds
  * out-of-bracket scores into tail sums and keeps the middle band, an exact
- * solve on the band, and certification with a deterministic full-sort
- * fallback when the bracket misses).
+ * solve on the band, and certification with a deterministic fallback when
+ * the bracket misses).  This library sorts only what the root needs: a
+ * bucket pass over the row (or band) locates the balancing bucket from
+ * order-free bucket sums, and only that bucket is sorted; the fallback nests
+ * the same selection over the whole row.
  *
  * Conventions shared by every entry point
  *   - Array arguments marked "device" are device pointers on the current HIP
@@ -70,13 +73,13 @@ typedef enum lapsum_path {
     LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
     LAPSUM_PATH_FULLSORT = 2, /* one radix (bucket) pass over the row, order-free bucket sums, locate,
                                  sort of the balancing bucket only, root + streaming apply */
-    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing with full-sort fallback */
+    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing with an exact whole-row fallback */
 } lapsum_path;
 
 /* Per-row flags in lapsum_row_stats.flags. */
 #define LAPSUM_FLAG_BRACKET 0x1     /* the bracketing path ran for this row */
 #define LAPSUM_FLAG_HIT 0x2         /* the first bracket held (certified) */
-#define LAPSUM_FLAG_FALLBACK 0x4    /* b came from the full-sort fallback */
+#define LAPSUM_FLAG_FALLBACK 0x4    /* b came from the exact whole-row fallback */
 #define LAPSUM_FLAG_OVERFLOW 0x8    /* the band exceeded its capacity (counted as a miss) */
 #define LAPSUM_FLAG_DEGENERATE 0x10 /* backward: every d_i was 0 in fp32, so dr = 0 and dk = 0 */
 

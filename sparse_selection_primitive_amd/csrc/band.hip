@@ -21,7 +21,7 @@
 //   band_locate_kernel   scan of the bucket aggregates between the tail
 //                        seeds, threshold curve at the bucket ends, the
 //                        balancing bucket, its sort and the root inside it,
-//                        certification, and the full-sort fallback of a row
+//                        certification, and the exact fallback of a row
 //                        whose bracket missed
 //
 // Every count is an integer, the bucket sums are fixed-point integer sums,

@@ -23,8 +23,8 @@ constexpr int kUnroll = 4;           // independent 16 B loads per thread per st
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
-// Arguments of the one-workgroup full-sort fallback (a row whose bracket
-// missed, or whose band overflowed, is sorted and solved in full).
+// Arguments of the one-workgroup exact fallback (a row whose bracket
+// missed, or whose band overflowed, is solved over all its scores).
 struct SegArgs {
   int rows;
   int64_t n;            // row length
