@@ -252,8 +252,6 @@ struct StageTimer {
   }
 };
 
-lapsum_status hip_status(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LAPSUM_ERR_HIP; }
-
 #define LAPSUM_TRY(expr)                       \
   do {                                         \
     hipError_t _e = (expr);                    \

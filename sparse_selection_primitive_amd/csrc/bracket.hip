@@ -401,7 +401,6 @@ __global__ __launch_bounds__(kSelThreads) void select_bucket_kernel(const float 
   const int64_t row = blockIdx.x;
   const float *X = samples + row * m;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  constexpr int kWaves = kSelThreads / kWave;
   {
     // bin starts of every group (16-bit, read as pairs): thread t reads
     // pair t & 511 of groups (t >> 9), (t >> 9) + 2, ...

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restri
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
 template <int NP>
-__global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int64_t rows, int n,
+__global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int n,
                                                                 double k, double t, float *__restrict__ p,
                                                                 double *__restrict__ b, lapsum_row_stats *stats) {
   constexpr int E = 16, LANES = NP / 16;
@@ -286,8 +286,7 @@ static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k,
 template <int NP>
 static hipError_t launch_fwd_block(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
                                    lapsum_row_stats *stats, hipStream_t s) {
-  hipLaunchKernelGGL((onchip_forward_block<NP>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, rows, n, k, t, p, b,
-                     stats);
+  hipLaunchKernelGGL((onchip_forward_block<NP>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, n, k, t, p, b, stats);
   return hipGetLastError();
 }
 
