@@ -15,11 +15,14 @@
  * closed-form root; and, for million-scale rows, probabilistic bracketing
  * (sample, binomial order-statistic bracket, one streaming pass that folds
  * out-of-bracket scores into tail sums and keeps the middle band, an exact
- * solve on the band, and certification with a deterministic fallback when
- * the bracket misses).  This library sorts only what the root needs: a
- * bucket pass over the row (or band) locates the balancing bucket from
- * order-free bucket sums, and only that bucket is sorted; the fallback nests
- * the same selection over the whole row.
+ * solve on the band, and certification; a bracket that fails it is widened
+ * and tried again).  This library sorts only what the root needs: a bucket
+ * pass over the row (or band) locates the balancing bucket from order-free
+ * bucket sums, and only that bucket is sorted.  A missed bracket is widened
+ * (wider order statistics of the same sample, one pass over the row by the
+ * workgroup that found the miss, the same bucket selection on the wider
+ * band); if every widened bracket fails too, a deterministic fallback nests
+ * the bucket selection over the whole row.
  *
  * Conventions shared by every entry point
  *   - Array arguments marked "device" are device pointers on the current HIP
@@ -33,8 +36,9 @@
  *     stream).  Outputs are valid once the stream reaches the call's end.
  *   - The returned status covers host-side argument checks and launch errors
  *     only.  Each call first clears any non-sticky HIP error left pending on
- *     the calling thread by earlier runtime calls.  Per-row outcomes (bracket hit/miss, fallback, degenerate
- *     backward) are reported through the optional `stats` array.
+ *     the calling thread by earlier runtime calls.  Per-row outcomes (bracket
+ *     hit/miss, widening, fallback, degenerate backward) are reported through
+ *     the optional `stats` array.
  *   - Scores must be finite; non-finite scores give unspecified outputs (the
  *     kernels still terminate).
  *   - Results are deterministic: the same inputs, options and seed give
@@ -73,15 +77,18 @@ typedef enum lapsum_path {
     LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
     LAPSUM_PATH_FULLSORT = 2, /* one radix (bucket) pass over the row, order-free bucket sums, locate,
                                  sort of the balancing bucket only, root + streaming apply */
-    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing with an exact whole-row fallback */
+    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing; a missed bracket is widened, then an
+                                 exact whole-row fallback */
 } lapsum_path;
 
 /* Per-row flags in lapsum_row_stats.flags. */
 #define LAPSUM_FLAG_BRACKET 0x1     /* the bracketing path ran for this row */
 #define LAPSUM_FLAG_HIT 0x2         /* the first bracket held (certified) */
 #define LAPSUM_FLAG_FALLBACK 0x4    /* b came from the exact whole-row fallback */
-#define LAPSUM_FLAG_OVERFLOW 0x8    /* the band exceeded its capacity (counted as a miss) */
+#define LAPSUM_FLAG_OVERFLOW 0x8    /* the first band exceeded its capacity (counted as a miss) */
 #define LAPSUM_FLAG_DEGENERATE 0x10 /* backward: every d_i was 0 in fp32, so dr = 0 and dk = 0 */
+#define LAPSUM_FLAG_WIDENED 0x20    /* the first bracket missed (or overflowed) and a widened
+                                       bracket held (certified); the stats describe it */
 
 /* Optional per-row diagnostics, written by lapsum_forward (all fields) and
  * lapsum_backward (flags |= LAPSUM_FLAG_DEGENERATE only).  Device memory. */
@@ -102,7 +109,7 @@ enum {
     LAPSUM_STAGE_SAMPLE = 2,     /* kernel-noised sample */
     LAPSUM_STAGE_SELECT = 3,     /* order statistics -> bracket */
     LAPSUM_STAGE_FILTER = 4,     /* streaming tail sums + band compaction */
-    LAPSUM_STAGE_BAND = 5,       /* band solve + certification (+ fallback of a missed row) */
+    LAPSUM_STAGE_BAND = 5,       /* band solve + certification (+ widening / fallback of a missed row) */
     LAPSUM_STAGE_FULLSORT = 6,   /* full-sort solve of whole rows (full-sort path) */
     LAPSUM_STAGE_APPLY = 7,      /* streaming Laplace-CDF apply */
     LAPSUM_STAGE_ONCHIP_BWD = 8, /* fused on-chip backward */
@@ -124,6 +131,13 @@ typedef struct lapsum_options {
     void *const *stage_events;      /* host array of 2*LAPSUM_STAGE_COUNT hipEvent_t or NULL;
                                        entries 2s and 2s+1 (if non-NULL) are recorded on the
                                        stream before and after stage s */
+    int32_t widen_steps;   /* bracketing: widened brackets tried after a miss before the
+                              whole-row fallback (section 2.2, step 4); step i uses the
+                              bracket indices for delta * 1e-6^i, skipped where they are
+                              no wider.  0 = 2, -1 = none, at most 4.  Rows whose bracket
+                              came from bracket_override have no sample and go straight
+                              to the fallback. */
+    int32_t reserved0;
 } lapsum_options;
 
 /* Resolved plan of a call (host-only query, no GPU needed). */

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "liblapsum.so")
 
 PATH_AUTO, PATH_ONCHIP, PATH_FULLSORT, PATH_BRACKET = 0, 1, 2, 3
 PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "fullsort": PATH_FULLSORT, "bracket": PATH_BRACKET}
-FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE = 0x1, 0x2, 0x4, 0x8, 0x10
+FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE, FLAG_WIDENED = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 ONCHIP_MAX_N = 8192
 (STAGE_ONCHIP_FWD, STAGE_INIT, STAGE_SAMPLE, STAGE_SELECT, STAGE_FILTER, STAGE_BAND, STAGE_FULLSORT,
  STAGE_APPLY, STAGE_ONCHIP_BWD, STAGE_BWD_REDUCE, STAGE_BWD_APPLY, STAGE_COUNT) = range(12)
@@ -49,7 +49,8 @@ class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("sample_log2", ctypes.c_int32), ("delta", ctypes.c_double),
                 ("seed", ctypes.c_uint64), ("band_capacity", ctypes.c_int64),
                 ("bracket_override", ctypes.POINTER(ctypes.c_double)),
-                ("stats", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("stats", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("widen_steps", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -106,7 +107,7 @@ def _check(rc: int, what: str):
 
 
 def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0, bracket_override=None,
-                 stats_ptr=None, stage_events=None):
+                 stats_ptr=None, stage_events=None, widen_steps=0):
     opt = Options()
     load_library().lapsum_options_init(ctypes.byref(opt))
     opt.path = PATHS[path] if isinstance(path, str) else int(path)
@@ -114,6 +115,7 @@ def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
     opt.delta = float(delta)
     opt.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     opt.band_capacity = int(band_capacity)
+    opt.widen_steps = int(widen_steps)
     keep = []
     if bracket_override is not None:
         arr = (ctypes.c_double * 2)(float(bracket_override[0]), float(bracket_override[1]))
@@ -187,7 +189,7 @@ def _as_rows(x, name):
 
 
 def lapsum_forward(r, k: float, t: float, *, path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
-                   bracket_override=None, stats=False, stage_events=None, out=None):
+                   bracket_override=None, stats=False, stage_events=None, out=None, widen_steps=0):
     """p, b (and per-row stats if stats=True) for scores r [rows, n] fp32 on GPU.
 
     p is fp32 [rows, n]; b is fp64 [rows].  Stats is an int/float dict of
@@ -202,7 +204,7 @@ def lapsum_forward(r, k: float, t: float, *, path="auto", sample_log2=0, delta=0
         b = torch.empty(rows, dtype=torch.float64, device=dev) if out is None else out[1]
         st = torch.empty(rows * ctypes.sizeof(RowStats), dtype=torch.uint8, device=dev) if stats else None
         opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
-                           st.data_ptr() if st is not None else None, stage_events)
+                           st.data_ptr() if st is not None else None, stage_events, widen_steps)
         nbytes = int(lib.lapsum_workspace_bytes(rows, n, float(k), float(t), ctypes.byref(opt)))
         wptr, wlen = _workspace(nbytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -280,13 +282,13 @@ class Operator:
     Outputs are written into caller-provided tensors."""
 
     def __init__(self, rows: int, n: int, k: float, t: float, device=None, stream=None, path="auto", seed=0,
-                 sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None):
+                 sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None, widen_steps=0):
         torch = _torch()
         self.lib = load_library()
         self.rows, self.n, self.k, self.t = int(rows), int(n), float(k), float(t)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
-                                stats_buf.data_ptr() if stats_buf is not None else None)
+                                stats_buf.data_ptr() if stats_buf is not None else None, widen_steps=widen_steps)
         nbytes = int(self.lib.lapsum_workspace_bytes(self.rows, self.n, self.k, self.t, ctypes.byref(self.opt)))
         self._ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device) if nbytes else None
         if self._ws is not None:

@@ -19,6 +19,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kOnchipMaxN = LAPSUM_ONCHIP_MAX_N;
 constexpr int64_t kFullsortMaxAutoN = (int64_t)1 << 20;
+constexpr int kDefaultWiden = 2;  // widened brackets tried after a miss, by default
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -88,6 +89,8 @@ struct Plan {
   int path = 0;
   int sample_log2 = 0;
   int64_t m = 0, lo = 0, hi = 0;
+  int nwiden = 0;  // widened brackets tried after a miss
+  int64_t wlo[kMaxWiden] = {}, whi[kMaxWiden] = {};
   int64_t cap = 0;  // band capacity per row
   bool band_onchip = false;
   // forward layout
@@ -103,14 +106,23 @@ struct Plan {
 };
 
 // Equal-tailed binomial order-statistic indices (host side of the
-// localisation step), with a one-entry cache per thread.
+// localisation step), with a small cache per thread (the first bracket and
+// its widened ones of the same call shape).
+struct BracketCacheEntry {
+  int64_t n = -1, m = -1, lo = 0, hi = 0;
+  double k = -1.0, delta = -1.0;
+};
+constexpr int kBracketCache = 8;
+
 lapsum_status bracket_indices(int64_t n, double k, int64_t m, double delta, int64_t *lo_out, int64_t *hi_out) {
-  thread_local int64_t c_n = -1, c_m = -1, c_lo = 0, c_hi = 0;
-  thread_local double c_k = -1.0, c_d = -1.0;
-  if (n == c_n && k == c_k && m == c_m && delta == c_d) {
-    *lo_out = c_lo;
-    *hi_out = c_hi;
-    return LAPSUM_OK;
+  thread_local BracketCacheEntry cache[kBracketCache];
+  thread_local int next = 0;
+  for (const BracketCacheEntry &e : cache) {
+    if (e.n == n && e.k == k && e.m == m && e.delta == delta) {
+      *lo_out = e.lo;
+      *hi_out = e.hi;
+      return LAPSUM_OK;
+    }
   }
   // N ~ Bin(m, q), q = 1 - k/n: log pmf by the ratio recurrence from j = 0
   const double lq = std::log1p(-k / (double)n);  // ln q
@@ -149,12 +161,14 @@ lapsum_status bracket_indices(int64_t n, double k, int64_t m, double delta, int6
     else
       break;
   }
-  c_n = n;
-  c_k = k;
-  c_m = m;
-  c_d = delta;
-  c_lo = lo;
-  c_hi = hi;
+  BracketCacheEntry &e = cache[next];
+  next = (next + 1) % kBracketCache;
+  e.n = n;
+  e.k = k;
+  e.m = m;
+  e.delta = delta;
+  e.lo = lo;
+  e.hi = hi;
   *lo_out = lo;
   *hi_out = hi;
   return LAPSUM_OK;
@@ -189,6 +203,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
   if (!(o.delta == 0.0 || (o.delta > 0.0 && o.delta < 1.0))) return LAPSUM_ERR_OPTION;
   if (o.band_capacity < 0) return LAPSUM_ERR_OPTION;
   if (o.bracket_override && !(o.bracket_override[0] < o.bracket_override[1])) return LAPSUM_ERR_OPTION;
+  if (o.widen_steps < -1 || o.widen_steps > kMaxWiden) return LAPSUM_ERR_OPTION;
 
   int path = o.path;
   if (path == LAPSUM_PATH_AUTO)
@@ -214,6 +229,23 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.m = (int64_t)1 << sl;
     const double delta = o.delta == 0.0 ? 1e-6 : o.delta;
     bracket_indices(n, k, P.m, delta, &P.lo, &P.hi);
+    // widened brackets: step i takes the indices for delta * 1e-6^i, kept
+    // only where they are wider than the bracket before them
+    const int steps = o.widen_steps == 0 ? kDefaultWiden : (o.widen_steps < 0 ? 0 : o.widen_steps);
+    int64_t plo = P.lo, phi = P.hi;
+    double d = delta;
+    for (int i = 0; i < steps; ++i) {
+      d *= 1e-6;
+      int64_t wl = 0, wh = 0;
+      bracket_indices(n, k, P.m, d, &wl, &wh);
+      if (wl < plo || wh > phi) {
+        P.wlo[P.nwiden] = wl;
+        P.whi[P.nwiden] = wh;
+        ++P.nwiden;
+        plo = wl;
+        phi = wh;
+      }
+    }
     if (o.band_capacity > 0) {
       P.cap = o.band_capacity;
     } else {
@@ -276,6 +308,10 @@ SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const f
   a.t = t;
   a.c = kLog2e / t;
   a.cf = (float)a.c;
+  a.samples = nullptr;
+  a.m = 0;
+  a.nwiden = 0;
+  for (int i = 0; i < kMaxWiden; ++i) a.wlo[i] = a.whi[i] = 0;
   return a;
 }
 
@@ -434,7 +470,16 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, ws + P.fpart, P.fgx, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
-    const SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
+    SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
+    if (!ovr) {  // a bracket given by the caller has no sample to widen from
+      fb.samples = reinterpret_cast<const float *>(ws + P.samples);
+      fb.m = P.m;
+      fb.nwiden = P.nwiden;
+      for (int i = 0; i < P.nwiden; ++i) {
+        fb.wlo[i] = P.wlo[i];
+        fb.whi[i] = P.whi[i];
+      }
+    }
     // the band kernels also run the fallback for rows whose bracket missed
     if (P.band_onchip)
       LAPSUM_TRY(launch_band_onchip(slots, ws + P.fpart, P.fgx, rows, n, P.cap, rs, k, t, fb, s));

@@ -32,6 +32,7 @@
 
 #include "bucket_dev.hpp"
 #include "filter_dev.hpp"
+#include "widen_dev.hpp"
 
 namespace lapsum {
 
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     }
   }
   __syncthreads();
-  if (sel_fb) fallback_row<kLocT>(fb, (int)row, L.fb);
+  if (sel_fb) missed_row<kLocT>(fb, (int)row, L.fb);
 }
 
 int band_count_blocks(int gx, int *group) {

@@ -258,16 +258,7 @@ LDEV double sorted_range_solve(uint32_t *kb, uint32_t *tb, int64_t cnt, uint32_t
 }
 
 // ----------------------------------------------------- one-workgroup fallback
-// The deterministic fallback for one row, run by a whole workgroup of NT
-// threads: the row's key range (one pass over the scores), then per level
-// the buckets of the current key set (counts and key extremes in one pass,
-// fixed-point sums in a second), the balancing bucket, and its keys gathered
-// into a key buffer.  A bucket of at most kFallbackSort keys (or of one
-// distinct key) is sorted and solved; a larger one becomes the next level's
-// set, seeded with everything around it.  Each level narrows the key range
-// by 2^11, so at most three levels follow the first.  The result is the
-// exact root of the whole row, independent of the bracket.
-constexpr int kFallbackSort = 1 << 16;
+constexpr int kFallbackSort = 1 << 16;  // largest balancing bucket sorted directly
 
 template <class F>
 LDEV void fallback_each_key(const SegArgs &a, int row, const uint32_t *src, int64_t len, int nt, F &&f) {
@@ -302,44 +293,29 @@ LDEV void fallback_each_key(const SegArgs &a, int row, const uint32_t *src, int6
   }
 }
 
+// Exact root over one key set and everything around it, by nested bucket
+// selection: per level the buckets of the current set (counts and key
+// extremes in one pass, fixed-point sums in a second), the balancing bucket,
+// and its keys gathered into a key buffer.  A bucket of at most
+// kFallbackSort keys (or of one distinct key) is sorted and solved; a larger
+// one becomes the next level's set, seeded with everything around it.  The
+// set is the row's scores (src == NULL, len = n) or len keys in src; kmin /
+// kmax bound its keys; slo / shi hold everything below / above it and cR
+// counts the elements above it.  Gathers go to the row's key buffer
+// `cur` (0: A, 1: B) first, then alternate.  Returns b on every thread.
 template <int NT>
-LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
+LDEV double bucket_set_solve(const SegArgs &a, int row, const uint32_t *src, int64_t len, int cur, uint32_t kmin,
+                             uint32_t kmax, Pre slo, Suf shi, double cR, SegLds<NT> &L) {
   constexpr int PER = kFallbackBuckets / NT;
   static_assert(PER * NT == kFallbackBuckets, "every bucket has a thread");
-  constexpr int NW = NT / kWave;
-  __shared__ uint32_t mm[2][NW];
-  __shared__ uint32_t ctr;
   BucketSelLds &B = L.bs;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t *buf[2] = {a.A + (int64_t)row * a.stride, a.B + (int64_t)row * a.stride};
   const double c = a.c;
-  // key range of the row
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  fallback_each_key(a, row, nullptr, a.n, NT, [&](uint32_t key) {
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
-  });
-  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
-  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
-  if (lane == 0) {
-    mm[0][w] = kmin;
-    mm[1][w] = kmax;
-  }
-  __syncthreads();
-  for (int i = 0; i < NW; ++i) {
-    kmin = min(kmin, mm[0][i]);
-    kmax = max(kmax, mm[1][i]);
-  }
-  const uint32_t *src = nullptr;  // the row's scores
-  int64_t len = a.n;
-  int cur = 0;                    // buffer the next gather writes
-  Pre slo{0.0f, 0.0};
-  Suf shi{0.0f, 0.0};
-  double cR = 0.0;
   double b = 0.0;
   for (;;) {
-    const uint32_t span = kmax - kmin;
+    const uint32_t span = len > 1 && kmax > kmin ? kmax - kmin : 0u;
     const int sbits = span == 0u ? 0 : 32 - __clz((int)span);
     const int shift = max(sbits - kFallbackBucketBits, 0);
     // counts and key extremes of the buckets
@@ -352,7 +328,7 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
     }
     __syncthreads();
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const uint32_t j = (key - kmin) >> shift;
+      const uint32_t j = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1));
       atomicAdd(&B.cnt[j], 1u);
       atomicMax(&B.kmx[j], key);
       atomicMin(&B.kmn[j], key);
@@ -360,7 +336,7 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
     __syncthreads();
     // fixed-point sums anchored at the bucket extremes
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const uint32_t j = (key - kmin) >> shift;
+      const uint32_t j = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1));
       const int fb = agg_frac_bits(B.cnt[j]);
       const double x = (double)value_of(key);
       atomicAdd(&B.sp[j], fixed_term(wexp(x - (double)value_of(B.kmx[j]), c), fb));
@@ -391,17 +367,17 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
       break;
     }
     // the keys of the balancing bucket into buf[cur]
-    if (threadIdx.x == 0) ctr = 0u;
+    if (threadIdx.x == 0) B.ctr = 0u;
     __syncthreads();
     const uint32_t J = (uint32_t)P.J;
     uint32_t *dst = buf[cur];
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const bool in = ((key - kmin) >> shift) == J;
+      const bool in = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1)) == J;
       const unsigned long long m = __ballot(in);
       if (m != 0ull) {
         const int leader = __ffsll((long long)m) - 1;
         uint32_t base = 0u;
-        if (lane == leader) base = atomicAdd(&ctr, (uint32_t)__popcll(m));
+        if (lane == leader) base = atomicAdd(&B.ctr, (uint32_t)__popcll(m));
         base = (uint32_t)__shfl((int)base, leader, kWave);
         if (in) dst[base + (uint32_t)__popcll(m & ltmask)] = key;
       }
@@ -424,6 +400,37 @@ LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
     shi = phi;
     cR = cR_eff;
   }
+  return b;
+}
+
+// The deterministic fallback for one row, run by a whole workgroup of NT
+// threads: the row's key range (one pass over the scores), then the nested
+// bucket selection over all of them.  Each level narrows the key range by
+// 2^11, so at most three levels follow the first.  The result is the exact
+// root of the whole row, independent of the bracket.
+template <int NT>
+LDEV void fallback_row(const SegArgs &a, int row, SegLds<NT> &L) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  // key range of the row (per-wave extremes through the widening scratch)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  fallback_each_key(a, row, nullptr, a.n, NT, [&](uint32_t key) {
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  });
+  kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+  kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+  if (lane == 0) {
+    L.wd.kext[0][w] = kmin;
+    L.wd.kext[1][w] = kmax;
+  }
+  __syncthreads();
+  for (int i = 0; i < NW; ++i) {
+    kmin = min(kmin, L.wd.kext[0][i]);
+    kmax = max(kmax, L.wd.kext[1][i]);
+  }
+  __syncthreads();
+  const double b = bucket_set_solve<NT>(a, row, nullptr, a.n, 0, kmin, kmax, Pre{0.0f, 0.0}, Suf{0.0f, 0.0}, 0.0, L);
   if (threadIdx.x == 0) a.st[row].b = b;
   __syncthreads();
 }

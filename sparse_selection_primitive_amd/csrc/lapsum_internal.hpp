@@ -23,8 +23,11 @@ constexpr int kUnroll = 4;           // independent 16 B loads per thread per st
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
-// Arguments of the one-workgroup exact fallback (a row whose bracket
-// missed, or whose band overflowed, is solved over all its scores).
+// Arguments of the one-workgroup treatment of a row whose bracket missed
+// (or whose band overflowed): up to `nwiden` widened brackets, each the
+// sample's order statistics of ranks wlo[i], whi[i] (1-based; 0 and m + 1
+// mean open ends), then the exact solve over all the row's scores.
+constexpr int kMaxWiden = 4;
 struct SegArgs {
   int rows;
   int64_t n;            // row length
@@ -38,6 +41,10 @@ struct SegArgs {
   RowState *st;         // [rows]
   double k, t, c;       // c = log2(e)/t
   float cf;
+  const float *samples; // [rows][m] noised sample of the bracketing path, or NULL (no widening)
+  int64_t m;
+  int nwiden;           // widening steps (0: none)
+  int64_t wlo[kMaxWiden], whi[kMaxWiden];
 };
 
 // Bucketed solve (bands too large for one workgroup, and whole rows of the

@@ -16,6 +16,7 @@
 // sums of the streaming pass, followed by the certification of step 4.
 #include "bucket_dev.hpp"
 #include "filter_dev.hpp"
+#include "widen_dev.hpp"
 
 namespace lapsum {
 
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   }
   if (threadIdx.x == 0) fall = (S.flags & LAPSUM_FLAG_FALLBACK) != 0;
   __syncthreads();
-  if (fall) fallback_row<kBandNT>(fb, (int)row, lds.full);
+  if (fall) missed_row<kBandNT>(fb, (int)row, lds.full);
 }
 
 hipError_t launch_band_onchip(const uint32_t *slots, const void *partials, int gx, int64_t rows, int64_t n,

@@ -35,6 +35,18 @@ constexpr int kFallbackBuckets = 1 << kFallbackBucketBits;
 struct BucketSelLds {
   uint32_t cnt[kFallbackBuckets], kmx[kFallbackBuckets], kmn[kFallbackBuckets];
   unsigned long long sp[kFallbackBuckets], ss[kFallbackBuckets];
+  uint32_t ctr;  // gather cursor
+};
+
+// Widening of a missed bracket: radix-select histograms of the sample (two
+// targets), and the per-wave partials of the row pass.
+struct WidenLds {
+  uint32_t hist[2][kFallbackBuckets];
+  uint32_t pick[2][3];  // bin, rank inside the bin, count: per target
+  double sum[2][16];
+  unsigned long long cnt[2][16];
+  uint32_t kext[2][16];
+  uint32_t ctr;
 };
 
 template <int NT>
@@ -42,6 +54,7 @@ union SegLds {
   RankLds<NT> rk;
   BlockTeamLds<NT, 1> tm;
   BucketSelLds bs;
+  WidenLds wd;
 };
 
 template <int NT>

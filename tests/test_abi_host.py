@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     # sizes fixed by the header's field lists (natural alignment on x86-64)
     assert ctypes.sizeof(L.RowStats) == 4 * 8 + 3 * 8 + 2 * 4
-    assert ctypes.sizeof(L.Options) == 4 + 4 + 8 + 8 + 8 + 8 + 8 + 8
+    assert ctypes.sizeof(L.Options) == 4 + 4 + 8 + 8 + 8 + 8 + 8 + 8 + 4 + 4
     assert ctypes.sizeof(L.PlanInfo) == 4 + 4 + 4 * 8 + 4 + 4 + 8 + 8
 
 

@@ -228,18 +228,26 @@ def test_fullsort_tiny_temperature(L, O, k):
 
 
 # ---------------------------------------------------------- bracketing path
+def _same_end(got, want):
+    return got == want if math.isinf(want) else abs(got - want) <= 2.5e-7 * abs(want) + 1e-30
+
+
 def check_bracket_stats(name, L, O, r, k, t, stats, seed, m_log2=None, delta=1e-6):
+    """Bracket ends against the oracle's own sample and order statistics (a
+    row flagged WIDENED: those of a widening step, delta * 1e-6^s), then the
+    exact tails and counts of the reported bracket."""
     from oracle import bracket as ob
     rows, n = r.shape
     plan = L.plan(rows, n, k, t, path="bracket", seed=seed, sample_log2=m_log2 or 0, delta=delta)
     m = plan["m"]
+    flags = stats["flags"].numpy()
     for i in range(rows):
-        a_lo, a_hi, lo, hi = ob.bracket(r[i], k, t, m, delta, seed, row=i)
-        for got, want in ((stats["a_lo"][i].item(), a_lo), (stats["a_hi"][i].item(), a_hi)):
-            if math.isinf(want):
-                assert got == want
-            else:
-                assert abs(got - want) <= 2.5e-7 * abs(want) + 1e-30, (name, i, got, want)
+        deltas = [delta]
+        if flags[i] & L.FLAG_WIDENED:
+            deltas = [delta * 1e-6, delta * 1e-6 * 1e-6]
+        got = (stats["a_lo"][i].item(), stats["a_hi"][i].item())
+        cands = [ob.bracket(r[i], k, t, m, d, seed, row=i)[:2] for d in deltas]
+        assert any(_same_end(got[0], c[0]) and _same_end(got[1], c[1]) for c in cands), (name, i, got, cands)
         ts = O.tail_sums(r[i], stats["a_lo"][i].item(), stats["a_hi"][i].item(), t)
         assert stats["count_lo"][i].item() == ts["c_L"]
         assert stats["count_hi"][i].item() == ts["c_R"]
@@ -339,12 +347,20 @@ def test_bracket_forced_miss_falls_back(L, O):
 
 
 def test_bracket_band_overflow_falls_back(L, O):
+    """A band over its capacity is a miss: with widening switched off the row
+    takes the whole-row fallback; by default a widened bracket (whose band
+    goes to the row's key buffer, not the capacity) rescues it."""
     from sparse_selection_primitive_amd import workloads
     w = workloads.coder(rows=2, n=65536)
-    res, _, _ = full_check("band overflow", L, O, w.r, None, w.k, w.t, path="bracket", band_capacity=16,
-                           stats=True)
+    res, _, _ = full_check("band overflow, no widening", L, O, w.r, None, w.k, w.t, path="bracket",
+                           band_capacity=16, widen_steps=-1, stats=True)
     fl = res["stats"]["flags"].numpy()
     assert np.all(fl & L.FLAG_OVERFLOW) and np.all(fl & L.FLAG_FALLBACK)
+    res, _, _ = full_check("band overflow, widened", L, O, w.r, w.g, w.k, w.t, path="bracket",
+                           band_capacity=16, stats=True)
+    fl = res["stats"]["flags"].numpy()
+    assert np.all(fl & L.FLAG_OVERFLOW) and np.all(fl & L.FLAG_WIDENED)
+    assert not np.any(fl & (L.FLAG_FALLBACK | L.FLAG_HIT))
 
 
 def test_fallback_nested_buckets(L, O):
@@ -383,17 +399,89 @@ def test_fallback_heavy_ties_overflow(L, O):
 
 
 def test_bracket_loose_delta_many_seeds(L, O):
-    """delta = 0.9 makes misses common; every row must still match."""
+    """delta = 0.9 makes misses common; every row must still match, through
+    the whole-row fallback when widening is off."""
     from sparse_selection_primitive_amd import workloads
     w = workloads.coder(rows=8, n=65536)
     p_or, b_or = O.forward(w.r, w.k, w.t)
     misses = 0
     for seed in range(6):
-        res = run(L, w.r, w.k, w.t, path="bracket", delta=0.9, seed=seed, stats=True)
+        res = run(L, w.r, w.k, w.t, path="bracket", delta=0.9, seed=seed, widen_steps=-1, stats=True)
         check_forward(f"delta=0.9 seed={seed}", w.k, w.t, res["p"], res["b"], p_or, b_or)
         misses += int(np.sum(res["stats"]["flags"].numpy() & L.FLAG_FALLBACK != 0))
     log(f"  fallbacks over 48 rows: {misses}")
     assert misses > 0
+
+
+def check_widened_rows(name, L, O, r, k, t, stats, seed, delta):
+    """Rows flagged WIDENED report the bracket of a widening step (the
+    sample's order statistics at the ranks for delta * 1e-6^i) and the exact
+    tails and counts of that bracket."""
+    from oracle import bracket as ob
+    rows, n = r.shape
+    m = L.plan(rows, n, k, t, path="bracket", seed=seed, delta=delta)["m"]
+    fl = stats["flags"].numpy()
+    widened = np.nonzero(fl & L.FLAG_WIDENED)[0]
+    for i in widened:
+        got = (stats["a_lo"][i].item(), stats["a_hi"][i].item())
+        cands = [ob.bracket(r[i], k, t, m, d, seed, row=int(i))[:2] for d in (delta * 1e-6, delta * 1e-6 * 1e-6)]
+        assert any(_same_end(got[0], c[0]) and _same_end(got[1], c[1]) for c in cands), (name, i, got, cands)
+        ts = O.tail_sums(r[i], got[0], got[1], t)
+        assert stats["count_lo"][i].item() == ts["c_L"] and stats["count_hi"][i].item() == ts["c_R"]
+        assert stats["band"][i].item() == ts["M"]
+        for key, ref in (("tail_lo", ts["S_L"]), ("tail_hi", ts["S_R"])):
+            assert abs(stats[key][i].item() - ref) <= 1e-5 * abs(ref) + 1e-30, (name, key, i)
+    return len(widened)
+
+
+@pytest.mark.parametrize("band_capacity", [0, 65536])
+def test_widening_rescues_missed_brackets(L, O, band_capacity):
+    """Section 2.2, step 4: a bracket that fails certification is widened
+    and tried again before any whole-row fallback.  delta = 0.9 makes first
+    brackets miss often; the widened ones (delta * 1e-6) hold.  On-chip band
+    solve (capacity derived, <= 8192) and bucketed band solve (capacity
+    65536) both hand their misses to the widening step."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.coder(rows=8, n=65536)
+    p_or, b_or = O.forward(w.r, w.k, w.t)
+    widened = 0
+    for seed in range(4):
+        opts = dict(path="bracket", delta=0.9, seed=seed, band_capacity=band_capacity, stats=True)
+        res = run(L, w.r, w.k, w.t, w.g, **opts)
+        name = f"widening seed={seed} cap={band_capacity}"
+        check_forward(name, w.k, w.t, res["p"], res["b"], p_or, b_or)
+        check_budget(name, w.k, res["p"])
+        dr_or, dk_or = O.backward(w.r, b_or, w.g, w.t)
+        check_backward(name, w.r, b_or, w.g, w.t, res["dr"], res["dk"], dr_or, dk_or)
+        fl = res["stats"]["flags"].numpy()
+        assert np.all((fl & L.FLAG_HIT) | (fl & L.FLAG_WIDENED)), fl
+        assert not np.any(fl & L.FLAG_FALLBACK), fl
+        widened += check_widened_rows(name, L, O, w.r, w.k, w.t, res["stats"], seed, 0.9)
+        again = run(L, w.r, w.k, w.t, w.g, **opts)
+        for key in ("p", "b", "dr", "dk"):
+            assert np.array_equal(res[key], again[key]), (name, key)
+    log(f"  widened rows over 32: {widened}")
+    assert widened > 0
+
+
+def test_widening_large_row(L, O):
+    """A 3,317,760-score row (|Laplace| magnitudes, k = 600) whose first
+    bracket misses: the workgroup that found the miss selects the widened
+    bracket from the sample, streams the row once and solves the wider band."""
+    from sparse_selection_primitive_amd import workloads
+    w = workloads.attack()
+    p_or, b_or = O.forward(w.r, w.k, w.t)
+    hit_widened = False
+    for seed in range(12):
+        res = run(L, w.r, w.k, w.t, path="bracket", delta=0.95, seed=seed, stats=True)
+        fl = res["stats"]["flags"][0].item()
+        assert fl & (L.FLAG_HIT | L.FLAG_WIDENED) and not fl & L.FLAG_FALLBACK, fl
+        if fl & L.FLAG_WIDENED:
+            check_forward(f"widened attack seed={seed}", w.k, w.t, res["p"], res["b"], p_or, b_or)
+            check_widened_rows("widened attack", L, O, w.r, w.k, w.t, res["stats"], seed, 0.95)
+            hit_widened = True
+            break
+    assert hit_widened
 
 
 def test_bracket_large_band_path(L, O):
