@@ -516,6 +516,27 @@ def test_bucket_band_multirow(L, O):
         assert np.array_equal(res[key], again[key]), key
 
 
+def test_bracket_batched_large_rows(L, O):
+    """Bracketing over a batch of million-scale rows of different shapes
+    (normal, |Laplace|, two-component mixture, uniform): one sample, filter
+    and band solve per row in the same launches; every row certified, bracket
+    ends and tails against the oracle, full parity."""
+    g0 = np.random.Generator(np.random.PCG64(3901))
+    rows, n = 4, 2_500_000
+    r = np.empty((rows, n), dtype=np.float32)
+    r[0] = g0.standard_normal(n)
+    r[1] = np.abs(g0.laplace(0.0, 1.0, n))
+    mix = g0.random(n) < 0.1
+    r[2] = np.where(mix, 3.0 + 0.5 * g0.standard_normal(n), g0.standard_normal(n))
+    r[3] = g0.random(n) * 10.0 - 5.0
+    g = g0.standard_normal((rows, n)).astype(np.float32)
+    k, t = 1000.0, 1e-3
+    res, _, _ = full_check("batched large rows", L, O, r, g, k, t, path="bracket", seed=7, stats=True)
+    fl = res["stats"]["flags"].numpy()
+    assert np.all(fl & (L.FLAG_HIT | L.FLAG_WIDENED)) and not np.any(fl & L.FLAG_FALLBACK), fl
+    check_bracket_stats("batched large rows", L, O, r, k, t, res["stats"], seed=7)
+
+
 @pytest.mark.parametrize("step", [1.0 / 64, 1.0 / 512])
 def test_bucket_band_quantized_ties(L, O, step):
     """Scores on a grid: each bucket holds whole runs of equal keys, 1.5K to
