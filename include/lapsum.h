@@ -89,6 +89,7 @@ typedef enum lapsum_path {
 #define LAPSUM_FLAG_DEGENERATE 0x10 /* backward: every d_i was 0 in fp32, so dr = 0 and dk = 0 */
 #define LAPSUM_FLAG_WIDENED 0x20    /* the first bracket missed (or overflowed) and a widened
                                        bracket held (certified); the stats describe it */
+#define LAPSUM_FLAG_INVALID 0x40    /* the row's per-row k or t was out of range: its outputs are NaN */
 
 /* Optional per-row diagnostics, written by lapsum_forward (all fields) and
  * lapsum_backward (flags |= LAPSUM_FLAG_DEGENERATE only).  Device memory. */
@@ -138,6 +139,15 @@ typedef struct lapsum_options {
                               came from bracket_override have no sample and go straight
                               to the fallback. */
     int32_t reserved0;
+    const double *k_rows;  /* device [rows] or NULL: a budget per row (the k argument is then
+                              not used).  Values must satisfy 0 < k_i < n; a row whose value
+                              does not gets NaN outputs and LAPSUM_FLAG_INVALID. */
+    const double *t_rows;  /* device [rows] or NULL: a temperature per row (the t argument is
+                              then not used), 0 < t_i < inf, likewise.  lapsum_backward reads
+                              it too.  With k_rows or t_rows the bracketing path is not
+                              available (its sample indices are set per k on the host): AUTO
+                              takes the full-sort path above 8192 scores, and a forced
+                              LAPSUM_PATH_BRACKET is LAPSUM_ERR_PATH. */
 } lapsum_options;
 
 /* Resolved plan of a call (host-only query, no GPU needed). */

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "liblapsum.so")
 
 PATH_AUTO, PATH_ONCHIP, PATH_FULLSORT, PATH_BRACKET = 0, 1, 2, 3
 PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "fullsort": PATH_FULLSORT, "bracket": PATH_BRACKET}
-FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE, FLAG_WIDENED = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
+FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE, FLAG_WIDENED, FLAG_INVALID = (
+    0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40)
 ONCHIP_MAX_N = 8192
 (STAGE_ONCHIP_FWD, STAGE_INIT, STAGE_SAMPLE, STAGE_SELECT, STAGE_FILTER, STAGE_BAND, STAGE_FULLSORT,
  STAGE_APPLY, STAGE_ONCHIP_BWD, STAGE_BWD_REDUCE, STAGE_BWD_APPLY, STAGE_COUNT) = range(12)
@@ -50,7 +51,8 @@ class Options(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("band_capacity", ctypes.c_int64),
                 ("bracket_override", ctypes.POINTER(ctypes.c_double)),
                 ("stats", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
-                ("widen_steps", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
+                ("widen_steps", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k_rows", ctypes.c_void_p), ("t_rows", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -107,7 +109,7 @@ def _check(rc: int, what: str):
 
 
 def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0, bracket_override=None,
-                 stats_ptr=None, stage_events=None, widen_steps=0):
+                 stats_ptr=None, stage_events=None, widen_steps=0, k_rows_ptr=None, t_rows_ptr=None):
     opt = Options()
     load_library().lapsum_options_init(ctypes.byref(opt))
     opt.path = PATHS[path] if isinstance(path, str) else int(path)
@@ -116,6 +118,8 @@ def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
     opt.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     opt.band_capacity = int(band_capacity)
     opt.widen_steps = int(widen_steps)
+    opt.k_rows = k_rows_ptr
+    opt.t_rows = t_rows_ptr
     keep = []
     if bracket_override is not None:
         arr = (ctypes.c_double * 2)(float(bracket_override[0]), float(bracket_override[1]))
@@ -188,27 +192,45 @@ def _as_rows(x, name):
     return x.contiguous()
 
 
-def lapsum_forward(r, k: float, t: float, *, path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
+def _per_row(x, rows: int, dev, name: str):
+    """A per-row parameter tensor as a contiguous float64 [rows] tensor on
+    dev (None for a scalar)."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        return None
+    if x.numel() != rows:
+        raise LapsumError(f"{name} must be a scalar or hold one value per row ({rows})")
+    return x.detach().reshape(rows).to(device=dev, dtype=torch.float64).contiguous()
+
+
+def lapsum_forward(r, k, t, *, path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
                    bracket_override=None, stats=False, stage_events=None, out=None, widen_steps=0):
     """p, b (and per-row stats if stats=True) for scores r [rows, n] fp32 on GPU.
 
-    p is fp32 [rows, n]; b is fp64 [rows].  Stats is an int/float dict of
-    per-row tensors (bracket ends, tail sums, counts, band size, flags)."""
+    k and t are floats, or tensors with one value per row (on-chip and
+    full-sort paths).  p is fp32 [rows, n]; b is fp64 [rows].  Stats is an
+    int/float dict of per-row tensors (bracket ends, tail sums, counts, band
+    size, flags)."""
     torch = _torch()
     lib = load_library()
     r2 = _as_rows(r, "r")
     rows, n = r2.shape
     dev = r2.device
     with torch.cuda.device(dev):
+        kr, tr = _per_row(k, rows, dev, "k"), _per_row(t, rows, dev, "t")
+        ks = 0.0 if kr is not None else float(k)
+        ts = 0.0 if tr is not None else float(t)
         p = torch.empty_like(r2) if out is None else out[0]
         b = torch.empty(rows, dtype=torch.float64, device=dev) if out is None else out[1]
         st = torch.empty(rows * ctypes.sizeof(RowStats), dtype=torch.uint8, device=dev) if stats else None
         opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
                            st.data_ptr() if st is not None else None, stage_events, widen_steps)
-        nbytes = int(lib.lapsum_workspace_bytes(rows, n, float(k), float(t), ctypes.byref(opt)))
+        opt.k_rows = kr.data_ptr() if kr is not None else None
+        opt.t_rows = tr.data_ptr() if tr is not None else None
+        nbytes = int(lib.lapsum_workspace_bytes(rows, n, ks, ts, ctypes.byref(opt)))
         wptr, wlen = _workspace(nbytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.lapsum_forward(r2.data_ptr(), rows, n, float(k), float(t), p.data_ptr(), b.data_ptr(),
+        rc = lib.lapsum_forward(r2.data_ptr(), rows, n, ks, ts, p.data_ptr(), b.data_ptr(),
                                 wptr, wlen, ctypes.byref(opt), stream)
         _check(rc, "lapsum_forward")
     if r.dim() == 1:
@@ -227,8 +249,9 @@ def decode_stats(buf, rows: int) -> dict:
     return {f: torch.tensor(v) for f, v in out.items()}
 
 
-def lapsum_backward(g, p, b, t: float, *, stats_buf=None, stage_events=None, out=None):
-    """dr [rows, n] fp32 and dk [rows] fp32: the analytic VJP of the forward."""
+def lapsum_backward(g, p, b, t, *, stats_buf=None, stage_events=None, out=None):
+    """dr [rows, n] fp32 and dk [rows] fp32: the analytic VJP of the forward
+    (t a float or one value per row, as in the forward)."""
     torch = _torch()
     lib = load_library()
     g2 = _as_rows(g, "g")
@@ -242,12 +265,15 @@ def lapsum_backward(g, p, b, t: float, *, stats_buf=None, stage_events=None, out
     with torch.cuda.device(dev):
         dr = torch.empty_like(g2) if out is None else out[0]
         dk = torch.empty(rows, dtype=torch.float32, device=dev) if out is None else out[1]
+        tr = _per_row(t, rows, dev, "t")
+        ts = 1.0 if tr is not None else float(t)
         opt = make_options(stats_ptr=stats_buf.data_ptr() if stats_buf is not None else None,
                            stage_events=stage_events)
-        nbytes = int(lib.lapsum_workspace_bytes(rows, n, 0.5 * n, float(t), None))
+        opt.t_rows = tr.data_ptr() if tr is not None else None
+        nbytes = int(lib.lapsum_workspace_bytes(rows, n, 0.5 * n, ts, None))
         wptr, wlen = _workspace(nbytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.lapsum_backward(g2.data_ptr(), p2.data_ptr(), b.contiguous().data_ptr(), rows, n, float(t),
+        rc = lib.lapsum_backward(g2.data_ptr(), p2.data_ptr(), b.contiguous().data_ptr(), rows, n, ts,
                                  dr.data_ptr(), dk.data_ptr(), wptr, wlen, ctypes.byref(opt), stream)
         _check(rc, "lapsum_backward")
     if g.dim() == 1:
@@ -255,24 +281,33 @@ def lapsum_backward(g, p, b, t: float, *, stats_buf=None, stage_events=None, out
     return dr, dk
 
 
-def soft_topk(r, k: float, t: float, **kw):
-    """Differentiable soft top-k: autograd wrapper over the two entry points."""
+def soft_topk(r, k, t, **kw):
+    """Differentiable soft top-k: autograd wrapper over the two entry points.
+
+    k may be a float or a tensor with one budget per row; a tensor k that
+    requires grad receives dk, the derivative of the loss with respect to each
+    row's budget.  t (float or one per row) gets no gradient."""
     torch = _torch()
 
     class _LapSum(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, x):
-            p, b = lapsum_forward(x, k, t, **kw)
+        def forward(ctx, x, kk):
+            p, b = lapsum_forward(x, kk if kk is not None else k, t, **kw)
             ctx.save_for_backward(p, b)
+            ctx.k_meta = None if kk is None else (kk.shape, kk.dtype, kk.device)
             return p
 
         @staticmethod
         def backward(ctx, gp):
             p, b = ctx.saved_tensors
-            dr, _ = lapsum_backward(gp.contiguous(), p, b, t)
-            return dr
+            dr, dk = lapsum_backward(gp.contiguous(), p, b, t)
+            gk = None
+            if ctx.k_meta is not None and ctx.needs_input_grad[1]:
+                shape, dtype, device = ctx.k_meta
+                gk = dk.to(device=device, dtype=dtype).reshape(shape)
+            return dr, gk
 
-    return _LapSum.apply(r)
+    return _LapSum.apply(r, k if isinstance(k, torch.Tensor) else None)
 
 
 class Operator:

@@ -192,12 +192,14 @@ void bwd_layout(int64_t rows, int64_t n, Plan &P) {
 }
 
 lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsum_options *opt, Plan &P) {
-  lapsum_status st = check_common(rows, n, t);
-  if (st != LAPSUM_OK) return st;
-  if (!std::isfinite(k) || !(k > 0.0) || !(k < (double)n)) return LAPSUM_ERR_K;
   lapsum_options o;
   lapsum_options_init(&o);
   if (opt) o = *opt;
+  // per-row values replace the scalars, which are then neither used nor checked
+  const bool per_row = o.k_rows != nullptr || o.t_rows != nullptr;
+  lapsum_status st = check_common(rows, n, o.t_rows ? 1.0 : t);
+  if (st != LAPSUM_OK) return st;
+  if (!o.k_rows && (!std::isfinite(k) || !(k > 0.0) || !(k < (double)n))) return LAPSUM_ERR_K;
   if (o.path < LAPSUM_PATH_AUTO || o.path > LAPSUM_PATH_BRACKET) return LAPSUM_ERR_OPTION;
   if (o.sample_log2 != 0 && (o.sample_log2 < 4 || o.sample_log2 > 20)) return LAPSUM_ERR_OPTION;
   if (!(o.delta == 0.0 || (o.delta > 0.0 && o.delta < 1.0))) return LAPSUM_ERR_OPTION;
@@ -207,8 +209,11 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
 
   int path = o.path;
   if (path == LAPSUM_PATH_AUTO)
-    path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP : (n <= kFullsortMaxAutoN ? LAPSUM_PATH_FULLSORT : LAPSUM_PATH_BRACKET);
+    path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP
+                            : (n <= kFullsortMaxAutoN || per_row ? LAPSUM_PATH_FULLSORT : LAPSUM_PATH_BRACKET);
   if (path == LAPSUM_PATH_ONCHIP && n > kOnchipMaxN) return LAPSUM_ERR_PATH;
+  // the bracket's sample indices are set per k on the host
+  if (path == LAPSUM_PATH_BRACKET && per_row) return LAPSUM_ERR_PATH;
   P.path = path;
 
   Layout F;
@@ -316,9 +321,10 @@ SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const f
 }
 
 BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots, uint32_t *offs,
-                   double k, double t, const float *r, int64_t n) {
+                   double k, double t, const float *r, int64_t n, RowParams rp) {
   const BandRegions &R = P.bnd;
   BandArgs a;
+  a.rp = rp;
   a.rows = (int)rows;
   a.gx = P.fgx;
   a.group = R.group;
@@ -427,13 +433,14 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const StageTimer tm{o.stage_events, s};
   char *ws = reinterpret_cast<char *>(workspace);
+  const RowParams rp{o.k_rows, o.t_rows};
   // Launch errors are read back with hipGetLastError(); drop any non-sticky
   // error an earlier, unrelated runtime call left pending on this thread.
   (void)hipGetLastError();
 
   if (P.path == LAPSUM_PATH_ONCHIP) {
     tm.mark(LAPSUM_STAGE_ONCHIP_FWD, 0);
-    LAPSUM_TRY(launch_onchip_forward(r, rows, (int)n, k, t, p, b, o.stats, s));
+    LAPSUM_TRY(launch_onchip_forward(r, rows, (int)n, k, t, rp, p, b, o.stats, s));
     tm.mark(LAPSUM_STAGE_ONCHIP_FWD, 1);
     return LAPSUM_OK;
   }
@@ -445,7 +452,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     tm.mark(LAPSUM_STAGE_INIT, 1);
     tm.mark(LAPSUM_STAGE_FULLSORT, 0);
     const SegArgs none{};  // full rows have no bracket, so no fallback
-    LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, nullptr, nullptr, k, t, r, n), none, s));
+    LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, nullptr, nullptr, k, t, r, n, rp), none, s));
     tm.mark(LAPSUM_STAGE_FULLSORT, 1);
   } else {
     const double *ovr = o.bracket_override;
@@ -484,11 +491,11 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     if (P.band_onchip)
       LAPSUM_TRY(launch_band_onchip(slots, ws + P.fpart, P.fgx, rows, n, P.cap, rs, k, t, fb, s));
     else
-      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t, nullptr, n), fb, s));
+      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t, nullptr, n, rp), fb, s));
     tm.mark(LAPSUM_STAGE_BAND, 1);
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);
-  LAPSUM_TRY(launch_apply(r, rows, n, rs, t, p, b, s));
+  LAPSUM_TRY(launch_apply(r, rows, n, rs, t, rp, p, b, s));
   tm.mark(LAPSUM_STAGE_APPLY, 1);
   if (o.stats) LAPSUM_TRY(launch_copy_stats(rs, rows, o.stats, s));
   return LAPSUM_OK;
@@ -497,9 +504,13 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
 lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
                               float *dr, float *dk, void *workspace, size_t workspace_bytes,
                               const lapsum_options *opt, void *stream) {
-  lapsum_status st0 = check_common(rows, n, t);
+  lapsum_options o;
+  lapsum_options_init(&o);
+  if (opt) o = *opt;
+  lapsum_status st0 = check_common(rows, n, o.t_rows ? 1.0 : t);
   if (st0 != LAPSUM_OK) return st0;
   if (!g || !p || !b || !dr || !dk) return LAPSUM_ERR_NULL;
+  const RowParams rp{nullptr, o.t_rows};
   Plan P;
   bwd_layout(rows, n, P);
   if (P.bwd_bytes > 0) {
@@ -507,15 +518,12 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
     if (workspace_bytes < P.bwd_bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
       return LAPSUM_ERR_WORKSPACE;
   }
-  lapsum_options o;
-  lapsum_options_init(&o);
-  if (opt) o = *opt;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const StageTimer tm{o.stage_events, s};
   (void)hipGetLastError();  // see lapsum_forward
   if (onchip_backward_supported(n)) {
     tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 0);
-    LAPSUM_TRY(launch_onchip_backward(g, p, rows, (int)n, t, dr, dk, o.stats, s));
+    LAPSUM_TRY(launch_onchip_backward(g, p, rows, (int)n, t, rp, dr, dk, o.stats, s));
     tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 1);
     return LAPSUM_OK;
   }
@@ -524,7 +532,7 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, ws + P.bpart, P.bgx, s));
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 1);
   tm.mark(LAPSUM_STAGE_BWD_APPLY, 0);
-  LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, ws + P.bpart, P.bgx, t, dr, dk, o.stats, s));
+  LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, ws + P.bpart, P.bgx, t, rp, dr, dk, o.stats, s));
   tm.mark(LAPSUM_STAGE_BWD_APPLY, 1);
   return LAPSUM_OK;
 }

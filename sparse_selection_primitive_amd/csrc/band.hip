@@ -43,6 +43,20 @@ static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of th
 
 LDEV bool band_active(const RowState &S) { return !(S.flags & LAPSUM_FLAG_OVERFLOW); }
 
+// Budget, temperature and c = log2(e)/t of one row: the call's, or the
+// row's own in full-row mode (false: per-row values out of range, replaced).
+LDEV bool band_row_params(const BandArgs &a, int64_t row, double &k, double &t, double &c, float &cf) {
+  k = a.k;
+  t = a.t;
+  c = a.c;
+  cf = a.cf;
+  if (!a.rp.any()) return true;
+  const bool ok = row_params(a.rp.k, a.rp.t, row, a.n, k, t);
+  c = kLog2e / t;
+  cf = (float)c;
+  return ok;
+}
+
 LDEV int band_shift(const RowState &S, int bbits) {
   const uint32_t span = (S.band > 1 && S.kmax > S.kmin) ? S.kmax - S.kmin : 0u;
   const int bits = span == 0u ? 0 : 32 - __clz((int)span);
@@ -379,6 +393,9 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
   const uint32_t *kb = a.keys + row * a.cap + bst;
   TileAgg *out = a.bagg + o + j;
   const int tl = threadIdx.x & (kAggTeam - 1);
+  double rk, rt, c;
+  float rcf;
+  band_row_params(a, row, rk, rt, c, rcf);
   if (threadIdx.x == 0) big = 0u;
   __syncthreads();
   if (cnt == 0) {
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
       write_agg(out, Pre{x, (double)cnt}, Suf{x, (double)cnt});
     }
   } else if (cnt <= kAggTeamMax) {
-    bucket_agg<kAggTeam>(kb, cnt, a.c, out);
+    bucket_agg<kAggTeam>(kb, cnt, c, out);
   } else if (tl == 0) {
     atomicOr(&big, 1u << q);
   }
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
   for (uint32_t m = big; m != 0u; m &= m - 1u, ++i) {
     if ((i & (kBT / kWave - 1)) != w) continue;
     const int jj = blk * kAggGroup + __ffs((int)m) - 1;
-    bucket_agg<kWave>(a.keys + row * a.cap + a.bstart[o + jj], (int)a.btot[o + jj], a.c, a.bagg + o + jj);
+    bucket_agg<kWave>(a.keys + row * a.cap + a.bstart[o + jj], (int)a.btot[o + jj], c, a.bagg + o + jj);
   }
 }
 
@@ -451,12 +468,14 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   const bool active = band_active(S);
   if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
   if (active) {
-    const double c = a.c;
+    double rk, rt, c;
+    float rcf;
+    const bool good = band_row_params(a, row, rk, rt, c, rcf);
     const int64_t M = (int64_t)S.band;
     const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
     const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
     const double cR = (double)S.count_hi;
-    const BucketPick P = bucket_search<kLocT, kLocScanT, kLocPer>(g, cnt, seed_lo, seed_hi, cR, M, a.k, c);
+    const BucketPick P = bucket_search<kLocT, kLocScanT, kLocPer>(g, cnt, seed_lo, seed_hi, cR, M, rk, c);
     const int J = P.J;
     const int64_t cJ = P.cnt, sJ = P.start;
     const Pre slo{P.lo_a, P.lo_s};
@@ -472,8 +491,8 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     part.last = P.last != 0;
     if (cJ <= (int64_t)kWaveBucket) {
       if (w == 0) {
-        const double bb = cJ <= 4 * kWave ? wave_sort_solve<4>(kb, (int)cJ, part, a.k, a.t, c, a.cf)
-                                          : wave_sort_solve<16>(kb, (int)cJ, part, a.k, a.t, c, a.cf);
+        const double bb = cJ <= 4 * kWave ? wave_sort_solve<4>(kb, (int)cJ, part, rk, rt, c, rcf)
+                                          : wave_sort_solve<16>(kb, (int)cJ, part, rk, rt, c, rcf);
         if (lane == 0) sel_b = bb;
       }
     } else {
@@ -482,13 +501,14 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       const int shift = band_shift(S, a.bbits);
       const double bb = sorted_range_solve<kLocT>(
           kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, slo, shi, cR_eff, part.first,
-          part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, a.k, a.t,
-          c, a.cf, L.fb);
+          part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, rk, rt,
+          c, rcf, L.fb);
       if (threadIdx.x == 0) sel_b = bb;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      const double bb = sel_b;
+      const double bb = good ? sel_b : __builtin_nan("");
+      if (!good) S.flags |= LAPSUM_FLAG_INVALID;
       S.b = bb;
       if (a.r == nullptr) {  // certification against the bracket
         const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);

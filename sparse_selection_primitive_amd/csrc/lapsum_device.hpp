@@ -34,6 +34,22 @@ namespace lapsum {
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int kWave = 64;
 
+// Budget and temperature of one row: from the optional per-row arrays,
+// else the call's (host-checked) scalars.  Per-row values outside
+// 0 < k < n, 0 < t < inf (NaN included) are replaced by k = n/2, t = 1, so
+// every kernel runs its normal course; the row's outputs are then set to
+// NaN and the row flagged invalid.  Returns whether the values were valid.
+LDEV bool row_params(const double *krow, const double *trow, int64_t row, int64_t n, double &k, double &t) {
+  if (krow) k = krow[row];
+  if (trow) t = trow[row];
+  const bool ok = k > 0.0 && k < (double)n && t > 0.0 && t < INFINITY;
+  if (!ok) {
+    k = 0.5 * (double)n;
+    t = 1.0;
+  }
+  return ok;
+}
+
 // ------------------------------------------------------------------ keys
 // Order-preserving map of fp32 onto uint32: the unsigned order of keys is
 // the numeric order of finite values (-0.0 sorts just below +0.0).

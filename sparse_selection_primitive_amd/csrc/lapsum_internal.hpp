@@ -23,6 +23,14 @@ constexpr int kUnroll = 4;           // independent 16 B loads per thread per st
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
+// Optional per-row budget and temperature (device arrays [rows], NULL: the
+// call's scalars).
+struct RowParams {
+  const double *k;
+  const double *t;
+  __host__ __device__ bool any() const { return k != nullptr || t != nullptr; }
+};
+
 // Arguments of the one-workgroup treatment of a row whose bracket missed
 // (or whose band overflowed): up to `nwiden` widened brackets, each the
 // sample's order statistics of ranks wlo[i], whi[i] (1-based; 0 and m + 1
@@ -85,15 +93,16 @@ struct BandArgs {
   int max_tiles;        // cap / kTile
   double k, t, c;
   float cf;
+  RowParams rp;         // per-row k and t (full-row mode), overriding k, t, c, cf
 };
 
 // Launchers (each returns the first HIP error, or hipSuccess).
 hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2,
                             hipStream_t s);
-hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
-                                 lapsum_row_stats *stats, hipStream_t s);
-hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, float *dr,
-                                  float *dk, lapsum_row_stats *stats, hipStream_t s);
+hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
+                                 double *b, lapsum_row_stats *stats, hipStream_t s);
+hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, RowParams rp,
+                                  float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s);
 bool onchip_backward_supported(int64_t n);
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
                          float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s);
@@ -112,12 +121,13 @@ hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fallback, hipSt
 int band_count_blocks(int gx, int *group);
 int full_count_blocks(int64_t n, int64_t *chunk);
 int bucket_bits(int64_t keys);
-hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p,
-                        double *b, hipStream_t s);
+hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, RowParams rp,
+                        float *p, double *b, hipStream_t s);
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, void *partials, int grid_x,
                              hipStream_t s);
 hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const void *partials,
-                            int npart, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s);
+                            int npart, double t, RowParams rp, float *dr, float *dk, lapsum_row_stats *stats,
+                            hipStream_t s);
 int bwd_grid_x(int64_t rows, int64_t n);
 size_t bwd_partial_bytes(int64_t rows, int grid_x);
 hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats *stats, hipStream_t s);

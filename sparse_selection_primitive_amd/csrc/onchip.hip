@@ -172,10 +172,11 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
 }
 
 // Whole forward of one row held by a team.  FULL: n == E * lanes, so every
-// lane holds E valid scores and no validity test is needed.
+// lane holds E valid scores and no validity test is needed.  good = false
+// (per-row k or t out of range) writes NaN p and b and flags the row.
 template <int E, bool FULL, class Team>
 LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool ok, double k, double t, float *pp,
-                             double *bout, lapsum_row_stats *stats, float *wbuf = nullptr) {
+                             double *bout, lapsum_row_stats *stats, float *wbuf = nullptr, bool good = true) {
   const int n = FULL ? E * Team::kLanes : n_arg;
   constexpr int LANES = Team::kLanes;
   const bool vec = (n & 3) == 0 && aligned16(rr) && aligned16(pp);
@@ -226,6 +227,11 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
     const float h = __builtin_amdgcn_exp2f(-1.0f - fabsf(z2));  // e^{-|z|}/2
     out[e] = z2 < 0.0f ? h : 1.0f - h;
   }
+  if (!good) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = __builtin_nanf("");
+    b = __builtin_nan("");
+  }
   store_row<E, LANES>(pp, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
     *bout = b;
@@ -237,16 +243,18 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
       stats->count_lo = 0;
       stats->count_hi = 0;
       stats->band = n;
-      stats->flags = 0;
+      stats->flags = good ? 0 : LAPSUM_FLAG_INVALID;
       stats->reserved = 0;
     }
   }
 }
 
 // Teams inside one wave: NP = LANES * E <= 1024, 256 threads = 256/LANES rows.
-template <int NP, int LANES, bool FULL>
+// PR: per-row k and t (then each team reads its own; the scalar build keeps
+// them uniform, in scalar registers).
+template <int NP, int LANES, bool FULL, bool PR>
 __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restrict__ r, int64_t rows, int n,
-                                                           double k, double t, float *__restrict__ p,
+                                                           double k, double t, RowParams rp, float *__restrict__ p,
                                                            double *__restrict__ b, lapsum_row_stats *stats) {
   constexpr int E = NP / LANES;
   __shared__ float wbuf[4 * 256];  // candidate buffers of the certified window, 4*LANES per team
@@ -254,53 +262,67 @@ __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restri
   const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
   const bool ok = row < rows;
   const int64_t rr = ok ? row : 0;
+  bool good = true;
+  if constexpr (PR) good = row_params(rp.k, rp.t, rr, n, k, t);
   onchip_row_forward<E, FULL>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr,
-                              wbuf + (threadIdx.x / LANES) * (4 * LANES));
+                              wbuf + (threadIdx.x / LANES) * (4 * LANES), good);
 }
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
-template <int NP>
+template <int NP, bool PR>
 __global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int n,
-                                                                double k, double t, float *__restrict__ p,
-                                                                double *__restrict__ b, lapsum_row_stats *stats) {
+                                                                double k, double t, RowParams rp,
+                                                                float *__restrict__ p, double *__restrict__ b,
+                                                                lapsum_row_stats *stats) {
   constexpr int E = 16, LANES = NP / 16;
   __shared__ BlockTeamLds<LANES, E> lds;
   BlockTeam<LANES, E> team(&lds);
   const int64_t row = blockIdx.x;
-  onchip_row_forward<E, false>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr);
+  bool good = true;
+  if constexpr (PR) good = row_params(rp.k, rp.t, row, n, k, t);
+  onchip_row_forward<E, false>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr,
+                               nullptr, good);
 }
 
-template <int NP, int LANES>
-static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
-                                  lapsum_row_stats *stats, hipStream_t s) {
+template <int NP, int LANES, bool PR>
+static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
+                                  double *b, lapsum_row_stats *stats, hipStream_t s) {
   constexpr int RPB = 256 / LANES;
   const int64_t grid = (rows + RPB - 1) / RPB;
   if (n == NP)
-    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, true>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n, k,
-                       t, p, b, stats);
+    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, true, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows,
+                       n, k, t, rp, p, b, stats);
   else
-    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, false>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n,
-                       k, t, p, b, stats);
+    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, false, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows,
+                       n, k, t, rp, p, b, stats);
   return hipGetLastError();
 }
 
-template <int NP>
-static hipError_t launch_fwd_block(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
-                                   lapsum_row_stats *stats, hipStream_t s) {
-  hipLaunchKernelGGL((onchip_forward_block<NP>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, n, k, t, p, b, stats);
+template <int NP, bool PR>
+static hipError_t launch_fwd_block(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
+                                   double *b, lapsum_row_stats *stats, hipStream_t s) {
+  hipLaunchKernelGGL((onchip_forward_block<NP, PR>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, n, k, t, rp, p,
+                     b, stats);
   return hipGetLastError();
 }
 
-hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, float *p, double *b,
-                                 lapsum_row_stats *stats, hipStream_t s) {
-  if (n <= 64) return launch_fwd_wave<64, 16>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 128) return launch_fwd_wave<128, 16>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 256) return launch_fwd_wave<256, 16>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 512) return launch_fwd_wave<512, 32>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 1024) return launch_fwd_wave<1024, 64>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 2048) return launch_fwd_block<2048>(r, rows, n, k, t, p, b, stats, s);
-  if (n <= 4096) return launch_fwd_block<4096>(r, rows, n, k, t, p, b, stats, s);
-  return launch_fwd_block<8192>(r, rows, n, k, t, p, b, stats, s);
+template <bool PR>
+static hipError_t onchip_forward_by_size(const float *r, int64_t rows, int n, double k, double t, RowParams rp,
+                                         float *p, double *b, lapsum_row_stats *stats, hipStream_t s) {
+  if (n <= 64) return launch_fwd_wave<64, 16, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 128) return launch_fwd_wave<128, 16, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 256) return launch_fwd_wave<256, 16, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 512) return launch_fwd_wave<512, 32, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 1024) return launch_fwd_wave<1024, 64, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 2048) return launch_fwd_block<2048, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  if (n <= 4096) return launch_fwd_block<4096, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+  return launch_fwd_block<8192, PR>(r, rows, n, k, t, rp, p, b, stats, s);
+}
+
+hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
+                                 double *b, lapsum_row_stats *stats, hipStream_t s) {
+  return rp.any() ? onchip_forward_by_size<true>(r, rows, n, k, t, rp, p, b, stats, s)
+                  : onchip_forward_by_size<false>(r, rows, n, k, t, rp, p, b, stats, s);
 }
 
 // ------------------------------------------------------------ backward
@@ -310,7 +332,7 @@ hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, 
 template <int NP, int LANES>
 LDEV void bwd_row(const WaveTeam<LANES> &team, const float (&gv)[NP / LANES], const float (&pv)[NP / LANES],
                   int64_t row, bool ok, int n, bool vec, float inv_t, float *__restrict__ dr, float *__restrict__ dk,
-                  lapsum_row_stats *stats) {
+                  lapsum_row_stats *stats, bool good = true) {
   constexpr int E = NP / LANES;
   double D = 0.0, G = 0.0;
   float q[E];
@@ -326,18 +348,21 @@ LDEV void bwd_row(const WaveTeam<LANES> &team, const float (&gv)[NP / LANES], co
   const double dkd = D > 0.0 ? G / D : 0.0;
   float out[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = D > 0.0 ? q[e] * inv_t * (float)((double)gv[e] - dkd) : 0.0f;
+  for (int e = 0; e < E; ++e)
+    out[e] = !good ? __builtin_nanf("") : (D > 0.0 ? q[e] * inv_t * (float)((double)gv[e] - dkd) : 0.0f);
   store_row<E, LANES>(dr + row * n, n, team.lane, ok, vec, out);
   if (ok && team.lane == 0) {
-    dk[row] = (float)dkd;
-    if (stats && !(D > 0.0)) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
+    dk[row] = good ? (float)dkd : __builtin_nanf("");
+    if (stats && !good) atomicOr(&stats[row].flags, LAPSUM_FLAG_INVALID);
+    else if (stats && !(D > 0.0)) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
   }
 }
 
-template <int NP, int LANES>
+template <int NP, int LANES, bool PR>
 __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restrict__ g, const float *__restrict__ p,
-                                                            int64_t rows, int n, double t, float *__restrict__ dr,
-                                                            float *__restrict__ dk, lapsum_row_stats *stats) {
+                                                            int64_t rows, int n, double t, RowParams rp,
+                                                            float *__restrict__ dr, float *__restrict__ dk,
+                                                            lapsum_row_stats *stats) {
   constexpr int E = NP / LANES, RPW = 256 / LANES;
   WaveTeam<LANES> team;
   const bool vec = (n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr);
@@ -362,7 +387,13 @@ __global__ __launch_bounds__(256) void onchip_backward_wave(const float *__restr
     load_row<E, LANES>(p + nr * n, n, team.lane, nok, vec, pn);
     const int64_t row = grp * RPW + sub;
     const bool ok = row < rows;
-    bwd_row<NP, LANES>(team, gv, pv, ok ? row : 0, ok, n, vec, inv_t, dr, dk, stats);
+    if constexpr (PR) {
+      double kr = 0.5 * (double)n, tr = t;
+      const bool good = row_params(nullptr, rp.t, ok ? row : 0, n, kr, tr);
+      bwd_row<NP, LANES>(team, gv, pv, ok ? row : 0, ok, n, vec, (float)(1.0 / tr), dr, dk, stats, good);
+    } else {
+      bwd_row<NP, LANES>(team, gv, pv, ok ? row : 0, ok, n, vec, inv_t, dr, dk, stats);
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       gv[e] = gn[e];
@@ -376,23 +407,27 @@ bool onchip_backward_supported(int64_t n) { return n >= 1 && n <= 1024; }
 constexpr int64_t kBwdMaxGroups = 4096;  // workgroups of the on-chip backward, at most
 
 template <int NP, int LANES>
-static hipError_t launch_bwd_wave(const float *g, const float *p, int64_t rows, int n, double t, float *dr, float *dk,
-                                  lapsum_row_stats *stats, hipStream_t s) {
+static hipError_t launch_bwd_wave(const float *g, const float *p, int64_t rows, int n, double t, RowParams rp,
+                                  float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
   constexpr int RPB = 256 / LANES;
   const int64_t groups = (rows + RPB - 1) / RPB;
   const int64_t grid = groups < kBwdMaxGroups ? groups : kBwdMaxGroups;
-  hipLaunchKernelGGL((onchip_backward_wave<NP, LANES>), dim3((unsigned)grid), dim3(256), 0, s, g, p, rows, n, t, dr,
-                     dk, stats);
+  if (rp.t != nullptr)
+    hipLaunchKernelGGL((onchip_backward_wave<NP, LANES, true>), dim3((unsigned)grid), dim3(256), 0, s, g, p, rows, n,
+                       t, rp, dr, dk, stats);
+  else
+    hipLaunchKernelGGL((onchip_backward_wave<NP, LANES, false>), dim3((unsigned)grid), dim3(256), 0, s, g, p, rows,
+                       n, t, rp, dr, dk, stats);
   return hipGetLastError();
 }
 
-hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, float *dr,
-                                  float *dk, lapsum_row_stats *stats, hipStream_t s) {
-  if (n <= 64) return launch_bwd_wave<64, 16>(g, p, rows, n, t, dr, dk, stats, s);
-  if (n <= 128) return launch_bwd_wave<128, 16>(g, p, rows, n, t, dr, dk, stats, s);
-  if (n <= 256) return launch_bwd_wave<256, 16>(g, p, rows, n, t, dr, dk, stats, s);
-  if (n <= 512) return launch_bwd_wave<512, 32>(g, p, rows, n, t, dr, dk, stats, s);
-  return launch_bwd_wave<1024, 64>(g, p, rows, n, t, dr, dk, stats, s);
+hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, RowParams rp,
+                                  float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+  if (n <= 64) return launch_bwd_wave<64, 16>(g, p, rows, n, t, rp, dr, dk, stats, s);
+  if (n <= 128) return launch_bwd_wave<128, 16>(g, p, rows, n, t, rp, dr, dk, stats, s);
+  if (n <= 256) return launch_bwd_wave<256, 16>(g, p, rows, n, t, rp, dr, dk, stats, s);
+  if (n <= 512) return launch_bwd_wave<512, 32>(g, p, rows, n, t, rp, dr, dk, stats, s);
+  return launch_bwd_wave<1024, 64>(g, p, rows, n, t, rp, dr, dk, stats, s);
 }
 
 // ----------------------------------------------------------- band solve

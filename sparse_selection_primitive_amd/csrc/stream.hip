@@ -66,9 +66,12 @@ size_t row_state_bytes() { return sizeof(RowState); }
 // ---------------------------------------------------------------- apply
 __global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__restrict__ r, int64_t n,
                                                                const RowState *__restrict__ st, double t,
-                                                               float *__restrict__ p, double *__restrict__ bout) {
+                                                               RowParams rp, float *__restrict__ p,
+                                                               double *__restrict__ bout) {
   const int64_t row = blockIdx.y;
-  const double b = st[row].b;
+  const double b = st[row].b;  // NaN for a row with invalid per-row k or t
+  double kr = 0.5 * (double)n;
+  if (rp.t) row_params(nullptr, rp.t, row, n, kr, t);
   const double c = kLog2e / t;
   if (blockIdx.x == 0 && threadIdx.x == 0) bout[row] = b;
   const float *rr = r + row * n;
@@ -114,10 +117,10 @@ static int stream_grid_x(int64_t rows, int64_t n) {
   return (int)gx;
 }
 
-hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, float *p, double *b,
-                        hipStream_t s) {
+hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, RowParams rp,
+                        float *p, double *b, hipStream_t s) {
   const int gx = stream_grid_x(rows, n);
-  hipLaunchKernelGGL(apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, t, p, b);
+  hipLaunchKernelGGL(apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, t, rp, p, b);
   return hipGetLastError();
 }
 
@@ -221,10 +224,15 @@ LDEV void bwd_row_total(const BwdPartial *__restrict__ vp, int gx, double *lds, 
 __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *__restrict__ g,
                                                                    const float *__restrict__ p, int64_t n,
                                                                    const BwdPartial *__restrict__ part, int gx,
-                                                                   double t, float *__restrict__ dr,
+                                                                   double t, RowParams rp, float *__restrict__ dr,
                                                                    float *__restrict__ dk, lapsum_row_stats *stats) {
   __shared__ double lds[2 * kStreamThreads / kWave];
   const int64_t row = blockIdx.y;
+  bool good = true;
+  if (rp.t) {
+    double kr = 0.5 * (double)n;
+    good = row_params(nullptr, rp.t, row, n, kr, t);
+  }
   const BwdPartial *vp = part + row * gx;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
@@ -250,6 +258,7 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
     };
     load(i0);
     bwd_row_total(vp, gx, lds, dkd, degenerate);
+    if (!good) dkd = __builtin_nan("");  // NaN through every dr of the row
     const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
     while (i0 < n4) {
 #pragma unroll
@@ -269,13 +278,15 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
     }
   } else {
     bwd_row_total(vp, gx, lds, dkd, degenerate);
+    if (!good) dkd = __builtin_nan("");
     const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
     for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
       dd[i] = fminf(pp[i], 1.0f - pp[i]) * inv_t * (float)((double)gg[i] - dkd);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     dk[row] = (float)dkd;
-    if (stats && degenerate) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
+    if (stats && !good) atomicOr(&stats[row].flags, LAPSUM_FLAG_INVALID);
+    else if (stats && degenerate) atomicOr(&stats[row].flags, LAPSUM_FLAG_DEGENERATE);
   }
 }
 
@@ -290,10 +301,11 @@ hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64
 }
 
 hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_t n, const void *partials,
-                            int npart, double t, float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s) {
+                            int npart, double t, RowParams rp, float *dr, float *dk, lapsum_row_stats *stats,
+                            hipStream_t s) {
   const int gx = stream_grid_x(rows, n);
   hipLaunchKernelGGL(bwd_apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
-                     reinterpret_cast<const BwdPartial *>(partials), npart, t, dr, dk, stats);
+                     reinterpret_cast<const BwdPartial *>(partials), npart, t, rp, dr, dk, stats);
   return hipGetLastError();
 }
 

@@ -50,8 +50,19 @@ def test_library_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     # sizes fixed by the header's field lists (natural alignment on x86-64)
     assert ctypes.sizeof(L.RowStats) == 4 * 8 + 3 * 8 + 2 * 4
-    assert ctypes.sizeof(L.Options) == 4 + 4 + 8 + 8 + 8 + 8 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(L.Options) == 4 + 4 + 8 + 8 + 8 + 8 + 8 + 8 + 4 + 4 + 8 + 8
     assert ctypes.sizeof(L.PlanInfo) == 4 + 4 + 4 * 8 + 4 + 4 + 8 + 8
+
+
+def test_flag_and_path_constants_match_header():
+    text = open(HEADER).read()
+    flags = dict(re.findall(r"#define LAPSUM_FLAG_(\w+) (0x[0-9a-fA-F]+)", text))
+    assert flags, "no flags parsed"
+    for name, value in flags.items():
+        assert getattr(L, "FLAG_" + name) == int(value, 16), name
+    paths = dict(re.findall(r"LAPSUM_PATH_(\w+) = (\d+)", text))
+    for name, value in paths.items():
+        assert getattr(L, "PATH_" + name) == int(value), name
 
 
 def test_status_strings(lib):
@@ -126,6 +137,29 @@ def test_plan_rejects_bad_options(lib):
                {"band_capacity": -1}, {"bracket_override": (1.0, 0.0)}, {"path": 7}):
         with pytest.raises(L.LapsumError, match="status 7"):
             L.plan(1, 10000, 5, 1.0, **kw)
+
+
+def test_plan_per_row_parameters(lib):
+    """Per-row k / t (device arrays, never read by the host): the scalars are
+    then not checked, AUTO takes the full-sort path above the on-chip size
+    (the bracket's sample indices need k on the host), and a forced
+    bracketing path is refused."""
+    dev = 4096  # a device address stand-in: planning never dereferences it
+    assert L.plan(64, 256, 0.0, 0.0, k_rows_ptr=dev, t_rows_ptr=dev)["path"] == L.PATH_ONCHIP
+    assert L.plan(2, 3_317_760, 0.0, 1e-3, k_rows_ptr=dev)["path"] == L.PATH_FULLSORT
+    assert L.plan(2, 3_317_760, 600, -1.0, t_rows_ptr=dev)["path"] == L.PATH_FULLSORT
+    with pytest.raises(L.LapsumError, match="status 6"):
+        L.plan(2, 3_317_760, 600, 1e-3, path="bracket", k_rows_ptr=dev)
+    with pytest.raises(L.LapsumError, match="status 3"):  # the scalar k is still checked without k_rows
+        L.plan(2, 20000, 0.0, 1e-3, t_rows_ptr=dev)
+
+
+def test_plan_widen_steps_range(lib):
+    for w in (-1, 0, 1, 4):
+        L.plan(1, 3_317_760, 600, 1e-3, widen_steps=w)
+    for w in (-2, 5):
+        with pytest.raises(L.LapsumError, match="status 7"):
+            L.plan(1, 3_317_760, 600, 1e-3, widen_steps=w)
 
 
 def test_forward_rejects_null_and_small_workspace_without_launching(lib):
