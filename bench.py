@@ -76,6 +76,9 @@ WORKLOADS = {
     "extreme": dict(gen="extreme", path="auto", fwd_b=12, bwd_b=20),
     "attack": dict(gen="attack", path="auto", fwd_b=12, bwd_b=20),
     "routing": dict(gen="routing", path="auto", fwd_b=8, bwd_b=12),
+    # the routing batch with a budget and a temperature per row (k_i in [2, 14],
+    # t_i log-uniform in [0.02, 0.1], seed 4700)
+    "routing_per_row": dict(gen="routing", path="auto", fwd_b=8, bwd_b=12, per_row=True),
     "coder_bracket": dict(gen="coder", path="bracket", fwd_b=12, bwd_b=20),
     "coder_fullsort": dict(gen="coder", path="fullsort", fwd_b=8, bwd_b=20),
     "tiny": dict(gen="tiny", path="auto", fwd_b=8, bwd_b=12),
@@ -136,7 +139,13 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
         sets.append((r, g, p, b, dr, dk))
     path = spec["path"]
     plan = L.plan(rows, n, w.k, w.t, path=path, seed=seed)
-    op = L.Operator(rows, n, w.k, w.t, device=dev, path=path, seed=seed)
+    k_rows = t_rows = None
+    if spec.get("per_row"):
+        import numpy as np
+        gk = np.random.Generator(np.random.PCG64(4700))
+        k_rows = torch.from_numpy(gk.uniform(2.0, 14.0, rows)).to(dev)
+        t_rows = torch.from_numpy(np.exp(gk.uniform(np.log(0.02), np.log(0.1), rows))).to(dev)
+    op = L.Operator(rows, n, w.k, w.t, device=dev, path=path, seed=seed, k_rows=k_rows, t_rows=t_rows)
 
     def step(i, ev=None):
         r, g, p, b, dr, dk = sets[i % nsets]
@@ -241,6 +250,9 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0):
     }
     if plan["path"] == L.PATH_BRACKET:
         out["bracket"] = {"m": plan["m"], "lo": plan["lo"], "hi": plan["hi"], "band_capacity": plan["band_capacity"]}
+    if spec.get("per_row"):
+        out["workload"] = w.name + "_per_row_k_t"
+        out["k"], out["t"] = "per row, uniform in [2, 14]", "per row, log-uniform in [0.02, 0.1]"
     return out, w
 
 
@@ -296,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="extreme,attack,routing,coder_bracket,coder_fullsort,tiny")
+    ap.add_argument("--configs", default="extreme,attack,routing,routing_per_row,coder_bracket,coder_fullsort,tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-trials", type=int, default=20)
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (HBM counter calibration)")

@@ -317,13 +317,20 @@ class Operator:
     Outputs are written into caller-provided tensors."""
 
     def __init__(self, rows: int, n: int, k: float, t: float, device=None, stream=None, path="auto", seed=0,
-                 sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None, widen_steps=0):
+                 sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None, widen_steps=0,
+                 k_rows=None, t_rows=None):
+        """k_rows / t_rows: optional per-row values (tensors of one value per
+        row; they replace k / t, which are then not used)."""
         torch = _torch()
         self.lib = load_library()
         self.rows, self.n, self.k, self.t = int(rows), int(n), float(k), float(t)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
                                 stats_buf.data_ptr() if stats_buf is not None else None, widen_steps=widen_steps)
+        self._k_rows = _per_row(k_rows, self.rows, self.device, "k_rows")
+        self._t_rows = _per_row(t_rows, self.rows, self.device, "t_rows")
+        self.opt.k_rows = self._k_rows.data_ptr() if self._k_rows is not None else None
+        self.opt.t_rows = self._t_rows.data_ptr() if self._t_rows is not None else None
         nbytes = int(self.lib.lapsum_workspace_bytes(self.rows, self.n, self.k, self.t, ctypes.byref(self.opt)))
         self._ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device) if nbytes else None
         if self._ws is not None:

@@ -448,7 +448,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   RowState *rs = reinterpret_cast<RowState *>(ws + P.st);
   if (P.path == LAPSUM_PATH_FULLSORT) {
     tm.mark(LAPSUM_STAGE_INIT, 0);
-    LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, s));
+    LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, n, k, t, rp, s));
     tm.mark(LAPSUM_STAGE_INIT, 1);
     tm.mark(LAPSUM_STAGE_FULLSORT, 0);
     const SegArgs none{};  // full rows have no bracket, so no fallback
@@ -458,7 +458,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     const double *ovr = o.bracket_override;
     if (ovr) {
       tm.mark(LAPSUM_STAGE_INIT, 0);
-      LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, s));
+      LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, n, k, t, RowParams{nullptr, nullptr}, s));
       tm.mark(LAPSUM_STAGE_INIT, 1);
     } else {
       // the sample kernel also resets the rows' state

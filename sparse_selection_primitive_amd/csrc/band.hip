@@ -43,18 +43,15 @@ static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of th
 
 LDEV bool band_active(const RowState &S) { return !(S.flags & LAPSUM_FLAG_OVERFLOW); }
 
-// Budget, temperature and c = log2(e)/t of one row: the call's, or the
-// row's own in full-row mode (false: per-row values out of range, replaced).
-LDEV bool band_row_params(const BandArgs &a, int64_t row, double &k, double &t, double &c, float &cf) {
-  k = a.k;
-  t = a.t;
-  c = a.c;
-  cf = a.cf;
-  if (!a.rp.any()) return true;
-  const bool ok = row_params(a.rp.k, a.rp.t, row, a.n, k, t);
-  c = kLog2e / t;
-  cf = (float)c;
-  return ok;
+// Budget, temperature and c = log2(e)/t of one row: the call's, or (with
+// per-row values, full-row mode) the row's own as the per-call reset stored
+// them (both uniform over the workgroup, so they stay in scalar registers).
+LDEV void band_row_params(const BandArgs &a, const RowState &S, double &k, double &t, double &c, float &cf) {
+  const bool pr = a.rp.any();
+  k = pr ? S.k : a.k;
+  t = pr ? S.t : a.t;
+  c = pr ? S.c : a.c;
+  cf = pr ? S.cf : a.cf;
 }
 
 LDEV int band_shift(const RowState &S, int bbits) {
@@ -395,7 +392,7 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
   const int tl = threadIdx.x & (kAggTeam - 1);
   double rk, rt, c;
   float rcf;
-  band_row_params(a, row, rk, rt, c, rcf);
+  band_row_params(a, S, rk, rt, c, rcf);
   if (threadIdx.x == 0) big = 0u;
   __syncthreads();
   if (cnt == 0) {
@@ -470,7 +467,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   if (active) {
     double rk, rt, c;
     float rcf;
-    const bool good = band_row_params(a, row, rk, rt, c, rcf);
+    band_row_params(a, S, rk, rt, c, rcf);
     const int64_t M = (int64_t)S.band;
     const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
     const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
@@ -507,8 +504,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      const double bb = good ? sel_b : __builtin_nan("");
-      if (!good) S.flags |= LAPSUM_FLAG_INVALID;
+      const double bb = (S.flags & LAPSUM_FLAG_INVALID) ? __builtin_nan("") : sel_b;
       S.b = bb;
       if (a.r == nullptr) {  // certification against the bracket
         const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);

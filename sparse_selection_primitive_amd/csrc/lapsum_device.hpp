@@ -762,6 +762,9 @@ struct RowState {
   uint32_t kmin, kmax;      // key range of the band
   int32_t flags;
   int32_t pad0;
+  double k, t, c;           // full-sort path: the row's budget, temperature, log2(e)/t
+  float cf;                 //   (its own with per-row values, else the call's)
+  int32_t pad1;
 };
 
 // Per-call reset of one row's state (bracket open unless forced).
@@ -779,6 +782,9 @@ LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_over
   z.kmax = 0u;
   z.flags = flags;
   z.pad0 = 0;
+  z.k = z.t = z.c = 0.0;
+  z.cf = 0.0f;
+  z.pad1 = 0;
   st[row] = z;
 }
 

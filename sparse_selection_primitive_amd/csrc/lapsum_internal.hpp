@@ -97,8 +97,8 @@ struct BandArgs {
 };
 
 // Launchers (each returns the first HIP error, or hipSuccess).
-hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2,
-                            hipStream_t s);
+hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, int64_t n,
+                            double k, double t, RowParams rp, hipStream_t s);
 hipError_t launch_onchip_forward(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
                                  double *b, lapsum_row_stats *stats, hipStream_t s);
 hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, int n, double t, RowParams rp,

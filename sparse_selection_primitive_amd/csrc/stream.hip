@@ -25,16 +25,27 @@ LDEV float cdf_at(float x, double b, double c) {
 }
 
 // ----------------------------------------------------------- row state
+// Per-call reset of every row's state, with the row's budget, temperature
+// and c = log2(e)/t (its own values if given: an out-of-range one is
+// replaced and the row flagged invalid).
 __global__ void init_rows_kernel(RowState *st, int64_t rows, int32_t flags, int has_override, double o_lo,
-                                 double o_hi) {
+                                 double o_hi, int64_t n, double k, double t, RowParams rp) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row < rows) reset_row_state(st, row, flags, has_override, o_lo, o_hi);
+  if (row >= rows) return;
+  const bool good = row_params(rp.k, rp.t, row, n, k, t);
+  reset_row_state(st, row, flags | (good ? 0 : LAPSUM_FLAG_INVALID), has_override, o_lo, o_hi);
+  RowState &S = st[row];
+  S.k = k;
+  S.t = t;
+  S.c = kLog2e / t;
+  S.cf = (float)S.c;
 }
 
-hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, hipStream_t s) {
+hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, int64_t n,
+                            double k, double t, RowParams rp, hipStream_t s) {
   const int64_t grid = (rows + 255) / 256;
   hipLaunchKernelGGL(init_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, st, rows, flags, override2 ? 1 : 0,
-                     override2 ? override2[0] : 0.0, override2 ? override2[1] : 0.0);
+                     override2 ? override2[0] : 0.0, override2 ? override2[1] : 0.0, n, k, t, rp);
   return hipGetLastError();
 }
 
@@ -210,6 +221,14 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float 
 // row in the same fixed order, so all of them hold the same dk (bitwise) and
 // no finalize launch is needed; the first one writes dk.  The first batch of
 // scores is already in flight while the partials are added.
+// The row's temperature into t (per-row value if given); false if that
+// value is out of range (then t = 1 and the row's outputs become NaN).
+LDEV bool bwd_row_t(const RowParams &rp, int64_t row, int64_t n, double &t) {
+  if (!rp.t) return true;
+  double kr = 0.5 * (double)n;
+  return row_params(nullptr, rp.t, row, n, kr, t);
+}
+
 LDEV void bwd_row_total(const BwdPartial *__restrict__ vp, int gx, double *lds, double &dkd, bool &degenerate) {
   double Ds = 0.0, Gs = 0.0;
   for (int i = threadIdx.x; i < gx; i += kStreamThreads) {
@@ -228,18 +247,13 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
                                                                    float *__restrict__ dk, lapsum_row_stats *stats) {
   __shared__ double lds[2 * kStreamThreads / kWave];
   const int64_t row = blockIdx.y;
-  bool good = true;
-  if (rp.t) {
-    double kr = 0.5 * (double)n;
-    good = row_params(nullptr, rp.t, row, n, kr, t);
-  }
   const BwdPartial *vp = part + row * gx;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
   float *dd = dr + row * n;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
   double dkd;
-  bool degenerate;
+  bool degenerate, good;
   if ((n & 3) == 0 && aligned16(g) && aligned16(p) && aligned16(dr)) {
     const int64_t n4 = n >> 2;
     const f4 *g4 = reinterpret_cast<const f4 *>(gg);
@@ -257,6 +271,7 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
       }
     };
     load(i0);
+    good = bwd_row_t(rp, row, n, t);
     bwd_row_total(vp, gx, lds, dkd, degenerate);
     if (!good) dkd = __builtin_nan("");  // NaN through every dr of the row
     const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);
@@ -277,6 +292,7 @@ __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *
       if (i0 < n4) load(i0);
     }
   } else {
+    good = bwd_row_t(rp, row, n, t);
     bwd_row_total(vp, gx, lds, dkd, degenerate);
     if (!good) dkd = __builtin_nan("");
     const float inv_t = degenerate ? 0.0f : (float)(1.0 / t);

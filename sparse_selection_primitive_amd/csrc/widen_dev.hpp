@@ -196,7 +196,9 @@ LDEV bool widen_row(const SegArgs &a, int row, SegLds<NT> &L) {
 }
 
 // A row whose bracket missed or whose band overflowed: widened brackets
-// first, then the exact whole-row fallback.
+// first, then the exact whole-row fallback.  (Inlined: a call would make
+// every launch of the band kernels set up a stack, which costs more than
+// the spills this path adds outside the hit path.)
 template <int NT>
 LDEV void missed_row(const SegArgs &a, int row, SegLds<NT> &L) {
   if (!widen_row<NT>(a, row, L)) fallback_row<NT>(a, row, L);
