@@ -253,11 +253,10 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
 // PR: per-row k and t (then each team reads its own; the scalar build keeps
 // them uniform, in scalar registers).
 template <int NP, int LANES, bool FULL, bool PR>
-__global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restrict__ r, int64_t rows, int n,
-                                                           double k, double t, RowParams rp, float *__restrict__ p,
-                                                           double *__restrict__ b, lapsum_row_stats *stats) {
+LDEV void onchip_forward_wave_body(const float *__restrict__ r, int64_t rows, int n, double k, double t,
+                                   const RowParams &rp, float *__restrict__ p, double *__restrict__ b,
+                                   lapsum_row_stats *stats, float *wbuf) {
   constexpr int E = NP / LANES;
-  __shared__ float wbuf[4 * 256];  // candidate buffers of the certified window, 4*LANES per team
   WaveTeam<LANES> team;
   const int64_t row = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
   const bool ok = row < rows;
@@ -266,6 +265,28 @@ __global__ __launch_bounds__(256) void onchip_forward_wave(const float *__restri
   if constexpr (PR) good = row_params(rp.k, rp.t, rr, n, k, t);
   onchip_row_forward<E, FULL>(team, r + rr * n, n, ok, k, t, p + rr * n, b + rr, stats ? stats + rr : nullptr,
                               wbuf + (threadIdx.x / LANES) * (4 * LANES), good);
+}
+
+// Rows of exactly NP scores: at most 128 VGPRs, so four waves fit on each
+// SIMD and a batch of small rows runs in one round (the per-row build would
+// otherwise just exceed it).
+template <int NP, int LANES, bool PR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void onchip_forward_wave(
+    const float *__restrict__ r, int64_t rows, int n, double k, double t, RowParams rp, float *__restrict__ p,
+    double *__restrict__ b, lapsum_row_stats *stats) {
+  __shared__ float wbuf[4 * 256];  // candidate buffers of the certified window, 4*LANES per team
+  onchip_forward_wave_body<NP, LANES, true, PR>(r, rows, n, k, t, rp, p, b, stats, wbuf);
+}
+
+// Ragged rows (n < NP): the validity tests need more registers, and two
+// waves per SIMD without spills beat four with them.
+template <int NP, int LANES, bool PR>
+__global__ __launch_bounds__(256) void onchip_forward_wave_ragged(const float *__restrict__ r, int64_t rows, int n,
+                                                                  double k, double t, RowParams rp,
+                                                                  float *__restrict__ p, double *__restrict__ b,
+                                                                  lapsum_row_stats *stats) {
+  __shared__ float wbuf[4 * 256];
+  onchip_forward_wave_body<NP, LANES, false, PR>(r, rows, n, k, t, rp, p, b, stats, wbuf);
 }
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
@@ -290,10 +311,10 @@ static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k,
   constexpr int RPB = 256 / LANES;
   const int64_t grid = (rows + RPB - 1) / RPB;
   if (n == NP)
-    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, true, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows,
-                       n, k, t, rp, p, b, stats);
+    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows, n, k,
+                       t, rp, p, b, stats);
   else
-    hipLaunchKernelGGL((onchip_forward_wave<NP, LANES, false, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows,
+    hipLaunchKernelGGL((onchip_forward_wave_ragged<NP, LANES, PR>), dim3((unsigned)grid), dim3(256), 0, s, r, rows,
                        n, k, t, rp, p, b, stats);
   return hipGetLastError();
 }
