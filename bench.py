@@ -81,6 +81,9 @@ WORKLOADS = {
     "routing_per_row": dict(gen="routing", path="auto", fwd_b=8, bwd_b=12, per_row=True),
     "coder_bracket": dict(gen="coder", path="bracket", fwd_b=12, bwd_b=20),
     "coder_fullsort": dict(gen="coder", path="fullsort", fwd_b=8, bwd_b=20),
+    # the 1e8 row through the full-sort path (the pages compare bracketing
+    # with a full sort at this size)
+    "extreme_fullsort": dict(gen="extreme", path="fullsort", fwd_b=8, bwd_b=20),
     "tiny": dict(gen="tiny", path="auto", fwd_b=8, bwd_b=12),
 }
 
@@ -308,7 +311,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="extreme,attack,routing,routing_per_row,coder_bracket,coder_fullsort,tiny")
+    ap.add_argument("--configs",
+                    default="extreme,attack,routing,routing_per_row,coder_bracket,coder_fullsort,extreme_fullsort,tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-trials", type=int, default=20)
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (HBM counter calibration)")
@@ -330,7 +334,7 @@ def main():
     results = {}
     extreme_w = None
     for name in names:
-        steps = args.steps if name == "extreme" else max(args.steps, 100)
+        steps = args.steps if name.startswith("extreme") else max(args.steps, 100)
         res, w = bench_workload(L, hip, torch, name, WORKLOADS[name], steps, args.warmup)
         results[name] = res
         if name == "extreme":

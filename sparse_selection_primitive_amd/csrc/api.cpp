@@ -58,7 +58,7 @@ SegRegions seg_regions(Layout &L, int64_t rows, int64_t len) {
 // the bracketing path (slots from gx filter workgroups), or whole rows of the
 // full-sort path (full = true, n scores per row).
 struct BandRegions {
-  size_t keys, tmp, hist, btot, bstart, bagg, tagg, tpre, tsuf, mm;
+  size_t keys, tmp, hist, hext, btot, bstart, bagg, bkey, bsum, tagg, tpre, tsuf, mm;
   int nblk, group, max_tiles;
   int64_t chunk;
 };
@@ -75,9 +75,12 @@ BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx, bool full
   r.keys = L.take(keys);
   r.tmp = L.take(keys);
   r.hist = L.take(nb * (size_t)r.nblk * sizeof(uint32_t));
+  r.hext = full ? L.take(2 * nb * (size_t)r.nblk * sizeof(uint32_t)) : 0;
   r.btot = L.take(nb * sizeof(uint32_t));
   r.bstart = L.take(nb * sizeof(uint32_t));
-  r.bagg = L.take(nb * tile_agg_bytes());
+  r.bagg = full ? 0 : L.take(nb * tile_agg_bytes());
+  r.bkey = full ? L.take(2 * nb * sizeof(uint32_t)) : 0;
+  r.bsum = full ? L.take(2 * nb * sizeof(unsigned long long)) : 0;
   r.tagg = L.take((size_t)rows * (size_t)r.max_tiles * tile_agg_bytes());
   r.tpre = L.take((size_t)rows * (size_t)r.max_tiles * pre_bytes());
   r.tsuf = L.take((size_t)rows * (size_t)r.max_tiles * suf_bytes());
@@ -345,7 +348,10 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   a.hist = reinterpret_cast<uint32_t *>(ws + R.hist);
   a.btot = reinterpret_cast<uint32_t *>(ws + R.btot);
   a.bstart = reinterpret_cast<uint32_t *>(ws + R.bstart);
-  a.bagg = reinterpret_cast<TileAgg *>(ws + R.bagg);
+  a.hext = r != nullptr ? reinterpret_cast<uint32_t *>(ws + R.hext) : nullptr;
+  a.bagg = r == nullptr ? reinterpret_cast<TileAgg *>(ws + R.bagg) : nullptr;
+  a.bkey = r != nullptr ? reinterpret_cast<uint32_t *>(ws + R.bkey) : nullptr;
+  a.bsum = r != nullptr ? reinterpret_cast<unsigned long long *>(ws + R.bsum) : nullptr;
   a.tagg = reinterpret_cast<TileAgg *>(ws + R.tagg);
   a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
   a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);

@@ -14,15 +14,20 @@
 // the one that holds the root.
 //
 //   band_minmax_kernel   (full-row mode) key range of each workgroup's chunk
-//   band_count_kernel    bucket counts of each workgroup's filter slots or chunk
-//   band_scan_kernel     per bucket, offsets of the workgroups inside it
+//   band_count_kernel    bucket counts and key extremes of each workgroup's
+//                        filter slots or chunk
+//   band_scan_kernel     per bucket, offsets of the workgroups inside it,
+//                        its size and key extremes
 //   band_scatter_kernel  keys to their bucket (order inside a bucket free)
-//   band_agg_kernel      anchored aggregates of every bucket, order-free
+//   band_agg_*_kernel    anchored sums of every bucket, order-free: by
+//                        buckets (band mode) or by key ranges (full-row
+//                        mode, where crowded buckets must be shared)
 //   band_locate_kernel   scan of the bucket aggregates between the tail
 //                        seeds, threshold curve at the bucket ends, the
-//                        balancing bucket, its sort and the root inside it,
-//                        certification, and the exact fallback of a row
-//                        whose bracket missed
+//                        balancing bucket, its sort (or nested bucket
+//                        selection when crowded) and the root inside it,
+//                        certification, and the widening or exact fallback
+//                        of a row whose bracket missed
 //
 // Every count is an integer, the bucket sums are fixed-point integer sums,
 // and the balancing bucket is sorted before anything is summed over it in
@@ -167,14 +172,18 @@ __global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
 }
 
 __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
-  __shared__ uint32_t h[kBandBuckets];
+  __shared__ uint32_t h[kBandBuckets], hmn[kBandBuckets], hmx[kBandBuckets];
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
   __shared__ uint32_t rng[2];
   const int64_t row = blockIdx.y;
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
   const int nb = 1 << a.bbits;
-  for (int j = threadIdx.x; j < nb; j += kBT) h[j] = 0u;
+  for (int j = threadIdx.x; j < nb; j += kBT) {
+    h[j] = 0u;
+    hmn[j] = 0xFFFFFFFFu;
+    hmx[j] = 0u;
+  }
   RowState R;  // the key range and count this workgroup buckets by
   const uint32_t *sb = soffs;
   if (a.r != nullptr) {
@@ -223,30 +232,81 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   }
   const uint32_t kmin = R.kmin;
   const int shift = band_shift(R, a.bbits);
-  for_each_band_key(a, row, blk, sb, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
-  __syncthreads();
   uint32_t *dst = a.hist + (row * a.nblk + blk) * (int64_t)kBandBuckets;
-  for (int j = threadIdx.x; j < nb; j += kBT) dst[j] = h[j];
+  if (a.r != nullptr) {
+    // full-row mode: counts and key extremes of the buckets in this chunk
+    for_each_band_key(a, row, blk, sb, [&](uint32_t key) {
+      const uint32_t j = (key - kmin) >> shift;
+      atomicAdd(&h[j], 1u);
+      atomicMin(&hmn[j], key);
+      atomicMax(&hmx[j], key);
+    });
+    __syncthreads();
+    uint32_t *ext = a.hext + (row * a.nblk + blk) * (int64_t)(2 * kBandBuckets);
+    for (int j = threadIdx.x; j < nb; j += kBT) {
+      dst[j] = h[j];
+      ext[j] = hmn[j];
+      ext[kBandBuckets + j] = hmx[j];
+    }
+  } else {
+    for_each_band_key(a, row, blk, sb, [&](uint32_t key) { atomicAdd(&h[(key - kmin) >> shift], 1u); });
+    __syncthreads();
+    for (int j = threadIdx.x; j < nb; j += kBT) dst[j] = h[j];
+  }
 }
 
 // one thread per bucket: exclusive scan over the count workgroups, in
-// place; every count is loaded before the first is used
+// place, kBandCountBlocks counts at a time (each batch loaded before any of
+// it is used); the bucket's key extremes over the workgroups; and its
+// fixed-point sums cleared for the scatter to add into
 __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   const int64_t row = blockIdx.y;
   const int j = blockIdx.x * kBT + threadIdx.x;
   if (j >= (1 << a.bbits)) return;
   uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
+  const uint32_t *ext = a.hext + row * a.nblk * (int64_t)(2 * kBandBuckets) + j;
   uint32_t v[kBandCountBlocks];
 #pragma unroll
   for (int b = 0; b < kBandCountBlocks; ++b) v[b] = b < a.nblk ? h[(int64_t)b * kBandBuckets] : 0u;
   if (!band_active(a.st[row])) return;
   uint32_t run = 0u;
+  for (int b0 = 0; b0 < a.nblk; b0 += kBandCountBlocks) {
+    if (b0 > 0) {
 #pragma unroll
-  for (int b = 0; b < kBandCountBlocks; ++b) {
-    if (b < a.nblk) h[(int64_t)b * kBandBuckets] = run;
-    run += v[b];
+      for (int b = 0; b < kBandCountBlocks; ++b)
+        v[b] = b0 + b < a.nblk ? h[(int64_t)(b0 + b) * kBandBuckets] : 0u;
+    }
+#pragma unroll
+    for (int b = 0; b < kBandCountBlocks; ++b) {
+      if (b0 + b < a.nblk) h[(int64_t)(b0 + b) * kBandBuckets] = run;
+      run += v[b];
+    }
   }
-  a.btot[row * kBandBuckets + j] = run;
+  const int64_t o = row * kBandBuckets + j;
+  a.btot[o] = run;
+  if (a.r == nullptr) return;
+  // full-row mode: key extremes over the workgroups (an empty share holds
+  // ~0 and 0), a batch of loads at a time
+  constexpr int kExtBatch = 16;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  for (int b0 = 0; b0 < a.nblk; b0 += kExtBatch) {
+    uint32_t lo[kExtBatch], hi[kExtBatch];
+#pragma unroll
+    for (int b = 0; b < kExtBatch; ++b) {
+      const bool in = b0 + b < a.nblk;
+      lo[b] = in ? ext[(int64_t)(b0 + b) * (2 * kBandBuckets)] : 0xFFFFFFFFu;
+      hi[b] = in ? ext[(int64_t)(b0 + b) * (2 * kBandBuckets) + kBandBuckets] : 0u;
+    }
+#pragma unroll
+    for (int b = 0; b < kExtBatch; ++b) {
+      kmn = min(kmn, lo[b]);
+      kmx = max(kmx, hi[b]);
+    }
+  }
+  a.bkey[2 * o] = kmn;
+  a.bkey[2 * o + 1] = kmx;
+  a.bsum[2 * o] = 0ull;
+  a.bsum[2 * o + 1] = 0ull;
 }
 
 __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
@@ -367,14 +427,15 @@ LDEV void bucket_agg(const uint32_t *kb, int cnt, double c, TileAgg *out) {
   if (team.lane == 0) agg_write(out, kmx, kmn, sp, ss, fb);
 }
 
-// Each workgroup owns kAggGroup consecutive buckets of one row, one per
-// 16-lane team; a bucket of more than kAggTeamMax keys is left to a whole
-// wave, the workgroup's large buckets dealt out to its waves in turn.
+// Band mode (a band's buckets hold a few dozen keys each): each workgroup
+// owns kAggGroup consecutive buckets of one row, one per 16-lane team; a
+// bucket of more than kAggTeamMax keys is left to a whole wave, the
+// workgroup's large buckets dealt out to its waves in turn.
 constexpr int kAggTeam = 16;
 constexpr int kAggGroup = kBT / kAggTeam;
 constexpr int kAggTeamMax = 4 * kAggE * kAggTeam;
 
-__global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
+__global__ __launch_bounds__(kBT) void band_agg_buckets_kernel(BandArgs a) {
   __shared__ uint32_t big;  // the workgroup's buckets too large for a team
   int64_t row;
   int blk;
@@ -418,6 +479,88 @@ __global__ __launch_bounds__(kBT) void band_agg_kernel(BandArgs a) {
   }
 }
 
+// Full-row mode: the key bits of a whole row can put millions of scores in
+// one bucket, so the work is split by key ranges, not by buckets.  Each
+// workgroup takes kAggChunk consecutive bucketed keys (a window of
+// consecutive buckets; 16 consecutive keys per thread, whose terms are
+// summed in registers over each run of one bucket), adds the runs into LDS
+// sums of the window and each window sum into the bucket's global sums with
+// one integer atomic.  The anchors are the bucket extremes the count and
+// scan recorded; integer sums make the order of the adds irrelevant.
+constexpr int kAggKeysPerThread = 16;
+constexpr int kAggChunk = kBT * kAggKeysPerThread;
+
+__global__ __launch_bounds__(kBT) void band_agg_keys_kernel(BandArgs a) {
+  __shared__ unsigned long long sp[kBandBuckets], ss[kBandBuckets];
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const int64_t row = blockIdx.y;
+  const RowState &S = a.st[row];
+  if (!band_active(S)) return;
+  const int64_t M = a.n;
+  const int64_t c0 = (int64_t)blockIdx.x * kAggChunk;
+  if (c0 >= M) return;
+  const int64_t c1 = min(M, c0 + (int64_t)kAggChunk);
+  double rk, rt, c;
+  float rcf;
+  band_row_params(a, S, rk, rt, c, rcf);
+  const uint32_t kmin = S.kmin;
+  const int shift = band_shift(S, a.bbits);
+  const uint32_t *kb = a.keys + row * a.cap;
+  const int64_t o = row * kBandBuckets;
+  // this thread's keys, loaded first (the row stride is a multiple of 4 keys)
+  constexpr int E = kAggKeysPerThread;
+  const int64_t t0 = c0 + (int64_t)threadIdx.x * E;
+  uint32_t key[E];
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    const u4 v = t0 + 4 * q < c1 ? *reinterpret_cast<const u4 *>(kb + t0 + 4 * q) : u4{0u, 0u, 0u, 0u};
+    key[4 * q] = v.x;
+    key[4 * q + 1] = v.y;
+    key[4 * q + 2] = v.z;
+    key[4 * q + 3] = v.w;
+  }
+  // the keys are in bucket order: the window is first key's bucket .. last key's
+  const uint32_t jf = (kb[c0] - kmin) >> shift, jl = (kb[c1 - 1] - kmin) >> shift;
+  for (uint32_t j = jf + threadIdx.x; j <= jl; j += kBT) {
+    sp[j - jf] = 0ull;
+    ss[j - jf] = 0ull;
+  }
+  __syncthreads();
+  const int nv = (int)max(min(c1 - t0, (int64_t)E), (int64_t)0);
+  if (nv > 0) {
+    uint32_t cj = (key[0] - kmin) >> shift;
+    uint32_t kn = a.bkey[2 * (o + cj)], kx = a.bkey[2 * (o + cj) + 1];
+    int fb = agg_frac_bits(a.btot[o + cj]);
+    unsigned long long accp = 0ull, accs = 0ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e < nv) {
+        const uint32_t j = (key[e] - kmin) >> shift;
+        if (j != cj) {  // a new run: flush the last one
+          atomicAdd(&sp[cj - jf], accp);
+          atomicAdd(&ss[cj - jf], accs);
+          accp = accs = 0ull;
+          cj = j;
+          kn = a.bkey[2 * (o + j)];
+          kx = a.bkey[2 * (o + j) + 1];
+          fb = agg_frac_bits(a.btot[o + j]);
+        }
+        const double x = (double)value_of(key[e]);
+        accp += fixed_term(wexp(x - (double)value_of(kx), c), fb);
+        accs += fixed_term(wexp((double)value_of(kn) - x, c), fb);
+      }
+    }
+    atomicAdd(&sp[cj - jf], accp);
+    atomicAdd(&ss[cj - jf], accs);
+  }
+  __syncthreads();
+  for (uint32_t j = jf + threadIdx.x; j <= jl; j += kBT) {
+    const unsigned long long p = sp[j - jf], q = ss[j - jf];
+    if (p != 0ull) atomicAdd(&a.bsum[2 * (o + j)], p);
+    if (q != 0ull) atomicAdd(&a.bsum[2 * (o + j) + 1], q);
+  }
+}
+
 // ---------------------------------------------------------------- locate
 // One workgroup of kLocT threads per row.  Its first kLocScanT threads
 // (two waves per SIMD) search the buckets, kLocPer consecutive buckets each:
@@ -456,11 +599,26 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
   TileAgg g[kLocPer];
   uint32_t cnt[kLocPer];
   const int nb = 1 << a.bbits;
+  if (a.r == nullptr) {
 #pragma unroll
-  for (int u = 0; u < kLocPer; ++u) {
-    const bool in = threadIdx.x < kLocScanT && j0 + u < nb;
-    g[u] = in ? a.bagg[o + j0 + u] : TileAgg{0.0f, 0.0f, 0.0, 0.0};
-    cnt[u] = in ? a.btot[o + j0 + u] : 0u;
+    for (int u = 0; u < kLocPer; ++u) {
+      const bool in = threadIdx.x < kLocScanT && j0 + u < nb;
+      g[u] = in ? a.bagg[o + j0 + u] : TileAgg{0.0f, 0.0f, 0.0, 0.0};
+      cnt[u] = in ? a.btot[o + j0 + u] : 0u;
+    }
+  } else {
+    // full-row mode: P-type sums anchored at the largest key, S-type at the
+    // smallest, from the fixed-point sums
+#pragma unroll
+    for (int u = 0; u < kLocPer; ++u) {
+      const bool in = threadIdx.x < kLocScanT && j0 + u < nb;
+      const int64_t q = o + j0 + u;
+      cnt[u] = in ? a.btot[q] : 0u;
+      const int fb = cnt[u] > 0u ? agg_frac_bits(cnt[u]) : 0;
+      g[u] = cnt[u] > 0u ? TileAgg{value_of(a.bkey[2 * q + 1]), value_of(a.bkey[2 * q]),
+                                   fixed_value(a.bsum[2 * q], fb), fixed_value(a.bsum[2 * q + 1], fb)}
+                         : TileAgg{0.0f, 0.0f, 0.0, 0.0};
+    }
   }
   const bool active = band_active(S);
   if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
@@ -492,7 +650,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
                                           : wave_sort_solve<16>(kb, (int)cJ, part, rk, rt, c, rcf);
         if (lane == 0) sel_b = bb;
       }
-    } else {
+    } else if (cJ <= (int64_t)kFallbackSort || band_shift(S, a.bbits) == 0) {
       // a bucket of several tiles: sorted in place by the workgroup, its tile
       // aggregates, then locate over them
       const int shift = band_shift(S, a.bbits);
@@ -500,6 +658,31 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
           kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, slo, shi, cR_eff, part.first,
           part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, rk, rt,
           c, rcf, L.fb);
+      if (threadIdx.x == 0) sel_b = bb;
+    } else {
+      // a crowded bucket (the key bits of a whole row spread values over
+      // binades, so one bucket can hold millions of keys): the nested bucket
+      // selection of the fallback on its keys, seeded with everything around
+      // it; gathers go to the scratch keys, then alternate with this row's
+      // bucketed keys (the bucket is read only by the first gather)
+      const int shift = band_shift(S, a.bbits);
+      const uint32_t kb0 = S.kmin + ((uint32_t)J << shift);
+      SegArgs sub = fb;
+      sub.A = a.tmp;
+      sub.B = a.keys;
+      sub.stride = a.cap;
+      sub.max_tiles = a.max_tiles;
+      sub.tagg = a.tagg;
+      sub.tpre = a.tpre;
+      sub.tsuf = a.tsuf;
+      sub.st = a.st;
+      sub.k = rk;
+      sub.t = rt;
+      sub.c = c;
+      sub.cf = rcf;
+      const uint64_t top = (uint64_t)kb0 + ((1ull << shift) - 1ull);  // the bucket's key bound
+      const uint32_t kb1 = top < (uint64_t)S.kmax ? (uint32_t)top : S.kmax;
+      const double bb = bucket_set_solve<kLocT>(sub, (int)row, kb, cJ, 0, kb0, kb1, slo, shi, cR_eff, L.fb);
       if (threadIdx.x == 0) sel_b = bb;
     }
     __syncthreads();
@@ -530,8 +713,14 @@ int bucket_bits(int64_t keys) {
 }
 
 int full_count_blocks(int64_t n, int64_t *chunk) {
+  // at least a tile per workgroup; up to kBandCountBlocks workgroups, more
+  // for rows beyond 2^22 scores (a chunk of at most 2^16 scores each, so a
+  // 1e8 row is bucketed by ~1500 workgroups instead of 64)
   int64_t nblk = (n + kTile - 1) / kTile;
-  if (nblk > kBandCountBlocks) nblk = kBandCountBlocks;
+  int64_t most = (n + kFullChunkMax - 1) / kFullChunkMax;
+  if (most < kBandCountBlocks) most = kBandCountBlocks;
+  if (most > kFullCountBlocksMax) most = kFullCountBlocksMax;
+  if (nblk > most) nblk = most;
   if (nblk < 1) nblk = 1;
   int64_t c = (n + nblk - 1) / nblk;
   c = (c + 3) / 4 * 4;
@@ -546,7 +735,12 @@ hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t
   const int nb = 1 << a.bbits;
   hipLaunchKernelGGL(band_scan_kernel, dim3((nb + kBT - 1) / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(band_agg_kernel, dim3((nb + kAggGroup - 1) / kAggGroup, (unsigned)a.rows), dim3(kBT), 0, s, a);
+  if (a.r != nullptr)
+    hipLaunchKernelGGL(band_agg_keys_kernel, dim3((unsigned)((a.n + kAggChunk - 1) / kAggChunk), (unsigned)a.rows),
+                       dim3(kBT), 0, s, a);
+  else
+    hipLaunchKernelGGL(band_agg_buckets_kernel, dim3((nb + kAggGroup - 1) / kAggGroup, (unsigned)a.rows), dim3(kBT),
+                       0, s, a);
   hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kLocT), 0, s, a, fb);
   return hipGetLastError();
 }

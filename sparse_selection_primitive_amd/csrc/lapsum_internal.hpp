@@ -62,7 +62,9 @@ struct SegArgs {
 // sorted.
 constexpr int kBandBucketBits = 11;
 constexpr int kBandBuckets = 1 << kBandBucketBits;
-constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row, at most
+constexpr int kBandCountBlocks = 64;  // count/scatter workgroups per row (band mode), at most
+constexpr int64_t kFullChunkMax = 1 << 16;  // full-row mode: scores per count/scatter workgroup beyond that
+constexpr int64_t kFullCountBlocksMax = 4096;
 
 struct FilterPartial;
 
@@ -83,9 +85,14 @@ struct BandArgs {
   uint32_t *keys;       // [rows][cap] bucketed band keys (the balancing bucket sorted by the locate)
   uint32_t *tmp;        // [rows][cap] scratch of the large-bucket sort
   uint32_t *hist;       // [rows][nblk][kBandBuckets] counts -> offsets inside buckets
+  uint32_t *hext;       // full-row mode: [rows][nblk][2][kBandBuckets] key minimum / maximum per count
+                        // workgroup and bucket
   uint32_t *btot;       // [rows][kBandBuckets] bucket sizes
   uint32_t *bstart;     // [rows][kBandBuckets] bucket starts
-  TileAgg *bagg;        // [rows][kBandBuckets] anchored aggregates of the buckets
+  TileAgg *bagg;        // band mode: [rows][kBandBuckets] anchored aggregates of the buckets
+  uint32_t *bkey;       // full-row mode: [rows][kBandBuckets][2] smallest and largest key of each bucket
+  unsigned long long *bsum;  // full-row mode: [rows][kBandBuckets][2] fixed-point sums anchored at the
+                             // largest / smallest key
   TileAgg *tagg;        // [rows][max_tiles] tile aggregates of a large balancing bucket
   Pre *tpre;            // [rows][max_tiles]
   Suf *tsuf;            // [rows][max_tiles]

@@ -195,6 +195,23 @@ def test_fullsort_tight_cluster(L, O):
     full_check("fullsort tight cluster", L, O, r, g, 30000.5, 1e-3, path="fullsort")
 
 
+def test_fullsort_crowded_bucket(L, O):
+    """Full-sort path on a 3M-score normal row with the root near 1.06: the
+    key bits put about 84K scores of [1, 1.125) into the balancing bucket,
+    above what the workgroup sorts directly, so the locate runs the nested
+    bucket selection on that bucket (seeded with everything around it); the
+    result must match the oracle and repeat bitwise."""
+    g0 = np.random.Generator(np.random.PCG64(3651))
+    n = 3_000_000
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = float(np.sum(r > 1.06)) + 0.5
+    res, _, _ = full_check("fullsort crowded bucket", L, O, r, g, k, 0.01, path="fullsort")
+    again = run(L, r, k, 0.01, g, path="fullsort")
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(res[key], again[key]), key
+
+
 @pytest.mark.parametrize("k", [1e-3, 0.5, 9999.5])
 def test_fullsort_end_budgets(L, O, k):
     """Budgets near 0 and near n: the balancing bucket is the first or the
