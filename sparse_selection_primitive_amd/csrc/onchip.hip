@@ -98,19 +98,21 @@ LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (
 // sorts the whole row) when k and n - k both exceed the lane count or the
 // candidates overflow the 4*LANES buffer.  buf: this team's 4*LANES floats
 // of LDS.
-template <int E, int LANES>
+// MIRROR (the complement, k > LANES) is a template argument so the sign
+// folds into the instructions' operand modifiers.
+template <int E, int LANES, bool MIRROR>
 LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const bool (&valid)[E], int n, double k,
                        double t, double c, float cf, float *buf, double &b_out) {
   constexpr int CAP = 4 * LANES;
-  const bool mirror = k > (double)LANES;
-  const double kk = mirror ? (double)n - k : k;
+  const double kk = MIRROR ? (double)n - k : k;
   if (kk > (double)LANES) return false;
-  const float sg = mirror ? -1.0f : 1.0f;
+  constexpr float sg = MIRROR ? -1.0f : 1.0f;
   float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    // the two largest: m2 <= m1 stays true, so the new second is a median
     const float w = valid[e] ? sg * v[e] : -INFINITY;
-    m2 = fmaxf(m2, fminf(m1, w));
+    m2 = __builtin_amdgcn_fmed3f(m1, m2, w);
     m1 = fmaxf(m1, w);
   }
   float x[1] = {m2};
@@ -167,7 +169,7 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
     part.nvalid = nv;
     bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
   }
-  b_out = mirror ? -bw : bw;
+  b_out = MIRROR ? -bw : bw;
   return true;
 }
 
@@ -192,7 +194,9 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
   double b = 0.0;
   bool done = !ok;  // rows past the end compute nothing and store nothing
   if constexpr (Team::kLanes <= kWave) {
-    if (wbuf != nullptr && !done) done = window_solve<E>(team, v, valid, n, k, t, c, cf, wbuf, b);
+    if (wbuf != nullptr && !done)
+      done = k > (double)LANES ? window_solve<E, LANES, true>(team, v, valid, n, k, t, c, cf, wbuf, b)
+                               : window_solve<E, LANES, false>(team, v, valid, n, k, t, c, cf, wbuf, b);
   }
   if (!done) {
     // the scores themselves are sorted (finite, so fp32 order is numeric
@@ -218,12 +222,14 @@ LDEV void onchip_row_forward(const Team &team, const float *rr, int n_arg, bool 
   }
 
   // p = F((x - b)/t) in fp32 with b split into bh + bl: x - bh is exact or
-  // rounds relative to itself, so p carries a few 1e-8 absolute error at most
+  // rounds relative to itself, and (x - bh) cf - bl cf is one fused
+  // multiply-add, so p carries a few 1e-8 absolute error at most
   const float bh = (float)b, bl = (float)(b - (double)bh);
+  const float blcf = bl * cf;
   float out[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float z2 = ((v[e] - bh) - bl) * cf;
+    const float z2 = __builtin_fmaf(v[e] - bh, cf, -blcf);
     const float h = __builtin_amdgcn_exp2f(-1.0f - fabsf(z2));  // e^{-|z|}/2
     out[e] = z2 < 0.0f ? h : 1.0f - h;
   }
