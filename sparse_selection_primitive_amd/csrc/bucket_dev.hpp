@@ -303,6 +303,13 @@ LDEV void fallback_each_key(const SegArgs &a, int row, const uint32_t *src, int6
 // kmax bound its keys; slo / shi hold everything below / above it and cR
 // counts the elements above it.  Gathers go to the row's key buffer
 // `cur` (0: A, 1: B) first, then alternate.  Returns b on every thread.
+// Bucket of a key in a set bucketed by its bits above kmin (clamped to the
+// last bucket).
+LDEV uint32_t bucket_of(uint32_t key, uint32_t kmin, int shift) {
+  const uint32_t j = (key - kmin) >> shift;
+  return j < (uint32_t)(kFallbackBuckets - 1) ? j : (uint32_t)(kFallbackBuckets - 1);
+}
+
 template <int NT>
 LDEV double bucket_set_solve(const SegArgs &a, int row, const uint32_t *src, int64_t len, int cur, uint32_t kmin,
                              uint32_t kmax, Pre slo, Suf shi, double cR, SegLds<NT> &L) {
@@ -328,7 +335,7 @@ LDEV double bucket_set_solve(const SegArgs &a, int row, const uint32_t *src, int
     }
     __syncthreads();
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const uint32_t j = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1));
+      const uint32_t j = bucket_of(key, kmin, shift);
       atomicAdd(&B.cnt[j], 1u);
       atomicMax(&B.kmx[j], key);
       atomicMin(&B.kmn[j], key);
@@ -336,7 +343,7 @@ LDEV double bucket_set_solve(const SegArgs &a, int row, const uint32_t *src, int
     __syncthreads();
     // fixed-point sums anchored at the bucket extremes
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const uint32_t j = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1));
+      const uint32_t j = bucket_of(key, kmin, shift);
       const int fb = agg_frac_bits(B.cnt[j]);
       const double x = (double)value_of(key);
       atomicAdd(&B.sp[j], fixed_term(wexp(x - (double)value_of(B.kmx[j]), c), fb));
@@ -372,7 +379,7 @@ LDEV double bucket_set_solve(const SegArgs &a, int row, const uint32_t *src, int
     const uint32_t J = (uint32_t)P.J;
     uint32_t *dst = buf[cur];
     fallback_each_key(a, row, src, len, NT, [&](uint32_t key) {
-      const bool in = min((key - kmin) >> shift, (uint32_t)(kFallbackBuckets - 1)) == J;
+      const bool in = bucket_of(key, kmin, shift) == J;
       const unsigned long long m = __ballot(in);
       if (m != 0ull) {
         const int leader = __ffsll((long long)m) - 1;

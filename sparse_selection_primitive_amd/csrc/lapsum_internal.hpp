@@ -16,7 +16,6 @@ struct Pre;
 struct Suf;
 
 constexpr int kTile = 4096;          // keys per tile of the large-row sort and scan
-constexpr int kSegThreads = 256;     // threads per workgroup of the large-row kernels
 constexpr int kSelectCap = 1024;     // direct-selection capacity of the bracket select
 constexpr int kStreamThreads = 256;  // threads per workgroup of the streaming kernels
 constexpr int kUnroll = 4;           // independent 16 B loads per thread per stream and iteration

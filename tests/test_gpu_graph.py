@@ -30,19 +30,31 @@ def _case(kind):
     if kind == "coder_bracket":
         w = workloads.coder(rows=8)
         return w.r, w.g, w.k, w.t, "bracket"
+    if kind == "fullsort_crowded":
+        # whole-row buckets of millions of keys: key-range bucket sums with
+        # integer atomics, nested selection inside the balancing bucket
+        g0 = np.random.Generator(np.random.PCG64(3502))
+        r = g0.standard_normal((1, 3_000_000)).astype(np.float32)
+        k = float(np.sum(r > 1.06)) + 0.5
+        return r, g0.standard_normal((1, 3_000_000)).astype(np.float32), k, 0.01, "fullsort"
     g0 = np.random.Generator(np.random.PCG64(3501))  # band above one workgroup
     r = g0.standard_normal((1, 2_000_000)).astype(np.float32)
     return r, g0.standard_normal((1, 2_000_000)).astype(np.float32), 20000.0, 0.01, "bracket"
 
 
-@pytest.mark.parametrize("kind", ["routing", "coder_bracket", "bucket_band"])
+@pytest.mark.parametrize("kind", ["routing", "routing_per_row", "coder_bracket", "bucket_band", "fullsort_crowded"])
 def test_graph_replay_matches_eager(L, kind):
-    r0, g0, k, t, path = _case(kind)
+    r0, g0, k, t, path = _case(kind.replace("_per_row", ""))
     rows, n = r0.shape
     dev = torch.device("cuda:0")
     r, g = torch.from_numpy(r0).to(dev), torch.from_numpy(g0).to(dev)
     other = torch.from_numpy(np.ascontiguousarray(r0[:, ::-1]) * 0.5).to(dev)
-    op = L.Operator(rows, n, k, t, device=dev, path=path)
+    per_row = {}
+    if kind.endswith("_per_row"):
+        gk = np.random.Generator(np.random.PCG64(3503))
+        per_row = dict(k_rows=torch.from_numpy(gk.uniform(1.0, 20.0, rows)).to(dev),
+                       t_rows=torch.from_numpy(gk.uniform(0.02, 0.2, rows)).to(dev))
+    op = L.Operator(rows, n, k, t, device=dev, path=path, **per_row)
     outs = [torch.empty_like(r), torch.empty(rows, dtype=torch.float64, device=dev), torch.empty_like(r),
             torch.empty(rows, dtype=torch.float32, device=dev)]
     p, b, dr, dk = outs
