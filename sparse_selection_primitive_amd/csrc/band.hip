@@ -562,30 +562,35 @@ __global__ __launch_bounds__(kBT) void band_agg_keys_kernel(BandArgs a) {
 }
 
 // ---------------------------------------------------------------- locate
-// One workgroup of kLocT threads per row.  Its first kLocScanT threads
+// One workgroup per row: 1024 threads for whole rows (crowded buckets are
+// common there), 512 for bands, where a bucket beyond one wave is rare: a
+// thread then has 256 registers instead of 128, and the bucket search and
+// the one-wave solve no longer spill.  Its first kLocScanT threads
 // (two waves per SIMD) search the buckets, kLocPer consecutive buckets each:
 // a scan of the bucket aggregates between the tail seeds (DPP inside waves,
 // the wave totals through LDS), the threshold curve at the bucket ends and
 // the balancing bucket.  Only that bucket is sorted: by one wave in
 // registers when it holds at most 1024 keys, else by the whole workgroup
 // (radix passes in place, then tile aggregates), and the root is taken
-// inside it.  A row whose root falls outside its bracket is then sorted and
-// solved in full by the same workgroup (the deterministic fallback), so no
-// separate launch is needed.
-constexpr int kLocT = 1024;
+// inside it.  A row whose root falls outside its bracket (or whose band
+// overflowed) is then widened or solved in full by the same workgroup, so no
+// separate launch is needed; whole rows have no bracket and never take it.
 constexpr int kLocScanT = 512;                     // threads of the bucket search
 constexpr int kLocScanW = kLocScanT / kWave;
 constexpr int kLocPer = kBandBuckets / kLocScanT;  // buckets per search thread
 static_assert(kLocPer * kLocScanT == kBandBuckets, "every bucket has a search thread");
 static_assert(kLocScanW <= 16, "wave totals are scanned inside one DPP row");
 
+template <int NT>
 union BandLocLds {
-  BlockTeamLds<kLocT, 1> team;
-  SegLds<kLocT> fb;
+  BlockTeamLds<NT, 1> team;
+  SegLds<NT> fb;
 };
 
-__global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs fb) {
-  __shared__ BandLocLds L;
+template <bool FULL, int NT = FULL ? 1024 : 512>
+__global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb) {
+  static_assert(NT >= kLocScanT, "the bucket search needs kLocScanT threads");
+  __shared__ BandLocLds<NT> L;
   __shared__ double sel_b;
   __shared__ int sel_fb;
   const int64_t row = xcd_linear();
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
     const Pre seed_lo{(float)S.a_lo, S.count_lo ? S.tail_lo : 0.0};
     const Suf seed_hi{(float)S.a_hi, S.count_hi ? S.tail_hi : 0.0};
     const double cR = (double)S.count_hi;
-    const BucketPick P = bucket_search<kLocT, kLocScanT, kLocPer>(g, cnt, seed_lo, seed_hi, cR, M, rk, c);
+    const BucketPick P = bucket_search<NT, kLocScanT, kLocPer>(g, cnt, seed_lo, seed_hi, cR, M, rk, c);
     const int J = P.J;
     const int64_t cJ = P.cnt, sJ = P.start;
     const Pre slo{P.lo_a, P.lo_s};
@@ -654,7 +659,7 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       // a bucket of several tiles: sorted in place by the workgroup, its tile
       // aggregates, then locate over them
       const int shift = band_shift(S, a.bbits);
-      const double bb = sorted_range_solve<kLocT>(
+      const double bb = sorted_range_solve<NT>(
           kb, a.tmp + row * a.cap + sJ, cJ, S.kmin + ((uint32_t)J << shift), shift, slo, shi, cR_eff, part.first,
           part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, rk, rt,
           c, rcf, L.fb);
@@ -682,22 +687,24 @@ __global__ __launch_bounds__(kLocT) void band_locate_kernel(BandArgs a, SegArgs 
       sub.cf = rcf;
       const uint64_t top = (uint64_t)kb0 + ((1ull << shift) - 1ull);  // the bucket's key bound
       const uint32_t kb1 = top < (uint64_t)S.kmax ? (uint32_t)top : S.kmax;
-      const double bb = bucket_set_solve<kLocT>(sub, (int)row, kb, cJ, 0, kb0, kb1, slo, shi, cR_eff, L.fb);
+      const double bb = bucket_set_solve<NT>(sub, (int)row, kb, cJ, 0, kb0, kb1, slo, shi, cR_eff, L.fb);
       if (threadIdx.x == 0) sel_b = bb;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
       const double bb = (S.flags & LAPSUM_FLAG_INVALID) ? __builtin_nan("") : sel_b;
       S.b = bb;
-      if (a.r == nullptr) {  // certification against the bracket
+      if (!FULL) {  // certification against the bracket
         const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
         S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
         sel_fb = hit ? 0 : 1;
       }
     }
   }
-  __syncthreads();
-  if (sel_fb) missed_row<kLocT>(fb, (int)row, L.fb);
+  if constexpr (!FULL) {
+    __syncthreads();
+    if (sel_fb) missed_row<NT>(fb, (int)row, L.fb);
+  }
 }
 
 int band_count_blocks(int gx, int *group) {
@@ -741,7 +748,10 @@ hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t
   else
     hipLaunchKernelGGL(band_agg_buckets_kernel, dim3((nb + kAggGroup - 1) / kAggGroup, (unsigned)a.rows), dim3(kBT),
                        0, s, a);
-  hipLaunchKernelGGL(band_locate_kernel, dim3((unsigned)a.rows), dim3(kLocT), 0, s, a, fb);
+  if (a.r != nullptr)
+    hipLaunchKernelGGL(band_locate_kernel<true>, dim3((unsigned)a.rows), dim3(1024), 0, s, a, fb);
+  else
+    hipLaunchKernelGGL(band_locate_kernel<false>, dim3((unsigned)a.rows), dim3(512), 0, s, a, fb);
   return hipGetLastError();
 }
 

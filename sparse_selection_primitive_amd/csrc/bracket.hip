@@ -80,23 +80,34 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__r
   const int64_t g0 = (int64_t)blockIdx.x * kSampleWg;
   if (blockIdx.x == 0 && threadIdx.x == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state
   cnt[threadIdx.x] = 0u;
-  // indices and noise of this thread's samples first, then all the gathers
+  // indices of this thread's samples first and all the gathers issued, then
+  // the noise, whose logarithms overlap the gathers' latency
   const uint64_t nn = (uint64_t)n;
   int64_t idx[kSamplePerThread];
-  double lap[kSamplePerThread];
+  uint32_t ubits[kSamplePerThread];
 #pragma unroll
   for (int q = 0; q < kSamplePerThread; ++q) {
     const int64_t j = g0 + q * kSampleThreads + threadIdx.x;
     uint32_t c[4] = {(uint32_t)j, (uint32_t)row, 0u, 0u};
     philox4x32_10(c, k0, k1);
     idx[q] = (int64_t)(((uint64_t)c[1] * nn + (((uint64_t)c[0] * nn) >> 32)) >> 32);
-    const double u = ((double)c[2] + 0.5) * 0x1p-32;
-    lap[q] = u < 0.5 ? log(2.0 * u) : -log(2.0 * (1.0 - u));
+    ubits[q] = c[2];
   }
+  // unconditional loads (score 0 stands in past the sample's end), so no
+  // branch makes each gather wait before the next is issued
   float rv[kSamplePerThread];
 #pragma unroll
   for (int q = 0; q < kSamplePerThread; ++q)
-    rv[q] = (g0 + q * kSampleThreads + threadIdx.x < m) ? r[row * n + idx[q]] : 0.0f;
+    rv[q] = r[row * n + ((g0 + q * kSampleThreads + threadIdx.x < m) ? idx[q] : 0)];
+  // L = F^-1(u): ln(2u) below 1/2, -ln(2(1 - u)) above (one logarithm)
+  double lap[kSamplePerThread];
+#pragma unroll
+  for (int q = 0; q < kSamplePerThread; ++q) {
+    const double u = ((double)ubits[q] + 0.5) * 0x1p-32;
+    const bool low = u < 0.5;
+    const double l = log(2.0 * (low ? u : 1.0 - u));
+    lap[q] = low ? l : -l;
+  }
   float x[kSamplePerThread];
   uint32_t bin[kSamplePerThread], slot[kSamplePerThread];
   __syncthreads();
