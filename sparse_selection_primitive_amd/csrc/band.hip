@@ -132,12 +132,36 @@ LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint3
     for_each_row_key(a, row, blk, f);
     return;
   }
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  // band mode: this workgroup's slots hold the band positions sb[0] ..
+  // sb[ns]; thread t takes positions t, t + kBT, ... of that range, U at a
+  // time, every load issued before any key is used (a slot's keys are a
+  // contiguous run, so positions map to slots by the bounds in sb)
+  constexpr int U = 8;
   const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
-  for (int i = w; i < ns; i += kBT / kWave) {
-    const uint32_t cnt = sb[i + 1] - sb[i];
-    const uint32_t *src = a.slots + (row * a.gx + s0 + i) * (int64_t)kBandSlot;
-    for (uint32_t q = lane; q < cnt; q += kWave) f(src[q]);
+  const uint32_t first = sb[0], total = sb[ns] - first;
+  const uint32_t *src = a.slots + (row * a.gx + s0) * (int64_t)kBandSlot;
+  for (uint32_t f0 = 0; f0 < total; f0 += U * kBT) {
+    // slot of this thread's first position: the last i with sb[i] <= it
+    const uint32_t g0 = first + min(f0 + threadIdx.x, total - 1u);
+    int sl = 0, hi = ns - 1;
+    while (sl < hi) {
+      const int mid = (sl + hi + 1) >> 1;
+      if (sb[mid] <= g0) sl = mid;
+      else hi = mid - 1;
+    }
+    uint32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t fi = f0 + u * kBT + threadIdx.x;
+      const bool in = fi < total;
+      const uint32_t g = first + fi;
+      if (in)
+        while (sb[sl + 1] <= g) ++sl;  // positions only grow with u
+      key[u] = src[in ? (int64_t)sl * kBandSlot + (g - sb[sl]) : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (f0 + u * kBT + threadIdx.x < total) f(key[u]);
   }
 }
 

@@ -38,23 +38,37 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
   __shared__ uint32_t lds_k[3 * NW];
   __shared__ uint32_t wsum[NW];
   __shared__ FilterTotals tot;
-  // a contiguous chunk of partials per thread, so the offsets come out in order
+  // a contiguous chunk of partials per thread, so the offsets come out in
+  // order; loaded four at a time at clamped indices (no load waits for the
+  // previous one), the counts kept for the offsets
+  constexpr int PMAX = (kMaxFilterBlocks + NT - 1) / NT;  // partials per thread, at most
+  static_assert(PMAX % 4 == 0, "partials are loaded four at a time");
   const int per = (gx + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
   double a = 0.0, b = 0.0;
   unsigned long long c0 = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, csum = 0u, big = 0u;
-  for (int i = 0; i < per; ++i) {
-    const int j = b0 + i;
-    if (j < gx) {
-      const FilterPartial fp = vp[j];
-      a += fp.sl;
-      b += fp.sr;
-      c0 += fp.cnl;
-      mn = min(mn, fp.kmn);
-      mx = max(mx, fp.kmx);
-      csum += fp.cnt;
-      big |= fp.cnt > (uint32_t)kBandSlot ? 1u : 0u;
+  uint32_t cs[PMAX];
+#pragma unroll
+  for (int c = 0; c < PMAX; c += 4) {
+    FilterPartial fp[4] = {};
+    if (c < per) {  // uniform over the workgroup
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fp[q] = vp[min(b0 + c + q, gx - 1)];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool in = c + q < per && b0 + c + q < gx;
+      cs[c + q] = in ? fp[q].cnt : 0u;
+      if (in) {
+        a += fp[q].sl;
+        b += fp[q].sr;
+        c0 += fp[q].cnl;
+        mn = min(mn, fp[q].kmn);
+        mx = max(mx, fp[q].kmx);
+        csum += fp[q].cnt;
+        big |= fp[q].cnt > (uint32_t)kBandSlot ? 1u : 0u;
+      }
     }
   }
   // exclusive scan of the chunk sums: inside each DPP row of 16 lanes, then
@@ -69,11 +83,11 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
     total += wsum[i];
   }
   uint32_t run = before + inc - csum;
-  for (int i = 0; i < per; ++i) {
-    const int j = b0 + i;
-    if (j < gx) {
-      ro[j] = run;
-      run += vp[j].cnt;
+#pragma unroll
+  for (int i = 0; i < PMAX; ++i) {
+    if (i < per && b0 + i < gx) {
+      ro[b0 + i] = run;
+      run += cs[i];
     }
   }
   if (threadIdx.x == NT - 1) ro[gx] = total;

@@ -485,14 +485,18 @@ LDEV void band_onchip_row(const uint32_t *__restrict__ slots, const uint32_t *so
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    // every load issued unconditionally (slot 0's first key past the band's
+    // end), so none waits for the one before
     const int j = base + e;
-    if (j < m) {
+    const bool in = j < m;
+    if (in)
       while ((int)soffs[b + 1] <= j) ++b;
-      key[e] = slots[(row * gx + b) * kBandSlot + (j - (int)soffs[b])];
-    } else {
-      key[e] = 0xFFFFFFFFu;
-    }
+    const int64_t at = in ? (row * gx + b) * kBandSlot + (j - (int)soffs[b]) : row * gx * kBandSlot;
+    key[e] = slots[at];
   }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (base + e >= m) key[e] = 0xFFFFFFFFu;
   bitonic_sort<E>(key, team);
   const int nv = min(max(m - base, 0), E);
   float s[E];
