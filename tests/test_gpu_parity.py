@@ -602,6 +602,39 @@ def test_bucket_band_spans_zero(L, O):
     assert res["stats"]["flags"][0].item() & L.FLAG_HIT
 
 
+def test_bucket_band_clustered_rows(L, O):
+    """Band scores packed into a few stretches of the row (half of each of
+    ten 4096-score stretches, all else far from b): the filter's band slots
+    are full or empty, so the bucket passes see groups of slots with no key
+    at all next to groups with ~2K keys per slot; the bucketed band solve is
+    forced.  Then the same row sorted: the band is one contiguous run that
+    overflows a single filter workgroup's slot, and the row is widened or
+    solved in full -- exact either way."""
+    g0 = np.random.Generator(np.random.PCG64(3401))
+    n, t = 2_000_000, 0.01
+    r = (g0.standard_normal(n) - 12.0).astype(np.float32)
+    idx = np.arange(n)
+    band = ((idx // 4096) < 10) & ((idx % 4096) < 2048)
+    r[band] = g0.uniform(0.0, 1.0, int(band.sum())).astype(np.float32)
+    top = (~band) & (idx % 997 == 5)
+    r[top] = (g0.standard_normal(int(top.sum())) + 12.0).astype(np.float32)
+    r = r[None, :]
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = float(top.sum()) + 0.5 * float(band.sum()) + 0.25
+    assert L.plan(1, n, k, t, path="bracket", band_capacity=1 << 16)["band_onchip"] == 0
+    res, _, _ = full_check("bucket band clustered", L, O, r, g, k, t, path="bracket", band_capacity=1 << 16,
+                           stats=True)
+    fl = res["stats"]["flags"][0].item()
+    log(f"  band M={res['stats']['band'][0].item()} flags={fl}")
+    assert fl & (L.FLAG_HIT | L.FLAG_WIDENED)
+    rs = np.sort(r, axis=1)
+    res, _, _ = full_check("bucket band sorted row", L, O, rs, g, k, t, path="bracket", band_capacity=1 << 16,
+                           stats=True)
+    fl = res["stats"]["flags"][0].item()
+    log(f"  sorted: band M={res['stats']['band'][0].item()} flags={fl}")
+    assert fl & (L.FLAG_HIT | L.FLAG_WIDENED | L.FLAG_FALLBACK)
+
+
 def test_bucket_band_forced_miss(L, O):
     """Certification on the bucketed band: a forced bracket below b must
     send every row to the fallback."""
