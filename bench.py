@@ -91,7 +91,7 @@ WORKLOADS = {
 # Source files each streaming kernel is compiled from (a change to any of them
 # invalidates the HBM traffic counters recorded for that kernel).
 _COMMON_SRC = ["lapsum_device.hpp", "lapsum_internal.hpp"]
-KERNEL_SOURCES = {"filter": ["bracket.hip"] + _COMMON_SRC,
+KERNEL_SOURCES = {"filter": ["bracket.hip", "filter_dev.hpp"] + _COMMON_SRC,
                   "apply": ["stream.hip"] + _COMMON_SRC,
                   "bwd_reduce": ["stream.hip"] + _COMMON_SRC,
                   "bwd_apply": ["stream.hip"] + _COMMON_SRC,
