@@ -119,9 +119,12 @@ __global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__re
   }
 }
 
+// Workgroups per row of the apply and backward passes: one per
+// kStreamThreads * kUnroll float4s, at most 4096 over all rows (16 per CU;
+// on the 1e8 row 4096 measured ~2 µs faster per pass than 2048, 1024 slower).
 static int stream_grid_x(int64_t rows, int64_t n) {
   const int64_t per_row_need = (n / 4 + kStreamThreads * kUnroll - 1) / (kStreamThreads * kUnroll);
-  int64_t target = 2048 / (rows > 0 ? rows : 1);
+  int64_t target = 4096 / (rows > 0 ? rows : 1);
   if (target < 1) target = 1;
   int64_t gx = per_row_need < target ? per_row_need : target;
   if (gx < 1) gx = 1;
