@@ -66,7 +66,10 @@ typedef enum lapsum_status {
     LAPSUM_ERR_HIP = 8        /* a HIP launch or runtime query failed */
 } lapsum_status;
 
-/* Longest row: sample indices use 32x32-bit products and tile counts fit int32. */
+/* Longest row: sample indices use 32x32-bit products and tile counts fit int32.
+ * Most rows per call: every path accepts up to 2^24 rows (launches fold rows
+ * over two grid dimensions, so no launch dimension exceeds its limit); the
+ * practical limit is device memory for r, p and the workspace. */
 #define LAPSUM_MAX_N ((int64_t)1 << 31)
 #define LAPSUM_MAX_ROWS ((int64_t)1 << 24)
 /* Longest row the on-chip (LDS/register) sort path takes. */
@@ -159,7 +162,9 @@ typedef struct lapsum_plan_info {
                               a_L = -inf, hi = m + 1 means a_R = +inf */
     int64_t band_capacity; /* bracketing: band buffer length per row */
     int32_t band_onchip;   /* bracketing: 1 if the band is solved on chip (capacity <= 8192) */
-    int32_t reserved;
+    int32_t filter_groups; /* bracketing: streaming-filter workgroups per row; their band slots
+                              (2048 keys each) hold at least twice the band capacity when the row
+                              is long enough to give each of them a full load */
     uint64_t forward_bytes;  /* workspace bytes lapsum_forward needs */
     uint64_t backward_bytes; /* workspace bytes lapsum_backward needs */
 } lapsum_plan_info;
@@ -209,7 +214,8 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
  *      min(p, 1 - p) is the Laplace density at the score)
  *   dr device [rows, n] fp32 output (may alias g, not p)
  *   dk device [rows]    fp32 output
- *   Only opt->stats and opt->stage_events are read.  Errors as forward. */
+ *   Only opt->stats, opt->stage_events and opt->t_rows (a temperature per
+ *   row, as in the forward) are read.  Errors as forward. */
 lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
                               float *dr, float *dk, void *workspace, size_t workspace_bytes,
                               const lapsum_options *opt, void *stream);

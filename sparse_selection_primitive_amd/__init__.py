@@ -58,7 +58,7 @@ class Options(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("sample_log2", ctypes.c_int32), ("m", ctypes.c_int64),
                 ("lo", ctypes.c_int64), ("hi", ctypes.c_int64), ("band_capacity", ctypes.c_int64),
-                ("band_onchip", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("band_onchip", ctypes.c_int32), ("filter_groups", ctypes.c_int32),
                 ("forward_bytes", ctypes.c_uint64), ("backward_bytes", ctypes.c_uint64)]
 
 
@@ -157,26 +157,28 @@ def workspace_bytes(rows: int, n: int, k: float, t: float, **opts) -> int:
 
 
 # --------------------------------------------------------------- torch side
-_ws_cache: dict = {}
-
-
 def _torch():
     import torch
     return torch
 
 
 def _workspace(nbytes: int, device):
-    """A cached, 256-byte-aligned device buffer of at least nbytes."""
+    """A 256-byte-aligned device buffer of at least nbytes for one call:
+    (buffer, aligned pointer, usable bytes).
+
+    It comes from torch's caching allocator on the current stream, which is
+    stream-ordered: once the call has been enqueued and the buffer dropped,
+    its memory goes back to the pool and is handed out again only to work
+    ordered after this call on the same stream (or to another stream after
+    the allocator has seen this stream's work end).  So calls on different
+    streams never share scratch memory, and a buffer is never reused while
+    a kernel that reads it is still queued."""
     torch = _torch()
     if nbytes == 0:
-        return None, 0
-    key = (device.type, device.index)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes + 256:
-        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+        return None, None, 0
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     ptr = buf.data_ptr()
-    return ptr + ((-ptr) % 256), buf.numel() - ((-ptr) % 256)
+    return buf, ptr + ((-ptr) % 256), buf.numel() - ((-ptr) % 256)
 
 
 def _as_rows(x, name):
@@ -228,10 +230,11 @@ def lapsum_forward(r, k, t, *, path="auto", sample_log2=0, delta=0.0, seed=0, ba
         opt.k_rows = kr.data_ptr() if kr is not None else None
         opt.t_rows = tr.data_ptr() if tr is not None else None
         nbytes = int(lib.lapsum_workspace_bytes(rows, n, ks, ts, ctypes.byref(opt)))
-        wptr, wlen = _workspace(nbytes, dev)
+        ws, wptr, wlen = _workspace(nbytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.lapsum_forward(r2.data_ptr(), rows, n, ks, ts, p.data_ptr(), b.data_ptr(),
                                 wptr, wlen, ctypes.byref(opt), stream)
+        del ws  # back to the pool, ordered after this call on its stream
         _check(rc, "lapsum_forward")
     if r.dim() == 1:
         p, b = p[0], b
@@ -271,10 +274,11 @@ def lapsum_backward(g, p, b, t, *, stats_buf=None, stage_events=None, out=None):
                            stage_events=stage_events)
         opt.t_rows = tr.data_ptr() if tr is not None else None
         nbytes = int(lib.lapsum_workspace_bytes(rows, n, 0.5 * n, ts, None))
-        wptr, wlen = _workspace(nbytes, dev)
+        ws, wptr, wlen = _workspace(nbytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.lapsum_backward(g2.data_ptr(), p2.data_ptr(), b.contiguous().data_ptr(), rows, n, ts,
                                  dr.data_ptr(), dk.data_ptr(), wptr, wlen, ctypes.byref(opt), stream)
+        del ws
         _check(rc, "lapsum_backward")
     if g.dim() == 1:
         dr = dr[0]

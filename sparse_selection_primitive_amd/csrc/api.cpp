@@ -269,7 +269,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.st = F.take((size_t)rows * row_state_bytes());
     P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
     P.spart = F.take(sample_start_bytes(rows, P.m));
-    P.fgx = filter_grid_x(rows, n);
+    P.fgx = filter_grid_x(rows, n, P.cap);
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
     P.offs = F.take(band_offs_bytes(rows, P.fgx));
@@ -411,6 +411,7 @@ lapsum_status lapsum_plan(int64_t rows, int64_t n, double k, double t, const lap
   out->hi = P.hi;
   out->band_capacity = P.cap;
   out->band_onchip = P.band_onchip ? 1 : 0;
+  out->filter_groups = P.fgx;
   out->forward_bytes = P.fwd_bytes;
   out->backward_bytes = P.bwd_bytes;
   return LAPSUM_OK;

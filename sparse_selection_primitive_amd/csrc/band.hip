@@ -69,10 +69,12 @@ LDEV int band_shift(const RowState &S, int bbits) {
 // an L2 of its own.  Renumbered so that consecutive (row, chunk) pairs share
 // an XCD, the partial-line key writes of one row (and their later reads)
 // stay inside one L2 instead of being merged from eight.
+// (Rows are folded over grid.y and grid.z; a renumbered row past the last
+// one belongs to no row and its workgroup returns.)
 constexpr int kXcds = 8;
 LDEV int64_t xcd_linear() {
-  const int64_t T = (int64_t)gridDim.x * gridDim.y;
-  const int64_t L = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+  const int64_t T = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t L = blockIdx.x + (int64_t)gridDim.x * grid_row();
   const int64_t x = L % kXcds, per = T / kXcds, rem = T % kXcds;
   return x * per + min(x, rem) + L / kXcds;
 }
@@ -168,7 +170,8 @@ LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint3
 // full-row mode: key minimum and maximum of each workgroup's chunk
 __global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
   __shared__ uint32_t lmn[kBT / kWave], lmx[kBT / kWave];
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= a.rows) return;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for_each_row_key(a, row, blockIdx.x, [&](uint32_t k) {
     mn = min(mn, k);
@@ -199,7 +202,8 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   __shared__ uint32_t h[kBandBuckets], hmn[kBandBuckets], hmx[kBandBuckets];
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
   __shared__ uint32_t rng[2];
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= a.rows) return;
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
   const int nb = 1 << a.bbits;
@@ -284,7 +288,8 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
 // it is used); the bucket's key extremes over the workgroups; and its
 // fixed-point sums cleared for the scatter to add into
 __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= a.rows) return;
   const int j = blockIdx.x * kBT + threadIdx.x;
   if (j >= (1 << a.bbits)) return;
   uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
@@ -340,6 +345,7 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   int64_t row;
   int blk;
   xcd_tile(row, blk);
+  if (row >= a.rows) return;
   const RowState &S = a.st[row];
   // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
   // inside each bucket and its slot bounds, all loaded before any is used
@@ -464,6 +470,7 @@ __global__ __launch_bounds__(kBT) void band_agg_buckets_kernel(BandArgs a) {
   int64_t row;
   int blk;
   xcd_tile(row, blk);
+  if (row >= a.rows) return;
   const RowState &S = a.st[row];
   const int64_t o = row * kBandBuckets;
   const int q = (int)threadIdx.x / kAggTeam;
@@ -517,7 +524,8 @@ constexpr int kAggChunk = kBT * kAggKeysPerThread;
 __global__ __launch_bounds__(kBT) void band_agg_keys_kernel(BandArgs a) {
   __shared__ unsigned long long sp[kBandBuckets], ss[kBandBuckets];
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= a.rows) return;
   const RowState &S = a.st[row];
   if (!band_active(S)) return;
   const int64_t M = a.n;
@@ -618,6 +626,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   __shared__ double sel_b;
   __shared__ int sel_fb;
   const int64_t row = xcd_linear();
+  if (row >= a.rows) return;
   RowState &S = a.st[row];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
@@ -731,6 +740,12 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   }
 }
 
+// Sizes of the records the host lays out in the workspace for the bucketed
+// solve, the sorted-tile solve and the exact fallback.
+size_t tile_agg_bytes() { return sizeof(TileAgg); }
+size_t pre_bytes() { return sizeof(Pre); }
+size_t suf_bytes() { return sizeof(Suf); }
+
 int band_count_blocks(int gx, int *group) {
   const int nblk = gx < kBandCountBlocks ? gx : kBandCountBlocks;
   *group = (gx + nblk - 1) / nblk;
@@ -760,22 +775,22 @@ int full_count_blocks(int64_t n, int64_t *chunk) {
 }
 
 hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t s) {
-  const dim3 blk((unsigned)a.nblk, (unsigned)a.rows);
+  const dim3 blk = rows_grid((unsigned)a.nblk, a.rows);
   if (a.r != nullptr) hipLaunchKernelGGL(band_minmax_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
   const int nb = 1 << a.bbits;
-  hipLaunchKernelGGL(band_scan_kernel, dim3((nb + kBT - 1) / kBT, (unsigned)a.rows), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
   if (a.r != nullptr)
-    hipLaunchKernelGGL(band_agg_keys_kernel, dim3((unsigned)((a.n + kAggChunk - 1) / kAggChunk), (unsigned)a.rows),
+    hipLaunchKernelGGL(band_agg_keys_kernel, rows_grid((unsigned)((a.n + kAggChunk - 1) / kAggChunk), a.rows),
                        dim3(kBT), 0, s, a);
   else
-    hipLaunchKernelGGL(band_agg_buckets_kernel, dim3((nb + kAggGroup - 1) / kAggGroup, (unsigned)a.rows), dim3(kBT),
-                       0, s, a);
+    hipLaunchKernelGGL(band_agg_buckets_kernel, rows_grid((unsigned)((nb + kAggGroup - 1) / kAggGroup), a.rows),
+                       dim3(kBT), 0, s, a);
   if (a.r != nullptr)
-    hipLaunchKernelGGL(band_locate_kernel<true>, dim3((unsigned)a.rows), dim3(1024), 0, s, a, fb);
+    hipLaunchKernelGGL(band_locate_kernel<true>, rows_grid(1u, a.rows), dim3(1024), 0, s, a, fb);
   else
-    hipLaunchKernelGGL(band_locate_kernel<false>, dim3((unsigned)a.rows), dim3(512), 0, s, a, fb);
+    hipLaunchKernelGGL(band_locate_kernel<false>, rows_grid(1u, a.rows), dim3(512), 0, s, a, fb);
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 // key (seed low, seed high) and counter (j, row, 0, 0): words x0, x1 give
 // I = floor((x1 2^32 + x0) n / 2^64), word x2 gives u = (x2 + 1/2)/2^32 and
 // L = F^-1(u) in fp64; X is rounded to fp32.
+#include <atomic>
+
 #include "filter_dev.hpp"
 #include "lapsum_device.hpp"
 #include "lapsum_internal.hpp"
@@ -68,15 +70,16 @@ LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__restrict__ r, int64_t n, double t,
-                                                                int64_t m, uint32_t k0, uint32_t k1,
-                                                                float *__restrict__ samples,
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__restrict__ r, int64_t rows,
+                                                                int64_t n, double t, int64_t m, uint32_t k0,
+                                                                uint32_t k1, float *__restrict__ samples,
                                                                 uint16_t *__restrict__ starts,
                                                                 RowState *__restrict__ st, int32_t flags) {
   __shared__ uint32_t cnt[kCoarseBins];
   __shared__ uint32_t wsum[kSampleThreads / kWave];
   __shared__ float stage[kSampleWg];
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const int64_t g0 = (int64_t)blockIdx.x * kSampleWg;
   if (blockIdx.x == 0 && threadIdx.x == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state
   cnt[threadIdx.x] = 0u;
@@ -139,8 +142,8 @@ size_t sample_start_bytes(int64_t rows, int64_t m) {
 
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
                          float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)sample_groups(m), (unsigned)rows), dim3(kSampleThreads), 0, s,
-                     r, n, t, m, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, starts, st,
+  hipLaunchKernelGGL(sample_kernel, rows_grid((unsigned)sample_groups(m), rows), dim3(kSampleThreads), 0, s, r,
+                     rows, n, t, m, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, starts, st,
                      flags);
   return hipGetLastError();
 }
@@ -232,11 +235,13 @@ LDEV void locate_ranks(int nbins, const uint32_t (&R)[2], const bool (&want)[2],
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ samples, int64_t m,
-                                                             int64_t lo, int64_t hi, RowState *__restrict__ st) {
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ samples, int64_t rows,
+                                                             int64_t m, int64_t lo, int64_t hi,
+                                                             RowState *__restrict__ st) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   SelectLds &L = *reinterpret_cast<SelectLds *>(lds_raw);
-  const int64_t row = blockIdx.x;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const float *X = samples + row * m;
   const bool want[2] = {lo >= 1, hi <= m};
   uint32_t R[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
@@ -406,10 +411,11 @@ LDEV void wave_locate(const uint32_t *h, const uint32_t (&R)[2], const bool (&wa
 
 __global__ __launch_bounds__(kSelThreads) void select_bucket_kernel(const float *__restrict__ samples,
                                                                     const uint16_t *__restrict__ starts,
-                                                                    int groups, int64_t m, int64_t lo, int64_t hi,
-                                                                    RowState *__restrict__ st) {
+                                                                    int64_t rows, int groups, int64_t m, int64_t lo,
+                                                                    int64_t hi, RowState *__restrict__ st) {
   __shared__ SelectBucketLds L;
-  const int64_t row = blockIdx.x;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const float *X = samples + row * m;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   {
@@ -566,19 +572,24 @@ __global__ __launch_bounds__(kSelThreads) void select_bucket_kernel(const float 
 hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
                          int64_t hi, RowState *st, hipStream_t s) {
   if (sample_groups(m) <= kSelMaxGroups) {
-    hipLaunchKernelGGL(select_bucket_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, s, samples, starts,
+    hipLaunchKernelGGL(select_bucket_kernel, rows_grid(1u, rows), dim3(kSelThreads), 0, s, samples, starts, rows,
                        sample_groups(m), m, lo, hi, st);
     return hipGetLastError();
   }
-  static bool attr_set = false;
+  // the kernel's dynamic LDS exceeds the default limit: raise it once per
+  // device (the attribute is set on the current device)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   const size_t lds = sizeof(SelectLds);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(kSelThreads), lds, s, samples, m, lo, hi, st);
+  hipLaunchKernelGGL(select_kernel, rows_grid(1u, rows), dim3(kSelThreads), lds, s, samples, rows, m, lo, hi, st);
   return hipGetLastError();
 }
 
@@ -635,12 +646,14 @@ LDEV void filter_items(const float (&x)[4 * kUnroll], const bool (&ok)[4 * kUnro
 __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__restrict__ r, int64_t n,
                                                                 const RowState *__restrict__ st,
                                                                 uint32_t *__restrict__ slots,
-                                                                FilterPartial *__restrict__ part, int gx, double t) {
+                                                                FilterPartial *__restrict__ part, int gx, double t,
+                                                                int64_t rows) {
   __shared__ double lds_d[2 * kStreamThreads / kWave];
   __shared__ unsigned long long lds_c[kStreamThreads / kWave];
   __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
   __shared__ uint32_t lcount;
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const RowState &S = st[row];
   if (threadIdx.x == 0) lcount = 0u;
   __syncthreads();
@@ -740,9 +753,17 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   }
 }
 
-int filter_grid_x(int64_t rows, int64_t n) {
+// Filter workgroups per row: about 1024 over all rows, but never fewer than
+// 2 cap / kBandSlot per row (when the row has that many vector groups), so
+// the workgroups' slots hold twice the band capacity (six times the expected
+// band) and a band that fits its capacity does not overflow a slot unless
+// its keys crowd into a few workgroups' chunks of the row.
+int filter_grid_x(int64_t rows, int64_t n, int64_t cap) {
   const int64_t per_row_need = (n / 4 + kStreamThreads * kUnroll - 1) / (kStreamThreads * kUnroll);
   int64_t target = 1024 / (rows > 0 ? rows : 1);
+  const int64_t slots_need = (2 * cap + kBandSlot - 1) / kBandSlot;
+  if (target < slots_need) target = slots_need;
+  if (target > kMaxFilterBlocks) target = kMaxFilterBlocks;
   if (target < 1) target = 1;
   int64_t gx = per_row_need < target ? per_row_need : target;
   return (int)(gx < 1 ? 1 : gx);
@@ -758,8 +779,8 @@ size_t band_offs_bytes(int64_t rows, int grid_x) { return sizeof(uint32_t) * (si
 
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
                          void *partials, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(filter_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, slots,
-                     reinterpret_cast<FilterPartial *>(partials), grid_x, t);
+  hipLaunchKernelGGL(filter_kernel, rows_grid((unsigned)grid_x, rows), dim3(kStreamThreads), 0, s, r, n, st, slots,
+                     reinterpret_cast<FilterPartial *>(partials), grid_x, t, rows);
   return hipGetLastError();
 }
 

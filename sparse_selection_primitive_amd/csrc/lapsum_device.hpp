@@ -158,6 +158,10 @@ LDEV uint32_t xor_lanes(uint32_t v) {
 
 LDEV int lane_id() { return (int)__lane_id(); }
 
+// Row of this workgroup in a launch whose rows are folded over grid.y and
+// grid.z (rows_grid in lapsum_internal.hpp); may be past the last row.
+LDEV int64_t grid_row() { return (int64_t)blockIdx.y + (int64_t)gridDim.y * (int64_t)blockIdx.z; }
+
 // ------------------------------------------------- whole-wave helpers
 // A 64-lane wave is four DPP rows of 16 lanes.  Butterflies and scans run
 // inside the rows on DPP moves; the four row results are then read once each

@@ -22,6 +22,19 @@ constexpr int kUnroll = 4;           // independent 16 B loads per thread per st
 constexpr int kBandSlot = 2048;      // band keys one filter workgroup may keep
 constexpr int kMaxFilterBlocks = 4096;  // filter workgroups per row, at most
 
+// Launch grids over rows.  Kernels with several workgroups per row put the
+// row's workgroups in grid.x and the rows in grid.y and grid.z (a launch
+// dimension other than x holds at most 65535 workgroups here); kernels with
+// one workgroup per row use the same folding with grid.x = 1, so no launch
+// exceeds 2^32 work-items in a dimension.  Device side: grid_row() in
+// lapsum_device.hpp; a workgroup whose row is past the last one returns.
+constexpr int64_t kGridDimMax = 65535;
+inline dim3 rows_grid(unsigned gx, int64_t rows) {
+  const int64_t z = (rows + kGridDimMax - 1) / kGridDimMax;
+  const int64_t y = (rows + z - 1) / z;
+  return dim3(gx, (unsigned)y, (unsigned)z);
+}
+
 // Optional per-row budget and temperature (device arrays [rows], NULL: the
 // call's scalars).
 struct RowParams {
@@ -117,7 +130,7 @@ hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t r
                          int64_t hi, RowState *st, hipStream_t s);
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
                          void *partials, int grid_x, hipStream_t s);
-int filter_grid_x(int64_t rows, int64_t n);
+int filter_grid_x(int64_t rows, int64_t n, int64_t cap);
 size_t filter_partial_bytes(int64_t rows, int grid_x);
 size_t band_slot_bytes(int64_t rows, int grid_x);
 size_t band_offs_bytes(int64_t rows, int grid_x);

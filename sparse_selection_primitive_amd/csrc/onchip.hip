@@ -297,14 +297,15 @@ __global__ __launch_bounds__(256) void onchip_forward_wave_ragged(const float *_
 
 // One row per workgroup: NP = 16 * LANES, LANES threads.
 template <int NP, bool PR>
-__global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int n,
+__global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__restrict__ r, int64_t rows, int n,
                                                                 double k, double t, RowParams rp,
                                                                 float *__restrict__ p, double *__restrict__ b,
                                                                 lapsum_row_stats *stats) {
   constexpr int E = 16, LANES = NP / 16;
   __shared__ BlockTeamLds<LANES, E> lds;
   BlockTeam<LANES, E> team(&lds);
-  const int64_t row = blockIdx.x;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   bool good = true;
   if constexpr (PR) good = row_params(rp.k, rp.t, row, n, k, t);
   onchip_row_forward<E, false>(team, r + row * n, n, true, k, t, p + row * n, b + row, stats ? stats + row : nullptr,
@@ -328,8 +329,8 @@ static hipError_t launch_fwd_wave(const float *r, int64_t rows, int n, double k,
 template <int NP, bool PR>
 static hipError_t launch_fwd_block(const float *r, int64_t rows, int n, double k, double t, RowParams rp, float *p,
                                    double *b, lapsum_row_stats *stats, hipStream_t s) {
-  hipLaunchKernelGGL((onchip_forward_block<NP, PR>), dim3((unsigned)rows), dim3(NP / 16), 0, s, r, n, k, t, rp, p,
-                     b, stats);
+  hipLaunchKernelGGL((onchip_forward_block<NP, PR>), rows_grid(1u, rows), dim3(NP / 16), 0, s, r, rows, n, k, t, rp,
+                     p, b, stats);
   return hipGetLastError();
 }
 
@@ -525,8 +526,9 @@ LDEV void band_onchip_row(const uint32_t *__restrict__ slots, const uint32_t *so
 template <int NPMAX>
 __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__restrict__ slots,
                                                              const FilterPartial *__restrict__ part, int gx,
-                                                             int64_t n, int64_t cap, RowState *__restrict__ st,
-                                                             double k, double t, SegArgs fb) {
+                                                             int64_t rows, int64_t n, int64_t cap,
+                                                             RowState *__restrict__ st, double k, double t,
+                                                             SegArgs fb) {
   union BandLds {
     BlockTeamLds<kBandNT, NPMAX / kBandNT> band;
     SegLds<kBandNT> full;
@@ -534,7 +536,8 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   __shared__ BandLds lds;
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
   __shared__ int fall;
-  const int64_t row = blockIdx.x;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   RowState &S = st[row];
   // the streaming filter's partials of the row: totals and slot offsets
   const FilterTotals T = filter_totals<kBandNT>(part + row * gx, gx, n, cap, soffs);
@@ -555,18 +558,19 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
 hipError_t launch_band_onchip(const uint32_t *slots, const void *partials, int gx, int64_t rows, int64_t n,
                               int64_t cap, RowState *st, double k, double t, const SegArgs &fb, hipStream_t s) {
   const FilterPartial *part = reinterpret_cast<const FilterPartial *>(partials);
+  const dim3 grid = rows_grid(1u, rows);
   if (cap <= 1024)
-    hipLaunchKernelGGL(band_solve_onchip<1024>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
-                       st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<1024>, grid, dim3(kBandNT), 0, s, slots, part, gx, rows, n, cap, st, k, t,
+                       fb);
   else if (cap <= 2048)
-    hipLaunchKernelGGL(band_solve_onchip<2048>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
-                       st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<2048>, grid, dim3(kBandNT), 0, s, slots, part, gx, rows, n, cap, st, k, t,
+                       fb);
   else if (cap <= 4096)
-    hipLaunchKernelGGL(band_solve_onchip<4096>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
-                       st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<4096>, grid, dim3(kBandNT), 0, s, slots, part, gx, rows, n, cap, st, k, t,
+                       fb);
   else
-    hipLaunchKernelGGL(band_solve_onchip<8192>, dim3((unsigned)rows), dim3(kBandNT), 0, s, slots, part, gx, n, cap,
-                       st, k, t, fb);
+    hipLaunchKernelGGL(band_solve_onchip<8192>, grid, dim3(kBandNT), 0, s, slots, part, gx, rows, n, cap, st, k, t,
+                       fb);
   return hipGetLastError();
 }
 

@@ -3,13 +3,16 @@
 //  * apply: p_i = F((r_i - b)/t) ("Fast LapSum: Exact Differentiable Top-k at
 //    Million Scale", section 2.1, eq. (1)), 4 B read + 4 B written per score;
 //  * backward, section 2.1 (analytic VJP): pass 1 reads g and p (8 B/score)
-//    and forms D = sum d, G = sum g d in fp64 with a deterministic
-//    last-block finalize giving dk = G/D; pass 2 reads g and p again and
-//    writes dr = d (g - dk) (12 B/score), d = min(p, 1 - p)/t.
+//    and leaves one fp64 partial (sum d, sum g d) per workgroup; pass 2
+//    reads g and p again, and every one of its workgroups first adds the
+//    row's partials in one fixed order (so all hold the same dk = G/D bit
+//    for bit, with no finalize launch), then writes dr = d (g - dk)
+//    (12 B/score), d = min(p, 1 - p)/t.
 //
 // Loads and stores are 16 B per lane and non-temporal: every byte is used
-// once, so nothing is worth keeping in the caches.  Grids are 2-D
-// (blocks per row x rows) with grid-stride loops inside a row.
+// once, so nothing is worth keeping in the caches.  Grids are workgroups
+// per row in x and rows folded over y and z (rows_grid), with grid-stride
+// loops inside a row.
 #include "lapsum_device.hpp"
 #include "lapsum_internal.hpp"
 
@@ -75,11 +78,12 @@ hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats 
 size_t row_state_bytes() { return sizeof(RowState); }
 
 // ---------------------------------------------------------------- apply
-__global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__restrict__ r, int64_t n,
-                                                               const RowState *__restrict__ st, double t,
-                                                               RowParams rp, float *__restrict__ p,
+__global__ __launch_bounds__(kStreamThreads) void apply_kernel(const float *__restrict__ r, int64_t rows,
+                                                               int64_t n, const RowState *__restrict__ st,
+                                                               double t, RowParams rp, float *__restrict__ p,
                                                                double *__restrict__ bout) {
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const double b = st[row].b;  // NaN for a row with invalid per-row k or t
   double kr = 0.5 * (double)n;
   if (rp.t) row_params(nullptr, rp.t, row, n, kr, t);
@@ -134,7 +138,8 @@ static int stream_grid_x(int64_t rows, int64_t n) {
 hipError_t launch_apply(const float *r, int64_t rows, int64_t n, const RowState *st, double t, RowParams rp,
                         float *p, double *b, hipStream_t s) {
   const int gx = stream_grid_x(rows, n);
-  hipLaunchKernelGGL(apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, r, n, st, t, rp, p, b);
+  hipLaunchKernelGGL(apply_kernel, rows_grid((unsigned)gx, rows), dim3(kStreamThreads), 0, s, r, rows, n, st, t, rp,
+                     p, b);
   return hipGetLastError();
 }
 
@@ -167,10 +172,12 @@ LDEV void block_sum2(double &a, double &b, double *lds) {
 }
 
 __global__ __launch_bounds__(kStreamThreads) void bwd_reduce_kernel(const float *__restrict__ g,
-                                                                    const float *__restrict__ p, int64_t n,
-                                                                    BwdPartial *__restrict__ part, int gx) {
+                                                                    const float *__restrict__ p, int64_t rows,
+                                                                    int64_t n, BwdPartial *__restrict__ part,
+                                                                    int gx) {
   __shared__ double lds[2 * kStreamThreads / kWave];
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
@@ -244,12 +251,14 @@ LDEV void bwd_row_total(const BwdPartial *__restrict__ vp, int gx, double *lds, 
 }
 
 __global__ __launch_bounds__(kStreamThreads) void bwd_apply_kernel(const float *__restrict__ g,
-                                                                   const float *__restrict__ p, int64_t n,
-                                                                   const BwdPartial *__restrict__ part, int gx,
-                                                                   double t, RowParams rp, float *__restrict__ dr,
-                                                                   float *__restrict__ dk, lapsum_row_stats *stats) {
+                                                                   const float *__restrict__ p, int64_t rows,
+                                                                   int64_t n, const BwdPartial *__restrict__ part,
+                                                                   int gx, double t, RowParams rp,
+                                                                   float *__restrict__ dr, float *__restrict__ dk,
+                                                                   lapsum_row_stats *stats) {
   __shared__ double lds[2 * kStreamThreads / kWave];
-  const int64_t row = blockIdx.y;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
   const BwdPartial *vp = part + row * gx;
   const float *gg = g + row * n;
   const float *pp = p + row * n;
@@ -314,8 +323,8 @@ size_t bwd_partial_bytes(int64_t rows, int grid_x) { return sizeof(BwdPartial) *
 
 hipError_t launch_bwd_reduce(const float *g, const float *p, int64_t rows, int64_t n, void *partials, int grid_x,
                              hipStream_t s) {
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid_x, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
-                     reinterpret_cast<BwdPartial *>(partials), grid_x);
+  hipLaunchKernelGGL(bwd_reduce_kernel, rows_grid((unsigned)grid_x, rows), dim3(kStreamThreads), 0, s, g, p, rows,
+                     n, reinterpret_cast<BwdPartial *>(partials), grid_x);
   return hipGetLastError();
 }
 
@@ -323,7 +332,7 @@ hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_
                             int npart, double t, RowParams rp, float *dr, float *dk, lapsum_row_stats *stats,
                             hipStream_t s) {
   const int gx = stream_grid_x(rows, n);
-  hipLaunchKernelGGL(bwd_apply_kernel, dim3(gx, (unsigned)rows), dim3(kStreamThreads), 0, s, g, p, n,
+  hipLaunchKernelGGL(bwd_apply_kernel, rows_grid((unsigned)gx, rows), dim3(kStreamThreads), 0, s, g, p, rows, n,
                      reinterpret_cast<const BwdPartial *>(partials), npart, t, rp, dr, dk, stats);
   return hipGetLastError();
 }

@@ -178,3 +178,19 @@ def test_forward_rejects_null_and_small_workspace_without_launching(lib):
     assert rc == 5
     rc = lib.lapsum_backward(None, None, None, 1, 100, 1.0, None, None, None, 0, None, None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("rows,n,k", [(64, 1 << 21, float(1 << 20)), (1, 100_000_000, 1e5), (32, 65536, 3277),
+                                      (64, 1 << 21, 3.0), (1000, 1 << 21, float(1 << 20))])
+def test_filter_slots_cover_the_band_capacity(lib, rows, n, k):
+    """The streaming filter keeps band keys in per-workgroup slots of 2048
+    keys; a row long enough to give every workgroup a full load gets slots
+    for at least twice its band capacity, so a band within its capacity does
+    not overflow a slot (64 rows of 2^21 scores at k = n/2 once had 16
+    workgroups per row: 32768 slots for a band of ~40000 keys)."""
+    p = L.plan(rows, n, k, 0.01, path="bracket")
+    gx = p["filter_groups"]
+    vector_groups = -(-(n // 4) // (256 * 4))  # 16-byte groups per row at 4 per thread and 256 threads
+    assert 1 <= gx <= 4096
+    assert gx * 2048 >= min(2 * p["band_capacity"], vector_groups * 2048, 4096 * 2048)
+
