@@ -19,6 +19,8 @@ Contents
   bracket              -- numpy: counter-based sampling, binomial
                           order-statistic indices, the bracket itself.
   brute                -- mpmath: exhaustive solve for n <= 8.
+  midpoint_mass        -- C, fp64: the DFTopK threshold (section 2.3) and the
+                          mass the Laplace kernel assigns at it.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts
 that do not come from the oracle itself (closed forms, brute force,
@@ -67,6 +69,8 @@ def _load():
     lib.oracle_tail_sums.argtypes = [dp, i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                      dp, dp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.oracle_tail_sums.restype = None
+    lib.oracle_midpoint_mass.argtypes = [dp, i64, i64, i64, ctypes.c_double, dp, dp, ctypes.c_int]
+    lib.oracle_midpoint_mass.restype = ctypes.c_int
     lib.oracle_laplace_cdf.argtypes = [ctypes.c_double]
     lib.oracle_laplace_cdf.restype = ctypes.c_double
     lib.oracle_laplace_quantile.argtypes = [ctypes.c_double]
@@ -165,3 +169,24 @@ def tail_sums(r_row, a_lo: float, a_hi: float, t: float):
                              ctypes.byref(sl), ctypes.byref(sr), ctypes.byref(cl), ctypes.byref(cr),
                              ctypes.byref(m))
     return {"S_L": sl.value, "S_R": sr.value, "c_L": cl.value, "c_R": cr.value, "M": m.value}
+
+
+def midpoint_mass(r, k: int, t: float, threads: int | None = None):
+    """Section 2.3 (relation to DFTopK): per row, the fixed threshold
+    b_mid = (s_(k) + s_(k+1))/2 (k-th and (k+1)-th largest scores, k an
+    integer in [1, n-1]) and mass = sum_i F((r_i - b_mid)/t).  Returns
+    (b_mid, mass), one value per row (scalars for a 1-D row)."""
+    r64 = _f64(r)
+    squeeze = r64.ndim == 1
+    if squeeze:
+        r64 = r64[None, :]
+    rows, n = r64.shape
+    if int(k) != k:
+        raise ValueError("midpoint_mass: k must be an integer")
+    bm = np.empty(rows, dtype=np.float64)
+    ms = np.empty(rows, dtype=np.float64)
+    rc = _load().oracle_midpoint_mass(_ptr(r64), rows, n, int(k), float(t), _ptr(bm), _ptr(ms),
+                                      threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_midpoint_mass: invalid arguments (need 1 <= k <= n-1, t > 0)")
+    return (bm[0], ms[0]) if squeeze else (bm, ms)

@@ -35,6 +35,9 @@
  *                         closed-form root), a second independent route.
  *   oracle_budget         f(b) itself.
  *   oracle_tail_sums      the bracketing tail sums for a given bracket.
+ *   oracle_midpoint_mass  the DFTopK threshold (midpoint of the k-th and
+ *                         (k+1)-th largest scores, section 2.3) and the mass
+ *                         the Laplace kernel assigns at it.
  *
  * Parity pins (tests/test_oracle_*.py): brute force over all "above" sets at
  * n <= 8 in 50-digit arithmetic, closed forms for n = 1 and constant rows,
@@ -359,4 +362,43 @@ void oracle_tail_sums(const double *r, int64_t n, double aL, double aR, double t
     *cL = nl;
     *cR = nr;
     *M = nm;
+}
+
+/* Section 2.3, relation to DFTopK: DFTopK fixes the threshold at the
+ * midpoint between the k-th and the (k+1)-th largest score instead of
+ * solving the budget equation, and the pages show it is the zero-temperature
+ * limit of LapSum.  At a positive temperature the mass the Laplace kernel
+ * assigns at that fixed threshold,
+ *     mass = sum_i F((r_i - b_mid)/t),   b_mid = (s_(k) + s_(k+1)) / 2,
+ * drifts away from k (the budget error the pages report for DFTopK).  Here
+ * k is an integer with 1 <= k <= n - 1, so both order statistics exist;
+ * with the scores sorted ascending, s_(k) = s[n-k] and s_(k+1) = s[n-k-1].
+ * Writes b_mid [rows] and mass [rows] (long double sum).  Returns 0 or -1. */
+int oracle_midpoint_mass(const double *r, int64_t rows, int64_t n, int64_t k, double t,
+                         double *b_mid, double *mass, int threads)
+{
+    if (rows < 1 || n < 2 || k < 1 || k > n - 1 || !(t > 0.0))
+        return -1;
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 0 ? threads : 1) if (rows > 1 && threads > 1)
+#endif
+    for (int64_t row = 0; row < rows; ++row) {
+        const double *rr = r + row * n;
+        double *s = (double *)malloc(sizeof(double) * (size_t)n);
+        if (!s) {
+            failed = 1;
+            continue;
+        }
+        memcpy(s, rr, sizeof(double) * (size_t)n);
+        qsort(s, (size_t)n, sizeof(double), cmp_double);
+        const double bm = 0.5 * (s[n - k] + s[n - k - 1]);
+        free(s);
+        long double m = 0.0L;
+        for (int64_t i = 0; i < n; ++i)
+            m += laplace_cdf((rr[i] - bm) / t);
+        b_mid[row] = bm;
+        mass[row] = (double)m;
+    }
+    return failed ? -1 : 0;
 }
