@@ -63,7 +63,9 @@ typedef enum lapsum_status {
     LAPSUM_ERR_WORKSPACE = 5, /* workspace smaller than lapsum_workspace_bytes() or not 256-byte aligned */
     LAPSUM_ERR_PATH = 6,      /* the requested path cannot run this shape */
     LAPSUM_ERR_OPTION = 7,    /* an option is out of range */
-    LAPSUM_ERR_HIP = 8        /* a HIP launch or runtime query failed */
+    LAPSUM_ERR_HIP = 8,       /* a HIP launch or runtime query failed */
+    LAPSUM_ERR_SCRATCH = 9    /* lapsum_backward_noalloc: the call needs more scratch than the
+                                 library's fixed buffer (LAPSUM_NOALLOC_SCRATCH_BYTES) holds */
 } lapsum_status;
 
 /* Longest row: sample indices use 32x32-bit products and tile counts fit int32.
@@ -219,6 +221,31 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
 lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
                               float *dr, float *dk, void *workspace, size_t workspace_bytes,
                               const lapsum_options *opt, void *stream);
+
+/* Size of the fixed device buffer lapsum_backward_noalloc uses instead of a
+ * workspace: one per device, held until the process ends. */
+#define LAPSUM_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+/* Backward without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and results (bitwise) as
+ * lapsum_backward, with the streaming pass's partial sums kept in a fixed
+ * device buffer of the library (LAPSUM_NOALLOC_SCRATCH_BYTES per device,
+ * looked up on the first call on each device) instead of a caller
+ * workspace.  The caller still passes every input and output.  Nothing is
+ * allocated or freed, by the library or by any routine it calls.
+ *   Arguments, layouts and opt fields read: as lapsum_backward (minus the
+ *   workspace).  Rows of at most 1024 scores need no scratch; longer rows
+ *   need 16 bytes per streaming workgroup, i.e. at most
+ *   16 * max(4096, rows) bytes, so up to 65536 rows of any length fit.
+ *   Errors: as lapsum_backward, plus LAPSUM_ERR_SCRATCH (nothing launched)
+ *   when the call needs more than the fixed buffer.
+ *   Concurrency: every call on one device shares that device's buffer, and
+ *   the buffer keeps whatever the last call left in it; calls that overlap
+ *   on one device (other streams, other threads) race and must be ordered
+ *   by the caller. */
+lapsum_status lapsum_backward_noalloc(const float *g, const float *p, const double *b, int64_t rows, int64_t n,
+                                      double t, float *dr, float *dk, const lapsum_options *opt, void *stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,8 @@ STAGE_NAMES = ["onchip_fwd", "init", "sample", "select", "filter", "band", "full
                "onchip_bwd", "bwd_reduce", "bwd_apply"]
 
 EXPORTED = ["lapsum_options_init", "lapsum_status_string", "lapsum_plan", "lapsum_bracket_indices",
-            "lapsum_workspace_bytes", "lapsum_forward", "lapsum_backward"]
+            "lapsum_workspace_bytes", "lapsum_forward", "lapsum_backward", "lapsum_backward_noalloc"]
+NOALLOC_SCRATCH_BYTES = 1 << 20  # LAPSUM_NOALLOC_SCRATCH_BYTES
 
 
 class LapsumError(RuntimeError):
@@ -98,6 +99,8 @@ def load_library():
     lib.lapsum_backward.argtypes = [vp, vp, vp, i64, i64, dbl, vp, vp, vp, ctypes.c_size_t,
                                     ctypes.POINTER(Options), vp]
     lib.lapsum_backward.restype = ctypes.c_int
+    lib.lapsum_backward_noalloc.argtypes = [vp, vp, vp, i64, i64, dbl, vp, vp, ctypes.POINTER(Options), vp]
+    lib.lapsum_backward_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -280,6 +283,38 @@ def lapsum_backward(g, p, b, t, *, stats_buf=None, stage_events=None, out=None):
                                  dr.data_ptr(), dk.data_ptr(), wptr, wlen, ctypes.byref(opt), stream)
         del ws
         _check(rc, "lapsum_backward")
+    if g.dim() == 1:
+        dr = dr[0]
+    return dr, dk
+
+
+def lapsum_backward_noalloc(g, p, b, t, *, out=None):
+    """The backward through the entry point that allocates nothing: the
+    library keeps the streaming pass's partials in its own fixed device
+    buffer (one per device), so no workspace is passed.  Calls that overlap
+    on one device race on that buffer.  With ``out`` = (dr, dk) no tensor is
+    allocated here either."""
+    torch = _torch()
+    lib = load_library()
+    g2 = _as_rows(g, "g")
+    p2 = _as_rows(p, "p")
+    if g2.shape != p2.shape:
+        raise LapsumError("g and p must have the same shape")
+    rows, n = g2.shape
+    dev = g2.device
+    if not (isinstance(b, torch.Tensor) and b.is_cuda and b.dtype == torch.float64 and b.numel() == rows):
+        raise LapsumError("b must be a float64 GPU tensor with one entry per row")
+    with torch.cuda.device(dev):
+        dr = torch.empty_like(g2) if out is None else out[0]
+        dk = torch.empty(rows, dtype=torch.float32, device=dev) if out is None else out[1]
+        tr = _per_row(t, rows, dev, "t")
+        ts = 1.0 if tr is not None else float(t)
+        opt = make_options()
+        opt.t_rows = tr.data_ptr() if tr is not None else None
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.lapsum_backward_noalloc(g2.data_ptr(), p2.data_ptr(), b.contiguous().data_ptr(), rows, n, ts,
+                                         dr.data_ptr(), dk.data_ptr(), ctypes.byref(opt), stream)
+        _check(rc, "lapsum_backward_noalloc")
     if g.dim() == 1:
         dr = dr[0]
     return dr, dk

@@ -385,6 +385,7 @@ const char *lapsum_status_string(lapsum_status st) {
     case LAPSUM_ERR_PATH: return "the requested path cannot run this shape";
     case LAPSUM_ERR_OPTION: return "an option is out of range";
     case LAPSUM_ERR_HIP: return "HIP launch or runtime error";
+    case LAPSUM_ERR_SCRATCH: return "the call needs more scratch than the fixed no-alloc buffer holds";
   }
   return "unknown status";
 }
@@ -508,9 +509,15 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   return LAPSUM_OK;
 }
 
-lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
-                              float *dr, float *dk, void *workspace, size_t workspace_bytes,
-                              const lapsum_options *opt, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward's argument checks and launch sequence on a given scratch
+// (a caller workspace, or the fixed no-alloc buffer when `fixed`).
+lapsum_status backward_impl(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
+                            float *dr, float *dk, void *workspace, size_t workspace_bytes, bool fixed,
+                            const lapsum_options *opt, void *stream) {
   lapsum_options o;
   lapsum_options_init(&o);
   if (opt) o = *opt;
@@ -520,7 +527,9 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   const RowParams rp{nullptr, o.t_rows};
   Plan P;
   bwd_layout(rows, n, P);
-  if (P.bwd_bytes > 0) {
+  if (fixed) {
+    if (P.bwd_bytes > LAPSUM_NOALLOC_SCRATCH_BYTES) return LAPSUM_ERR_SCRATCH;
+  } else if (P.bwd_bytes > 0) {
     if (!workspace) return LAPSUM_ERR_NULL;
     if (workspace_bytes < P.bwd_bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
       return LAPSUM_ERR_WORKSPACE;
@@ -534,6 +543,7 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
     tm.mark(LAPSUM_STAGE_ONCHIP_BWD, 1);
     return LAPSUM_OK;
   }
+  if (fixed) LAPSUM_TRY(noalloc_scratch(&workspace));
   char *ws = reinterpret_cast<char *>(workspace);
   tm.mark(LAPSUM_STAGE_BWD_REDUCE, 0);
   LAPSUM_TRY(launch_bwd_reduce(g, p, rows, n, ws + P.bpart, P.bgx, s));
@@ -542,6 +552,21 @@ lapsum_status lapsum_backward(const float *g, const float *p, const double *b, i
   LAPSUM_TRY(launch_bwd_apply(g, p, rows, n, ws + P.bpart, P.bgx, t, rp, dr, dk, o.stats, s));
   tm.mark(LAPSUM_STAGE_BWD_APPLY, 1);
   return LAPSUM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
+                              float *dr, float *dk, void *workspace, size_t workspace_bytes,
+                              const lapsum_options *opt, void *stream) {
+  return backward_impl(g, p, b, rows, n, t, dr, dk, workspace, workspace_bytes, false, opt, stream);
+}
+
+lapsum_status lapsum_backward_noalloc(const float *g, const float *p, const double *b, int64_t rows, int64_t n,
+                                      double t, float *dr, float *dk, const lapsum_options *opt, void *stream) {
+  return backward_impl(g, p, b, rows, n, t, dr, dk, nullptr, 0, true, opt, stream);
 }
 
 }  // extern "C"

@@ -149,6 +149,9 @@ hipError_t launch_bwd_apply(const float *g, const float *p, int64_t rows, int64_
                             hipStream_t s);
 int bwd_grid_x(int64_t rows, int64_t n);
 size_t bwd_partial_bytes(int64_t rows, int grid_x);
+// Device address of the fixed no-alloc scratch (LAPSUM_NOALLOC_SCRATCH_BYTES)
+// on the current device.
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_copy_stats(const RowState *st, int64_t rows, lapsum_row_stats *stats, hipStream_t s);
 
 size_t row_state_bytes();

@@ -13,10 +13,47 @@
 // once, so nothing is worth keeping in the caches.  Grids are workgroups
 // per row in x and rows folded over y and z (rows_grid), with grid-stride
 // loops inside a row.
+#include <atomic>
+#include <mutex>
+
 #include "lapsum_device.hpp"
 #include "lapsum_internal.hpp"
 
+// Fixed device scratch of lapsum_backward_noalloc (for callers that cannot
+// allocate): the streaming backward's per-workgroup partials, written in
+// full by the reduce pass before the apply pass reads them, so nothing in
+// it needs clearing.  Each device holds its own copy for the life of the
+// process; calls that overlap on one device share it and race.  Host code
+// never passes this name to a kernel: it passes the device address that
+// noalloc_scratch() looks up per device.
+static __device__ __align__(256) unsigned char scratch[LAPSUM_NOALLOC_SCRATCH_BYTES];
+
 namespace lapsum {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *q = addr[dev].load(std::memory_order_acquire);
+  if (q == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    q = addr[dev].load(std::memory_order_relaxed);
+    if (q == nullptr) {
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (q == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(q, std::memory_order_release);
+    }
+  }
+  *ptr = q;
+  return hipSuccess;
+}
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 

@@ -194,3 +194,22 @@ def test_filter_slots_cover_the_band_capacity(lib, rows, n, k):
     assert 1 <= gx <= 4096
     assert gx * 2048 >= min(2 * p["band_capacity"], vector_groups * 2048, 4096 * 2048)
 
+
+def test_noalloc_backward_rejects_sizes_beyond_its_buffer(lib):
+    """lapsum_backward_noalloc checks its scratch need against the fixed
+    buffer before touching the device: 16 bytes per streaming workgroup,
+    one workgroup per row once rows exceed 4096, so 65536 rows of more than
+    1024 scores fit and 65537 do not; rows of at most 1024 scores need no
+    scratch.  (The pointers below are never dereferenced.)"""
+    assert L.NOALLOC_SCRATCH_BYTES == 1 << 20
+    fake = ctypes.c_void_p(256)
+    assert lib.lapsum_backward_noalloc(fake, fake, fake, 65537, 2048, 1.0, fake, fake, None, None) == 9
+    assert lib.lapsum_backward_noalloc(fake, fake, fake, 1 << 20, 1100, 1.0, fake, fake, None, None) == 9
+    assert "fixed no-alloc buffer" in lib.lapsum_status_string(9).decode()
+    # argument checks come first, as in lapsum_backward
+    assert lib.lapsum_backward_noalloc(None, None, None, 1, 100, 1.0, None, None, None, None) == 1
+    assert lib.lapsum_backward_noalloc(fake, fake, fake, 1, 100, 0.0, fake, fake, None, None) == 4
+    assert lib.lapsum_backward_noalloc(fake, fake, fake, 0, 100, 1.0, fake, fake, None, None) == 2
+    # the largest streaming batch that fits: 65536 rows x 2 partials would not, 1 per row does
+    assert L.plan(65536, 2048, 1.0, 1.0)["backward_bytes"] <= L.NOALLOC_SCRATCH_BYTES
+    assert L.plan(1, 100_000_000, 1.0, 1.0)["backward_bytes"] <= L.NOALLOC_SCRATCH_BYTES
