@@ -16,13 +16,16 @@
  * (sample, binomial order-statistic bracket, one streaming pass that folds
  * out-of-bracket scores into tail sums and keeps the middle band, an exact
  * solve on the band, and certification; a bracket that fails it is widened
- * and tried again).  This library sorts only what the root needs: a bucket
- * pass over the row (or band) locates the balancing bucket from order-free
- * bucket sums, and only that bucket is sorted.  A missed bracket is widened
- * (wider order statistics of the same sample, one pass over the row by the
- * workgroup that found the miss, the same bucket selection on the wider
- * band); if every widened bracket fails too, a deterministic fallback nests
- * the bucket selection over the whole row.
+ * and tried again).  The full-sort solver exists as written (the SORT path:
+ * every score of the row radix-sorted) and in a form that sorts only what
+ * the root needs (the BUCKET path: one bucket pass over the row or band
+ * locates the balancing bucket from order-free bucket sums, and only that
+ * bucket is sorted).  A missed bracket is widened (wider order statistics
+ * of the same sample, one pass over the row by the workgroup that found the
+ * miss, the same bucket selection on the wider band); if every widened
+ * bracket fails too, a deterministic fallback nests the bucket selection
+ * over the whole row.  The iterative bisection that the full-sort solver
+ * replaces is available as a baseline (the BISECT path).
  *
  * Conventions shared by every entry point
  *   - Array arguments marked "device" are device pointers on the current HIP
@@ -78,12 +81,18 @@ typedef enum lapsum_status {
 #define LAPSUM_ONCHIP_MAX_N 8192
 
 typedef enum lapsum_path {
-    LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: FULLSORT; else BRACKET */
+    LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: BUCKET; else BRACKET */
     LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
-    LAPSUM_PATH_FULLSORT = 2, /* one radix (bucket) pass over the row, order-free bucket sums, locate,
-                                 sort of the balancing bucket only, root + streaming apply */
-    LAPSUM_PATH_BRACKET = 3   /* probabilistic bracketing; a missed bracket is widened, then an
+    LAPSUM_PATH_BUCKET = 2,   /* the full-sort solver sorting only the balancing bucket: one radix
+                                 (bucket) pass over the row, order-free bucket sums, locate, sort of
+                                 that bucket, root + streaming apply */
+    LAPSUM_PATH_BRACKET = 3,  /* probabilistic bracketing; a missed bracket is widened, then an
                                  exact whole-row fallback */
+    LAPSUM_PATH_SORT = 4,     /* the full-sort solver as the pages state it: a radix sort of every
+                                 score of the row (4 passes of 8-bit digits), the threshold curve
+                                 over the sorted row, locate, root + streaming apply */
+    LAPSUM_PATH_BISECT = 5    /* baseline: bisection of the monotone budget f(b) in fp64, no sort
+                                 (on chip up to 16384 scores, else one streaming pass per halving) */
 } lapsum_path;
 
 /* Per-row flags in lapsum_row_stats.flags. */
@@ -116,12 +125,15 @@ enum {
     LAPSUM_STAGE_SELECT = 3,     /* order statistics -> bracket */
     LAPSUM_STAGE_FILTER = 4,     /* streaming tail sums + band compaction */
     LAPSUM_STAGE_BAND = 5,       /* band solve + certification (+ widening / fallback of a missed row) */
-    LAPSUM_STAGE_FULLSORT = 6,   /* full-sort solve of whole rows (full-sort path) */
+    LAPSUM_STAGE_BUCKET = 6,     /* bucketed solve of whole rows (BUCKET path) */
     LAPSUM_STAGE_APPLY = 7,      /* streaming Laplace-CDF apply */
     LAPSUM_STAGE_ONCHIP_BWD = 8, /* fused on-chip backward */
     LAPSUM_STAGE_BWD_REDUCE = 9, /* streaming backward reductions (D, G) */
     LAPSUM_STAGE_BWD_APPLY = 10, /* streaming backward elementwise dr */
-    LAPSUM_STAGE_COUNT = 11
+    LAPSUM_STAGE_SORT = 11,      /* SORT path: radix sort of every row */
+    LAPSUM_STAGE_SOLVE = 12,     /* SORT path: threshold curve, locate and root over the sorted rows */
+    LAPSUM_STAGE_BISECT = 13,    /* BISECT path: the bisection (on chip it also writes p) */
+    LAPSUM_STAGE_COUNT = 14
 };
 
 typedef struct lapsum_options {
@@ -151,7 +163,7 @@ typedef struct lapsum_options {
                               then not used), 0 < t_i < inf, likewise.  lapsum_backward reads
                               it too.  With k_rows or t_rows the bracketing path is not
                               available (its sample indices are set per k on the host): AUTO
-                              takes the full-sort path above 8192 scores, and a forced
+                              takes the BUCKET path above 8192 scores, and a forced
                               LAPSUM_PATH_BRACKET is LAPSUM_ERR_PATH. */
 } lapsum_options;
 
@@ -221,6 +233,27 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
 lapsum_status lapsum_backward(const float *g, const float *p, const double *b, int64_t rows, int64_t n, double t,
                               float *dr, float *dk, void *workspace, size_t workspace_bytes,
                               const lapsum_options *opt, void *stream);
+
+/* DFTopK diagnostic (section 2.3, relation to DFTopK; section 4.1, budget
+ * accuracy): DFTopK fixes the threshold at the midpoint of the k-th and the
+ * (k+1)-th largest score instead of solving the budget equation, and is
+ * LapSum's zero-temperature limit.  For each row this computes that fixed
+ * threshold and the mass the Laplace kernel of temperature t assigns at it,
+ *     b_mid = (s_(k) + s_(k+1)) / 2,   mass = sum_i F((r_i - b_mid)/t),
+ * so mass / k - 1 is the budget drift of the fixed midpoint (LapSum's own
+ * threshold gives exactly k).  The order statistics come from the SORT
+ * path's radix sort of the row; mass is an exact count of the scores above
+ * b_mid plus fp64 sums of the terms e^{-|r - b_mid|/t}/2.
+ *   r      device [rows, n] fp32 scores
+ *   k      integer budget, 1 <= k <= n - 1 (else LAPSUM_ERR_K; n >= 2)
+ *   t      temperature, finite and > 0
+ *   b_mid  device [rows] fp64 output
+ *   mass   device [rows] fp64 output
+ *   workspace: lapsum_midpoint_workspace_bytes(rows, n) bytes, 256-byte
+ *   aligned.  Errors as lapsum_forward. */
+size_t lapsum_midpoint_workspace_bytes(int64_t rows, int64_t n);
+lapsum_status lapsum_midpoint_mass(const float *r, int64_t rows, int64_t n, int64_t k, double t, double *b_mid,
+                                   double *mass, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Size of the fixed device buffer lapsum_backward_noalloc uses instead of a
  * workspace: one per device, held until the process ends. */

@@ -21,18 +21,21 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblapsum.so")
 
-PATH_AUTO, PATH_ONCHIP, PATH_FULLSORT, PATH_BRACKET = 0, 1, 2, 3
-PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "fullsort": PATH_FULLSORT, "bracket": PATH_BRACKET}
+PATH_AUTO, PATH_ONCHIP, PATH_BUCKET, PATH_BRACKET, PATH_SORT, PATH_BISECT = 0, 1, 2, 3, 4, 5
+PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "bucket": PATH_BUCKET, "bracket": PATH_BRACKET,
+         "sort": PATH_SORT, "bisect": PATH_BISECT}
 FLAG_BRACKET, FLAG_HIT, FLAG_FALLBACK, FLAG_OVERFLOW, FLAG_DEGENERATE, FLAG_WIDENED, FLAG_INVALID = (
     0x1, 0x2, 0x4, 0x8, 0x10, 0x20, 0x40)
 ONCHIP_MAX_N = 8192
-(STAGE_ONCHIP_FWD, STAGE_INIT, STAGE_SAMPLE, STAGE_SELECT, STAGE_FILTER, STAGE_BAND, STAGE_FULLSORT,
- STAGE_APPLY, STAGE_ONCHIP_BWD, STAGE_BWD_REDUCE, STAGE_BWD_APPLY, STAGE_COUNT) = range(12)
-STAGE_NAMES = ["onchip_fwd", "init", "sample", "select", "filter", "band", "fullsort", "apply",
-               "onchip_bwd", "bwd_reduce", "bwd_apply"]
+(STAGE_ONCHIP_FWD, STAGE_INIT, STAGE_SAMPLE, STAGE_SELECT, STAGE_FILTER, STAGE_BAND, STAGE_BUCKET,
+ STAGE_APPLY, STAGE_ONCHIP_BWD, STAGE_BWD_REDUCE, STAGE_BWD_APPLY, STAGE_SORT, STAGE_SOLVE, STAGE_BISECT,
+ STAGE_COUNT) = range(15)
+STAGE_NAMES = ["onchip_fwd", "init", "sample", "select", "filter", "band", "bucket", "apply",
+               "onchip_bwd", "bwd_reduce", "bwd_apply", "sort", "solve", "bisect"]
 
 EXPORTED = ["lapsum_options_init", "lapsum_status_string", "lapsum_plan", "lapsum_bracket_indices",
-            "lapsum_workspace_bytes", "lapsum_forward", "lapsum_backward", "lapsum_backward_noalloc"]
+            "lapsum_workspace_bytes", "lapsum_forward", "lapsum_backward", "lapsum_backward_noalloc",
+            "lapsum_midpoint_workspace_bytes", "lapsum_midpoint_mass"]
 NOALLOC_SCRATCH_BYTES = 1 << 20  # LAPSUM_NOALLOC_SCRATCH_BYTES
 
 
@@ -101,6 +104,10 @@ def load_library():
     lib.lapsum_backward.restype = ctypes.c_int
     lib.lapsum_backward_noalloc.argtypes = [vp, vp, vp, i64, i64, dbl, vp, vp, ctypes.POINTER(Options), vp]
     lib.lapsum_backward_noalloc.restype = ctypes.c_int
+    lib.lapsum_midpoint_workspace_bytes.argtypes = [i64, i64]
+    lib.lapsum_midpoint_workspace_bytes.restype = ctypes.c_size_t
+    lib.lapsum_midpoint_mass.argtypes = [vp, i64, i64, i64, dbl, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.lapsum_midpoint_mass.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -318,6 +325,32 @@ def lapsum_backward_noalloc(g, p, b, t, *, out=None):
     if g.dim() == 1:
         dr = dr[0]
     return dr, dk
+
+
+def midpoint_mass(r, k: int, t: float):
+    """DFTopK diagnostic (section 2.3): per row, the fixed threshold
+    b_mid = (s_(k) + s_(k+1))/2 of the k-th and (k+1)-th largest scores and
+    the Laplace mass sum_i F((r_i - b_mid)/t) at it (fp64 tensors [rows]);
+    mass / k - 1 is the fixed midpoint's budget drift.  k: integer in
+    [1, n - 1]."""
+    torch = _torch()
+    lib = load_library()
+    r2 = _as_rows(r, "r")
+    rows, n = r2.shape
+    if int(k) != k:
+        raise LapsumError("midpoint_mass: k must be an integer")
+    dev = r2.device
+    with torch.cuda.device(dev):
+        b_mid = torch.empty(rows, dtype=torch.float64, device=dev)
+        mass = torch.empty(rows, dtype=torch.float64, device=dev)
+        nbytes = int(lib.lapsum_midpoint_workspace_bytes(rows, n))
+        ws, wptr, wlen = _workspace(max(nbytes, 1), dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.lapsum_midpoint_mass(r2.data_ptr(), rows, n, int(k), float(t), b_mid.data_ptr(), mass.data_ptr(),
+                                      wptr, wlen, stream)
+        del ws
+        _check(rc, "lapsum_midpoint_mass")
+    return b_mid, mass
 
 
 def soft_topk(r, k, t, **kw):

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblapsum.so")
-SOURCES = ["api.cpp", "onchip.hip", "stream.hip", "bracket.hip", "band.hip"]
+SOURCES = ["api.cpp", "onchip.hip", "stream.hip", "bracket.hip", "band.hip", "sort.hip", "bisect.hip"]
 ARCH = "gfx950"
 
 

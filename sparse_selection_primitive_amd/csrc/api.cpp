@@ -18,7 +18,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kOnchipMaxN = LAPSUM_ONCHIP_MAX_N;
-constexpr int64_t kFullsortMaxAutoN = (int64_t)1 << 20;
+constexpr int64_t kBucketMaxAutoN = (int64_t)1 << 20;
 constexpr int kDefaultWiden = 2;  // widened brackets tried after a miss, by default
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -88,6 +88,53 @@ BandRegions band_regions(Layout &L, int64_t rows, int64_t cap, int gx, bool full
   return r;
 }
 
+// Offsets of the workspace regions of the whole-row radix sort and the
+// solve over the sorted rows.
+struct SortRegions {
+  size_t A, B, cnt, dtot, ta, tp, ts;
+  int64_t stride;
+  int ntiles, nst;
+};
+
+SortRegions sort_regions(Layout &L, int64_t rows, int64_t n) {
+  SortRegions r;
+  r.stride = sort_stride(n);
+  r.ntiles = sort_tiles(n);
+  r.nst = solve_tiles(n);
+  const size_t keys = (size_t)rows * (size_t)r.stride * sizeof(uint32_t);
+  r.A = L.take(keys);
+  r.B = L.take(keys);
+  r.cnt = L.take((size_t)rows * 256 * (size_t)r.ntiles * sizeof(uint32_t));
+  r.dtot = L.take((size_t)rows * 256 * sizeof(uint32_t));
+  r.ta = L.take((size_t)rows * (size_t)r.nst * tile_agg_bytes());
+  r.tp = L.take((size_t)rows * (size_t)r.nst * pre_bytes());
+  r.ts = L.take((size_t)rows * (size_t)r.nst * suf_bytes());
+  return r;
+}
+
+SortArgs sort_args(const SortRegions &R, char *ws, int64_t rows, int64_t n, const float *r, RowState *st, double k,
+                   double t, RowParams rp) {
+  SortArgs a;
+  a.rows = rows;
+  a.n = n;
+  a.r = r;
+  a.A = reinterpret_cast<uint32_t *>(ws + R.A);
+  a.B = reinterpret_cast<uint32_t *>(ws + R.B);
+  a.stride = R.stride;
+  a.ntiles = R.ntiles;
+  a.cnt = reinterpret_cast<uint32_t *>(ws + R.cnt);
+  a.dtot = reinterpret_cast<uint32_t *>(ws + R.dtot);
+  a.nst = R.nst;
+  a.ta = reinterpret_cast<TileAgg *>(ws + R.ta);
+  a.tp = reinterpret_cast<Pre *>(ws + R.tp);
+  a.ts = reinterpret_cast<Suf *>(ws + R.ts);
+  a.st = st;
+  a.k = k;
+  a.t = t;
+  a.rp = rp;
+  return a;
+}
+
 struct Plan {
   int path = 0;
   int sample_log2 = 0;
@@ -102,6 +149,9 @@ struct Plan {
   int fgx = 0;
   BandRegions bnd{};
   SegRegions full_seg{};
+  SortRegions srt{};
+  size_t bis_state = 0, bis_part = 0;
+  int bis_gx = 0;
   // backward layout
   size_t bwd_bytes = 0;
   size_t bpart = 0;
@@ -203,7 +253,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
   lapsum_status st = check_common(rows, n, o.t_rows ? 1.0 : t);
   if (st != LAPSUM_OK) return st;
   if (!o.k_rows && (!std::isfinite(k) || !(k > 0.0) || !(k < (double)n))) return LAPSUM_ERR_K;
-  if (o.path < LAPSUM_PATH_AUTO || o.path > LAPSUM_PATH_BRACKET) return LAPSUM_ERR_OPTION;
+  if (o.path < LAPSUM_PATH_AUTO || o.path > LAPSUM_PATH_BISECT) return LAPSUM_ERR_OPTION;
   if (o.sample_log2 != 0 && (o.sample_log2 < 4 || o.sample_log2 > 20)) return LAPSUM_ERR_OPTION;
   if (!(o.delta == 0.0 || (o.delta > 0.0 && o.delta < 1.0))) return LAPSUM_ERR_OPTION;
   if (o.band_capacity < 0) return LAPSUM_ERR_OPTION;
@@ -213,17 +263,27 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
   int path = o.path;
   if (path == LAPSUM_PATH_AUTO)
     path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP
-                            : (n <= kFullsortMaxAutoN || per_row ? LAPSUM_PATH_FULLSORT : LAPSUM_PATH_BRACKET);
+                            : (n <= kBucketMaxAutoN || per_row ? LAPSUM_PATH_BUCKET : LAPSUM_PATH_BRACKET);
   if (path == LAPSUM_PATH_ONCHIP && n > kOnchipMaxN) return LAPSUM_ERR_PATH;
   // the bracket's sample indices are set per k on the host
   if (path == LAPSUM_PATH_BRACKET && per_row) return LAPSUM_ERR_PATH;
   P.path = path;
 
   Layout F;
-  if (path == LAPSUM_PATH_FULLSORT) {
+  if (path == LAPSUM_PATH_BUCKET) {
     P.st = F.take((size_t)rows * row_state_bytes());
     P.cap = round_up(n, kTile);
     P.bnd = band_regions(F, rows, P.cap, 0, true, n);
+  } else if (path == LAPSUM_PATH_SORT) {
+    P.st = F.take((size_t)rows * row_state_bytes());
+    P.srt = sort_regions(F, rows, n);
+  } else if (path == LAPSUM_PATH_BISECT) {
+    P.st = F.take((size_t)rows * row_state_bytes());
+    if (!bisect_onchip(n)) {
+      P.bis_gx = bisect_grid_x(rows, n);
+      P.bis_state = F.take(bisect_state_bytes(rows));
+      P.bis_part = F.take(bisect_partial_bytes(rows, P.bis_gx));
+    }
   } else if (path == LAPSUM_PATH_BRACKET) {
     int sl = o.sample_log2;
     if (sl == 0) {
@@ -454,14 +514,39 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   }
 
   RowState *rs = reinterpret_cast<RowState *>(ws + P.st);
-  if (P.path == LAPSUM_PATH_FULLSORT) {
+  if (P.path == LAPSUM_PATH_BUCKET) {
     tm.mark(LAPSUM_STAGE_INIT, 0);
     LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, n, k, t, rp, s));
     tm.mark(LAPSUM_STAGE_INIT, 1);
-    tm.mark(LAPSUM_STAGE_FULLSORT, 0);
+    tm.mark(LAPSUM_STAGE_BUCKET, 0);
     const SegArgs none{};  // full rows have no bracket, so no fallback
     LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, nullptr, nullptr, k, t, r, n, rp), none, s));
-    tm.mark(LAPSUM_STAGE_FULLSORT, 1);
+    tm.mark(LAPSUM_STAGE_BUCKET, 1);
+  } else if (P.path == LAPSUM_PATH_SORT) {
+    tm.mark(LAPSUM_STAGE_INIT, 0);
+    LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, n, k, t, rp, s));
+    tm.mark(LAPSUM_STAGE_INIT, 1);
+    const SortArgs sa = sort_args(P.srt, ws, rows, n, r, rs, k, t, rp);
+    tm.mark(LAPSUM_STAGE_SORT, 0);
+    LAPSUM_TRY(launch_row_sort(sa, s));
+    tm.mark(LAPSUM_STAGE_SORT, 1);
+    tm.mark(LAPSUM_STAGE_SOLVE, 0);
+    LAPSUM_TRY(launch_row_sort_solve(sa, s));
+    tm.mark(LAPSUM_STAGE_SOLVE, 1);
+  } else if (P.path == LAPSUM_PATH_BISECT) {
+    tm.mark(LAPSUM_STAGE_INIT, 0);
+    LAPSUM_TRY(launch_init_rows(rs, rows, 0, nullptr, n, k, t, rp, s));
+    tm.mark(LAPSUM_STAGE_INIT, 1);
+    tm.mark(LAPSUM_STAGE_BISECT, 0);
+    if (bisect_onchip(n)) {
+      // the on-chip bisection writes p and b itself
+      LAPSUM_TRY(launch_bisect_onchip(r, rows, n, k, t, rp, p, b, s));
+      tm.mark(LAPSUM_STAGE_BISECT, 1);
+      if (o.stats) LAPSUM_TRY(launch_copy_stats(rs, rows, o.stats, s));
+      return LAPSUM_OK;
+    }
+    LAPSUM_TRY(launch_bisect_stream(r, rows, n, k, t, rp, ws + P.bis_state, ws + P.bis_part, P.bis_gx, rs, s));
+    tm.mark(LAPSUM_STAGE_BISECT, 1);
   } else {
     const double *ovr = o.bracket_override;
     if (ovr) {
@@ -506,6 +591,35 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
   LAPSUM_TRY(launch_apply(r, rows, n, rs, t, rp, p, b, s));
   tm.mark(LAPSUM_STAGE_APPLY, 1);
   if (o.stats) LAPSUM_TRY(launch_copy_stats(rs, rows, o.stats, s));
+  return LAPSUM_OK;
+}
+
+size_t lapsum_midpoint_workspace_bytes(int64_t rows, int64_t n) {
+  if (check_common(rows, n, 1.0) != LAPSUM_OK) return 0;
+  Layout L;
+  sort_regions(L, rows, n);
+  L.take(midpoint_partial_bytes(rows, midpoint_grid_x(rows, n)));
+  return L.off;
+}
+
+lapsum_status lapsum_midpoint_mass(const float *r, int64_t rows, int64_t n, int64_t k, double t, double *b_mid,
+                                   double *mass, void *workspace, size_t workspace_bytes, void *stream) {
+  const lapsum_status st0 = check_common(rows, n, t);
+  if (st0 != LAPSUM_OK) return st0;
+  if (n < 2 || k < 1 || k > n - 1) return LAPSUM_ERR_K;
+  if (!r || !b_mid || !mass || !workspace) return LAPSUM_ERR_NULL;
+  Layout L;
+  const SortRegions R = sort_regions(L, rows, n);
+  const int gx = midpoint_grid_x(rows, n);
+  const size_t part = L.take(midpoint_partial_bytes(rows, gx));
+  if (workspace_bytes < L.off || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return LAPSUM_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  (void)hipGetLastError();  // see lapsum_forward
+  const SortArgs sa = sort_args(R, ws, rows, n, r, nullptr, (double)k, t, RowParams{nullptr, nullptr});
+  LAPSUM_TRY(launch_row_sort(sa, s));
+  LAPSUM_TRY(launch_midpoint(sa, k, b_mid, mass, ws + part, gx, s));
   return LAPSUM_OK;
 }
 

@@ -115,6 +115,46 @@ struct BandArgs {
   RowParams rp;         // per-row k and t (full-row mode), overriding k, t, c, cf
 };
 
+// Whole-row radix sort and the solve over the sorted rows (sort.hip): pass
+// outputs alternate A, B, A, B, so the sorted keys end in B.
+struct SortArgs {
+  int64_t rows, n;
+  const float *r;        // [rows][n] scores
+  uint32_t *A, *B;       // [rows][stride] key buffers
+  int64_t stride;        // per-row stride of A and B (a multiple of the solve tile)
+  int ntiles;            // sort tiles per row
+  uint32_t *cnt;         // [rows][256][ntiles] digit counts -> offsets inside the digit
+  uint32_t *dtot;        // [rows][256] digit totals
+  int nst;               // solve tiles per row
+  TileAgg *ta;           // [rows][nst] anchored aggregates of the solve tiles
+  Pre *tp;               // [rows][nst] scratch of the locate
+  Suf *ts;               // [rows][nst]
+  RowState *st;          // [rows]: b
+  double k, t;
+  RowParams rp;
+};
+hipError_t launch_row_sort(const SortArgs &a, hipStream_t s);
+hipError_t launch_row_sort_solve(const SortArgs &a, hipStream_t s);
+int sort_tiles(int64_t n);
+int solve_tiles(int64_t n);
+int64_t sort_stride(int64_t n);
+// DFTopK midpoint on the sorted rows (kk-th and (kk+1)-th largest) and the
+// Laplace mass there.
+hipError_t launch_midpoint(const SortArgs &a, int64_t kk, double *b_mid, double *mass, void *partials, int gx,
+                           hipStream_t s);
+int midpoint_grid_x(int64_t rows, int64_t n);
+size_t midpoint_partial_bytes(int64_t rows, int gx);
+
+// Bisection baseline (bisect.hip).
+bool bisect_onchip(int64_t n);
+hipError_t launch_bisect_onchip(const float *r, int64_t rows, int64_t n, double k, double t, RowParams rp, float *p,
+                                double *b, hipStream_t s);
+hipError_t launch_bisect_stream(const float *r, int64_t rows, int64_t n, double k, double t, RowParams rp,
+                                void *state, void *partials, int gx, RowState *st, hipStream_t s);
+int bisect_grid_x(int64_t rows, int64_t n);
+size_t bisect_state_bytes(int64_t rows);
+size_t bisect_partial_bytes(int64_t rows, int gx);
+
 // Launchers (each returns the first HIP error, or hipSuccess).
 hipError_t launch_init_rows(RowState *st, int64_t rows, int32_t flags, const double *override2, int64_t n,
                             double k, double t, RowParams rp, hipStream_t s);

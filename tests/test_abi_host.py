@@ -66,7 +66,7 @@ def test_flag_and_path_constants_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.lapsum_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.lapsum_status_string(99).decode() == "unknown status"
@@ -106,7 +106,7 @@ def test_path_choice_and_plan(lib):
     assert L.plan(8, 1024, 32, 0.1)["path"] == L.PATH_ONCHIP
     assert L.plan(8, 1024, 32, 0.1)["forward_bytes"] == 0
     p = L.plan(32, 65536, 3277, 0.01)
-    assert p["path"] == L.PATH_FULLSORT and p["forward_bytes"] > 2 * 32 * 65536 * 4
+    assert p["path"] == L.PATH_BUCKET and p["forward_bytes"] > 2 * 32 * 65536 * 4
     p = L.plan(1, 3_317_760, 600, 1e-3)
     assert p["path"] == L.PATH_BRACKET and p["m"] == 65536 and p["band_onchip"] == 1
     assert (p["lo"], p["hi"]) == (65504, 65537)
@@ -141,13 +141,13 @@ def test_plan_rejects_bad_options(lib):
 
 def test_plan_per_row_parameters(lib):
     """Per-row k / t (device arrays, never read by the host): the scalars are
-    then not checked, AUTO takes the full-sort path above the on-chip size
+    then not checked, AUTO takes the bucket path above the on-chip size
     (the bracket's sample indices need k on the host), and a forced
     bracketing path is refused."""
     dev = 4096  # a device address stand-in: planning never dereferences it
     assert L.plan(64, 256, 0.0, 0.0, k_rows_ptr=dev, t_rows_ptr=dev)["path"] == L.PATH_ONCHIP
-    assert L.plan(2, 3_317_760, 0.0, 1e-3, k_rows_ptr=dev)["path"] == L.PATH_FULLSORT
-    assert L.plan(2, 3_317_760, 600, -1.0, t_rows_ptr=dev)["path"] == L.PATH_FULLSORT
+    assert L.plan(2, 3_317_760, 0.0, 1e-3, k_rows_ptr=dev)["path"] == L.PATH_BUCKET
+    assert L.plan(2, 3_317_760, 600, -1.0, t_rows_ptr=dev)["path"] == L.PATH_BUCKET
     with pytest.raises(L.LapsumError, match="status 6"):
         L.plan(2, 3_317_760, 600, 1e-3, path="bracket", k_rows_ptr=dev)
     with pytest.raises(L.LapsumError, match="status 3"):  # the scalar k is still checked without k_rows
@@ -213,3 +213,46 @@ def test_noalloc_backward_rejects_sizes_beyond_its_buffer(lib):
     # the largest streaming batch that fits: 65536 rows x 2 partials would not, 1 per row does
     assert L.plan(65536, 2048, 1.0, 1.0)["backward_bytes"] <= L.NOALLOC_SCRATCH_BYTES
     assert L.plan(1, 100_000_000, 1.0, 1.0)["backward_bytes"] <= L.NOALLOC_SCRATCH_BYTES
+
+
+def test_stage_constants_match_header():
+    text = open(HEADER).read()
+    stages = dict(re.findall(r"LAPSUM_STAGE_(\w+) = (\d+)", text))
+    assert stages["COUNT"] == str(L.STAGE_COUNT)
+    for name, value in stages.items():
+        if name != "COUNT":
+            assert L.STAGE_NAMES[int(value)] == name.lower(), name
+
+
+def test_sort_and_bisect_plans(lib):
+    """The whole-row sort keeps two key buffers per row (strided to the
+    16384-key solve tile) plus digit counts per 4096-key tile; the bisection
+    needs no sort buffers: nothing but the row state on chip (up to 16384
+    scores), a double-buffered bracket and partials when streaming."""
+    p = L.plan(1, 100_000_000, 1e5, 0.01, path="sort")
+    assert p["path"] == L.PATH_SORT
+    stride = -(-100_000_000 // 16384) * 16384
+    assert p["forward_bytes"] >= 2 * stride * 4 + 256 * (-(-100_000_000 // 4096)) * 4
+    assert p["forward_bytes"] < 2 * stride * 4 + 40_000_000
+    p = L.plan(32, 65536, 3277, 0.01, path="bisect")
+    assert p["path"] == L.PATH_BISECT and p["forward_bytes"] < 1 << 20
+    assert L.plan(4, 16384, 10, 0.1, path="bisect")["forward_bytes"] < 4096
+    assert L.plan(1, 100_000_000, 1e5, 0.01, path="bisect")["forward_bytes"] < 1 << 20
+    # per-row k and t are accepted on both paths
+    assert L.plan(4, 20000, 0.0, 0.0, path="sort", k_rows_ptr=4096, t_rows_ptr=4096)["path"] == L.PATH_SORT
+    assert L.plan(4, 20000, 0.0, 0.1, path="bisect", k_rows_ptr=4096)["path"] == L.PATH_BISECT
+
+
+def test_midpoint_entry_checks(lib):
+    fake = ctypes.c_void_p(256)
+    need = lib.lapsum_midpoint_workspace_bytes(3, 5000)
+    assert need >= 2 * 3 * 16384 * 4
+    assert lib.lapsum_midpoint_workspace_bytes(0, 5000) == 0
+    # k must be an integer budget with 1 <= k <= n - 1 (n >= 2); checked before any launch
+    for k in (0, 5000, -1):
+        assert lib.lapsum_midpoint_mass(fake, 3, 5000, k, 0.1, fake, fake, fake, need, None) == 3
+    assert lib.lapsum_midpoint_mass(fake, 3, 1, 1, 0.1, fake, fake, fake, need, None) == 3
+    assert lib.lapsum_midpoint_mass(fake, 3, 5000, 5, 0.0, fake, fake, fake, need, None) == 4
+    assert lib.lapsum_midpoint_mass(None, 3, 5000, 5, 0.1, fake, fake, fake, need, None) == 1
+    assert lib.lapsum_midpoint_mass(fake, 3, 5000, 5, 0.1, fake, fake, fake, need - 1, None) == 5
+    assert lib.lapsum_midpoint_mass(fake, 3, 5000, 5, 0.1, fake, fake, ctypes.c_void_p(257), need, None) == 5

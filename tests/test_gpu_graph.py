@@ -30,19 +30,19 @@ def _case(kind):
     if kind == "coder_bracket":
         w = workloads.coder(rows=8)
         return w.r, w.g, w.k, w.t, "bracket"
-    if kind == "fullsort_crowded":
+    if kind == "bucket_crowded":
         # whole-row buckets of millions of keys: key-range bucket sums with
         # integer atomics, nested selection inside the balancing bucket
         g0 = np.random.Generator(np.random.PCG64(3502))
         r = g0.standard_normal((1, 3_000_000)).astype(np.float32)
         k = float(np.sum(r > 1.06)) + 0.5
-        return r, g0.standard_normal((1, 3_000_000)).astype(np.float32), k, 0.01, "fullsort"
+        return r, g0.standard_normal((1, 3_000_000)).astype(np.float32), k, 0.01, "bucket"
     g0 = np.random.Generator(np.random.PCG64(3501))  # band above one workgroup
     r = g0.standard_normal((1, 2_000_000)).astype(np.float32)
     return r, g0.standard_normal((1, 2_000_000)).astype(np.float32), 20000.0, 0.01, "bracket"
 
 
-@pytest.mark.parametrize("kind", ["routing", "routing_per_row", "coder_bracket", "bucket_band", "fullsort_crowded"])
+@pytest.mark.parametrize("kind", ["routing", "routing_per_row", "coder_bracket", "bucket_band", "bucket_crowded"])
 def test_graph_replay_matches_eager(L, kind):
     r0, g0, k, t, path = _case(kind.replace("_per_row", ""))
     rows, n = r0.shape

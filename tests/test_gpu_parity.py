@@ -154,35 +154,35 @@ def test_onchip_tiny_temperature_limit(L, O):
     assert np.max(np.abs(res["p"] - p_or)) <= 2e-5
 
 
-# ----------------------------------------------------------- full-sort path
-def test_fullsort_coder(L, O):
+# ------------------------------------------------- bucket path (full-sort solver, balancing bucket only)
+def test_bucket_coder(L, O):
     from sparse_selection_primitive_amd import workloads
     w = workloads.coder()
-    full_check(w.name + " fullsort", L, O, w.r, w.g, w.k, w.t, path="fullsort")
+    full_check(w.name + " bucket", L, O, w.r, w.g, w.k, w.t, path="bucket")
 
 
 @pytest.mark.parametrize("n,rows", [(8193, 3), (10000, 2), (70001, 2), (300, 4)])
-def test_fullsort_ragged(L, O, n, rows):
+def test_bucket_ragged(L, O, n, rows):
     g0 = np.random.Generator(np.random.PCG64(2000 + n))
     r = g0.standard_normal((rows, n)).astype(np.float32)
     g = g0.standard_normal((rows, n)).astype(np.float32)
     k = float(g0.uniform(1, n - 1))
-    full_check(f"fullsort n={n}", L, O, r, g, k, 0.05, path="fullsort")
+    full_check(f"bucket n={n}", L, O, r, g, k, 0.05, path="bucket")
 
 
-def test_fullsort_auto_boundary(L, O):
+def test_bucket_auto_boundary(L, O):
     """n = 2^20, the largest row the automatic dispatch sends to the
-    full-sort path (2048 buckets of about 512 keys)."""
+    bucket path (2048 buckets of about 512 keys)."""
     n = 1 << 20
-    assert L.plan(1, n, 1000.0, 0.01)["path"] == L.PATH_FULLSORT
+    assert L.plan(1, n, 1000.0, 0.01)["path"] == L.PATH_BUCKET
     assert L.plan(1, n + 1, 1000.0, 0.01)["path"] == L.PATH_BRACKET
     g0 = np.random.Generator(np.random.PCG64(2101))
     r = g0.standard_normal((1, n)).astype(np.float32)
     g = g0.standard_normal((1, n)).astype(np.float32)
-    full_check("fullsort n=2^20", L, O, r, g, 1000.0, 0.01)
+    full_check("bucket n=2^20", L, O, r, g, 1000.0, 0.01)
 
 
-def test_fullsort_tight_cluster(L, O):
+def test_bucket_tight_cluster(L, O):
     """Most of each row in a cluster far narrower than the bucket width the
     outliers force: the balancing bucket holds tens of thousands of keys, so
     its sums take whole waves and its sort the workgroup radix passes."""
@@ -193,10 +193,10 @@ def test_fullsort_tight_cluster(L, O):
         idx = g0.choice(n, size=60000, replace=False)
         r[i, idx] = (1.0 + 1e-4 * g0.standard_normal(60000)).astype(np.float32)
     g = g0.standard_normal((rows, n)).astype(np.float32)
-    full_check("fullsort tight cluster", L, O, r, g, 30000.5, 1e-3, path="fullsort")
+    full_check("bucket tight cluster", L, O, r, g, 30000.5, 1e-3, path="bucket")
 
 
-def test_fullsort_crowded_bucket(L, O):
+def test_bucket_crowded_bucket(L, O):
     """Full-sort path on a 3M-score normal row with the root near 1.06: the
     key bits put about 84K scores of [1, 1.125) into the balancing bucket,
     above what the workgroup sorts directly, so the locate runs the nested
@@ -207,24 +207,24 @@ def test_fullsort_crowded_bucket(L, O):
     r = g0.standard_normal((1, n)).astype(np.float32)
     g = g0.standard_normal((1, n)).astype(np.float32)
     k = float(np.sum(r > 1.06)) + 0.5
-    res, _, _ = full_check("fullsort crowded bucket", L, O, r, g, k, 0.01, path="fullsort")
-    again = run(L, r, k, 0.01, g, path="fullsort")
+    res, _, _ = full_check("bucket crowded bucket", L, O, r, g, k, 0.01, path="bucket")
+    again = run(L, r, k, 0.01, g, path="bucket")
     for key in ("p", "b", "dr", "dk"):
         assert np.array_equal(res[key], again[key]), key
 
 
 @pytest.mark.parametrize("k", [1e-3, 0.5, 9999.5])
-def test_fullsort_end_budgets(L, O, k):
+def test_bucket_end_budgets(L, O, k):
     """Budgets near 0 and near n: the balancing bucket is the first or the
     last non-empty one."""
     g0 = np.random.Generator(np.random.PCG64(2301))
     n = 10000
     r = g0.standard_normal((2, n)).astype(np.float32)
     g = g0.standard_normal((2, n)).astype(np.float32)
-    full_check(f"fullsort end budget k={k}", L, O, r, g, k, 0.05, path="fullsort")
+    full_check(f"bucket end budget k={k}", L, O, r, g, k, 0.05, path="bucket")
 
 
-def test_fullsort_constant_rows(L, O):
+def test_bucket_constant_rows(L, O):
     """Rows of one value (every bucket key equal) and a row of two values:
     the aggregates come from the counts alone, b sits at the value."""
     n = 20000
@@ -232,17 +232,17 @@ def test_fullsort_constant_rows(L, O):
     r[1, :] = -3.0
     r[2, : n // 2] = 1.0
     r[2, n // 2:] = 2.0
-    full_check("fullsort constant rows", L, O, r, None, 1234.5, 0.1, path="fullsort")
+    full_check("bucket constant rows", L, O, r, None, 1234.5, 0.1, path="bucket")
 
 
 @pytest.mark.parametrize("k", [1000.0, 1000.5])
-def test_fullsort_tiny_temperature(L, O, k):
+def test_bucket_tiny_temperature(L, O, k):
     """t = 1e-6, far below the gaps between neighbouring scores: the budget is
     flat between knots and b rests on sums e^{-gap/t} far below the fp32 range
     (an integer k puts b where the two neighbouring tails balance)."""
     g0 = np.random.Generator(np.random.PCG64(3601 + 20000 % 83))
     r = g0.standard_normal((2, 20000)).astype(np.float32)
-    full_check(f"fullsort tiny t k={k}", L, O, r, None, k, 1e-6, path="fullsort")
+    full_check(f"bucket tiny t k={k}", L, O, r, None, k, 1e-6, path="bucket")
 
 
 # ---------------------------------------------------------- bracketing path
@@ -274,14 +274,14 @@ def check_bracket_stats(name, L, O, r, k, t, stats, seed, m_log2=None, delta=1e-
             assert abs(stats[key][i].item() - ref) <= 1e-5 * abs(ref) + 1e-30, (name, key)
 
 
-def test_bracket_coder_matches_fullsort(L, O):
+def test_bracket_coder_matches_bucket(L, O):
     from sparse_selection_primitive_amd import workloads
     w = workloads.coder()
     res, p_or, b_or = full_check(w.name + " bracket", L, O, w.r, w.g, w.k, w.t, path="bracket", stats=True)
     st = res["stats"]
     assert np.all(st["flags"].numpy() & L.FLAG_HIT), st["flags"]
     check_bracket_stats(w.name, L, O, w.r, w.k, w.t, st, seed=0)
-    full = run(L, w.r, w.k, w.t, path="fullsort")
+    full = run(L, w.r, w.k, w.t, path="bucket")
     assert np.max(np.abs(full["p"] - res["p"])) <= 2e-5
     assert np.max(np.abs(full["b"] - res["b"])) / w.t <= 1e-4
 
@@ -673,12 +673,13 @@ def _max_abs_diff_chunked(a32, b64, chunk=10_000_000):
     return worst
 
 
-@pytest.mark.parametrize("path", ["bracket", "fullsort"])
-def test_extreme_row_sampled(L, O, path):
-    """1e8 scores, through the bracketing path and through the full-sort path
-    (whose balancing bucket holds millions of keys), all against the oracle's
-    bisection over the whole row: b, p at every one of the 1e8 indices, the
-    budget, dr over the whole row and dk."""
+@pytest.mark.parametrize("path", ["bracket", "bucket", "sort", "bisect"])
+def test_extreme_row(L, O, path):
+    """1e8 scores through every path that takes a row this long: bracketing,
+    the bucket path (whose balancing bucket holds millions of keys), the
+    whole-row radix sort and the streaming bisection; all against the
+    oracle's bisection over the whole row: b, p at every one of the 1e8
+    indices, the budget, dr over the whole row and dk."""
     E = _extreme_case(O)
     w, b_or, p_or = E["w"], E["b_or"], E["p_or"]
     log(f"[case] {w.name} k={w.k} t={w.t} path={path}")
@@ -713,7 +714,7 @@ def test_extreme_row_sampled(L, O, path):
 
 
 # ------------------------------------------------------- non-finite scores
-@pytest.mark.parametrize("path,n", [("onchip", 300), ("fullsort", 20000), ("bracket", 300_000)])
+@pytest.mark.parametrize("path,n", [("onchip", 300), ("bucket", 20000), ("bracket", 300_000)])
 def test_non_finite_rows_stay_contained(L, O, path, n):
     """Non-finite scores break the operator's precondition, so their rows'
     outputs are unspecified; the call must still return, and the finite row
@@ -739,7 +740,7 @@ def test_non_finite_rows_stay_contained(L, O, path, n):
 def test_determinism(L):
     from sparse_selection_primitive_amd import workloads
     w = workloads.coder(rows=4)
-    for path in ("bracket", "fullsort"):
+    for path in ("bracket", "bucket"):
         a = run(L, w.r, w.k, w.t, w.g, path=path)
         b = run(L, w.r, w.k, w.t, w.g, path=path)
         for key in ("p", "b", "dr", "dk"):
@@ -765,7 +766,7 @@ def test_autograd_wrapper(L):
 _MANY = {}
 
 
-@pytest.mark.parametrize("path", ["auto", "fullsort", "bracket"])
+@pytest.mark.parametrize("path", ["auto", "bucket", "bracket"])
 def test_many_rows_beyond_one_grid_dimension(L, O, path):
     """70000 rows of 1100 scores: more rows than one launch dimension holds
     (65535), on every path (auto: the on-chip forward and the streaming
@@ -797,7 +798,7 @@ def test_concurrent_streams_match_eager(L):
     same calls give one after the other: scratch memory comes from the
     stream-ordered allocator per call, so the streams never share it."""
     from sparse_selection_primitive_amd import workloads
-    cases = [(workloads.coder(rows=8), "bracket"), (workloads.coder(rows=8, seed=311), "fullsort"),
+    cases = [(workloads.coder(rows=8), "bracket"), (workloads.coder(rows=8, seed=311), "bucket"),
              (workloads.routing(rows=4096), "auto"), (workloads.attack(), "bracket")]
     ins = [(gpu(w.r), gpu(w.g)) for w, _ in cases]
     eager = []

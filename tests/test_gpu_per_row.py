@@ -4,7 +4,7 @@ against the oracle solved row by row with that row's values.
 Operator: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
 section 2.1 (eqs. (1)-(2), analytic VJP) -- the operator is defined per
 row, so per-row k and t change nothing but which values each row uses.
-Paths: on-chip (wave teams and one-workgroup rows) and full-sort (AUTO takes
+Paths: on-chip (wave teams and one-workgroup rows) and bucket (AUTO takes
 it above 8192 scores when per-row values are given).  Tolerances:
 tests/parity.py.
 """
@@ -84,18 +84,18 @@ def test_per_row_onchip(L, O, rows, n, k_hi):
     _check_rows("per-row on-chip", O, r, g, k, t, res)
 
 
-def test_per_row_fullsort(L, O):
-    """Rows above the on-chip size take the full-sort path (AUTO), each with
+def test_per_row_bucket(L, O):
+    """Rows above the on-chip size take the bucket path (AUTO), each with
     its own budget and temperature."""
     r, g, k, t = _case(4201, 6, 20000, 1.0, 19000.0, 1e-3, 0.5)
-    assert L.plan(6, 20000, 0.0, 0.0, k_rows_ptr=4096, t_rows_ptr=4096)["path"] == L.PATH_FULLSORT
-    log("[case] per-row full-sort rows=6 n=20000")
+    assert L.plan(6, 20000, 0.0, 0.0, k_rows_ptr=4096, t_rows_ptr=4096)["path"] == L.PATH_BUCKET
+    log("[case] per-row bucket rows=6 n=20000")
     res = _run(L, r, g, k, t, stats=True)
-    _check_rows("per-row full-sort", O, r, g, k, t, res)
+    _check_rows("per-row bucket", O, r, g, k, t, res)
 
 
 def test_per_row_large_rows(L, O):
-    """Two 2.5M-score rows with their own k and t: AUTO takes the full-sort
+    """Two 2.5M-score rows with their own k and t: AUTO takes the bucket
     path (bracketing needs k on the host), the streaming backward reads t per
     row."""
     g0 = np.random.Generator(np.random.PCG64(4301))
