@@ -5,14 +5,17 @@
 One step = one forward (threshold b and probabilities p) plus one backward
 (dr, dk) over one batch, inputs resident in HBM.  The headline workload is
 the single row of 1e8 scores (mixture 0.9 N(0,1) + 0.1 N(3, 0.5), k = 1e5,
-t = 0.01, bracketing path); the other workloads are reported beside it.
-Prints ONE JSON line.
+t = 0.01, bracketing path); the other workloads are reported beside it, each
+with its step-time distribution, the oracle timed on the host cores, the
+bracketing hit rate where it applies and the budget drift of DFTopK's fixed
+midpoint threshold.  Prints ONE JSON line.
 
 Byte model (algorithmic bytes per score, what the method itself must move):
-  on-chip rows:   fwd 8 (r in, p out), bwd 12 (g, p in, dr out)
-  bracketing:     fwd 12 (r read by the filter pass and the apply pass, p out),
-                  bwd 20 (g, p read twice, dr out: dk needs the whole row)
-  full-sort rows: fwd 8 compulsory (sort traffic measured, not credited), bwd 20
+  on-chip rows:        fwd 8 (r in, p out), bwd 12 (g, p in, dr out)
+  bracketing:          fwd 12 (r read by the filter pass and the apply pass, p out),
+                       bwd 20 (g, p read twice, dr out: dk needs the whole row)
+  bucket, sort and bisection rows: fwd 8 compulsory (sort and bisection
+                       traffic measured, not credited), bwd 20
 Per-kernel algorithmic bytes: filter 4, apply 8, bwd_reduce 8, bwd_apply 12,
 on-chip fwd 8, on-chip bwd 12 (x scores per launch).
 """
@@ -37,9 +40,10 @@ MALL_BYTES = 256 << 20
 STAGE_BYTES = {"onchip_fwd": 8, "filter": 4, "apply": 8, "onchip_bwd": 12, "bwd_reduce": 8, "bwd_apply": 12}
 KERNEL_NAMES = {"onchip_fwd": "onchip_forward_wave", "filter": "filter_kernel", "apply": "apply_kernel",
                 "onchip_bwd": "onchip_backward_wave", "bwd_reduce": "bwd_reduce_kernel",
-                "bwd_apply": "bwd_apply_kernel", "band": "band_solve_onchip / segment_kernel",
-                "select": "select_kernel", "sample": "sample_kernel", "fullsort": "segment_kernel",
-                "init": "init_rows_kernel"}
+                "bwd_apply": "bwd_apply_kernel", "band": "band_solve_onchip / band_*_kernel",
+                "select": "select_bucket_kernel", "sample": "sample_kernel", "bucket": "band_*_kernel",
+                "init": "init_rows_kernel", "sort": "rsort_*_kernel", "solve": "rsort_agg/locate_kernel",
+                "bisect": "bisect_*_kernel"}
 
 
 class Hip:
@@ -81,7 +85,7 @@ class Hip:
 
 
 WORKLOADS = {
-    # name: (generator kwargs, path, bytes fwd, bytes bwd, steps scale)
+    # name: generator, path, algorithmic bytes per score fwd / bwd
     "extreme": dict(gen="extreme", path="auto", fwd_b=12, bwd_b=20),
     "attack": dict(gen="attack", path="auto", fwd_b=12, bwd_b=20),
     "routing": dict(gen="routing", path="auto", fwd_b=8, bwd_b=12),
@@ -89,12 +93,47 @@ WORKLOADS = {
     # t_i log-uniform in [0.02, 0.1], seed 4700)
     "routing_per_row": dict(gen="routing", path="auto", fwd_b=8, bwd_b=12, per_row=True),
     "coder_bracket": dict(gen="coder", path="bracket", fwd_b=12, bwd_b=20),
-    "coder_fullsort": dict(gen="coder", path="fullsort", fwd_b=8, bwd_b=20),
-    # the 1e8 row through the full-sort path (the pages compare bracketing
-    # with a full sort at this size)
-    "extreme_fullsort": dict(gen="extreme", path="fullsort", fwd_b=8, bwd_b=20),
+    "coder_bucket": dict(gen="coder", path="bucket", fwd_b=8, bwd_b=20),
+    "coder_sort": dict(gen="coder", path="sort", fwd_b=8, bwd_b=20),
+    "coder_bisect": dict(gen="coder", path="bisect", fwd_b=8, bwd_b=20),
+    # the 1e8 row through the other exact solvers: the pages compare
+    # bracketing with a full sort at this size, and the full sort with
+    # per-query bisection
+    "extreme_bucket": dict(gen="extreme", path="bucket", fwd_b=8, bwd_b=20),
+    "extreme_sort": dict(gen="extreme", path="sort", fwd_b=8, bwd_b=20),
+    "extreme_bisect": dict(gen="extreme", path="bisect", fwd_b=8, bwd_b=20),
     "tiny": dict(gen="tiny", path="auto", fwd_b=8, bwd_b=12),
 }
+DEFAULT_CONFIGS = ("extreme,attack,routing,routing_per_row,coder_bracket,coder_bucket,coder_sort,coder_bisect,"
+                   "extreme_bucket,extreme_sort,extreme_bisect,tiny")
+
+# Bracketing hit-rate trials (seeds) per workload: 100 x 32 rows for the
+# coder batch, 1000 for the attack row, 100 for the 1e8 row.
+HIT_TRIALS = {"coder": 100, "attack": 1000, "extreme": 100}
+
+# CPU oracle baseline per workload: threads and runs (median), and for the
+# 1e8 row a bounded prefix sample (the oracle's bisection runs at ~2e5
+# scores/s on one core, so the full row would take about ten minutes).
+# Batches use every host core, single rows one core; about 30 s in all.
+CPU_PLAN = {"tiny": dict(threads="all", runs=3), "routing": dict(threads="all", runs=3),
+            "coder": dict(threads="all", runs=3), "attack": dict(threads=1, runs=1),
+            "extreme": dict(threads=1, runs=1, prefix=1_000_000)}
+
+_WORKLOAD_CACHE = {}
+
+
+def workload(gen):
+    """Each generator's arrays once per run (the 1e8 row takes seconds to draw)."""
+    from sparse_selection_primitive_amd import workloads
+    if gen not in _WORKLOAD_CACHE:
+        _WORKLOAD_CACHE[gen] = workloads.by_name(gen)
+    return _WORKLOAD_CACHE[gen]
+
+
+def quantiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
 
 
 # Source files each streaming kernel is compiled from (a change to any of them
@@ -122,10 +161,13 @@ def source_sha(files=None) -> str:
 def stages_of(L, plan, n):
     """Stage ids a call with this plan records (forward, then backward)."""
     path = plan["path"]
+    bis_stream = n > 16384
     fwd = {L.PATH_ONCHIP: [L.STAGE_ONCHIP_FWD],
-           L.PATH_FULLSORT: [L.STAGE_INIT, L.STAGE_FULLSORT, L.STAGE_APPLY],
+           L.PATH_BUCKET: [L.STAGE_INIT, L.STAGE_BUCKET, L.STAGE_APPLY],
            L.PATH_BRACKET: [L.STAGE_SAMPLE, L.STAGE_SELECT, L.STAGE_FILTER, L.STAGE_BAND,
-                            L.STAGE_APPLY]}[path]  # the fallback runs inside the band stage
+                            L.STAGE_APPLY],  # the fallback runs inside the band stage
+           L.PATH_SORT: [L.STAGE_INIT, L.STAGE_SORT, L.STAGE_SOLVE, L.STAGE_APPLY],
+           L.PATH_BISECT: [L.STAGE_INIT, L.STAGE_BISECT] + ([L.STAGE_APPLY] if bis_stream else [])}[path]
     bwd = [L.STAGE_ONCHIP_BWD] if n <= 1024 else [L.STAGE_BWD_REDUCE, L.STAGE_BWD_APPLY]
     return fwd + bwd
 
@@ -133,11 +175,13 @@ def stages_of(L, plan, n):
 def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_dominant=True):
     """live_dominant: time the dominant kernel with an event pair inside the
     timed region (the headline workload, run first); otherwise its time comes
-    from the instrumented pass and the timed region records no event (event
-    records were measured to turn into GPU round trips late in a long run of
-    workloads, inflating their timed loops several times over)."""
-    from sparse_selection_primitive_amd import workloads
-    w = workloads.by_name(spec["gen"])
+    from the instrumented pass and the timed region records no per-kernel
+    event (event records were measured to turn into GPU round trips late in a
+    long run of workloads, inflating their timed loops several times over).
+    The step-time distribution comes from one event per chunk of steps (one
+    step per chunk when a step is long, enough steps for ~0.2 ms otherwise)."""
+    import numpy as np
+    w = workload(spec["gen"])
     rows, n = w.rows, w.n
     elems = rows * n
     set_bytes = 4 * 4 * elems
@@ -158,7 +202,6 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
     plan = L.plan(rows, n, w.k, w.t, path=path, seed=seed)
     k_rows = t_rows = None
     if spec.get("per_row"):
-        import numpy as np
         gk = np.random.Generator(np.random.PCG64(4700))
         k_rows = torch.from_numpy(gk.uniform(2.0, 14.0, rows)).to(dev)
         t_rows = torch.from_numpy(np.exp(gk.uniform(np.log(0.02), np.log(0.1), rows))).to(dev)
@@ -184,27 +227,37 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
     torch.cuda.synchronize()
     ran = stages_of(L, plan, n)
     for evs in evsets:
-        for s in ran:
-            ms = hip.elapsed_ms(evs[2 * s], evs[2 * s + 1])
-            stage_ms.setdefault(L.STAGE_NAMES[s], []).append(ms)
+        for s_ in ran:
+            ms = hip.elapsed_ms(evs[2 * s_], evs[2 * s_ + 1])
+            stage_ms.setdefault(L.STAGE_NAMES[s_], []).append(ms)
         hip.destroy(evs)
     stage_avg = {k: sum(v) / len(v) for k, v in stage_ms.items()}
     dominant = max((k for k in stage_avg if k in STAGE_BYTES), key=lambda k: stage_avg[k])
     dom_id = L.STAGE_NAMES.index(dominant)
+    est_step_ms = max(sum(stage_avg.values()), 1e-3)
+    chunk = max(1, int(round(0.2 / est_step_ms)))
+    chunk = min(chunk, max(1, steps // 10))
 
-    # timed region: K steps, events only around the dominant kernel
+    # timed region: K steps; events only around the dominant kernel (headline)
+    # and at chunk boundaries (on the stream every call is launched on)
     dom_events = [(hip.event(), hip.event()) for _ in range(steps)] if live_dominant else []
     ev_lists = []
     for a, b_ in dom_events:
         evs = [None] * (2 * L.STAGE_COUNT)
         evs[2 * dom_id], evs[2 * dom_id + 1] = a, b_
         ev_lists.append(evs)
+    stream = torch.cuda.current_stream(dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps // chunk + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record(stream)
     for i in range(steps):
         step(i, ev_lists[i] if live_dominant else None)
+        if (i + 1) % chunk == 0:
+            marks[(i + 1) // chunk].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_step = [marks[j].elapsed_time(marks[j + 1]) / chunk for j in range(len(marks) - 1)]
     if live_dominant:
         dom_ms = [hip.elapsed_ms(a, b_) for a, b_ in dom_events]
         hip.destroy([e for pair in dom_events for e in pair])
@@ -251,12 +304,13 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
     ms_graph = 1e3 * wall_graph / steps
     step_bytes = (spec["fwd_b"] + spec["bwd_b"]) * elems
     dom_bytes = STAGE_BYTES[dominant] * elems
+    path_name = ["auto", "onchip", "bucket", "bracket", "sort", "bisect"][plan["path"]]
     out = {
-        "workload": w.name, "rows": rows, "n": n, "k": w.k, "t": w.t, "path": ["auto", "onchip", "fullsort",
-                                                                              "bracket"][plan["path"]],
+        "workload": w.name, "rows": rows, "n": n, "k": w.k, "t": w.t, "path": path_name,
         "fwd_bwd_elements_per_s": elems / (ms_step * 1e-3),
         "fwd_elements_per_s": elems / (ms_fwd * 1e-3),
         "ms_per_step": ms_step, "ms_fwd": ms_fwd,
+        "step_ms_quantiles": {**quantiles(per_step), "chunk_steps": chunk, "chunks": len(per_step)},
         "hbm_fraction_step": step_bytes / (ms_step * 1e-3) / HBM_PEAK,
         "hbm_fraction_fwd": spec["fwd_b"] * elems / (ms_fwd * 1e-3) / HBM_PEAK,
         "ms_per_step_graph": ms_graph,
@@ -274,47 +328,77 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
     if spec.get("per_row"):
         out["workload"] = w.name + "_per_row_k_t"
         out["k"], out["t"] = "per row, uniform in [2, 14]", "per row, log-uniform in [0.02, 0.1]"
-    return out, w
+    return out
 
 
-def hit_rate(L, torch, name, path, trials):
-    from sparse_selection_primitive_amd import workloads
-    w = workloads.by_name(name)
+def hit_rate(L, torch, gen, trials):
+    """Rows certified at the first bracket over `trials` sample seeds."""
+    w = workload(gen)
     r = torch.from_numpy(w.r).cuda()
-    hits = total = 0
+    hits = total = widened = 0
     bands = []
     for seed in range(trials):
-        _, _, st = L.lapsum_forward(r, w.k, w.t, path=path, seed=1000 + seed, stats=True)
+        _, _, st = L.lapsum_forward(r, w.k, w.t, path="bracket", seed=1000 + seed, stats=True)
         fl = st["flags"]
         hits += int(((fl & L.FLAG_HIT) != 0).sum().item())
+        widened += int(((fl & L.FLAG_WIDENED) != 0).sum().item())
         total += fl.numel()
         bands.append(float(st["band"].double().mean().item()))
-    return {"hits": hits, "total": total, "rate": hits / total, "mean_band": sum(bands) / len(bands)}
+    return {"hits": hits, "total": total, "rate": hits / total, "widened": widened, "seeds": trials,
+            "mean_band": sum(bands) / len(bands)}
 
 
-def cpu_baseline(w_extreme_r, k, t, n_sample):
-    """The oracle as it stands, on the first n_sample scores of the row with
-    the budget scaled to keep k/n, forward (bisection) + backward."""
+def midpoint_drift(L, torch, gen):
+    """DFTopK's fixed midpoint threshold on the workload's rows: the mass the
+    Laplace kernel assigns there against k (LapSum's own threshold gives k)."""
+    w = workload(gen)
+    k = int(round(w.k))
+    _, mass = L.midpoint_mass(torch.from_numpy(w.r).cuda(), k, w.t)
+    rel = (mass / k - 1.0).cpu()
+    return {"k": k, "mass_mean": float(mass.mean().item()), "drift_mean": float(rel.mean().item()),
+            "drift_max_abs": float(rel.abs().max().item())}
+
+
+def cpu_baseline(gen):
+    """The oracle as it stands, timed on the host cores: forward (bisection)
+    and forward + backward, median over runs; rows split across all cores for
+    batches, one core for single rows, and for the 1e8 row a prefix sample
+    with k scaled to keep k/n."""
     import numpy as np
 
     import oracle
-    r = np.ascontiguousarray(w_extreme_r[0, :n_sample])
-    ks = k * n_sample / w_extreme_r.shape[1]
-    g = np.random.Generator(np.random.PCG64(502)).standard_normal(n_sample).astype(np.float32)
-    threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    _, b = oracle.forward(r, ks, t, threads=threads)
-    oracle.backward(r, b, g, t, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": n_sample / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_sample} scores of the 1e8 row, k scaled to {ks:g} (same k/n), t={t}; "
-                      f"fp64 bisection forward + analytic VJP, {dt:.2f} s wall"}
+    w = workload(gen)
+    plan = CPU_PLAN[gen]
+    threads = oracle.default_threads() if plan["threads"] == "all" else plan["threads"]
+    r, g, k = w.r, w.g, w.k
+    sample = f"all {w.rows}x{w.n} scores"
+    if "prefix" in plan and plan["prefix"] < w.n:
+        m = plan["prefix"]
+        r = np.ascontiguousarray(w.r[:, :m])
+        g = np.ascontiguousarray(w.g[:, :m])
+        k = w.k * m / w.n
+        sample = f"first {m} scores of the {w.n}-score row, k scaled to {k:g} (same k/n)"
+    fwd, both = [], []
+    for _ in range(plan["runs"]):
+        t0 = time.perf_counter()
+        _, b = oracle.forward(r, k, w.t, threads=threads)
+        t1 = time.perf_counter()
+        oracle.backward(r, b, g, w.t, threads=threads)
+        t2 = time.perf_counter()
+        fwd.append(t1 - t0)
+        both.append(t2 - t0)
+    elems = r.size
+    fwd_s, both_s = sorted(fwd)[len(fwd) // 2], sorted(both)[len(both) // 2]
+    return {"value": elems / both_s, "unit": "elements/s", "fwd_elements_per_s": elems / fwd_s, "cores": threads,
+            "runs": plan["runs"], "kind": "oracle",
+            "sample": f"{sample}, t={w.t}; fp64 bisection forward + analytic VJP, median of {plan['runs']} "
+                      f"({both_s:.2f} s fwd+bwd)"}
 
 
-def load_traffic(kernel_stage: str, workload: str):
+def load_traffic(kernel_stage: str, workload_name: str):
     """Calibrated HBM bytes per launch from the committed counter summary, or
     None when there is none or the kernel's sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_stage}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_stage}_{workload_name}.json")
     if not os.path.exists(path) or kernel_stage not in KERNEL_SOURCES:
         return None
     with open(path) as f:
@@ -324,15 +408,38 @@ def load_traffic(kernel_stage: str, workload: str):
     return tr.get("bytes_per_launch")
 
 
+def comparisons(results):
+    """The pages' relative-speed claims, re-measured here (forward only)."""
+    out = {}
+
+    def ratio(slow, fast):
+        if slow in results and fast in results:
+            return results[slow]["ms_fwd"] / results[fast]["ms_fwd"]
+        return None
+    pairs = {"bracket_vs_sort_1e8": ("extreme_sort", "extreme"),
+             "bracket_vs_bucket_1e8": ("extreme_bucket", "extreme"),
+             "sort_vs_bisect_1e8": ("extreme_bisect", "extreme_sort"),
+             "bracket_vs_sort_32x65536": ("coder_sort", "coder_bracket"),
+             "sort_vs_bisect_32x65536": ("coder_bisect", "coder_sort"),
+             "bucket_vs_sort_32x65536": ("coder_sort", "coder_bucket")}
+    for key, (slow, fast) in pairs.items():
+        v = ratio(slow, fast)
+        if v is not None:
+            out[key] = {"speedup_fwd": v, "slower": slow, "faster": fast}
+    out["pages"] = {"bracket_vs_full_sort_1e8": "up to 19x", "full_sort_vs_bisection": "nearly two orders of magnitude",
+                    "note": "hardware, precision and workload not stated"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs",
-                    default="extreme,attack,routing,routing_per_row,coder_bracket,coder_fullsort,extreme_fullsort,tiny")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--hit-trials", type=int, default=20)
+    ap.add_argument("--hit-trials", type=float, default=1.0,
+                    help="scale of the planned hit-rate trial counts (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -350,19 +457,18 @@ def main():
     hip = Hip()
     names = [c for c in args.configs.split(",") if c]
     results = {}
-    extreme_w = None
     head_name = "extreme" if "extreme" in names else names[0]
     for name in names:
         steps = args.steps if name.startswith("extreme") else max(args.steps, 100)
-        res, w = bench_workload(L, hip, torch, name, WORKLOADS[name], steps, args.warmup,
-                                live_dominant=(name == head_name))
+        res = bench_workload(L, hip, torch, name, WORKLOADS[name], steps, args.warmup,
+                             live_dominant=(name == head_name))
         results[name] = res
-        if name == "extreme":
-            extreme_w = w
-        print(f"# {name}: {res['fwd_bwd_elements_per_s']:.3e} el/s fwd+bwd, {res['ms_per_step']:.4f} ms/step, "
+        q = res["step_ms_quantiles"]
+        print(f"# {name}: {res['fwd_bwd_elements_per_s']:.3e} el/s fwd+bwd, {res['ms_per_step']:.4f} ms/step "
+              f"(median {q['median']:.4f}, p10 {q['p10']:.4f}, p90 {q['p90']:.4f}), "
               f"{100 * res['hbm_fraction_step']:.1f}% HBM (graph replay {res['ms_per_step_graph']:.4f} ms, "
-              f"{100 * res['hbm_fraction_step_graph']:.1f}%), dominant {res['dominant']['stage']} "
-              f"{res['dominant']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+              f"{100 * res['hbm_fraction_step_graph']:.1f}%), fwd {res['ms_fwd']:.4f} ms, dominant "
+              f"{res['dominant']['stage']} {res['dominant']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -372,18 +478,39 @@ def main():
         torch.cuda.synchronize()
         del a, bb
 
-    hits = {}
+    gens = []
+    for name in names:
+        gen = WORKLOADS[name]["gen"]
+        if gen not in gens:
+            gens.append(gen)
+    # bracketing hit rates (every configuration that brackets this generator's rows)
     if args.hit_trials > 0:
-        if "extreme" in names:
-            hits["extreme"] = hit_rate(L, torch, "extreme", "auto", args.hit_trials)
-        if "attack" in names:
-            hits["attack"] = hit_rate(L, torch, "attack", "auto", 5 * args.hit_trials)
-        if "coder_bracket" in names:
-            hits["coder"] = hit_rate(L, torch, "coder", "bracket", args.hit_trials)
-    for k_, v in hits.items():
-        key = {"coder": "coder_bracket"}.get(k_, k_)
-        if key in results:
-            results[key]["hit_rate"] = v
+        for gen, trials in HIT_TRIALS.items():
+            users = [nm for nm in names if WORKLOADS[nm]["gen"] == gen and results[nm]["path"] == "bracket"]
+            if users:
+                hr = hit_rate(L, torch, gen, max(1, int(round(trials * args.hit_trials))))
+                for nm in users:
+                    results[nm]["hit_rate"] = hr
+                print(f"# hit rate {gen}: {hr['hits']}/{hr['total']}", file=sys.stderr, flush=True)
+    # DFTopK fixed-midpoint budget drift, per workload
+    for gen in gens:
+        md = midpoint_drift(L, torch, gen)
+        for nm in names:
+            if WORKLOADS[nm]["gen"] == gen and not WORKLOADS[nm].get("per_row"):
+                results[nm]["dftopk_midpoint"] = md
+        print(f"# DFTopK midpoint {gen}: mass/k - 1 = {md['drift_mean']:.3e}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    # the oracle on the host cores, per workload
+    cpu_by_gen = {}
+    if not args.no_cpu_baseline:
+        for gen in gens:
+            cpu_by_gen[gen] = cpu_baseline(gen)
+            for nm in names:
+                if WORKLOADS[nm]["gen"] == gen:
+                    results[nm]["cpu_baseline"] = cpu_by_gen[gen]
+            print(f"# oracle {gen}: {cpu_by_gen[gen]['value']:.3e} el/s fwd+bwd on {cpu_by_gen[gen]['cores']} cores",
+                  file=sys.stderr, flush=True)
 
     head = results[head_name]
     sha = source_sha()
@@ -392,10 +519,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": dom["GBps"] * 1e9 / HBM_PEAK, "traffic": traffic,
                 "kernel": dom["kernel"], "algorithmic_bytes_per_launch": dom["bytes"],
-                "avg_launch_ms": dom["avg_ms"]}
-    cpu = None
-    if not args.no_cpu_baseline and extreme_w is not None:
-        cpu = cpu_baseline(extreme_w.r, extreme_w.k, extreme_w.t, 20_000_000)
+                "avg_launch_ms": dom["avg_ms"], "step_frac": head["hbm_fraction_step"]}
     line = {
         "metric": "soft top-k elements/s fwd+bwd and % HBM roofline, n=3.3M and n=1e8, 1 GPU",
         "value": head["fwd_bwd_elements_per_s"],
@@ -413,10 +537,11 @@ def main():
                    "t": head["t"], "path": head["path"], "parallelism": "single GPU"},
         "hbm_fraction_step": head["hbm_fraction_step"],
         "roofline": roofline,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_by_gen.get(WORKLOADS[head_name]["gen"]),
         "source_sha": sha,
         "pages_context": {"n": 100_000_000, "ms": 5.23,
                           "note": "hardware, precision, k, t, distribution and fwd/bwd not stated"},
+        "comparisons": comparisons(results),
         "configs": results,
     }
     print(json.dumps(line))
