@@ -63,9 +63,10 @@ def check_backward(name, r, b_or, g, t, dr_gpu, dk_gpu, dr_or, dk_or):
     inherit it as floor_dr = 2^-24/t ||g - dk||_{p>1/2} and
     floor_dk = 2^-24/t sum_{p>1/2} |g - dk| / D.  The bound used is
     max(plain bound, floor), never their sum: where the floor is below the
-    plain bound (every standard workload) the check is exactly the plain one.
-    Returns the worst relative errors and the worst floor / plain-bound ratios
-    (a ratio above 1 means the floor decided that row's bound)."""
+    plain bound the check is exactly the plain one.
+    Returns the worst plain relative errors (err / ||dr_or||, err / scale_dk);
+    check_backward.last holds the worst floor / plain-bound ratios and the
+    number of rows whose bound the floor decided."""
     r = np.asarray(r, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     if r.ndim == 1:
@@ -75,37 +76,38 @@ def check_backward(name, r, b_or, g, t, dr_gpu, dk_gpu, dr_or, dk_or):
     dk_gpu = np.atleast_1d(np.asarray(dk_gpu, dtype=np.float64))
     dk_or = np.atleast_1d(np.asarray(dk_or, dtype=np.float64))
     u = 2.0 ** -24
-    worst_dr = worst_dk = 0.0
+    rel_dr = rel_dk = 0.0
     ratio_dr = ratio_dk = 0.0
+    floor_rows = 0
     for i in range(r.shape[0]):
         zed = (r[i] - b_or[i]) / t
         above = zed > 0                      # p > 1/2
         dev = g[i] - dk_or[i]
         floor_dr = (u / t) * float(np.linalg.norm(dev[above]))
-        plain_dr = TOL_GRAD * float(np.linalg.norm(dr_or[i]))
-        bound_dr = max(plain_dr, floor_dr)
-        if plain_dr > 0:
-            ratio_dr = max(ratio_dr, floor_dr / plain_dr)
+        norm_dr = float(np.linalg.norm(dr_or[i]))
         err_dr = float(np.linalg.norm(dr_gpu[i] - dr_or[i]))
-        if bound_dr > 0:
-            worst_dr = max(worst_dr, TOL_GRAD * err_dr / bound_dr)
-        else:
-            assert err_dr == 0.0, f"{name}: row {i}: dr must be 0"
+        assert err_dr <= max(TOL_GRAD * norm_dr, floor_dr), (
+            f"{name}: row {i}: ||ddr|| = {err_dr:.3e}, ||dr|| = {norm_dr:.3e}, floor {floor_dr:.3e}")
+        if norm_dr > 0:
+            rel_dr = max(rel_dr, err_dr / norm_dr)
+            ratio_dr = max(ratio_dr, floor_dr / (TOL_GRAD * norm_dr))
         a = np.abs(zed)
         w = np.exp(-(a - a.min()))
         scale = float(np.sum(w * np.abs(g[i])) / np.sum(w))
         D = float(np.sum(0.5 * np.exp(-a))) / t
         floor_dk = (u / t) * float(np.sum(np.abs(dev[above]))) / D if D > 0 else math.inf
-        plain_dk = TOL_GRAD * scale
-        bound_dk = max(plain_dk, floor_dk)
-        if plain_dk > 0 and math.isfinite(floor_dk):
-            ratio_dk = max(ratio_dk, floor_dk / plain_dk)
-        if bound_dk > 0 and math.isfinite(bound_dk):
-            worst_dk = max(worst_dk, TOL_GRAD * abs(dk_gpu[i] - dk_or[i]) / bound_dk)
-    assert worst_dr <= TOL_GRAD, f"{name}: dr rel err = {worst_dr:.3e} (floor/bound {ratio_dr:.2e})"
-    assert worst_dk <= TOL_GRAD, f"{name}: dk rel err = {worst_dk:.3e} (floor/bound {ratio_dk:.2e})"
-    check_backward.last_floor_ratio = (ratio_dr, ratio_dk)
-    return worst_dr, worst_dk
+        err_dk = abs(dk_gpu[i] - dk_or[i])
+        if math.isfinite(floor_dk):
+            assert err_dk <= max(TOL_GRAD * scale, floor_dk), (
+                f"{name}: row {i}: |ddk| = {err_dk:.3e}, scale {scale:.3e}, floor {floor_dk:.3e}")
+        if scale > 0:
+            rel_dk = max(rel_dk, err_dk / scale)
+            if math.isfinite(floor_dk):
+                ratio_dk = max(ratio_dk, floor_dk / (TOL_GRAD * scale))
+        if floor_dr > TOL_GRAD * norm_dr or (math.isfinite(floor_dk) and floor_dk > TOL_GRAD * scale):
+            floor_rows += 1
+    check_backward.last = (ratio_dr, ratio_dk, floor_rows)
+    return rel_dr, rel_dk
 
 
-check_backward.last_floor_ratio = (0.0, 0.0)
+check_backward.last = (0.0, 0.0, 0)

@@ -65,8 +65,9 @@ def full_check(name, L, O, r, g, k, t, **opts):
     if g is not None:
         dr_or, dk_or = O.backward(r, b_or, g, t)
         edr, edk = check_backward(name, r, b_or, g, t, res["dr"], res["dk"], dr_or, dk_or)
-        fr = check_backward.last_floor_ratio
-        out += f" dr_rel={edr:.2e} dk_rel={edk:.2e} fp32-floor/bound dr={fr[0]:.2e} dk={fr[1]:.2e}"
+        fr = check_backward.last
+        out += (f" dr_rel={edr:.2e} dk_rel={edk:.2e} fp32-floor/bound dr={fr[0]:.2e} dk={fr[1]:.2e}"
+                f" rows decided by the floor={fr[2]}")
     log(out)
     return res, p_or, b_or
 
