@@ -145,7 +145,8 @@ struct Plan {
   bool band_onchip = false;
   // forward layout
   size_t fwd_bytes = 0;
-  size_t st = 0, samples = 0, spart = 0, fpart = 0, slots = 0, offs = 0;
+  size_t st = 0, samples = 0, spart = 0, fpart = 0, slots = 0, offs = 0, tail = 0;
+  int tailq = 0;  // depth of the per-group top lists (0: the general selection)
   int fgx = 0;
   BandRegions bnd{};
   SegRegions full_seg{};
@@ -329,6 +330,8 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.st = F.take((size_t)rows * row_state_bytes());
     P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
     P.spart = F.take(sample_start_bytes(rows, P.m));
+    P.tailq = tail_depth(P.m, P.lo, P.hi);
+    if (P.tailq > 0) P.tail = F.take(tail_bytes(rows, P.m, P.tailq));
     P.fgx = filter_grid_x(rows, n, P.cap);
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
@@ -558,10 +561,15 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
       float *samples = reinterpret_cast<float *>(ws + P.samples);
       uint16_t *spart = reinterpret_cast<uint16_t *>(ws + P.spart);
       tm.mark(LAPSUM_STAGE_SAMPLE, 0);
-      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, spart, rs, LAPSUM_FLAG_BRACKET, s));
+      uint32_t *tail = P.tailq > 0 ? reinterpret_cast<uint32_t *>(ws + P.tail) : nullptr;
+      LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, spart, rs, LAPSUM_FLAG_BRACKET, tail, P.tailq,
+                               s));
       tm.mark(LAPSUM_STAGE_SAMPLE, 1);
       tm.mark(LAPSUM_STAGE_SELECT, 0);
-      LAPSUM_TRY(launch_select(samples, spart, rows, P.m, P.lo, P.hi, rs, s));
+      if (tail != nullptr)
+        LAPSUM_TRY(launch_select_tail(tail, rows, P.m, P.tailq, P.lo, P.hi, rs, s));
+      else
+        LAPSUM_TRY(launch_select(samples, spart, rows, P.m, P.lo, P.hi, rs, s));
       tm.mark(LAPSUM_STAGE_SELECT, 1);
     }
     uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);

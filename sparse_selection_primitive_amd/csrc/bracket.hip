@@ -15,6 +15,7 @@
 // key (seed low, seed high) and counter (j, row, 0, 0): words x0, x1 give
 // I = floor((x1 2^32 + x0) n / 2^64), word x2 gives u = (x2 + 1/2)/2^32 and
 // L = F^-1(u) in fp64; X is rounded to fp32.
+#include <algorithm>
 #include <atomic>
 
 #include "filter_dev.hpp"
@@ -53,6 +54,34 @@ constexpr int kCoarseBits = 10;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 static_assert(kCoarseBins == kSampleThreads, "one coarse bin per sample thread");
 
+// Top-side selection ("tail mode"): when both bracket ranks lie within the
+// Q largest samples, each sample workgroup also writes its own Q largest
+// keys, sorted descending; the R-th largest of the whole sample (R <= Q) is
+// then the R-th largest of those lists (no group contributes more than R of
+// its own keys to the top R), so the selection reads groups x Q keys instead
+// of the whole sample.
+constexpr int kTailWaveSort = 16 * kWave;  // largest candidate set one wave sorts
+template <int E>
+LDEV void wave_sort_pick(const uint32_t *f, int nf, uint32_t R, uint32_t *out);
+constexpr int kTailMaxKeys = 4096;        // groups x Q the selection holds in LDS
+
+// One wave sorts the nc candidate scores src[0..nc) (with nc, Q <= 64*E) and
+// writes the Q largest keys, descending, to out (key 0, below every key, pads).
+template <int E>
+LDEV void wave_top_sorted(const float *src, int nc, int Q, uint32_t *out) {
+  WaveTeam<kWave> team;
+  const int base = team.lane * E;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = base + e < nc ? key_of(src[base + e]) : 0u;
+  bitonic_sort<E>(key, team);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = kWave * E - 1 - (base + e);  // rank from the top
+    if (i < Q) out[i] = key[e];
+  }
+}
+
 LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   uint32_t inc = v;
@@ -70,11 +99,13 @@ LDEV uint32_t block_excl_scan_u32(uint32_t v, uint32_t *wsum) {
   return before + inc - v;
 }
 
+template <bool TAIL>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__restrict__ r, int64_t rows,
                                                                 int64_t n, double t, int64_t m, uint32_t k0,
                                                                 uint32_t k1, float *__restrict__ samples,
                                                                 uint16_t *__restrict__ starts,
-                                                                RowState *__restrict__ st, int32_t flags) {
+                                                                RowState *__restrict__ st, int32_t flags,
+                                                                uint32_t *__restrict__ tail, int Q) {
   __shared__ uint32_t cnt[kCoarseBins];
   __shared__ uint32_t wsum[kSampleThreads / kWave];
   __shared__ float stage[kSampleWg];
@@ -133,6 +164,48 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__r
   __syncthreads();
   const int nvalid = (int)min(m - g0, (int64_t)kSampleWg);
   for (int i = threadIdx.x; i < nvalid; i += kSampleThreads) samples[row * m + g0 + i] = stage[i];
+  if constexpr (TAIL) {
+    // this group's Q largest keys, descending: the candidates are the staged
+    // scores from the start of the coarse bin that holds the Q-th largest on
+    // (stage is in ascending bin order; cnt holds the bin starts)
+    __shared__ uint32_t cbeg;
+    __shared__ BlockTeamLds<kSampleThreads, 2> blds;
+    const int j0 = nvalid > Q ? nvalid - Q : 0;
+    {
+      const uint32_t s0 = cnt[threadIdx.x];
+      const uint32_t s1 = threadIdx.x + 1 < (unsigned)kCoarseBins ? cnt[threadIdx.x + 1] : (uint32_t)nvalid;
+      if (s0 <= (uint32_t)j0 && (uint32_t)j0 < s1) cbeg = s0;  // exactly one bin holds j0
+    }
+    __syncthreads();
+    const int nc = nvalid - (int)cbeg;
+    uint32_t *out = tail + (row * gridDim.x + blockIdx.x) * (int64_t)Q;
+    const int need = nc > Q ? nc : Q;
+    if (need <= kTailWaveSort) {
+      if (threadIdx.x < kWave) {
+        const float *src = stage + cbeg;
+        if (need <= 64) wave_top_sorted<1>(src, nc, Q, out);
+        else if (need <= 128) wave_top_sorted<2>(src, nc, Q, out);
+        else if (need <= 256) wave_top_sorted<4>(src, nc, Q, out);
+        else if (need <= 512) wave_top_sorted<8>(src, nc, Q, out);
+        else wave_top_sorted<16>(src, nc, Q, out);
+      }
+    } else {
+      // a crowded coarse bin: the whole workgroup sorts all its samples
+      BlockTeam<kSampleThreads, 2> team(&blds);
+      uint32_t key[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * (int)threadIdx.x + e;
+        key[e] = i < nvalid ? key_of(stage[i]) : 0u;
+      }
+      bitonic_sort<2>(key, team);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = kSampleWg - 1 - (2 * (int)threadIdx.x + e);
+        if (i < Q) out[i] = key[e];
+      }
+    }
+  }
 }
 
 int sample_groups(int64_t m) { return (int)((m + kSampleWg - 1) / kSampleWg); }
@@ -141,10 +214,188 @@ size_t sample_start_bytes(int64_t rows, int64_t m) {
 }
 
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, rows_grid((unsigned)sample_groups(m), rows), dim3(kSampleThreads), 0, s, r,
-                     rows, n, t, m, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), samples, starts, st,
-                     flags);
+                         float *samples, uint16_t *starts, RowState *st, int32_t flags, uint32_t *tail, int Q,
+                         hipStream_t s) {
+  const dim3 grid = rows_grid((unsigned)sample_groups(m), rows);
+  const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
+  if (tail != nullptr)
+    hipLaunchKernelGGL(sample_kernel<true>, grid, dim3(kSampleThreads), 0, s, r, rows, n, t, m, k0, k1, samples,
+                       starts, st, flags, tail, Q);
+  else
+    hipLaunchKernelGGL(sample_kernel<false>, grid, dim3(kSampleThreads), 0, s, r, rows, n, t, m, k0, k1, samples,
+                       starts, st, flags, tail, Q);
+  return hipGetLastError();
+}
+
+// Top-side depth of the bracket ranks: the lo-th and hi-th smallest of m
+// samples are the (m - lo + 1)-th and (m - hi + 1)-th largest.  Returns the
+// depth Q the tail lists must hold, or 0 when tail mode does not apply.
+int tail_depth(int64_t m, int64_t lo, int64_t hi) {
+  int64_t q = 1;
+  if (lo >= 1) q = std::max(q, m - lo + 1);
+  if (hi <= m) q = std::max(q, m - hi + 1);
+  const int64_t groups = sample_groups(m);
+  if (q > kTailWaveSort || groups * q > kTailMaxKeys) return 0;
+  return (int)q;
+}
+size_t tail_bytes(int64_t rows, int64_t m, int Q) {
+  return sizeof(uint32_t) * (size_t)rows * (size_t)sample_groups(m) * (size_t)Q;
+}
+
+// One workgroup per row: the bracket ends from the groups' top-Q lists.
+// For each target, the ascending rank groups*Q - R among the groups*Q keys
+// (held 16 per thread) is found by bucketing relative to the keys' own
+// range: 2048 LDS buckets over the top 11 bits of (key - kmin), the bucket
+// that holds the rank, and, while that bucket holds more than one wave can
+// sort, the same again inside it on the next bits; the last bucket's keys
+// are gathered and sorted by one wave.  (Digit passes over the raw key bits
+// would pile every candidate of a narrow range onto one LDS counter.)
+constexpr int kTailThreads = 256;
+constexpr int kTailPerThread = kTailMaxKeys / kTailThreads;
+constexpr int kTailBinBits = 11;
+constexpr int kTailBins = 1 << kTailBinBits;
+constexpr int kTailBinsPer = kTailBins / kTailThreads;
+
+struct TailLds {
+  uint32_t hist[kTailBins];
+  uint32_t cand[kTailWaveSort];
+  uint32_t wsum[kTailThreads / kWave];
+  uint32_t red[2 * kTailThreads / kWave];
+  uint32_t bin, rank, count, ncand, result;
+};
+
+// Key of ascending rank `rank` among the N valid keys, all of which lie in
+// [lo, lo + 2^wbits).  Each pass splits the current range into at most
+// kTailBins buckets of 2^shift keys and keeps the one that holds the rank.
+LDEV uint32_t tail_select_rank(const uint32_t (&key)[kTailPerThread], int N, uint32_t rank, uint32_t lo,
+                               int wbits, TailLds &L) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  uint32_t cnt = (uint32_t)N;
+  for (;;) {
+    const int shift = wbits > kTailBinBits ? wbits - kTailBinBits : 0;
+    const uint64_t width = (uint64_t)1 << wbits;
+    for (int j = threadIdx.x; j < kTailBins; j += kTailThreads) L.hist[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTailPerThread; ++j) {
+      const uint32_t kk = key[j];
+      if (j * kTailThreads + (int)threadIdx.x < N && kk >= lo && (uint64_t)(kk - lo) < width)
+        atomicAdd(&L.hist[(kk - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    // exclusive scan over the buckets (kTailBinsPer consecutive ones per thread)
+    uint32_t c[kTailBinsPer], local = 0u;
+#pragma unroll
+    for (int q = 0; q < kTailBinsPer; ++q) {
+      c[q] = L.hist[threadIdx.x * kTailBinsPer + q];
+      local += c[q];
+    }
+    const uint32_t inc = wave_incl_scan(local);
+    if (lane == kWave - 1) L.wsum[w] = inc;
+    __syncthreads();
+    uint32_t acc = inc - local;
+    for (int i = 0; i < w; ++i) acc += L.wsum[i];
+    if (rank >= acc && rank < acc + local) {  // exactly one thread
+#pragma unroll
+      for (int q = 0; q < kTailBinsPer; ++q) {
+        if (rank >= acc && rank < acc + c[q]) {
+          L.bin = threadIdx.x * kTailBinsPer + q;
+          L.rank = rank - acc;
+          L.count = c[q];
+        }
+        acc += c[q];
+      }
+    }
+    __syncthreads();
+    lo += L.bin << shift;
+    rank = L.rank;
+    cnt = L.count;
+    wbits = shift;
+    __syncthreads();
+    if (wbits == 0) return lo;  // the bucket holds a single key value
+    if (cnt <= (uint32_t)kTailWaveSort) break;
+  }
+  // gather the keys of the last bucket and let one wave sort them
+  if (threadIdx.x == 0) L.ncand = 0u;
+  __syncthreads();
+  const uint64_t width = (uint64_t)1 << wbits;
+#pragma unroll
+  for (int j = 0; j < kTailPerThread; ++j) {
+    const uint32_t kk = key[j];
+    if (j * kTailThreads + (int)threadIdx.x < N && kk >= lo && (uint64_t)(kk - lo) < width)
+      L.cand[atomicAdd(&L.ncand, 1u)] = kk;  // cnt <= kTailWaveSort of them
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int nf = (int)L.ncand;
+    if (nf <= 64) wave_sort_pick<1>(L.cand, nf, rank, &L.result);
+    else if (nf <= 128) wave_sort_pick<2>(L.cand, nf, rank, &L.result);
+    else if (nf <= 256) wave_sort_pick<4>(L.cand, nf, rank, &L.result);
+    else if (nf <= 512) wave_sort_pick<8>(L.cand, nf, rank, &L.result);
+    else wave_sort_pick<16>(L.cand, nf, rank, &L.result);
+  }
+  __syncthreads();
+  const uint32_t res = L.result;
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kTailThreads) void select_tail_kernel(const uint32_t *__restrict__ tail, int64_t rows,
+                                                                   int groups, int Q, int64_t m, int64_t lo,
+                                                                   int64_t hi, RowState *__restrict__ st) {
+  __shared__ TailLds L;
+  const int64_t row = grid_row();
+  if (row >= rows) return;
+  const int N = groups * Q;
+  const uint32_t *src = tail + row * (int64_t)N;
+  uint32_t key[kTailPerThread];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kTailPerThread; ++j) {
+    const int i = j * kTailThreads + (int)threadIdx.x;
+    key[j] = src[i < N ? i : 0];
+  }
+#pragma unroll
+  for (int j = 0; j < kTailPerThread; ++j) {
+    if (j * kTailThreads + (int)threadIdx.x < N) {
+      mn = min(mn, key[j]);
+      mx = max(mx, key[j]);
+    }
+  }
+  // the keys' range over the workgroup (padding keys 0 included)
+  mn = wave_reduce(mn, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+  mx = wave_reduce(mx, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  if (lane == 0) {
+    L.red[2 * w] = mn;
+    L.red[2 * w + 1] = mx;
+  }
+  __syncthreads();
+  for (int i = 0; i < kTailThreads / kWave; ++i) {
+    mn = min(mn, L.red[2 * i]);
+    mx = max(mx, L.red[2 * i + 1]);
+  }
+  const uint32_t span = mx - mn;
+  const int bits = span == 0u ? 0 : 32 - __clz((int)span);
+  const int wbits = bits > kTailBinBits ? bits : kTailBinBits;
+  const bool want[2] = {lo >= 1, hi <= m};
+  uint32_t res[2] = {0u, 0u};
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg) {
+    if (!want[tg]) continue;  // uniform over the workgroup
+    const uint32_t R = (uint32_t)(tg == 0 ? m - lo + 1 : m - hi + 1);
+    res[tg] = span == 0u ? mn : tail_select_rank(key, N, (uint32_t)N - R, mn, wbits, L);
+  }
+  if (threadIdx.x == 0) {
+    st[row].a_lo = want[0] ? (double)value_of(res[0]) : -INFINITY;
+    st[row].a_hi = want[1] ? (double)value_of(res[1]) : INFINITY;
+  }
+}
+
+hipError_t launch_select_tail(const uint32_t *tail, int64_t rows, int64_t m, int Q, int64_t lo, int64_t hi,
+                              RowState *st, hipStream_t s) {
+  hipLaunchKernelGGL(select_tail_kernel, rows_grid(1u, rows), dim3(kTailThreads), 0, s, tail, rows,
+                     sample_groups(m), Q, m, lo, hi, st);
   return hipGetLastError();
 }
 

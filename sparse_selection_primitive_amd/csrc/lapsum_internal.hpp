@@ -164,7 +164,14 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
                                   float *dr, float *dk, lapsum_row_stats *stats, hipStream_t s);
 bool onchip_backward_supported(int64_t n);
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
-                         float *samples, uint16_t *starts, RowState *st, int32_t flags, hipStream_t s);
+                         float *samples, uint16_t *starts, RowState *st, int32_t flags, uint32_t *tail, int Q,
+                         hipStream_t s);
+// Top-side selection of the bracket: the depth Q of the per-group top lists
+// (0: not applicable), their size, and the selection over them.
+int tail_depth(int64_t m, int64_t lo, int64_t hi);
+size_t tail_bytes(int64_t rows, int64_t m, int Q);
+hipError_t launch_select_tail(const uint32_t *tail, int64_t rows, int64_t m, int Q, int64_t lo, int64_t hi,
+                              RowState *st, hipStream_t s);
 size_t sample_start_bytes(int64_t rows, int64_t m);
 hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
                          int64_t hi, RowState *st, hipStream_t s);

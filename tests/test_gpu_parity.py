@@ -303,6 +303,8 @@ def _row_case(kind, n, seed):
         r = g0.standard_normal((1, n))
     elif kind == "grid":  # 1/8 grid: samples tie exactly when t is far below the grid
         r = np.round(g0.standard_normal((1, n)) * 8.0) / 8.0
+    elif kind == "crowded":  # every score, and every noised sample, in the coarse bin [1, 1.5)
+        r = 1.05 + 0.4 * g0.random((1, n))
     else:
         raise ValueError(kind)
     return r.astype(np.float32), g0.standard_normal((1, n)).astype(np.float32)
@@ -313,6 +315,8 @@ def _row_case(kind, n, seed):
     ("grid", 1.0 / 3.0, 1e-12, 0),  # every sample on the grid: selection ends on a whole key
     ("normal", 0.01, 0.01, 18),    # sample above the register-resident size
     ("normal", 0.2, 0.05, 4),      # 16 samples
+    ("normal", 0.001, 0.01, 0),    # top-side ranks: each sample group's top list, one wave's sort
+    ("crowded", 0.005, 1e-4, 0),   # top-side ranks in one crowded coarse bin: the group sorts all
 ])
 def test_bracket_select_paths(L, O, kind, k_frac, t, m_log2):
     """Bracket ends against the oracle's own Philox sample and order
