@@ -5,6 +5,11 @@
 Every translation unit is compiled by hipcc for gfx950 only, with packed
 fp32 instructions disabled, then linked into one shared library next to this
 file.  Object files go to ``_build/`` (not tracked).
+
+``build_host_sanitized(path)`` builds a second copy of the library for CPU
+checks of the host runtime: its host code instrumented with AddressSanitizer
+and UndefinedBehaviorSanitizer (the device code is built as usual, without
+them).
 """
 from __future__ import annotations
 
@@ -46,6 +51,35 @@ def _compile(src: str) -> str:
     if errs.strip():
         sys.stderr.write(errs + "\n")
     return obj
+
+
+def build_host_sanitized(out: str, jobs: int | None = None) -> str:
+    """Host-only ASan + UBSan build of every translation unit, linked to
+    ``out``.  The sanitizer runtime is not linked in: the program that loads
+    the library must carry it (a sanitized executable, or the runtime
+    preloaded)."""
+    objdir = out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    flags = ["-x", "hip", f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-I", os.path.join(HERE, "..", "include")]
+
+    def one(src: str) -> str:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        res = subprocess.run([hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj], capture_output=True,
+                             text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitized host build failed for {src}:\n{res.stderr}")
+        return obj
+
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    res = subprocess.run([hipcc(), "-shared", "-fPIC", "-o", out, *objs], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized host link failed:\n{res.stderr}")
+    return out
 
 
 def build(jobs: int | None = None) -> str:
