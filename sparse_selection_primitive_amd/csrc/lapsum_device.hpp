@@ -312,6 +312,34 @@ struct WaveTeam {
     const uint32_t lo = f((uint32_t)u), hi = f((uint32_t)(u >> 32));
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
   }
+  template <int OFF>
+  LDEV static double up64(double v) {
+    return move64<OFF>(v, [](uint32_t x) { return up<OFF>(x); });
+  }
+  template <int OFF>
+  LDEV static double down64(double v) {
+    return move64<OFF>(v, [](uint32_t x) { return down<OFF>(x); });
+  }
+  // exclusive prefix and suffix sums of v over the team (plain fp64)
+  template <int OFF>
+  LDEV void sum_scan_steps(double &pre, double &suf) const {
+    if constexpr (OFF < LANES) {
+      const double yp = up64<OFF>(pre), ys = down64<OFF>(suf);
+      if (lane >= OFF) pre += yp;
+      if (lane + OFF < LANES) suf += ys;
+      sum_scan_steps<2 * OFF>(pre, suf);
+    }
+  }
+  // (the exclusive values are the neighbours' inclusive ones, not the
+  // inclusive ones minus the lane's own: that difference would cancel when
+  // the lane's own value dwarfs the rest)
+  LDEV void excl_sums(double vp, double vs, double *pre, double *suf) const {
+    double ip = vp, is = vs;
+    sum_scan_steps<1>(ip, is);
+    const double ep = up64<1>(ip), es = down64<1>(is);
+    *pre = lane == 0 ? 0.0 : ep;
+    *suf = lane == LANES - 1 ? 0.0 : es;
+  }
   template <int M>
   LDEV static void sum_steps(int &v) {
     if constexpr (M < LANES) {

@@ -88,6 +88,108 @@ LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (
   }
 }
 
+// Root over the certified window's sorted candidates when they span few
+// temperatures.  The candidates s_0 <= ... <= s_{M-1} (blocked: lane l holds
+// s[l*E .. l*E+nv-1]) all lie at or above a0, everything below a0 is the
+// tail S = sum e^{(r - a0)/t}, and nothing lies above the window.  With every
+// sum anchored at a0 (u_i = e^{(s_i - a0)/t} >= 1 and v_i = 1/u_i, both
+// finite in fp32 when (s_{M-1} - a0) c <= kWindowSpan), the threshold curve at
+// knot j is
+//   g_j = (S + sum_{i<j} u_i) v_j / 2 + (M - j - 1/2) - u_j (sum_{i>j} v_i) / 2
+// (the knot itself counts F(0) = 1/2): plain prefix and suffix sums over the
+// team replace the re-anchored scans.  The last knot with g_j >= k is just
+// below the root, and the closed form between it and the next knot gives b
+// (section 2.2, full-sort solver: threshold curve, index lookup, closed-form
+// root).  Returns b on every team lane.
+constexpr float kWindowSpan = 120.0f;  // largest (s_{M-1} - a0) log2(e)/t of the fast solve
+
+template <int E, int LANES>
+LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv, int M, float a0, double S,
+                        double k, double t) {
+  // u = 2^z and v = 2^-z, z = (s - a0) log2(e)/t formed in fp64 and split
+  // into its integer part (applied exactly by ldexp) and a fraction in
+  // [0, 1) for exp2: u and v carry the exp2's relative error only, however
+  // large z is
+  float u[E], v[E];
+  double lu = 0.0, lv = 0.0;
+  const double c = kLog2e / t;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double z = ((double)s[e] - (double)a0) * c;  // >= 0
+    const double zi = floor(z);
+    const float zf = (float)(z - zi);
+    u[e] = e < nv ? __builtin_ldexpf(__builtin_amdgcn_exp2f(zf), (int)zi) : 0.0f;
+    v[e] = e < nv ? __builtin_ldexpf(__builtin_amdgcn_exp2f(-zf), -(int)zi) : 0.0f;
+    lu += (double)u[e];
+    lv += (double)v[e];
+  }
+  // the u sums of the lanes before this one, the v sums of those after it
+  double pu, sv;
+  team.excl_sums(lu, lv, &pu, &sv);
+  const int base = team.lane * E;
+  // threshold curve at this lane's knots; the count of knots with g >= k
+  double below[E], above[E];
+  {
+    double acc = S + pu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      below[e] = acc;  // S + sum over knots before this one, at a0
+      acc += (double)u[e];
+    }
+    double acc2 = sv;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) {
+      above[e] = acc2;  // sum over knots after this one, at a0
+      acc2 += (double)v[e];
+    }
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < nv) {
+      const double g = 0.5 * below[e] * (double)v[e] + ((double)(M - base - e) - 0.5) - 0.5 * (double)u[e] * above[e];
+      cnt += g >= k ? 1 : 0;
+    }
+  }
+  const int js = team.sum(cnt) - 1;  // -1 .. M-1: the last knot with g >= k
+  const int owner = js < 0 ? 0 : js / E;
+  // the first knot above the root, for the clamp (this lane's next knot is
+  // its own or the first of the next lane)
+  const float nxt_lane = __uint_as_float(WaveTeam<LANES>::template down<1>(__float_as_uint(s[0])));
+  double b = 0.0;
+  if (team.lane == owner) {
+    double x, PA, QA, cab, hi;
+    if (js < 0) {  // below every knot: everything at a0
+      x = a0;
+      PA = S;
+      QA = sv + lv;  // lane 0: all of the knots
+      cab = (double)M;
+      hi = s[0];
+    } else {
+      const int e0 = js - base;
+      x = s[0];
+      PA = below[0] * (double)v[0] + 1.0;
+      QA = (double)u[0] * above[0];
+      hi = js + 1 < M ? nxt_lane : INFINITY;
+#pragma unroll
+      for (int e = 1; e < E; ++e) {
+        if (e == e0) {
+          x = s[e];
+          PA = below[e] * (double)v[e] + 1.0;
+          QA = (double)u[e] * above[e];
+        }
+        if (e == e0 + 1 && e < nv) hi = s[e];
+      }
+      cab = (double)(M - 1 - js);
+    }
+    const double lP = PA > 0.0 ? log_pos(PA) : -INFINITY;
+    const double lQ = QA > 0.0 ? log_pos(QA) : -INFINITY;
+    b = solve_root(x, lP, lQ, cab, k, t);
+    b = fmin(fmax(b, x), hi);
+  }
+  return team.bcast(b, owner);
+}
+
 // Certified window for a small budget: with the K-th largest (K = ceil(k))
 // of the lanes' second-largest scores as a, at least 2K >= 2k scores are
 // >= a, each with p >= 1/2 at b = a, so f(a) >= k and b >= a.  Only the
@@ -156,8 +258,14 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
     const int nv = min(max(C - 2 * team.lane, 0), 2);
 #pragma unroll
     for (int q = 0; q < 2; ++q) s2[q] = q < nv ? s2[q] : 0.0f;
-    part.nvalid = nv;
-    bw = segment_solve<2>(s2, nv, part, kk, t, c, cf, team);
+    // the window's span: its largest candidate is the team's last valid one
+    const float top = team.bcast(nv == 2 ? s2[1] : s2[0], (C - 1) / 2);
+    if ((top - a) * cf <= kWindowSpan) {
+      bw = window_root<2>(team, s2, nv, C, a, S, kk, t);
+    } else {
+      part.nvalid = nv;
+      bw = segment_solve<2>(s2, nv, part, kk, t, c, cf, team);
+    }
   } else {
     float s4[4];
 #pragma unroll

@@ -421,6 +421,69 @@ def test_fallback_heavy_ties_overflow(L, O):
     assert fl & L.FLAG_OVERFLOW and fl & L.FLAG_FALLBACK
 
 
+def _onchip_band_case(name, L, O, r, g, k, t, lo, hi):
+    n = r.shape[1]
+    assert L.plan(1, n, k, t, path="bracket")["band_onchip"] == 1
+    res, _, _ = full_check(name, L, O, r, g, k, t, path="bracket", bracket_override=(lo, hi), stats=True)
+    st = res["stats"]
+    fl = st["flags"][0].item()
+    log(f"  band M={st['band'][0].item()} flags={fl}")
+    assert fl & L.FLAG_HIT and not fl & L.FLAG_FALLBACK, fl
+    again = run(L, r, k, t, g, path="bracket", bracket_override=(lo, hi))
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(res[key], again[key]), key
+    return st
+
+
+def test_bracket_onchip_band_nested_bucket(L, O):
+    """On-chip band whose keys are ~2000 distinct values packed into 5e-4
+    (five temperatures) next to a few far ones, with the root inside the
+    cluster: the band's key range is dominated by the far keys, while the
+    root's neighbourhood is crowded."""
+    g0 = np.random.Generator(np.random.PCG64(3901))
+    n, t = 1_000_000, 1e-4
+    r = (g0.standard_normal((1, n)) - 6.0).astype(np.float32)
+    idx = g0.choice(n, size=2100, replace=False)
+    r[0, idx[:2000]] = g0.uniform(1.0, 1.0005, 2000).astype(np.float32)
+    r[0, idx[2000:2010]] = g0.uniform(1.3, 1.45, 10).astype(np.float32)  # far band keys
+    r[0, idx[2010:]] = g0.uniform(2.0, 3.0, 90).astype(np.float32)       # above the band
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = O.budget(r[0], 1.00025, t)  # the root in the middle of the cluster
+    st = _onchip_band_case("onchip band nested bucket", L, O, r, g, k, t, 0.9, 1.5)
+    assert st["band"][0].item() == 2010
+
+
+def test_bracket_onchip_band_heavy_ties(L, O):
+    """On-chip band holding 600 copies of one value right above the root:
+    the knot just above b is a run of equal keys."""
+    g0 = np.random.Generator(np.random.PCG64(4001))
+    n, t = 1_000_000, 0.01
+    r = (g0.standard_normal((1, n)) - 6.0).astype(np.float32)
+    idx = g0.choice(n, size=1000, replace=False)
+    r[0, idx[:600]] = 1.0
+    r[0, idx[600:800]] = g0.uniform(0.6, 1.4, 200).astype(np.float32)
+    r[0, idx[800:]] = g0.uniform(2.0, 3.0, 200).astype(np.float32)
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = O.budget(r[0], 0.999, t)  # the root just below the repeated value
+    st = _onchip_band_case("onchip band heavy ties", L, O, r, g, k, t, 0.5, 1.5)
+    assert st["band"][0].item() == 800
+
+
+def test_bracket_onchip_band_empty(L, O):
+    """A bracket over a gap in the scores (six temperatures wide) that holds
+    the root: the band is empty and the tail sums alone place b."""
+    g0 = np.random.Generator(np.random.PCG64(4101))
+    n, t = 1_000_000, 0.5
+    r = (g0.standard_normal((1, n)) - 7.0).astype(np.float32)
+    idx = g0.choice(n, size=300, replace=False)
+    r[0, idx] = g0.uniform(2.0, 3.0, 300).astype(np.float32)
+    assert not np.any((r >= 0.0) & (r < 1.0))
+    g = g0.standard_normal((1, n)).astype(np.float32)
+    k = O.budget(r[0], 0.5, t)
+    st = _onchip_band_case("onchip band empty", L, O, r, g, k, t, 0.0, 1.0)
+    assert st["band"][0].item() == 0
+
+
 def test_bracket_loose_delta_many_seeds(L, O):
     """delta = 0.9 makes misses common; every row must still match, through
     the whole-row fallback when widening is off."""
