@@ -265,30 +265,32 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
     else:
         dom_avg = stage_avg[dominant]
 
-    # the same steps replayed from HIP graphs (one captured forward+backward
-    # per buffer set): the launch cost of each kernel leaves the step
-    graphs = []
+    # the same steps replayed from one HIP graph that holds a forward+backward
+    # on every buffer set in turn: the launch cost of each kernel leaves the
+    # step, and one graph launch covers nsets steps (a graph launch per
+    # ~20 us step would leave the GPU waiting on the host)
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(torch.cuda.current_stream(dev))
+    gr = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cap):
-        for i in range(nsets):
-            r, g, p, b, dr, dk = sets[i]
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=cap):
-                cs = cap.cuda_stream
+        with torch.cuda.graph(gr, stream=cap):
+            cs = cap.cuda_stream
+            for i in range(nsets):
+                r, g, p, b, dr, dk = sets[i]
                 op.forward(r, p, b, stream=cs)
                 op.backward(g, p, b, dr, dk, stream=cs)
-            graphs.append(gr)
     torch.cuda.current_stream(dev).wait_stream(cap)
-    for i in range(max(warmup, nsets)):
-        graphs[i % nsets].replay()
+    for _ in range(max(1, warmup // nsets)):
+        gr.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-steps // nsets))
     t2 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % nsets].replay()
+    for _ in range(reps):
+        gr.replay()
     torch.cuda.synchronize()
     wall_graph = time.perf_counter() - t2
-    del graphs
+    graph_steps = reps * nsets
+    del gr
 
     # forward-only timing (same rotation)
     torch.cuda.synchronize()
@@ -301,7 +303,7 @@ def bench_workload(L, hip, torch, name, spec, steps, warmup, seed=0, live_domina
 
     ms_step = 1e3 * wall / steps
     ms_fwd = 1e3 * wall_fwd / steps
-    ms_graph = 1e3 * wall_graph / steps
+    ms_graph = 1e3 * wall_graph / graph_steps
     step_bytes = (spec["fwd_b"] + spec["bwd_b"]) * elems
     dom_bytes = STAGE_BYTES[dominant] * elems
     path_name = ["auto", "onchip", "bucket", "bracket", "sort", "bisect"][plan["path"]]
