@@ -81,7 +81,8 @@ typedef enum lapsum_status {
 #define LAPSUM_ONCHIP_MAX_N 8192
 
 typedef enum lapsum_path {
-    LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: BUCKET; else BRACKET */
+    LAPSUM_PATH_AUTO = 0,     /* n <= 8192: ONCHIP; n <= 2^20: BUCKET; else BRACKET (also with
+                                 per-row k or t) */
     LAPSUM_PATH_ONCHIP = 1,   /* fused per-row bitonic sort + scan + root + apply (n <= 8192) */
     LAPSUM_PATH_BUCKET = 2,   /* the full-sort solver sorting only the balancing bucket: one radix
                                  (bucket) pass over the row, order-free bucket sums, locate, sort of
@@ -161,10 +162,13 @@ typedef struct lapsum_options {
                               does not gets NaN outputs and LAPSUM_FLAG_INVALID. */
     const double *t_rows;  /* device [rows] or NULL: a temperature per row (the t argument is
                               then not used), 0 < t_i < inf, likewise.  lapsum_backward reads
-                              it too.  With k_rows or t_rows the bracketing path is not
-                              available (its sample indices are set per k on the host): AUTO
-                              takes the BUCKET path above 8192 scores, and a forced
-                              LAPSUM_PATH_BRACKET is LAPSUM_ERR_PATH. */
+                              it too.  On the bracketing path with k_rows or t_rows each row's
+                              order-statistic indices come from its own k (computed on the
+                              device, from the same binomial definition), its sample is noised
+                              with its own t, the band is sized for the widest bracket (that of
+                              k = n/2) and solved by the bucketed band solve, and a row whose
+                              bracket misses goes straight to the exact whole-row fallback (no
+                              widening: the widened indices would depend on k). */
 } lapsum_options;
 
 /* Resolved plan of a call (host-only query, no GPU needed). */
@@ -173,7 +177,8 @@ typedef struct lapsum_plan_info {
     int32_t sample_log2;   /* bracketing: log2(m) */
     int64_t m;             /* bracketing: sample size */
     int64_t lo, hi;        /* bracketing: 1-based order-statistic indices; lo = 0 means
-                              a_L = -inf, hi = m + 1 means a_R = +inf */
+                              a_L = -inf, hi = m + 1 means a_R = +inf; both -1 when every
+                              row has its own (per-row budgets or temperatures) */
     int64_t band_capacity; /* bracketing: band buffer length per row */
     int32_t band_onchip;   /* bracketing: 1 if the band is solved on chip (capacity <= 8192) */
     int32_t filter_groups; /* bracketing: streaming-filter workgroups per row; their band slots

@@ -143,6 +143,8 @@ struct Plan {
   int64_t wlo[kMaxWiden] = {}, whi[kMaxWiden] = {};
   int64_t cap = 0;  // band capacity per row
   bool band_onchip = false;
+  bool per_row = false;  // per-row k or t
+  double delta = 0.0;    // bracketing: the miss bound of the first bracket
   // forward layout
   size_t fwd_bytes = 0;
   size_t st = 0, samples = 0, spart = 0, fpart = 0, slots = 0, offs = 0, tail = 0;
@@ -263,12 +265,10 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
 
   int path = o.path;
   if (path == LAPSUM_PATH_AUTO)
-    path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP
-                            : (n <= kBucketMaxAutoN || per_row ? LAPSUM_PATH_BUCKET : LAPSUM_PATH_BRACKET);
+    path = n <= kOnchipMaxN ? LAPSUM_PATH_ONCHIP : (n <= kBucketMaxAutoN ? LAPSUM_PATH_BUCKET : LAPSUM_PATH_BRACKET);
   if (path == LAPSUM_PATH_ONCHIP && n > kOnchipMaxN) return LAPSUM_ERR_PATH;
-  // the bracket's sample indices are set per k on the host
-  if (path == LAPSUM_PATH_BRACKET && per_row) return LAPSUM_ERR_PATH;
   P.path = path;
+  P.per_row = per_row;
 
   Layout F;
   if (path == LAPSUM_PATH_BUCKET) {
@@ -297,10 +297,14 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.sample_log2 = sl;
     P.m = (int64_t)1 << sl;
     const double delta = o.delta == 0.0 ? 1e-6 : o.delta;
-    bracket_indices(n, k, P.m, delta, &P.lo, &P.hi);
+    P.delta = delta;
+    // with a budget per row the indices are the rows' own (set on the device);
+    // the band is sized for the widest bracket, that of k = n/2
+    bracket_indices(n, per_row && o.k_rows ? 0.5 * (double)n : k, P.m, delta, &P.lo, &P.hi);
     // widened brackets: step i takes the indices for delta * 1e-6^i, kept
-    // only where they are wider than the bracket before them
-    const int steps = o.widen_steps == 0 ? kDefaultWiden : (o.widen_steps < 0 ? 0 : o.widen_steps);
+    // only where they are wider than the bracket before them (none with
+    // per-row budgets: a missed row goes straight to the exact fallback)
+    const int steps = per_row ? 0 : (o.widen_steps == 0 ? kDefaultWiden : (o.widen_steps < 0 ? 0 : o.widen_steps));
     int64_t plo = P.lo, phi = P.hi;
     double d = delta;
     for (int i = 0; i < steps; ++i) {
@@ -325,12 +329,14 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
       P.cap = (int64_t)std::ceil(cap);
     }
     if (P.cap < 1) P.cap = 1;
-    P.band_onchip = P.cap <= kOnchipMaxN;
+    // per-row values: the bucketed band solve, which reads each row's own
+    // k and t (the on-chip one takes the call's)
+    P.band_onchip = P.cap <= kOnchipMaxN && !per_row;
     if (!P.band_onchip) P.cap = round_up(P.cap, kTile);
     P.st = F.take((size_t)rows * row_state_bytes());
     P.samples = F.take((size_t)rows * (size_t)P.m * sizeof(float));
     P.spart = F.take(sample_start_bytes(rows, P.m));
-    P.tailq = tail_depth(P.m, P.lo, P.hi);
+    P.tailq = per_row ? 0 : tail_depth(P.m, P.lo, P.hi);
     if (P.tailq > 0) P.tail = F.take(tail_bytes(rows, P.m, P.tailq));
     P.fgx = filter_grid_x(rows, n, P.cap);
     P.fpart = F.take(filter_partial_bytes(rows, P.fgx));
@@ -471,8 +477,8 @@ lapsum_status lapsum_plan(int64_t rows, int64_t n, double k, double t, const lap
   out->path = P.path;
   out->sample_log2 = P.sample_log2;
   out->m = P.m;
-  out->lo = P.lo;
-  out->hi = P.hi;
+  out->lo = P.per_row && P.path == LAPSUM_PATH_BRACKET ? -1 : P.lo;
+  out->hi = P.per_row && P.path == LAPSUM_PATH_BRACKET ? -1 : P.hi;
   out->band_capacity = P.cap;
   out->band_onchip = P.band_onchip ? 1 : 0;
   out->filter_groups = P.fgx;
@@ -554,7 +560,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     const double *ovr = o.bracket_override;
     if (ovr) {
       tm.mark(LAPSUM_STAGE_INIT, 0);
-      LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, n, k, t, RowParams{nullptr, nullptr}, s));
+      LAPSUM_TRY(launch_init_rows(rs, rows, LAPSUM_FLAG_BRACKET, ovr, n, k, t, rp, s));
       tm.mark(LAPSUM_STAGE_INIT, 1);
     } else {
       // the sample kernel also resets the rows' state
@@ -563,22 +569,28 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
       tm.mark(LAPSUM_STAGE_SAMPLE, 0);
       uint32_t *tail = P.tailq > 0 ? reinterpret_cast<uint32_t *>(ws + P.tail) : nullptr;
       LAPSUM_TRY(launch_sample(r, rows, n, t, P.m, o.seed, samples, spart, rs, LAPSUM_FLAG_BRACKET, tail, P.tailq,
-                               s));
+                               o.t_rows, s));
       tm.mark(LAPSUM_STAGE_SAMPLE, 1);
       tm.mark(LAPSUM_STAGE_SELECT, 0);
-      if (tail != nullptr)
+      if (P.per_row) {
+        // each row's own indices (and k, t) into its state; the selection reads them
+        LAPSUM_TRY(launch_bracket_rows(o.k_rows, o.t_rows, k, t, rows, n, P.m, P.delta, rs, s));
+        LAPSUM_TRY(launch_select(samples, spart, rows, P.m, -1, -1, rs, s));
+      } else if (tail != nullptr) {
         LAPSUM_TRY(launch_select_tail(tail, rows, P.m, P.tailq, P.lo, P.hi, rs, s));
-      else
+      } else {
         LAPSUM_TRY(launch_select(samples, spart, rows, P.m, P.lo, P.hi, rs, s));
+      }
       tm.mark(LAPSUM_STAGE_SELECT, 1);
     }
     uint32_t *slots = reinterpret_cast<uint32_t *>(ws + P.slots);
     uint32_t *offs = reinterpret_cast<uint32_t *>(ws + P.offs);
     tm.mark(LAPSUM_STAGE_FILTER, 0);
-    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, ws + P.fpart, P.fgx, s));
+    LAPSUM_TRY(launch_filter(r, rows, n, t, rs, slots, ws + P.fpart, P.fgx, P.per_row, s));
     tm.mark(LAPSUM_STAGE_FILTER, 1);
     tm.mark(LAPSUM_STAGE_BAND, 0);
     SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
+    fb.per_row = P.per_row ? 1 : 0;
     if (!ovr) {  // a bracket given by the caller has no sample to widen from
       fb.samples = reinterpret_cast<const float *>(ws + P.samples);
       fb.m = P.m;

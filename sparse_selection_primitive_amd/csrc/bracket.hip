@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__r
                                                                 uint32_t k1, float *__restrict__ samples,
                                                                 uint16_t *__restrict__ starts,
                                                                 RowState *__restrict__ st, int32_t flags,
-                                                                uint32_t *__restrict__ tail, int Q) {
+                                                                uint32_t *__restrict__ tail, int Q,
+                                                                const double *__restrict__ t_rows) {
   __shared__ uint32_t cnt[kCoarseBins];
   __shared__ uint32_t wsum[kSampleThreads / kWave];
   __shared__ float stage[kSampleWg];
@@ -113,6 +114,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float *__r
   if (row >= rows) return;
   const int64_t g0 = (int64_t)blockIdx.x * kSampleWg;
   if (blockIdx.x == 0 && threadIdx.x == 0) reset_row_state(st, row, flags, 0, 0.0, 0.0);  // this call's state
+  if (t_rows != nullptr) {  // the row's own temperature (an out-of-range one: 1, the row is flagged later)
+    const double tr = t_rows[row];
+    t = tr > 0.0 && tr < INFINITY ? tr : 1.0;
+  }
   cnt[threadIdx.x] = 0u;
   // indices of this thread's samples first and all the gathers issued, then
   // the noise, whose logarithms overlap the gathers' latency
@@ -215,15 +220,135 @@ size_t sample_start_bytes(int64_t rows, int64_t m) {
 
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
                          float *samples, uint16_t *starts, RowState *st, int32_t flags, uint32_t *tail, int Q,
-                         hipStream_t s) {
+                         const double *t_rows, hipStream_t s) {
   const dim3 grid = rows_grid((unsigned)sample_groups(m), rows);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   if (tail != nullptr)
     hipLaunchKernelGGL(sample_kernel<true>, grid, dim3(kSampleThreads), 0, s, r, rows, n, t, m, k0, k1, samples,
-                       starts, st, flags, tail, Q);
+                       starts, st, flags, tail, Q, t_rows);
   else
     hipLaunchKernelGGL(sample_kernel<false>, grid, dim3(kSampleThreads), 0, s, r, rows, n, t, m, k0, k1, samples,
-                       starts, st, flags, tail, Q);
+                       starts, st, flags, tail, Q, t_rows);
+  return hipGetLastError();
+}
+
+// ------------------------------------------- per-row bracket indices
+// With a budget per row, step 1's order-statistic indices depend on the row:
+// one workgroup per row computes them on the device from the same
+// definition the host applies to a single budget.  With N ~ Bin(m, q),
+// q = 1 - k/n (the share of the row below b),
+//   lo = max{l in [0, m]   : P(N <= l - 1) <= delta/2},
+//   hi = min{h in [1, m+1] : P(N >= h)     <= delta/2}.
+// The pmf is summed over mean +- 40 sd (the rest of its mass is far below
+// fp64 resolution): each thread walks its stretch of j with the ratio
+// recurrence from a start value taken from lgamma, and the tail sums come
+// from block prefix / suffix sums of the stretches.  The row's k and t (an
+// out-of-range value replaced and the row flagged invalid) and c go to its
+// state for the later stages.
+constexpr int kBrThreads = 1024;
+
+__global__ __launch_bounds__(kBrThreads) void bracket_rows_kernel(const double *__restrict__ k_rows,
+                                                                  const double *__restrict__ t_rows, double k,
+                                                                  double t, int64_t rows, int64_t n, int64_t m,
+                                                                  double delta, RowState *__restrict__ st) {
+  __shared__ double wsum[2][kBrThreads / kWave];
+  __shared__ int wext[2][kBrThreads / kWave];
+  const int64_t row = grid_row();
+  if (row >= rows) return;
+  const bool good = row_params(k_rows, t_rows, row, n, k, t);
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  constexpr int NW = kBrThreads / kWave;
+  const double pk = k / (double)n;  // 1 - q
+  const double qd = 1.0 - pk;
+  const double lq = log1p(-pk), l1q = log(pk), ratio = qd / pk;
+  const double mean = (double)m * qd, sd = sqrt((double)m * qd * pk);
+  const double wdt = 40.0 * sd + 40.0;
+  const int64_t j0 = (int64_t)fmax(0.0, floor(mean - wdt)), j1 = (int64_t)fmin((double)m, ceil(mean + wdt));
+  const int64_t len = j1 - j0 + 1, per = (len + kBrThreads - 1) / kBrThreads;
+  const int64_t js = j0 + (int64_t)threadIdx.x * per, je = min(js + per - 1, j1);
+  // log pmf relative to its value at the mode (the bulk stays near 1)
+  const double lgm = lgamma((double)m + 1.0);
+  auto lpmf = [&](int64_t j) {
+    return lgm - lgamma((double)j + 1.0) - lgamma((double)(m - j) + 1.0) + (double)j * lq + (double)(m - j) * l1q;
+  };
+  const int64_t mode = min(max((int64_t)floor((double)(m + 1) * qd), (int64_t)0), m);
+  const double lref = lpmf(mode);
+  const double p0 = js <= je ? exp(lpmf(js) - lref) : 0.0;
+  double part = 0.0;
+  {
+    double p = p0;
+    for (int64_t j = js; j <= je; ++j) {
+      part += p;
+      p *= (double)(m - j) / (double)(j + 1) * ratio;
+    }
+  }
+  // exclusive prefix and suffix of the stretch sums (each a sum over the
+  // other stretches only, never a difference), and the total
+  double inc = part, sinc = part;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(inc, off, kWave), z = __shfl_down(sinc, off, kWave);
+    if (lane >= off) inc += y;
+    if (lane + off < kWave) sinc += z;
+  }
+  if (lane == kWave - 1) wsum[0][w] = inc;
+  if (lane == 0) wsum[1][w] = sinc;
+  const double exc = __shfl_up(inc, 1, kWave), sexc = __shfl_down(sinc, 1, kWave);
+  __syncthreads();
+  double before = lane == 0 ? 0.0 : exc, after = lane == kWave - 1 ? 0.0 : sexc, tot = 0.0;
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) before += wsum[0][i];
+    if (i > w) after += wsum[1][i];
+    tot += wsum[0][i];
+  }
+  const double half = 0.5 * delta * tot;
+  // walks: the last j with P(N <= j) <= half, the first h with P(N >= h) <= half
+  int cand_lo = -1, cand_hi = (int)m + 2;  // m <= 2^20
+  {
+    double p = p0, acc = before;
+    for (int64_t j = js; j <= je; ++j) {
+      acc += p;
+      if (acc <= half) cand_lo = (int)j;
+      p *= (double)(m - j) / (double)(j + 1) * ratio;
+    }
+  }
+  if (js <= je) {
+    // backwards from je: the stretch's pmf values again, from its end
+    double pe = exp(lpmf(je) - lref), acc = after;
+    for (int64_t j = je; j >= js; --j) {
+      acc += pe;
+      if (acc <= half) cand_hi = (int)j;
+      pe *= (double)j / (double)(m - j + 1) / ratio;
+    }
+  }
+  cand_lo = wave_reduce(cand_lo, [](int x, int y) { return x > y ? x : y; });
+  cand_hi = wave_reduce(cand_hi, [](int x, int y) { return x < y ? x : y; });
+  if (lane == 0) {
+    wext[0][w] = cand_lo;
+    wext[1][w] = cand_hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t cl = -1, ch = m + 2;
+    for (int i = 0; i < NW; ++i) {
+      cl = max(cl, wext[0][i]);
+      ch = min(ch, wext[1][i]);
+    }
+    RowState &S = st[row];
+    S.blo = cl >= 0 ? cl + 1 : j0;
+    S.bhi = ch <= m ? ch : j1 + 1;
+    S.k = k;
+    S.t = t;
+    S.c = kLog2e / t;
+    S.cf = (float)S.c;
+    if (!good) S.flags |= LAPSUM_FLAG_INVALID;
+  }
+}
+
+hipError_t launch_bracket_rows(const double *k_rows, const double *t_rows, double k, double t, int64_t rows,
+                               int64_t n, int64_t m, double delta, RowState *st, hipStream_t s) {
+  hipLaunchKernelGGL(bracket_rows_kernel, rows_grid(1u, rows), dim3(kBrThreads), 0, s, k_rows, t_rows, k, t, rows, n,
+                     m, delta, st);
   return hipGetLastError();
 }
 
@@ -493,6 +618,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
   SelectLds &L = *reinterpret_cast<SelectLds *>(lds_raw);
   const int64_t row = grid_row();
   if (row >= rows) return;
+  if (lo < 0) {  // per-row indices
+    lo = st[row].blo;
+    hi = st[row].bhi;
+  }
   const float *X = samples + row * m;
   const bool want[2] = {lo >= 1, hi <= m};
   uint32_t R[2] = {(uint32_t)(lo - 1), (uint32_t)(hi - 1)};
@@ -667,6 +796,10 @@ __global__ __launch_bounds__(kSelThreads) void select_bucket_kernel(const float 
   __shared__ SelectBucketLds L;
   const int64_t row = grid_row();
   if (row >= rows) return;
+  if (lo < 0) {  // per-row indices
+    lo = st[row].blo;
+    hi = st[row].bhi;
+  }
   const float *X = samples + row * m;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   {
@@ -898,7 +1031,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
                                                                 const RowState *__restrict__ st,
                                                                 uint32_t *__restrict__ slots,
                                                                 FilterPartial *__restrict__ part, int gx, double t,
-                                                                int64_t rows) {
+                                                                int64_t rows, int per_row) {
   __shared__ double lds_d[2 * kStreamThreads / kWave];
   __shared__ unsigned long long lds_c[kStreamThreads / kWave];
   __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
@@ -909,7 +1042,7 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   if (threadIdx.x == 0) lcount = 0u;
   __syncthreads();
   const float aL = (float)S.a_lo, aR = (float)S.a_hi;
-  const float cf = (float)(kLog2e / t);
+  const float cf = per_row ? S.cf : (float)(kLog2e / t);
   const float *rr = r + row * n;
   uint32_t *slot = slots + ((int64_t)row * gx + blockIdx.x) * kBandSlot;
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
@@ -1029,9 +1162,9 @@ size_t band_slot_bytes(int64_t rows, int grid_x) {
 size_t band_offs_bytes(int64_t rows, int grid_x) { return sizeof(uint32_t) * (size_t)rows * (size_t)(grid_x + 1); }
 
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
-                         void *partials, int grid_x, hipStream_t s) {
+                         void *partials, int grid_x, bool per_row, hipStream_t s) {
   hipLaunchKernelGGL(filter_kernel, rows_grid((unsigned)grid_x, rows), dim3(kStreamThreads), 0, s, r, n, st, slots,
-                     reinterpret_cast<FilterPartial *>(partials), grid_x, t, rows);
+                     reinterpret_cast<FilterPartial *>(partials), grid_x, t, rows, per_row ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -797,6 +797,7 @@ struct RowState {
   double k, t, c;           // full-sort path: the row's budget, temperature, log2(e)/t
   float cf;                 //   (its own with per-row values, else the call's)
   int32_t pad1;
+  int64_t blo, bhi;         // bracketing with per-row budgets: the row's order-statistic indices
 };
 
 // Per-call reset of one row's state (bracket open unless forced).
@@ -817,6 +818,8 @@ LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_over
   z.k = z.t = z.c = 0.0;
   z.cf = 0.0f;
   z.pad1 = 0;
+  z.blo = 0;
+  z.bhi = 0;
   st[row] = z;
 }
 

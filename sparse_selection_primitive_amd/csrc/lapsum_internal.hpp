@@ -65,6 +65,7 @@ struct SegArgs {
   int64_t m;
   int nwiden;           // widening steps (0: none)
   int64_t wlo[kMaxWiden], whi[kMaxWiden];
+  int per_row;          // rows carry their own k, t, c, cf (in RowState): the fallback uses those
 };
 
 // Bucketed solve (bands too large for one workgroup, and whole rows of the
@@ -165,7 +166,12 @@ hipError_t launch_onchip_backward(const float *g, const float *p, int64_t rows, 
 bool onchip_backward_supported(int64_t n);
 hipError_t launch_sample(const float *r, int64_t rows, int64_t n, double t, int64_t m, uint64_t seed,
                          float *samples, uint16_t *starts, RowState *st, int32_t flags, uint32_t *tail, int Q,
-                         hipStream_t s);
+                         const double *t_rows, hipStream_t s);
+// Per-row bracket indices (and the rows' k, t, c, validity) into the row
+// state, after the sample kernel reset it; the selection then reads them
+// (lo < 0 asks for that).
+hipError_t launch_bracket_rows(const double *k_rows, const double *t_rows, double k, double t, int64_t rows,
+                               int64_t n, int64_t m, double delta, RowState *st, hipStream_t s);
 // Top-side selection of the bracket: the depth Q of the per-group top lists
 // (0: not applicable), their size, and the selection over them.
 int tail_depth(int64_t m, int64_t lo, int64_t hi);
@@ -176,7 +182,7 @@ size_t sample_start_bytes(int64_t rows, int64_t m);
 hipError_t launch_select(const float *samples, const uint16_t *starts, int64_t rows, int64_t m, int64_t lo,
                          int64_t hi, RowState *st, hipStream_t s);
 hipError_t launch_filter(const float *r, int64_t rows, int64_t n, double t, RowState *st, uint32_t *slots,
-                         void *partials, int grid_x, hipStream_t s);
+                         void *partials, int grid_x, bool per_row, hipStream_t s);
 int filter_grid_x(int64_t rows, int64_t n, int64_t cap);
 size_t filter_partial_bytes(int64_t rows, int grid_x);
 size_t band_slot_bytes(int64_t rows, int grid_x);

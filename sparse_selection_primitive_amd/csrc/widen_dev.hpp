@@ -199,8 +199,27 @@ LDEV bool widen_row(const SegArgs &a, int row, SegLds<NT> &L) {
 // first, then the exact whole-row fallback.  (Inlined: a call would make
 // every launch of the band kernels set up a stack, which costs more than
 // the spills this path adds outside the hit path.)
+// With per-row budgets the row's own k, t (as the per-row bracket kernel
+// stored them) replace the call's, there are no widened brackets (their
+// indices depend on k), and a row whose k or t was out of range gets NaN.
 template <int NT>
 LDEV void missed_row(const SegArgs &a, int row, SegLds<NT> &L) {
+  if (a.per_row) {
+    const RowState &S = a.st[row];
+    if (S.flags & LAPSUM_FLAG_INVALID) {
+      if (threadIdx.x == 0) a.st[row].b = __builtin_nan("");
+      __syncthreads();
+      return;
+    }
+    SegArgs r = a;
+    r.k = S.k;
+    r.t = S.t;
+    r.c = S.c;
+    r.cf = S.cf;
+    r.nwiden = 0;
+    fallback_row<NT>(r, row, L);
+    return;
+  }
   if (!widen_row<NT>(a, row, L)) fallback_row<NT>(a, row, L);
 }
 

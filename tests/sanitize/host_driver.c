@@ -102,15 +102,17 @@ static void rejected_arguments(void) {
     lapsum_options_init(&o);
     o.band_capacity = -1;
     EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_ERR_OPTION, "capacity -1");
-    /* per-row parameters rule out a forced bracketing path (the pointer is
-     * only compared with NULL on the host) */
+    /* per-row parameters: bracketing reports its indices as per row (the
+     * pointer is only compared with NULL on the host) */
     lapsum_options_init(&o);
     static const double fake_rows[1] = {1.0};
     o.k_rows = fake_rows;
     o.path = LAPSUM_PATH_BRACKET;
-    EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_ERR_PATH, "per-row bracket");
+    EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_OK && info.lo == -1 && info.hi == -1,
+           "per-row bracket");
     o.path = LAPSUM_PATH_AUTO;
-    EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_OK, "per-row auto");
+    EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_OK && info.path == LAPSUM_PATH_BRACKET,
+           "per-row auto");
 }
 
 static void bracket_index_grid(void) {

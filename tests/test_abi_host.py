@@ -141,15 +141,19 @@ def test_plan_rejects_bad_options(lib):
 
 def test_plan_per_row_parameters(lib):
     """Per-row k / t (device arrays, never read by the host): the scalars are
-    then not checked, AUTO takes the bucket path above the on-chip size
-    (the bracket's sample indices need k on the host), and a forced
-    bracketing path is refused."""
+    then not checked, AUTO picks the path by n as for scalar values, and the
+    bracketing plan reports its indices as per row (-1), sizes the band for
+    the widest bracket (that of k = n/2) and solves it with the bucketed
+    band solve (the one that reads each row's own k and t)."""
     dev = 4096  # a device address stand-in: planning never dereferences it
     assert L.plan(64, 256, 0.0, 0.0, k_rows_ptr=dev, t_rows_ptr=dev)["path"] == L.PATH_ONCHIP
-    assert L.plan(2, 3_317_760, 0.0, 1e-3, k_rows_ptr=dev)["path"] == L.PATH_BUCKET
-    assert L.plan(2, 3_317_760, 600, -1.0, t_rows_ptr=dev)["path"] == L.PATH_BUCKET
-    with pytest.raises(L.LapsumError, match="status 6"):
-        L.plan(2, 3_317_760, 600, 1e-3, path="bracket", k_rows_ptr=dev)
+    assert L.plan(6, 20000, 0.0, 1e-3, k_rows_ptr=dev)["path"] == L.PATH_BUCKET
+    pl = L.plan(2, 3_317_760, 0.0, 1e-3, k_rows_ptr=dev)
+    assert pl["path"] == L.PATH_BRACKET and pl["lo"] == -1 and pl["hi"] == -1 and pl["band_onchip"] == 0
+    widest = L.plan(2, 3_317_760, 0.5 * 3_317_760, 1e-3)
+    assert pl["band_capacity"] == widest["band_capacity"]
+    assert L.plan(2, 3_317_760, 600, -1.0, t_rows_ptr=dev)["path"] == L.PATH_BRACKET
+    assert L.plan(2, 300_000, 600, 1e-3, path="bracket", k_rows_ptr=dev)["path"] == L.PATH_BRACKET
     with pytest.raises(L.LapsumError, match="status 3"):  # the scalar k is still checked without k_rows
         L.plan(2, 20000, 0.0, 1e-3, t_rows_ptr=dev)
 

@@ -4,11 +4,14 @@ against the oracle solved row by row with that row's values.
 Operator: "Fast LapSum: Exact Differentiable Top-k at Million Scale",
 section 2.1 (eqs. (1)-(2), analytic VJP) -- the operator is defined per
 row, so per-row k and t change nothing but which values each row uses.
-Paths: on-chip (wave teams and one-workgroup rows) and bucket (AUTO takes
-it above 8192 scores when per-row values are given).  Tolerances:
-tests/parity.py.
+Paths: on-chip (wave teams and one-workgroup rows), bucket (AUTO above
+8192 scores up to 2^20) and bracketing (AUTO above 2^20, or forced), where
+every row's order-statistic indices come from its own k (section 2.2,
+probabilistic bracketing, step 1) and its sample is noised with its own t.
+Tolerances: tests/parity.py.
 """
 import ctypes
+import math
 
 import numpy as np
 import pytest
@@ -94,18 +97,80 @@ def test_per_row_bucket(L, O):
     _check_rows("per-row bucket", O, r, g, k, t, res)
 
 
+def _same_end(got, want):
+    return got == want if math.isinf(want) else abs(got - want) <= 2.5e-7 * abs(want) + 1e-30
+
+
+def _check_brackets(L, r, k, t, stats, seed=0, delta=1e-6):
+    """Each valid row's bracket ends against the oracle's own sample of that
+    row (noised with its t) and the binomial indices of its k."""
+    from oracle import bracket as ob
+    rows, n = r.shape
+    m = 1 << ob.default_sample_log2(n)
+    flags = stats["flags"].numpy()
+    for i in range(rows):
+        if flags[i] & L.FLAG_INVALID:
+            continue
+        want = ob.bracket(r[i], float(k[i]), float(t[i]), m, delta, seed, row=i)
+        got = (stats["a_lo"][i].item(), stats["a_hi"][i].item())
+        assert _same_end(got[0], want[0]) and _same_end(got[1], want[1]), (i, got, want[:2], want[2:])
+
+
 def test_per_row_large_rows(L, O):
-    """Two 2.5M-score rows with their own k and t: AUTO takes the bucket
-    path (bracketing needs k on the host), the streaming backward reads t per
-    row."""
+    """Two 2.5M-score rows with their own k and t: AUTO takes the
+    bracketing path, each row's bracket comes from its own k's indices and
+    its own t's noise and holds b; the streaming backward reads t per row."""
     g0 = np.random.Generator(np.random.PCG64(4301))
     r = g0.standard_normal((2, 2_500_000)).astype(np.float32)
     g = g0.standard_normal((2, 2_500_000)).astype(np.float32)
     k = np.array([1000.5, 123456.0])
     t = np.array([1e-3, 0.05])
+    plan = L.plan(2, 2_500_000, 0.0, 0.0, k_rows_ptr=4096, t_rows_ptr=4096)
+    assert plan["path"] == L.PATH_BRACKET and plan["lo"] == -1 and plan["band_onchip"] == 0
     log("[case] per-row large rows 2 x 2.5M")
-    res = _run(L, r, g, k, t)
+    res = _run(L, r, g, k, t, stats=True)
+    flags = res["stats"]["flags"].numpy()
+    log(f"  flags {flags}")
+    assert np.all(flags & L.FLAG_HIT) and not np.any(flags & (L.FLAG_FALLBACK | L.FLAG_INVALID)), flags
+    _check_brackets(L, r, k, t, res["stats"])
     _check_rows("per-row large", O, r, g, k, t, res)
+
+
+def test_per_row_bracket_forced_wide_budgets(L, O):
+    """Forced bracketing on shorter rows whose budgets run from near 0 to
+    near n (open lower or upper bracket ends) with temperatures over three
+    decades: brackets and results against the oracle, row by row."""
+    rows, n = 8, 300_000
+    r, g, _, _ = _case(4501, rows, n, 1.0, 2.0, 0.1, 0.2)
+    k = np.array([0.5, 3.0, 600.0, 0.25 * n, 0.5 * n + 0.5, n - 700.0, n - 2.0, n - 0.5])
+    t = np.exp(np.random.Generator(np.random.PCG64(4502)).uniform(np.log(1e-3), np.log(1.0), rows))
+    log(f"[case] per-row forced bracket rows={rows} n={n}")
+    res = _run(L, r, g, k, t, path="bracket", stats=True)
+    flags = res["stats"]["flags"].numpy()
+    log(f"  flags {flags}")
+    assert np.all(flags & L.FLAG_BRACKET) and not np.any(flags & L.FLAG_INVALID), flags
+    _check_brackets(L, r, k, t, res["stats"])
+    _check_rows("per-row forced bracket", O, r, g, k, t, res)
+
+
+def test_per_row_bracket_invalid_rows(L, O):
+    """Bracketing rows whose k or t is out of range get NaN outputs and the
+    INVALID flag; the other rows of the call are unaffected."""
+    rows, n = 4, 1_500_000
+    r, g, _, _ = _case(4601, rows, n, 1.0, 2.0, 0.1, 0.2)
+    k = np.array([800.0, 0.0, 5000.5, 900.0])
+    t = np.array([0.01, 0.01, 0.02, -1.0])
+    log("[case] per-row bracket invalid rows")
+    res = _run(L, r, g, k, t, stats=True)
+    flags = res["stats"]["flags"].numpy()
+    log(f"  flags {flags}")
+    for i in (1, 3):
+        assert flags[i] & L.FLAG_INVALID, (i, flags)
+        assert np.all(np.isnan(res["p"][i])) and np.isnan(res["b"][i]), i
+    for i in (0, 2):
+        assert not flags[i] & L.FLAG_INVALID and flags[i] & L.FLAG_HIT, (i, flags)
+    _check_brackets(L, r, k, t, res["stats"])
+    _check_rows("per-row bracket valid rows", O, r, None, k, t, res, rows_idx=[0, 2])
 
 
 @pytest.mark.parametrize("n", [256, 3000, 20000])
