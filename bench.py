@@ -464,6 +464,9 @@ def main():
         steps = args.steps if name.startswith("extreme") else max(args.steps, 100)
         res = bench_workload(L, hip, torch, name, WORKLOADS[name], steps, args.warmup,
                              live_dominant=(name == head_name))
+        # calibrated HBM bytes of the dominant kernel from the committed
+        # counter summary (null when none matches the current sources)
+        res["dominant"]["traffic"] = load_traffic(res["dominant"]["stage"], name)
         results[name] = res
         q = res["step_ms_quantiles"]
         print(f"# {name}: {res['fwd_bwd_elements_per_s']:.3e} el/s fwd+bwd, {res['ms_per_step']:.4f} ms/step "
