@@ -19,7 +19,9 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblapsum.so")
+# LAPSUM_LIBRARY selects another build of the library (the LDS-poisoning
+# debug copy); by default the in-tree liblapsum.so
+LIB_PATH = os.environ.get("LAPSUM_LIBRARY") or os.path.join(_HERE, "liblapsum.so")
 
 PATH_AUTO, PATH_ONCHIP, PATH_BUCKET, PATH_BRACKET, PATH_SORT, PATH_BISECT = 0, 1, 2, 3, 4, 5
 PATHS = {"auto": PATH_AUTO, "onchip": PATH_ONCHIP, "bucket": PATH_BUCKET, "bracket": PATH_BRACKET,

@@ -6,6 +6,9 @@ Every translation unit is compiled by hipcc for gfx950 only, with packed
 fp32 instructions disabled, then linked into one shared library next to this
 file.  Object files go to ``_build/`` (not tracked).
 
+``build_lds_poison()`` builds a debug copy whose kernels fill their LDS with
+0xFF bytes at entry (``liblapsum_ldspoison.so``, loaded only by its GPU test).
+
 ``build_host_sanitized(path)`` builds a second copy of the library for CPU
 checks of the host runtime: its host code instrumented with AddressSanitizer
 and UndefinedBehaviorSanitizer (the device code is built as usual, without
@@ -41,9 +44,9 @@ def _flags():
             "-I", os.path.join(HERE, "..", "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, objdir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
@@ -82,18 +85,29 @@ def build_host_sanitized(out: str, jobs: int | None = None) -> str:
     return out
 
 
-def build(jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, out: str = LIB, defines=()) -> str:
+    objdir = BUILD if not defines else os.path.join(BUILD, "_".join(d.lower() for d in defines))
+    os.makedirs(objdir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, objdir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+POISON_LIB = os.path.join(HERE, "liblapsum_ldspoison.so")
+
+
+def build_lds_poison(jobs: int | None = None) -> str:
+    """The debug copy of the library whose kernels set their LDS to 0xFF
+    bytes at entry (LAPSUM_LDS_POISON), for the GPU test that runs the
+    parity cases against it."""
+    return build(jobs, POISON_LIB, ("LAPSUM_LDS_POISON",))
 
 
 if __name__ == "__main__":

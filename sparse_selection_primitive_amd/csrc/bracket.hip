@@ -1036,6 +1036,10 @@ __global__ __launch_bounds__(kStreamThreads) void filter_kernel(const float *__r
   __shared__ unsigned long long lds_c[kStreamThreads / kWave];
   __shared__ uint32_t lds_k[2 * kStreamThreads / kWave];
   __shared__ uint32_t lcount;
+  lds_poison(lds_d);
+  lds_poison(lds_c);
+  lds_poison(lds_k);
+  lds_poison(lcount);
   const int64_t row = grid_row();
   if (row >= rows) return;
   const RowState &S = st[row];

@@ -38,6 +38,11 @@ LDEV FilterTotals filter_totals(const FilterPartial *__restrict__ vp, int gx, in
   __shared__ uint32_t lds_k[3 * NW];
   __shared__ uint32_t wsum[NW];
   __shared__ FilterTotals tot;
+  lds_poison(lds_d);
+  lds_poison(lds_c);
+  lds_poison(lds_k);
+  lds_poison(wsum);
+  lds_poison(tot);
   // a contiguous chunk of partials per thread, so the offsets come out in
   // order; loaded four at a time at clamped indices (no load waits for the
   // previous one), the counts kept for the offsets

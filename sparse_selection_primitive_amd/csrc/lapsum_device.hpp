@@ -50,6 +50,24 @@ LDEV bool row_params(const double *krow, const double *trow, int64_t row, int64_
   return ok;
 }
 
+// ------------------------------------------------------ LDS poisoning
+// Debug build (compiled with LAPSUM_LDS_POISON): every byte of an LDS object
+// is set to 0xFF at kernel entry (NaN as fp32 and fp64, all ones as an
+// integer), so a read of LDS that no thread of the launch wrote first shows
+// up as NaN or a wrong count in the outputs.  Every thread of the workgroup
+// must call it.  In the product build it compiles to nothing.
+template <class T>
+LDEV void lds_poison(T &obj) {
+#ifdef LAPSUM_LDS_POISON
+  static_assert(sizeof(T) % 4 == 0, "LDS objects are poisoned a word at a time");
+  uint32_t *q = reinterpret_cast<uint32_t *>(&obj);
+  for (uint32_t i = threadIdx.x; i < (uint32_t)(sizeof(T) / 4); i += blockDim.x) q[i] = 0xFFFFFFFFu;
+  __syncthreads();
+#else
+  (void)obj;
+#endif
+}
+
 // ------------------------------------------------------------------ keys
 // Order-preserving map of fp32 onto uint32: the unsigned order of keys is
 // the numeric order of finite values (-0.0 sorts just below +0.0).

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void o
     const float *__restrict__ r, int64_t rows, int n, double k, double t, RowParams rp, float *__restrict__ p,
     double *__restrict__ b, lapsum_row_stats *stats) {
   __shared__ float wbuf[4 * 256];  // candidate buffers of the certified window, 4*LANES per team
+  lds_poison(wbuf);
   onchip_forward_wave_body<NP, LANES, true, PR>(r, rows, n, k, t, rp, p, b, stats, wbuf);
 }
 
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(256) void onchip_forward_wave_ragged(const float *_
                                                                   float *__restrict__ p, double *__restrict__ b,
                                                                   lapsum_row_stats *stats) {
   __shared__ float wbuf[4 * 256];
+  lds_poison(wbuf);
   onchip_forward_wave_body<NP, LANES, false, PR>(r, rows, n, k, t, rp, p, b, stats, wbuf);
 }
 
@@ -411,6 +413,7 @@ __global__ __launch_bounds__(NP / 16) void onchip_forward_block(const float *__r
                                                                 lapsum_row_stats *stats) {
   constexpr int E = 16, LANES = NP / 16;
   __shared__ BlockTeamLds<LANES, E> lds;
+  lds_poison(lds);
   BlockTeam<LANES, E> team(&lds);
   const int64_t row = grid_row();
   if (row >= rows) return;
@@ -644,6 +647,9 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   __shared__ BandLds lds;
   __shared__ uint32_t soffs[kMaxFilterBlocks + 1];
   __shared__ int fall;
+  lds_poison(lds);
+  lds_poison(soffs);
+  lds_poison(fall);
   const int64_t row = grid_row();
   if (row >= rows) return;
   RowState &S = st[row];
