@@ -397,6 +397,8 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   const BandRegions &R = P.bnd;
   BandArgs a;
   a.rp = rp;
+  a.nested = 0;  // the launcher decides
+  a.src2 = nullptr;
   a.rows = (int)rows;
   a.gx = P.fgx;
   a.group = R.group;

@@ -46,7 +46,12 @@ constexpr int kBPT = kBandBuckets / kBT;   // buckets per thread in the per-row 
 constexpr int kWaveBucket = 16 * kWave;    // largest balancing bucket one wave sorts
 static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of the workgroup size");
 
-LDEV bool band_active(const RowState &S) { return !(S.flags & LAPSUM_FLAG_OVERFLOW); }
+// A row takes part in a launch unless its band overflowed (it then takes
+// the fallback); on the second level of whole rows, only if its balancing
+// bucket was crowded.
+LDEV bool band_active(const BandArgs &a, const RowState &S) {
+  return a.src2 != nullptr ? (S.flags & kFlagNested) != 0 : !(S.flags & LAPSUM_FLAG_OVERFLOW);
+}
 
 // Budget, temperature and c = log2(e)/t of one row: the call's, or (with
 // per-row values, full-row mode) the row's own as the per-call reset stored
@@ -93,10 +98,38 @@ LDEV void load_slot_bounds(const BandArgs &a, int64_t row, int blk, uint32_t *sb
   const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
   for (int i = threadIdx.x; i <= ns; i += kBT) sb[i] = ro[s0 + i];
 }
+// Keys of second-level workgroup `blk`: an equal share of the crowded
+// bucket (S.band keys from S.set0 in the first level's keys), kRowLoads
+// loads per thread in flight (the bucket may start anywhere, so no vectors).
+template <class F>
+LDEV void for_each_set_key(const BandArgs &a, int64_t row, int blk, F &&f) {
+  constexpr int kRowLoads = 8;
+  const RowState &S = a.st[row];
+  const int64_t len = (int64_t)S.band;
+  const int64_t chunk = (len + a.nblk - 1) / a.nblk;
+  const int64_t c0 = (int64_t)blk * chunk, c1 = min(len, c0 + chunk);
+  const uint32_t *src = a.src2 + row * a.cap + S.set0;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += (int64_t)kBT * kRowLoads) {
+    uint32_t v[kRowLoads];
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u) {
+      const int64_t ii = i + (int64_t)u * kBT;
+      v[u] = ii < c1 ? src[ii] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u)
+      if (i + (int64_t)u * kBT < c1) f(v[u]);
+  }
+}
+
 // Scores of full-row workgroup `blk`: its chunk, 16 bytes per thread and
 // step on the vector path.
 template <class F>
 LDEV void for_each_row_key(const BandArgs &a, int64_t row, int blk, F &&f) {
+  if (a.src2 != nullptr) {
+    for_each_set_key(a, row, blk, f);
+    return;
+  }
   typedef float f4 __attribute__((ext_vector_type(4)));
   const float *rr = a.r + row * a.n;
   const int64_t c0 = (int64_t)blk * a.chunk, c1 = min(a.n, c0 + a.chunk);
@@ -206,6 +239,7 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   if (row >= a.rows) return;
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
+  if (a.src2 != nullptr && !band_active(a, S)) return;
   const int nb = 1 << a.bbits;
   for (int j = threadIdx.x; j < nb; j += kBT) {
     h[j] = 0u;
@@ -214,7 +248,13 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   }
   RowState R;  // the key range and count this workgroup buckets by
   const uint32_t *sb = soffs;
-  if (a.r != nullptr) {
+  if (a.src2 != nullptr) {
+    // second level: the crowded bucket's extremes and size, recorded by the
+    // first level's locate
+    R.kmin = S.kmin;
+    R.kmax = S.kmax;
+    R.band = S.band;
+  } else if (a.r != nullptr) {
     // full-row mode: the row's key range from the min/max partials; the
     // first workgroup records it (and the key count) for the later kernels
     if (threadIdx.x < kWave) {
@@ -297,7 +337,7 @@ __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   uint32_t v[kBandCountBlocks];
 #pragma unroll
   for (int b = 0; b < kBandCountBlocks; ++b) v[b] = b < a.nblk ? h[(int64_t)b * kBandBuckets] : 0u;
-  if (!band_active(a.st[row])) return;
+  if (!band_active(a, a.st[row])) return;
   uint32_t run = 0u;
   for (int b0 = 0; b0 < a.nblk; b0 += kBandCountBlocks) {
     if (b0 > 0) {
@@ -360,7 +400,7 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
     hv[u] = j < nb ? hin[j] : 0u;
   }
   if (a.r == nullptr) load_slot_bounds(a, row, blk, sb);
-  if (!band_active(S)) return;
+  if (!band_active(a, S)) return;
   const uint32_t kmin = S.kmin;
   const int shift = band_shift(S, a.bbits);
   uint32_t sum = 0u;
@@ -477,7 +517,7 @@ __global__ __launch_bounds__(kBT) void band_agg_buckets_kernel(BandArgs a) {
   const int j = blk * kAggGroup + q;
   const int cnt = (int)a.btot[o + j];
   const uint32_t bst = a.bstart[o + j];
-  if (!band_active(S)) return;
+  if (!band_active(a, S)) return;
   const int shift = band_shift(S, a.bbits);
   const uint32_t *kb = a.keys + row * a.cap + bst;
   TileAgg *out = a.bagg + o + j;
@@ -527,8 +567,8 @@ __global__ __launch_bounds__(kBT) void band_agg_keys_kernel(BandArgs a) {
   const int64_t row = grid_row();
   if (row >= a.rows) return;
   const RowState &S = a.st[row];
-  if (!band_active(S)) return;
-  const int64_t M = a.n;
+  if (!band_active(a, S)) return;
+  const int64_t M = a.src2 != nullptr ? (int64_t)S.band : a.n;
   const int64_t c0 = (int64_t)blockIdx.x * kAggChunk;
   if (c0 >= M) return;
   const int64_t c1 = min(M, c0 + (int64_t)kAggChunk);
@@ -628,6 +668,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   const int64_t row = xcd_linear();
   if (row >= a.rows) return;
   RowState &S = a.st[row];
+  if (a.src2 != nullptr && !band_active(a, S)) return;  // second level: rows without a crowded bucket
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
   // The bucket search runs on the first kLocScanW waves only (two per SIMD):
@@ -658,7 +699,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
                          : TileAgg{0.0f, 0.0f, 0.0, 0.0};
     }
   }
-  const bool active = band_active(S);
+  const bool active = band_active(a, S);
   if (threadIdx.x == 0) sel_fb = active ? 0 : 1;  // overflow: the row is already flagged for the fallback
   if (active) {
     double rk, rt, c;
@@ -697,6 +738,26 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
           part.last, a.tagg + row * a.max_tiles, a.tpre + row * a.max_tiles, a.tsuf + row * a.max_tiles, rk, rt,
           c, rcf, L.fb);
       if (threadIdx.x == 0) sel_b = bb;
+    } else if (FULL && a.nested) {
+      // a crowded bucket of a whole row, left to the second bucket level:
+      // its place, size and exact key extremes, and everything around it
+      // (the first level has no seeds, so the keys below it are sJ of the
+      // row's scores) into the row state
+      __syncthreads();  // every thread has read the state the search used
+      if (threadIdx.x == 0) {
+        S.set0 = sJ;
+        S.band = (unsigned long long)cJ;
+        S.kmin = a.bkey[2 * (o + J)];
+        S.kmax = a.bkey[2 * (o + J) + 1];
+        S.a_lo = (double)slo.a;
+        S.tail_lo = slo.s;
+        S.count_lo = (unsigned long long)sJ;
+        S.a_hi = (double)shi.a;
+        S.tail_hi = shi.s;
+        S.count_hi = (unsigned long long)cR_eff;
+        S.flags |= kFlagNested;
+      }
+      return;
     } else {
       // a crowded bucket (the key bits of a whole row spread values over
       // binades, so one bucket can hold millions of keys): the nested bucket
@@ -727,6 +788,15 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
     if (threadIdx.x == 0) {
       const double bb = (S.flags & LAPSUM_FLAG_INVALID) ? __builtin_nan("") : sel_b;
       S.b = bb;
+      if (FULL && a.src2 != nullptr) {
+        // second level done: the row state describes the whole row again
+        S.a_lo = -INFINITY;
+        S.a_hi = INFINITY;
+        S.tail_lo = S.tail_hi = 0.0;
+        S.count_lo = S.count_hi = 0ull;
+        S.band = (unsigned long long)a.n;
+        S.flags &= ~kFlagNested;
+      }
       if (!FULL) {  // certification against the bracket
         const bool hit = (bb >= S.a_lo) && (bb < S.a_hi);
         S.flags |= hit ? LAPSUM_FLAG_HIT : LAPSUM_FLAG_FALLBACK;
@@ -774,16 +844,26 @@ int full_count_blocks(int64_t n, int64_t *chunk) {
   return (int)((n + c - 1) / c);
 }
 
-hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t s) {
+// Whole rows of at least this many scores take the second bucket level: a
+// crowded balancing bucket (more than kFallbackSort keys) is bucketed again
+// by every count/scatter workgroup instead of one.  Its launches cost a few
+// microseconds when no row needs them; shorter rows rarely crowd a bucket,
+// and there one workgroup selects inside it.
+constexpr int64_t kNestedMinN = (int64_t)1 << 22;
+
+hipError_t launch_band_buckets(const BandArgs &a_in, const SegArgs &fb, hipStream_t s) {
+  BandArgs a = a_in;
+  a.src2 = nullptr;
+  a.nested = a.r != nullptr && a.n >= kNestedMinN ? 1 : 0;
   const dim3 blk = rows_grid((unsigned)a.nblk, a.rows);
   if (a.r != nullptr) hipLaunchKernelGGL(band_minmax_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
   const int nb = 1 << a.bbits;
   hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
+  const dim3 agg_keys = rows_grid((unsigned)((a.n + kAggChunk - 1) / kAggChunk), a.rows);
   if (a.r != nullptr)
-    hipLaunchKernelGGL(band_agg_keys_kernel, rows_grid((unsigned)((a.n + kAggChunk - 1) / kAggChunk), a.rows),
-                       dim3(kBT), 0, s, a);
+    hipLaunchKernelGGL(band_agg_keys_kernel, agg_keys, dim3(kBT), 0, s, a);
   else
     hipLaunchKernelGGL(band_agg_buckets_kernel, rows_grid((unsigned)((nb + kAggGroup - 1) / kAggGroup), a.rows),
                        dim3(kBT), 0, s, a);
@@ -791,6 +871,23 @@ hipError_t launch_band_buckets(const BandArgs &a, const SegArgs &fb, hipStream_t
     hipLaunchKernelGGL(band_locate_kernel<true>, rows_grid(1u, a.rows), dim3(1024), 0, s, a, fb);
   else
     hipLaunchKernelGGL(band_locate_kernel<false>, rows_grid(1u, a.rows), dim3(512), 0, s, a, fb);
+  if (a.nested) {
+    // second level over the crowded buckets the locate recorded: the first
+    // level's bucketed keys are the input, its scratch the output, and the
+    // bucket records are reused (rows without a crowded bucket return at once)
+    BandArgs a2 = a;
+    a2.nested = 0;
+    a2.src2 = a.keys;
+    a2.keys = a.tmp;
+    a2.tmp = a.keys;
+    a2.bbits = kBandBucketBits;
+    const int nb2 = 1 << a2.bbits;
+    hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a2);
+    hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb2 + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a2);
+    hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a2);
+    hipLaunchKernelGGL(band_agg_keys_kernel, agg_keys, dim3(kBT), 0, s, a2);
+    hipLaunchKernelGGL(band_locate_kernel<true>, rows_grid(1u, a.rows), dim3(1024), 0, s, a2, fb);
+  }
   return hipGetLastError();
 }
 

@@ -816,7 +816,14 @@ struct RowState {
   float cf;                 //   (its own with per-row values, else the call's)
   int32_t pad1;
   int64_t blo, bhi;         // bracketing with per-row budgets: the row's order-statistic indices
+  int64_t set0;             // whole rows, second bucket level: start of the crowded bucket in the first
+                            // level's keys (its size in band, its key extremes in kmin / kmax, everything
+                            // below / above it in a_lo, tail_lo, count_lo / a_hi, tail_hi, count_hi)
 };
+
+// Row state flag (never reported): the row's crowded balancing bucket waits
+// for the second bucket level.
+constexpr int32_t kFlagNested = 1 << 16;
 
 // Per-call reset of one row's state (bracket open unless forced).
 LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_override, double o_lo, double o_hi) {
@@ -838,6 +845,7 @@ LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_over
   z.pad1 = 0;
   z.blo = 0;
   z.bhi = 0;
+  z.set0 = 0;
   st[row] = z;
 }
 

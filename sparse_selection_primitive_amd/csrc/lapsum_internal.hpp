@@ -114,6 +114,10 @@ struct BandArgs {
   double k, t, c;
   float cf;
   RowParams rp;         // per-row k and t (full-row mode), overriding k, t, c, cf
+  int nested;           // full-row mode: a crowded balancing bucket is recorded in the row state and left
+                        // to a second, multi-workgroup bucket level (else one workgroup selects inside it)
+  const uint32_t *src2; // second level (non-null): the first level's bucketed keys [rows][cap]; each flagged
+                        // row's set is its crowded bucket, keys / tmp are this level's buffers
 };
 
 // Whole-row radix sort and the solve over the sorted rows (sort.hip): pass

@@ -214,6 +214,91 @@ def test_bucket_crowded_bucket(L, O):
         assert np.array_equal(res[key], again[key]), key
 
 
+def _float_keys(r):
+    """The order-preserving 32-bit keys of fp32 scores (sign bit flipped for
+    positives, all bits for negatives)."""
+    b = np.ascontiguousarray(r, dtype=np.float32).view(np.uint32)
+    return np.where(b & 0x80000000, ~b, b | 0x80000000).astype(np.uint32)
+
+
+def _root_bucket_size(r, b):
+    """Scores of a whole row that share the threshold's bucket when the row
+    is spread over 2048 buckets by its key bits above the smallest key."""
+    kk = _float_keys(r).astype(np.int64)
+    lo = int(kk.min())
+    shift = max(int(kk.max() - lo).bit_length() - 11, 0)
+    b = float(np.asarray(b, dtype=np.float64).ravel()[0])
+    jb = (int(_float_keys(np.array([b], dtype=np.float32))[0]) - lo) >> shift
+    return int(np.sum((kk - lo) >> shift == jb))
+
+
+def _second_level_rows():
+    """Rows of 5M scores whose balancing bucket holds far more keys than one
+    workgroup sorts: a normal row with the root near 1.06; a uniform row on
+    [1, 2) with two outliers that stretch the key range over every binade
+    (a quarter of the row in one bucket); the same on a grid of 1000 values
+    (runs of ~5000 equal scores inside the bucket)."""
+    g0 = np.random.Generator(np.random.PCG64(3671))
+    n = 5_000_000
+    normal = g0.standard_normal(n).astype(np.float32)
+    uni = g0.uniform(1.0, 2.0, n).astype(np.float32)
+    uni[[17, n - 5]] = [1e-30, -1e30]
+    grid = (np.floor(g0.uniform(1.0, 2.0, n) * 1000.0) / 1000.0).astype(np.float32)
+    grid[[3, n // 2]] = [1e-30, -1e30]
+    return [("normal, root near 1.06", normal, float(np.sum(normal > 1.06)) + 0.5, 0.01),
+            ("uniform with outliers", uni, 0.5 * n + 0.25, 1e-3),
+            ("grid of 1000 values", grid, 0.5 * n + 0.5, 1e-4)], g0
+
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_bucket_second_level(L, O, case):
+    """Whole rows of 4M+ scores take the second, multi-workgroup bucket level
+    when their balancing bucket is crowded: the first level's locate records
+    the bucket and everything around it, every count/scatter workgroup
+    buckets it again, and the second locate solves inside the new balancing
+    bucket.  Against the oracle, bitwise repeatable, and the row's stats
+    describe the whole row again afterwards."""
+    rows, g0 = _second_level_rows()
+    name, r, k, t = rows[case]
+    r = r[None, :]
+    g = g0.standard_normal(r.shape).astype(np.float32)
+    res, p_or, b_or = full_check(f"bucket second level: {name}", L, O, r, g, k, t, path="bucket", stats=True)
+    crowd = _root_bucket_size(r[0], b_or[0])
+    log(f"  first-level balancing bucket ~{crowd} keys")
+    assert crowd > 65536, crowd
+    st = res["stats"]
+    assert st["flags"][0].item() == 0 and st["band"][0].item() == r.shape[1], st
+    assert st["a_lo"][0].item() == -math.inf and st["a_hi"][0].item() == math.inf, st
+    again = run(L, r, k, t, g, path="bucket")
+    for key in ("p", "b", "dr", "dk"):
+        assert np.array_equal(res[key], again[key]), key
+
+
+def test_bucket_second_level_mixed_rows(L, O):
+    """A batch where only some rows crowd their balancing bucket: the
+    second-level launches must leave the other rows' results alone (the
+    batch's per-row results equal the single-row calls bitwise)."""
+    g0 = np.random.Generator(np.random.PCG64(3677))
+    n = 4_200_000
+    r = g0.standard_normal((3, n)).astype(np.float32)
+    r[1] = np.abs(r[1])  # root deep in the upper tail: a sparse bucket
+    k, t = 40.5, 0.02
+    ks = [float(np.sum(r[0] > 1.06)) + 0.5, k, float(np.sum(r[2] > -0.3)) + 0.5]
+    log(f"[case] bucket second level, mixed batch 3 x {n}, per-row k {ks}")
+    rt = gpu(r)
+    kt = torch.tensor(ks, dtype=torch.float64, device="cuda")
+    p, b = L.lapsum_forward(rt, kt, t, path="bucket")[:2]
+    torch.cuda.synchronize()
+    p, b = p.cpu().numpy(), b.cpu().numpy()
+    for i in range(3):
+        p_or, b_or = O.forward(r[i], ks[i], t)
+        check_forward(f"mixed batch row {i}", ks[i], t, p[i], b[i], p_or, b_or)
+        check_budget(f"mixed batch row {i}", ks[i], p[i][None, :])
+        one = run(L, r[i:i + 1], ks[i], t, path="bucket")
+        assert np.array_equal(one["p"][0], p[i]) and one["b"][0] == b[i], i
+        log(f"  row {i}: balancing bucket ~{_root_bucket_size(r[i], b_or)} keys")
+
+
 @pytest.mark.parametrize("k", [1e-3, 0.5, 9999.5])
 def test_bucket_end_budgets(L, O, k):
     """Budgets near 0 and near n: the balancing bucket is the first or the
