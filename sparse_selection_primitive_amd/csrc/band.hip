@@ -16,8 +16,10 @@
 //   band_minmax_kernel   (full-row mode) key range of each workgroup's chunk
 //   band_count_kernel    bucket counts and key extremes of each workgroup's
 //                        filter slots or chunk
-//   band_scan_kernel     per bucket, offsets of the workgroups inside it,
-//                        its size and key extremes
+//   band_scan_kernel     per bucket, offsets of the workgroups inside it
+//                        and its size (band mode; band_scan_full_kernel for
+//                        whole rows, with many more workgroups, also the
+//                        bucket's key extremes)
 //   band_scatter_kernel  keys to their bucket (order inside a bucket free)
 //   band_agg_*_kernel    anchored sums of every bucket, order-free: by
 //                        buckets (band mode) or by key ranges (full-row
@@ -28,6 +30,12 @@
 //                        selection when crowded) and the root inside it,
 //                        certification, and the widening or exact fallback
 //                        of a row whose bracket missed
+//
+// Whole rows of at least kNestedMinN scores bucket a crowded balancing
+// bucket (the key bits of a row spread over binades can put millions of
+// scores in one) a second time with the same kernels, every workgroup
+// taking part: the first locate records the bucket and everything around
+// it in the row state, and the second level reads that bucket's keys.
 //
 // Every count is an integer, the bucket sums are fixed-point integer sums,
 // and the balancing bucket is sorted before anything is summed over it in
@@ -51,6 +59,16 @@ static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of th
 // bucket was crowded.
 LDEV bool band_active(const BandArgs &a, const RowState &S) {
   return a.src2 != nullptr ? (S.flags & kFlagNested) != 0 : !(S.flags & LAPSUM_FLAG_OVERFLOW);
+}
+
+// Count/scatter workgroups that take part for a row: all of them, or on the
+// second level one per kSetChunk keys of the crowded bucket (the others
+// return at once; the scan reads only the records of those that took part).
+constexpr int64_t kSetChunk = 8192;
+LDEV int row_blocks(const BandArgs &a, const RowState &S) {
+  if (a.src2 == nullptr) return a.nblk;
+  const int64_t want = ((int64_t)S.band + kSetChunk - 1) / kSetChunk;
+  return (int)min(max(want, (int64_t)1), (int64_t)a.nblk);
 }
 
 // Budget, temperature and c = log2(e)/t of one row: the call's, or (with
@@ -98,15 +116,17 @@ LDEV void load_slot_bounds(const BandArgs &a, int64_t row, int blk, uint32_t *sb
   const int s0 = blk * a.group, ns = min(a.gx - s0, a.group);
   for (int i = threadIdx.x; i <= ns; i += kBT) sb[i] = ro[s0 + i];
 }
-// Keys of second-level workgroup `blk`: an equal share of the crowded
-// bucket (S.band keys from S.set0 in the first level's keys), kRowLoads
-// loads per thread in flight (the bucket may start anywhere, so no vectors).
+// Keys of second-level workgroup `blk` (< row_blocks): an equal share of
+// the crowded bucket (S.band keys from S.set0 in the first level's keys),
+// kRowLoads loads per thread in flight (the bucket may start anywhere, so
+// no vectors).
 template <class F>
 LDEV void for_each_set_key(const BandArgs &a, int64_t row, int blk, F &&f) {
   constexpr int kRowLoads = 8;
   const RowState &S = a.st[row];
   const int64_t len = (int64_t)S.band;
-  const int64_t chunk = (len + a.nblk - 1) / a.nblk;
+  const int nbr = row_blocks(a, S);
+  const int64_t chunk = (len + nbr - 1) / nbr;
   const int64_t c0 = (int64_t)blk * chunk, c1 = min(len, c0 + chunk);
   const uint32_t *src = a.src2 + row * a.cap + S.set0;
   for (int64_t i = c0 + threadIdx.x; i < c1; i += (int64_t)kBT * kRowLoads) {
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   if (row >= a.rows) return;
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
-  if (a.src2 != nullptr && !band_active(a, S)) return;
+  if (a.src2 != nullptr && (!band_active(a, S) || blk >= row_blocks(a, S))) return;
   const int nb = 1 << a.bbits;
   for (int j = threadIdx.x; j < nb; j += kBT) {
     h[j] = 0u;
@@ -323,10 +343,12 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   }
 }
 
-// one thread per bucket: exclusive scan over the count workgroups, in
-// place, kBandCountBlocks counts at a time (each batch loaded before any of
-// it is used); the bucket's key extremes over the workgroups; and its
-// fixed-point sums cleared for the scatter to add into
+// One thread per bucket (band mode, and whole rows of at most
+// kBandCountBlocks count workgroups): exclusive scan over the count
+// workgroups, in place, kBandCountBlocks counts at a time (each batch loaded
+// before any of it is used); for whole rows the bucket's key extremes over
+// the workgroups and its fixed-point sums cleared for the aggregate kernel
+// to add into
 __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   const int64_t row = grid_row();
   if (row >= a.rows) return;
@@ -378,15 +400,104 @@ __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   a.bsum[2 * o + 1] = 0ull;
 }
 
+// Whole rows of more count workgroups (up to kFullCountBlocksMax), and the
+// second level (its row_blocks vary by row): a workgroup per kWave
+// consecutive buckets, lane = bucket, so every load is one
+// coalesced row of the per-workgroup records; each of its waves takes a
+// contiguous share of the count workgroups.  Pass 1 adds each lane's share
+// and its key extremes (an empty share holds ~0 and 0), the shares are
+// combined across the waves through LDS, pass 2 rewrites the counts as
+// exclusive offsets; the bucket's size, key extremes and cleared
+// fixed-point sums (for the aggregate kernel to add into) follow.
+constexpr int kScanT = 1024;
+constexpr int kScanW = kScanT / kWave;
+constexpr int kScanBatch = 16;  // count workgroups per batch of loads in pass 1 (3 loads each)
+constexpr int kOffBatch = 32;   // and in pass 2
+
+__global__ __launch_bounds__(kScanT) void band_scan_full_kernel(BandArgs a) {
+  __shared__ uint32_t wt[kScanW][kWave], wmn[kScanW][kWave], wmx[kScanW][kWave];
+  const int64_t row = grid_row();
+  if (row >= a.rows) return;
+  const RowState &S = a.st[row];
+  if (!band_active(a, S)) return;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int j = blockIdx.x * kWave + lane;
+  const bool jin = j < (1 << a.bbits);
+  const int nbr = row_blocks(a, S);
+  const int per = (nbr + kScanW - 1) / kScanW;
+  const int b0 = min(w * per, nbr), b1 = min(nbr, b0 + per);
+  uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
+  const uint32_t *ext = a.hext + row * a.nblk * (int64_t)(2 * kBandBuckets) + j;
+  uint32_t sum = 0u, mn = 0xFFFFFFFFu, mx = 0u;
+  for (int c = b0; c < b1; c += kScanBatch) {
+    uint32_t v[kScanBatch], lo[kScanBatch], hi[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const bool in = jin && c + u < b1;
+      const int64_t q = (int64_t)(c + u);
+      v[u] = in ? h[q * kBandBuckets] : 0u;
+      lo[u] = in ? ext[q * (2 * kBandBuckets)] : 0xFFFFFFFFu;
+      hi[u] = in ? ext[q * (2 * kBandBuckets) + kBandBuckets] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      sum += v[u];
+      mn = min(mn, lo[u]);
+      mx = max(mx, hi[u]);
+    }
+  }
+  wt[w][lane] = sum;
+  wmn[w][lane] = mn;
+  wmx[w][lane] = mx;
+  __syncthreads();
+  uint32_t run = 0u, tot = 0u;
+  for (int i = 0; i < kScanW; ++i) {
+    const uint32_t x = wt[i][lane];
+    run += i < w ? x : 0u;
+    tot += x;
+  }
+  for (int c = b0; c < b1; c += kOffBatch) {
+    uint32_t v[kOffBatch];
+#pragma unroll
+    for (int u = 0; u < kOffBatch; ++u) v[u] = jin && c + u < b1 ? h[(int64_t)(c + u) * kBandBuckets] : 0u;
+#pragma unroll
+    for (int u = 0; u < kOffBatch; ++u) {
+      if (jin && c + u < b1) h[(int64_t)(c + u) * kBandBuckets] = run;
+      run += v[u];
+    }
+  }
+  if (w == 0 && jin) {
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int i = 0; i < kScanW; ++i) {
+      kmn = min(kmn, wmn[i][lane]);
+      kmx = max(kmx, wmx[i][lane]);
+    }
+    const int64_t o = row * kBandBuckets + j;
+    a.btot[o] = tot;
+    a.bkey[2 * o] = kmn;
+    a.bkey[2 * o + 1] = kmx;
+    a.bsum[2 * o] = 0ull;
+    a.bsum[2 * o + 1] = 0ull;
+  }
+}
+
 __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   __shared__ uint32_t base[kBandBuckets];
   __shared__ uint32_t wsum[kBT / kWave];
   __shared__ uint32_t sb[kMaxGroup + 1];
   int64_t row;
   int blk;
-  xcd_tile(row, blk);
+  if (a.src2 != nullptr) {
+    // second level: only the first row_blocks workgroups of a row take
+    // part, so they keep the launch order (spread over every XCD)
+    row = grid_row();
+    blk = blockIdx.x;
+  } else {
+    xcd_tile(row, blk);
+  }
   if (row >= a.rows) return;
   const RowState &S = a.st[row];
+  if (a.src2 != nullptr && (!band_active(a, S) || blk >= row_blocks(a, S))) return;
   // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
   // inside each bucket and its slot bounds, all loaded before any is used
   const int64_t o = row * kBandBuckets;
@@ -859,7 +970,11 @@ hipError_t launch_band_buckets(const BandArgs &a_in, const SegArgs &fb, hipStrea
   if (a.r != nullptr) hipLaunchKernelGGL(band_minmax_kernel, blk, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a);
   const int nb = 1 << a.bbits;
-  hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a);
+  if (a.nblk > kBandCountBlocks)
+    hipLaunchKernelGGL(band_scan_full_kernel, rows_grid((unsigned)((nb + kWave - 1) / kWave), a.rows), dim3(kScanT),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a);
   const dim3 agg_keys = rows_grid((unsigned)((a.n + kAggChunk - 1) / kAggChunk), a.rows);
   if (a.r != nullptr)
@@ -883,7 +998,8 @@ hipError_t launch_band_buckets(const BandArgs &a_in, const SegArgs &fb, hipStrea
     a2.bbits = kBandBucketBits;
     const int nb2 = 1 << a2.bbits;
     hipLaunchKernelGGL(band_count_kernel, blk, dim3(kBT), 0, s, a2);
-    hipLaunchKernelGGL(band_scan_kernel, rows_grid((unsigned)((nb2 + kBT - 1) / kBT), a.rows), dim3(kBT), 0, s, a2);
+    hipLaunchKernelGGL(band_scan_full_kernel, rows_grid((unsigned)((nb2 + kWave - 1) / kWave), a.rows),
+                       dim3(kScanT), 0, s, a2);
     hipLaunchKernelGGL(band_scatter_kernel, blk, dim3(kBT), 0, s, a2);
     hipLaunchKernelGGL(band_agg_keys_kernel, agg_keys, dim3(kBT), 0, s, a2);
     hipLaunchKernelGGL(band_locate_kernel<true>, rows_grid(1u, a.rows), dim3(1024), 0, s, a2, fb);
