@@ -350,6 +350,36 @@ def hit_rate(L, torch, gen, trials):
             "mean_band": sum(bands) / len(bands)}
 
 
+def miss_cost(L, torch, gen):
+    """Forward times (ms, CUDA events, median) on the workload's rows: a
+    bracket that holds, with and without the spread fallback (what the
+    option costs when nothing misses), and a bracket forced to miss (below
+    every score's b), solved by one workgroup's whole-row fallback or by the
+    spread whole-row bucket solve."""
+    import numpy as np
+    w = workload(gen)
+    r = torch.from_numpy(w.r).cuda()
+    lo = float(np.min(w.r)) - 2.0
+    cases = {"hit": (dict(path="bracket"), 5), "hit_spread": (dict(path="bracket", spread_fallback=True), 5),
+             "miss_spread": (dict(path="bracket", bracket_override=(lo - 1.0, lo), spread_fallback=True), 3),
+             "miss_one_workgroup": (dict(path="bracket", bracket_override=(lo - 1.0, lo)), 1)}
+    out = {}
+    for name, (opts, reps) in cases.items():
+        L.lapsum_forward(r, w.k, w.t, **opts)  # warm-up
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            L.lapsum_forward(r, w.k, w.t, **opts)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out[name + "_ms"] = float(np.median(times))
+    out["note"] = ("forward only, one call per timing (workspace from the caching allocator); the forced "
+                   "miss uses a bracket below every score")
+    return out
+
+
 def midpoint_drift(L, torch, gen):
     """DFTopK's fixed midpoint threshold on the workload's rows: the mass the
     Laplace kernel assigns there against k (LapSum's own threshold gives k)."""
@@ -442,6 +472,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-trials", type=float, default=1.0,
                     help="scale of the planned hit-rate trial counts (0 skips them)")
+    ap.add_argument("--no-miss-cost", action="store_true", help="skip the forced-miss forward timings")
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -497,6 +528,16 @@ def main():
                 for nm in users:
                     results[nm]["hit_rate"] = hr
                 print(f"# hit rate {gen}: {hr['hits']}/{hr['total']}", file=sys.stderr, flush=True)
+    # cost of a missed bracket, and of the spread fallback when nothing misses
+    if not args.no_miss_cost:
+        for gen in ("extreme", "attack"):
+            users = [nm for nm in names if WORKLOADS[nm]["gen"] == gen and results[nm]["path"] == "bracket"]
+            if users:
+                mc = miss_cost(L, torch, gen)
+                for nm in users:
+                    results[nm]["miss_cost"] = mc
+                print(f"# miss cost {gen}: " + ", ".join(f"{k} {v:.3f}" for k, v in mc.items() if k != "note"),
+                      file=sys.stderr, flush=True)
     # DFTopK fixed-midpoint budget drift, per workload
     for gen in gens:
         md = midpoint_drift(L, torch, gen)

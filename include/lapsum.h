@@ -156,7 +156,14 @@ typedef struct lapsum_options {
                               no wider.  0 = 2, -1 = none, at most 4.  Rows whose bracket
                               came from bracket_override have no sample and go straight
                               to the fallback. */
-    int32_t reserved0;
+    int32_t spread_fallback; /* bracketing: 1 = a row whose bracket misses (or whose band
+                              overflows) is solved exactly by the whole-row bucket solve,
+                              launched after the band solve and spread over every workgroup
+                              (no widening; its b is the bucket path's for that row); 0 (the
+                              default) = widening, then the exact fallback, both inside the
+                              one workgroup that found the miss.  The extra launches cost a
+                              few microseconds each when every row hits, and the workspace
+                              grows by the bucket solve's (about 8 bytes per score). */
     const double *k_rows;  /* device [rows] or NULL: a budget per row (the k argument is then
                               not used).  Values must satisfy 0 < k_i < n; a row whose value
                               does not gets NaN outputs and LAPSUM_FLAG_INVALID. */

@@ -57,7 +57,7 @@ class Options(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("band_capacity", ctypes.c_int64),
                 ("bracket_override", ctypes.POINTER(ctypes.c_double)),
                 ("stats", ctypes.c_void_p), ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
-                ("widen_steps", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("widen_steps", ctypes.c_int32), ("spread_fallback", ctypes.c_int32),
                 ("k_rows", ctypes.c_void_p), ("t_rows", ctypes.c_void_p)]
 
 
@@ -121,7 +121,8 @@ def _check(rc: int, what: str):
 
 
 def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0, bracket_override=None,
-                 stats_ptr=None, stage_events=None, widen_steps=0, k_rows_ptr=None, t_rows_ptr=None):
+                 stats_ptr=None, stage_events=None, widen_steps=0, k_rows_ptr=None, t_rows_ptr=None,
+                 spread_fallback=0):
     opt = Options()
     load_library().lapsum_options_init(ctypes.byref(opt))
     opt.path = PATHS[path] if isinstance(path, str) else int(path)
@@ -130,6 +131,7 @@ def make_options(path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
     opt.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     opt.band_capacity = int(band_capacity)
     opt.widen_steps = int(widen_steps)
+    opt.spread_fallback = int(spread_fallback)
     opt.k_rows = k_rows_ptr
     opt.t_rows = t_rows_ptr
     keep = []
@@ -218,13 +220,16 @@ def _per_row(x, rows: int, dev, name: str):
 
 
 def lapsum_forward(r, k, t, *, path="auto", sample_log2=0, delta=0.0, seed=0, band_capacity=0,
-                   bracket_override=None, stats=False, stage_events=None, out=None, widen_steps=0):
+                   bracket_override=None, stats=False, stage_events=None, out=None, widen_steps=0,
+                   spread_fallback=False):
     """p, b (and per-row stats if stats=True) for scores r [rows, n] fp32 on GPU.
 
     k and t are floats, or tensors with one value per row (on-chip and
     full-sort paths).  p is fp32 [rows, n]; b is fp64 [rows].  Stats is an
     int/float dict of per-row tensors (bracket ends, tail sums, counts, band
-    size, flags)."""
+    size, flags).  spread_fallback: on the bracketing path, rows whose
+    bracket misses are solved by the whole-row bucket launches on every
+    workgroup instead of widening and one workgroup's fallback."""
     torch = _torch()
     lib = load_library()
     r2 = _as_rows(r, "r")
@@ -238,7 +243,8 @@ def lapsum_forward(r, k, t, *, path="auto", sample_log2=0, delta=0.0, seed=0, ba
         b = torch.empty(rows, dtype=torch.float64, device=dev) if out is None else out[1]
         st = torch.empty(rows * ctypes.sizeof(RowStats), dtype=torch.uint8, device=dev) if stats else None
         opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
-                           st.data_ptr() if st is not None else None, stage_events, widen_steps)
+                           st.data_ptr() if st is not None else None, stage_events, widen_steps,
+                           spread_fallback=int(bool(spread_fallback)))
         opt.k_rows = kr.data_ptr() if kr is not None else None
         opt.t_rows = tr.data_ptr() if tr is not None else None
         nbytes = int(lib.lapsum_workspace_bytes(rows, n, ks, ts, ctypes.byref(opt)))
@@ -392,7 +398,7 @@ class Operator:
 
     def __init__(self, rows: int, n: int, k: float, t: float, device=None, stream=None, path="auto", seed=0,
                  sample_log2=0, delta=0.0, band_capacity=0, bracket_override=None, stats_buf=None, widen_steps=0,
-                 k_rows=None, t_rows=None):
+                 k_rows=None, t_rows=None, spread_fallback=False):
         """k_rows / t_rows: optional per-row values (tensors of one value per
         row; they replace k / t, which are then not used)."""
         torch = _torch()
@@ -400,7 +406,8 @@ class Operator:
         self.rows, self.n, self.k, self.t = int(rows), int(n), float(k), float(t)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.opt = make_options(path, sample_log2, delta, seed, band_capacity, bracket_override,
-                                stats_buf.data_ptr() if stats_buf is not None else None, widen_steps=widen_steps)
+                                stats_buf.data_ptr() if stats_buf is not None else None, widen_steps=widen_steps,
+                                spread_fallback=int(bool(spread_fallback)))
         self._k_rows = _per_row(k_rows, self.rows, self.device, "k_rows")
         self._t_rows = _per_row(t_rows, self.rows, self.device, "t_rows")
         self.opt.k_rows = self._k_rows.data_ptr() if self._k_rows is not None else None

@@ -152,6 +152,12 @@ struct Plan {
   int fgx = 0;
   BandRegions bnd{};
   SegRegions full_seg{};
+  // bracketing with the spread fallback: the missed rows' own states and the
+  // whole-row bucket regions their solve runs in
+  bool spread = false;
+  size_t st2 = 0;
+  int64_t spread_cap = 0;
+  BandRegions spread_bnd{};
   SortRegions srt{};
   size_t bis_state = 0, bis_part = 0;
   int bis_gx = 0;
@@ -262,6 +268,7 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
   if (o.band_capacity < 0) return LAPSUM_ERR_OPTION;
   if (o.bracket_override && !(o.bracket_override[0] < o.bracket_override[1])) return LAPSUM_ERR_OPTION;
   if (o.widen_steps < -1 || o.widen_steps > kMaxWiden) return LAPSUM_ERR_OPTION;
+  if (o.spread_fallback < 0 || o.spread_fallback > 1) return LAPSUM_ERR_OPTION;
 
   int path = o.path;
   if (path == LAPSUM_PATH_AUTO)
@@ -303,8 +310,11 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     bracket_indices(n, per_row && o.k_rows ? 0.5 * (double)n : k, P.m, delta, &P.lo, &P.hi);
     // widened brackets: step i takes the indices for delta * 1e-6^i, kept
     // only where they are wider than the bracket before them (none with
-    // per-row budgets: a missed row goes straight to the exact fallback)
-    const int steps = per_row ? 0 : (o.widen_steps == 0 ? kDefaultWiden : (o.widen_steps < 0 ? 0 : o.widen_steps));
+    // per-row budgets or the spread fallback: a missed row goes straight to
+    // the exact whole-row solve)
+    const int steps = (per_row || o.spread_fallback)
+                          ? 0
+                          : (o.widen_steps == 0 ? kDefaultWiden : (o.widen_steps < 0 ? 0 : o.widen_steps));
     int64_t plo = P.lo, phi = P.hi;
     double d = delta;
     for (int i = 0; i < steps; ++i) {
@@ -343,7 +353,24 @@ lapsum_status make_plan(int64_t rows, int64_t n, double k, double t, const lapsu
     P.slots = F.take(band_slot_bytes(rows, P.fgx));
     P.offs = F.take(band_offs_bytes(rows, P.fgx));
     if (!P.band_onchip) P.bnd = band_regions(F, rows, P.cap, P.fgx, false, n);
-    P.full_seg = seg_regions(F, rows, n);
+    if (o.spread_fallback) {
+      // a missed row is solved by the whole-row bucket launches after the
+      // band kernels; the one-workgroup fallback's buffers are not needed
+      // (its argument block points at the bucket regions, never read)
+      P.spread = true;
+      P.st2 = F.take((size_t)rows * row_state_bytes());
+      P.spread_cap = round_up(n, kTile);
+      P.spread_bnd = band_regions(F, rows, P.spread_cap, 0, true, n);
+      P.full_seg.A = P.spread_bnd.keys;
+      P.full_seg.B = P.spread_bnd.tmp;
+      P.full_seg.tagg = P.spread_bnd.tagg;
+      P.full_seg.tpre = P.spread_bnd.tpre;
+      P.full_seg.tsuf = P.spread_bnd.tsuf;
+      P.full_seg.stride = P.spread_cap;
+      P.full_seg.max_tiles = P.spread_bnd.max_tiles;
+    } else {
+      P.full_seg = seg_regions(F, rows, n);
+    }
   }
   P.fwd_bytes = F.off;
 
@@ -369,7 +396,7 @@ struct StageTimer {
 
 SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const float *r, RowState *st, double k,
                  double t) {
-  SegArgs a;
+  SegArgs a{};
   a.rows = (int)rows;
   a.n = n;
   a.r = r;
@@ -392,13 +419,17 @@ SegArgs seg_args(const SegRegions &R, char *ws, int64_t rows, int64_t n, const f
   return a;
 }
 
-BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const uint32_t *slots, uint32_t *offs,
-                   double k, double t, const float *r, int64_t n, RowParams rp) {
-  const BandRegions &R = P.bnd;
-  BandArgs a;
+// Band mode (slots non-null: the plan's band regions and capacity) or whole
+// rows (r non-null: the given regions, cap = the padded row length).
+BandArgs band_args(const Plan &P, const BandRegions &R, int64_t cap, char *ws, int64_t rows, RowState *st,
+                   const uint32_t *slots, uint32_t *offs, double k, double t, const float *r, int64_t n,
+                   RowParams rp) {
+  BandArgs a{};
   a.rp = rp;
   a.nested = 0;  // the launcher decides
   a.src2 = nullptr;
+  a.need = 0;
+  a.st_out = nullptr;
   a.rows = (int)rows;
   a.gx = P.fgx;
   a.group = R.group;
@@ -411,7 +442,7 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   a.chunk = R.chunk;
   // about 32 keys per bucket: the whole row, or the band expected for this
   // capacity (a third of it)
-  a.bbits = bucket_bits(r != nullptr ? n : P.cap / 3);
+  a.bbits = bucket_bits(r != nullptr ? n : cap / 3);
   a.mm = r != nullptr ? reinterpret_cast<uint32_t *>(ws + R.mm) : nullptr;
   a.st = st;
   a.keys = reinterpret_cast<uint32_t *>(ws + R.keys);
@@ -426,7 +457,7 @@ BandArgs band_args(const Plan &P, char *ws, int64_t rows, RowState *st, const ui
   a.tagg = reinterpret_cast<TileAgg *>(ws + R.tagg);
   a.tpre = reinterpret_cast<Pre *>(ws + R.tpre);
   a.tsuf = reinterpret_cast<Suf *>(ws + R.tsuf);
-  a.cap = P.cap;
+  a.cap = cap;
   a.max_tiles = R.max_tiles;
   a.k = k;
   a.t = t;
@@ -531,7 +562,8 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     tm.mark(LAPSUM_STAGE_INIT, 1);
     tm.mark(LAPSUM_STAGE_BUCKET, 0);
     const SegArgs none{};  // full rows have no bracket, so no fallback
-    LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, nullptr, nullptr, k, t, r, n, rp), none, s));
+    LAPSUM_TRY(launch_band_buckets(band_args(P, P.bnd, P.cap, ws, rows, rs, nullptr, nullptr, k, t, r, n, rp), none,
+                                   s));
     tm.mark(LAPSUM_STAGE_BUCKET, 1);
   } else if (P.path == LAPSUM_PATH_SORT) {
     tm.mark(LAPSUM_STAGE_INIT, 0);
@@ -593,6 +625,7 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     tm.mark(LAPSUM_STAGE_BAND, 0);
     SegArgs fb = seg_args(P.full_seg, ws, rows, n, r, rs, k, t);
     fb.per_row = P.per_row ? 1 : 0;
+    fb.defer = P.spread ? 1 : 0;
     if (!ovr) {  // a bracket given by the caller has no sample to widen from
       fb.samples = reinterpret_cast<const float *>(ws + P.samples);
       fb.m = P.m;
@@ -606,7 +639,17 @@ lapsum_status lapsum_forward(const float *r, int64_t rows, int64_t n, double k, 
     if (P.band_onchip)
       LAPSUM_TRY(launch_band_onchip(slots, ws + P.fpart, P.fgx, rows, n, P.cap, rs, k, t, fb, s));
     else
-      LAPSUM_TRY(launch_band_buckets(band_args(P, ws, rows, rs, slots, offs, k, t, nullptr, n, rp), fb, s));
+      LAPSUM_TRY(launch_band_buckets(band_args(P, P.bnd, P.cap, ws, rows, rs, slots, offs, k, t, nullptr, n, rp), fb,
+                                     s));
+    if (P.spread) {
+      // the rows whose bracket missed (flagged in their own states): the
+      // whole-row bucket solve on every workgroup, b written back to rs
+      RowState *rs2 = reinterpret_cast<RowState *>(ws + P.st2);
+      BandArgs wa = band_args(P, P.spread_bnd, P.spread_cap, ws, rows, rs2, nullptr, nullptr, k, t, r, n, rp);
+      wa.need = kFlagDeferred;
+      wa.st_out = rs;
+      LAPSUM_TRY(launch_band_buckets(wa, SegArgs{}, s));
+    }
     tm.mark(LAPSUM_STAGE_BAND, 1);
   }
   tm.mark(LAPSUM_STAGE_APPLY, 0);

@@ -55,11 +55,14 @@ constexpr int kWaveBucket = 16 * kWave;    // largest balancing bucket one wave 
 static_assert(kBPT * kBT == kBandBuckets, "bucket count must be a multiple of the workgroup size");
 
 // A row takes part in a launch unless its band overflowed (it then takes
-// the fallback); on the second level of whole rows, only if its balancing
-// bucket was crowded.
+// the fallback), and only if its flags hold the launch's `need` bits (the
+// second level of whole rows: a crowded balancing bucket; the whole-row
+// solve after the band kernels: a missed bracket).
 LDEV bool band_active(const BandArgs &a, const RowState &S) {
-  return a.src2 != nullptr ? (S.flags & kFlagNested) != 0 : !(S.flags & LAPSUM_FLAG_OVERFLOW);
+  return (a.need == 0 || (S.flags & a.need) != 0) && !(S.flags & LAPSUM_FLAG_OVERFLOW);
 }
+// Launches restricted to flagged rows check the row first, before any load.
+LDEV bool band_skip(const BandArgs &a, const RowState &S) { return a.need != 0 && !band_active(a, S); }
 
 // Count/scatter workgroups that take part for a row: all of them, or on the
 // second level one per kSetChunk keys of the crowded bucket (the others
@@ -221,10 +224,34 @@ LDEV void for_each_band_key(const BandArgs &a, int64_t row, int blk, const uint3
 }
 
 // full-row mode: key minimum and maximum of each workgroup's chunk
+// The first launch of the spread fallback's whole-row solve: the rows the
+// band kernels left flagged FALLBACK (their bracket missed or their band
+// overflowed; a row with an invalid per-row k or t already holds b = NaN)
+// take part, each in a state of its own (flagged, with the row's k and t)
+// that its first workgroup writes; every other row's state is cleared.
+LDEV bool spread_begin(const BandArgs &a, int64_t row) {
+  const RowState &P = a.st_out[row];
+  const bool missed = (P.flags & LAPSUM_FLAG_FALLBACK) && !(P.flags & LAPSUM_FLAG_INVALID);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (missed) {
+      reset_row_state(a.st, row, kFlagDeferred, 0, 0.0, 0.0);
+      RowState &D = a.st[row];
+      D.k = P.k;
+      D.t = P.t;
+      D.c = P.c;
+      D.cf = P.cf;
+    } else {
+      a.st[row].flags = 0;
+    }
+  }
+  return missed;
+}
+
 __global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
   __shared__ uint32_t lmn[kBT / kWave], lmx[kBT / kWave];
   const int64_t row = grid_row();
   if (row >= a.rows) return;
+  if (a.need == kFlagDeferred ? !spread_begin(a, row) : band_skip(a, a.st[row])) return;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for_each_row_key(a, row, blockIdx.x, [&](uint32_t k) {
     mn = min(mn, k);
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   if (row >= a.rows) return;
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
-  if (a.src2 != nullptr && (!band_active(a, S) || blk >= row_blocks(a, S))) return;
+  if (band_skip(a, S) || blk >= row_blocks(a, S)) return;
   const int nb = 1 << a.bbits;
   for (int j = threadIdx.x; j < nb; j += kBT) {
     h[j] = 0u;
@@ -353,7 +380,7 @@ __global__ __launch_bounds__(kBT) void band_scan_kernel(BandArgs a) {
   const int64_t row = grid_row();
   if (row >= a.rows) return;
   const int j = blockIdx.x * kBT + threadIdx.x;
-  if (j >= (1 << a.bbits)) return;
+  if (j >= (1 << a.bbits) || band_skip(a, a.st[row])) return;
   uint32_t *h = a.hist + row * a.nblk * (int64_t)kBandBuckets + j;
   const uint32_t *ext = a.hext + row * a.nblk * (int64_t)(2 * kBandBuckets) + j;
   uint32_t v[kBandCountBlocks];
@@ -497,7 +524,7 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   }
   if (row >= a.rows) return;
   const RowState &S = a.st[row];
-  if (a.src2 != nullptr && (!band_active(a, S) || blk >= row_blocks(a, S))) return;
+  if (band_skip(a, S) || blk >= row_blocks(a, S)) return;
   // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
   // inside each bucket and its slot bounds, all loaded before any is used
   const int64_t o = row * kBandBuckets;
@@ -779,7 +806,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   const int64_t row = xcd_linear();
   if (row >= a.rows) return;
   RowState &S = a.st[row];
-  if (a.src2 != nullptr && !band_active(a, S)) return;  // second level: rows without a crowded bucket
+  if (band_skip(a, S)) return;  // a launch for flagged rows only
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
   // The bucket search runs on the first kLocScanW waves only (two per SIMD):
@@ -899,6 +926,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
     if (threadIdx.x == 0) {
       const double bb = (S.flags & LAPSUM_FLAG_INVALID) ? __builtin_nan("") : sel_b;
       S.b = bb;
+      if (a.st_out != nullptr) a.st_out[row].b = bb;
       if (FULL && a.src2 != nullptr) {
         // second level done: the row state describes the whole row again
         S.a_lo = -INFINITY;
@@ -917,7 +945,7 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   }
   if constexpr (!FULL) {
     __syncthreads();
-    if (sel_fb) missed_row<NT>(fb, (int)row, L.fb);
+    if (sel_fb && !fb.defer) missed_row<NT>(fb, (int)row, L.fb);
   }
 }
 
@@ -992,6 +1020,7 @@ hipError_t launch_band_buckets(const BandArgs &a_in, const SegArgs &fb, hipStrea
     // bucket records are reused (rows without a crowded bucket return at once)
     BandArgs a2 = a;
     a2.nested = 0;
+    a2.need = kFlagNested;
     a2.src2 = a.keys;
     a2.keys = a.tmp;
     a2.tmp = a.keys;

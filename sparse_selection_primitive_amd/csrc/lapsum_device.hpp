@@ -821,9 +821,11 @@ struct RowState {
                             // below / above it in a_lo, tail_lo, count_lo / a_hi, tail_hi, count_hi)
 };
 
-// Row state flag (never reported): the row's crowded balancing bucket waits
-// for the second bucket level.
+// Row state flags (never reported): the row's crowded balancing bucket
+// waits for the second bucket level; the row's bracket missed and its
+// whole-row solve waits for the bucket launches after the band kernels.
 constexpr int32_t kFlagNested = 1 << 16;
+constexpr int32_t kFlagDeferred = 1 << 17;
 
 // Per-call reset of one row's state (bracket open unless forced).
 LDEV void reset_row_state(RowState *st, int64_t row, int32_t flags, int has_override, double o_lo, double o_hi) {

@@ -66,6 +66,8 @@ struct SegArgs {
   int nwiden;           // widening steps (0: none)
   int64_t wlo[kMaxWiden], whi[kMaxWiden];
   int per_row;          // rows carry their own k, t, c, cf (in RowState): the fallback uses those
+  int defer;            // a missed row is left flagged for the whole-row bucket solve launched after
+                        // the band kernels (the spread fallback), not solved here
 };
 
 // Bucketed solve (bands too large for one workgroup, and whole rows of the
@@ -118,6 +120,9 @@ struct BandArgs {
                         // to a second, multi-workgroup bucket level (else one workgroup selects inside it)
   const uint32_t *src2; // second level (non-null): the first level's bucketed keys [rows][cap]; each flagged
                         // row's set is its crowded bucket, keys / tmp are this level's buffers
+  int32_t need;         // only rows whose state flags hold these bits take part (0: every row)
+  RowState *st_out;     // non-null: each final b is also written to this state array (the whole-row
+                        // solve of rows whose bracket missed, run on a state array of its own)
 };
 
 // Whole-row radix sort and the solve over the sorted rows (sort.hip): pass

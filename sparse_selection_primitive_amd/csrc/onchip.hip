@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kBandNT) void band_solve_onchip(const uint32_t *__r
   }
   if (threadIdx.x == 0) fall = (S.flags & LAPSUM_FLAG_FALLBACK) != 0;
   __syncthreads();
-  if (fall) missed_row<kBandNT>(fb, (int)row, lds.full);
+  if (fall && !fb.defer) missed_row<kBandNT>(fb, (int)row, lds.full);
 }
 
 hipError_t launch_band_onchip(const uint32_t *slots, const void *partials, int gx, int64_t rows, int64_t n,

@@ -202,6 +202,7 @@ LDEV bool widen_row(const SegArgs &a, int row, SegLds<NT> &L) {
 // With per-row budgets the row's own k, t (as the per-row bracket kernel
 // stored them) replace the call's, there are no widened brackets (their
 // indices depend on k), and a row whose k or t was out of range gets NaN.
+// (With the spread fallback the band kernels do not call it.)
 template <int NT>
 LDEV void missed_row(const SegArgs &a, int row, SegLds<NT> &L) {
   if (a.per_row) {

@@ -166,6 +166,24 @@ def test_plan_widen_steps_range(lib):
             L.plan(1, 3_317_760, 600, 1e-3, widen_steps=w)
 
 
+def test_plan_spread_fallback(lib):
+    """The spread fallback is a 0/1 option; it replaces the one-workgroup
+    fallback's two key buffers by the whole-row bucket regions (keys, scratch,
+    per-workgroup histograms) and a second row-state array, and it takes the
+    header's former reserved slot, so the options struct keeps its size."""
+    assert ctypes.sizeof(L.Options) == 80
+    n = 3_317_760
+    base = L.plan(2, n, 600, 1e-3)
+    spread = L.plan(2, n, 600, 1e-3, spread_fallback=1)
+    assert spread["path"] == L.PATH_BRACKET and spread["band_capacity"] == base["band_capacity"]
+    grown = spread["forward_bytes"] - base["forward_bytes"]
+    assert 0 < grown < 2 * 4 * n, grown  # histograms and states beyond the same two key buffers
+    assert L.plan(2, 20000, 600, 1e-3, spread_fallback=1)["path"] == L.PATH_BUCKET  # no bracket, no effect
+    for v in (-1, 2):
+        with pytest.raises(L.LapsumError, match="status 7"):
+            L.plan(1, n, 600, 1e-3, spread_fallback=v)
+
+
 def test_forward_rejects_null_and_small_workspace_without_launching(lib):
     opt = L.make_options()
     # NULL r with a valid shape: checked before anything is launched

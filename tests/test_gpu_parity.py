@@ -866,6 +866,36 @@ def test_extreme_row(L, O, path):
         f"dr_rel={rel:.2e} dk_rel={dk_rel:.2e} band={st['band'][0].item()}")
 
 
+def test_extreme_row_spread_miss(L, O):
+    """The 1e8 row with a bracket forced to miss and the spread fallback: the
+    row is solved by the whole-row bucket launches after the band solve (two
+    levels, every workgroup) instead of one workgroup's fallback.  b and p
+    against the oracle at every index, and p equal to the bucket path's bit
+    for bit; the forward's time is logged."""
+    E = _extreme_case(O)
+    w, b_or, p_or = E["w"], E["b_or"], E["p_or"]
+    log(f"[case] {w.name} forced miss, spread fallback")
+    rt = gpu(w.r)
+    opts = dict(path="bracket", bracket_override=(-3.0, -2.0), spread_fallback=True)
+    L.lapsum_forward(rt, w.k, w.t, **opts)  # warm-up (workspace, code)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    p, b, st = L.lapsum_forward(rt, w.k, w.t, stats=True, **opts)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert st["flags"][0].item() & L.FLAG_FALLBACK
+    db = abs(b.item() - b_or[0]) / w.t
+    assert db <= 1e-4, db
+    pg = p[0].cpu().numpy()
+    dp = _max_abs_diff_chunked(pg, p_or[0])
+    assert dp <= 2e-5, dp
+    pb, bb = L.lapsum_forward(rt, w.k, w.t, path="bucket")
+    torch.cuda.synchronize()
+    assert bb.item() == b.item() and torch.equal(pb, p)
+    log(f"  db/t={db:.2e} max|dp|={dp:.2e} forward with the miss {ms:.3f} ms (stats call)")
+
+
 # ------------------------------------------------------- non-finite scores
 @pytest.mark.parametrize("path,n", [("onchip", 300), ("bucket", 20000), ("bracket", 300_000)])
 def test_non_finite_rows_stay_contained(L, O, path, n):
