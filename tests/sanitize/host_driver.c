@@ -66,6 +66,8 @@ static void grid_of_plans(void) {
                         check_plan(rows, n, ks[e], t_list[d], &o);
                         o.band_capacity = 16;
                         check_plan(rows, n, ks[e], t_list[d], &o);
+                        o.spread_fallback = 1;
+                        check_plan(rows, n, ks[e], t_list[d], &o);
                     }
                 }
     check_plan(1, 1000, 10.0, 0.1, NULL);
@@ -102,6 +104,9 @@ static void rejected_arguments(void) {
     lapsum_options_init(&o);
     o.band_capacity = -1;
     EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_ERR_OPTION, "capacity -1");
+    lapsum_options_init(&o);
+    o.spread_fallback = 2;
+    EXPECT(lapsum_plan(1, 1 << 22, 1.0, 1.0, &o, &info) == LAPSUM_ERR_OPTION, "spread fallback 2");
     /* per-row parameters: bracketing reports its indices as per row (the
      * pointer is only compared with NULL on the host) */
     lapsum_options_init(&o);
