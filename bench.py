@@ -117,7 +117,7 @@ HIT_TRIALS = {"coder": 100, "attack": 1000, "extreme": 100}
 # Batches use every host core, single rows one core; about 30 s in all.
 CPU_PLAN = {"tiny": dict(threads="all", runs=3), "routing": dict(threads="all", runs=3),
             "coder": dict(threads="all", runs=3), "attack": dict(threads=1, runs=1),
-            "extreme": dict(threads=1, runs=1, prefix=1_000_000)}
+            "extreme": dict(threads=1, runs=1, prefix=5_000_000)}
 
 _WORKLOAD_CACHE = {}
 
