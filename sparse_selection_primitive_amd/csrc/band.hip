@@ -252,6 +252,8 @@ __global__ __launch_bounds__(kBT) void band_minmax_kernel(BandArgs a) {
   const int64_t row = grid_row();
   if (row >= a.rows) return;
   if (a.need == kFlagDeferred ? !spread_begin(a, row) : band_skip(a, a.st[row])) return;
+  lds_poison(lmn);
+  lds_poison(lmx);
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for_each_row_key(a, row, blockIdx.x, [&](uint32_t k) {
     mn = min(mn, k);
@@ -287,6 +289,11 @@ __global__ __launch_bounds__(kBT) void band_count_kernel(BandArgs a) {
   const int blk = blockIdx.x;
   RowState &S = a.st[row];
   if (band_skip(a, S) || blk >= row_blocks(a, S)) return;
+  lds_poison(h);
+  lds_poison(hmn);
+  lds_poison(hmx);
+  lds_poison(soffs);
+  lds_poison(rng);
   const int nb = 1 << a.bbits;
   for (int j = threadIdx.x; j < nb; j += kBT) {
     h[j] = 0u;
@@ -447,6 +454,9 @@ __global__ __launch_bounds__(kScanT) void band_scan_full_kernel(BandArgs a) {
   if (row >= a.rows) return;
   const RowState &S = a.st[row];
   if (!band_active(a, S)) return;
+  lds_poison(wt);
+  lds_poison(wmn);
+  lds_poison(wmx);
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int j = blockIdx.x * kWave + lane;
   const bool jin = j < (1 << a.bbits);
@@ -525,6 +535,9 @@ __global__ __launch_bounds__(kBT) void band_scatter_kernel(BandArgs a) {
   if (row >= a.rows) return;
   const RowState &S = a.st[row];
   if (band_skip(a, S) || blk >= row_blocks(a, S)) return;
+  lds_poison(base);
+  lds_poison(wsum);
+  lds_poison(sb);
   // bucket sizes (thread i owns buckets i*kBPT ..), this workgroup's offset
   // inside each bucket and its slot bounds, all loaded before any is used
   const int64_t o = row * kBandBuckets;
@@ -656,6 +669,7 @@ __global__ __launch_bounds__(kBT) void band_agg_buckets_kernel(BandArgs a) {
   const int cnt = (int)a.btot[o + j];
   const uint32_t bst = a.bstart[o + j];
   if (!band_active(a, S)) return;
+  lds_poison(big);
   const int shift = band_shift(S, a.bbits);
   const uint32_t *kb = a.keys + row * a.cap + bst;
   TileAgg *out = a.bagg + o + j;
@@ -709,6 +723,8 @@ __global__ __launch_bounds__(kBT) void band_agg_keys_kernel(BandArgs a) {
   const int64_t M = a.src2 != nullptr ? (int64_t)S.band : a.n;
   const int64_t c0 = (int64_t)blockIdx.x * kAggChunk;
   if (c0 >= M) return;
+  lds_poison(sp);
+  lds_poison(ss);
   const int64_t c1 = min(M, c0 + (int64_t)kAggChunk);
   double rk, rt, c;
   float rcf;
@@ -807,6 +823,9 @@ __global__ __launch_bounds__(NT) void band_locate_kernel(BandArgs a, SegArgs fb)
   if (row >= a.rows) return;
   RowState &S = a.st[row];
   if (band_skip(a, S)) return;  // a launch for flagged rows only
+  lds_poison(L);
+  lds_poison(sel_b);
+  lds_poison(sel_fb);
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t o = row * kBandBuckets;
   // The bucket search runs on the first kLocScanW waves only (two per SIMD):

@@ -30,6 +30,13 @@ def _case(kind):
     if kind == "coder_bracket":
         w = workloads.coder(rows=8)
         return w.r, w.g, w.k, w.t, "bracket"
+    if kind == "spread_miss":
+        # every row's bracket forced below b, solved by the spread fallback:
+        # its row states are set up afresh by each call's first bucket launch
+        g0 = np.random.Generator(np.random.PCG64(3504))
+        r = g0.standard_normal((2, 4_500_000)).astype(np.float32)
+        k = float(np.sum(r[0] > 1.06)) + 0.5
+        return r, g0.standard_normal((2, 4_500_000)).astype(np.float32), k, 0.01, "bracket"
     if kind == "bucket_crowded":
         # whole-row buckets of millions of keys: key-range bucket sums with
         # integer atomics, nested selection inside the balancing bucket
@@ -42,7 +49,8 @@ def _case(kind):
     return r, g0.standard_normal((1, 2_000_000)).astype(np.float32), 20000.0, 0.01, "bracket"
 
 
-@pytest.mark.parametrize("kind", ["routing", "routing_per_row", "coder_bracket", "bucket_band", "bucket_crowded"])
+@pytest.mark.parametrize("kind", ["routing", "routing_per_row", "coder_bracket", "bucket_band", "bucket_crowded",
+                                  "spread_miss"])
 def test_graph_replay_matches_eager(L, kind):
     r0, g0, k, t, path = _case(kind.replace("_per_row", ""))
     rows, n = r0.shape
@@ -54,6 +62,8 @@ def test_graph_replay_matches_eager(L, kind):
         gk = np.random.Generator(np.random.PCG64(3503))
         per_row = dict(k_rows=torch.from_numpy(gk.uniform(1.0, 20.0, rows)).to(dev),
                        t_rows=torch.from_numpy(gk.uniform(0.02, 0.2, rows)).to(dev))
+    if kind == "spread_miss":
+        per_row = dict(bracket_override=(-5.0, -4.0), spread_fallback=True)
     op = L.Operator(rows, n, k, t, device=dev, path=path, **per_row)
     outs = [torch.empty_like(r), torch.empty(rows, dtype=torch.float64, device=dev), torch.empty_like(r),
             torch.empty(rows, dtype=torch.float32, device=dev)]

@@ -1,6 +1,7 @@
 """The LDS-poisoning debug build (liblapsum_ldspoison.so, compiled with
 LAPSUM_LDS_POISON): the on-chip forward kernels, the on-chip band solve, the
-filter and its per-row totals set every byte of their LDS to 0xFF (NaN as
+filter and its per-row totals, and the bucket kernels (count, scans,
+scatter, aggregates, locate) set every byte of their LDS to 0xFF (NaN as
 fp32 and fp64, all ones as an integer) at entry.  Run against it, the parity
 cases below would show NaN or wrong values wherever a kernel read LDS that no
 thread of its launch had written.  The library is loaded in a child process
@@ -56,6 +57,18 @@ c = workloads.coder(rows=4)
 case("bracket coder (on-chip band)", c.r, c.k, c.t, c.g, path="bracket")
 r = (np.abs(rng.laplace(size=(1, 1_500_000)))).astype(np.float32)
 case("bracket attack-like row", r, 600.0, 1e-3, rng.standard_normal((1, 1_500_000)).astype(np.float32))
+# the bucket kernels: whole rows (few count workgroups, one-thread scan),
+# a bucketed band (capacity above the on-chip band), a 4.5M row whose crowded
+# balancing bucket takes the second level (wide scan), and a forced miss
+# solved by the spread fallback
+r = rng.standard_normal((3, 20000)).astype(np.float32)
+case("bucket rows", r, 3000.5, 0.05, rng.standard_normal((3, 20000)).astype(np.float32), path="bucket")
+r = rng.standard_normal((2, 600_000)).astype(np.float32)
+case("bracket bucketed band", r, 150_000.5, 0.01, path="bracket")
+r = rng.standard_normal((1, 4_500_000)).astype(np.float32)
+case("bucket second level", r, float(np.sum(r > 1.06)) + 0.5, 0.01, path="bucket")
+case("spread fallback", r, float(np.sum(r > 1.06)) + 0.5, 0.01, path="bracket", bracket_override=(-5.0, -4.0),
+     spread_fallback=True)
 print("all poison cases ok", flush=True)
 '''
 
