@@ -92,16 +92,16 @@ LDEV void store_row(float *pp, int n, int lane, bool ok, bool vec, const float (
 // temperatures.  The candidates s_0 <= ... <= s_{M-1} (blocked: lane l holds
 // s[l*E .. l*E+nv-1]) all lie at or above a0, everything below a0 is the
 // tail S = sum e^{(r - a0)/t}, and nothing lies above the window.  With every
-// sum anchored at a0 (u_i = e^{(s_i - a0)/t} >= 1 and v_i = 1/u_i, both
-// finite in fp32 when (s_{M-1} - a0) c <= kWindowSpan), the threshold curve at
-// knot j is
+// sum anchored at a0 (u_i = e^{(s_i - a0)/t} >= 1 and v_i = 1/u_i, held in
+// fp64, whose range covers them and their sums over at most 1024 knots when
+// (s_{M-1} - a0) c <= kWindowSpan), the threshold curve at knot j is
 //   g_j = (S + sum_{i<j} u_i) v_j / 2 + (M - j - 1/2) - u_j (sum_{i>j} v_i) / 2
 // (the knot itself counts F(0) = 1/2): plain prefix and suffix sums over the
 // team replace the re-anchored scans.  The last knot with g_j >= k is just
 // below the root, and the closed form between it and the next knot gives b
 // (section 2.2, full-sort solver: threshold curve, index lookup, closed-form
 // root).  Returns b on every team lane.
-constexpr float kWindowSpan = 120.0f;  // largest (s_{M-1} - a0) log2(e)/t of the fast solve
+constexpr float kWindowSpan = 1000.0f;  // largest (s_{M-1} - a0) log2(e)/t of the fast solve
 
 template <int E, int LANES>
 LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv, int M, float a0, double S,
@@ -110,7 +110,7 @@ LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv
   // into its integer part (applied exactly by ldexp) and a fraction in
   // [0, 1) for exp2: u and v carry the exp2's relative error only, however
   // large z is
-  float u[E], v[E];
+  double u[E], v[E];
   double lu = 0.0, lv = 0.0;
   const double c = kLog2e / t;
 #pragma unroll
@@ -118,10 +118,10 @@ LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv
     const double z = ((double)s[e] - (double)a0) * c;  // >= 0
     const double zi = floor(z);
     const float zf = (float)(z - zi);
-    u[e] = e < nv ? __builtin_ldexpf(__builtin_amdgcn_exp2f(zf), (int)zi) : 0.0f;
-    v[e] = e < nv ? __builtin_ldexpf(__builtin_amdgcn_exp2f(-zf), -(int)zi) : 0.0f;
-    lu += (double)u[e];
-    lv += (double)v[e];
+    u[e] = e < nv ? __builtin_ldexp((double)__builtin_amdgcn_exp2f(zf), (int)zi) : 0.0;
+    v[e] = e < nv ? __builtin_ldexp((double)__builtin_amdgcn_exp2f(-zf), -(int)zi) : 0.0;
+    lu += u[e];
+    lv += v[e];
   }
   // the u sums of the lanes before this one, the v sums of those after it
   double pu, sv;
@@ -134,20 +134,20 @@ LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       below[e] = acc;  // S + sum over knots before this one, at a0
-      acc += (double)u[e];
+      acc += u[e];
     }
     double acc2 = sv;
 #pragma unroll
     for (int e = E - 1; e >= 0; --e) {
       above[e] = acc2;  // sum over knots after this one, at a0
-      acc2 += (double)v[e];
+      acc2 += v[e];
     }
   }
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e < nv) {
-      const double g = 0.5 * below[e] * (double)v[e] + ((double)(M - base - e) - 0.5) - 0.5 * (double)u[e] * above[e];
+      const double g = 0.5 * below[e] * v[e] + ((double)(M - base - e) - 0.5) - 0.5 * u[e] * above[e];
       cnt += g >= k ? 1 : 0;
     }
   }
@@ -168,15 +168,15 @@ LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv
     } else {
       const int e0 = js - base;
       x = s[0];
-      PA = below[0] * (double)v[0] + 1.0;
-      QA = (double)u[0] * above[0];
+      PA = below[0] * v[0] + 1.0;
+      QA = u[0] * above[0];
       hi = js + 1 < M ? nxt_lane : INFINITY;
 #pragma unroll
       for (int e = 1; e < E; ++e) {
         if (e == e0) {
           x = s[e];
-          PA = below[e] * (double)v[e] + 1.0;
-          QA = (double)u[e] * above[e];
+          PA = below[e] * v[e] + 1.0;
+          QA = u[e] * above[e];
         }
         if (e == e0 + 1 && e < nv) hi = s[e];
       }
@@ -274,8 +274,14 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
     const int nv = min(max(C - 4 * team.lane, 0), 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) s4[q] = q < nv ? s4[q] : 0.0f;
-    part.nvalid = nv;
-    bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
+    const float last = nv == 4 ? s4[3] : (nv == 3 ? s4[2] : (nv == 2 ? s4[1] : s4[0]));
+    const float top = team.bcast(last, (C - 1) / 4);
+    if ((top - a) * cf <= kWindowSpan) {
+      bw = window_root<4>(team, s4, nv, C, a, S, kk, t);
+    } else {
+      part.nvalid = nv;
+      bw = segment_solve<4>(s4, nv, part, kk, t, c, cf, team);
+    }
   }
   b_out = MIRROR ? -bw : bw;
   return true;

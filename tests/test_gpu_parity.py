@@ -134,6 +134,20 @@ def test_onchip_end_cases(L, O, k):
     full_check(f"onchip k={k}", L, O, r, g, k, 0.3)
 
 
+@pytest.mark.parametrize("n,k,t", [(256, 8.0, 0.01), (256, 8.0, 0.004), (256, 14.5, 0.02), (256, 256 - 13.5, 0.01),
+                                   (64, 6.0, 0.005), (1024, 60.0, 0.003), (512, 31.0, 0.05)])
+def test_onchip_window_spans(L, O, n, k, t):
+    """The certified window of small budgets (and of the complement) at
+    temperatures where the window spans hundreds of log2 units (its anchored
+    sums are kept in fp64 up to a span of 1000), and budgets near the lane
+    count, whose window holds more than two candidates per lane."""
+    g0 = np.random.Generator(np.random.PCG64(2600 + n + int(k)))
+    rows = 256 if n <= 256 else 32
+    r = g0.standard_normal((rows, n)).astype(np.float32)
+    g = g0.standard_normal((rows, n)).astype(np.float32)
+    full_check(f"onchip window n={n} k={k} t={t}", L, O, r, g, k, t)
+
+
 def test_onchip_constant_and_single(L, O):
     r = np.full((2, 300), -2.5, np.float32)
     full_check("constant rows", L, O, r, None, 7.0, 0.05)
