@@ -288,6 +288,22 @@ def test_bucket_second_level(L, O, case):
         assert np.array_equal(res[key], again[key]), key
 
 
+@pytest.mark.parametrize("share", [0.3, 0.97])
+def test_bucket_second_level_heavy_tie(L, O, share):
+    """A 4.5M row where a share of the scores equals 1.0 exactly and the
+    root lies inside that run: the crowded bucket holds the run (with a few
+    neighbours, or nothing else when the run is almost the whole row), so
+    the second level meets a bucket of one distinct key."""
+    g0 = np.random.Generator(np.random.PCG64(3681))
+    n = 4_500_000
+    r = g0.standard_normal((1, n)).astype(np.float32)
+    r[0, g0.random(n) < share] = 1.0
+    above, tie = float(np.sum(r > 1.0)), float(np.sum(r == 1.0))
+    k = above + 0.37 * tie
+    res, _, _ = full_check(f"bucket second level, tie share {share}", L, O, r, None, k, 0.01, path="bucket")
+    assert np.array_equal(res["p"], run(L, r, k, 0.01, path="bucket")["p"])
+
+
 def test_bucket_second_level_mixed_rows(L, O):
     """A batch where only some rows crowd their balancing bucket: the
     second-level launches must leave the other rows' results alone (the
