@@ -191,8 +191,9 @@ LDEV double window_root(const WaveTeam<LANES> &team, const float (&s)[E], int nv
 }
 
 // Certified window for a small budget: with the K-th largest (K = ceil(k))
-// of the lanes' second-largest scores as a, at least 2K >= 2k scores are
-// >= a, each with p >= 1/2 at b = a, so f(a) >= k and b >= a.  Only the
+// of the lanes' second-largest scores as a (for K above half the lane
+// count, the 2K-th largest of the lanes' two largest), at least 2K >= 2k
+// scores are >= a, each with p >= 1/2 at b = a, so f(a) >= k and b >= a.  Only the
 // scores >= a (the candidates, typically a few times k) are sorted and
 // scanned; everything below a enters as one exact tail sum anchored at a,
 // exactly as the bracketing band solve seeds its scan.  A budget near n uses
@@ -217,10 +218,20 @@ LDEV bool window_solve(const WaveTeam<LANES> &team, const float (&v)[E], const b
     m2 = __builtin_amdgcn_fmed3f(m1, m2, w);
     m1 = fmaxf(m1, w);
   }
-  float x[1] = {m2};
-  bitonic_sort<1>(x, team);
   const int K = (int)ceil(kk);
-  const float a = team.bcast(x[0], LANES - K);
+  float a;
+  if (K > LANES / 2) {
+    // a budget near the lane count: the 2K-th largest of the lanes' two
+    // largest scores (at least 2K scores are >= it, and it is never below
+    // the K-th largest second score), which keeps the window small
+    float x2[2] = {m2, m1};
+    bitonic_sort<2>(x2, team);
+    a = team.bcast(x2[0], LANES - K);
+  } else {
+    float x[1] = {m2};
+    bitonic_sort<1>(x, team);
+    a = team.bcast(x[0], LANES - K);
+  }
   if (!(a > -INFINITY)) return false;
   int mine = 0;
 #pragma unroll
