@@ -32,7 +32,7 @@ def header_functions():
     return sorted(set(re.findall(r"\b(lapsum_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_north_star_entry_points():
+def test_header_declares_the_forward_and_backward_entry_points():
     fns = header_functions()
     for name in ("lapsum_forward", "lapsum_backward", "lapsum_workspace_bytes", "lapsum_status_string"):
         assert name in fns
