@@ -979,12 +979,14 @@ def test_autograd_wrapper(L):
 _MANY = {}
 
 
-@pytest.mark.parametrize("path", ["auto", "bucket", "bracket"])
+@pytest.mark.parametrize("path", ["auto", "bucket", "bracket", "spread"])
 def test_many_rows_beyond_one_grid_dimension(L, O, path):
     """70000 rows of 1100 scores: more rows than one launch dimension holds
     (65535), on every path (auto: the on-chip forward and the streaming
     backward, whose two passes put rows in the launch's second and third
-    dimensions), against the oracle on every row."""
+    dimensions; spread: bracketing with every bracket forced to miss, so
+    every row goes through the spread fallback's whole-row launches),
+    against the oracle on every row."""
     if not _MANY:
         g0 = np.random.Generator(np.random.PCG64(7001))
         r = g0.standard_normal((70000, 1100)).astype(np.float32)
@@ -995,7 +997,10 @@ def test_many_rows_beyond_one_grid_dimension(L, O, path):
         _MANY.update(r=r, g=g, k=k, t=t, p_or=p_or, b_or=b_or, dr_or=dr_or, dk_or=dk_or)
     M = _MANY
     log(f"[case] 70000x1100 rows path={path}")
-    res = run(L, M["r"], M["k"], M["t"], M["g"], path=path)
+    opts = dict(path=path)
+    if path == "spread":
+        opts = dict(path="bracket", bracket_override=(-20.0, -19.0), spread_fallback=True)
+    res = run(L, M["r"], M["k"], M["t"], M["g"], **opts)
     name = f"70000 rows ({path})"
     dp, db = check_forward(name, M["k"], M["t"], res["p"], res["b"], M["p_or"], M["b_or"])
     sums = res["p"].astype(np.float64).sum(axis=1)
